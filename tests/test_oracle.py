@@ -1,0 +1,475 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a value the pages print, a closed form,
+an invariant, a library routine (torch CPU in float64), brute force on tiny
+inputs, or finite differences. None of these tests touches the GPU library.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+torch.set_grad_enabled(True)
+
+
+def _tiny(**kw):
+    return W.get("tiny").with_(**kw)
+
+
+# ---------------------------------------------------------------- layout
+
+def test_param_counts_match_report():
+    """The d12 report prints 286.3M parameters, 261.1M of them non-embedding."""
+    cfg = W.get("d12")
+    offs, total = oracle.param_offsets(cfg)
+    non_emb = total - np.prod(offs["wte"][1])
+    assert round(total / 1e6, 1) == 286.3
+    assert round(non_emb / 1e6, 1) == 261.1
+    assert total == 286_288_920 and non_emb == 261_123_096
+
+
+def test_param_counts_other_configs():
+    got = {n: oracle.param_offsets(W.get(n))[1] for n in W.CONFIGS}
+    assert got == {"tiny": 590_084, "d12": 286_288_920, "d12_gqa": 176_170_008,
+                   "d20": 896_660_520, "d26": 1_682_066_100}
+
+
+def test_every_tensor_is_64_aligned():
+    for cfg in W.CONFIGS.values():
+        offs, _ = oracle.param_offsets(cfg)
+        for name, (o, s) in offs.items():
+            if not name.endswith("lambdas"):
+                assert o % 64 == 0, (cfg.name, name)
+
+
+def test_layer_patterns():
+    def pat(cfg):
+        L = cfg.n_layer
+        return ("".join("L" if oracle.layer_is_full(l, L) else "S" for l in range(L)),
+                [l for l in range(L) if oracle.layer_has_ve(l, L)])
+    assert pat(W.get("tiny")) == ("SL", [1])
+    # the report: value embeddings on layers 1, 3, 5, 7, 9, 11 of d12
+    assert pat(W.get("d12")) == ("SSSL" * 3, [1, 3, 5, 7, 9, 11])
+    assert pat(W.get("d20")) == ("SSSL" * 5, list(range(1, 20, 2)))
+    s26, ve26 = pat(W.get("d26"))
+    assert s26 == "SSSL" * 6 + "SL" and s26[-1] == "L"      # last layer forced full
+    assert ve26 == list(range(1, 26, 2)) and 25 in ve26
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rms_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 33)) * 3
+    y, r = oracle.rms_fwd(x, 2.0 ** -23)
+    ref = F.rms_norm(torch.from_numpy(x), (33,), eps=2.0 ** -23).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-14)
+    # invariant: mean(y^2) = ms / (ms + eps)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), ms / (ms + 2.0 ** -23), rtol=1e-13)
+
+
+def test_rms_bwd_matches_autograd():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 16))
+    gy = rng.standard_normal((5, 16))
+    y, r = oracle.rms_fwd(x, 1e-5)
+    xt = torch.from_numpy(x).requires_grad_()
+    F.rms_norm(xt, (16,), eps=1e-5).backward(torch.from_numpy(gy))
+    np.testing.assert_allclose(oracle.rms_bwd(gy, y, r), xt.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_invariants():
+    rng = np.random.default_rng(2)
+    T, D = 40, 64
+    cos, sin = oracle.rope_tables(T, D, 10000.0)
+    x = rng.standard_normal((1, T, 3, D))
+    y = oracle.rope_fwd(x, cos, sin)
+    # rotation: every (i, i + D/2) pair keeps its length
+    h = D // 2
+    np.testing.assert_allclose(x[..., :h] ** 2 + x[..., h:] ** 2,
+                               y[..., :h] ** 2 + y[..., h:] ** 2, rtol=1e-12)
+    # position 0 is the identity
+    np.testing.assert_allclose(y[:, 0], x[:, 0], rtol=0, atol=0)
+    # backward = inverse rotation
+    np.testing.assert_allclose(oracle.rope_bwd(y, cos, sin), x, atol=1e-12)
+    # <rope_m q, rope_n k> depends only on m - n
+    q = np.broadcast_to(rng.standard_normal(D), (1, T, 1, D))
+    k = np.broadcast_to(rng.standard_normal(D), (1, T, 1, D))
+    qr, kr = oracle.rope_fwd(q, cos, sin), oracle.rope_fwd(k, cos, sin)
+    d1 = np.dot(qr[0, 10, 0], kr[0, 3, 0])
+    d2 = np.dot(qr[0, 30, 0], kr[0, 23, 0])
+    assert abs(d1 - d2) < 1e-10
+    # frequencies: pair i advances by theta^(-2i/D) per position
+    assert abs(math.atan2(sin[1, 1], cos[1, 1]) - 10000.0 ** (-2 / D)) < 1e-14
+
+
+def test_rope_then_norm_commutes():
+    rng = np.random.default_rng(3)
+    T, D = 9, 64
+    cos, sin = oracle.rope_tables(T, D, 10000.0)
+    x = rng.standard_normal((2, T, 2, D))
+    a, _ = oracle.rms_fwd(oracle.rope_fwd(x, cos, sin), 2.0 ** -23)
+    b = oracle.rope_fwd(oracle.rms_fwd(x, 2.0 ** -23)[0], cos, sin)
+    np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+# ---------------------------------------------------------------- attention
+
+def _loop_attention(q, k, v, full, Wn):
+    """Brute force with scalar loops over (t, s)."""
+    B, T, H, D = q.shape
+    Hk = k.shape[2]
+    G = H // Hk
+    y = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            j = h // G
+            for t in range(T):
+                keys = [s for s in range(T) if s <= t and (full or t - s <= Wn)]
+                sc = np.array([np.dot(q[b, t, h], k[b, s, j]) / math.sqrt(D) for s in keys])
+                w = np.exp(sc - sc.max())
+                w /= w.sum()
+                y[b, t, h] = sum(wi * v[b, s, j] for wi, s in zip(w, keys))
+    return y
+
+
+@pytest.mark.parametrize("full", [True, False])
+def test_attention_matches_loops(full):
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((2, 13, 4, 8))
+    k = rng.standard_normal((2, 13, 2, 8))
+    v = rng.standard_normal((2, 13, 2, 8))
+    np.testing.assert_allclose(oracle.attention_fwd(q, k, v, full, 4),
+                               _loop_attention(q, k, v, full, 4), atol=1e-13)
+
+
+def test_attention_causal_equals_sdpa_with_repeated_kv():
+    """Full layers = torch SDPA is_causal; GQA = MHA with K/V heads repeated
+    contiguously; a window >= T - 1 reduces a short layer to causal."""
+    rng = np.random.default_rng(5)
+    B, T, H, Hk, D = 2, 37, 6, 2, 16
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, Hk, D))
+    v = rng.standard_normal((B, T, Hk, D))
+    t = lambda a: torch.from_numpy(a).transpose(1, 2)
+    kr = t(k).repeat_interleave(H // Hk, dim=1)
+    vr = t(v).repeat_interleave(H // Hk, dim=1)
+    ref = F.scaled_dot_product_attention(t(q), kr, vr, is_causal=True).transpose(1, 2).numpy()
+    np.testing.assert_allclose(oracle.attention_fwd(q, k, v, True, 0), ref, atol=1e-12)
+    np.testing.assert_allclose(oracle.attention_fwd(q, k, v, False, T - 1), ref, atol=1e-12)
+
+
+def test_attention_window_edge_and_degenerate():
+    rng = np.random.default_rng(6)
+    B, T, D = 1, 20, 8
+    q = rng.standard_normal((B, T, 1, D))
+    k = rng.standard_normal((B, T, 1, D))
+    v = rng.standard_normal((B, T, 1, D))
+    m = oracle.visible(T, False, 5)
+    assert m[10, 5] and not m[10, 4] and m[10, 10] and not m[10, 11]
+    assert m.sum(axis=1).min() >= 1
+    # W = 0: every query sees only itself -> y = v
+    np.testing.assert_allclose(oracle.attention_fwd(q, k, v, False, 0), v, atol=1e-14)
+    # T = 1 -> y = v
+    np.testing.assert_allclose(oracle.attention_fwd(q[:, :1], k[:, :1], v[:, :1], True, 0),
+                               v[:, :1], atol=1e-14)
+
+
+def test_attention_bwd_matches_autograd():
+    rng = np.random.default_rng(7)
+    B, T, H, Hk, D, Wn = 2, 23, 4, 2, 8, 6
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, Hk, D))
+    v = rng.standard_normal((B, T, Hk, D))
+    gy = rng.standard_normal((B, T, H, D))
+    for full in (True, False):
+        y = oracle.attention_fwd(q, k, v, full, Wn)
+        gq, gk, gv = oracle.attention_bwd(q, k, v, y, gy, full, Wn)
+        mask = torch.from_numpy(oracle.visible(T, full, Wn))
+        qt, kt, vt = (torch.from_numpy(a).requires_grad_() for a in (q, k, v))
+        tt = lambda a: a.transpose(1, 2)
+        out = F.scaled_dot_product_attention(
+            tt(qt), tt(kt).repeat_interleave(H // Hk, 1), tt(vt).repeat_interleave(H // Hk, 1),
+            attn_mask=mask)
+        out.transpose(1, 2).backward(torch.from_numpy(gy))
+        np.testing.assert_allclose(gq, qt.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(gk, kt.grad.numpy(), atol=1e-12)
+        np.testing.assert_allclose(gv, vt.grad.numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------- softcap + CE
+
+def test_softcap_ce_matches_torch():
+    rng = np.random.default_rng(8)
+    z = rng.standard_normal((9, 50)) * 20
+    y = rng.integers(0, 50, 9)
+    y[3] = -1
+    loss, gz, c = oracle.softcap_ce_fwd_bwd(z, y, 15.0)
+    assert np.abs(c).max() <= 15.0
+    zt = torch.from_numpy(z).requires_grad_()
+    ref = F.cross_entropy(15 * torch.tanh(zt / 15), torch.from_numpy(y), ignore_index=-1)
+    ref.backward()
+    assert abs(loss - ref.item()) < 1e-13
+    np.testing.assert_allclose(gz, zt.grad.numpy(), atol=1e-15)
+    # small-z expansion: 15 tanh(z/15) ~ z - z^3/675
+    zs = np.array([[1e-3, -2e-3]])
+    _, _, cs = oracle.softcap_ce_fwd_bwd(zs, np.array([0]), 15.0)
+    np.testing.assert_allclose(cs, zs - zs ** 3 / 675, rtol=1e-12)
+    # each valid row's logit gradient sums to zero
+    assert np.abs(gz.sum(axis=1)[y >= 0] / (1 - 0)).max() < 1  # bounded
+    _, gz0, _ = oracle.softcap_ce_fwd_bwd(np.zeros((4, 10)), np.array([1, 2, 3, -1]), 15.0)
+    np.testing.assert_allclose(gz0.sum(axis=1), 0, atol=1e-16)
+
+
+@pytest.mark.parametrize("name", ["tiny"])
+def test_zero_lm_head_gives_ln_vocab(name):
+    """All-zero lm_head: every logit is 0, so the loss is ln V exactly and
+    the logit gradient is (1/V - onehot) / N."""
+    cfg = W.get(name)
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 7).astype(np.float64)
+    o, s = offs["lm_head"]
+    p[o:o + np.prod(s)] = 0
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    loss, grads, acts = oracle.forward_backward(cfg, p, tok, tgt, return_acts=True)
+    assert abs(loss - math.log(cfg.vocab)) < 1e-12
+    assert abs(math.log(512) - 6.2383) < 1e-4
+    gz = acts["final"]["gz"]
+    N = tgt.size
+    ref = np.full_like(gz, 1.0 / cfg.vocab / N)
+    ref[np.arange(N), tgt.reshape(-1)] -= 1.0 / N
+    np.testing.assert_allclose(gz, ref, atol=1e-17)
+
+
+def test_init_loss_near_ln_vocab():
+    """With N(0, 0.02^2) weights the logits are small; the loss sits near
+    ln V + 0.02^2 * C / 2 (a statistical statement, tolerance 1e-2)."""
+    cfg = W.get("tiny")
+    _, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, W.weight_seed(cfg)).astype(np.float64)
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    loss = oracle.forward_loss(cfg, p, tok, tgt)
+    assert abs(loss - (math.log(512) + 0.02 ** 2 * 128 / 2)) < 2e-2
+
+
+# ---------------------------------------------------------------- structure
+
+def test_uniform_attention_closed_form():
+    """Wq = Wk = 0 makes q = k = 0 after RoPE and QK-norm, so each query
+    averages v over its visible keys; Wg = 0 makes the value-embedding gate
+    exactly 1/2. With an identity-like Wo and zero MLP the block output is
+    checked against cumulative means, for the short and the full layer."""
+    cfg = _tiny(n_layer=2, batch=1)
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, 2, 11).astype(np.float64)
+    P = oracle.unpack(cfg, p)
+    for l in range(2):
+        P[f"l{l}.q"][...] = 0
+        P[f"l{l}.k"][...] = 0
+        P[f"l{l}.fc"][...] = 0
+    P["l1.veg"][...] = 0
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    _, _, acts = oracle.forward_backward(cfg, p, tok, tgt, return_acts=True)
+    T, Wn = cfg.seq_len, cfg.short_window
+    for l, full in ((0, False), (1, True)):
+        c = acts[l]
+        xn = c["xn"]
+        v = (xn @ P[f"l{l}.v"].T).reshape(T, cfg.n_kv_head, cfg.head_dim)
+        if l == 1:
+            v = v + 0.5 * P["l1.ve"][tok[0]].reshape(T, cfg.n_kv_head, cfg.head_dim)
+        ref = np.zeros((T, cfg.n_head, cfg.head_dim))
+        for t in range(T):
+            lo = 0 if full else max(0, t - Wn)
+            ref[t] = np.repeat(v[lo:t + 1].mean(axis=0), cfg.n_head // cfg.n_kv_head, axis=0)
+        np.testing.assert_allclose(c["y"][0], ref, atol=1e-12)
+        # the residual stream after the block: xin + y Wo^T (MLP is zero)
+        np.testing.assert_allclose(c["xm"], c["xin"] + ref.reshape(T, -1) @ P[f"l{l}.o"].T,
+                                   atol=1e-12)
+    # the mix: xin = lr * x + l0 * x0 with x0 = wte[tok]
+    x0 = P["wte"][tok[0]]
+    lr, l0 = P["resid_lambdas"], P["x0_lambdas"]
+    np.testing.assert_allclose(acts[0]["xin"], (lr[0] + l0[0]) * x0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(acts[1]["xin"], lr[1] * acts[0]["xm"] + l0[1] * x0,
+                               rtol=0, atol=1e-15)
+
+
+def test_identity_blocks_reduce_to_unigram_model():
+    """o = mp = 0 makes every block add nothing, so the loss depends only on
+    wte and lm_head through rms, softcap and CE (torch library routines)."""
+    cfg = W.get("tiny")
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 12).astype(np.float64) * 10
+    P = oracle.unpack(cfg, p)
+    for l in range(cfg.n_layer):
+        P[f"l{l}.o"][...] = 0
+        P[f"l{l}.mp"][...] = 0
+    P["resid_lambdas"][...] = [0.7, 1.3]
+    P["x0_lambdas"][...] = [0.2, 0.5]
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    loss = oracle.forward_loss(cfg, p, tok, tgt)
+    x0 = torch.from_numpy(P["wte"][tok.reshape(-1)])
+    a = (0.7 * 1 + 0.2) * 1.3 + 0.5           # x after two mixes = a * x0
+    xf = F.rms_norm(a * x0, (cfg.n_embd,), eps=2.0 ** -23)
+    z = xf @ torch.from_numpy(P["lm_head"]).T
+    ref = F.cross_entropy(15 * torch.tanh(z / 15), torch.from_numpy(tgt.reshape(-1)).long())
+    assert abs(loss - ref.item()) < 1e-12
+
+
+# ---------------------------------------------------------------- gradients
+
+def _fd_entries(cfg, rng, per_tensor=20):
+    offs, total = oracle.param_offsets(cfg)
+    idx = []
+    for name, (o, s) in offs.items():
+        n = int(np.prod(s))
+        if name.endswith("lambdas"):
+            idx += [o + i for i in range(n)]
+        else:
+            idx += list(o + rng.choice(n, size=min(per_tensor, n), replace=False))
+    return idx
+
+
+def test_finite_differences_tiny():
+    """Central differences in float64 on every lambda and 20 random entries
+    of every other tensor. Entries of the embedding tables are drawn from the
+    rows the batch uses, where the gradient is not trivially zero."""
+    cfg = W.get("tiny")
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, W.weight_seed(cfg)).astype(np.float64)
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    _, g = oracle.forward_backward(cfg, p, tok, tgt)
+    rng = np.random.default_rng(9)
+    idx = _fd_entries(cfg, rng)
+    used = np.unique(tok)
+    for name in ("wte", "l1.ve"):
+        o, s = offs[name]
+        rows = rng.choice(used, 20)
+        cols = rng.integers(0, s[1], 20)
+        idx += list(o + rows * s[1] + cols)
+    h = 1e-5
+    worst = 0.0
+    for i in idx:
+        pp = p.copy(); pp[i] += h
+        pm = p.copy(); pm[i] -= h
+        fd = (oracle.forward_loss(cfg, pp, tok, tgt) - oracle.forward_loss(cfg, pm, tok, tgt)) / (2 * h)
+        err = abs(fd - g[i]) / max(abs(g[i]), 1e-4)
+        worst = max(worst, err)
+        assert err < 1e-6, (i, fd, g[i])
+    assert worst < 1e-6
+
+
+def _torch_model_loss(cfg, params, tok, tgt):
+    """The model assembled from torch library ops (rms_norm, SDPA with an
+    explicit mask, cross_entropy) for an autograd cross-check."""
+    L, C, H, Hk, D = cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_kv_head, cfg.head_dim
+    B, T = tok.shape
+    offs, _ = oracle.param_offsets(cfg)
+    Pt = {n: params[o:o + int(np.prod(s))].view(*s) for n, (o, s) in offs.items()}
+    tk = torch.from_numpy(tok).long()
+    eps = cfg.norm_eps
+    pos = torch.arange(T, dtype=torch.float64)[:, None]
+    inv = cfg.rope_theta ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+    ang = pos * inv[None]
+    cs, sn = torch.cos(ang)[None, :, None, :], torch.sin(ang)[None, :, None, :]
+
+    def rot(x):
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return torch.cat([a * cs - b * sn, a * sn + b * cs], -1)
+
+    x0 = F.embedding(tk, Pt["wte"])
+    x = x0
+    for l in range(L):
+        x = Pt["resid_lambdas"][l] * x + Pt["x0_lambdas"][l] * x0
+        xn = F.rms_norm(x, (C,), eps=eps)
+        q = F.linear(xn, Pt[f"l{l}.q"]).view(B, T, H, D)
+        k = F.linear(xn, Pt[f"l{l}.k"]).view(B, T, Hk, D)
+        v = F.linear(xn, Pt[f"l{l}.v"]).view(B, T, Hk, D)
+        q = F.rms_norm(rot(q), (D,), eps=eps)
+        k = F.rms_norm(rot(k), (D,), eps=eps)
+        if oracle.layer_has_ve(l, L):
+            g = torch.sigmoid(F.linear(xn, Pt[f"l{l}.veg"]))[..., None]
+            v = v + g * F.embedding(tk, Pt[f"l{l}.ve"]).view(B, T, Hk, D)
+        full = l % 4 == 3 or l == L - 1
+        ti = torch.arange(T)
+        mask = (ti[None, :] <= ti[:, None])
+        if not full:
+            mask &= (ti[:, None] - ti[None, :]) <= cfg.short_window
+        y = F.scaled_dot_product_attention(
+            q.transpose(1, 2), k.transpose(1, 2).repeat_interleave(H // Hk, 1),
+            v.transpose(1, 2).repeat_interleave(H // Hk, 1), attn_mask=mask)
+        x = x + F.linear(y.transpose(1, 2).reshape(B, T, H * D), Pt[f"l{l}.o"])
+        x = x + F.linear(F.relu(F.linear(F.rms_norm(x, (C,), eps=eps), Pt[f"l{l}.fc"])).square(),
+                         Pt[f"l{l}.mp"])
+    z = F.linear(F.rms_norm(x, (C,), eps=eps), Pt["lm_head"])
+    c = cfg.softcap * torch.tanh(z / cfg.softcap)
+    return F.cross_entropy(c.view(B * T, -1), torch.from_numpy(tgt).long().view(-1),
+                           ignore_index=-1)
+
+
+@pytest.mark.parametrize("variant", ["tiny", "tiny_gqa_ignore"])
+def test_full_model_matches_torch_autograd(variant):
+    cfg = W.get("tiny")
+    if variant == "tiny_gqa_ignore":
+        cfg = cfg.with_(n_head=4, n_kv_head=2, head_dim=32, n_layer=4, short_window=5)
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 21).astype(np.float64)
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    if variant == "tiny_gqa_ignore":
+        tgt = tgt.copy()
+        tgt[0, :5] = -1
+    loss, g = oracle.forward_backward(cfg, p, tok, tgt)
+    pt = torch.from_numpy(p.copy()).requires_grad_()
+    ref = _torch_model_loss(cfg, pt, tok, tgt)
+    ref.backward()
+    assert abs(loss - ref.item()) < 1e-12 * abs(loss)
+    ref_g = pt.grad.numpy()
+    for name, (o, s) in offs.items():
+        n = int(np.prod(s))
+        a, b = g[o:o + n], ref_g[o:o + n]
+        assert np.linalg.norm(a - b) <= 1e-10 * max(np.linalg.norm(b), 1e-30), name
+
+
+def test_fp32_mode_close_to_fp64():
+    cfg = W.get("tiny")
+    _, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 5)
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    l64, g64 = oracle.forward_backward(cfg, p.astype(np.float64), tok, tgt)
+    l32, g32 = oracle.forward_backward(cfg, p, tok, tgt, dtype=np.float32)
+    assert abs(l32 - l64) / l64 < 1e-6
+    assert np.linalg.norm(g32 - g64) / np.linalg.norm(g64) < 1e-5
+
+
+# ---------------------------------------------------------------- fp8
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_rounding_matches_torch(fmt, tdt):
+    codes = torch.arange(256, dtype=torch.uint8).view(tdt).double().numpy()
+    codes = codes[np.isfinite(codes)]
+    np.testing.assert_array_equal(oracle.fp8.round_fp8(codes, fmt), codes)
+    fmax = oracle.fp8.FORMATS[fmt][2]
+    rng = np.random.default_rng(10)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-5, 1e-2, 1, 30, 3000)])
+    x = np.clip(x, -fmax, fmax)
+    ref = torch.from_numpy(x).to(tdt).double().numpy()
+    np.testing.assert_array_equal(oracle.fp8.round_fp8(x, fmt), ref)
+    # saturation
+    assert oracle.fp8.round_fp8(np.array([1e9, -1e9]), fmt).tolist() == [fmax, -fmax]
+
+
+def test_fp8_qdq_scaling():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(1000)
+    q = oracle.fp8.qdq(x, "e4m3")
+    i = np.argmax(np.abs(x))
+    assert abs(q[i] - x[i]) <= 1e-6 * abs(x[i])        # amax maps to +-fmax exactly
+    assert np.max(np.abs(q - x)) <= np.max(np.abs(x)) * 2.0 ** -4
+    assert np.all(oracle.fp8.qdq(np.zeros(5), "e5m2") == 0)
