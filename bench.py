@@ -1,0 +1,186 @@
+"""Throughput of the nanochat GPT forward+backward step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
+                    [--no-cpu-baseline] [--profile-site PREFIX]
+
+One step = one gpt_fwd_bwd call (loss + every parameter gradient) over one
+batch of seeded synthetic tokens, inputs already resident in HBM. Prints one
+JSON line with tokens/s, the model-FLOP fraction of the dense bf16 MFMA peak,
+the roofline figures of the dominant kernel (timed with HIP events on the
+call's stream during the timed steps) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E (published)
+METRIC = "train tokens/sec (fwd+bwd) d12 seq2048, 1 GPU; MFMA util vs bf16 peak"
+
+
+def _full(l, L):
+    return l % 4 == 3 or l == L - 1
+
+
+def _ve(l, L):
+    return (l % 2) == ((L - 1) % 2)
+
+
+def model_flops_per_token(w) -> float:
+    """6 FLOPs per matrix weight used in a product (forward 2, backward 4)
+    plus 12 * H * D per visible key per layer (useful attention only; the
+    window and the causal mask are not counted)."""
+    C, H, Hk, D, F, V, L = (w.n_embd, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden,
+                            w.vocab, w.n_layer)
+    T, Wn = w.seq_len, w.short_window
+    n_mat = V * C
+    kbar = 0.0
+    for l in range(L):
+        n_mat += (H + 2 * Hk) * D * C + C * H * D + 2 * F * C
+        if _ve(l, L):
+            n_mat += Hk * C
+        if _full(l, L):
+            kbar += (T + 1) / 2
+        else:
+            win = min(Wn, T - 1)
+            kbar += (win * (win + 1) / 2 + (T - win) * (win + 1)) / T
+    return 6.0 * n_mat + 12.0 * H * D * kbar
+
+
+def lm_head_fwd_flops(w) -> float:
+    """Algorithmic FLOPs of one lm_head forward launch: 2 * N * V * C."""
+    return 2.0 * w.batch * w.seq_len * w.vocab * w.n_embd
+
+
+def param_total(w) -> int:
+    C, H, Hk, D, F, V, L = (w.n_embd, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden,
+                            w.vocab, w.n_layer)
+    n = 2 * V * C + 2 * L
+    for l in range(L):
+        n += (H + 2 * Hk) * D * C + C * H * D + 2 * F * C
+        if _ve(l, L):
+            n += V * Hk * D + Hk * C
+    return n
+
+
+def cpu_baseline(w, params, tokens, targets, rows: int):
+    """The oracle (unchanged) on the first `rows` batch rows of the same
+    inputs: tokens/s of its fwd+bwd, on the host's cores."""
+    import oracle  # test infrastructure: only this leg of the benchmark uses it
+    sub = w.with_(batch=rows)
+    t0 = time.perf_counter()
+    oracle.forward_backward(sub, params, tokens[:rows], targets[:rows], dtype=np.float32)
+    dt = time.perf_counter() - t0
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads", 0) for i in info), default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"value": rows * w.seq_len / dt, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{rows} of {w.batch} batch rows ({rows * w.seq_len} tokens) of the "
+                      f"{w.name} workload, one fp32 forward+backward, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="d12")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1)
+    ap.add_argument("--profile-site", default="gemm.lm.fwd",
+                    help="launch site timed with HIP events for the roofline figure")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is "
+              "not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decoder_only_pretraining_amd import binding as B
+
+    w = W.get(args.config)
+    total = param_total(w)
+    params = W.gen_params(total, w.n_layer, W.weight_seed(w))
+    tokens, targets = W.split_tokens(W.gen_tokens(w))
+    step = B.Step(w, params, tokens, targets, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        step.run(stream)
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B.profile_begin(args.profile_site)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step.run(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms, kern_n = B.profile_end()
+    gpu_ms = start.elapsed_time(stop)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    loss = float(step.loss.item())
+    assert np.isfinite(loss), loss
+
+    ntok = w.batch * w.seq_len
+    tps = ntok / (ms_per_step / 1e3)
+    mflop = model_flops_per_token(w)
+    frac = tps * mflop / PEAK_BF16_FLOPS
+
+    roof = None
+    if kern_n > 0:
+        avg_s = kern_ms / kern_n / 1e3
+        if args.profile_site == "gemm.lm.fwd":
+            achieved = lm_head_fwd_flops(w) / avg_s / 1e12
+            roof = {"kernel": "gemm.lm.fwd (lm_head GEMM + tanh softcap epilogue)",
+                    "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                    "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4), "traffic": None,
+                    "avg_launch_ms": round(avg_s * 1e3, 4), "launches": kern_n}
+        else:
+            roof = {"kernel": args.profile_site, "avg_launch_ms": round(avg_s * 1e3, 4),
+                    "launches": kern_n}
+
+    out = {
+        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) weights)",
+        "config": {"workload": f"{w.name}: {w.n_layer} layers, n_embd {w.n_embd}, heads "
+                               f"{w.n_head}/{w.n_kv_head}, head_dim {w.head_dim}, MLP "
+                               f"{w.mlp_hidden}, vocab {w.vocab}, seq {w.seq_len}, batch "
+                               f"{w.batch}, window {w.short_window}",
+                   "seq_len": w.seq_len, "batch": w.batch, "tokens_per_step": ntok,
+                   "parallelism": "none (1 GPU)"},
+        "mfma_util_vs_bf16_peak": round(frac, 4),
+        "model_mflop_per_token": round(mflop / 1e6, 3),
+        "loss": round(loss, 5),
+        "roofline": roof,
+        "context": {"pages_rtx4070_full_step_tokens_per_s": 55670},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, params, tokens, targets, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+"""ctypes binding of libgptstep.so (the gfx950 GPT step library).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/gpt_step.h. torch is used for
+device memory and the current stream. The library must have been built
+(``decoder_only_pretraining_amd.build``); loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgptstep.so")
+
+GPT_ABI_VERSION = 1
+GPT_DT_F32, GPT_DT_BF16 = 0, 1
+GPT_F_ACCUMULATE = 1
+
+STATUS = {0: "GPT_OK", -1: "GPT_E_INVAL", -2: "GPT_E_NULLPTR", -3: "GPT_E_ALIGN",
+          -4: "GPT_E_WORKSPACE", -5: "GPT_E_UNSUPPORTED", -6: "GPT_E_HIP"}
+
+EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_param_info",
+           "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region", "gpt_fwd_bwd",
+           "gpt_fwd", "gpt_status_string", "gpt_last_error", "gpt_profile_begin",
+           "gpt_profile_end"]
+
+
+class GptConfig(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("n_layer", ctypes.c_int32),
+                ("n_embd", ctypes.c_int32), ("n_head", ctypes.c_int32),
+                ("n_kv_head", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("mlp_hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("short_window", ctypes.c_int32), ("compute_dtype", ctypes.c_int32),
+                ("fp8_linears", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float),
+                ("softcap", ctypes.c_float)]
+
+
+class GptError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "python -m decoder_only_pretraining_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        P = c.POINTER
+        L.gpt_abi_version.restype = c.c_int
+        L.gpt_config_validate.argtypes = [P(GptConfig)]
+        L.gpt_param_count.argtypes = [P(GptConfig), P(c.c_int64), P(c.c_int64)]
+        L.gpt_param_info.argtypes = [P(GptConfig), c.c_int64, c.c_char_p, P(c.c_int64),
+                                     P(c.c_int64), P(c.c_int64)]
+        L.gpt_layer_info.argtypes = [P(GptConfig), c.c_int32, P(c.c_int32), P(c.c_int32)]
+        L.gpt_workspace_size.argtypes = [P(GptConfig), P(c.c_size_t)]
+        L.gpt_workspace_region.argtypes = [P(GptConfig), c.c_char_p, c.c_int32,
+                                           P(c.c_size_t), P(c.c_size_t)]
+        L.gpt_fwd_bwd.argtypes = [P(GptConfig), c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                  c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
+        L.gpt_fwd.argtypes = [P(GptConfig), c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                              c.c_void_p, c.c_size_t, c.c_void_p]
+        L.gpt_status_string.restype = c.c_char_p
+        L.gpt_status_string.argtypes = [c.c_int]
+        L.gpt_last_error.restype = c.c_char_p
+        L.gpt_profile_begin.argtypes = [c.c_char_p]
+        L.gpt_profile_begin.restype = c.c_int
+        L.gpt_profile_end.argtypes = [P(c.c_double), P(c.c_int64)]
+        L.gpt_profile_end.restype = c.c_int
+        for name in ("gpt_config_validate", "gpt_param_count", "gpt_param_info",
+                     "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region",
+                     "gpt_fwd_bwd", "gpt_fwd"):
+            getattr(L, name).restype = c.c_int
+        if L.gpt_abi_version() != GPT_ABI_VERSION:
+            raise RuntimeError("libgptstep.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(fn, st):
+    if st != 0:
+        raise GptError(fn, st, lib().gpt_last_error().decode())
+
+
+def make_config(w, flags: int = 0, **over) -> GptConfig:
+    """GptConfig from a workload description (attribute access)."""
+    f = dict(abi_version=GPT_ABI_VERSION, n_layer=w.n_layer, n_embd=w.n_embd,
+             n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+             mlp_hidden=w.mlp_hidden, vocab=w.vocab, seq_len=w.seq_len, batch=w.batch,
+             short_window=w.short_window,
+             compute_dtype=GPT_DT_BF16 if w.compute_dtype == "bf16" else GPT_DT_F32,
+             fp8_linears=int(bool(w.fp8_linears)), flags=flags, rope_theta=w.rope_theta,
+             norm_eps=w.norm_eps, softcap=w.softcap)
+    f.update(over)
+    return GptConfig(**f)
+
+
+def validate(cfg: GptConfig) -> int:
+    return lib().gpt_config_validate(ctypes.byref(cfg))
+
+
+def param_count(cfg):
+    nt, ne = ctypes.c_int64(), ctypes.c_int64()
+    _check("gpt_param_count", lib().gpt_param_count(ctypes.byref(cfg), ctypes.byref(nt),
+                                                    ctypes.byref(ne)))
+    return nt.value, ne.value
+
+
+def param_layout(cfg):
+    """[(name, offset, rows, cols)] in canonical order."""
+    nt, _ = param_count(cfg)
+    out = []
+    buf = ctypes.create_string_buffer(64)
+    o, r, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    for i in range(nt):
+        _check("gpt_param_info", lib().gpt_param_info(ctypes.byref(cfg), i, buf, ctypes.byref(o),
+                                                      ctypes.byref(r), ctypes.byref(c)))
+        out.append((buf.value.decode(), o.value, r.value, c.value))
+    return out
+
+
+def layer_info(cfg, l):
+    f, v = ctypes.c_int32(), ctypes.c_int32()
+    _check("gpt_layer_info", lib().gpt_layer_info(ctypes.byref(cfg), l, ctypes.byref(f),
+                                                  ctypes.byref(v)))
+    return bool(f.value), bool(v.value)
+
+
+def workspace_size(cfg) -> int:
+    b = ctypes.c_size_t()
+    _check("gpt_workspace_size", lib().gpt_workspace_size(ctypes.byref(cfg), ctypes.byref(b)))
+    return b.value
+
+
+def workspace_region(cfg, name: str, layer: int = 0):
+    o, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("gpt_workspace_region", lib().gpt_workspace_region(
+        ctypes.byref(cfg), name.encode(), layer, ctypes.byref(o), ctypes.byref(b)))
+    return o.value, b.value
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def fwd_bwd(cfg, params, tokens, targets, loss, grads, workspace, stream=None):
+    """Enqueue one forward+backward on `stream` (default: torch's current
+    stream). All tensors are device tensors owned by the caller."""
+    st = lib().gpt_fwd_bwd(ctypes.byref(cfg), params.data_ptr(), tokens.data_ptr(),
+                           targets.data_ptr(), loss.data_ptr(), grads.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream_ptr(stream))
+    _check("gpt_fwd_bwd", st)
+
+
+def fwd(cfg, params, tokens, targets, loss, workspace, stream=None):
+    st = lib().gpt_fwd(ctypes.byref(cfg), params.data_ptr(), tokens.data_ptr(),
+                       targets.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    _check("gpt_fwd", st)
+
+
+def profile_begin(site_prefix: str):
+    _check("gpt_profile_begin", lib().gpt_profile_begin(site_prefix.encode()))
+
+
+def profile_end():
+    """(summed kernel milliseconds, launches) since profile_begin."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check("gpt_profile_end", lib().gpt_profile_end(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+class Step:
+    """Device buffers for repeated calls on one workload: params, grads,
+    tokens, targets, loss and the workspace, allocated once with torch."""
+
+    def __init__(self, w, params_np, tokens_np, targets_np, flags=0, device="cuda"):
+        import torch
+        self.cfg = make_config(w, flags)
+        _check("gpt_config_validate", validate(self.cfg))
+        self.n_tensors, self.n_elems = param_count(self.cfg)
+        assert params_np.size == self.n_elems
+        self.params = torch.from_numpy(params_np).to(device)
+        self.grads = torch.empty(self.n_elems, dtype=torch.float32, device=device)
+        self.tokens = torch.from_numpy(tokens_np).to(device).contiguous()
+        self.targets = torch.from_numpy(targets_np).to(device).contiguous()
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self.ws_bytes = workspace_size(self.cfg)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def run(self, stream=None):
+        fwd_bwd(self.cfg, self.params, self.tokens, self.targets, self.loss, self.grads,
+                self.workspace, stream)
+
+    def forward(self, stream=None):
+        fwd(self.cfg, self.params, self.tokens, self.targets, self.loss, self.workspace, stream)
+
+    def region(self, name, layer=0):
+        """A saved forward tensor inside the workspace (see gpt_workspace_region)."""
+        import torch
+        off, nbytes = workspace_region(self.cfg, name, layer)
+        return self.workspace[off:off + nbytes]

@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 kernels: element types, conversions,
+// wavefront (64-lane) reductions and the MFMA fragment operations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace gk {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Sum / max over the 64 lanes of a wavefront; every lane gets the result.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// Sum over the 32 lanes of each half-wavefront (lanes 0-31 and 32-63).
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA fragments. A 32x32 output tile is accumulated over 16-wide slices of
+// the contraction index. For one slice every lane holds 8 operand elements:
+// lane l supplies row (l % 32) of the 32-row operand and the 8 contraction
+// slots 8*(l/32) .. 8*(l/32)+7. The accumulator element e of lane l is
+// output row 8*(e/4) + 4*(l/32) + (e%4), column l % 32.
+//
+// bf16: one v_mfma_f32_32x32x16_bf16 per slice.
+// fp32: eight v_mfma_f32_32x32x2_f32; call j pairs slot j of both lane
+//       halves, so the 16 slots are summed exactly as in the bf16 case.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ __forceinline__ void frag_load(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void frag_load(Frag<float>& f, const float* p) {
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void frag_set(Frag<bf16>& f, int j, float x) { f.v[j] = static_cast<bf16>(x); }
+__device__ __forceinline__ void frag_set(Frag<float>& f, int j, float x) {
+  if (j < 4) f.lo[j] = x; else f.hi[j - 4] = x;
+}
+__device__ __forceinline__ void frag_zero(Frag<bf16>& f) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = static_cast<bf16>(0.0f);
+}
+__device__ __forceinline__ void frag_zero(Frag<float>& f) {
+  f.lo = f32x4{0, 0, 0, 0};
+  f.hi = f32x4{0, 0, 0, 0};
+}
+
+__device__ __forceinline__ void mfma(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[j], b.lo[j], acc, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[j], b.hi[j], acc, 0, 0, 0);
+}
+
+// Output row (within a 32x32 tile) of accumulator element e for lane l.
+__device__ __forceinline__ int acc_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
+
+}  // namespace gk

@@ -1,0 +1,570 @@
+// Host side of the GPT step library: config validation, the canonical
+// parameter layout, the workspace plan, the launch sequence of one forward +
+// backward pass, and the extern "C" entry points declared in gpt_step.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "internal.h"
+
+namespace gpt {
+
+static thread_local char g_err[512] = "";
+
+static int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+// ---------------------------------------------------------------- profiling
+// When enabled, every launch whose site name starts with the chosen prefix is
+// bracketed by two HIP events recorded on the launch stream. Events come from
+// a pool that grows on demand and is reused across calls.
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::string prefix;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+};
+static Profiler g_prof;
+
+template <class Fn>
+static void site(const char* name, hipStream_t s, Fn&& fn) {
+  if (g_prof.on && strncmp(name, g_prof.prefix.c_str(), g_prof.prefix.size()) == 0) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    while (g_prof.pool.size() < g_prof.used + 2) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) {
+        fn();
+        return;
+      }
+      g_prof.pool.push_back(e);
+    }
+    hipEvent_t a = g_prof.pool[g_prof.used], b = g_prof.pool[g_prof.used + 1];
+    g_prof.used += 2;
+    (void)hipEventRecord(a, s);
+    fn();
+    (void)hipEventRecord(b, s);
+  } else {
+    fn();
+  }
+}
+
+// Sliding-window pattern: three short-window layers then one full layer,
+// tiled over depth, with the last layer always full ("Nanochat在nanoGPT之上
+// 的新增功能", notes on the sliding window).
+bool layer_full(int l, int L) { return (l % 4 == 3) || (l == L - 1); }
+// Value embeddings on every other layer, the last one included (same page,
+// notes on value residuals).
+bool layer_ve(int l, int L) { return (l % 2) == ((L - 1) % 2); }
+
+Dims make_dims(const gpt_config& c) {
+  Dims d{};
+  d.L = c.n_layer;
+  d.C = c.n_embd;
+  d.H = c.n_head;
+  d.Hk = c.n_kv_head;
+  d.D = c.head_dim;
+  d.F = c.mlp_hidden;
+  d.V = c.vocab;
+  d.T = c.seq_len;
+  d.B = c.batch;
+  d.W = c.short_window;
+  d.N = (int64_t)c.batch * c.seq_len;
+  d.Cq = d.H * d.D;
+  d.Ckv = d.Hk * d.D;
+  d.Qkv = d.Cq + 2 * d.Ckv;
+  d.G = d.Hk > 0 ? d.H / d.Hk : 0;
+  d.bf16 = c.compute_dtype == GPT_DT_BF16;
+  d.act_bytes = d.bf16 ? 2 : 4;
+  d.theta = c.rope_theta;
+  d.eps = c.norm_eps;
+  d.cap = c.softcap;
+  d.accumulate = (c.flags & GPT_F_ACCUMULATE) != 0;
+  return d;
+}
+
+static int validate(const gpt_config* c) {
+  if (!c) return fail(GPT_E_NULLPTR, "config is NULL");
+  if (c->abi_version != GPT_ABI_VERSION)
+    return fail(GPT_E_INVAL, "abi_version %d != %d", c->abi_version, GPT_ABI_VERSION);
+  if (c->n_layer < 1 || c->n_layer > 256) return fail(GPT_E_INVAL, "n_layer %d not in [1, 256]", c->n_layer);
+  if (c->n_embd < 64 || c->n_embd > 2048 || c->n_embd % 64)
+    return fail(GPT_E_INVAL, "n_embd %d: need a multiple of 64 in [64, 2048]", c->n_embd);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(GPT_E_INVAL, "head_dim %d: need 64 or 128", c->head_dim);
+  if (c->n_head < 1 || c->n_kv_head < 1 || c->n_kv_head > 16 || c->n_head % c->n_kv_head)
+    return fail(GPT_E_INVAL, "n_head %d / n_kv_head %d: need n_kv_head in [1, 16] dividing n_head",
+                c->n_head, c->n_kv_head);
+  if ((int64_t)c->n_head * c->head_dim > 16384) return fail(GPT_E_INVAL, "n_head * head_dim too large");
+  if (c->mlp_hidden < 64 || c->mlp_hidden % 64 || c->mlp_hidden > 65536)
+    return fail(GPT_E_INVAL, "mlp_hidden %d: need a multiple of 64 in [64, 65536]", c->mlp_hidden);
+  if (c->vocab < 64 || c->vocab % 64 || c->vocab > (1 << 24))
+    return fail(GPT_E_INVAL, "vocab %d: need a multiple of 64 in [64, 2^24]", c->vocab);
+  if (c->seq_len < 1 || c->batch < 1) return fail(GPT_E_INVAL, "seq_len and batch must be >= 1");
+  const int64_t N = (int64_t)c->seq_len * c->batch;
+  if (N > (1 << 22)) return fail(GPT_E_INVAL, "batch * seq_len = %lld exceeds 2^22", (long long)N);
+  if (c->short_window < 0) return fail(GPT_E_INVAL, "short_window %d < 0", c->short_window);
+  if (c->compute_dtype != GPT_DT_F32 && c->compute_dtype != GPT_DT_BF16)
+    return fail(GPT_E_INVAL, "compute_dtype %d unknown", c->compute_dtype);
+  if (c->fp8_linears != 0 && c->fp8_linears != 1) return fail(GPT_E_INVAL, "fp8_linears must be 0 or 1");
+  if (c->flags & ~GPT_F_ACCUMULATE) return fail(GPT_E_INVAL, "unknown flag bits 0x%x", c->flags);
+  if (!(std::isfinite(c->rope_theta) && c->rope_theta > 1.0f))
+    return fail(GPT_E_INVAL, "rope_theta must be finite and > 1");
+  if (!(std::isfinite(c->norm_eps) && c->norm_eps > 0.0f)) return fail(GPT_E_INVAL, "norm_eps must be > 0");
+  if (!(std::isfinite(c->softcap) && c->softcap > 0.0f)) return fail(GPT_E_INVAL, "softcap must be > 0");
+  if (c->fp8_linears) return fail(GPT_E_UNSUPPORTED, "fp8 linears are not built into this library");
+  return GPT_OK;
+}
+
+std::vector<TensorInfo> param_layout(const gpt_config& c) {
+  const Dims d = make_dims(c);
+  std::vector<TensorInfo> v;
+  int64_t o = 0;
+  auto add = [&](const std::string& name, int64_t r, int64_t cc) {
+    v.push_back({name, o, r, cc});
+    o += r * cc;
+  };
+  add("wte", d.V, d.C);
+  for (int l = 0; l < d.L; ++l) {
+    const std::string p = "l" + std::to_string(l) + ".";
+    add(p + "q", d.Cq, d.C);
+    add(p + "k", d.Ckv, d.C);
+    add(p + "v", d.Ckv, d.C);
+    add(p + "o", d.C, d.Cq);
+    add(p + "fc", d.F, d.C);
+    add(p + "mp", d.C, d.F);
+    if (layer_ve(l, d.L)) {
+      add(p + "ve", d.V, d.Ckv);
+      add(p + "veg", d.Hk, d.C);
+    }
+  }
+  add("lm_head", d.V, d.C);
+  add("resid_lambdas", d.L, 1);
+  add("x0_lambdas", d.L, 1);
+  return v;
+}
+
+static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan make_plan(const Dims& d) {
+  Plan p{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o += al(bytes);
+    return r;
+  };
+  const size_t N = (size_t)d.N, A = (size_t)d.act_bytes;
+  int64_t n_elems = 0;
+  {
+    // total parameter count, same walk as param_layout
+    n_elems = (int64_t)d.V * d.C * 2 + 2 * d.L;
+    for (int l = 0; l < d.L; ++l) {
+      n_elems += (int64_t)d.Qkv * d.C + (int64_t)d.C * d.Cq + 2 * (int64_t)d.F * d.C;
+      if (layer_ve(l, d.L)) n_elems += (int64_t)d.V * d.Ckv + (int64_t)d.Hk * d.C;
+    }
+  }
+  p.wc = take(d.bf16 ? (size_t)n_elems * 2 : 0);
+  p.rope = take((size_t)d.T * d.D * 4);
+  p.x = take((size_t)(d.L + 1) * N * d.C * 4);
+  p.xin = take(N * d.C * 4);
+  p.xmid = take(N * d.C * 4);
+  // per-layer saved activations
+  size_t lo = 0;
+  auto ltake = [&](size_t bytes) {
+    const size_t r = lo;
+    lo += al(bytes);
+    return r;
+  };
+  p.l_xn = ltake(N * d.C * A);
+  p.l_r1 = ltake(N * 4);
+  p.l_qkv = ltake(N * d.Qkv * A);
+  p.l_rqk = ltake(N * (d.H + d.Hk) * 4);
+  p.l_a = ltake(N * d.Hk * 4);
+  p.l_attn = ltake(N * d.Cq * A);
+  p.l_lse = ltake(N * d.H * 4);
+  p.l_xn2 = ltake(N * d.C * A);
+  p.l_r2 = ltake(N * 4);
+  p.l_u = ltake(N * d.F * A);
+  p.layer_bytes = lo;
+  p.layers = take(lo * d.L);
+  p.xf = take(N * d.C * A);
+  p.rf = take(N * 4);
+  p.logits = take(N * d.V * A);
+  p.rowsum = take(N * 4);
+  p.scalars = take(256);
+  p.gx = take(N * d.C * 4);
+  p.gxc = take(N * d.C * A);
+  p.gx0 = take(N * d.C * 4);
+  p.gu = take(N * d.F * A);
+  p.gtmp = take(N * d.C * 4);
+  p.gO = take(N * d.Cq * A);
+  p.gqkv = take(N * d.Qkv * A);
+  p.delta = take(N * d.H * 4);
+  p.ga = take(N * d.Hk * 4);
+  p.lam_blocks = (int)((d.N + 3) / 4);
+  p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
+  p.veg_splits = 64;
+  p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
+  p.total = o;
+  return p;
+}
+
+struct Offs {
+  int64_t wte, lm, lr, l0;
+  std::vector<int64_t> q, o, fc, mp, ve, veg;
+};
+
+static Offs offsets(const gpt_config& c) {
+  Offs f;
+  const int L = c.n_layer;
+  f.q.assign(L, -1);
+  f.o.assign(L, -1);
+  f.fc.assign(L, -1);
+  f.mp.assign(L, -1);
+  f.ve.assign(L, -1);
+  f.veg.assign(L, -1);
+  for (const auto& t : param_layout(c)) {
+    const std::string& n = t.name;
+    if (n == "wte") f.wte = t.offset;
+    else if (n == "lm_head") f.lm = t.offset;
+    else if (n == "resid_lambdas") f.lr = t.offset;
+    else if (n == "x0_lambdas") f.l0 = t.offset;
+    else {
+      const size_t dot = n.find('.');
+      const int l = std::stoi(n.substr(1, dot - 1));
+      const std::string k = n.substr(dot + 1);
+      if (k == "q") f.q[l] = t.offset;
+      else if (k == "o") f.o[l] = t.offset;
+      else if (k == "fc") f.fc[l] = t.offset;
+      else if (k == "mp") f.mp[l] = t.offset;
+      else if (k == "ve") f.ve[l] = t.offset;
+      else if (k == "veg") f.veg[l] = t.offset;
+    }
+  }
+  return f;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int run(const gpt_config* cfg, const float* params, const int32_t* tokens,
+               const int32_t* targets, float* loss, float* grads, void* workspace,
+               size_t workspace_bytes, void* stream, bool backward) {
+  g_err[0] = 0;
+  int st = validate(cfg);
+  if (st) return st;
+  if (!params || !tokens || !targets || !loss || !workspace || (backward && !grads))
+    return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+  if (!aligned(params, 256) || !aligned(workspace, 256) || (backward && !aligned(grads, 256)) ||
+      !aligned(tokens, 4) || !aligned(targets, 4) || !aligned(loss, 4))
+    return fail(GPT_E_ALIGN, "params/grads/workspace need 256-byte alignment, tokens/targets/loss 4");
+  const Dims d = make_dims(*cfg);
+  const Plan P = make_plan(d);
+  if (workspace_bytes < P.total)
+    return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, P.total);
+  const Offs F = offsets(*cfg);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+
+  char* W = static_cast<char*>(workspace);
+  const size_t A = (size_t)d.act_bytes;
+  // compute-dtype weights: a mirror of params with the same element offsets
+  const char* wc = d.bf16 ? W + P.wc : reinterpret_cast<const char*>(params);
+  auto wmat = [&](int64_t off) { return static_cast<const void*>(wc + off * A); };
+  if (d.bf16) {
+    std::vector<CastSeg> segs;
+    for (int l = 0; l < d.L; ++l) {
+      segs.push_back({F.q[l], F.mp[l] + (int64_t)d.C * d.F - F.q[l]});  // q k v o fc mp
+      if (F.veg[l] >= 0) segs.push_back({F.veg[l], (int64_t)d.Hk * d.C});
+    }
+    segs.push_back({F.lm, (int64_t)d.V * d.C});
+    launch_cast(params, W + P.wc, segs, s);
+  }
+  float* cs = reinterpret_cast<float*>(W + P.rope);
+  launch_rope_table(cs, d.T, d.D, d.theta, s);
+
+  const size_t xstride = (size_t)d.N * d.C;
+  auto X = [&](int l) { return reinterpret_cast<float*>(W + P.x) + (size_t)l * xstride; };
+  auto LY = [&](int l, size_t off) { return W + P.layers + (size_t)l * P.layer_bytes + off; };
+  float* xin = reinterpret_cast<float*>(W + P.xin);
+  float* xmid = reinterpret_cast<float*>(W + P.xmid);
+  const int64_t N = d.N;
+
+  site("embed.fwd", s, [&] { launch_embed(params + F.wte, tokens, X(0), N, d.C, s); });
+  for (int l = 0; l < d.L; ++l) {
+    const bool ve = layer_ve(l, d.L), full = layer_full(l, d.L);
+    void* xn = LY(l, P.l_xn);
+    float* r1 = reinterpret_cast<float*>(LY(l, P.l_r1));
+    void* qkv = LY(l, P.l_qkv);
+    float* rqk = reinterpret_cast<float*>(LY(l, P.l_rqk));
+    float* a = reinterpret_cast<float*>(LY(l, P.l_a));
+    void* att = LY(l, P.l_attn);
+    float* lse = reinterpret_cast<float*>(LY(l, P.l_lse));
+    void* xn2 = LY(l, P.l_xn2);
+    float* r2 = reinterpret_cast<float*>(LY(l, P.l_r2));
+    void* u = LY(l, P.l_u);
+    launch_mix_norm(d, X(l), X(0), params + F.lr + l, params + F.l0 + l, xin, xn, r1,
+                    ve ? params + F.veg[l] : nullptr, ve ? a : nullptr, s);
+    site("gemm.qkv.fwd", s, [&] { gemm_nt_store(d, N, d.Qkv, d.C, xn, wmat(F.q[l]), qkv, s); });
+    site("rope.fwd", s, [&] { launch_rope_qk_ve_fwd(d, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr, tokens, s); });
+    site("attn.fwd", s, [&] { launch_attn_fwd(d, full, qkv, att, lse, s); });
+    site("gemm.o.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.Cq, att, wmat(F.o[l]), xin, xmid, false, s); });
+    launch_mix_norm(d, xmid, nullptr, nullptr, nullptr, nullptr, xn2, r2, nullptr, nullptr, s);
+    site("gemm.fc.fwd", s, [&] { gemm_nt_store(d, N, d.F, d.C, xn2, wmat(F.fc[l]), u, s); });
+    site("gemm.mp.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.F, u, wmat(F.mp[l]), xmid, X(l + 1), true, s); });
+  }
+  void* xf = W + P.xf;
+  float* rf = reinterpret_cast<float*>(W + P.rf);
+  void* logits = W + P.logits;
+  float* rowsum = reinterpret_cast<float*>(W + P.rowsum);
+  float* scalars = reinterpret_cast<float*>(W + P.scalars);
+  launch_mix_norm(d, X(d.L), nullptr, nullptr, nullptr, nullptr, xf, rf, nullptr, nullptr, s);
+  launch_zero(rowsum, N, s);
+  site("gemm.lm.fwd", s, [&] { gemm_nt_softcap(d, N, d.V, d.C, xf, wmat(F.lm), logits, rowsum, s); });
+  site("loss", s, [&] { launch_loss(d, logits, targets, rowsum, scalars, loss, s); });  // rowsum -> 1 / rowsum
+
+  if (backward) {
+    const bool acc = d.accumulate;
+    if (!acc) {
+      launch_zero(grads + F.wte, (int64_t)d.V * d.C, s);
+      for (int l = 0; l < d.L; ++l)
+        if (F.ve[l] >= 0) launch_zero(grads + F.ve[l], (int64_t)d.V * d.Ckv, s);
+    }
+    float* gx = reinterpret_cast<float*>(W + P.gx);
+    void* gxc = d.bf16 ? static_cast<void*>(W + P.gxc) : static_cast<void*>(gx);
+    float* gx0 = reinterpret_cast<float*>(W + P.gx0);
+    void* gu = W + P.gu;
+    float* gtmp = reinterpret_cast<float*>(W + P.gtmp);
+    void* gO = W + P.gO;
+    void* gqkv = W + P.gqkv;
+    float* delta = reinterpret_cast<float*>(W + P.delta);
+    float* ga = reinterpret_cast<float*>(W + P.ga);
+    float* lam_part = reinterpret_cast<float*>(W + P.lam_part);
+    float* veg_part = reinterpret_cast<float*>(W + P.veg_part);
+
+    site("gemm.lm.dgrad", s, [&] { gemm_nn_ce(d, N, d.C, d.V, logits, wmat(F.lm), rowsum, targets, scalars, gtmp, s); });
+    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad_ce(d, d.V, d.C, N, logits, xf, rowsum, targets, scalars, grads + F.lm, acc, s); });
+    NormBwdArgs nb{};
+    nb.mode = NB_FINAL;
+    nb.gin = gtmp;
+    nb.y = xf;
+    nb.r = rf;
+    nb.gx = gx;
+    nb.gxc = d.bf16 ? gxc : nullptr;
+    launch_norm_bwd(d, nb, s);
+    for (int l = d.L - 1; l >= 0; --l) {
+      const bool ve = layer_ve(l, d.L), full = layer_full(l, d.L);
+      const void* xn = LY(l, P.l_xn);
+      const float* r1 = reinterpret_cast<const float*>(LY(l, P.l_r1));
+      const void* qkv = LY(l, P.l_qkv);
+      const float* rqk = reinterpret_cast<const float*>(LY(l, P.l_rqk));
+      const float* a = reinterpret_cast<const float*>(LY(l, P.l_a));
+      const void* att = LY(l, P.l_attn);
+      const float* lse = reinterpret_cast<const float*>(LY(l, P.l_lse));
+      const void* xn2 = LY(l, P.l_xn2);
+      const float* r2 = reinterpret_cast<const float*>(LY(l, P.l_r2));
+      const void* u = LY(l, P.l_u);
+      // MLP
+      site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s); });
+      site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, true, s); });
+      site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s); });
+      site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, false, s); });
+      nb = NormBwdArgs{};
+      nb.mode = NB_NORM2;
+      nb.gin = gtmp;
+      nb.y = xn2;
+      nb.r = r2;
+      nb.gx = gx;
+      nb.gxc = d.bf16 ? gxc : nullptr;
+      launch_norm_bwd(d, nb, s);
+      // attention
+      site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s); });
+      site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, false, s); });
+      site("attn.delta", s, [&] { launch_attn_delta(d, gO, att, delta, s); });
+      site("attn.bwd", s, [&] { launch_attn_bwd(d, full, qkv, gO, lse, delta, gqkv, s); });
+      launch_rope_qk_ve_bwd(d, gqkv, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr,
+                            ve ? grads + F.ve[l] : nullptr, ga, tokens, s);
+      site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s); });
+      site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, false, s); });
+      if (ve) launch_veg_wgrad(d, ga, xn, veg_part, P.veg_splits, grads + F.veg[l], s);
+      nb = NormBwdArgs{};
+      nb.mode = NB_NORM1;
+      nb.gin = gtmp;
+      nb.y = xn;
+      nb.r = r1;
+      nb.gx = gx;
+      nb.gxc = d.bf16 ? gxc : nullptr;
+      nb.ga = ve ? ga : nullptr;
+      nb.wg = ve ? params + F.veg[l] : nullptr;
+      nb.x = X(l);
+      nb.x0 = X(0);
+      nb.lam_r = params + F.lr + l;
+      nb.lam_0 = params + F.l0 + l;
+      nb.gx0 = gx0;
+      nb.gx0_first = l == d.L - 1;
+      nb.last_layer0 = l == 0;
+      nb.lam_part = lam_part + (size_t)l * P.lam_blocks * 2;
+      launch_norm_bwd(d, nb, s);
+    }
+    site("embed.bwd", s, [&] { launch_embed_bwd(gx0, tokens, grads + F.wte, N, d.C, s); });
+    for (int l = 0; l < d.L; ++l)
+      launch_lambda_finalize(d, lam_part + (size_t)l * P.lam_blocks * 2, P.lam_blocks,
+                             grads + F.lr + l, grads + F.l0 + l, s);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
+  return GPT_OK;
+}
+
+}  // namespace gpt
+
+using namespace gpt;
+
+extern "C" {
+
+int gpt_abi_version(void) { return GPT_ABI_VERSION; }
+
+int gpt_config_validate(const gpt_config* cfg) {
+  g_err[0] = 0;
+  return validate(cfg);
+}
+
+int gpt_param_count(const gpt_config* cfg, int64_t* n_tensors, int64_t* n_elems) {
+  g_err[0] = 0;
+  int st = validate(cfg);
+  if (st && st != GPT_E_UNSUPPORTED) return st;
+  if (!n_tensors || !n_elems) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  const auto v = param_layout(*cfg);
+  *n_tensors = (int64_t)v.size();
+  *n_elems = v.back().offset + v.back().rows * v.back().cols;
+  return GPT_OK;
+}
+
+int gpt_param_info(const gpt_config* cfg, int64_t i, char name[64], int64_t* offset,
+                   int64_t* rows, int64_t* cols) {
+  g_err[0] = 0;
+  int st = validate(cfg);
+  if (st && st != GPT_E_UNSUPPORTED) return st;
+  if (!name || !offset || !rows || !cols) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  const auto v = param_layout(*cfg);
+  if (i < 0 || i >= (int64_t)v.size()) return fail(GPT_E_INVAL, "tensor index %lld out of range", (long long)i);
+  snprintf(name, 64, "%s", v[i].name.c_str());
+  *offset = v[i].offset;
+  *rows = v[i].rows;
+  *cols = v[i].cols;
+  return GPT_OK;
+}
+
+int gpt_layer_info(const gpt_config* cfg, int32_t l, int32_t* is_full, int32_t* has_ve) {
+  g_err[0] = 0;
+  int st = validate(cfg);
+  if (st && st != GPT_E_UNSUPPORTED) return st;
+  if (!is_full || !has_ve) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  if (l < 0 || l >= cfg->n_layer) return fail(GPT_E_INVAL, "layer %d out of range", l);
+  *is_full = layer_full(l, cfg->n_layer) ? 1 : 0;
+  *has_ve = layer_ve(l, cfg->n_layer) ? 1 : 0;
+  return GPT_OK;
+}
+
+int gpt_workspace_size(const gpt_config* cfg, size_t* bytes) {
+  g_err[0] = 0;
+  int st = validate(cfg);
+  if (st) return st;
+  if (!bytes) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  *bytes = make_plan(make_dims(*cfg)).total;
+  return GPT_OK;
+}
+
+int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer, size_t* offset,
+                         size_t* bytes) {
+  g_err[0] = 0;
+  int st = validate(cfg);
+  if (st) return st;
+  if (!name || !offset || !bytes) return fail(GPT_E_NULLPTR, "pointer is NULL");
+  const Dims d = make_dims(*cfg);
+  const Plan P = make_plan(d);
+  const size_t N = (size_t)d.N, A = (size_t)d.act_bytes;
+  const std::string n(name);
+  if (n == "x") {
+    if (layer < 0 || layer > d.L) return fail(GPT_E_INVAL, "layer out of range");
+    *offset = P.x + (size_t)layer * N * d.C * 4;
+    *bytes = N * d.C * 4;
+    return GPT_OK;
+  }
+  if (n == "xf") { *offset = P.xf; *bytes = N * d.C * A; return GPT_OK; }
+  if (n == "logits") { *offset = P.logits; *bytes = N * d.V * A; return GPT_OK; }
+  if (layer < 0 || layer >= d.L) return fail(GPT_E_INVAL, "layer out of range");
+  const size_t base = P.layers + (size_t)layer * P.layer_bytes;
+  if (n == "xn") { *offset = base + P.l_xn; *bytes = N * d.C * A; return GPT_OK; }
+  if (n == "qkv") { *offset = base + P.l_qkv; *bytes = N * d.Qkv * A; return GPT_OK; }
+  if (n == "attn") { *offset = base + P.l_attn; *bytes = N * d.Cq * A; return GPT_OK; }
+  if (n == "xn2") { *offset = base + P.l_xn2; *bytes = N * d.C * A; return GPT_OK; }
+  if (n == "u") { *offset = base + P.l_u; *bytes = N * d.F * A; return GPT_OK; }
+  return fail(GPT_E_INVAL, "unknown region '%s'", name);
+}
+
+int gpt_fwd_bwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
+                const int32_t* targets, float* loss, float* grads, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return run(cfg, params, tokens, targets, loss, grads, workspace, workspace_bytes, stream, true);
+}
+
+int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
+            const int32_t* targets, float* loss, void* workspace, size_t workspace_bytes,
+            void* stream) {
+  return run(cfg, params, tokens, targets, loss, nullptr, workspace, workspace_bytes, stream, false);
+}
+
+const char* gpt_status_string(int status) {
+  switch (status) {
+    case GPT_OK: return "ok";
+    case GPT_E_INVAL: return "invalid argument";
+    case GPT_E_NULLPTR: return "null pointer";
+    case GPT_E_ALIGN: return "misaligned pointer";
+    case GPT_E_WORKSPACE: return "workspace too small";
+    case GPT_E_UNSUPPORTED: return "unsupported configuration";
+    case GPT_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* gpt_last_error(void) { return g_err; }
+
+int gpt_profile_begin(const char* site_prefix) {
+  g_err[0] = 0;
+  if (!site_prefix) return fail(GPT_E_NULLPTR, "site_prefix is NULL");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.prefix = site_prefix;
+  g_prof.used = 0;
+  g_prof.on = true;
+  return GPT_OK;
+}
+
+int gpt_profile_end(double* total_ms, int64_t* launches) {
+  g_err[0] = 0;
+  if (!total_ms || !launches) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  double ms = 0.0;
+  for (size_t i = 0; i + 1 < g_prof.used; i += 2) {
+    if (hipEventSynchronize(g_prof.pool[i + 1]) != hipSuccess)
+      return fail(GPT_E_HIP, "hipEventSynchronize failed");
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, g_prof.pool[i], g_prof.pool[i + 1]) != hipSuccess)
+      return fail(GPT_E_HIP, "hipEventElapsedTime failed");
+    ms += t;
+  }
+  *total_ms = ms;
+  *launches = (int64_t)(g_prof.used / 2);
+  g_prof.used = 0;
+  return GPT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Internal interfaces of the gfx950 GPT step library: derived sizes, the
+// parameter layout, the workspace plan and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "gpt_step.h"
+
+namespace gpt {
+
+struct Dims {
+  int L, C, H, Hk, D, F, V, T, B, W;
+  int64_t N;        // tokens per call = B * T
+  int Cq, Ckv, Qkv; // H*D, Hk*D, Cq + 2*Ckv
+  int G;            // H / Hk
+  bool bf16;        // compute dtype
+  int act_bytes;    // 2 (bf16) or 4 (fp32)
+  float theta, eps, cap;
+  bool accumulate;
+};
+
+Dims make_dims(const gpt_config& c);
+bool layer_full(int l, int L);
+bool layer_ve(int l, int L);
+
+struct TensorInfo {
+  std::string name;
+  int64_t offset, rows, cols;
+};
+std::vector<TensorInfo> param_layout(const gpt_config& c);
+
+// Workspace plan: byte offsets of every region (all 256-byte aligned).
+struct Plan {
+  size_t wc;            // compute-dtype mirror of params (bf16 only)
+  size_t rope;          // fp32 cos [T][D/2], sin [T][D/2]
+  size_t x;             // fp32 [(L+1)][N][C] residual stream per layer boundary
+  size_t xin, xmid;     // fp32 [N][C] scratch
+  // per layer, stride `layer_bytes`, starting at `layers`
+  size_t layers, layer_bytes;
+  size_t l_xn, l_r1, l_qkv, l_rqk, l_a, l_attn, l_lse, l_xn2, l_r2, l_u;
+  size_t xf, rf, logits, rowsum, scalars;
+  size_t gx, gxc, gx0, gu, gtmp, gO, gqkv, delta, ga, lam_part, veg_part;
+  int lam_blocks, veg_splits;
+  size_t total;
+};
+Plan make_plan(const Dims& d);
+
+// ------------------------------------------------------------ launchers
+// `act` pointers hold compute-dtype elements (bf16 or fp32 per d.bf16).
+
+struct CastSeg {
+  int64_t off, n;
+};
+void launch_cast(const float* src, void* dst, const std::vector<CastSeg>& segs, hipStream_t s);
+void launch_zero(float* p, int64_t n, hipStream_t s);
+void launch_rope_table(float* cs, int T, int D, float theta, hipStream_t s);
+void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C, hipStream_t s);
+
+// rows of x (fp32 [N][C]): if x0 != nullptr, xin = lr*x + l0*x0 (written to
+// xin_out if non-null) else xin = x; y = rms(xin) (act), r (fp32 [N]).
+// If wg != nullptr, a[n][j] = <y[n], wg[j]> for j < hk (fp32 [N][hk]).
+void launch_mix_norm(const Dims& d, const float* x, const float* x0, const float* lam_r,
+                     const float* lam_0, float* xin_out, void* y, float* r,
+                     const float* wg, float* a, hipStream_t s);
+
+void launch_rope_qk_ve_fwd(const Dims& d, void* qkv, float* rqk, const float* cs,
+                           const float* a, const float* ve_table, const int32_t* tok,
+                           hipStream_t s);
+void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const float* rqk,
+                           const float* cs, const float* a, const float* ve_table,
+                           float* gve_table, float* ga, const int32_t* tok, hipStream_t s);
+
+void launch_attn_fwd(const Dims& d, bool full, const void* qkv, void* out, float* lse,
+                     hipStream_t s);
+void launch_attn_delta(const Dims& d, const void* gO, const void* O, float* delta, hipStream_t s);
+void launch_attn_bwd(const Dims& d, bool full, const void* qkv, const void* gO,
+                     const float* lse, const float* delta, void* gqkv, hipStream_t s);
+
+// Norm backward modes.
+enum NormBwdMode { NB_FINAL = 0, NB_NORM2 = 1, NB_NORM1 = 2 };
+struct NormBwdArgs {
+  int mode;
+  const float* gin;     // fp32 [N][C] gradient w.r.t. the norm output
+  const void* y;        // act [N][C] norm output
+  const float* r;       // fp32 [N]
+  float* gx;            // fp32 [N][C] residual gradient (in/out)
+  void* gxc;            // act [N][C] copy of the new gx (may be null)
+  // NB_NORM1 only
+  const float* ga;      // fp32 [N][Hk] or null
+  const float* wg;      // fp32 [Hk][C] or null
+  const float* x;       // fp32 [N][C] block input
+  const float* x0;      // fp32 [N][C]
+  const float* lam_r;   // device scalar
+  const float* lam_0;
+  float* gx0;           // fp32 [N][C]
+  int gx0_first;        // gx0 = ... instead of +=
+  int last_layer0;      // layer 0: add the final gx into gx0
+  float* lam_part;      // fp32 [blocks][2]
+};
+void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s);
+
+void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
+                            float* g_l0, hipStream_t s);
+void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* part,
+                      int splits, float* gwg, hipStream_t s);
+void launch_loss(const Dims& d, const void* logits, const int32_t* tgt, float* rowsum,
+                 float* scalars, float* loss, hipStream_t s);
+void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t N, int C,
+                      hipStream_t s);
+
+// ------------------------------------------------------------ GEMMs
+// Shapes: C[M][N] = sum_k A(m,k) B(n,k).
+// "nt": A [M][K], B [N][K] (both contraction-contiguous).
+// "nn": A [M][K], B [K][N].
+// "tn": A [K][M], B [K][N] (weight gradients: K = tokens).
+void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                   void* C, hipStream_t s);
+void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                   const float* R, float* C, bool relu2_a, hipStream_t s);
+void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                     void* C, float* rowsum, hipStream_t s);
+void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                   void* C, hipStream_t s);
+void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                 float* C, hipStream_t s);
+void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                      const void* U, void* C, hipStream_t s);
+// A = softcap-CE logit gradient computed on load from logits [M][K].
+void gemm_nn_ce(const Dims& d, int64_t M, int N, int K, const void* logits, const void* B,
+                const float* inv_rowsum, const int32_t* tgt, const float* inv_nvalid,
+                float* C, hipStream_t s);
+// Weight gradients. relu2_b: B = relu(B)^2 on load. ce_a: A from logits.
+void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
+                   float* C, bool accumulate, bool relu2_b, hipStream_t s);
+void gemm_tn_wgrad_ce(const Dims& d, int M, int N, int64_t K, const void* logits,
+                      const void* B, const float* inv_rowsum, const int32_t* tgt,
+                      const float* inv_nvalid, float* C, bool accumulate, hipStream_t s);
+
+}  // namespace gpt

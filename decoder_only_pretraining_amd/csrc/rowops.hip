@@ -1,0 +1,562 @@
+// Memory-bound kernels of the GPT step: weight cast, embedding gather and
+// scatter, residual mix + RMSNorm (forward and backward), RoPE + QK-norm +
+// value-embedding gate (forward and backward), softcap cross-entropy loss,
+// and the small deterministic reductions for the lambda and gate weights.
+//
+// Row kernels give one 64-lane wavefront to one row of n_embd features and
+// reduce with cross-lane shuffles; feature loads are 16-byte vectors.
+#include "device_common.h"
+#include "internal.h"
+
+namespace gk {
+
+constexpr int kMaxC4 = 8;  // n_embd <= 64 lanes * 8 float4 = 2048
+
+// ------------------------------------------------------------ cast / zero
+struct CastTable {
+  gpt::CastSeg seg[128];
+  int nseg;
+};
+
+__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src,
+                                                   bf16* __restrict__ dst, CastTable t) {
+  const gpt::CastSeg sg = t.seg[blockIdx.y];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < sg.n; i += stride) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src + sg.off + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(src + sg.off + i + 4);
+    bf16x8 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = static_cast<bf16>(a[j]);
+      o[j + 4] = static_cast<bf16>(b[j]);
+    }
+    *reinterpret_cast<bf16x8*>(dst + sg.off + i) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n4 = n / 4;
+  for (int64_t j = i; j < n4; j += stride) reinterpret_cast<f32x4*>(p)[j] = f32x4{0, 0, 0, 0};
+  for (int64_t j = n4 * 4 + i; j < n; j += stride) p[j] = 0.0f;
+}
+
+// cos / sin of t * theta^(-2i/D), evaluated in double precision.
+__global__ void rope_table_kernel(float* __restrict__ cs, int T, int D, double theta) {
+  const int h = D / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * h) return;
+  const int t = (int)(idx / h), i = (int)(idx % h);
+  const double inv = pow(theta, -2.0 * i / (double)D);
+  const double phi = (double)t * inv;
+  cs[idx] = (float)cos(phi);
+  cs[(int64_t)T * h + idx] = (float)sin(phi);
+}
+
+// ------------------------------------------------------------ embedding
+__global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wte,
+                                                    const int32_t* __restrict__ tok,
+                                                    float* __restrict__ x0, int64_t N, int C) {
+  const int64_t n = blockIdx.x;
+  const int64_t row = tok[n];
+  const f32x4* s = reinterpret_cast<const f32x4*>(wte + row * C);
+  f32x4* o = reinterpret_cast<f32x4*>(x0 + n * C);
+  for (int c = threadIdx.x; c < C / 4; c += blockDim.x) o[c] = s[c];
+}
+
+__global__ __launch_bounds__(256) void embed_bwd_kernel(const float* __restrict__ gx0,
+                                                        const int32_t* __restrict__ tok,
+                                                        float* __restrict__ gwte, int C) {
+  const int64_t n = blockIdx.x;
+  const int64_t row = tok[n];
+  for (int c = threadIdx.x; c < C; c += blockDim.x)
+    atomicAdd(gwte + row * C + c, gx0[n * C + c]);
+}
+
+// ------------------------------------------------------------ mix + RMSNorm
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, const f32x4& v) {
+  bf16x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = static_cast<bf16>(v[j]);
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+               static_cast<float>(v[3])};
+}
+__device__ __forceinline__ f32x4 round4(const f32x4& v, float) { return v; }
+__device__ __forceinline__ f32x4 round4(const f32x4& v, bf16) {
+  f32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = static_cast<float>(static_cast<bf16>(v[j]));
+  return r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void mix_norm_kernel(
+    const float* __restrict__ x, const float* __restrict__ x0, const float* __restrict__ lam_r,
+    const float* __restrict__ lam_0, float* __restrict__ xin_out, T* __restrict__ y,
+    float* __restrict__ r_out, const float* __restrict__ wg, float* __restrict__ a, int64_t N,
+    int C, int hk, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int C4 = C / 4;
+  const float lr = x0 ? lam_r[0] : 1.0f, l0 = x0 ? lam_0[0] : 0.0f;
+  f32x4 v[kMaxC4];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxC4; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) {
+      f32x4 xv = reinterpret_cast<const f32x4*>(x + n * C)[c4];
+      if (x0) {
+        const f32x4 zv = reinterpret_cast<const f32x4*>(x0 + n * C)[c4];
+        xv = lr * xv + l0 * zv;
+        if (xin_out) reinterpret_cast<f32x4*>(xin_out + n * C)[c4] = xv;
+      }
+      v[i] = xv;
+      ss += xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)C + eps);
+  if (lane == 0) r_out[n] = r;
+  float gdot[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) gdot[j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxC4; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) {
+      const f32x4 yv = v[i] * r;
+      store4<T>(y + n * C + c4 * 4, yv);
+      if (wg) {
+        const f32x4 yr = round4(yv, T{});
+        for (int j = 0; j < hk; ++j) {
+          const f32x4 w = reinterpret_cast<const f32x4*>(wg + (int64_t)j * C)[c4];
+          gdot[j] += yr[0] * w[0] + yr[1] * w[1] + yr[2] * w[2] + yr[3] * w[3];
+        }
+      }
+    }
+  }
+  if (wg) {
+    for (int j = 0; j < hk; ++j) {
+      const float s = wave_sum(gdot[j]);
+      if (lane == 0) a[n * hk + j] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------ norm backward
+template <typename T>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(gpt::NormBwdArgs p, int64_t N, int C,
+                                                       int hk) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wv;
+  const int C4 = C / 4;
+  const T* y = static_cast<const T*>(p.y);
+  T* gxc = static_cast<T*>(p.gxc);
+  __shared__ float part[4][2];
+  float s_lr = 0.0f, s_l0 = 0.0f;
+  if (n < N) {
+    f32x4 g[kMaxC4], yv[kMaxC4];
+    float ga[16];
+    if (p.mode == gpt::NB_NORM1 && p.ga) {
+      for (int j = 0; j < hk; ++j) ga[j] = p.ga[n * hk + j];
+    }
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxC4; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+        f32x4 gv = reinterpret_cast<const f32x4*>(p.gin + n * C)[c4];
+        if (p.mode == gpt::NB_NORM1 && p.ga) {
+          for (int j = 0; j < hk; ++j)
+            gv += ga[j] * reinterpret_cast<const f32x4*>(p.wg + (int64_t)j * C)[c4];
+        }
+        g[i] = gv;
+        yv[i] = load4<T>(y + n * C + c4 * 4);
+        dot += gv[0] * yv[i][0] + gv[1] * yv[i][1] + gv[2] * yv[i][2] + gv[3] * yv[i][3];
+      }
+    }
+    dot = wave_sum(dot) / (float)C;
+    const float r = p.r[n];
+    const float lr = p.mode == gpt::NB_NORM1 ? p.lam_r[0] : 1.0f;
+    const float l0 = p.mode == gpt::NB_NORM1 ? p.lam_0[0] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxC4; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+        f32x4 gx = r * (g[i] - yv[i] * dot);
+        if (p.mode != gpt::NB_FINAL) gx += reinterpret_cast<const f32x4*>(p.gx + n * C)[c4];
+        if (p.mode == gpt::NB_NORM1) {
+          // gx is now the gradient w.r.t. xin = lr * x + l0 * x0
+          const f32x4 xv = reinterpret_cast<const f32x4*>(p.x + n * C)[c4];
+          const f32x4 zv = reinterpret_cast<const f32x4*>(p.x0 + n * C)[c4];
+          s_lr += gx[0] * xv[0] + gx[1] * xv[1] + gx[2] * xv[2] + gx[3] * xv[3];
+          s_l0 += gx[0] * zv[0] + gx[1] * zv[1] + gx[2] * zv[2] + gx[3] * zv[3];
+          f32x4 g0 = l0 * gx;
+          if (p.last_layer0) g0 += lr * gx;
+          if (!p.gx0_first) g0 += reinterpret_cast<const f32x4*>(p.gx0 + n * C)[c4];
+          reinterpret_cast<f32x4*>(p.gx0 + n * C)[c4] = g0;
+          gx = lr * gx;
+        }
+        if (!(p.mode == gpt::NB_NORM1 && p.last_layer0)) {
+          reinterpret_cast<f32x4*>(p.gx + n * C)[c4] = gx;
+          if (gxc) store4<T>(gxc + n * C + c4 * 4, gx);
+        }
+      }
+    }
+    if (p.mode == gpt::NB_NORM1) {
+      s_lr = wave_sum(s_lr);
+      s_l0 = wave_sum(s_l0);
+    }
+  }
+  if (p.mode == gpt::NB_NORM1) {
+    if (lane == 0) {
+      part[wv][0] = s_lr;
+      part[wv][1] = s_l0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      p.lam_part[blockIdx.x * 2 + 0] = part[0][0] + part[1][0] + part[2][0] + part[3][0];
+      p.lam_part[blockIdx.x * 2 + 1] = part[0][1] + part[1][1] + part[2][1] + part[3][1];
+    }
+  }
+}
+
+// Per-layer lambda gradients: fixed-order sums of the per-block partials.
+__global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __restrict__ part,
+                                                              int nblk, float* g_lr, float* g_l0,
+                                                              int accumulate) {
+  __shared__ double red[2][256];
+  double a = 0.0, b = 0.0;
+  for (int i = threadIdx.x; i < nblk; i += 256) {
+    a += part[2 * i];
+    b += part[2 * i + 1];
+  }
+  red[0][threadIdx.x] = a;
+  red[1][threadIdx.x] = b;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + s];
+      red[1][threadIdx.x] += red[1][threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float va = (float)red[0][0], vb = (float)red[1][0];
+    *g_lr = accumulate ? *g_lr + va : va;
+    *g_l0 = accumulate ? *g_l0 + vb : vb;
+  }
+}
+
+// Gate weight gradient g_Wg[j][c] = sum_n ga[n][j] * xn[n][c]: per-split
+// partial sums, then a fixed-order sum over splits.
+template <typename T>
+__global__ __launch_bounds__(256) void veg_partial_kernel(const float* __restrict__ ga,
+                                                          const T* __restrict__ xn,
+                                                          float* __restrict__ part, int64_t N,
+                                                          int C, int hk, int splits) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int sp = blockIdx.y;
+  if (c >= C) return;
+  const int64_t per = (N + splits - 1) / splits;
+  const int64_t lo = sp * per, hi = lo + per < N ? lo + per : N;
+  float acc[16];
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  for (int64_t n = lo; n < hi; ++n) {
+    const float xv = to_f(xn[n * C + c]);
+    for (int j = 0; j < hk; ++j) acc[j] += ga[n * hk + j] * xv;
+  }
+  for (int j = 0; j < hk; ++j) part[((int64_t)sp * hk + j) * C + c] = acc[j];
+}
+
+__global__ __launch_bounds__(256) void veg_finalize_kernel(const float* __restrict__ part,
+                                                           float* __restrict__ g, int C, int hk,
+                                                           int splits, int accumulate) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= C * hk) return;
+  float s = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) s += part[(int64_t)sp * hk * C + i];
+  g[i] = accumulate ? g[i] + s : s;
+}
+
+// ------------------------------------------------------------ RoPE + QK-norm + VE
+// One block of 4 wavefronts per token. Head slots 0..H-1 are q heads,
+// H..H+Hk-1 k heads, H+Hk..H+2Hk-1 v heads (value-embedding layers only).
+// Lane p < D/2 owns the rotation pair (p, p + D/2).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rqk,
+                                                       const float* __restrict__ cs,
+                                                       const float* __restrict__ a,
+                                                       const float* __restrict__ ve,
+                                                       const int32_t* __restrict__ tok, int T_,
+                                                       int H, int Hk, int D, int Qkv, float eps) {
+  const int64_t n = blockIdx.x;
+  const int t = (int)(n % T_);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int h2 = D / 2;
+  const int nslots = H + Hk + (ve ? Hk : 0);
+  T* row = qkv + n * Qkv;
+  for (int sl = wv; sl < nslots; sl += 4) {
+    if (sl < H + Hk) {
+      T* hp = row + sl * D;  // k heads follow the q heads contiguously
+      float y1 = 0.0f, y2 = 0.0f;
+      if (lane < h2) {
+        const float c = cs[t * h2 + lane], s = cs[(int64_t)T_ * h2 + t * h2 + lane];
+        const float x1 = to_f(hp[lane]), x2 = to_f(hp[lane + h2]);
+        y1 = x1 * c - x2 * s;
+        y2 = x1 * s + x2 * c;
+      }
+      const float ss = wave_sum(y1 * y1 + y2 * y2);
+      const float r = 1.0f / sqrtf(ss / (float)D + eps);
+      if (lane < h2) {
+        hp[lane] = from_f<T>(y1 * r);
+        hp[lane + h2] = from_f<T>(y2 * r);
+      }
+      if (lane == 0) rqk[n * (H + Hk) + sl] = r;
+    } else {
+      const int j = sl - H - Hk;
+      T* vp = row + (H + Hk) * D + j * D;
+      const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
+      const float* er = ve + (int64_t)tok[n] * Hk * D + j * D;
+      for (int dd = lane; dd < D; dd += 64) vp[dd] = from_f<T>(to_f(vp[dd]) + g * er[dd]);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_bwd_kernel(
+    T* __restrict__ gqkv, const T* __restrict__ qkv, const float* __restrict__ rqk,
+    const float* __restrict__ cs, const float* __restrict__ a, const float* __restrict__ ve,
+    float* __restrict__ gve, float* __restrict__ ga, const int32_t* __restrict__ tok, int T_,
+    int H, int Hk, int D, int Qkv) {
+  const int64_t n = blockIdx.x;
+  const int t = (int)(n % T_);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int h2 = D / 2;
+  const int nslots = H + Hk + (ve ? Hk : 0);
+  T* grow = gqkv + n * Qkv;
+  const T* row = qkv + n * Qkv;
+  for (int sl = wv; sl < nslots; sl += 4) {
+    if (sl < H + Hk) {
+      T* gp = grow + sl * D;
+      const T* yp = row + sl * D;
+      float g1 = 0.0f, g2 = 0.0f, y1 = 0.0f, y2 = 0.0f;
+      if (lane < h2) {
+        g1 = to_f(gp[lane]);
+        g2 = to_f(gp[lane + h2]);
+        y1 = to_f(yp[lane]);
+        y2 = to_f(yp[lane + h2]);
+      }
+      const float dot = wave_sum(g1 * y1 + g2 * y2) / (float)D;
+      const float r = rqk[n * (H + Hk) + sl];
+      if (lane < h2) {
+        const float a1 = r * (g1 - y1 * dot), a2 = r * (g2 - y2 * dot);
+        const float c = cs[t * h2 + lane], s = cs[(int64_t)T_ * h2 + t * h2 + lane];
+        gp[lane] = from_f<T>(a1 * c + a2 * s);
+        gp[lane + h2] = from_f<T>(-a1 * s + a2 * c);
+      }
+    } else {
+      const int j = sl - H - Hk;
+      const T* gp = grow + (H + Hk) * D + j * D;
+      const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
+      const int64_t off = (int64_t)tok[n] * Hk * D + j * D;
+      float dot = 0.0f;
+      for (int dd = lane; dd < D; dd += 64) {
+        const float gv = to_f(gp[dd]);
+        dot += gv * ve[off + dd];
+        atomicAdd(gve + off + dd, g * gv);
+      }
+      dot = wave_sum(dot);
+      if (lane == 0) ga[n * Hk + j] = g * (1.0f - g) * dot;
+    }
+  }
+}
+
+// ------------------------------------------------------------ loss
+// Per token: lse = cap + log(sum exp(c - cap)); loss_n = lse - c[y]. Writes
+// 1/rowsum per token and 1/n_valid for the logit-gradient prologue, then the
+// mean loss. One block; fixed-order reduction in double.
+template <typename T>
+__global__ __launch_bounds__(1024) void loss_kernel(const T* __restrict__ logits,
+                                                    const int32_t* __restrict__ tgt,
+                                                    float* __restrict__ rowsum,
+                                                    float* __restrict__ scalars,
+                                                    float* __restrict__ loss, int64_t N, int V,
+                                                    float cap) {
+  __shared__ double s_loss[1024];
+  __shared__ int s_cnt[1024];
+  double acc = 0.0;
+  int cnt = 0;
+  for (int64_t n = threadIdx.x; n < N; n += 1024) {
+    const float rs = rowsum[n];
+    const int y = tgt[n];
+    if (y >= 0) {
+      acc += (double)cap + log((double)rs) - (double)to_f(logits[n * V + y]);
+      ++cnt;
+    }
+    rowsum[n] = 1.0f / rs;
+  }
+  s_loss[threadIdx.x] = acc;
+  s_cnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      s_loss[threadIdx.x] += s_loss[threadIdx.x + s];
+      s_cnt[threadIdx.x] += s_cnt[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int nv = s_cnt[0] > 0 ? s_cnt[0] : 1;
+    loss[0] = (float)(s_loss[0] / nv);
+    scalars[0] = 1.0f / (float)nv;
+  }
+}
+
+}  // namespace gk
+
+namespace gpt {
+using namespace gk;
+
+static unsigned blocks_for(int64_t n, int per) {
+  int64_t b = (n + per - 1) / per;
+  if (b > 65535 * 16) b = 65535 * 16;
+  return (unsigned)(b < 1 ? 1 : b);
+}
+
+void launch_cast(const float* src, void* dst, const std::vector<CastSeg>& segs, hipStream_t s) {
+  for (size_t base = 0; base < segs.size(); base += 128) {
+    CastTable t{};
+    t.nseg = (int)std::min<size_t>(128, segs.size() - base);
+    int64_t mx = 0;
+    for (int i = 0; i < t.nseg; ++i) {
+      t.seg[i] = segs[base + i];
+      mx = std::max(mx, t.seg[i].n);
+    }
+    dim3 grid(std::min<unsigned>(blocks_for(mx, 256 * 8), 1024), t.nseg);
+    hipLaunchKernelGGL(cast_kernel, grid, dim3(256), 0, s, src, static_cast<bf16*>(dst), t);
+  }
+}
+
+void launch_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(zero_kernel, dim3(std::min<unsigned>(blocks_for(n, 256 * 4), 8192)),
+                     dim3(256), 0, s, p, n);
+}
+
+void launch_rope_table(float* cs, int T, int D, float theta, hipStream_t s) {
+  const int64_t n = (int64_t)T * (D / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, cs, T, D,
+                     (double)theta);
+}
+
+void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C,
+                  hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)N), dim3(256), 0, s, wte, tok, x0, N, C);
+}
+
+void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t N, int C,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(embed_bwd_kernel, dim3((unsigned)N), dim3(256), 0, s, gx0, tok, gwte, C);
+}
+
+void launch_mix_norm(const Dims& d, const float* x, const float* x0, const float* lam_r,
+                     const float* lam_0, float* xin_out, void* y, float* r, const float* wg,
+                     float* a, hipStream_t s) {
+  dim3 grid((unsigned)((d.N + 3) / 4));
+  if (d.bf16)
+    hipLaunchKernelGGL(mix_norm_kernel<bf16>, grid, dim3(256), 0, s, x, x0, lam_r, lam_0,
+                       xin_out, static_cast<bf16*>(y), r, wg, a, d.N, d.C, d.Hk, d.eps);
+  else
+    hipLaunchKernelGGL(mix_norm_kernel<float>, grid, dim3(256), 0, s, x, x0, lam_r, lam_0,
+                       xin_out, static_cast<float*>(y), r, wg, a, d.N, d.C, d.Hk, d.eps);
+}
+
+void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((d.N + 3) / 4));
+  if (d.bf16)
+    hipLaunchKernelGGL(norm_bwd_kernel<bf16>, grid, dim3(256), 0, s, a, d.N, d.C, d.Hk);
+  else
+    hipLaunchKernelGGL(norm_bwd_kernel<float>, grid, dim3(256), 0, s, a, d.N, d.C, d.Hk);
+}
+
+void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
+                            float* g_l0, hipStream_t s) {
+  hipLaunchKernelGGL(lambda_finalize_kernel, dim3(1), dim3(256), 0, s, lam_part, nblk, g_lr,
+                     g_l0, d.accumulate ? 1 : 0);
+}
+
+void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* part, int splits,
+                      float* gwg, hipStream_t s) {
+  dim3 grid((unsigned)((d.C + 255) / 256), (unsigned)splits);
+  if (d.bf16)
+    hipLaunchKernelGGL(veg_partial_kernel<bf16>, grid, dim3(256), 0, s, ga,
+                       static_cast<const bf16*>(xn), part, d.N, d.C, d.Hk, splits);
+  else
+    hipLaunchKernelGGL(veg_partial_kernel<float>, grid, dim3(256), 0, s, ga,
+                       static_cast<const float*>(xn), part, d.N, d.C, d.Hk, splits);
+  hipLaunchKernelGGL(veg_finalize_kernel, dim3((unsigned)((d.C * d.Hk + 255) / 256)), dim3(256),
+                     0, s, part, gwg, d.C, d.Hk, splits, d.accumulate ? 1 : 0);
+}
+
+void launch_rope_qk_ve_fwd(const Dims& d, void* qkv, float* rqk, const float* cs, const float* a,
+                           const float* ve_table, const int32_t* tok, hipStream_t s) {
+  if (d.bf16)
+    hipLaunchKernelGGL(rope_fwd_kernel<bf16>, dim3((unsigned)d.N), dim3(256), 0, s,
+                       static_cast<bf16*>(qkv), rqk, cs, a, ve_table, tok, d.T, d.H, d.Hk, d.D,
+                       d.Qkv, d.eps);
+  else
+    hipLaunchKernelGGL(rope_fwd_kernel<float>, dim3((unsigned)d.N), dim3(256), 0, s,
+                       static_cast<float*>(qkv), rqk, cs, a, ve_table, tok, d.T, d.H, d.Hk, d.D,
+                       d.Qkv, d.eps);
+}
+
+void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const float* rqk,
+                           const float* cs, const float* a, const float* ve_table,
+                           float* gve_table, float* ga, const int32_t* tok, hipStream_t s) {
+  if (d.bf16)
+    hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3((unsigned)d.N), dim3(256), 0, s,
+                       static_cast<bf16*>(gqkv), static_cast<const bf16*>(qkv), rqk, cs, a,
+                       ve_table, gve_table, ga, tok, d.T, d.H, d.Hk, d.D, d.Qkv);
+  else
+    hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3((unsigned)d.N), dim3(256), 0, s,
+                       static_cast<float*>(gqkv), static_cast<const float*>(qkv), rqk, cs, a,
+                       ve_table, gve_table, ga, tok, d.T, d.H, d.Hk, d.D, d.Qkv);
+}
+
+void launch_loss(const Dims& d, const void* logits, const int32_t* tgt, float* rowsum,
+                 float* scalars, float* loss, hipStream_t s) {
+  if (d.bf16)
+    hipLaunchKernelGGL(loss_kernel<bf16>, dim3(1), dim3(1024), 0, s,
+                       static_cast<const bf16*>(logits), tgt, rowsum, scalars, loss, d.N, d.V,
+                       d.cap);
+  else
+    hipLaunchKernelGGL(loss_kernel<float>, dim3(1), dim3(1024), 0, s,
+                       static_cast<const float*>(logits), tgt, rowsum, scalars, loss, d.N, d.V,
+                       d.cap);
+}
+
+}  // namespace gpt

@@ -1,0 +1,187 @@
+/*
+ * gpt_step.h -- C ABI of the nanochat GPT forward+backward step on gfx950.
+ *
+ * One call computes the training loss of one batch and the gradient of every
+ * parameter of the decoder-only GPT that these pages describe:
+ *   - "Nanochat在nanoGPT之上的新增功能" (nanochat additions over nanoGPT),
+ *     section 1 feature table and the notes under it: RoPE, parameter-free
+ *     RMSNorm, ReLU^2 MLP, separate c_q/c_k/c_v/c_proj, GQA, QK-norm after
+ *     RoPE, no bias, untied lm_head, no dropout, tanh softcap +-15, SSSL
+ *     sliding windows (short = 1/4 context, last layer full), value
+ *     embeddings v += gate * ve on alternating layers, per-layer
+ *     resid / x0 lambdas, dynamic per-tensor fp8 linears;
+ *   - "NanoChat基础训练报告" (d12 training report), architecture block: the
+ *     d12 shape, bf16 training, value embeddings on odd layers;
+ *   - "nanochat — 架构与原理" (architecture overview), section 4: the -1
+ *     ignore index of the loss.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (device) are HIP device pointers; (host) are host
+ *     pointers. Every buffer is owned by the caller; the library allocates
+ *     nothing and frees nothing.
+ *   - Status: GPT_OK (0) or a negative gpt_status. Validation errors return
+ *     before anything is enqueued. gpt_last_error() gives a per-thread text.
+ *   - Device work is enqueued on `stream` (a hipStream_t passed as void*;
+ *     NULL = the null stream) and the call returns without synchronising.
+ */
+#ifndef GPT_STEP_H
+#define GPT_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPT_ABI_VERSION 1
+
+typedef enum gpt_status {
+  GPT_OK = 0,
+  GPT_E_INVAL = -1,        /* a config field or size is out of range        */
+  GPT_E_NULLPTR = -2,      /* a required pointer is NULL                     */
+  GPT_E_ALIGN = -3,        /* a pointer breaks the alignment rule below      */
+  GPT_E_WORKSPACE = -4,    /* workspace smaller than gpt_workspace_size      */
+  GPT_E_UNSUPPORTED = -5,  /* valid model, but not built into this library   */
+  GPT_E_HIP = -6           /* the HIP runtime reported an error              */
+} gpt_status;
+
+enum { GPT_DT_F32 = 0, GPT_DT_BF16 = 1 };
+
+/* flags */
+enum {
+  GPT_F_ACCUMULATE = 1     /* grads += new grads instead of grads = new grads */
+};
+
+/*
+ * Model and batch description. All sizes are element counts.
+ *   n_embd = n_head * head_dim is not required (c_q/c_proj use n_head*head_dim).
+ *   head_dim in {64, 128}; n_head % n_kv_head == 0; n_embd, mlp_hidden and
+ *   vocab multiples of 64 (the additions page pads the vocabulary to a
+ *   multiple of 64); 1 <= seq_len; 1 <= batch; 0 <= short_window.
+ *   Layer l uses the full causal context iff l % 4 == 3 or l == n_layer-1,
+ *   else the short window: key s is visible to query t iff
+ *   0 <= t - s <= short_window. Layer l has a value embedding iff
+ *   l % 2 == (n_layer - 1) % 2.
+ */
+typedef struct gpt_config {
+  int32_t abi_version;     /* GPT_ABI_VERSION                                */
+  int32_t n_layer;
+  int32_t n_embd;          /* C                                              */
+  int32_t n_head;          /* H                                              */
+  int32_t n_kv_head;       /* Hk                                             */
+  int32_t head_dim;        /* D                                              */
+  int32_t mlp_hidden;      /* F                                              */
+  int32_t vocab;           /* V                                              */
+  int32_t seq_len;         /* T                                              */
+  int32_t batch;           /* B                                              */
+  int32_t short_window;    /* W                                              */
+  int32_t compute_dtype;   /* GPT_DT_F32 | GPT_DT_BF16                       */
+  int32_t fp8_linears;     /* 0 | 1 (1: not built yet -> GPT_E_UNSUPPORTED)  */
+  int32_t flags;           /* GPT_F_*                                        */
+  float rope_theta;        /* RoPE base, > 1                                 */
+  float norm_eps;          /* RMSNorm epsilon (all norms), > 0               */
+  float softcap;           /* logit cap c = softcap * tanh(z / softcap), > 0 */
+} gpt_config;
+
+/* GPT_ABI_VERSION of the loaded library. */
+int gpt_abi_version(void);
+
+/* Host only. GPT_OK if the library can run `cfg`, else the reason. */
+int gpt_config_validate(const gpt_config* cfg);
+
+/*
+ * Host only. Canonical parameter layout: params and grads are flat fp32
+ * arrays, row-major, no padding, tensors in this order:
+ *   wte [V, C];
+ *   per layer l: l.q [H*D, C], l.k [Hk*D, C], l.v [Hk*D, C], l.o [C, H*D],
+ *                l.fc [F, C], l.mp [C, F], and on value-embedding layers
+ *                l.ve [V, Hk*D], l.veg [Hk, C];
+ *   lm_head [V, C]; resid_lambdas [L]; x0_lambdas [L].
+ * Linear weights are [out, in] (y = x W^T). Names are "wte", "l3.q", ...
+ * gpt_param_count: number of tensors and total element count.
+ * gpt_param_info: tensor i's name (NUL-terminated, < 64 bytes), element
+ * offset, rows and cols (cols = 1 for the lambda vectors).
+ */
+int gpt_param_count(const gpt_config* cfg, int64_t* n_tensors, int64_t* n_elems);
+int gpt_param_info(const gpt_config* cfg, int64_t i, char name[64],
+                   int64_t* offset, int64_t* rows, int64_t* cols);
+
+/* Host only. Window and value-embedding pattern of layer l (0/1 each). */
+int gpt_layer_info(const gpt_config* cfg, int32_t l, int32_t* is_full, int32_t* has_ve);
+
+/* Host only. Bytes of device workspace gpt_fwd_bwd needs for `cfg`. */
+int gpt_workspace_size(const gpt_config* cfg, size_t* bytes);
+
+/*
+ * Host only. Where the forward keeps a saved tensor inside the workspace,
+ * for inspection after a synchronised call. `name` is one of:
+ *   "x"    fp32 [N, C]   residual stream entering layer `layer`
+ *                        (layer = n_layer: the stream before the final norm)
+ *   "xn"   act  [N, C]   RMSNorm output feeding c_q/c_k/c_v
+ *   "qkv"  act  [N, (H+2Hk)*D]  q, k after RoPE+QK-norm; v after the
+ *                        value embedding; head-major columns
+ *   "attn" act  [N, H*D] attention output
+ *   "xn2"  act  [N, C]   RMSNorm output feeding the MLP
+ *   "u"    act  [N, F]   c_fc output before ReLU^2
+ *   "xf"   act  [N, C]   final RMSNorm output (layer ignored)
+ *   "logits" act [N, V]  softcapped logits (layer ignored)
+ * N = batch * seq_len, row n = b * seq_len + t; act = compute_dtype.
+ * Returns the byte offset and size. GPT_E_INVAL for an unknown name/layer.
+ */
+int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
+                         size_t* offset, size_t* bytes);
+
+/*
+ * Forward + backward of one batch.
+ *   params    (device) fp32 [n_elems], canonical layout; read only.
+ *   tokens    (device) int32 [batch, seq_len], ids in [0, vocab).
+ *   targets   (device) int32 [batch, seq_len], ids in [0, vocab) or -1
+ *             (ignored). The loss is the mean over non-ignored targets
+ *             (0 if there are none).
+ *   loss      (device) fp32 [1], written.
+ *   grads     (device) fp32 [n_elems], canonical layout; overwritten, or
+ *             added to with GPT_F_ACCUMULATE.
+ *   workspace (device) >= gpt_workspace_size bytes; scratch, contents
+ *             undefined after the call.
+ * Alignment: params, grads and workspace 256-byte aligned; tokens, targets
+ * and loss 4-byte aligned. Out-of-range token ids are a precondition
+ * violation (not checked). Concurrent calls need distinct workspaces,
+ * grads and loss buffers.
+ */
+int gpt_fwd_bwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
+                const int32_t* targets, float* loss, float* grads,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward only: the loss (same arguments and rules, no grads). */
+int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
+            const int32_t* targets, float* loss,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host only; measurement support. After gpt_profile_begin(prefix), every
+ * kernel launch of gpt_fwd_bwd / gpt_fwd whose launch-site name starts with
+ * `prefix` is bracketed by two HIP events recorded on the call's stream.
+ * Site names: "embed.fwd", "gemm.qkv.fwd", "rope.fwd", "attn.fwd",
+ * "gemm.o.fwd", "gemm.fc.fwd", "gemm.mp.fwd", "gemm.lm.fwd", "loss",
+ * "gemm.lm.dgrad", "gemm.lm.wgrad", "gemm.mp.dgrad", "gemm.mp.wgrad",
+ * "gemm.fc.dgrad", "gemm.fc.wgrad", "gemm.o.dgrad", "gemm.o.wgrad",
+ * "attn.delta", "attn.bwd", "gemm.qkv.dgrad", "gemm.qkv.wgrad", "embed.bwd".
+ * gpt_profile_end waits for the recorded events, returns the summed
+ * kernel time in milliseconds and the number of bracketed launches, and
+ * stops recording. Process-wide state: not for concurrent callers.
+ */
+int gpt_profile_begin(const char* site_prefix);
+int gpt_profile_end(double* total_ms, int64_t* launches);
+
+/* Static text for a status code. */
+const char* gpt_status_string(int status);
+
+/* Per-thread detail of the last error ("" if none). */
+const char* gpt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT_STEP_H */

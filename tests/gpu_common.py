@@ -1,0 +1,57 @@
+"""Helpers shared by the GPU tests: run the HIP path through the C ABI and
+compare it with the oracle tensor by tensor."""
+import numpy as np
+
+import oracle
+import workloads as W
+from decoder_only_pretraining_amd import binding as B
+
+
+def gpu_step(w, params, tok, tgt, flags=0):
+    import torch
+    step = B.Step(w, params, tok, tgt, flags)
+    step.run()
+    torch.cuda.synchronize()
+    return float(step.loss.item()), step.grads.cpu().numpy(), step
+
+
+def inputs(w, wseed=None, tseed=None):
+    _, total = oracle.param_offsets(w)
+    p = W.gen_params(total, w.n_layer, W.weight_seed(w) if wseed is None else wseed)
+    tok, tgt = W.split_tokens(W.gen_tokens(w, tseed))
+    return p, tok, tgt
+
+
+def per_tensor(w, a, b):
+    """name -> (rel_l2, cosine) of a against reference b, in float64."""
+    out = {}
+    for name, (o, s) in oracle.param_offsets(w)[0].items():
+        n = int(np.prod(s))
+        x = a[o:o + n].astype(np.float64)
+        y = b[o:o + n].astype(np.float64)
+        ny = np.linalg.norm(y)
+        rel = np.linalg.norm(x - y) / ny if ny > 0 else np.linalg.norm(x)
+        cos = float(np.dot(x, y) / (np.linalg.norm(x) * ny)) if ny > 0 and np.linalg.norm(x) > 0 else (1.0 if ny == 0 and np.linalg.norm(x) == 0 else 0.0)
+        out[name] = (float(rel), cos)
+    return out
+
+
+def assert_fp32_parity(w, loss_g, grads_g, loss_o, grads_o, tol=1e-4, zero=()):
+    """zero: tensors whose gradient is analytically 0 for this input (both
+    sides then hold rounding noise); they must be negligible instead."""
+    assert abs(loss_g - loss_o) <= tol * abs(loss_o), (loss_g, loss_o)
+    offs = oracle.param_offsets(w)[0]
+    total = np.linalg.norm(grads_o)
+    for name in zero:
+        o, s = offs[name]
+        n = int(np.prod(s))
+        assert np.linalg.norm(grads_g[o:o + n]) <= 1e-6 * total, name
+    bad = {k: v for k, v in per_tensor(w, grads_g, grads_o).items()
+           if k not in zero and not v[0] <= tol}
+    assert not bad, bad
+
+
+def assert_bf16_parity(w, loss_g, grads_g, loss_o, grads_o, ltol=1e-2, cmin=0.999):
+    assert abs(loss_g - loss_o) <= ltol * abs(loss_o), (loss_g, loss_o)
+    bad = {k: v for k, v in per_tensor(w, grads_g, grads_o).items() if not v[1] >= cmin}
+    assert not bad, bad
