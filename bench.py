@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="d12")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1)
+    ap.add_argument("--cpu-rows", type=int, default=3)
     ap.add_argument("--profile-site", default="gemm.lm.fwd",
                     help="launch site timed with HIP events for the roofline figure")
     args = ap.parse_args()

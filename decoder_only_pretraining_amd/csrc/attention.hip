@@ -78,6 +78,40 @@ __device__ __forceinline__ void store_col4<float>(float* p, float a, float b, fl
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
+// Fragment of an operand whose 32 rows run along the columns of an LDS tile
+// T[row][col] and whose contraction slots run down the rows: lane l takes
+// column col0 + l%32; slot jj (0..7) is row kbase + 8*(jj/4) + 4*(l/32) + jj%4
+// (the slot order of the accumulator rows, so probabilities and score
+// gradients feed MFMAs straight from the accumulators). bf16 uses two
+// transposing LDS reads (ds_read_b64_tr_b16): in a 16-lane group, source lane
+// 4q + a addresses T[k0 + q][m0 + 4a] and output lane i receives
+// T[k0 .. k0+3][m0 + i].
+template <int PITCH>
+__device__ __forceinline__ void frag_down(Frag<bf16>& f, const bf16* lds, int kbase, int col0,
+                                          int lane) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int g16 = lane >> 4, L = lane & 15;
+  const int k0 = kbase + (g16 >> 1) * 4 + (L >> 2);
+  const int m = col0 + (g16 & 1) * 16 + (L & 3) * 4;
+  const bf16* p = lds + k0 * PITCH + m;
+  union {
+    struct { v4i16 a, b; } s;
+    bf16x8 v;
+  } u;
+  u.s.a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  u.s.b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * PITCH));
+  f.v = u.v;
+}
+template <int PITCH>
+__device__ __forceinline__ void frag_down(Frag<float>& f, const float* lds, int kbase, int col0,
+                                          int lane) {
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj)
+    frag_set(f, jj, lds[(kbase + (jj >> 2) * 8 + (lane >> 5) * 4 + (jj & 3)) * PITCH + col0 +
+                        (lane & 31)]);
+}
+
 // ------------------------------------------------------------ forward
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
@@ -164,11 +198,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           Frag<T> vf;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int sl = sb * 32 + 16 * c + (jj >> 2) * 8 + hi * 4 + (jj & 3);
-            frag_set(vf, jj, to_f(Vs[sl][db * 32 + (lane & 31)]));
-          }
+          frag_down<D + PAD>(vf, &Vs[0][0], sb * 32 + 16 * c, db * 32, lane);
           mfma(o[db], vf, pf);
         }
       }
@@ -285,12 +315,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             Frag<T> doT, qT;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              const int tl = tb * 32 + 16 * c + (jj >> 2) * 8 + hi * 4 + (jj & 3);
-              frag_set(doT, jj, to_f(dOs[tl][db * 32 + (lane & 31)]));
-              frag_set(qT, jj, to_f(Qs[tl][db * 32 + (lane & 31)]));
-            }
+            frag_down<D + PAD>(doT, &dOs[0][0], tb * 32 + 16 * c, db * 32, lane);
+            frag_down<D + PAD>(qT, &Qs[0][0], tb * 32 + 16 * c, db * 32, lane);
             mfma(dv[db], doT, pf);
             mfma(dk[db], qT, dsf);
           }
@@ -387,11 +413,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           Frag<T> kT;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int sl = sb * 32 + 16 * c + (jj >> 2) * 8 + hi * 4 + (jj & 3);
-            frag_set(kT, jj, to_f(Ks[sl][db * 32 + (lane & 31)]));
-          }
+          frag_down<D + PAD>(kT, &Ks[0][0], sb * 32 + 16 * c, db * 32, lane);
           mfma(dq[db], kT, dsf);
         }
       }

@@ -1,110 +1,201 @@
-// Tiled MFMA GEMM for gfx950: C[M][N] = sum_k A(m,k) * B(n,k), fp32
-// accumulation, with fused operand prologues and output epilogues.
+// GEMM launchers of the GPT step: C[M][N] = sum_k A(m,k) * B(n,k) with fused
+// operand prologues (ReLU^2, softcap cross-entropy gradient) and output
+// epilogues (store, residual add, ReLU^2 backward, softcap + row sums,
+// split-K atomic accumulation).
 //
-// Each operand is either contraction-contiguous ("K-major": row m holds k)
-// or output-contiguous ("MN-major": row k holds m). Global tiles are read
-// with 16-byte vector loads along the contiguous axis and written to LDS in
-// a [row][k] layout (MN-major operands are transposed on the LDS write), so
-// the MFMA fragment read is one 16-byte LDS load per lane for every layout.
-// Two LDS stages: the global loads of tile k+1 are issued before the MFMAs
-// of tile k.
+// bf16 products run on the tiled MFMA core in gemm_core.h. fp32 products
+// (the small fp32 configuration) use the plain kernel below: each operand is
+// either contraction-contiguous ("K-major": row m holds k) or output-
+// contiguous ("MN-major": row k holds m); tiles are written to LDS in a
+// [row][k] layout (MN-major operands transposed on the LDS write).
 #include "device_common.h"
+#include "gemm_core.h"
 #include "internal.h"
+
+#include <algorithm>
 
 namespace gk {
 
 // ------------------------------------------------------------ prologues
+// A prologue transforms each 8-element (bf16) or 4-element (fp32) operand
+// vector after its global load; `vec<ALONG_K>` gets the coordinates of the
+// vector's first element and whether the vector runs along the contraction
+// index. init() runs once per thread before the first tile.
 struct PreId {
   static constexpr bool kActive = false;
-  __device__ float operator()(float v, int64_t, int64_t) const { return v; }
+  __device__ void init() {}
+  template <bool ALONG_K, int NE>
+  __device__ void vec(float*, int64_t, int64_t) const {}
 };
 struct PreRelu2 {  // ReLU^2 of the MLP hidden pre-activation
   static constexpr bool kActive = true;
-  __device__ float operator()(float v, int64_t, int64_t) const {
-    float r = fmaxf(v, 0.0f);
-    return r * r;
+  __device__ void init() {}
+  template <bool ALONG_K, int NE>
+  __device__ void vec(float* v, int64_t, int64_t) const {
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const float r = fmaxf(v[j], 0.0f);
+      v[j] = r * r;
+    }
   }
 };
-// Gradient of mean cross-entropy through the tanh softcap, from a stored
-// softcapped logit c: (exp(c - cap) / rowsum - [v == y]) * (1 - (c/cap)^2) / n_valid.
-// |c| <= cap, so exp(c - cap) never overflows and the row sums of
-// exp(c - cap) need no running maximum.
-struct PreCE {
-  static constexpr bool kActive = true;
-  const float* inv_rowsum;
-  const int32_t* tgt;
-  const float* inv_nvalid;
-  float cap;
-  int token_is_mn;  // 1: operand rows are tokens; 0: operand rows are vocab ids
-  __device__ float operator()(float c, int64_t mn, int64_t k) const {
-    const int64_t n = token_is_mn ? mn : k;
-    const int64_t v = token_is_mn ? k : mn;
-    const int y = tgt[n];
-    if (y < 0) return 0.0f;
-    float p = __expf(c - cap) * inv_rowsum[n];
-    if (v == y) p -= 1.0f;
-    const float q = c / cap;
-    return p * (1.0f - q * q) * inv_nvalid[0];
+// ------------------------------------------------------------ epilogues
+// value(m, n, acc): per-element transform in the accumulator layout;
+// rowterm(value): the row-sum contribution (kRowSum epilogues only);
+// store4(m, n, v, cnt): write columns n .. n+cnt-1 of row m (cnt <= 4).
+// operator() is the element-wise form used by the fp32 kernel.
+template <typename T>
+__device__ __forceinline__ void put4(T* p, const f32x4& v, int cnt) {
+  if (cnt == 4) {
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = static_cast<bf16>(v[j]);
+      *reinterpret_cast<bf16x4*>(p) = o;
+    } else {
+      *reinterpret_cast<f32x4*>(p) = v;
+    }
+  } else {
+    for (int j = 0; j < cnt; ++j) p[j] = from_f<T>(v[j]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ f32x4 get4(const T* p, int cnt) {
+  if (cnt == 4) {
+    if constexpr (sizeof(T) == 2) {
+      const bf16x4 o = *reinterpret_cast<const bf16x4*>(p);
+      return f32x4{static_cast<float>(o[0]), static_cast<float>(o[1]), static_cast<float>(o[2]),
+                   static_cast<float>(o[3])};
+    } else {
+      return *reinterpret_cast<const f32x4*>(p);
+    }
+  }
+  f32x4 r{0, 0, 0, 0};
+  for (int j = 0; j < cnt; ++j) r[j] = to_f(p[j]);
+  return r;
+}
+
+template <class Derived>
+struct EpBase {
+  static constexpr bool kRowSum = false;
+  static constexpr bool kScalar = false;  // store1 with one column per lane
+  __device__ float value(int64_t, int64_t, float v) const { return v; }
+  __device__ float rowterm(float) const { return 0.0f; }
+  __device__ float operator()(int64_t m, int64_t n, float acc) const {
+    const Derived& d = static_cast<const Derived&>(*this);
+    const float v = d.value(m, n, acc);
+    d.store4(m, n, f32x4{v, 0, 0, 0}, 1);
+    return Derived::kRowSum ? d.rowterm(v) : 0.0f;
   }
 };
 
-// ------------------------------------------------------------ epilogues
 template <typename T>
-struct EpStore {
-  static constexpr bool kRowSum = false;
+struct EpStore : EpBase<EpStore<T>> {
   T* C;
   int64_t ldc;
-  __device__ float operator()(int64_t m, int64_t n, float v) const {
-    C[m * ldc + n] = from_f<T>(v);
-    return 0.0f;
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    put4<T>(C + m * ldc + n, v, cnt);
   }
 };
-struct EpF32 {
-  static constexpr bool kRowSum = false;
+struct EpF32 : EpBase<EpF32> {
   float* C;
   int64_t ldc;
   int accumulate;
-  __device__ float operator()(int64_t m, int64_t n, float v) const {
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
     float* p = C + m * ldc + n;
-    *p = accumulate ? *p + v : v;
-    return 0.0f;
+    if (accumulate) v += get4<float>(p, cnt);
+    put4<float>(p, v, cnt);
   }
 };
-struct EpResid {  // C = R + acc (residual stream, fp32)
-  static constexpr bool kRowSum = false;
+struct EpAtomic : EpBase<EpAtomic> {  // C += acc with fp32 atomics (split-K partial sums)
+  static constexpr bool kScalar = true;
+  float* C;
+  int64_t ldc;
+  __device__ void store1(int64_t m, int64_t n, float v) const { atomicAdd(C + m * ldc + n, v); }
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    for (int j = 0; j < cnt; ++j) store1(m, n + j, v[j]);
+  }
+};
+struct EpResid : EpBase<EpResid> {  // C = R + acc (residual stream, fp32)
   const float* R;
   float* C;
   int64_t ldc;
-  __device__ float operator()(int64_t m, int64_t n, float v) const {
-    C[m * ldc + n] = R[m * ldc + n] + v;
-    return 0.0f;
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    put4<float>(C + m * ldc + n, v + get4<float>(R + m * ldc + n, cnt), cnt);
   }
 };
 template <typename T>
-struct EpRelu2Bwd {  // C = acc * d/du relu(u)^2 = acc * 2 max(u, 0)
-  static constexpr bool kRowSum = false;
+struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {  // C = acc * d/du relu(u)^2 = acc * 2 max(u, 0)
   const T* U;
   T* C;
   int64_t ldc;
-  __device__ float operator()(int64_t m, int64_t n, float v) const {
-    const float u = to_f(U[m * ldc + n]);
-    C[m * ldc + n] = from_f<T>(u > 0.0f ? 2.0f * u * v : 0.0f);
-    return 0.0f;
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    const f32x4 u = get4<T>(U + m * ldc + n, cnt);
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = u[j] > 0.0f ? 2.0f * u[j] * v[j] : 0.0f;
+    put4<T>(C + m * ldc + n, o, cnt);
   }
 };
 template <typename T>
-struct EpSoftcap {  // c = cap * tanh(z / cap), stored; row sums of exp(c - cap)
+struct EpSoftcap : EpBase<EpSoftcap<T>> {  // c = cap * tanh(z / cap); row sums of exp(c - cap)
   static constexpr bool kRowSum = true;
   T* C;
   int64_t ldc;
   float cap;
-  float* rowsum;
-  __device__ float operator()(int64_t m, int64_t n, float v) const {
-    const T c = from_f<T>(cap * tanhf(v / cap));
-    C[m * ldc + n] = c;
-    return __expf(to_f(c) - cap);
+  // the stored (rounded) value, so the row sums match what the backward reads
+  __device__ float value(int64_t, int64_t, float z) const {
+    return to_f(from_f<T>(cap * tanhf(z / cap)));
+  }
+  __device__ float rowterm(float c) const { return __expf(c - cap); }
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    put4<T>(C + m * ldc + n, v, cnt);
   }
 };
+
+template <typename T>
+EpStore<T> mk_store(void* C, int64_t ld) {
+  EpStore<T> e;
+  e.C = static_cast<T*>(C);
+  e.ldc = ld;
+  return e;
+}
+inline EpF32 mk_f32(float* C, int64_t ld, int acc) {
+  EpF32 e;
+  e.C = C;
+  e.ldc = ld;
+  e.accumulate = acc;
+  return e;
+}
+inline EpAtomic mk_atomic(float* C, int64_t ld) {
+  EpAtomic e;
+  e.C = C;
+  e.ldc = ld;
+  return e;
+}
+inline EpResid mk_resid(const float* R, float* C, int64_t ld) {
+  EpResid e;
+  e.R = R;
+  e.C = C;
+  e.ldc = ld;
+  return e;
+}
+template <typename T>
+EpRelu2Bwd<T> mk_relu2bwd(const void* U, void* C, int64_t ld) {
+  EpRelu2Bwd<T> e;
+  e.U = static_cast<const T*>(U);
+  e.C = static_cast<T*>(C);
+  e.ldc = ld;
+  return e;
+}
+template <typename T>
+EpSoftcap<T> mk_softcap(void* C, int64_t ld, float cap) {
+  EpSoftcap<T> e;
+  e.C = static_cast<T*>(C);
+  e.ldc = ld;
+  e.cap = cap;
+  return e;
+}
 
 // ------------------------------------------------------------ tile loader
 struct alignas(16) Vec16 {
@@ -149,18 +240,20 @@ struct TileLoader {
       const int v = tid + i * 256;
       T* e = reinterpret_cast<T*>(&raw[i]);
       if (PRE::kActive && ok[i]) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          int64_t mn, k;
-          if (KMAJ) {
-            mn = mn0 + v / (BK / VEC);
-            k = k0 + (v % (BK / VEC)) * VEC + j;
-          } else {
-            k = k0 + v / (ROWS / VEC);
-            mn = mn0 + (v % (ROWS / VEC)) * VEC + j;
-          }
-          e[j] = from_f<T>(pre(to_f(e[j]), mn, k));
+        int64_t mn, k;
+        if (KMAJ) {
+          mn = mn0 + v / (BK / VEC);
+          k = k0 + (v % (BK / VEC)) * VEC;
+        } else {
+          k = k0 + v / (ROWS / VEC);
+          mn = mn0 + (v % (ROWS / VEC)) * VEC;
         }
+        float f[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) f[j] = to_f(e[j]);
+        pre.template vec<KMAJ, VEC>(f, mn, k);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) e[j] = from_f<T>(f[j]);
       }
       if (KMAJ) {
         const int row = v / (BK / VEC), kk = (v % (BK / VEC)) * VEC;
@@ -179,7 +272,7 @@ template <typename T, int BM, int BN, int BK, bool AK, bool BKM, class PA, class
 __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int64_t lda,
                                                    const T* __restrict__ B, int64_t ldb,
                                                    int64_t M, int64_t N, int64_t K, PA pa,
-                                                   PB pb, EP ep, float* rowsum) {
+                                                   PB pb, EP ep, float* rowpart) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int LDK = BK + VEC;
   constexpr int TM = BM / 64, TN = BN / 64;
@@ -194,6 +287,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
 
   TileLoader<T, BM, BK, AK> la;
   TileLoader<T, BN, BK, BKM> lb;
+  pa.init();
+  pb.init();
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -252,20 +347,76 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
       }
       if (EP::kRowSum) {
         rs = half_sum(rs);
-        if ((lane & 31) == 0 && m < M) atomicAdd(rowsum + m, rs);
+        if ((lane & 31) == 0 && m < M) rowpart[m * (2 * gridDim.x) + blockIdx.x * 2 + wn] = rs;
       }
     }
   }
 }
 
 template <typename T, bool AK, bool BKM, class PA, class PB, class EP>
-void run(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
-         int64_t K, PA pa, PB pb, EP ep, float* rowsum, hipStream_t s) {
-  constexpr int BM = 128, BN = 128, BK = sizeof(T) == 2 ? 32 : 16;
+void run_f32(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
+             int64_t K, PA pa, PB pb, EP ep, float* rowpart, hipStream_t s) {
+  constexpr int BM = 128, BN = 128, BK = 16;
   dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
                      static_cast<const T*>(A), lda, static_cast<const T*>(B), ldb, M, N, K, pa,
-                     pb, ep, rowsum);
+                     pb, ep, rowpart);
+}
+
+// ------------------------------------------------------------ bf16 dispatch
+struct Tile {
+  int bm, bn;
+};
+
+// Output tile for a product: the largest tile that still gives the 256 CUs
+// at least one full wave of workgroups.
+static Tile pick_tile(int64_t M, int64_t N) {
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (N % 256 == 0 && tiles(256, 256) >= 512) return {256, 256};
+  if (N % 192 == 0 && tiles(256, 192) >= 256) return {256, 192};
+  if (tiles(256, 128) >= 256) return {256, 128};
+  return {128, 128};
+}
+
+// Tile for a weight gradient (split-K fills the machine instead).
+static Tile pick_tile_wgrad(int64_t M, int64_t N) {
+  if (N % 256 == 0 && M % 256 == 0) return {256, 256};
+  if (N % 192 == 0) return {256, 192};
+  return {256, 128};
+}
+
+// K split so that tiles * splits >= 512 workgroups, chunks >= 256 and a
+// multiple of 32.
+static int64_t pick_kchunk(int64_t tiles, int64_t K, int64_t min_chunk = 256) {
+  int64_t splits = (512 + tiles - 1) / tiles;
+  int64_t chunk = (K + splits - 1) / splits;
+  chunk = std::max<int64_t>(chunk, min_chunk);
+  chunk = (chunk + 31) / 32 * 32;
+  return std::min<int64_t>(chunk, (K + 31) / 32 * 32);
+}
+
+template <int BM, int BN, bool AK, bool BKM, class PA, class PB, class EP>
+void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
+                 int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, float* rowsum, hipStream_t s) {
+  const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+  const int splits = (int)((K + kchunk - 1) / kchunk);
+  dim3 grid((unsigned)(tm * tn), 1, (unsigned)std::max(splits, 1));
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 32, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
+                     static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M, N, K,
+                     kchunk, tm, tn, pa, pb, ep, rowsum);
+}
+
+template <bool AK, bool BKM, class PA, class PB, class EP>
+void run_bf16(Tile t, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
+              int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, float* rowsum, hipStream_t s) {
+  if (t.bm == 256 && t.bn == 256)
+    launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
+  else if (t.bm == 256 && t.bn == 192)
+    launch_bf16<256, 192, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
+  else if (t.bm == 256 && t.bn == 128)
+    launch_bf16<256, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
+  else
+    launch_bf16<128, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
 }
 
 }  // namespace gk
@@ -273,83 +424,117 @@ void run(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int6
 namespace gpt {
 using namespace gk;
 
-#define DISPATCH_T(d, ...)        \
-  if ((d).bf16) {                 \
-    using T = bf16;               \
-    __VA_ARGS__;                  \
-  } else {                        \
-    using T = float;              \
-    __VA_ARGS__;                  \
-  }
-
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s) {
-  DISPATCH_T(d, (run<T, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
-                                    EpStore<T>{static_cast<T*>(C), N}, nullptr, s)));
+  if (d.bf16)
+    run_bf16<true, true>(pick_tile(M, N), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_store<bf16>(C, N), nullptr, s);
+  else
+    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
+                               mk_store<float>(C, N), nullptr, s);
 }
 
 void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    const float* R, float* C, bool relu2_a, hipStream_t s) {
-  if (relu2_a) {
-    DISPATCH_T(d, (run<T, true, true>(A, K, B, K, M, N, K, PreRelu2{}, PreId{},
-                                      EpResid{R, C, N}, nullptr, s)));
+  const Tile t = pick_tile(M, N);
+  if (d.bf16) {
+    if (relu2_a)
+      run_bf16<true, true>(t, A, K, B, K, M, N, K, K, PreRelu2{}, PreId{}, mk_resid(R, C, N),
+                           nullptr, s);
+    else
+      run_bf16<true, true>(t, A, K, B, K, M, N, K, K, PreId{}, PreId{}, mk_resid(R, C, N),
+                           nullptr, s);
   } else {
-    DISPATCH_T(d, (run<T, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
-                                      EpResid{R, C, N}, nullptr, s)));
+    if (relu2_a)
+      run_f32<float, true, true>(A, K, B, K, M, N, K, PreRelu2{}, PreId{}, mk_resid(R, C, N),
+                                 nullptr, s);
+    else
+      run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_resid(R, C, N),
+                                 nullptr, s);
   }
 }
 
-void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                     void* C, float* rowsum, hipStream_t s) {
-  DISPATCH_T(d, (run<T, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
-                                    EpSoftcap<T>{static_cast<T*>(C), N, d.cap, rowsum}, rowsum,
-                                    s)));
+int gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                    void* C, float* rowpart, hipStream_t s) {
+  if (d.bf16) {
+    const Tile t = pick_tile(M, N);
+    run_bf16<true, true>(t, A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_softcap<bf16>(C, N, d.cap), rowpart, s);
+    return 2 * (int)((N + t.bn - 1) / t.bn);
+  }
+  run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
+                             mk_softcap<float>(C, N, d.cap), rowpart, s);
+  return 2 * (int)((N + 127) / 128);
 }
 
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s) {
-  DISPATCH_T(d, (run<T, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{},
-                                     EpStore<T>{static_cast<T*>(C), N}, nullptr, s)));
+  if (d.bf16)
+    run_bf16<true, false>(pick_tile(M, N), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+                          mk_store<bf16>(C, N), nullptr, s);
+  else
+    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{},
+                                mk_store<float>(C, N), nullptr, s);
 }
 
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                  float* C, hipStream_t s) {
-  DISPATCH_T(d, (run<T, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, EpF32{C, N, 0},
-                                     nullptr, s)));
+  if (d.bf16)
+    run_bf16<true, false>(pick_tile(M, N), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+                          mk_f32(C, N, 0), nullptr, s);
+  else
+    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), nullptr,
+                                s);
 }
 
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                       const void* U, void* C, hipStream_t s) {
-  DISPATCH_T(d, (run<T, true, false>(
-                    A, K, B, N, M, N, K, PreId{}, PreId{},
-                    EpRelu2Bwd<T>{static_cast<const T*>(U), static_cast<T*>(C), N}, nullptr, s)));
+  if (d.bf16)
+    run_bf16<true, false>(pick_tile(M, N), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+                          mk_relu2bwd<bf16>(U, C, N),
+                          nullptr, s);
+  else
+    run_f32<float, true, false>(
+        A, K, B, N, M, N, K, PreId{}, PreId{},
+        mk_relu2bwd<float>(U, C, N), nullptr, s);
 }
 
-void gemm_nn_ce(const Dims& d, int64_t M, int N, int K, const void* logits, const void* B,
-                const float* inv_rowsum, const int32_t* tgt, const float* inv_nvalid, float* C,
-                hipStream_t s) {
-  PreCE pre{inv_rowsum, tgt, inv_nvalid, d.cap, 1};
-  DISPATCH_T(d, (run<T, true, false>(logits, K, B, N, M, N, K, pre, PreId{}, EpF32{C, N, 0},
-                                     nullptr, s)));
+void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                        float* C, hipStream_t s) {
+  if (d.bf16) {
+    const Tile t = pick_tile(M, N);
+    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const int64_t kc = pick_kchunk(tiles, K, 4096);
+    launch_zero(C, M * N, s);
+    run_bf16<true, false>(t, A, K, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), nullptr,
+                          s);
+  } else {
+    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), nullptr,
+                                s);
+  }
 }
 
 void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
                    float* C, bool accumulate, bool relu2_b, hipStream_t s) {
-  if (relu2_b) {
-    DISPATCH_T(d, (run<T, false, false>(A, M, B, N, M, N, K, PreId{}, PreRelu2{},
-                                        EpF32{C, N, accumulate ? 1 : 0}, nullptr, s)));
+  if (d.bf16) {
+    const Tile t = pick_tile_wgrad(M, N);
+    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const int64_t kc = pick_kchunk(tiles, K);
+    if (!accumulate) launch_zero(C, (int64_t)M * N, s);
+    if (relu2_b)
+      run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreRelu2{}, mk_atomic(C, N),
+                             nullptr, s);
+    else
+      run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N),
+                             nullptr, s);
   } else {
-    DISPATCH_T(d, (run<T, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
-                                        EpF32{C, N, accumulate ? 1 : 0}, nullptr, s)));
+    if (relu2_b)
+      run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreRelu2{},
+                                   mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
+    else
+      run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
+                                   mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
   }
-}
-
-void gemm_tn_wgrad_ce(const Dims& d, int M, int N, int64_t K, const void* logits, const void* B,
-                      const float* inv_rowsum, const int32_t* tgt, const float* inv_nvalid,
-                      float* C, bool accumulate, hipStream_t s) {
-  PreCE pre{inv_rowsum, tgt, inv_nvalid, d.cap, 0};
-  DISPATCH_T(d, (run<T, false, false>(logits, M, B, N, M, N, K, pre, PreId{},
-                                      EpF32{C, N, accumulate ? 1 : 0}, nullptr, s)));
 }
 
 }  // namespace gpt

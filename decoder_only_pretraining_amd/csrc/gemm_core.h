@@ -1,0 +1,275 @@
+// bf16 MFMA GEMM core for gfx950: C[M][N] = sum_k A(m,k) * B(n,k), fp32
+// accumulation, templated on the block tile, the operand layouts, operand
+// prologues and the output epilogue.
+//
+// Operand layouts. A "K-major" operand stores rows of the contraction index
+// (row m holds A(m, k) contiguously); an "MN-major" operand stores rows of
+// the output index (row k holds A(m, k) contiguously). Activations enter the
+// weight-gradient products MN-major (the contraction runs over tokens).
+//
+// LDS. K-major tiles are kept as [rows][BK] with 16-byte granules XOR-
+// swizzled by row, so both the global->LDS writes and the MFMA fragment
+// reads (one 16-byte read per lane) are free of bank conflicts. MN-major
+// tiles are kept as they are in memory, [BK][rows + 32] (the pad spreads
+// four consecutive k rows over all 64 banks), and fragments are read with
+// the gfx950 transposing LDS load ds_read_b64_tr_b16: within a 16-lane
+// group, source lane 4q + a addresses T[k0 + q][m0 + 4a .. +3] and output
+// lane i receives T[k0 .. k0 + 3][m0 + i], i.e. four consecutive
+// contraction slots of one output row. Two such loads make the 8-slot
+// fragment of v_mfma_f32_32x32x16_bf16.
+//
+// Block: 256 threads = 4 wavefronts in a 2x2 grid; each wavefront owns a
+// (BM/2) x (BN/2) accumulator tile of 32x32 MFMA blocks. Two LDS stages:
+// global loads for stage k+1 are issued before the MFMAs of stage k. The
+// epilogue reuses the LDS to turn the MFMA accumulator layout (four rows by
+// one column per lane) into row-contiguous 4-column vectors for the global
+// stores and the loads of epilogue operands.
+//
+// Grid: blockIdx.x enumerates output tiles, blockIdx.z splits K. Tile order
+// is XCD-aware: the dispatcher deals consecutive workgroups to the 8 XCDs in
+// turn, so the linear id is remapped to give each XCD a contiguous range of
+// tiles, walked in groups of 8 tile rows that share B panels in its L2.
+#pragma once
+#include "device_common.h"
+
+namespace gk {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+struct alignas(16) U128 {
+  uint32_t w[4];
+};
+
+template <int ROWS, int BK, bool KMAJ>
+struct TileGeom {
+  static constexpr int G = BK / 8;               // 16-byte granules per K-major row
+  static constexpr int RPS = 16 / G;             // K-major rows per 256 bytes
+  static constexpr int PITCH = ROWS + 32;        // MN-major row pitch (elements)
+  static constexpr int ELEMS = KMAJ ? ROWS * BK : BK * PITCH;
+  static constexpr int NV = ROWS * BK / 8 / 256; // 16-byte vectors per thread per stage
+  static_assert(NV >= 1, "tile too small");
+  __device__ static __forceinline__ int kmaj_off(int r, int g) {
+    return r * BK + ((g ^ ((r / RPS) & (G - 1))) << 3);
+  }
+};
+
+template <int ROWS, int BK, bool KMAJ>
+struct Loader {
+  using Geo = TileGeom<ROWS, BK, KMAJ>;
+  U128 raw[Geo::NV];
+  bool ok[Geo::NV];
+
+  __device__ __forceinline__ void load(const bf16* __restrict__ p, int64_t ld, int64_t mn0,
+                                       int64_t MN, int64_t k0, int64_t khi, int tid) {
+#pragma unroll
+    for (int i = 0; i < Geo::NV; ++i) {
+      const int v = tid + i * 256;
+      int64_t mn, k;
+      if (KMAJ) {
+        mn = mn0 + v / Geo::G;
+        k = k0 + (v % Geo::G) * 8;
+      } else {
+        k = k0 + v / (ROWS / 8);
+        mn = mn0 + (v % (ROWS / 8)) * 8;
+      }
+      ok[i] = (mn < MN) && (k < khi);
+      if (ok[i])
+        raw[i] = *reinterpret_cast<const U128*>(KMAJ ? p + mn * ld + k : p + k * ld + mn);
+      else
+        raw[i] = U128{{0, 0, 0, 0}};
+    }
+  }
+
+  template <class PRE>
+  __device__ __forceinline__ void store(bf16* lds, int64_t mn0, int64_t k0, int tid,
+                                        const PRE& pre) {
+#pragma unroll
+    for (int i = 0; i < Geo::NV; ++i) {
+      const int v = tid + i * 256;
+      if (PRE::kActive && ok[i]) {
+        bf16* e = reinterpret_cast<bf16*>(&raw[i]);
+        int64_t mn, k;
+        if (KMAJ) {
+          mn = mn0 + v / Geo::G;
+          k = k0 + (v % Geo::G) * 8;
+        } else {
+          k = k0 + v / (ROWS / 8);
+          mn = mn0 + (v % (ROWS / 8)) * 8;
+        }
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = static_cast<float>(e[j]);
+        pre.template vec<KMAJ, 8>(f, mn, k);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = static_cast<bf16>(f[j]);
+      }
+      int off;
+      if (KMAJ)
+        off = Geo::kmaj_off(v / Geo::G, v % Geo::G);
+      else
+        off = (v / (ROWS / 8)) * Geo::PITCH + (v % (ROWS / 8)) * 8;
+      *reinterpret_cast<U128*>(lds + off) = raw[i];
+    }
+  }
+};
+
+// Fragment of 32 operand rows starting at `row0` for the 16-wide
+// contraction slice `ks` (lane l: row row0 + l%32, slots 8*(l/32) .. +7).
+template <int ROWS, int BK, bool KMAJ>
+__device__ __forceinline__ void read_frag(Frag<bf16>& f, const bf16* lds, int row0, int ks,
+                                          int lane) {
+  using Geo = TileGeom<ROWS, BK, KMAJ>;
+  if (KMAJ) {
+    const int r = row0 + (lane & 31);
+    const int g = (lane >> 5) + 2 * ks;
+    f.v = *reinterpret_cast<const bf16x8*>(lds + Geo::kmaj_off(r, g));
+  } else {
+    const int g16 = lane >> 4, L = lane & 15;
+    const int k = ks * 16 + (g16 >> 1) * 8 + (L >> 2);
+    const int m = row0 + (g16 & 1) * 16 + (L & 3) * 4;
+    const bf16* p0 = lds + k * Geo::PITCH + m;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * Geo::PITCH));
+    union {
+      struct { v4i16 a, b; } s;
+      bf16x8 v;
+    } u;
+    u.s.a = lo;
+    u.s.b = hi;
+    f.v = u.v;
+  }
+}
+
+template <int BM, int BN, int BK, bool AK, bool BKM, class PA, class PB, class EP>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(
+    const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
+    int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep,
+    float* rowpart) {
+  using GA = TileGeom<BM, BK, AK>;
+  using GB = TileGeom<BN, BK, BKM>;
+  constexpr int TM = BM / 64, TN = BN / 64;
+  constexpr int WN = BN / 2;
+  constexpr int SP = WN + 4;  // epilogue staging row pitch (floats)
+  constexpr int MAIN_BYTES = 2 * (GA::ELEMS + GB::ELEMS) * 2;
+  constexpr int STAGE_BYTES = 4 * 32 * SP * 4;
+  __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES];
+  bf16 (*As)[GA::ELEMS] = reinterpret_cast<bf16 (*)[GA::ELEMS]>(smem);
+  bf16 (*Bs)[GB::ELEMS] = reinterpret_cast<bf16 (*)[GB::ELEMS]>(smem + 2 * GA::ELEMS * 2);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // XCD-aware, grouped tile order
+  int pid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  constexpr int GM = 8;
+  const int group = pid / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % (GM * tiles_n)) % gsize;
+  const int tn = (pid % (GM * tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t k_lo = (int64_t)blockIdx.z * kchunk;
+  const int64_t k_hi = min(K, k_lo + kchunk);
+
+  Loader<BM, BK, AK> la;
+  Loader<BN, BK, BKM> lb;
+  pa.init();
+  pb.init();
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int64_t nk = (k_hi - k_lo + BK - 1) / BK;
+  if (nk > 0) {
+    la.load(A, lda, m0, M, k_lo, k_hi, tid);
+    lb.load(B, ldb, n0, N, k_lo, k_hi, tid);
+    la.store(As[0], m0, k_lo, tid, pa);
+    lb.store(Bs[0], n0, k_lo, tid, pb);
+  }
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    const int64_t kn = k_lo + (kt + 1) * BK;
+    if (more) {
+      la.load(A, lda, m0, M, kn, k_hi, tid);
+      lb.load(B, ldb, n0, N, kn, k_hi, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      Frag<bf16> a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) read_frag<BM, BK, AK>(a[i], As[cur], wm * (BM / 2) + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) read_frag<BN, BK, BKM>(b[j], Bs[cur], wn * (BN / 2) + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) mfma(acc[i][j], a[i], b[j]);
+    }
+    if (more) {
+      la.store(As[cur ^ 1], m0, kn, tid, pa);
+      lb.store(Bs[cur ^ 1], n0, kn, tid, pb);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue, one 32-row slab of the wavefront tile at a time: transform
+  // the accumulators in their MFMA layout (row sums for the softcap), stage
+  // the slab in LDS as fp32, then write it back with 4-column vectors.
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SP;
+  const int64_t mw = m0 + wm * (BM / 2), nw = n0 + wn * WN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = acc_row(e, lane);
+      const int64_t m = mw + i * 32 + r;
+      float rs = 0.0f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t n = nw + j * 32 + (lane & 31);
+        const float v = ep.value(m, n, acc[i][j][e]);
+        if (EP::kRowSum && m < M && n < N) rs += ep.rowterm(v);
+        stage[r * SP + j * 32 + (lane & 31)] = v;
+      }
+      if (EP::kRowSum) {  // deterministic per-(tile, wavefront column) partials
+        rs = half_sum(rs);
+        if ((lane & 31) == 0 && m < M) rowpart[m * (2 * tiles_n) + tn * 2 + wn] = rs;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (EP::kScalar) {
+      // one column per lane: consecutive lanes hit consecutive addresses
+#pragma unroll
+      for (int v = lane; v < 32 * WN; v += 64) {
+        const int r = v / WN, cc = v % WN;
+        const int64_t m = mw + i * 32 + r, n = nw + cc;
+        if (m < M && n < N) ep.store1(m, n, stage[r * SP + cc]);
+      }
+    } else {
+#pragma unroll
+      for (int v = lane; v < 32 * WN / 4; v += 64) {
+        const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+        const int64_t m = mw + i * 32 + r, n = nw + c4;
+        if (m < M && n < N) {
+          const f32x4 val = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
+          ep.store4(m, n, val, (int)min<int64_t>(4, N - n));
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace gk

@@ -175,7 +175,6 @@ Plan make_plan(const Dims& d) {
   p.rope = take((size_t)d.T * d.D * 4);
   p.x = take((size_t)(d.L + 1) * N * d.C * 4);
   p.xin = take(N * d.C * 4);
-  p.xmid = take(N * d.C * 4);
   // per-layer saved activations
   size_t lo = 0;
   auto ltake = [&](size_t bytes) {
@@ -190,6 +189,7 @@ Plan make_plan(const Dims& d) {
   p.l_a = ltake(N * d.Hk * 4);
   p.l_attn = ltake(N * d.Cq * A);
   p.l_lse = ltake(N * d.H * 4);
+  p.l_xmid = ltake(N * d.C * 4);
   p.l_xn2 = ltake(N * d.C * A);
   p.l_r2 = ltake(N * 4);
   p.l_u = ltake(N * d.F * A);
@@ -198,7 +198,9 @@ Plan make_plan(const Dims& d) {
   p.xf = take(N * d.C * A);
   p.rf = take(N * 4);
   p.logits = take(N * d.V * A);
-  p.rowsum = take(N * 4);
+  p.rowparts = d.V / 64;  // two partials per column tile of >= 128
+  p.rowpart = take(N * p.rowparts * 4);
+  p.lossrow = take(N * 4);
   p.scalars = take(256);
   p.gx = take(N * d.C * 4);
   p.gxc = take(N * d.C * A);
@@ -211,7 +213,7 @@ Plan make_plan(const Dims& d) {
   p.ga = take(N * d.Hk * 4);
   p.lam_blocks = (int)((d.N + 3) / 4);
   p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
-  p.veg_splits = 64;
+  p.veg_splits = 256;
   p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
   p.total = o;
   return p;
@@ -294,7 +296,6 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   auto X = [&](int l) { return reinterpret_cast<float*>(W + P.x) + (size_t)l * xstride; };
   auto LY = [&](int l, size_t off) { return W + P.layers + (size_t)l * P.layer_bytes + off; };
   float* xin = reinterpret_cast<float*>(W + P.xin);
-  float* xmid = reinterpret_cast<float*>(W + P.xmid);
   const int64_t N = d.N;
 
   site("embed.fwd", s, [&] { launch_embed(params + F.wte, tokens, X(0), N, d.C, s); });
@@ -307,6 +308,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     float* a = reinterpret_cast<float*>(LY(l, P.l_a));
     void* att = LY(l, P.l_attn);
     float* lse = reinterpret_cast<float*>(LY(l, P.l_lse));
+    float* xmid = reinterpret_cast<float*>(LY(l, P.l_xmid));
     void* xn2 = LY(l, P.l_xn2);
     float* r2 = reinterpret_cast<float*>(LY(l, P.l_r2));
     void* u = LY(l, P.l_u);
@@ -323,12 +325,15 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   void* xf = W + P.xf;
   float* rf = reinterpret_cast<float*>(W + P.rf);
   void* logits = W + P.logits;
-  float* rowsum = reinterpret_cast<float*>(W + P.rowsum);
+  float* rowpart = reinterpret_cast<float*>(W + P.rowpart);
+  float* lossrow = reinterpret_cast<float*>(W + P.lossrow);
   float* scalars = reinterpret_cast<float*>(W + P.scalars);
   launch_mix_norm(d, X(d.L), nullptr, nullptr, nullptr, nullptr, xf, rf, nullptr, nullptr, s);
-  launch_zero(rowsum, N, s);
-  site("gemm.lm.fwd", s, [&] { gemm_nt_softcap(d, N, d.V, d.C, xf, wmat(F.lm), logits, rowsum, s); });
-  site("loss", s, [&] { launch_loss(d, logits, targets, rowsum, scalars, loss, s); });  // rowsum -> 1 / rowsum
+  int nparts = 0;
+  launch_count_valid(d, targets, scalars, s);
+  site("gemm.lm.fwd", s, [&] { nparts = gemm_nt_softcap(d, N, d.V, d.C, xf, wmat(F.lm), logits, rowpart, s); });
+  // the loss; in a backward call the logits become the logit gradient g_z
+  site("loss", s, [&] { launch_loss(d, logits, targets, rowpart, nparts, scalars, lossrow, loss, backward, s); });
 
   if (backward) {
     const bool acc = d.accumulate;
@@ -349,12 +354,12 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     float* lam_part = reinterpret_cast<float*>(W + P.lam_part);
     float* veg_part = reinterpret_cast<float*>(W + P.veg_part);
 
-    site("gemm.lm.dgrad", s, [&] { gemm_nn_ce(d, N, d.C, d.V, logits, wmat(F.lm), rowsum, targets, scalars, gtmp, s); });
-    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad_ce(d, d.V, d.C, N, logits, xf, rowsum, targets, scalars, grads + F.lm, acc, s); });
+    site("gemm.lm.dgrad", s, [&] { gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, s); });
+    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, false, s); });
     NormBwdArgs nb{};
     nb.mode = NB_FINAL;
     nb.gin = gtmp;
-    nb.y = xf;
+    nb.ysrc = X(d.L);
     nb.r = rf;
     nb.gx = gx;
     nb.gxc = d.bf16 ? gxc : nullptr;
@@ -368,6 +373,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       const float* a = reinterpret_cast<const float*>(LY(l, P.l_a));
       const void* att = LY(l, P.l_attn);
       const float* lse = reinterpret_cast<const float*>(LY(l, P.l_lse));
+      const float* xmid = reinterpret_cast<const float*>(LY(l, P.l_xmid));
       const void* xn2 = LY(l, P.l_xn2);
       const float* r2 = reinterpret_cast<const float*>(LY(l, P.l_r2));
       const void* u = LY(l, P.l_u);
@@ -379,7 +385,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       nb = NormBwdArgs{};
       nb.mode = NB_NORM2;
       nb.gin = gtmp;
-      nb.y = xn2;
+      nb.ysrc = xmid;
       nb.r = r2;
       nb.gx = gx;
       nb.gxc = d.bf16 ? gxc : nullptr;
@@ -397,7 +403,6 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       nb = NormBwdArgs{};
       nb.mode = NB_NORM1;
       nb.gin = gtmp;
-      nb.y = xn;
       nb.r = r1;
       nb.gx = gx;
       nb.gxc = d.bf16 ? gxc : nullptr;
@@ -490,23 +495,52 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
   if (!name || !offset || !bytes) return fail(GPT_E_NULLPTR, "pointer is NULL");
   const Dims d = make_dims(*cfg);
   const Plan P = make_plan(d);
-  const size_t N = (size_t)d.N, A = (size_t)d.act_bytes;
+  const size_t N = (size_t)d.N, A = (size_t)d.act_bytes, C = (size_t)d.C;
   const std::string n(name);
+  struct R {
+    const char* name;
+    size_t off, bytes;
+  };
   if (n == "x") {
     if (layer < 0 || layer > d.L) return fail(GPT_E_INVAL, "layer out of range");
-    *offset = P.x + (size_t)layer * N * d.C * 4;
-    *bytes = N * d.C * 4;
+    *offset = P.x + (size_t)layer * N * C * 4;
+    *bytes = N * C * 4;
     return GPT_OK;
   }
-  if (n == "xf") { *offset = P.xf; *bytes = N * d.C * A; return GPT_OK; }
-  if (n == "logits") { *offset = P.logits; *bytes = N * d.V * A; return GPT_OK; }
-  if (layer < 0 || layer >= d.L) return fail(GPT_E_INVAL, "layer out of range");
-  const size_t base = P.layers + (size_t)layer * P.layer_bytes;
-  if (n == "xn") { *offset = base + P.l_xn; *bytes = N * d.C * A; return GPT_OK; }
-  if (n == "qkv") { *offset = base + P.l_qkv; *bytes = N * d.Qkv * A; return GPT_OK; }
-  if (n == "attn") { *offset = base + P.l_attn; *bytes = N * d.Cq * A; return GPT_OK; }
-  if (n == "xn2") { *offset = base + P.l_xn2; *bytes = N * d.C * A; return GPT_OK; }
-  if (n == "u") { *offset = base + P.l_u; *bytes = N * d.F * A; return GPT_OK; }
+  const R global[] = {
+      {"wc", P.wc, d.bf16 ? (P.rope - P.wc) : 0}, {"rope", P.rope, (size_t)d.T * d.D * 4},
+      {"xin", P.xin, N * C * 4}, {"xf", P.xf, N * C * A}, {"rf", P.rf, N * 4},
+      {"logits", P.logits, N * d.V * A}, {"rowpart", P.rowpart, N * P.rowparts * 4},
+{"lossrow", P.lossrow, N * 4}, {"scalars", P.scalars, 256},
+      {"gx", P.gx, N * C * 4}, {"gxc", P.gxc, N * C * A}, {"gx0", P.gx0, N * C * 4},
+      {"gu", P.gu, N * d.F * A}, {"gtmp", P.gtmp, N * C * 4}, {"gO", P.gO, N * d.Cq * A},
+      {"gqkv", P.gqkv, N * d.Qkv * A}, {"delta", P.delta, N * d.H * 4},
+      {"ga", P.ga, N * d.Hk * 4}, {"lam_part", P.lam_part, (size_t)d.L * P.lam_blocks * 8},
+      {"veg_part", P.veg_part, (size_t)P.veg_splits * d.Hk * C * 4}};
+  for (const R& r : global)
+    if (n == r.name) {
+      *offset = r.off;
+      *bytes = r.bytes;
+      return GPT_OK;
+    }
+  const R per_layer[] = {{"xn", P.l_xn, N * C * A},
+                         {"r1", P.l_r1, N * 4},
+                         {"qkv", P.l_qkv, N * d.Qkv * A},
+                         {"rqk", P.l_rqk, N * (d.H + d.Hk) * 4},
+                         {"a", P.l_a, N * d.Hk * 4},
+                         {"attn", P.l_attn, N * d.Cq * A},
+                         {"lse", P.l_lse, N * d.H * 4},
+                         {"xmid", P.l_xmid, N * C * 4},
+                         {"xn2", P.l_xn2, N * C * A},
+                         {"r2", P.l_r2, N * 4},
+                         {"u", P.l_u, N * d.F * A}};
+  for (const R& r : per_layer)
+    if (n == r.name) {
+      if (layer < 0 || layer >= d.L) return fail(GPT_E_INVAL, "layer out of range");
+      *offset = P.layers + (size_t)layer * P.layer_bytes + r.off;
+      *bytes = r.bytes;
+      return GPT_OK;
+    }
   return fail(GPT_E_INVAL, "unknown region '%s'", name);
 }
 

@@ -38,11 +38,12 @@ struct Plan {
   size_t wc;            // compute-dtype mirror of params (bf16 only)
   size_t rope;          // fp32 cos [T][D/2], sin [T][D/2]
   size_t x;             // fp32 [(L+1)][N][C] residual stream per layer boundary
-  size_t xin, xmid;     // fp32 [N][C] scratch
+  size_t xin;           // fp32 [N][C] scratch
   // per layer, stride `layer_bytes`, starting at `layers`
   size_t layers, layer_bytes;
-  size_t l_xn, l_r1, l_qkv, l_rqk, l_a, l_attn, l_lse, l_xn2, l_r2, l_u;
-  size_t xf, rf, logits, rowsum, scalars;
+  size_t l_xn, l_r1, l_qkv, l_rqk, l_a, l_attn, l_lse, l_xmid, l_xn2, l_r2, l_u;
+  size_t xf, rf, logits, rowpart, lossrow, scalars;
+  int rowparts;         // max row-sum partials per token
   size_t gx, gxc, gx0, gu, gtmp, gO, gqkv, delta, ga, lam_part, veg_part;
   int lam_blocks, veg_splits;
   size_t total;
@@ -85,14 +86,16 @@ enum NormBwdMode { NB_FINAL = 0, NB_NORM2 = 1, NB_NORM1 = 2 };
 struct NormBwdArgs {
   int mode;
   const float* gin;     // fp32 [N][C] gradient w.r.t. the norm output
-  const void* y;        // act [N][C] norm output
+  const float* ysrc;    // fp32 [N][C] norm input (NB_FINAL, NB_NORM2); the norm
+                        // output is recomputed as ysrc * r in fp32
   const float* r;       // fp32 [N]
   float* gx;            // fp32 [N][C] residual gradient (in/out)
   void* gxc;            // act [N][C] copy of the new gx (may be null)
+  int gxc_bf16;         // set by the launcher
   // NB_NORM1 only
   const float* ga;      // fp32 [N][Hk] or null
   const float* wg;      // fp32 [Hk][C] or null
-  const float* x;       // fp32 [N][C] block input
+  const float* x;       // fp32 [N][C] block input (norm input = lr * x + l0 * x0)
   const float* x0;      // fp32 [N][C]
   const float* lam_r;   // device scalar
   const float* lam_0;
@@ -107,8 +110,14 @@ void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, floa
                             float* g_l0, hipStream_t s);
 void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* part,
                       int splits, float* gwg, hipStream_t s);
-void launch_loss(const Dims& d, const void* logits, const int32_t* tgt, float* rowsum,
-                 float* scalars, float* loss, hipStream_t s);
+// 1 / n_valid into scalars[0].
+void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipStream_t s);
+// Softcap cross-entropy loss from the stored logits and the per-tile row sums
+// of exp(c - cap) (nparts per token, summed in a fixed order); with `grad`
+// the logits are overwritten in place by the logit gradient of the mean loss.
+void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* rowpart,
+                 int nparts, const float* scalars, float* lossrow, float* loss, bool grad,
+                 hipStream_t s);
 void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t N, int C,
                       hipStream_t s);
 
@@ -121,23 +130,22 @@ void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const 
                    void* C, hipStream_t s);
 void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    const float* R, float* C, bool relu2_a, hipStream_t s);
-void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                     void* C, float* rowsum, hipStream_t s);
+// Softcapped logits; row sums of exp(c - cap) as per-tile partials
+// rowpart[m * P + j], j < P; returns P.
+int gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                    void* C, float* rowpart, hipStream_t s);
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s);
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                  float* C, hipStream_t s);
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                       const void* U, void* C, hipStream_t s);
-// A = softcap-CE logit gradient computed on load from logits [M][K].
-void gemm_nn_ce(const Dims& d, int64_t M, int N, int K, const void* logits, const void* B,
-                const float* inv_rowsum, const int32_t* tgt, const float* inv_nvalid,
-                float* C, hipStream_t s);
-// Weight gradients. relu2_b: B = relu(B)^2 on load. ce_a: A from logits.
+// Like gemm_nn_f32 for a long contraction: K split across workgroups, C
+// zeroed and accumulated with fp32 atomics.
+void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                        float* C, hipStream_t s);
+// Weight gradients C[M][N] (+)= sum_k A[k][m] B[k][n]; relu2_b: B = relu(B)^2 on load.
 void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
                    float* C, bool accumulate, bool relu2_b, hipStream_t s);
-void gemm_tn_wgrad_ce(const Dims& d, int M, int N, int64_t K, const void* logits,
-                      const void* B, const float* inv_rowsum, const int32_t* tgt,
-                      const float* inv_nvalid, float* C, bool accumulate, hipStream_t s);
 
 }  // namespace gpt

@@ -10,7 +10,6 @@
 
 namespace gk {
 
-constexpr int kMaxC4 = 8;  // n_embd <= 64 lanes * 8 float4 = 2048
 
 // ------------------------------------------------------------ cast / zero
 struct CastTable {
@@ -109,7 +108,7 @@ __device__ __forceinline__ f32x4 round4(const f32x4& v, bf16) {
   return r;
 }
 
-template <typename T>
+template <typename T, int NC>
 __global__ __launch_bounds__(256) void mix_norm_kernel(
     const float* __restrict__ x, const float* __restrict__ x0, const float* __restrict__ lam_r,
     const float* __restrict__ lam_0, float* __restrict__ xin_out, T* __restrict__ y,
@@ -120,10 +119,10 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
   if (n >= N) return;
   const int C4 = C / 4;
   const float lr = x0 ? lam_r[0] : 1.0f, l0 = x0 ? lam_0[0] : 0.0f;
-  f32x4 v[kMaxC4];
+  f32x4 v[NC];
   float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxC4; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const int c4 = lane + i * 64;
     if (c4 < C4) {
       f32x4 xv = reinterpret_cast<const f32x4*>(x + n * C)[c4];
@@ -139,76 +138,90 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)C + eps);
   if (lane == 0) r_out[n] = r;
-  float gdot[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) gdot[j] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMaxC4; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const int c4 = lane + i * 64;
     if (c4 < C4) {
-      const f32x4 yv = v[i] * r;
-      store4<T>(y + n * C + c4 * 4, yv);
-      if (wg) {
-        const f32x4 yr = round4(yv, T{});
-        for (int j = 0; j < hk; ++j) {
-          const f32x4 w = reinterpret_cast<const f32x4*>(wg + (int64_t)j * C)[c4];
-          gdot[j] += yr[0] * w[0] + yr[1] * w[1] + yr[2] * w[2] + yr[3] * w[3];
-        }
-      }
+      v[i] = round4(v[i] * r, T{});
+      store4<T>(y + n * C + c4 * 4, v[i]);
     }
   }
-  if (wg) {
+  if (wg) {  // gate logits from the rounded norm output, one KV head at a time
     for (int j = 0; j < hk; ++j) {
-      const float s = wave_sum(gdot[j]);
-      if (lane == 0) a[n * hk + j] = s;
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c4 = lane + i * 64;
+        if (c4 < C4) {
+          const f32x4 w = reinterpret_cast<const f32x4*>(wg + (int64_t)j * C)[c4];
+          dot += v[i][0] * w[0] + v[i][1] * w[1] + v[i][2] * w[2] + v[i][3] * w[3];
+        }
+      }
+      dot = wave_sum(dot);
+      if (lane == 0) a[n * hk + j] = dot;
     }
   }
 }
 
 // ------------------------------------------------------------ norm backward
-template <typename T>
+// g_in -> g w.r.t. the norm input: r * (g - y * mean(g * y)), with the norm
+// output y recomputed in fp32 from the fp32 norm input, so the result is
+// orthogonal to that input to fp32 precision (the lambda gradients are
+// projections on it).
+template <int NC>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(gpt::NormBwdArgs p, int64_t N, int C,
                                                        int hk) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int64_t n = (int64_t)blockIdx.x * 4 + wv;
   const int C4 = C / 4;
-  const T* y = static_cast<const T*>(p.y);
-  T* gxc = static_cast<T*>(p.gxc);
   __shared__ float part[4][2];
   float s_lr = 0.0f, s_l0 = 0.0f;
+  const bool norm1 = p.mode == gpt::NB_NORM1;
   if (n < N) {
-    f32x4 g[kMaxC4], yv[kMaxC4];
-    float ga[16];
-    if (p.mode == gpt::NB_NORM1 && p.ga) {
-      for (int j = 0; j < hk; ++j) ga[j] = p.ga[n * hk + j];
-    }
+    f32x4 g[NC], yv[NC];
+    const float r = p.r[n];
+    const float lr = norm1 ? p.lam_r[0] : 1.0f;
+    const float l0 = norm1 ? p.lam_0[0] : 0.0f;
     float dot = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxC4; ++i) {
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) g[i] = reinterpret_cast<const f32x4*>(p.gin + n * C)[c4];
+    }
+    if (norm1 && p.ga) {  // the value-embedding gate's share: g += sum_j ga[j] * wg[j]
+      for (int j = 0; j < hk; ++j) {
+        const float gj = p.ga[n * hk + j];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c4 = lane + i * 64;
+          if (c4 < C4) g[i] += gj * reinterpret_cast<const f32x4*>(p.wg + (int64_t)j * C)[c4];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
       const int c4 = lane + i * 64;
       if (c4 < C4) {
-        f32x4 gv = reinterpret_cast<const f32x4*>(p.gin + n * C)[c4];
-        if (p.mode == gpt::NB_NORM1 && p.ga) {
-          for (int j = 0; j < hk; ++j)
-            gv += ga[j] * reinterpret_cast<const f32x4*>(p.wg + (int64_t)j * C)[c4];
-        }
-        g[i] = gv;
-        yv[i] = load4<T>(y + n * C + c4 * 4);
+        const f32x4 gv = g[i];
+        f32x4 src;
+        if (norm1)
+          src = lr * reinterpret_cast<const f32x4*>(p.x + n * C)[c4] +
+                l0 * reinterpret_cast<const f32x4*>(p.x0 + n * C)[c4];
+        else
+          src = reinterpret_cast<const f32x4*>(p.ysrc + n * C)[c4];
+        yv[i] = src * r;
         dot += gv[0] * yv[i][0] + gv[1] * yv[i][1] + gv[2] * yv[i][2] + gv[3] * yv[i][3];
       }
     }
     dot = wave_sum(dot) / (float)C;
-    const float r = p.r[n];
-    const float lr = p.mode == gpt::NB_NORM1 ? p.lam_r[0] : 1.0f;
-    const float l0 = p.mode == gpt::NB_NORM1 ? p.lam_0[0] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxC4; ++i) {
+    for (int i = 0; i < NC; ++i) {
       const int c4 = lane + i * 64;
       if (c4 < C4) {
         f32x4 gx = r * (g[i] - yv[i] * dot);
         if (p.mode != gpt::NB_FINAL) gx += reinterpret_cast<const f32x4*>(p.gx + n * C)[c4];
-        if (p.mode == gpt::NB_NORM1) {
+        if (norm1) {
           // gx is now the gradient w.r.t. xin = lr * x + l0 * x0
           const f32x4 xv = reinterpret_cast<const f32x4*>(p.x + n * C)[c4];
           const f32x4 zv = reinterpret_cast<const f32x4*>(p.x0 + n * C)[c4];
@@ -220,18 +233,23 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(gpt::NormBwdArgs p, int64
           reinterpret_cast<f32x4*>(p.gx0 + n * C)[c4] = g0;
           gx = lr * gx;
         }
-        if (!(p.mode == gpt::NB_NORM1 && p.last_layer0)) {
+        if (!(norm1 && p.last_layer0)) {
           reinterpret_cast<f32x4*>(p.gx + n * C)[c4] = gx;
-          if (gxc) store4<T>(gxc + n * C + c4 * 4, gx);
+          if (p.gxc) {
+            if (p.gxc_bf16)
+              store4<bf16>(static_cast<bf16*>(p.gxc) + n * C + c4 * 4, gx);
+            else
+              store4<float>(static_cast<float*>(p.gxc) + n * C + c4 * 4, gx);
+          }
         }
       }
     }
-    if (p.mode == gpt::NB_NORM1) {
+    if (norm1) {
       s_lr = wave_sum(s_lr);
       s_l0 = wave_sum(s_l0);
     }
   }
-  if (p.mode == gpt::NB_NORM1) {
+  if (norm1) {
     if (lane == 0) {
       part[wv][0] = s_lr;
       part[wv][1] = s_l0;
@@ -396,44 +414,91 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(
 }
 
 // ------------------------------------------------------------ loss
-// Per token: lse = cap + log(sum exp(c - cap)); loss_n = lse - c[y]. Writes
-// 1/rowsum per token and 1/n_valid for the logit-gradient prologue, then the
-// mean loss. One block; fixed-order reduction in double.
-template <typename T>
-__global__ __launch_bounds__(1024) void loss_kernel(const T* __restrict__ logits,
-                                                    const int32_t* __restrict__ tgt,
-                                                    float* __restrict__ rowsum,
-                                                    float* __restrict__ scalars,
-                                                    float* __restrict__ loss, int64_t N, int V,
-                                                    float cap) {
-  __shared__ double s_loss[1024];
+// 1 / n_valid (scalars[0]) from the targets; one block.
+__global__ __launch_bounds__(1024) void count_valid_kernel(const int32_t* __restrict__ tgt,
+                                                           float* __restrict__ scalars, int64_t N) {
   __shared__ int s_cnt[1024];
-  double acc = 0.0;
   int cnt = 0;
-  for (int64_t n = threadIdx.x; n < N; n += 1024) {
-    const float rs = rowsum[n];
-    const int y = tgt[n];
-    if (y >= 0) {
-      acc += (double)cap + log((double)rs) - (double)to_f(logits[n * V + y]);
-      ++cnt;
-    }
-    rowsum[n] = 1.0f / rs;
-  }
-  s_loss[threadIdx.x] = acc;
+  for (int64_t n = threadIdx.x; n < N; n += 1024) cnt += tgt[n] >= 0 ? 1 : 0;
   s_cnt[threadIdx.x] = cnt;
   __syncthreads();
   for (int s = 512; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      s_loss[threadIdx.x] += s_loss[threadIdx.x + s];
-      s_cnt[threadIdx.x] += s_cnt[threadIdx.x + s];
-    }
+    if (threadIdx.x < s) s_cnt[threadIdx.x] += s_cnt[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    const int nv = s_cnt[0] > 0 ? s_cnt[0] : 1;
-    loss[0] = (float)(s_loss[0] / nv);
-    scalars[0] = 1.0f / (float)nv;
+  if (threadIdx.x == 0) scalars[0] = 1.0f / (float)(s_cnt[0] > 0 ? s_cnt[0] : 1);
+}
+
+// One wavefront per token. rowsum = fixed-order sum of the per-tile
+// partials of exp(c - cap); loss_n = cap + log(rowsum) - c[y] (0 if
+// ignored). With `grad`, the token's softcapped logits are then replaced in
+// place by the gradient of the mean loss w.r.t. the raw logits z:
+//   (exp(c - cap) / rowsum - [v == y]) * (1 - (c / cap)^2) / n_valid.
+// |c| <= cap, so exp(c - cap) in [e^(-2 cap), 1] needs no running maximum.
+template <typename T>
+__global__ __launch_bounds__(256) void ce_rows_kernel(T* __restrict__ logits,
+                                                      const int32_t* __restrict__ tgt,
+                                                      const float* __restrict__ part, int nparts,
+                                                      const float* __restrict__ scalars,
+                                                      float* __restrict__ lossrow, int64_t N, int V,
+                                                      float cap, int grad) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  float s = 0.0f;
+  for (int j = lane; j < nparts; j += 64) s += part[n * nparts + j];
+  s = wave_sum(s);
+  const int y = tgt[n];
+  T* row = logits + n * V;
+  float cy = 0.0f;
+  if (y >= 0) cy = to_f(row[y]);
+  if (lane == 0) lossrow[n] = y >= 0 ? cap + logf(s) - cy : 0.0f;
+  if (!grad) return;
+  const float inv = 1.0f / s, inv_nv = scalars[0], icap = 1.0f / cap;
+  constexpr int VEC = 16 / sizeof(T);
+  for (int v0 = lane * VEC; v0 < V; v0 += 64 * VEC) {
+    Frag<T> f;
+    frag_load(f, row + v0);  // 16 bytes
+    float e[VEC];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) e[j] = static_cast<float>(f.v[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) e[j] = f.lo[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float c = e[j];
+      float p = y >= 0 ? __expf(c - cap) * inv : 0.0f;
+      if (v0 + j == y) p -= 1.0f;
+      const float q = c * icap;
+      e[j] = p * (1.0f - q * q) * inv_nv;
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) f.v[j] = static_cast<bf16>(e[j]);
+      *reinterpret_cast<bf16x8*>(row + v0) = f.v;
+    } else {
+      *reinterpret_cast<f32x4*>(row + v0) = f32x4{e[0], e[1], e[2], e[3]};
+    }
   }
+}
+
+// Mean over valid tokens: fixed-order reduction in double.
+__global__ __launch_bounds__(1024) void loss_kernel(const float* __restrict__ lossrow,
+                                                    const float* __restrict__ scalars,
+                                                    float* __restrict__ loss, int64_t N) {
+  __shared__ double s_loss[1024];
+  double acc = 0.0;
+  for (int64_t n = threadIdx.x; n < N; n += 1024) acc += lossrow[n];
+  s_loss[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (threadIdx.x < s) s_loss[threadIdx.x] += s_loss[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(s_loss[0] * (double)scalars[0]);
 }
 
 }  // namespace gk
@@ -483,24 +548,62 @@ void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t
   hipLaunchKernelGGL(embed_bwd_kernel, dim3((unsigned)N), dim3(256), 0, s, gx0, tok, gwte, C);
 }
 
+template <typename T, int NC>
+static void mix_norm_nc(const Dims& d, const float* x, const float* x0, const float* lam_r,
+                        const float* lam_0, float* xin_out, void* y, float* r, const float* wg,
+                        float* a, hipStream_t s) {
+  hipLaunchKernelGGL((mix_norm_kernel<T, NC>), dim3((unsigned)((d.N + 3) / 4)), dim3(256), 0, s,
+                     x, x0, lam_r, lam_0, xin_out, static_cast<T*>(y), r, wg, a, d.N, d.C, d.Hk,
+                     d.eps);
+}
+
 void launch_mix_norm(const Dims& d, const float* x, const float* x0, const float* lam_r,
                      const float* lam_0, float* xin_out, void* y, float* r, const float* wg,
                      float* a, hipStream_t s) {
-  dim3 grid((unsigned)((d.N + 3) / 4));
-  if (d.bf16)
-    hipLaunchKernelGGL(mix_norm_kernel<bf16>, grid, dim3(256), 0, s, x, x0, lam_r, lam_0,
-                       xin_out, static_cast<bf16*>(y), r, wg, a, d.N, d.C, d.Hk, d.eps);
-  else
-    hipLaunchKernelGGL(mix_norm_kernel<float>, grid, dim3(256), 0, s, x, x0, lam_r, lam_0,
-                       xin_out, static_cast<float*>(y), r, wg, a, d.N, d.C, d.Hk, d.eps);
+#define MN_CALL(T, NC) mix_norm_nc<T, NC>(d, x, x0, lam_r, lam_0, xin_out, y, r, wg, a, s)
+  const int nc = (d.C + 255) / 256;
+  if (d.bf16) {
+    switch (nc) {
+      case 1: MN_CALL(bf16, 1); break;
+      case 2: MN_CALL(bf16, 2); break;
+      case 3: MN_CALL(bf16, 3); break;
+      case 4: MN_CALL(bf16, 4); break;
+      case 5: MN_CALL(bf16, 5); break;
+      case 6: MN_CALL(bf16, 6); break;
+      case 7: MN_CALL(bf16, 7); break;
+      default: MN_CALL(bf16, 8); break;
+    }
+  } else {
+    switch (nc) {
+      case 1: MN_CALL(float, 1); break;
+      case 2: MN_CALL(float, 2); break;
+      case 3: MN_CALL(float, 3); break;
+      case 4: MN_CALL(float, 4); break;
+      case 5: MN_CALL(float, 5); break;
+      case 6: MN_CALL(float, 6); break;
+      case 7: MN_CALL(float, 7); break;
+      default: MN_CALL(float, 8); break;
+    }
+  }
+#undef MN_CALL
 }
 
 void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((d.N + 3) / 4));
-  if (d.bf16)
-    hipLaunchKernelGGL(norm_bwd_kernel<bf16>, grid, dim3(256), 0, s, a, d.N, d.C, d.Hk);
-  else
-    hipLaunchKernelGGL(norm_bwd_kernel<float>, grid, dim3(256), 0, s, a, d.N, d.C, d.Hk);
+  NormBwdArgs b = a;
+  b.gxc_bf16 = d.bf16 ? 1 : 0;
+#define NB_CALL(NC) hipLaunchKernelGGL(norm_bwd_kernel<NC>, grid, dim3(256), 0, s, b, d.N, d.C, d.Hk)
+  switch ((d.C + 255) / 256) {
+    case 1: NB_CALL(1); break;
+    case 2: NB_CALL(2); break;
+    case 3: NB_CALL(3); break;
+    case 4: NB_CALL(4); break;
+    case 5: NB_CALL(5); break;
+    case 6: NB_CALL(6); break;
+    case 7: NB_CALL(7); break;
+    default: NB_CALL(8); break;
+  }
+#undef NB_CALL
 }
 
 void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
@@ -547,16 +650,21 @@ void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const flo
                        ve_table, gve_table, ga, tok, d.T, d.H, d.Hk, d.D, d.Qkv);
 }
 
-void launch_loss(const Dims& d, const void* logits, const int32_t* tgt, float* rowsum,
-                 float* scalars, float* loss, hipStream_t s) {
+void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipStream_t s) {
+  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(1024), 0, s, tgt, scalars, d.N);
+}
+
+void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* rowpart,
+                 int nparts, const float* scalars, float* lossrow, float* loss, bool grad,
+                 hipStream_t s) {
+  dim3 grid((unsigned)((d.N + 3) / 4));
   if (d.bf16)
-    hipLaunchKernelGGL(loss_kernel<bf16>, dim3(1), dim3(1024), 0, s,
-                       static_cast<const bf16*>(logits), tgt, rowsum, scalars, loss, d.N, d.V,
-                       d.cap);
+    hipLaunchKernelGGL(ce_rows_kernel<bf16>, grid, dim3(256), 0, s, static_cast<bf16*>(logits),
+                       tgt, rowpart, nparts, scalars, lossrow, d.N, d.V, d.cap, grad ? 1 : 0);
   else
-    hipLaunchKernelGGL(loss_kernel<float>, dim3(1), dim3(1024), 0, s,
-                       static_cast<const float*>(logits), tgt, rowsum, scalars, loss, d.N, d.V,
-                       d.cap);
+    hipLaunchKernelGGL(ce_rows_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(logits),
+                       tgt, rowpart, nparts, scalars, lossrow, d.N, d.V, d.cap, grad ? 1 : 0);
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, lossrow, scalars, loss, d.N);
 }
 
 }  // namespace gpt

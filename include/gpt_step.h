@@ -114,18 +114,25 @@ int gpt_layer_info(const gpt_config* cfg, int32_t l, int32_t* is_full, int32_t* 
 int gpt_workspace_size(const gpt_config* cfg, size_t* bytes);
 
 /*
- * Host only. Where the forward keeps a saved tensor inside the workspace,
- * for inspection after a synchronised call. `name` is one of:
+ * Host only. Where a named buffer lives inside the workspace, for inspection
+ * after a synchronised call (contents are defined only for the forward
+ * tensors below). Saved forward tensors:
  *   "x"    fp32 [N, C]   residual stream entering layer `layer`
  *                        (layer = n_layer: the stream before the final norm)
  *   "xn"   act  [N, C]   RMSNorm output feeding c_q/c_k/c_v
  *   "qkv"  act  [N, (H+2Hk)*D]  q, k after RoPE+QK-norm; v after the
  *                        value embedding; head-major columns
  *   "attn" act  [N, H*D] attention output
+ *   "xmid" fp32 [N, C]   residual stream after the attention block
  *   "xn2"  act  [N, C]   RMSNorm output feeding the MLP
  *   "u"    act  [N, F]   c_fc output before ReLU^2
- *   "xf"   act  [N, C]   final RMSNorm output (layer ignored)
- *   "logits" act [N, V]  softcapped logits (layer ignored)
+ *   "xf"   act  [N, C]   final RMSNorm output
+ *   "logits" act [N, V]  softcapped logits after gpt_fwd; after gpt_fwd_bwd
+ *                        the gradient of the loss w.r.t. the raw logits
+ * Scratch (layout only): "wc", "rope", "xin", "rf", "rowpart",
+ * "lossrow", "scalars", "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv",
+ * "delta", "ga", "lam_part", "veg_part"; per layer "r1", "rqk", "a", "lse",
+ * "r2". All regions are disjoint. `layer` is ignored for global regions.
  * N = batch * seq_len, row n = b * seq_len + t; act = compute_dtype.
  * Returns the byte offset and size. GPT_E_INVAL for an unknown name/layer.
  */

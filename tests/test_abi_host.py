@@ -109,3 +109,30 @@ def test_entry_points_reject_bad_pointers_before_any_launch():
     cfg8 = B.make_config(w, fp8_linears=1)
     assert L.gpt_fwd_bwd(ctypes.byref(cfg8), p, p, p, p, p, p, ws, None) == -5
     assert L.gpt_status_string(-4).decode() == "workspace too small"
+
+
+GLOBAL_REGIONS = ["wc", "rope", "xin", "xf", "rf", "logits", "rowpart", "lossrow",
+                  "scalars", "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga",
+                  "lam_part", "veg_part"]
+LAYER_REGIONS = ["xn", "r1", "qkv", "rqk", "a", "attn", "lse", "xmid", "xn2", "r2", "u"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "d12", "d12_gqa", "d26"])
+def test_workspace_regions_disjoint(name):
+    w = W.get(name)
+    cfg = B.make_config(w, fp8_linears=0)
+    ws = B.workspace_size(cfg)
+    spans = []
+    for r in GLOBAL_REGIONS:
+        spans.append((r, *B.workspace_region(cfg, r, 0)))
+    for l in range(w.n_layer):
+        for r in LAYER_REGIONS:
+            spans.append((f"{r}[{l}]", *B.workspace_region(cfg, r, l)))
+    for l in range(w.n_layer + 1):
+        spans.append((f"x[{l}]", *B.workspace_region(cfg, "x", l)))
+    spans = [s for s in spans if s[2] > 0]
+    spans.sort(key=lambda s: s[1])
+    for (n1, o1, b1), (n2, o2, b2) in zip(spans, spans[1:]):
+        assert o1 + b1 <= o2, (n1, n2)
+    assert all(o % 256 == 0 for _, o, _ in spans)
+    assert spans[-1][1] + spans[-1][2] <= ws

@@ -1,0 +1,49 @@
+"""Full-size workloads (the launch configuration bench.py times) against the
+oracle's stored results: the loss, and every parameter tensor's gradient on
+the entries chosen by tests/golden/sampling.py (all of them for the lambda
+vectors, eight used rows of each embedding table, 1024 seeded entries of
+every other tensor). The stored values come from
+tests/golden/make_golden.py, which calls only the oracle.
+
+Bar (bf16): loss relative error <= 1e-2; per-tensor cosine >= 0.999 on the
+sampled entries; the full gradient norm within 5% of the oracle's.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.golden.sampling import sample_indices
+from tests.gpu_common import gpu_step, inputs
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.mark.parametrize("name", ["d12", "d12_gqa", "d20"])
+def test_full_size_against_stored_oracle(name):
+    path = os.path.join(GOLDEN, f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle results for {name}")
+    ref = np.load(path)
+    w = W.get(name)
+    p, tok, tgt = inputs(w)
+    lg, gg, _ = gpu_step(w, p, tok, tgt)
+    lo = float(ref["loss"])
+    assert abs(lg - lo) <= 1e-2 * abs(lo), (lg, lo)
+    offs, _ = oracle.param_offsets(w)
+    idx = sample_indices(offs, tok)
+    bad = {}
+    for k, (o, s) in offs.items():
+        n = int(np.prod(s))
+        full = gg[o:o + n].astype(np.float64)
+        a = full[idx[k]]
+        b = ref["val/" + k].astype(np.float64)
+        cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+        ratio = float(np.linalg.norm(full) / ref["norm/" + k])
+        if not (cos >= 0.999 and abs(ratio - 1) <= 0.05):
+            bad[k] = (cos, ratio)
+    assert not bad, bad
