@@ -125,15 +125,30 @@ struct EpResid : EpBase<EpResid> {  // C = R + acc (residual stream, fp32)
   }
 };
 template <typename T>
-struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {  // C = acc * d/du relu(u)^2 = acc * 2 max(u, 0)
-  const T* U;
+struct EpRelu2 : EpBase<EpRelu2<T>> {  // C = relu(acc)^2 (the MLP hidden activation h)
   T* C;
   int64_t ldc;
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
-    const f32x4 u = get4<T>(U + m * ldc + n, cnt);
     f32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = u[j] > 0.0f ? 2.0f * u[j] * v[j] : 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const float r = fmaxf(v[j], 0.0f);
+      o[j] = r * r;
+    }
+    put4<T>(C + m * ldc + n, o, cnt);
+  }
+};
+template <typename T>
+struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {
+  // g_u = g_h * d/du relu(u)^2 = g_h * 2 relu(u), with relu(u) = sqrt(h)
+  const T* H;
+  T* C;
+  int64_t ldc;
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    const f32x4 h = get4<T>(H + m * ldc + n, cnt);
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = 2.0f * sqrtf(h[j]) * v[j];
     put4<T>(C + m * ldc + n, o, cnt);
   }
 };
@@ -181,9 +196,16 @@ inline EpResid mk_resid(const float* R, float* C, int64_t ld) {
   return e;
 }
 template <typename T>
-EpRelu2Bwd<T> mk_relu2bwd(const void* U, void* C, int64_t ld) {
+EpRelu2<T> mk_relu2(void* C, int64_t ld) {
+  EpRelu2<T> e;
+  e.C = static_cast<T*>(C);
+  e.ldc = ld;
+  return e;
+}
+template <typename T>
+EpRelu2Bwd<T> mk_relu2bwd(const void* H, void* C, int64_t ld) {
   EpRelu2Bwd<T> e;
-  e.U = static_cast<const T*>(U);
+  e.H = static_cast<const T*>(H);
   e.C = static_cast<T*>(C);
   e.ldc = ld;
   return e;
@@ -380,19 +402,21 @@ static Tile pick_tile(int64_t M, int64_t N) {
 
 // Tile for a weight gradient (split-K fills the machine instead).
 static Tile pick_tile_wgrad(int64_t M, int64_t N) {
-  if (N % 256 == 0 && M % 256 == 0) return {256, 256};
   if (N % 192 == 0) return {256, 192};
+  if (N % 256 == 0 && M % 256 == 0) return {256, 256};
   return {256, 128};
 }
 
-// K split so that tiles * splits >= 512 workgroups, chunks >= 256 and a
-// multiple of 32.
-static int64_t pick_kchunk(int64_t tiles, int64_t K, int64_t min_chunk = 256) {
-  int64_t splits = (512 + tiles - 1) / tiles;
+// K split for about one workgroup per CU (256): every extra split adds a
+// full pass of fp32 atomics over C, which costs more than the idle CUs of a
+// partly filled wave (measured on the d12 weight gradients). Chunks are
+// multiples of 64 and at least `min_chunk`.
+static int64_t pick_kchunk(int64_t tiles, int64_t K, int64_t min_chunk = 512) {
+  int64_t splits = std::max<int64_t>(1, (256 + tiles / 2) / tiles);
   int64_t chunk = (K + splits - 1) / splits;
   chunk = std::max<int64_t>(chunk, min_chunk);
-  chunk = (chunk + 31) / 32 * 32;
-  return std::min<int64_t>(chunk, (K + 31) / 32 * 32);
+  chunk = (chunk + 63) / 64 * 64;
+  return std::min<int64_t>(chunk, (K + 63) / 64 * 64);
 }
 
 template <int BM, int BN, bool AK, bool BKM, class PA, class PB, class EP>
@@ -401,7 +425,7 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const int splits = (int)((K + kchunk - 1) / kchunk);
   dim3 grid((unsigned)(tm * tn), 1, (unsigned)std::max(splits, 1));
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 32, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
                      static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M, N, K,
                      kchunk, tm, tn, pa, pb, ep, rowsum);
 }
@@ -435,23 +459,23 @@ void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const 
 }
 
 void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                   const float* R, float* C, bool relu2_a, hipStream_t s) {
-  const Tile t = pick_tile(M, N);
-  if (d.bf16) {
-    if (relu2_a)
-      run_bf16<true, true>(t, A, K, B, K, M, N, K, K, PreRelu2{}, PreId{}, mk_resid(R, C, N),
-                           nullptr, s);
-    else
-      run_bf16<true, true>(t, A, K, B, K, M, N, K, K, PreId{}, PreId{}, mk_resid(R, C, N),
-                           nullptr, s);
-  } else {
-    if (relu2_a)
-      run_f32<float, true, true>(A, K, B, K, M, N, K, PreRelu2{}, PreId{}, mk_resid(R, C, N),
-                                 nullptr, s);
-    else
-      run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_resid(R, C, N),
-                                 nullptr, s);
-  }
+                   const float* R, float* C, hipStream_t s) {
+  if (d.bf16)
+    run_bf16<true, true>(pick_tile(M, N), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_resid(R, C, N), nullptr, s);
+  else
+    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_resid(R, C, N), nullptr,
+                               s);
+}
+
+void gemm_nt_relu2(const Dims& d, int64_t M, int N, int K, const void* A, const void* B, void* C,
+                   hipStream_t s) {
+  if (d.bf16)
+    run_bf16<true, true>(pick_tile(M, N), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_relu2<bf16>(C, N), nullptr, s);
+  else
+    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_relu2<float>(C, N),
+                               nullptr, s);
 }
 
 int gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
@@ -505,6 +529,11 @@ void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, c
     const Tile t = pick_tile(M, N);
     const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
     const int64_t kc = pick_kchunk(tiles, K, 4096);
+    if (kc >= K) {
+      run_bf16<true, false>(t, A, K, B, N, M, N, K, K, PreId{}, PreId{}, mk_f32(C, N, 0), nullptr,
+                            s);
+      return;
+    }
     launch_zero(C, M * N, s);
     run_bf16<true, false>(t, A, K, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), nullptr,
                           s);
@@ -515,25 +544,22 @@ void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, c
 }
 
 void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
-                   float* C, bool accumulate, bool relu2_b, hipStream_t s) {
+                   float* C, bool accumulate, hipStream_t s) {
   if (d.bf16) {
     const Tile t = pick_tile_wgrad(M, N);
     const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
     const int64_t kc = pick_kchunk(tiles, K);
+    if (kc >= K) {  // one split: plain (accumulating) stores
+      run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{},
+                             mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
+      return;
+    }
     if (!accumulate) launch_zero(C, (int64_t)M * N, s);
-    if (relu2_b)
-      run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreRelu2{}, mk_atomic(C, N),
-                             nullptr, s);
-    else
-      run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N),
-                             nullptr, s);
+    run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), nullptr,
+                           s);
   } else {
-    if (relu2_b)
-      run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreRelu2{},
-                                   mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
-    else
-      run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
-                                   mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
+    run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
+                                 mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
   }
 }
 

@@ -195,6 +195,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     lb.store(Bs[0], n0, k_lo, tid, pb);
   }
   __syncthreads();
+  // Fragments of the next 16-wide k-slice are read into a second register
+  // set before the MFMAs of the current slice are issued, so LDS latency
+  // overlaps matrix work; the next stage's LDS stores follow the last
+  // slice's MFMAs.
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
@@ -203,17 +207,28 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
       la.load(A, lda, m0, M, kn, k_hi, tid);
       lb.load(B, ldb, n0, N, kn, k_hi, tid);
     }
+    Frag<bf16> a[2][TM], b[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_frag<BM, BK, AK>(a[0][i], As[cur], wm * (BM / 2) + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) read_frag<BN, BK, BKM>(b[0][j], Bs[cur], wn * (BN / 2) + j * 32, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      Frag<bf16> a[TM], b[TN];
+      const int p = ks & 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) read_frag<BM, BK, AK>(a[i], As[cur], wm * (BM / 2) + i * 32, ks, lane);
+        for (int i = 0; i < TM; ++i)
+          read_frag<BM, BK, AK>(a[p ^ 1][i], As[cur], wm * (BM / 2) + i * 32, ks + 1, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) read_frag<BN, BK, BKM>(b[j], Bs[cur], wn * (BN / 2) + j * 32, ks, lane);
+        for (int j = 0; j < TN; ++j)
+          read_frag<BN, BK, BKM>(b[p ^ 1][j], Bs[cur], wn * (BN / 2) + j * 32, ks + 1, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads ahead of the MFMAs
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) mfma(acc[i][j], a[i], b[j]);
+        for (int j = 0; j < TN; ++j) mfma(acc[i][j], a[p][i], b[p][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
       la.store(As[cur ^ 1], m0, kn, tid, pa);

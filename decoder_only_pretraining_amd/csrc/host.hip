@@ -317,10 +317,10 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     site("gemm.qkv.fwd", s, [&] { gemm_nt_store(d, N, d.Qkv, d.C, xn, wmat(F.q[l]), qkv, s); });
     site("rope.fwd", s, [&] { launch_rope_qk_ve_fwd(d, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr, tokens, s); });
     site("attn.fwd", s, [&] { launch_attn_fwd(d, full, qkv, att, lse, s); });
-    site("gemm.o.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.Cq, att, wmat(F.o[l]), xin, xmid, false, s); });
+    site("gemm.o.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.Cq, att, wmat(F.o[l]), xin, xmid, s); });
     launch_mix_norm(d, xmid, nullptr, nullptr, nullptr, nullptr, xn2, r2, nullptr, nullptr, s);
-    site("gemm.fc.fwd", s, [&] { gemm_nt_store(d, N, d.F, d.C, xn2, wmat(F.fc[l]), u, s); });
-    site("gemm.mp.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.F, u, wmat(F.mp[l]), xmid, X(l + 1), true, s); });
+    site("gemm.fc.fwd", s, [&] { gemm_nt_relu2(d, N, d.F, d.C, xn2, wmat(F.fc[l]), u, s); });
+    site("gemm.mp.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.F, u, wmat(F.mp[l]), xmid, X(l + 1), s); });
   }
   void* xf = W + P.xf;
   float* rf = reinterpret_cast<float*>(W + P.rf);
@@ -355,7 +355,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     float* veg_part = reinterpret_cast<float*>(W + P.veg_part);
 
     site("gemm.lm.dgrad", s, [&] { gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, s); });
-    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, false, s); });
+    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, s); });
     NormBwdArgs nb{};
     nb.mode = NB_FINAL;
     nb.gin = gtmp;
@@ -379,9 +379,9 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       const void* u = LY(l, P.l_u);
       // MLP
       site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s); });
-      site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, true, s); });
+      site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, s); });
       site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s); });
-      site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, false, s); });
+      site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, s); });
       nb = NormBwdArgs{};
       nb.mode = NB_NORM2;
       nb.gin = gtmp;
@@ -392,13 +392,13 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       launch_norm_bwd(d, nb, s);
       // attention
       site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s); });
-      site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, false, s); });
+      site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, s); });
       site("attn.delta", s, [&] { launch_attn_delta(d, gO, att, delta, s); });
       site("attn.bwd", s, [&] { launch_attn_bwd(d, full, qkv, gO, lse, delta, gqkv, s); });
       launch_rope_qk_ve_bwd(d, gqkv, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr,
                             ve ? grads + F.ve[l] : nullptr, ga, tokens, s);
       site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s); });
-      site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, false, s); });
+      site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, s); });
       if (ve) launch_veg_wgrad(d, ga, xn, veg_part, P.veg_splits, grads + F.veg[l], s);
       nb = NormBwdArgs{};
       nb.mode = NB_NORM1;
@@ -533,7 +533,7 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
                          {"xmid", P.l_xmid, N * C * 4},
                          {"xn2", P.l_xn2, N * C * A},
                          {"r2", P.l_r2, N * 4},
-                         {"u", P.l_u, N * d.F * A}};
+                         {"h", P.l_u, N * d.F * A}};
   for (const R& r : per_layer)
     if (n == r.name) {
       if (layer < 0 || layer >= d.L) return fail(GPT_E_INVAL, "layer out of range");

@@ -129,7 +129,10 @@ void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s);
 void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                   const float* R, float* C, bool relu2_a, hipStream_t s);
+                   const float* R, float* C, hipStream_t s);
+// C = relu(A B^T)^2 (the MLP hidden activation)
+void gemm_nt_relu2(const Dims& d, int64_t M, int N, int K, const void* A, const void* B, void* C,
+                   hipStream_t s);
 // Softcapped logits; row sums of exp(c - cap) as per-tile partials
 // rowpart[m * P + j], j < P; returns P.
 int gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
@@ -138,14 +141,15 @@ void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const 
                    void* C, hipStream_t s);
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                  float* C, hipStream_t s);
+// C = (A B) * 2 sqrt(H): the MLP hidden gradient from h = relu(u)^2
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                      const void* U, void* C, hipStream_t s);
+                      const void* H, void* C, hipStream_t s);
 // Like gemm_nn_f32 for a long contraction: K split across workgroups, C
 // zeroed and accumulated with fp32 atomics.
 void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                         float* C, hipStream_t s);
-// Weight gradients C[M][N] (+)= sum_k A[k][m] B[k][n]; relu2_b: B = relu(B)^2 on load.
+// Weight gradients C[M][N] (+)= sum_k A[k][m] B[k][n].
 void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
-                   float* C, bool accumulate, bool relu2_b, hipStream_t s);
+                   float* C, bool accumulate, hipStream_t s);
 
 }  // namespace gpt

@@ -125,7 +125,7 @@ int gpt_workspace_size(const gpt_config* cfg, size_t* bytes);
  *   "attn" act  [N, H*D] attention output
  *   "xmid" fp32 [N, C]   residual stream after the attention block
  *   "xn2"  act  [N, C]   RMSNorm output feeding the MLP
- *   "u"    act  [N, F]   c_fc output before ReLU^2
+ *   "h"    act  [N, F]   MLP hidden activation relu(c_fc output)^2
  *   "xf"   act  [N, C]   final RMSNorm output
  *   "logits" act [N, V]  softcapped logits after gpt_fwd; after gpt_fwd_bwd
  *                        the gradient of the loss w.r.t. the raw logits

@@ -114,7 +114,7 @@ def test_entry_points_reject_bad_pointers_before_any_launch():
 GLOBAL_REGIONS = ["wc", "rope", "xin", "xf", "rf", "logits", "rowpart", "lossrow",
                   "scalars", "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga",
                   "lam_part", "veg_part"]
-LAYER_REGIONS = ["xn", "r1", "qkv", "rqk", "a", "attn", "lse", "xmid", "xn2", "r2", "u"]
+LAYER_REGIONS = ["xn", "r1", "qkv", "rqk", "a", "attn", "lse", "xmid", "xn2", "r2", "h"]
 
 
 @pytest.mark.parametrize("name", ["tiny", "d12", "d12_gqa", "d26"])
