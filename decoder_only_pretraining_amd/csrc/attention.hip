@@ -19,35 +19,17 @@
 //
 // Softmax works in base 2: the saved statistic is lse2 = log2(sum_s 2^(S*c))
 // with c = log2(e) / sqrt(D), so P = 2^(S*c - lse2).
+//
+// All three kernels stream their tiles through two LDS buffers: the global
+// loads of the next tile are in flight while the current tile's MFMAs run.
+// Blocks of the score matrix that lie wholly inside the causal window skip
+// the per-element mask.
 #include "device_common.h"
 #include "internal.h"
 
 namespace gk {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-
-template <typename T, int ROWS, int D>
-__device__ __forceinline__ void load_rows_lds(T (*lds)[D + 16 / sizeof(T)], const T* __restrict__ src,
-                                              int64_t row0, int nvalid, int64_t ld, int tid) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int NV = ROWS * D / VEC / 256;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * 256;
-    const int r = v / (D / VEC), c = (v % (D / VEC)) * VEC;
-    Frag<T> f;
-    if (r < nvalid) {
-      frag_load(f, src + (row0 + r) * ld + c);
-    } else {
-      frag_zero(f);
-    }
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<bf16x8*>(&lds[r][c]) = f.v;
-    } else {
-      *reinterpret_cast<f32x4*>(&lds[r][c]) = f.lo;
-    }
-  }
-}
 
 // Per-lane query fragments for 32 query rows (B operand of K Q^T).
 template <typename T, int D>
@@ -112,14 +94,50 @@ __device__ __forceinline__ void frag_down(Frag<float>& f, const float* lds, int 
                         (lane & 31)]);
 }
 
+// A ROWS x D tile of head rows on its way from global memory (rows
+// row0 .. row0 + ROWS - 1 of a matrix with row stride ld, rows past nvalid
+// read as zero) to an LDS buffer with row pitch PITCH, held in registers in
+// between so the global loads of the next tile overlap the current tile's
+// MFMAs.
+struct alignas(16) V16 {
+  uint32_t w[4];
+};
+template <typename T, int ROWS, int D>
+struct RowStage {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int NV = ROWS * D / VEC / 256;
+  V16 v[NV];
+  __device__ __forceinline__ void load(const T* __restrict__ src, int64_t row0, int nvalid,
+                                       int64_t ld, int tid) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = tid + i * 256;
+      const int r = idx / (D / VEC), c = (idx % (D / VEC)) * VEC;
+      if (r < nvalid)
+        v[i] = *reinterpret_cast<const V16*>(src + (row0 + r) * ld + c);
+      else
+        v[i] = V16{{0, 0, 0, 0}};
+    }
+  }
+  template <int PITCH>
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = tid + i * 256;
+      const int r = idx / (D / VEC), c = (idx % (D / VEC)) * VEC;
+      *reinterpret_cast<V16*>(lds + r * PITCH + c) = v[i];
+    }
+  }
+};
+
 // ------------------------------------------------------------ forward
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
                                                        float* __restrict__ lse2, int T_, int H,
                                                        int Hk, int W, int full, float c2) {
-  constexpr int BQ = 128, BKV = 64, PAD = 16 / sizeof(T);
-  __shared__ T Ks[BKV][D + PAD];
-  __shared__ T Vs[BKV][D + PAD];
+  constexpr int BQ = 128, BKV = 64, PAD = 16 / sizeof(T), P = D + PAD;
+  __shared__ __attribute__((aligned(16))) T Ks[2][BKV * P];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BKV * P];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int h = blockIdx.y, b = blockIdx.z;
@@ -127,6 +145,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
   const int Qkv = (H + 2 * Hk) * D;
   const int64_t rb = (int64_t)b * T_;
   const int t0 = qt * BQ, tw = t0 + wv * 32, t = tw + (lane & 31);
+  const T* kbase = qkv + (H + j) * D;
+  const T* vbase = qkv + (H + Hk + j) * D;
 
   Frag<T> qf[D / 16];
   load_row_frags<T, D>(qf, qkv + (rb + t) * Qkv + h * D, t < T_, lane);
@@ -138,70 +158,97 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
     for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
   float m_i = kNegInf, l_i = 0.0f;
 
-  const int lo = full ? 0 : max(0, t0 - W);
+  const int first = ((full ? 0 : max(0, t0 - W)) / BKV) * BKV;
   const int hi_k = min(T_, t0 + BQ);
+  const int ntile = (hi_k - first + BKV - 1) / BKV;
   const int w_lo = full ? 0 : max(0, tw - W), w_hi = min(T_, tw + 32);
-  for (int s0 = (lo / BKV) * BKV; s0 < hi_k; s0 += BKV) {
-    __syncthreads();
-    load_rows_lds<T, BKV, D>(Ks, qkv + (H + j) * D, rb + s0, T_ - s0, Qkv, tid);
-    load_rows_lds<T, BKV, D>(Vs, qkv + (H + Hk + j) * D, rb + s0, T_ - s0, Qkv, tid);
-    __syncthreads();
-    if (s0 >= w_hi || s0 + BKV <= w_lo) continue;
-    f32x16 sacc[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[sb][e] = 0.0f;
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        Frag<T> kf;
-        frag_load(kf, &Ks[sb * 32 + (lane & 31)][kc * 16 + hi * 8]);
-        mfma(sacc[sb], kf, qf[kc]);
-      }
+  RowStage<T, BKV, D> kst, vst;
+  kst.load(kbase, rb + first, T_ - first, Qkv, tid);
+  vst.load(vbase, rb + first, T_ - first, Qkv, tid);
+  kst.template store<P>(Ks[0], tid);
+  vst.template store<P>(Vs[0], tid);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int s0 = first + it * BKV, cur = it & 1;
+    const bool more = it + 1 < ntile;
+    if (more) {
+      kst.load(kbase, rb + s0 + BKV, T_ - s0 - BKV, Qkv, tid);
+      vst.load(vbase, rb + s0 + BKV, T_ - s0 - BKV, Qkv, tid);
     }
-    float mx = kNegInf;
+    if (s0 < w_hi && s0 + BKV > w_lo) {
+      // every key of the tile visible to every query of the wavefront
+      const bool interior = (s0 + BKV - 1 <= tw) && (full || tw + 31 - s0 <= W);
+      f32x16 sacc[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int s = s0 + sb * 32 + acc_row(e, lane);
-        const bool vis = s <= t && (full || t - s <= W);
-        const float v = vis ? sacc[sb][e] * c2 : kNegInf;
-        sacc[sb][e] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = exp2f(m_i - m_use);
-    float ps = 0.0f;
+        for (int e = 0; e < 16; ++e) sacc[sb][e] = 0.0f;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(sacc[sb][e] - m_use);
-        sacc[sb][e] = p;
-        ps += p;
-      }
-    ps += __shfl_xor(ps, 32, 64);
-    l_i = l_i * alpha + ps;
-    m_i = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        Frag<T> pf;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) frag_set(pf, jj, sacc[sb][8 * c + jj]);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          Frag<T> vf;
-          frag_down<D + PAD>(vf, &Vs[0][0], sb * 32 + 16 * c, db * 32, lane);
-          mfma(o[db], vf, pf);
+        for (int kc = 0; kc < D / 16; ++kc) {
+          Frag<T> kf;
+          frag_load(kf, &Ks[cur][(sb * 32 + (lane & 31)) * P + kc * 16 + hi * 8]);
+          mfma(sacc[sb], kf, qf[kc]);
         }
       }
+      float mx = kNegInf;
+      if (interior) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            sacc[sb][e] *= c2;
+            mx = fmaxf(mx, sacc[sb][e]);
+          }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int sidx = s0 + sb * 32 + acc_row(e, lane);
+            const bool vis = sidx <= t && (full || t - sidx <= W);
+            const float v = vis ? sacc[sb][e] * c2 : kNegInf;
+            sacc[sb][e] = v;
+            mx = fmaxf(mx, v);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_i, mx);
+      const float m_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = exp2f(m_i - m_use);
+      float ps = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(sacc[sb][e] - m_use);
+          sacc[sb][e] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 32, 64);
+      l_i = l_i * alpha + ps;
+      m_i = m_new;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<T> pf;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) frag_set(pf, jj, sacc[sb][8 * c + jj]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<T> vf;
+            frag_down<P>(vf, Vs[cur], sb * 32 + 16 * c, db * 32, lane);
+            mfma(o[db], vf, pf);
+          }
+        }
+    }
+    if (more) {
+      kst.template store<P>(Ks[cur ^ 1], tid);
+      vst.template store<P>(Vs[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
   if (t < T_) {
     const float inv = 1.0f / l_i;
@@ -239,10 +286,10 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
     const T* __restrict__ qkv, const T* __restrict__ gO, const float* __restrict__ lse2,
     const float* __restrict__ delta, T* __restrict__ gqkv, int T_, int H, int Hk, int W, int full,
     float c2, float scale) {
-  constexpr int BK2 = 128, BQ2 = 64, PAD = 16 / sizeof(T);
-  __shared__ T Qs[BQ2][D + PAD];
-  __shared__ T dOs[BQ2][D + PAD];
-  __shared__ float ls[BQ2], dl[BQ2];
+  constexpr int BK2 = 128, BQ2 = 64, PAD = 16 / sizeof(T), P = D + PAD;
+  __shared__ __attribute__((aligned(16))) T Qs[2][BQ2 * P];
+  __shared__ __attribute__((aligned(16))) T dOs[2][BQ2 * P];
+  __shared__ __attribute__((aligned(16))) float ls[2][BQ2], dl[2][BQ2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
   const int kt = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int G = H / Hk;
@@ -263,66 +310,101 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
       dv[i][e] = 0.0f;
     }
 
+  // (head, query tile) steps of this key tile, walked with a one-step prefetch
+  const int q_first = (s0 / BQ2) * BQ2;
   const int q_hi = full ? T_ : min(T_, s0 + BK2 + W);  // exclusive
-  const int w_q_lo = sw, w_q_hi = full ? T_ : min(T_, sw + 32 + W);
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = j * G + hh;
-    for (int t0 = (s0 / BQ2) * BQ2; t0 < q_hi; t0 += BQ2) {
-      __syncthreads();
-      load_rows_lds<T, BQ2, D>(Qs, qkv + h * D, rb + t0, T_ - t0, Qkv, tid);
-      load_rows_lds<T, BQ2, D>(dOs, gO + h * D, rb + t0, T_ - t0, Cq, tid);
-      if (tid < BQ2) {
-        const bool ok = t0 + tid < T_;
-        ls[tid] = ok ? lse2[(rb + t0 + tid) * H + h] : 0.0f;
-        dl[tid] = ok ? delta[(rb + t0 + tid) * H + h] : 0.0f;
+  const int nq = (q_hi - q_first + BQ2 - 1) / BQ2;
+  const int nstep = G * nq;
+  RowStage<T, BQ2, D> qst, dst;
+  float st_l = 0.0f, st_d = 0.0f;
+  auto fetch = [&](int step) {
+    const int h = j * G + step / nq, t0 = q_first + (step % nq) * BQ2;
+    qst.load(qkv + h * D, rb + t0, T_ - t0, Qkv, tid);
+    dst.load(gO + h * D, rb + t0, T_ - t0, Cq, tid);
+    if (tid < BQ2) {
+      const bool ok = t0 + tid < T_;
+      st_l = ok ? lse2[(rb + t0 + tid) * H + h] : 0.0f;
+      st_d = ok ? delta[(rb + t0 + tid) * H + h] : 0.0f;
+    }
+  };
+  auto put = [&](int buf) {
+    qst.template store<P>(Qs[buf], tid);
+    dst.template store<P>(dOs[buf], tid);
+    if (tid < BQ2) {
+      ls[buf][tid] = st_l;
+      dl[buf][tid] = st_d;
+    }
+  };
+  if (nstep > 0) {
+    fetch(0);
+    put(0);
+  }
+  __syncthreads();
+  for (int step = 0; step < nstep; ++step) {
+    const int cur = step & 1;
+    const bool more = step + 1 < nstep;
+    const int t0 = q_first + (step % nq) * BQ2;
+    if (more) fetch(step + 1);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int tlo = t0 + tb * 32;
+      // any (query, key) pair of this 32x32 block visible?
+      if (!(tlo < T_ && tlo + 31 >= sw && (full || tlo - (sw + 31) <= W))) continue;
+      const bool interior = tlo >= sw + 31 && (full || tlo + 31 - sw <= W) && tlo + 31 < T_;
+      f32x16 sa, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sa[e] = 0.0f;
+        dp[e] = 0.0f;
       }
-      __syncthreads();
-      if (t0 >= w_q_hi || t0 + BQ2 <= w_q_lo) continue;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x16 sa, dp;
+      for (int kc = 0; kc < D / 16; ++kc) {
+        Frag<T> qa, da;
+        frag_load(qa, &Qs[cur][(tb * 32 + (lane & 31)) * P + kc * 16 + hi * 8]);
+        frag_load(da, &dOs[cur][(tb * 32 + (lane & 31)) * P + kc * 16 + hi * 8]);
+        mfma(sa, qa, kf[kc]);
+        mfma(dp, da, vf[kc]);
+      }
+      // accumulator rows t = tlo + 8*(e/4) + 4*hi + e%4: four consecutive
+      // rows per group g = e/4, so their statistics load as one vector
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sa[e] = 0.0f;
-          dp[e] = 0.0f;
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int tl = tb * 32 + g * 8 + hi * 4;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&ls[cur][tl]);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&dl[cur][tl]);
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          Frag<T> qa, da;
-          frag_load(qa, &Qs[tb * 32 + (lane & 31)][kc * 16 + hi * 8]);
-          frag_load(da, &dOs[tb * 32 + (lane & 31)][kc * 16 + hi * 8]);
-          mfma(sa, qa, kf[kc]);
-          mfma(dp, da, vf[kc]);
-        }
-        // rows t (local tb*32 + acc_row), column s
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tl = tb * 32 + acc_row(e, lane);
-          const int t = t0 + tl;
-          const bool vis = t < T_ && s <= t && (full || t - s <= W);
-          const float p = vis ? exp2f(sa[e] * c2 - ls[tl]) : 0.0f;
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          bool vis = true;
+          if (!interior) {
+            const int tq = t0 + tl + r;
+            vis = tq < T_ && s <= tq && (full || tq - s <= W);
+          }
+          const float p = vis ? exp2f(sa[e] * c2 - lv[r]) : 0.0f;
           sa[e] = p;
-          dp[e] = p * (dp[e] - dl[tl]);
+          dp[e] = p * (dp[e] - dv4[r]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag<T> pf, dsf;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          frag_set(pf, jj, sa[8 * c + jj]);
+          frag_set(dsf, jj, dp[8 * c + jj]);
         }
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          Frag<T> pf, dsf;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            frag_set(pf, jj, sa[8 * c + jj]);
-            frag_set(dsf, jj, dp[8 * c + jj]);
-          }
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            Frag<T> doT, qT;
-            frag_down<D + PAD>(doT, &dOs[0][0], tb * 32 + 16 * c, db * 32, lane);
-            frag_down<D + PAD>(qT, &Qs[0][0], tb * 32 + 16 * c, db * 32, lane);
-            mfma(dv[db], doT, pf);
-            mfma(dk[db], qT, dsf);
-          }
+        for (int db = 0; db < D / 32; ++db) {
+          Frag<T> doT, qT;
+          frag_down<P>(doT, dOs[cur], tb * 32 + 16 * c, db * 32, lane);
+          frag_down<P>(qT, Qs[cur], tb * 32 + 16 * c, db * 32, lane);
+          mfma(dv[db], doT, pf);
+          mfma(dk[db], qT, dsf);
         }
       }
     }
+    if (more) put(cur ^ 1);
+    __syncthreads();
   }
   if (s < T_) {
     T* kp = gqkv + (rb + s) * Qkv + (H + j) * D;
@@ -346,9 +428,9 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
     const T* __restrict__ qkv, const T* __restrict__ gO, const float* __restrict__ lse2,
     const float* __restrict__ delta, T* __restrict__ gqkv, int T_, int H, int Hk, int W, int full,
     float c2, float scale) {
-  constexpr int BQ = 128, BKV = 64, PAD = 16 / sizeof(T);
-  __shared__ T Ks[BKV][D + PAD];
-  __shared__ T Vs[BKV][D + PAD];
+  constexpr int BQ = 128, BKV = 64, PAD = 16 / sizeof(T), P = D + PAD;
+  __shared__ __attribute__((aligned(16))) T Ks[2][BKV * P];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BKV * P];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
   const int qt = gridDim.x - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -357,6 +439,8 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
   const int64_t rb = (int64_t)b * T_;
   const int t0 = qt * BQ, tw = t0 + wv * 32, t = tw + (lane & 31);
   const bool tv = t < T_;
+  const T* kbase = qkv + (H + j) * D;
+  const T* vbase = qkv + (H + Hk + j) * D;
 
   Frag<T> qf[D / 16], df[D / 16];
   load_row_frags<T, D>(qf, qkv + (rb + t) * Qkv + h * D, tv, lane);
@@ -370,53 +454,72 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[i][e] = 0.0f;
 
-  const int lo = full ? 0 : max(0, t0 - W);
+  const int first = ((full ? 0 : max(0, t0 - W)) / BKV) * BKV;
   const int hi_k = min(T_, t0 + BQ);
+  const int ntile = (hi_k - first + BKV - 1) / BKV;
   const int w_lo = full ? 0 : max(0, tw - W), w_hi = min(T_, tw + 32);
-  for (int s0 = (lo / BKV) * BKV; s0 < hi_k; s0 += BKV) {
-    __syncthreads();
-    load_rows_lds<T, BKV, D>(Ks, qkv + (H + j) * D, rb + s0, T_ - s0, Qkv, tid);
-    load_rows_lds<T, BKV, D>(Vs, qkv + (H + Hk + j) * D, rb + s0, T_ - s0, Qkv, tid);
-    __syncthreads();
-    if (s0 >= w_hi || s0 + BKV <= w_lo) continue;
-    f32x16 sa[2], dp[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sa[sb][e] = 0.0f;
-        dp[sb][e] = 0.0f;
-      }
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        Frag<T> ka, va;
-        frag_load(ka, &Ks[sb * 32 + (lane & 31)][kc * 16 + hi * 8]);
-        frag_load(va, &Vs[sb * 32 + (lane & 31)][kc * 16 + hi * 8]);
-        mfma(sa[sb], ka, qf[kc]);
-        mfma(dp[sb], va, df[kc]);
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int sidx = s0 + sb * 32 + acc_row(e, lane);
-        const bool vis = tv && sidx <= t && (full || t - sidx <= W);
-        const float p = vis ? exp2f(sa[sb][e] * c2 - lt) : 0.0f;
-        dp[sb][e] = p * (dp[sb][e] - dt);
-      }
+  RowStage<T, BKV, D> kst, vst;
+  kst.load(kbase, rb + first, T_ - first, Qkv, tid);
+  vst.load(vbase, rb + first, T_ - first, Qkv, tid);
+  kst.template store<P>(Ks[0], tid);
+  vst.template store<P>(Vs[0], tid);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int s0 = first + it * BKV, cur = it & 1;
+    const bool more = it + 1 < ntile;
+    if (more) {
+      kst.load(kbase, rb + s0 + BKV, T_ - s0 - BKV, Qkv, tid);
+      vst.load(vbase, rb + s0 + BKV, T_ - s0 - BKV, Qkv, tid);
     }
+    if (s0 < w_hi && s0 + BKV > w_lo) {
+      const bool interior = (s0 + BKV - 1 <= tw) && (full || tw + 31 - s0 <= W);
+      f32x16 sa[2], dp[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        Frag<T> dsf;
+        for (int e = 0; e < 16; ++e) {
+          sa[sb][e] = 0.0f;
+          dp[sb][e] = 0.0f;
+        }
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) frag_set(dsf, jj, dp[sb][8 * c + jj]);
+        for (int kc = 0; kc < D / 16; ++kc) {
+          Frag<T> ka, va;
+          frag_load(ka, &Ks[cur][(sb * 32 + (lane & 31)) * P + kc * 16 + hi * 8]);
+          frag_load(va, &Vs[cur][(sb * 32 + (lane & 31)) * P + kc * 16 + hi * 8]);
+          mfma(sa[sb], ka, qf[kc]);
+          mfma(dp[sb], va, df[kc]);
+        }
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          Frag<T> kT;
-          frag_down<D + PAD>(kT, &Ks[0][0], sb * 32 + 16 * c, db * 32, lane);
-          mfma(dq[db], kT, dsf);
+        for (int e = 0; e < 16; ++e) {
+          bool vis = tv;
+          if (!interior) {
+            const int sidx = s0 + sb * 32 + acc_row(e, lane);
+            vis = tv && sidx <= t && (full || t - sidx <= W);
+          }
+          const float p = vis ? exp2f(sa[sb][e] * c2 - lt) : 0.0f;
+          dp[sb][e] = p * (dp[sb][e] - dt);
         }
       }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<T> dsf;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) frag_set(dsf, jj, dp[sb][8 * c + jj]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<T> kT;
+            frag_down<P>(kT, Ks[cur], sb * 32 + 16 * c, db * 32, lane);
+            mfma(dq[db], kT, dsf);
+          }
+        }
+    }
+    if (more) {
+      kst.template store<P>(Ks[cur ^ 1], tid);
+      vst.template store<P>(Vs[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
   if (tv) {
     T* qp = gqkv + (rb + t) * Qkv + h * D;
