@@ -59,9 +59,26 @@ def model_flops_per_token(w) -> float:
     return 6.0 * n_mat + 12.0 * H * D * kbar
 
 
-def lm_head_fwd_flops(w) -> float:
-    """Algorithmic FLOPs of one lm_head forward launch: 2 * N * V * C."""
-    return 2.0 * w.batch * w.seq_len * w.vocab * w.n_embd
+# Kernels the roofline figure can be taken for: the launch sites that run
+# it (timed with HIP events on the call's stream) and the algorithmic FLOPs
+# of those launches in one step.
+def _wgrad_flops(w):
+    N = w.batch * w.seq_len
+    C, Cq, Qkv, F = (w.n_embd, w.n_head * w.head_dim,
+                     (w.n_head + 2 * w.n_kv_head) * w.head_dim, w.mlp_hidden)
+    return w.n_layer * 2.0 * N * (Qkv * C + 2 * F * C + C * Cq)
+
+
+ROOF_KERNELS = {
+    "wgrad": dict(
+        sites="gemm.qkv.wgrad,gemm.fc.wgrad,gemm.mp.wgrad,gemm.o.wgrad",
+        desc="weight-gradient GEMMs of the blocks (split-K, fp32 atomics): "
+             "gemm_bf16_kernel<256, 192, 64, false, false, PreId, PreId, EpAtomic>",
+        flops=_wgrad_flops, pmc="profiles/gemm_wgrad_d12_pmc.txt"),
+    "lm_fwd": dict(
+        sites="gemm.lm.fwd", desc="lm_head GEMM + tanh softcap epilogue",
+        flops=lambda w: 2.0 * w.batch * w.seq_len * w.vocab * w.n_embd, pmc=None),
+}
 
 
 def param_total(w) -> int:
@@ -103,9 +120,21 @@ def main():
     ap.add_argument("--config", default="d12")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3)
-    ap.add_argument("--profile-site", default="gemm.lm.fwd",
-                    help="launch site timed with HIP events for the roofline figure")
+    ap.add_argument("--roofline-kernel", default="wgrad", choices=sorted(ROOF_KERNELS),
+                    help="kernel whose launches are timed with HIP events for the roofline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is "
               "not part of this library", file=sys.stderr)
@@ -126,7 +155,8 @@ def main():
     torch.cuda.synchronize()
 
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    B.profile_begin(args.profile_site)
+    roof_k = ROOF_KERNELS[args.roofline_kernel]
+    B.profile_begin(roof_k["sites"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
@@ -148,17 +178,18 @@ def main():
 
     roof = None
     if kern_n > 0:
-        avg_s = kern_ms / kern_n / 1e3
-        if args.profile_site == "gemm.lm.fwd":
-            achieved = lm_head_fwd_flops(w) / avg_s / 1e12
-            roof = {"kernel": "gemm.lm.fwd (lm_head GEMM + tanh softcap epilogue)",
-                    "bound": "mfma", "achieved": round(achieved, 2),
-                    "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                    "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4), "traffic": None,
-                    "avg_launch_ms": round(avg_s * 1e3, 4), "launches": kern_n}
-        else:
-            roof = {"kernel": args.profile_site, "avg_launch_ms": round(avg_s * 1e3, 4),
-                    "launches": kern_n}
+        flops = roof_k["flops"](w) * args.steps
+        achieved = flops / (kern_ms / 1e3) / 1e12
+        traffic = None
+        if roof_k["pmc"] and w.name == "d12":
+            from decoder_only_pretraining_amd.profiling import traffic_for
+            traffic = traffic_for(os.path.join(ROOT, roof_k["pmc"]))
+        roof = {"kernel": roof_k["desc"], "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4),
+                "traffic": traffic, "launches": kern_n,
+                "avg_launch_ms": round(kern_ms / kern_n, 4),
+                "algorithmic_flop_per_launch": round(flops / kern_n)}
 
     out = {
         "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1,

@@ -424,7 +424,7 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
                  int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, float* rowsum, hipStream_t s) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const int splits = (int)((K + kchunk - 1) / kchunk);
-  dim3 grid((unsigned)(tm * tn), 1, (unsigned)std::max(splits, 1));
+  dim3 grid((unsigned)(tm * tn * std::max(splits, 1)));
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
                      static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M, N, K,
                      kchunk, tm, tn, pa, pb, ep, rowsum);

@@ -20,15 +20,20 @@
 //
 // Block: 256 threads = 4 wavefronts in a 2x2 grid; each wavefront owns a
 // (BM/2) x (BN/2) accumulator tile of 32x32 MFMA blocks. Two LDS stages:
-// global loads for stage k+1 are issued before the MFMAs of stage k. The
+// stage k+1 streams in while the MFMAs of stage k run. When both operands
+// are K-major the fill uses direct global->LDS loads (no VGPR staging, no
+// ds_write: on gfx950 the ds_write bandwidth is about half the ds_read
+// bandwidth); products with an MN-major operand measured faster with the
+// register-staged fill, stored after the stage's MFMAs. The
 // epilogue reuses the LDS to turn the MFMA accumulator layout (four rows by
 // one column per lane) into row-contiguous 4-column vectors for the global
 // stores and the loads of epilogue operands.
 //
-// Grid: blockIdx.x enumerates output tiles, blockIdx.z splits K. Tile order
-// is XCD-aware: the dispatcher deals consecutive workgroups to the 8 XCDs in
-// turn, so the linear id is remapped to give each XCD a contiguous range of
-// tiles, walked in groups of 8 tile rows that share B panels in its L2.
+// Grid: blockIdx.x enumerates (K split, output tile) pairs, split-major.
+// Tile order is XCD-aware: the dispatcher deals consecutive workgroups to
+// the 8 XCDs in turn, so the linear id is remapped to give each XCD a
+// contiguous range of one split's tiles, walked in groups of 8 tile rows
+// that share B panels in its L2.
 #pragma once
 #include "device_common.h"
 
@@ -114,6 +119,53 @@ struct Loader {
   }
 };
 
+// Zero page for tile slots outside the matrix: lanes whose slot lies past
+// M, N or K copy zeros from here, so ragged K tails contribute nothing.
+__device__ __attribute__((aligned(256))) uint32_t g_zero_page[256];
+
+// Direct global->LDS stage loader (gfx950 global_load_lds, 16 bytes per
+// lane): one wavefront instruction fills a contiguous 1 KiB of LDS, lane l
+// writing bytes 16l .. 16l+15. Each lane therefore fetches the global
+// element that belongs at its LDS slot (undoing the XOR swizzle of K-major
+// tiles); slots in the row padding of MN-major tiles, or past the tile, are
+// masked off. The data never passes through VGPRs and no ds_write is
+// issued, so the LDS fill overlaps the MFMAs of the current stage.
+template <int ROWS, int BK, bool KMAJ>
+struct DirectLoader {
+  using Geo = TileGeom<ROWS, BK, KMAJ>;
+  static constexpr int BYTES = Geo::ELEMS * 2;
+  static constexpr int CHUNKS = (BYTES + 1023) / 1024;
+  __device__ __forceinline__ static void issue(const bf16* __restrict__ p, int64_t ld, int64_t mn0,
+                                               int64_t MN, int64_t k0, int64_t khi, bf16* lds,
+                                               int wave, int lane) {
+#pragma unroll
+    for (int c = wave; c < CHUNKS; c += 4) {
+      const int o = c * 1024 + lane * 16;  // byte offset of this lane's slot
+      int64_t mn, k;
+      bool slot = o < BYTES;
+      if (KMAJ) {
+        const int r = o / (BK * 2), pg = (o % (BK * 2)) / 16;
+        const int g = pg ^ ((r / Geo::RPS) & (Geo::G - 1));
+        mn = mn0 + r;
+        k = k0 + g * 8;
+      } else {
+        const int r = o / (Geo::PITCH * 2), cb = o % (Geo::PITCH * 2);
+        slot = slot && cb < ROWS * 2;
+        k = k0 + r;
+        mn = mn0 + cb / 2;
+      }
+      const bool ok = (mn < MN) && (k < khi);
+      const bf16* src = ok ? (KMAJ ? p + mn * ld + k : p + k * ld + mn)
+                           : reinterpret_cast<const bf16*>(g_zero_page) + (lane & 15) * 8;
+      if (slot)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)src,
+            (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(lds) + c * 1024), 16,
+            0, 0);
+    }
+  }
+};
+
 // Fragment of 32 operand rows starting at `row0` for the 16-wide
 // contraction slice `ks` (lane l: row row0 + l%32, slots 8*(l/32) .. +7).
 template <int ROWS, int BK, bool KMAJ>
@@ -146,6 +198,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep,
     float* rowpart) {
+  static_assert(!PA::kActive && !PB::kActive, "direct LDS loads take operands as stored");
   using GA = TileGeom<BM, BK, AK>;
   using GB = TileGeom<BN, BK, BKM>;
   constexpr int TM = BM / 64, TN = BN / 64;
@@ -161,10 +214,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // XCD-aware, grouped tile order
+  // XCD-aware, grouped tile order. The linear id runs over (split, tile),
+  // split-major; consecutive ids are dealt to the 8 XCDs in turn, so the id
+  // is remapped to give each XCD a contiguous range: its co-resident
+  // workgroups then share one K range and neighbouring tiles in its L2.
   int pid = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  const int ntiles = tiles_m * tiles_n;
+  const int split = pid / ntiles;
+  pid -= split * ntiles;
   constexpr int GM = 8;
   const int group = pid / (GM * tiles_n);
   const int first_m = group * GM;
@@ -172,13 +231,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   const int tm = first_m + (pid % (GM * tiles_n)) % gsize;
   const int tn = (pid % (GM * tiles_n)) / gsize;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t k_lo = (int64_t)blockIdx.z * kchunk;
+  const int64_t k_lo = (int64_t)split * kchunk;
   const int64_t k_hi = min(K, k_lo + kchunk);
 
-  Loader<BM, BK, AK> la;
-  Loader<BN, BK, BKM> lb;
-  pa.init();
-  pb.init();
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -188,25 +243,43 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int64_t nk = (k_hi - k_lo + BK - 1) / BK;
+  // When both operands are K-major they stream straight into LDS; otherwise
+  // both go through registers and are stored after the stage's MFMAs
+  // (mixing the two fills measured slower than either).
+  constexpr bool kDirect = AK && BKM;
+  using DA = DirectLoader<BM, BK, AK>;
+  using DB = DirectLoader<BN, BK, BKM>;
+  Loader<BM, BK, AK> ra;
+  Loader<BN, BK, BKM> rb;
+  auto fetch = [&](int64_t k0, int buf) {
+    if constexpr (kDirect) {
+      DA::issue(A, lda, m0, M, k0, k_hi, As[buf], wave, lane);
+      DB::issue(B, ldb, n0, N, k0, k_hi, Bs[buf], wave, lane);
+    } else {
+      ra.load(A, lda, m0, M, k0, k_hi, tid);
+      rb.load(B, ldb, n0, N, k0, k_hi, tid);
+    }
+  };
+  auto place = [&](int64_t k0, int buf) {
+    if constexpr (!kDirect) {
+      ra.store(As[buf], m0, k0, tid, pa);
+      rb.store(Bs[buf], n0, k0, tid, pb);
+    }
+  };
   if (nk > 0) {
-    la.load(A, lda, m0, M, k_lo, k_hi, tid);
-    lb.load(B, ldb, n0, N, k_lo, k_hi, tid);
-    la.store(As[0], m0, k_lo, tid, pa);
-    lb.store(Bs[0], n0, k_lo, tid, pb);
+    fetch(k_lo, 0);
+    place(k_lo, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's LDS fills landed
   __syncthreads();
   // Fragments of the next 16-wide k-slice are read into a second register
   // set before the MFMAs of the current slice are issued, so LDS latency
-  // overlaps matrix work; the next stage's LDS stores follow the last
-  // slice's MFMAs.
+  // overlaps matrix work; the next stage streams in meanwhile.
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     const int64_t kn = k_lo + (kt + 1) * BK;
-    if (more) {
-      la.load(A, lda, m0, M, kn, k_hi, tid);
-      lb.load(B, ldb, n0, N, kn, k_hi, tid);
-    }
+    if (more) fetch(kn, cur ^ 1);
     Frag<bf16> a[2][TM], b[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) read_frag<BM, BK, AK>(a[0][i], As[cur], wm * (BM / 2) + i * 32, 0, lane);
@@ -230,10 +303,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         for (int j = 0; j < TN; ++j) mfma(acc[i][j], a[p][i], b[p][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      la.store(As[cur ^ 1], m0, kn, tid, pa);
-      lb.store(Bs[cur ^ 1], n0, kn, tid, pb);
-    }
+    if (more) place(kn, cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): next stage's direct fills landed
     __syncthreads();
   }
 

@@ -34,9 +34,22 @@ struct Profiler {
 };
 static Profiler g_prof;
 
+// Does `name` start with one of the comma-separated prefixes?
+static bool site_selected(const char* name) {
+  const std::string& p = g_prof.prefix;
+  size_t b = 0;
+  while (b <= p.size()) {
+    size_t e = p.find(',', b);
+    if (e == std::string::npos) e = p.size();
+    if (e > b && strncmp(name, p.c_str() + b, e - b) == 0) return true;
+    b = e + 1;
+  }
+  return false;
+}
+
 template <class Fn>
 static void site(const char* name, hipStream_t s, Fn&& fn) {
-  if (g_prof.on && strncmp(name, g_prof.prefix.c_str(), g_prof.prefix.size()) == 0) {
+  if (g_prof.on && site_selected(name)) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     while (g_prof.pool.size() < g_prof.used + 2) {
       hipEvent_t e;

@@ -1,0 +1,139 @@
+"""Summaries of rocprofv3 output for the measurement records kept in profiles/.
+
+    python -m decoder_only_pretraining_amd.profiling stats KERNEL_STATS_CSV \
+        --title TITLE --command CMD --steps K [--top 30] --out FILE
+    python -m decoder_only_pretraining_amd.profiling pmc \
+        --fetch FETCH_CSV --write WRITE_CSV --copy-fetch CSV --copy-write CSV \
+        --copy-bytes BYTES --kernel SUBSTRING --command CMD --out FILE
+
+`stats` turns a `rocprofv3 --kernel-trace --stats --output-format csv`
+kernel_stats.csv into a per-kernel table (total, share, calls, average).
+`pmc` averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernels
+whose name contains SUBSTRING, calibrates both counters with a plain device
+copy of known size, and records the HBM bytes per launch together with a
+hash of the GEMM sources, so a later change of the kernel invalidates the
+figure (see `traffic_for`).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemm_core.h", "gemm.hip")]
+
+
+def source_hash(paths=GEMM_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _short(name: str, n: int = 120) -> str:
+    name = name.replace("void gk::", "").replace("gk::", "")
+    cut = name.find("(")
+    if cut > 0:
+        name = name[:cut]
+    return name[:n]
+
+
+def stats_table(path: str, steps: int, top: int = 30):
+    rows = list(csv.DictReader(open(path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"{'ms/step':>9} {'share':>6} {'calls/step':>10} {'avg us':>9}  kernel"]
+    for r in rows[:top]:
+        t = float(r["TotalDurationNs"])
+        lines.append(f"{t / steps / 1e6:9.3f} {100 * t / total:5.1f}% "
+                     f"{int(r['Calls']) / steps:10.1f} {float(r['AverageNs']) / 1e3:9.1f}  "
+                     f"{_short(r['Name'])}")
+    lines.append(f"{total / steps / 1e6:9.3f} total kernel time per step ({len(rows)} kernels)")
+    return lines
+
+
+def _counter_avg(path: str, counter: str, kernel_substr: str | None):
+    """Average per dispatch of `counter` over dispatches whose kernel name
+    contains `kernel_substr` (None: the dispatch with the largest value)."""
+    vals, best = [], None
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        v = float(r["Counter_Value"])
+        name = r.get("Kernel_Name", "")
+        if kernel_substr is None:
+            if best is None or v > best[0]:
+                best = (v, name)
+        elif kernel_substr in name:
+            vals.append(v)
+    if kernel_substr is None:
+        return best
+    return (sum(vals) / len(vals) if vals else float("nan"), len(vals))
+
+
+def traffic_for(summary_path: str):
+    """HBM bytes per launch recorded in a pmc summary, or None if the file
+    is missing or the GEMM sources changed since the counters were taken."""
+    if not os.path.exists(summary_path):
+        return None
+    kv = {}
+    for line in open(summary_path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--steps", type=int, required=True)
+    s.add_argument("--top", type=int, default=30)
+    s.add_argument("--out", required=True)
+    p = sub.add_parser("pmc")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--command",
+              "--out", "--title"):
+        p.add_argument(a, required=True)
+    p.add_argument("--copy-bytes", type=float, required=True)
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        lines = [f"# {args.title}", f"# command: {args.command}",
+                 f"# per step = totals / {args.steps} profiled steps (warmup included)", ""]
+        lines += stats_table(args.csv, args.steps, args.top)
+        open(args.out, "w").write("\n".join(lines) + "\n")
+    else:
+        f_avg, f_n = _counter_avg(args.fetch, "FETCH_SIZE", args.kernel)
+        w_avg, w_n = _counter_avg(args.write, "WRITE_SIZE", args.kernel)
+        cf, cf_name = _counter_avg(args.copy_fetch, "FETCH_SIZE", None)
+        cw, cw_name = _counter_avg(args.copy_write, "WRITE_SIZE", None)
+        fs = args.copy_bytes / (cf * 1024.0)
+        ws = args.copy_bytes / (cw * 1024.0)
+        traffic = f_avg * 1024.0 * fs + w_avg * 1024.0 * ws
+        lines = [f"# {args.title}",
+                 f"# command: {args.command}",
+                 f"kernel: {args.kernel}",
+                 f"source_sha256: {source_hash()}",
+                 f"FETCH_SIZE_kib_per_dispatch: {f_avg:.1f} (over {f_n} dispatches)",
+                 f"WRITE_SIZE_kib_per_dispatch: {w_avg:.1f} (over {w_n} dispatches)",
+                 f"copy_bytes: {args.copy_bytes:.0f}",
+                 f"copy_FETCH_SIZE_kib: {cf:.1f} ({_short(cf_name, 60)})",
+                 f"copy_WRITE_SIZE_kib: {cw:.1f} ({_short(cw_name, 60)})",
+                 f"fetch_scale: {fs:.4f}",
+                 f"write_scale: {ws:.4f}",
+                 f"traffic_bytes_per_launch: {traffic:.0f}"]
+        open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -166,9 +166,10 @@ int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Host only; measurement support. After gpt_profile_begin(prefix), every
+ * Host only; measurement support. After gpt_profile_begin(prefixes), every
  * kernel launch of gpt_fwd_bwd / gpt_fwd whose launch-site name starts with
- * `prefix` is bracketed by two HIP events recorded on the call's stream.
+ * one of the comma-separated `prefixes` is bracketed by two HIP events
+ * recorded on the call's stream.
  * Site names: "embed.fwd", "gemm.qkv.fwd", "rope.fwd", "attn.fwd",
  * "gemm.o.fwd", "gemm.fc.fwd", "gemm.mp.fwd", "gemm.lm.fwd", "loss",
  * "gemm.lm.dgrad", "gemm.lm.wgrad", "gemm.mp.dgrad", "gemm.mp.wgrad",
