@@ -366,9 +366,10 @@ def test_finite_differences_tiny():
     assert worst < 1e-6
 
 
-def _torch_model_loss(cfg, params, tok, tgt):
+def _torch_model_loss(cfg, params, tok, tgt, linear=F.linear):
     """The model assembled from torch library ops (rms_norm, SDPA with an
-    explicit mask, cross_entropy) for an autograd cross-check."""
+    explicit mask, cross_entropy) for an autograd cross-check. ``linear``
+    computes the six block linears (the ve gate and lm_head use F.linear)."""
     L, C, H, Hk, D = cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_kv_head, cfg.head_dim
     B, T = tok.shape
     offs, _ = oracle.param_offsets(cfg)
@@ -389,9 +390,9 @@ def _torch_model_loss(cfg, params, tok, tgt):
     for l in range(L):
         x = Pt["resid_lambdas"][l] * x + Pt["x0_lambdas"][l] * x0
         xn = F.rms_norm(x, (C,), eps=eps)
-        q = F.linear(xn, Pt[f"l{l}.q"]).view(B, T, H, D)
-        k = F.linear(xn, Pt[f"l{l}.k"]).view(B, T, Hk, D)
-        v = F.linear(xn, Pt[f"l{l}.v"]).view(B, T, Hk, D)
+        q = linear(xn, Pt[f"l{l}.q"]).view(B, T, H, D)
+        k = linear(xn, Pt[f"l{l}.k"]).view(B, T, Hk, D)
+        v = linear(xn, Pt[f"l{l}.v"]).view(B, T, Hk, D)
         q = F.rms_norm(rot(q), (D,), eps=eps)
         k = F.rms_norm(rot(k), (D,), eps=eps)
         if oracle.layer_has_ve(l, L):
@@ -405,9 +406,9 @@ def _torch_model_loss(cfg, params, tok, tgt):
         y = F.scaled_dot_product_attention(
             q.transpose(1, 2), k.transpose(1, 2).repeat_interleave(H // Hk, 1),
             v.transpose(1, 2).repeat_interleave(H // Hk, 1), attn_mask=mask)
-        x = x + F.linear(y.transpose(1, 2).reshape(B, T, H * D), Pt[f"l{l}.o"])
-        x = x + F.linear(F.relu(F.linear(F.rms_norm(x, (C,), eps=eps), Pt[f"l{l}.fc"])).square(),
-                         Pt[f"l{l}.mp"])
+        x = x + linear(y.transpose(1, 2).reshape(B, T, H * D), Pt[f"l{l}.o"])
+        x = x + linear(F.relu(linear(F.rms_norm(x, (C,), eps=eps), Pt[f"l{l}.fc"])).square(),
+                       Pt[f"l{l}.mp"])
     z = F.linear(F.rms_norm(x, (C,), eps=eps), Pt["lm_head"])
     c = cfg.softcap * torch.tanh(z / cfg.softcap)
     return F.cross_entropy(c.view(B * T, -1), torch.from_numpy(tgt).long().view(-1),
@@ -473,3 +474,94 @@ def test_fp8_qdq_scaling():
     assert abs(q[i] - x[i]) <= 1e-6 * abs(x[i])        # amax maps to +-fmax exactly
     assert np.max(np.abs(q - x)) <= np.max(np.abs(x)) * 2.0 ** -4
     assert np.all(oracle.fp8.qdq(np.zeros(5), "e5m2") == 0)
+
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_encode_decode_all_codes(fmt, tdt):
+    """Byte codes and values agree with torch's float8 dtypes on every
+    finite code (library)."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    vals = codes.view(tdt).double().numpy()
+    ok = np.isfinite(vals)
+    np.testing.assert_array_equal(oracle.fp8.encode(vals[ok], fmt), codes.numpy()[ok])
+    np.testing.assert_array_equal(oracle.fp8.decode(codes.numpy()[ok], fmt), vals[ok])
+
+
+def _torch_codes(x, fmt, tdt):
+    """Per-tensor codes from torch: fp32 scale fmax / amax, fp32 product,
+    clamp, torch's round-to-nearest-even float8 cast."""
+    fmax = oracle.fp8.FORMATS[fmt][2]
+    xt = torch.from_numpy(np.asarray(x)).float()
+    amax = xt.abs().max()
+    s = torch.tensor(fmax, dtype=torch.float32) / amax if amax > 0 else torch.tensor(1.0)
+    return (xt * s).clamp(-fmax, fmax).to(tdt).view(torch.uint8).numpy(), s.item()
+
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_quantize_codes_match_torch(fmt, tdt):
+    rng = np.random.default_rng(12)
+    for scale in (1e-3, 1.0, 40.0):
+        x = (rng.standard_normal(50000) * scale).astype(np.float32)
+        x[rng.integers(0, x.size, 50)] = 0.0
+        codes, s = oracle.fp8.quantize(x, fmt)
+        ref, s_ref = _torch_codes(x, fmt, tdt)
+        assert np.float32(s) == np.float32(s_ref)
+        np.testing.assert_array_equal(codes, ref)
+        # the element of largest magnitude maps to +-fmax
+        i = np.argmax(np.abs(x))
+        assert abs(oracle.fp8.decode(codes[i:i + 1], fmt)[0]) == oracle.fp8.FORMATS[fmt][2]
+    # all-zero tensor: scale 1, all codes 0
+    codes, s = oracle.fp8.quantize(np.zeros(7, np.float32), fmt)
+    assert s == 1.0 and not codes.any()
+
+
+class _FakeQuantLinear(torch.autograd.Function):
+    """y = Q(x) Q(W)^T; g_x = Q(g_y) Q(W); g_W = Q(g_y)^T Q(x), with Q the
+    per-tensor quantise-dequantise built from torch's float8 casts."""
+
+    @staticmethod
+    def _q(t, fmt, tdt):
+        codes, s = _torch_codes(t.detach().numpy(), fmt, tdt)
+        v = torch.from_numpy(codes.copy()).view(tdt).double()
+        return (v / s).reshape(t.shape)
+
+    @staticmethod
+    def forward(ctx, x, w):
+        ctx.save_for_backward(x, w)
+        e4 = torch.float8_e4m3fn
+        return _FakeQuantLinear._q(x, "e4m3", e4) @ _FakeQuantLinear._q(w, "e4m3", e4).T
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, w = ctx.saved_tensors
+        e4, e5 = torch.float8_e4m3fn, torch.float8_e5m2
+        q = _FakeQuantLinear._q
+        g = q(gy.reshape(-1, gy.shape[-1]), "e5m2", e5)
+        xq = q(x.reshape(-1, x.shape[-1]), "e4m3", e4)
+        wq = q(w, "e4m3", e4)
+        return (g @ wq).reshape(x.shape), g.T @ xq
+
+
+@pytest.mark.parametrize("variant", ["tiny", "tiny_gqa"])
+def test_fp8_model_matches_torch_fake_quant(variant):
+    """The oracle's fp8 mode against torch autograd through a fake-quant
+    linear whose rounding is torch's own float8 cast."""
+    cfg = W.get("tiny").with_(fp8_linears=True)
+    if variant == "tiny_gqa":
+        cfg = cfg.with_(n_head=4, n_kv_head=2, head_dim=32, n_layer=3, short_window=7)
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 23).astype(np.float64)
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    loss, g = oracle.forward_backward(cfg, p, tok, tgt)
+    pt = torch.from_numpy(p.copy()).requires_grad_()
+    ref = _torch_model_loss(cfg, pt, tok, tgt, linear=_FakeQuantLinear.apply)
+    ref.backward()
+    assert abs(loss - ref.item()) < 1e-9 * abs(loss)
+    ref_g = pt.grad.numpy()
+    for name, (o, s) in offs.items():
+        n = int(np.prod(s))
+        a, b = g[o:o + n], ref_g[o:o + n]
+        assert np.linalg.norm(a - b) <= 1e-8 * max(np.linalg.norm(b), 1e-30), name
+    # fp8 really changes the result relative to the unquantised model
+    l0, _ = oracle.forward_backward(cfg, p, tok, tgt, fp8=False)
+    assert abs(l0 - loss) > 1e-6
