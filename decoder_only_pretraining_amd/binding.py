@@ -22,8 +22,9 @@ STATUS = {0: "GPT_OK", -1: "GPT_E_INVAL", -2: "GPT_E_NULLPTR", -3: "GPT_E_ALIGN"
 
 EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_param_info",
            "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region", "gpt_fwd_bwd",
-           "gpt_fwd", "gpt_status_string", "gpt_last_error", "gpt_profile_begin",
-           "gpt_profile_end"]
+           "gpt_fwd", "gpt_fp8_quantize", "gpt_status_string", "gpt_last_error",
+           "gpt_profile_begin", "gpt_profile_end"]
+FP8_E4M3, FP8_E5M2 = 0, 1
 
 
 class GptConfig(ctypes.Structure):
@@ -70,6 +71,8 @@ def lib():
                                   c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p]
         L.gpt_fwd.argtypes = [P(GptConfig), c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                               c.c_void_p, c.c_size_t, c.c_void_p]
+        L.gpt_fp8_quantize.argtypes = [c.c_void_p, c.c_int32, c.c_int64, c.c_int64, c.c_int32,
+                                       c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p]
         L.gpt_status_string.restype = c.c_char_p
         L.gpt_status_string.argtypes = [c.c_int]
         L.gpt_last_error.restype = c.c_char_p
@@ -79,7 +82,7 @@ def lib():
         L.gpt_profile_end.restype = c.c_int
         for name in ("gpt_config_validate", "gpt_param_count", "gpt_param_info",
                      "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region",
-                     "gpt_fwd_bwd", "gpt_fwd"):
+                     "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -171,6 +174,20 @@ def fwd(cfg, params, tokens, targets, loss, workspace, stream=None):
                        targets.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
                        workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check("gpt_fwd", st)
+
+
+def fp8_quantize(src, fmt, codes=None, codes_t=None, pitch_t=0, amax=None, stream=None):
+    """Per-tensor fp8 codes of the 2-D device tensor `src` (fp32 or bf16):
+    row-major into `codes` and/or transposed into `codes_t` [cols, pitch_t]
+    (uint8 device tensors), the bit pattern of max |src| into `amax`
+    (int32 device tensor of one element)."""
+    import torch
+    rows, cols = src.shape
+    dt = GPT_DT_BF16 if src.dtype == torch.bfloat16 else GPT_DT_F32
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib().gpt_fp8_quantize(src.data_ptr(), dt, rows, cols, fmt, ptr(codes), ptr(codes_t),
+                                pitch_t, ptr(amax), _stream_ptr(stream))
+    _check("gpt_fp8_quantize", st)
 
 
 def profile_begin(site_prefix: str):

@@ -84,6 +84,13 @@ __device__ __forceinline__ void mfma(f32x16& acc, const Frag<float>& a, const Fr
   for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[j], b.hi[j], acc, 0, 0, 0);
 }
 
+// Per-tensor fp8 scale fmax / amax from the bit pattern of amax (fp32,
+// correctly rounded); 1 when amax is 0 or not finite.
+__device__ __forceinline__ float fp8_scale(uint32_t bits, float fmax) {
+  const float a = __uint_as_float(bits);
+  return (a > 0.0f && a <= 3.402823466e38f) ? __fdiv_rn(fmax, a) : 1.0f;
+}
+
 // Output row (within a 32x32 tile) of accumulator element e for lane l.
 __device__ __forceinline__ int acc_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
 

@@ -425,9 +425,9 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const int splits = (int)((K + kchunk - 1) / kchunk);
   dim3 grid((unsigned)(tm * tn * std::max(splits, 1)));
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
-                     static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M, N, K,
-                     kchunk, tm, tn, pa, pb, ep, rowsum);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq>), grid, dim3(256),
+                     0, s, static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M,
+                     N, K, kchunk, tm, tn, pa, pb, ep, rowsum, NoDeq{});
 }
 
 template <bool AK, bool BKM, class PA, class PB, class EP>
@@ -443,10 +443,109 @@ void run_bf16(Tile t, const void* A, int64_t lda, const void* B, int64_t ldb, in
     launch_bf16<128, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
 }
 
+// ------------------------------------------------------------ fp8 dispatch
+// fp8 operands go through the same kernel as 2-byte units (a pair of codes
+// per unit), so K, the leading dimensions and the K chunk are halved.
+template <int BM, int BN, int MODE, class EP>
+void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M, int64_t N,
+               int64_t K, int64_t kchunk, EP ep, const Deq8& dq, hipStream_t s) {
+  const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+  const int64_t Kp = K / 2, kc = kchunk / 2;
+  const int splits = (int)((Kp + kc - 1) / kc);
+  dim3 grid((unsigned)(tm * tn * std::max(splits, 1)));
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, true, true, MODE, PreId, PreId, EP, Deq8>), grid,
+                     dim3(256), 0, s, reinterpret_cast<const bf16*>(A), lda / 2,
+                     reinterpret_cast<const bf16*>(B), ldb / 2, M, N, Kp, kc, tm, tn, PreId{},
+                     PreId{}, ep, nullptr, dq);
+}
+
+template <int MODE, class EP>
+void run_f8(Tile t, const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M,
+            int64_t N, int64_t K, int64_t kchunk, EP ep, const Deq8& dq, hipStream_t s) {
+  if (t.bm == 256 && t.bn == 256)
+    launch_f8<256, 256, MODE>(A, lda, B, ldb, M, N, K, kchunk, ep, dq, s);
+  else if (t.bm == 256 && t.bn == 192)
+    launch_f8<256, 192, MODE>(A, lda, B, ldb, M, N, K, kchunk, ep, dq, s);
+  else if (t.bm == 256 && t.bn == 128)
+    launch_f8<256, 128, MODE>(A, lda, B, ldb, M, N, K, kchunk, ep, dq, s);
+  else
+    launch_f8<128, 128, MODE>(A, lda, B, ldb, M, N, K, kchunk, ep, dq, s);
+}
+
 }  // namespace gk
 
 namespace gpt {
 using namespace gk;
+
+static Deq8 to_deq(const Fp8Deq& q) {
+  Deq8 d{};
+  d.amax = q.amax;
+  d.axis = q.axis;
+  d.nseg = q.nseg;
+  d.end[0] = q.end[0];
+  d.end[1] = q.end[1];
+  for (int i = 0; i < 3; ++i) {
+    d.sa[i] = q.sa[i < q.nseg ? i : 0];
+    d.sb[i] = q.sb[i < q.nseg ? i : 0];
+  }
+  d.fa = q.fa == FP8_E4M3 ? 448.0f : 57344.0f;
+  d.fb = q.fb == FP8_E4M3 ? 448.0f : 57344.0f;
+  return d;
+}
+
+// MODE of an fp8 product: 1 for e4m3 x e4m3 (forward), 2 for e5m2 x e4m3
+// (gradient products).
+#define GPT_F8_DISPATCH(dq, call1, call2) \
+  do {                                     \
+    if ((dq).fa == FP8_E5M2) call2;        \
+    else call1;                            \
+  } while (0)
+
+void gemm8_store(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s) {
+  const Tile t = pick_tile(M, N);
+  const Deq8 q = to_deq(dq);
+  GPT_F8_DISPATCH(dq, (run_f8<1>(t, A, lda, B, ldb, M, N, K, K, mk_store<bf16>(C, N), q, s)),
+                  (run_f8<2>(t, A, lda, B, ldb, M, N, K, K, mk_store<bf16>(C, N), q, s)));
+}
+
+void gemm8_resid(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const float* R, float* C,
+                 hipStream_t s) {
+  run_f8<1>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_resid(R, C, N), to_deq(dq), s);
+}
+
+void gemm8_relu2(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s) {
+  run_f8<1>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_relu2<bf16>(C, N), to_deq(dq), s);
+}
+
+void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                    const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const void* H, void* C,
+                    hipStream_t s) {
+  run_f8<2>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_relu2bwd<bf16>(H, C, N), to_deq(dq),
+            s);
+}
+
+void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+               const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, hipStream_t s) {
+  run_f8<2>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_f32(C, N, 0), to_deq(dq), s);
+}
+
+void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                 hipStream_t s) {
+  const Tile t = pick_tile_wgrad(M, N);
+  const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+  const int64_t kc = 2 * pick_kchunk(tiles, K / 2);  // in codes
+  const Deq8 q = to_deq(dq);
+  if (kc >= K) {
+    run_f8<2>(t, A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0), q, s);
+    return;
+  }
+  if (!accumulate) launch_zero(C, M * N, s);
+  run_f8<2>(t, A, lda, B, ldb, M, N, K, kc, mk_atomic(C, N), q, s);
+}
 
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s) {

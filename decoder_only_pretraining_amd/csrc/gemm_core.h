@@ -37,6 +37,8 @@
 #pragma once
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace gk {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -193,12 +195,66 @@ __device__ __forceinline__ void read_frag(Frag<bf16>& f, const bf16* lds, int ro
   }
 }
 
-template <int BM, int BN, int BK, bool AK, bool BKM, class PA, class PB, class EP>
+// ---------------------------------------------------------------- fp8 mode
+// An fp8 operand tile is stored exactly like a bf16 K-major tile with BK
+// 2-byte units per row: a 128-byte row holds 128 codes. One
+// v_mfma_f32_32x32x64_f8f6f4 consumes a 64-wide contraction slice; lane l
+// supplies 32 codes of row l % 32, bytes 32*(l/32) .. +31 of the slice. The
+// instruction sums over all 64 slots, so any fixed assignment of lane bytes
+// to contraction slots is correct as long as A and B use the same one.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+struct Frag8 {
+  i32x8 v;
+};
+
+template <int ROWS, int BK>
+__device__ __forceinline__ void read_frag8(Frag8& f, const bf16* lds, int row0, int ks, int lane) {
+  using Geo = TileGeom<ROWS, BK, true>;
+  const int r = row0 + (lane & 31);
+  const int g = 4 * ks + 2 * (lane >> 5);
+  const U128 lo = *reinterpret_cast<const U128*>(lds + Geo::kmaj_off(r, g));
+  const U128 hi = *reinterpret_cast<const U128*>(lds + Geo::kmaj_off(r, g + 1));
+  f.v = i32x8{(int)lo.w[0], (int)lo.w[1], (int)lo.w[2], (int)lo.w[3],
+              (int)hi.w[0], (int)hi.w[1], (int)hi.w[2], (int)hi.w[3]};
+}
+
+// MODE 0: bf16 operands. MODE 1: e4m3 x e4m3. MODE 2: e5m2 (A) x e4m3 (B).
+template <int MODE>
+__device__ __forceinline__ void mfma8(f32x16& acc, const Frag8& a, const Frag8& b) {
+  constexpr int FA = MODE == 2 ? 1 : 0;  // operand format codes: 0 e4m3, 1 e5m2
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, acc, FA, 0, 0, 0, 0, 0);
+}
+
+// Dequantisation of an fp8 product. NoDeq: bf16 products. Deq8: in segment
+// i of the M, N or K index (axis 0, 1, 2; at most 3 segments) the code sums
+// are multiplied by f_i = 1 / (s_a,i * s_b,i), s = fmax / amax (1 if amax is
+// 0 or not finite). Along K the accumulator is rescaled by f_old / f_new
+// where the segment changes, and by the last f at the end.
+struct NoDeq {
+  static constexpr bool kOn = false;
+};
+struct Deq8 {
+  static constexpr bool kOn = true;
+  const uint32_t* amax;
+  int axis, nseg;
+  int64_t end[2];
+  int sa[3], sb[3];
+  float fa, fb;
+  __device__ __forceinline__ int seg(int64_t i) const {
+    return (nseg > 1 && i >= end[0]) + (nseg > 2 && i >= end[1]);
+  }
+};
+
+template <int BM, int BN, int BK, bool AK, bool BKM, int MODE, class PA, class PB, class EP,
+          class DQ>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep,
-    float* rowpart) {
+    float* rowpart, DQ dq) {
   static_assert(!PA::kActive && !PB::kActive, "direct LDS loads take operands as stored");
+  constexpr bool F8 = MODE != 0;
+  static_assert(!F8 || (AK && BKM), "fp8 products take K-major operands");
+  static_assert(F8 == DQ::kOn, "fp8 products need a dequantisation");
   using GA = TileGeom<BM, BK, AK>;
   using GB = TileGeom<BN, BK, BKM>;
   constexpr int TM = BM / 64, TN = BN / 64;
@@ -242,6 +298,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // fp8: dequantisation factor of each segment; the K segment in progress
+  float fdq[3] = {1.0f, 1.0f, 1.0f};
+  int kseg = 0;
+  if constexpr (F8) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (i < dq.nseg)
+        fdq[i] = 1.0f / (fp8_scale(dq.amax[dq.sa[i]], dq.fa) * fp8_scale(dq.amax[dq.sb[i]], dq.fb));
+    if (dq.axis == 2) kseg = dq.seg(2 * k_lo);
+  }
+
   const int64_t nk = (k_hi - k_lo + BK - 1) / BK;
   // When both operands are K-major they stream straight into LDS; otherwise
   // both go through registers and are stored after the stage's MFMAs
@@ -280,6 +347,44 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const bool more = kt + 1 < nk;
     const int64_t kn = k_lo + (kt + 1) * BK;
     if (more) fetch(kn, cur ^ 1);
+    if constexpr (F8) {
+      // 64-wide contraction slices; per-tensor scales may change along K
+      constexpr int KS = BK / 32;
+      Frag8 a[2][TM], b[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) read_frag8<BM, BK>(a[0][i], As[cur], wm * (BM / 2) + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) read_frag8<BN, BK>(b[0][j], Bs[cur], wn * (BN / 2) + j * 32, 0, lane);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int p = ks & 1;
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            read_frag8<BM, BK>(a[p ^ 1][i], As[cur], wm * (BM / 2) + i * 32, ks + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            read_frag8<BN, BK>(b[p ^ 1][j], Bs[cur], wn * (BN / 2) + j * 32, ks + 1, lane);
+        }
+        if (dq.axis == 2) {
+          const int sg = dq.seg(2 * (k_lo + kt * BK) + 64 * ks);
+          if (sg != kseg) {
+            const float r = fdq[kseg] / fdq[sg];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j) acc[i][j] *= r;
+            kseg = sg;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) mfma8<MODE>(acc[i][j], a[p][i], b[p][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
     Frag<bf16> a[2][TM], b[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) read_frag<BM, BK, AK>(a[0][i], As[cur], wm * (BM / 2) + i * 32, 0, lane);
@@ -303,6 +408,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         for (int j = 0; j < TN; ++j) mfma(acc[i][j], a[p][i], b[p][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    }
     if (more) place(kn, cur ^ 1);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): next stage's direct fills landed
     __syncthreads();
@@ -323,7 +429,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int64_t n = nw + j * 32 + (lane & 31);
-        const float v = ep.value(m, n, acc[i][j][e]);
+        float x = acc[i][j][e];
+        if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.axis == 1 ? dq.seg(n) : kseg];
+        const float v = ep.value(m, n, x);
         if (EP::kRowSum && m < M && n < N) rs += ep.rowterm(v);
         stage[r * SP + j * 32 + (lane & 31)] = v;
       }

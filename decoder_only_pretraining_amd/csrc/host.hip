@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 
 #include "internal.h"
@@ -95,6 +96,7 @@ Dims make_dims(const gpt_config& c) {
   d.Qkv = d.Cq + 2 * d.Ckv;
   d.G = d.Hk > 0 ? d.H / d.Hk : 0;
   d.bf16 = c.compute_dtype == GPT_DT_BF16;
+  d.fp8 = c.fp8_linears != 0;
   d.act_bytes = d.bf16 ? 2 : 4;
   d.theta = c.rope_theta;
   d.eps = c.norm_eps;
@@ -132,7 +134,8 @@ static int validate(const gpt_config* c) {
     return fail(GPT_E_INVAL, "rope_theta must be finite and > 1");
   if (!(std::isfinite(c->norm_eps) && c->norm_eps > 0.0f)) return fail(GPT_E_INVAL, "norm_eps must be > 0");
   if (!(std::isfinite(c->softcap) && c->softcap > 0.0f)) return fail(GPT_E_INVAL, "softcap must be > 0");
-  if (c->fp8_linears) return fail(GPT_E_UNSUPPORTED, "fp8 linears are not built into this library");
+  if (c->fp8_linears && c->compute_dtype != GPT_DT_BF16)
+    return fail(GPT_E_INVAL, "fp8 linears need bf16 compute");
   return GPT_OK;
 }
 
@@ -206,6 +209,13 @@ Plan make_plan(const Dims& d) {
   p.l_xn2 = ltake(N * d.C * A);
   p.l_r2 = ltake(N * 4);
   p.l_u = ltake(N * d.F * A);
+  if (d.fp8) {  // transposed activation codes for the weight gradients
+    const size_t Np = (size_t)((d.N + 127) / 128 * 128);
+    p.l_x8t = ltake(d.C * Np);
+    p.l_a8t = ltake(d.Cq * Np);
+    p.l_x28t = ltake(d.C * Np);
+    p.l_h8t = ltake(d.F * Np);
+  }
   p.layer_bytes = lo;
   p.layers = take(lo * d.L);
   p.xf = take(N * d.C * A);
@@ -228,6 +238,20 @@ Plan make_plan(const Dims& d) {
   p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
   p.veg_splits = 256;
   p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
+  if (d.fp8) {
+    auto P128 = [](int64_t x) { return (size_t)((x + 127) / 128 * 128); };
+    const size_t C = d.C, Cq = d.Cq, F = d.F, Qkv = d.Qkv;
+    p.Np = (int64_t)P128(d.N);
+    const size_t Np = (size_t)p.Np;
+    p.amax = take((size_t)16 * d.L * 4);
+    p.w8_layer = al(Qkv * C + C * Cq + F * C + C * F);
+    p.w8 = take(p.w8_layer * d.L);
+    p.w8t_layer = al(C * P128(Qkv) + Cq * P128(C) + C * P128(F) + F * P128(C));
+    p.w8t = take(p.w8t_layer * d.L);
+    const size_t wmax = std::max(std::max(C, Cq), std::max(F, Qkv));
+    p.q8 = take(N * wmax);
+    p.g8t = take(std::max(std::max(C, F), Qkv) * Np);
+  }
   p.total = o;
   return p;
 }
@@ -296,7 +320,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   if (d.bf16) {
     std::vector<CastSeg> segs;
     for (int l = 0; l < d.L; ++l) {
-      segs.push_back({F.q[l], F.mp[l] + (int64_t)d.C * d.F - F.q[l]});  // q k v o fc mp
+      if (!d.fp8) segs.push_back({F.q[l], F.mp[l] + (int64_t)d.C * d.F - F.q[l]});  // q k v o fc mp
       if (F.veg[l] >= 0) segs.push_back({F.veg[l], (int64_t)d.Hk * d.C});
     }
     segs.push_back({F.lm, (int64_t)d.V * d.C});
@@ -308,8 +332,104 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   const size_t xstride = (size_t)d.N * d.C;
   auto X = [&](int l) { return reinterpret_cast<float*>(W + P.x) + (size_t)l * xstride; };
   auto LY = [&](int l, size_t off) { return W + P.layers + (size_t)l * P.layer_bytes + off; };
+  auto LY8 = [&](int l, size_t off) { return reinterpret_cast<uint8_t*>(LY(l, off)); };
   float* xin = reinterpret_cast<float*>(W + P.xin);
   const int64_t N = d.N;
+
+  // ---- fp8 linears: amax slots 16 l + {0..5: W q k v o fc mp; 6..9: inputs
+  // xn, attn, xn2, h; 10..15: output gradients of mp, fc, o, q, k, v}
+  uint32_t* amax = d.fp8 ? reinterpret_cast<uint32_t*>(W + P.amax) : nullptr;
+  uint8_t* q8 = d.fp8 ? reinterpret_cast<uint8_t*>(W + P.q8) : nullptr;
+  uint8_t* g8t = d.fp8 ? reinterpret_cast<uint8_t*>(W + P.g8t) : nullptr;
+  const int64_t Np = P.Np, Nk = (N + 15) / 16 * 16;  // code pitch / K of token contractions
+  auto P128 = [](int64_t x) { return (x + 127) / 128 * 128; };
+  auto slot = [](int l, int k) { return 16 * l + k; };
+  // per-layer fp8 weights: row-major for the forward, transposed for dgrad
+  auto w8 = [&](int l, int which) {
+    uint8_t* b = reinterpret_cast<uint8_t*>(W + P.w8 + (size_t)l * P.w8_layer);
+    const int64_t C = d.C, Cq = d.Cq, Fh = d.F, Qkv = d.Qkv;
+    const int64_t off[4] = {0, Qkv * C, Qkv * C + C * Cq, Qkv * C + C * Cq + Fh * C};
+    return b + off[which];
+  };
+  auto w8t = [&](int l, int which) {
+    uint8_t* b = reinterpret_cast<uint8_t*>(W + P.w8t + (size_t)l * P.w8t_layer);
+    const int64_t C = d.C, Cq = d.Cq, Fh = d.F, Qkv = d.Qkv;
+    const int64_t o1 = C * P128(Qkv), o2 = o1 + Cq * P128(C), o3 = o2 + C * P128(Fh);
+    const int64_t off[4] = {0, o1, o2, o3};
+    return b + off[which];
+  };
+  auto segs3 = [&](int64_t e0, int64_t e1, int s0, int s1, int s2) {
+    Segs g{};
+    g.n = 3;
+    g.end[0] = e0;
+    g.end[1] = e1;
+    g.end[2] = INT64_MAX;
+    g.slot[0] = s0;
+    g.slot[1] = s1;
+    g.slot[2] = s2;
+    return g;
+  };
+  // dequantisation of a product: one segment, or three along `axis`
+  auto deq1 = [&](int sa, int sb, int fa) {
+    Fp8Deq q{};
+    q.amax = amax;
+    q.axis = 1;
+    q.nseg = 1;
+    q.sa[0] = sa;
+    q.sb[0] = sb;
+    q.fa = fa;
+    q.fb = FP8_E4M3;
+    return q;
+  };
+  auto deq3 = [&](int axis, int sa0, int sa1, int sa2, int sb0, int sb1, int sb2, int fa) {
+    Fp8Deq q{};
+    q.amax = amax;
+    q.axis = axis;
+    q.nseg = 3;
+    q.end[0] = d.Cq;
+    q.end[1] = d.Cq + d.Ckv;
+    q.end[2] = INT64_MAX;
+    q.sa[0] = sa0; q.sa[1] = sa1; q.sa[2] = sa2;
+    q.sb[0] = sb0; q.sb[1] = sb1; q.sb[2] = sb2;
+    q.fa = fa;
+    q.fb = FP8_E4M3;
+    return q;
+  };
+  // amax, then codes of a token-major tensor [N][cols]: row-major into q8,
+  // transposed into outT (backward calls only)
+  auto quant_tok = [&](const void* src, bool bf, int64_t cols, const Segs& sg, int fmt,
+                       uint8_t* outT) {
+    launch_fp8_amax(src, bf, N * cols, cols, sg, amax, s);
+    launch_fp8_quant(src, bf, N, cols, false, sg, amax, fmt, q8, backward ? outT : nullptr, Np, s);
+  };
+  if (d.fp8) {
+    launch_zero(reinterpret_cast<float*>(amax), 16 * d.L, s);
+    site("fp8.weights", s, [&] {
+      for (int l = 0; l < d.L; ++l) {
+        const int64_t C = d.C, Cq = d.Cq, Ckv = d.Ckv, Fh = d.F;
+        Segs g{};
+        g.n = 6;
+        const int64_t ends[6] = {Cq * C, (Cq + Ckv) * C, (Cq + 2 * Ckv) * C,
+                                 (Cq + 2 * Ckv) * C + C * Cq, (Cq + 2 * Ckv) * C + C * Cq + Fh * C,
+                                 INT64_MAX};
+        for (int k = 0; k < 6; ++k) {
+          g.end[k] = ends[k];
+          g.slot[k] = slot(l, k);
+        }
+        const int64_t n = F.mp[l] + C * Fh - F.q[l];
+        launch_fp8_amax(params + F.q[l], false, n, n, g, amax, s);
+        const Segs gq = segs3(Cq, Cq + Ckv, slot(l, 0), slot(l, 1), slot(l, 2));
+        launch_fp8_quant(params + F.q[l], false, d.Qkv, C, true, gq, amax, FP8_E4M3, w8(l, 0),
+                         backward ? w8t(l, 0) : nullptr, P128(d.Qkv), s);
+        launch_fp8_quant(params + F.o[l], false, C, Cq, true, one_seg(slot(l, 3)), amax, FP8_E4M3,
+                         w8(l, 1), backward ? w8t(l, 1) : nullptr, P128(C), s);
+        launch_fp8_quant(params + F.fc[l], false, Fh, C, true, one_seg(slot(l, 4)), amax,
+                         FP8_E4M3, w8(l, 2), backward ? w8t(l, 2) : nullptr, P128(Fh), s);
+        launch_fp8_quant(params + F.mp[l], false, C, Fh, true, one_seg(slot(l, 5)), amax,
+                         FP8_E4M3, w8(l, 3), backward ? w8t(l, 3) : nullptr, P128(C), s);
+      }
+    });
+  }
 
   site("embed.fwd", s, [&] { launch_embed(params + F.wte, tokens, X(0), N, d.C, s); });
   for (int l = 0; l < d.L; ++l) {
@@ -327,13 +447,42 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     void* u = LY(l, P.l_u);
     launch_mix_norm(d, X(l), X(0), params + F.lr + l, params + F.l0 + l, xin, xn, r1,
                     ve ? params + F.veg[l] : nullptr, ve ? a : nullptr, s);
-    site("gemm.qkv.fwd", s, [&] { gemm_nt_store(d, N, d.Qkv, d.C, xn, wmat(F.q[l]), qkv, s); });
+    if (d.fp8) {
+      site("fp8.quant", s, [&] { quant_tok(xn, true, d.C, one_seg(slot(l, 6)), FP8_E4M3, LY8(l, P.l_x8t)); });
+      site("gemm.qkv.fwd", s, [&] {
+        gemm8_store(N, d.Qkv, d.C, q8, d.C, w8(l, 0), d.C,
+                    deq3(1, slot(l, 6), slot(l, 6), slot(l, 6), slot(l, 0), slot(l, 1), slot(l, 2),
+                         FP8_E4M3), qkv, s);
+      });
+    } else {
+      site("gemm.qkv.fwd", s, [&] { gemm_nt_store(d, N, d.Qkv, d.C, xn, wmat(F.q[l]), qkv, s); });
+    }
     site("rope.fwd", s, [&] { launch_rope_qk_ve_fwd(d, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr, tokens, s); });
     site("attn.fwd", s, [&] { launch_attn_fwd(d, full, qkv, att, lse, s); });
-    site("gemm.o.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.Cq, att, wmat(F.o[l]), xin, xmid, s); });
+    if (d.fp8) {
+      site("fp8.quant", s, [&] { quant_tok(att, true, d.Cq, one_seg(slot(l, 7)), FP8_E4M3, LY8(l, P.l_a8t)); });
+      site("gemm.o.fwd", s, [&] {
+        gemm8_resid(N, d.C, d.Cq, q8, d.Cq, w8(l, 1), d.Cq, deq1(slot(l, 7), slot(l, 3), FP8_E4M3),
+                    xin, xmid, s);
+      });
+    } else {
+      site("gemm.o.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.Cq, att, wmat(F.o[l]), xin, xmid, s); });
+    }
     launch_mix_norm(d, xmid, nullptr, nullptr, nullptr, nullptr, xn2, r2, nullptr, nullptr, s);
-    site("gemm.fc.fwd", s, [&] { gemm_nt_relu2(d, N, d.F, d.C, xn2, wmat(F.fc[l]), u, s); });
-    site("gemm.mp.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.F, u, wmat(F.mp[l]), xmid, X(l + 1), s); });
+    if (d.fp8) {
+      site("fp8.quant", s, [&] { quant_tok(xn2, true, d.C, one_seg(slot(l, 8)), FP8_E4M3, LY8(l, P.l_x28t)); });
+      site("gemm.fc.fwd", s, [&] {
+        gemm8_relu2(N, d.F, d.C, q8, d.C, w8(l, 2), d.C, deq1(slot(l, 8), slot(l, 4), FP8_E4M3), u, s);
+      });
+      site("fp8.quant", s, [&] { quant_tok(u, true, d.F, one_seg(slot(l, 9)), FP8_E4M3, LY8(l, P.l_h8t)); });
+      site("gemm.mp.fwd", s, [&] {
+        gemm8_resid(N, d.C, d.F, q8, d.F, w8(l, 3), d.F, deq1(slot(l, 9), slot(l, 5), FP8_E4M3),
+                    xmid, X(l + 1), s);
+      });
+    } else {
+      site("gemm.fc.fwd", s, [&] { gemm_nt_relu2(d, N, d.F, d.C, xn2, wmat(F.fc[l]), u, s); });
+      site("gemm.mp.fwd", s, [&] { gemm_nt_resid(d, N, d.C, d.F, u, wmat(F.mp[l]), xmid, X(l + 1), s); });
+    }
   }
   void* xf = W + P.xf;
   float* rf = reinterpret_cast<float*>(W + P.rf);
@@ -391,10 +540,32 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       const float* r2 = reinterpret_cast<const float*>(LY(l, P.l_r2));
       const void* u = LY(l, P.l_u);
       // MLP
-      site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s); });
-      site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, s); });
-      site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s); });
-      site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, s); });
+      if (d.fp8) {
+        const int64_t C = d.C, Fh = d.F;
+        site("fp8.quant", s, [&] { quant_tok(gxc, true, C, one_seg(slot(l, 10)), FP8_E5M2, g8t); });
+        site("gemm.mp.dgrad", s, [&] {
+          gemm8_relu2bwd(N, Fh, C, q8, C, w8t(l, 3), P128(C),
+                         deq1(slot(l, 10), slot(l, 5), FP8_E5M2), u, gu, s);
+        });
+        site("gemm.mp.wgrad", s, [&] {
+          gemm8_wgrad(C, Fh, Nk, g8t, Np, LY8(l, P.l_h8t), Np,
+                      deq1(slot(l, 10), slot(l, 9), FP8_E5M2), grads + F.mp[l], acc, s);
+        });
+        site("fp8.quant", s, [&] { quant_tok(gu, true, Fh, one_seg(slot(l, 11)), FP8_E5M2, g8t); });
+        site("gemm.fc.dgrad", s, [&] {
+          gemm8_f32(N, C, Fh, q8, Fh, w8t(l, 2), P128(Fh), deq1(slot(l, 11), slot(l, 4), FP8_E5M2),
+                    gtmp, s);
+        });
+        site("gemm.fc.wgrad", s, [&] {
+          gemm8_wgrad(Fh, C, Nk, g8t, Np, LY8(l, P.l_x28t), Np,
+                      deq1(slot(l, 11), slot(l, 8), FP8_E5M2), grads + F.fc[l], acc, s);
+        });
+      } else {
+        site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s); });
+        site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, s); });
+        site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s); });
+        site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, s); });
+      }
       nb = NormBwdArgs{};
       nb.mode = NB_NORM2;
       nb.gin = gtmp;
@@ -404,14 +575,43 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       nb.gxc = d.bf16 ? gxc : nullptr;
       launch_norm_bwd(d, nb, s);
       // attention
-      site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s); });
-      site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, s); });
+      if (d.fp8) {
+        site("fp8.quant", s, [&] { quant_tok(gxc, true, d.C, one_seg(slot(l, 12)), FP8_E5M2, g8t); });
+        site("gemm.o.dgrad", s, [&] {
+          gemm8_store(N, d.Cq, d.C, q8, d.C, w8t(l, 1), P128(d.C),
+                      deq1(slot(l, 12), slot(l, 3), FP8_E5M2), gO, s);
+        });
+        site("gemm.o.wgrad", s, [&] {
+          gemm8_wgrad(d.C, d.Cq, Nk, g8t, Np, LY8(l, P.l_a8t), Np,
+                      deq1(slot(l, 12), slot(l, 7), FP8_E5M2), grads + F.o[l], acc, s);
+        });
+      } else {
+        site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s); });
+        site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, s); });
+      }
       site("attn.delta", s, [&] { launch_attn_delta(d, gO, att, delta, s); });
       site("attn.bwd", s, [&] { launch_attn_bwd(d, full, qkv, gO, lse, delta, gqkv, s); });
       launch_rope_qk_ve_bwd(d, gqkv, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr,
                             ve ? grads + F.ve[l] : nullptr, ga, tokens, s);
-      site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s); });
-      site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, s); });
+      if (d.fp8) {
+        const int g0 = slot(l, 13), g1 = slot(l, 14), g2 = slot(l, 15);
+        site("fp8.quant", s, [&] {
+          quant_tok(gqkv, true, d.Qkv, segs3(d.Cq, d.Cq + d.Ckv, g0, g1, g2), FP8_E5M2, g8t);
+        });
+        // the q, k and v gradients carry their own scales along the contraction
+        site("gemm.qkv.dgrad", s, [&] {
+          gemm8_f32(N, d.C, d.Qkv, q8, d.Qkv, w8t(l, 0), P128(d.Qkv),
+                    deq3(2, g0, g1, g2, slot(l, 0), slot(l, 1), slot(l, 2), FP8_E5M2), gtmp, s);
+        });
+        site("gemm.qkv.wgrad", s, [&] {
+          const int x = slot(l, 6);
+          gemm8_wgrad(d.Qkv, d.C, Nk, g8t, Np, LY8(l, P.l_x8t), Np,
+                      deq3(0, g0, g1, g2, x, x, x, FP8_E5M2), grads + F.q[l], acc, s);
+        });
+      } else {
+        site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s); });
+        site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, s); });
+      }
       if (ve) launch_veg_wgrad(d, ga, xn, veg_part, P.veg_splits, grads + F.veg[l], s);
       nb = NormBwdArgs{};
       nb.mode = NB_NORM1;
@@ -529,7 +729,12 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
       {"gu", P.gu, N * d.F * A}, {"gtmp", P.gtmp, N * C * 4}, {"gO", P.gO, N * d.Cq * A},
       {"gqkv", P.gqkv, N * d.Qkv * A}, {"delta", P.delta, N * d.H * 4},
       {"ga", P.ga, N * d.Hk * 4}, {"lam_part", P.lam_part, (size_t)d.L * P.lam_blocks * 8},
-      {"veg_part", P.veg_part, (size_t)P.veg_splits * d.Hk * C * 4}};
+      {"veg_part", P.veg_part, (size_t)P.veg_splits * d.Hk * C * 4},
+      {"amax", P.amax, d.fp8 ? (size_t)16 * d.L * 4 : 0},
+      {"w8", P.w8, d.fp8 ? P.w8_layer * d.L : 0},
+      {"w8t", P.w8t, d.fp8 ? P.w8t_layer * d.L : 0},
+      {"q8", P.q8, d.fp8 ? N * std::max(std::max(C, (size_t)d.Cq), std::max((size_t)d.F, (size_t)d.Qkv)) : 0},
+      {"g8t", P.g8t, d.fp8 ? std::max(std::max(C, (size_t)d.F), (size_t)d.Qkv) * (size_t)P.Np : 0}};
   for (const R& r : global)
     if (n == r.name) {
       *offset = r.off;
@@ -546,7 +751,11 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
                          {"xmid", P.l_xmid, N * C * 4},
                          {"xn2", P.l_xn2, N * C * A},
                          {"r2", P.l_r2, N * 4},
-                         {"h", P.l_u, N * d.F * A}};
+                         {"h", P.l_u, N * d.F * A},
+                         {"x8t", P.l_x8t, d.fp8 ? C * (size_t)P.Np : 0},
+                         {"a8t", P.l_a8t, d.fp8 ? (size_t)d.Cq * P.Np : 0},
+                         {"x28t", P.l_x28t, d.fp8 ? C * (size_t)P.Np : 0},
+                         {"h8t", P.l_h8t, d.fp8 ? (size_t)d.F * P.Np : 0}};
   for (const R& r : per_layer)
     if (n == r.name) {
       if (layer < 0 || layer >= d.L) return fail(GPT_E_INVAL, "layer out of range");
@@ -567,6 +776,34 @@ int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
             const int32_t* targets, float* loss, void* workspace, size_t workspace_bytes,
             void* stream) {
   return run(cfg, params, tokens, targets, loss, nullptr, workspace, workspace_bytes, stream, false);
+}
+
+int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                     int32_t fmt, uint8_t* codes, uint8_t* codes_t, int64_t pitch_t,
+                     uint32_t* amax, void* stream) {
+  g_err[0] = 0;
+  if (!src || !amax) return fail(GPT_E_NULLPTR, "src and amax are required");
+  if (src_dtype != GPT_DT_F32 && src_dtype != GPT_DT_BF16)
+    return fail(GPT_E_INVAL, "src_dtype %d unknown", src_dtype);
+  if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(GPT_E_INVAL, "fmt %d unknown", fmt);
+  if (rows < 1 || cols < 64 || cols % 64 || rows > ((int64_t)1 << 31) || cols > (1 << 20))
+    return fail(GPT_E_INVAL, "rows %lld / cols %lld: need rows >= 1, cols a multiple of 64",
+                (long long)rows, (long long)cols);
+  if (codes_t && (pitch_t < rows || pitch_t % 128))
+    return fail(GPT_E_INVAL, "pitch_t %lld: need a multiple of 128 >= rows", (long long)pitch_t);
+  if (!aligned(src, 16) || (codes && !aligned(codes, 16)) || (codes_t && !aligned(codes_t, 16)) ||
+      !aligned(amax, 4))
+    return fail(GPT_E_ALIGN, "src, codes, codes_t need 16-byte alignment, amax 4");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const bool bf = src_dtype == GPT_DT_BF16;
+  const Segs sg = one_seg(0);
+  launch_zero(reinterpret_cast<float*>(amax), 1, s);
+  launch_fp8_amax(src, bf, rows * cols, rows * cols, sg, amax, s);
+  launch_fp8_quant(src, bf, rows, cols, false, sg, amax, fmt, codes, codes_t, pitch_t, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
+  return GPT_OK;
 }
 
 const char* gpt_status_string(int status) {

@@ -18,6 +18,7 @@ struct Dims {
   int Cq, Ckv, Qkv; // H*D, Hk*D, Cq + 2*Ckv
   int G;            // H / Hk
   bool bf16;        // compute dtype
+  bool fp8;         // block linears in dynamic per-tensor fp8
   int act_bytes;    // 2 (bf16) or 4 (fp32)
   float theta, eps, cap;
   bool accumulate;
@@ -46,6 +47,16 @@ struct Plan {
   int rowparts;         // max row-sum partials per token
   size_t gx, gxc, gx0, gu, gtmp, gO, gqkv, delta, ga, lam_part, veg_part;
   int lam_blocks, veg_splits;
+  // fp8 linears only (0 bytes otherwise). Token-major code tensors that the
+  // weight gradients contract over are stored transposed, [features][Np],
+  // Np = N rounded up to 128, zero beyond N.
+  int64_t Np;
+  size_t amax;                // uint32 [16 L] amax slots
+  size_t w8, w8_layer;        // per layer: qkv [Qkv][C], o [C][Cq], fc [F][C], mp [C][F]
+  size_t w8t, w8t_layer;      // per layer: qkv^T [C][P(Qkv)], o^T [Cq][P(C)], fc^T [C][P(F)], mp^T [F][P(C)]
+  size_t l_x8t, l_a8t, l_x28t, l_h8t;  // per layer: xn, attn, xn2, h codes, transposed
+  size_t q8;                  // [N][max(C, Cq, F, Qkv)] row-major codes (scratch)
+  size_t g8t;                 // [max(C, F, Qkv)][Np] transposed gradient codes (scratch)
   size_t total;
 };
 Plan make_plan(const Dims& d);
@@ -151,5 +162,70 @@ void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, c
 // Weight gradients C[M][N] (+)= sum_k A[k][m] B[k][n].
 void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
                    float* C, bool accumulate, hipStream_t s);
+
+// ------------------------------------------------------------ fp8 linears
+// Per-tensor dynamic scaling: s = fmax / amax in fp32; codes are
+// RNE(clamp(x * s)) in OCP e4m3 (forward operands) or e5m2 (output
+// gradients). amax slots are uint32 bit patterns of max |x|.
+enum Fp8Fmt { FP8_E4M3 = 0, FP8_E5M2 = 1 };
+
+// Up to 6 consecutive segments of an index range, each with its own amax
+// slot: segment i ends (exclusive) at end[i]; the last one is open-ended.
+struct Segs {
+  int n;
+  int64_t end[6];
+  int slot[6];
+};
+inline Segs one_seg(int slot) {
+  Segs s{};
+  s.n = 1;
+  s.end[0] = INT64_MAX;
+  s.slot[0] = slot;
+  return s;
+}
+
+// amax of x (n elements, a multiple of 8; bf16 or fp32): the segment of an
+// element is looked up from (index mod period) and every boundary is a
+// multiple of 8.
+void launch_fp8_amax(const void* x, bool bf16_src, int64_t n, int64_t period, const Segs& sg,
+                     uint32_t* amax, hipStream_t s);
+// Codes of src [R][C] (C a multiple of 64) row-major into out [R][C] and/or
+// transposed into outT [C][pitchT] (pitchT a multiple of 128 and >= R; rows
+// R .. pitchT-1 written as 0). Segments along rows (seg_rows) or columns.
+void launch_fp8_quant(const void* src, bool bf16_src, int64_t R, int64_t C, bool seg_rows,
+                      const Segs& sg, const uint32_t* amax, int fmt, uint8_t* out, uint8_t* outT,
+                      int64_t pitchT, hipStream_t s);
+
+// Dequantisation of an fp8 product: in segment i of the M, N or K index
+// (axis 0, 1, 2) the sum of code products is multiplied by
+// 1 / (s(amax[sa[i]], fa) * s(amax[sb[i]], fb)).
+struct Fp8Deq {
+  const uint32_t* amax;
+  int axis;
+  int nseg;
+  int64_t end[3];
+  int sa[3], sb[3];
+  int fa, fb;
+};
+
+// fp8 products, both operands K-major: C[M][N] = sum_k A[m][k] B[n][k] with
+// A [M][lda] and B [N][ldb] byte codes (K, lda, ldb multiples of 16).
+void gemm8_store(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s);
+void gemm8_resid(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const float* R, float* C,
+                 hipStream_t s);
+void gemm8_relu2(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s);
+void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                    const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const void* H, void* C,
+                    hipStream_t s);
+void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+               const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, hipStream_t s);
+// Weight gradient (K = tokens, split over workgroups with fp32 atomics when
+// that fills the machine); C (+)= the product.
+void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                 hipStream_t s);
 
 }  // namespace gpt

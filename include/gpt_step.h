@@ -77,7 +77,7 @@ typedef struct gpt_config {
   int32_t batch;           /* B                                              */
   int32_t short_window;    /* W                                              */
   int32_t compute_dtype;   /* GPT_DT_F32 | GPT_DT_BF16                       */
-  int32_t fp8_linears;     /* 0 | 1 (1: not built yet -> GPT_E_UNSUPPORTED)  */
+  int32_t fp8_linears;     /* 0 | 1: block linears in per-tensor fp8 (bf16 only) */
   int32_t flags;           /* GPT_F_*                                        */
   float rope_theta;        /* RoPE base, > 1                                 */
   float norm_eps;          /* RMSNorm epsilon (all norms), > 0               */
@@ -132,7 +132,9 @@ int gpt_workspace_size(const gpt_config* cfg, size_t* bytes);
  * Scratch (layout only): "wc", "rope", "xin", "rf", "rowpart",
  * "lossrow", "scalars", "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv",
  * "delta", "ga", "lam_part", "veg_part"; per layer "r1", "rqk", "a", "lse",
- * "r2". All regions are disjoint. `layer` is ignored for global regions.
+ * "r2". With fp8_linears = 1 also "amax", "w8", "w8t", "q8", "g8t" and per
+ * layer "x8t", "a8t", "x28t", "h8t" (fp8 codes; 0 bytes otherwise).
+ * All regions are disjoint. `layer` is ignored for global regions.
  * N = batch * seq_len, row n = b * seq_len + t; act = compute_dtype.
  * Returns the byte offset and size. GPT_E_INVAL for an unknown name/layer.
  */
@@ -166,6 +168,29 @@ int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dynamic per-tensor fp8 quantisation of a row-major matrix: the operation
+ * applied to every operand of the six block linears when fp8_linears = 1
+ * (additions page, feature table: dynamic per-tensor fp8, e4m3 / e5m2;
+ * overview page, section 4: quantise / dequantise around each scaled
+ * matmul). amax = max |x| over the matrix; s = fmax / amax in fp32 (s = 1
+ * if amax is 0 or not finite), fmax = 448 (e4m3) or 57344 (e5m2);
+ * code = round-to-nearest-even of clamp(fp32(x * s), -fmax, fmax) in the
+ * OCP encoding (sign, biased exponent, mantissa; e4m3 bias 7, e5m2 bias 15).
+ *   src      (device) [rows, cols], fp32 (GPT_DT_F32) or bf16 (GPT_DT_BF16),
+ *            16-byte aligned; cols a multiple of 64.
+ *   fmt      0: e4m3, 1: e5m2.
+ *   codes    (device) uint8 [rows, cols], written; may be NULL.
+ *   codes_t  (device) uint8 [cols, pitch_t]: the transposed codes, written
+ *            with zeros in columns rows .. pitch_t-1; may be NULL.
+ *            pitch_t is a multiple of 128 and >= rows (ignored if NULL).
+ *   amax     (device) uint32 [1]: the bit pattern of amax as fp32, written.
+ * codes and codes_t 16-byte aligned. Enqueued on `stream`.
+ */
+int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                     int32_t fmt, uint8_t* codes, uint8_t* codes_t, int64_t pitch_t,
+                     uint32_t* amax, void* stream);
+
+/*
  * Host only; measurement support. After gpt_profile_begin(prefixes), every
  * kernel launch of gpt_fwd_bwd / gpt_fwd whose launch-site name starts with
  * one of the comma-separated `prefixes` is bracketed by two HIP events
@@ -174,7 +199,9 @@ int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
  * "gemm.o.fwd", "gemm.fc.fwd", "gemm.mp.fwd", "gemm.lm.fwd", "loss",
  * "gemm.lm.dgrad", "gemm.lm.wgrad", "gemm.mp.dgrad", "gemm.mp.wgrad",
  * "gemm.fc.dgrad", "gemm.fc.wgrad", "gemm.o.dgrad", "gemm.o.wgrad",
- * "attn.delta", "attn.bwd", "gemm.qkv.dgrad", "gemm.qkv.wgrad", "embed.bwd".
+ * "attn.delta", "attn.bwd", "gemm.qkv.dgrad", "gemm.qkv.wgrad", "embed.bwd",
+ * and with fp8 linears "fp8.weights" (weight amax + codes) and "fp8.quant"
+ * (amax + codes of an activation or gradient).
  * gpt_profile_end waits for the recorded events, returns the summed
  * kernel time in milliseconds and the number of bracketed launches, and
  * stops recording. Process-wide state: not for concurrent callers.

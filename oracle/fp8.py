@@ -72,6 +72,15 @@ def decode(codes, fmt):
     return np.where(c & 0x80, -mag, mag)
 
 
+def round_bf16(x):
+    """Nearest bfloat16 value (8 significant bits, ties to even) of float32
+    values, returned as float32: add half of the dropped 16 bits (plus the
+    kept bit for ties) and truncate. Finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
 def scale_for(x, fmt):
     """Per-tensor scale fmax / amax, in float32 as a device would hold it."""
     fmax = FORMATS[fmt][2]

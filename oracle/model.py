@@ -246,22 +246,30 @@ class _Lin:
     ("additions" table: dynamic per-tensor fp8, e4m3 / e5m2; "overview"
     section 4: quantise and dequantise around each matmul). In fp8 mode the
     forward operands are quantised to e4m3 and the output gradient to e5m2,
-    each with its own scale fmax / amax."""
+    each with its own scale fmax / amax.
 
-    def __init__(self, fp8: bool):
+    fp8_round="bf16" rounds the activation and output-gradient operands to
+    bfloat16 before they are quantised (weights are quantised from their
+    fp32 values either way): the operands as a bf16-activation
+    implementation holds them. Both variants are valid readings; the tests
+    use the distance between them as the scale of fp8's own sensitivity."""
+
+    def __init__(self, fp8: bool, fp8_round=None):
         self.fp8 = fp8
+        assert fp8_round in (None, "bf16")
+        self.rnd = (lambda a: _fp8.round_bf16(a).astype(a.dtype)) if fp8_round else (lambda a: a)
 
     def fwd(self, x, W):
         if self.fp8:
-            x = _fp8.qdq(x, "e4m3")
+            x = _fp8.qdq(self.rnd(x), "e4m3")
             W = _fp8.qdq(W, "e4m3")
         return x @ W.T
 
     def bwd(self, gy, x, W):
         """(g_x, g_W)."""
         if self.fp8:
-            gy = _fp8.qdq(gy, "e5m2")
-            x = _fp8.qdq(x, "e4m3")
+            gy = _fp8.qdq(self.rnd(gy), "e5m2")
+            x = _fp8.qdq(self.rnd(x), "e4m3")
             W = _fp8.qdq(W, "e4m3")
         return gy @ W, gy.T @ x
 
@@ -358,7 +366,7 @@ def _layer_bwd(l, cfg, P, c, gx, tok, cos, sin, lin, dt, G):
 
 
 def forward_backward(cfg, params, tokens, targets, dtype=np.float64,
-                     fp8=None, return_acts=False):
+                     fp8=None, return_acts=False, fp8_round=None):
     """Loss and the flat gradient of every parameter, in canonical order.
 
     cfg: a workload description with the fields n_layer, n_embd, n_head,
@@ -369,7 +377,7 @@ def forward_backward(cfg, params, tokens, targets, dtype=np.float64,
     """
     dt = np.dtype(dtype)
     fp8 = cfg.fp8_linears if fp8 is None else fp8
-    lin = _Lin(fp8)
+    lin = _Lin(fp8, fp8_round)
     P = unpack(cfg, params)
     offs, total = param_offsets(cfg)
     grads = np.zeros(total, dtype=dt)
@@ -414,11 +422,11 @@ def forward_backward(cfg, params, tokens, targets, dtype=np.float64,
     return loss, grads
 
 
-def forward_loss(cfg, params, tokens, targets, dtype=np.float64, fp8=None):
+def forward_loss(cfg, params, tokens, targets, dtype=np.float64, fp8=None, fp8_round=None):
     """Loss only (the forward half of ``forward_backward``)."""
     dt = np.dtype(dtype)
     fp8 = cfg.fp8_linears if fp8 is None else fp8
-    lin = _Lin(fp8)
+    lin = _Lin(fp8, fp8_round)
     P = unpack(cfg, params)
     tok = np.asarray(tokens)
     B, T = tok.shape

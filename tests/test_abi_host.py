@@ -69,8 +69,10 @@ def test_validation_errors():
     for kw in bad:
         assert B.validate(B.make_config(w, **kw)) == -1, kw
         assert B.lib().gpt_last_error().decode() != ""
-    # fp8 linears are a valid model this library does not run yet
-    assert B.validate(B.make_config(w, fp8_linears=1)) == -5
+    # fp8 linears run with bf16 compute only
+    assert B.validate(B.make_config(w, fp8_linears=1)) == -1
+    assert "bf16" in B.lib().gpt_last_error().decode()
+    assert B.validate(B.make_config(w, fp8_linears=1, compute_dtype=B.GPT_DT_BF16)) == 0
     assert B.lib().gpt_config_validate(None) == -2
 
 
@@ -106,22 +108,30 @@ def test_entry_points_reject_bad_pointers_before_any_launch():
     assert st == -4
     st = L.gpt_fwd(ctypes.byref(cfg), p, p, p, p, p, ws - 1, None)
     assert st == -4
-    cfg8 = B.make_config(w, fp8_linears=1)
-    assert L.gpt_fwd_bwd(ctypes.byref(cfg8), p, p, p, p, p, p, ws, None) == -5
+    cfg8 = B.make_config(w, fp8_linears=1)   # fp8 with fp32 compute
+    assert L.gpt_fwd_bwd(ctypes.byref(cfg8), p, p, p, p, p, p, ws, None) == -1
     assert L.gpt_status_string(-4).decode() == "workspace too small"
 
 
 GLOBAL_REGIONS = ["wc", "rope", "xin", "xf", "rf", "logits", "rowpart", "lossrow",
                   "scalars", "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga",
-                  "lam_part", "veg_part"]
-LAYER_REGIONS = ["xn", "r1", "qkv", "rqk", "a", "attn", "lse", "xmid", "xn2", "r2", "h"]
+                  "lam_part", "veg_part", "amax", "w8", "w8t", "q8", "g8t"]
+LAYER_REGIONS = ["xn", "r1", "qkv", "rqk", "a", "attn", "lse", "xmid", "xn2", "r2", "h",
+                 "x8t", "a8t", "x28t", "h8t"]
 
 
-@pytest.mark.parametrize("name", ["tiny", "d12", "d12_gqa", "d26"])
-def test_workspace_regions_disjoint(name):
-    w = W.get(name)
-    cfg = B.make_config(w, fp8_linears=0)
+@pytest.mark.parametrize("name,fp8", [("tiny", 0), ("d12", 0), ("d12_gqa", 0), ("d26", 0),
+                                      ("d26", 1), ("small_fp8", 1)])
+def test_workspace_regions_disjoint(name, fp8):
+    w = W.get(name) if name != "small_fp8" else W.get("d12").with_(
+        n_layer=3, seq_len=200, batch=1, vocab=1024, fp8_linears=True)
+    cfg = B.make_config(w, fp8_linears=fp8)
     ws = B.workspace_size(cfg)
+    N, Np = w.batch * w.seq_len, (w.batch * w.seq_len + 127) // 128 * 128
+    fp8_sizes = {"x8t": w.n_embd * Np, "a8t": w.n_head * w.head_dim * Np,
+                 "x28t": w.n_embd * Np, "h8t": w.mlp_hidden * Np, "amax": 16 * w.n_layer * 4}
+    for r, nb in fp8_sizes.items():
+        assert B.workspace_region(cfg, r, 0)[1] == (nb if fp8 else 0), r
     spans = []
     for r in GLOBAL_REGIONS:
         spans.append((r, *B.workspace_region(cfg, r, 0)))
@@ -136,3 +146,19 @@ def test_workspace_regions_disjoint(name):
         assert o1 + b1 <= o2, (n1, n2)
     assert all(o % 256 == 0 for _, o, _ in spans)
     assert spans[-1][1] + spans[-1][2] <= ws
+
+
+def test_fp8_quantize_rejects_bad_arguments_before_any_launch():
+    L = B.lib()
+    p = ctypes.c_void_p(4096)
+    q = lambda *a: L.gpt_fp8_quantize(*a)
+    assert q(None, 0, 4, 64, 0, p, p, 128, p, None) == -2            # src
+    assert q(p, 0, 4, 64, 0, p, p, 128, None, None) == -2            # amax
+    assert q(p, 7, 4, 64, 0, p, p, 128, p, None) == -1               # dtype
+    assert q(p, 0, 4, 64, 3, p, p, 128, p, None) == -1               # format
+    assert q(p, 0, 4, 96, 0, p, p, 128, p, None) == -1               # cols % 64
+    assert q(p, 0, 0, 64, 0, p, p, 128, p, None) == -1               # rows
+    assert q(p, 0, 200, 64, 0, p, p, 128, p, None) == -1             # pitch < rows
+    assert q(p, 0, 4, 64, 0, p, p, 100, p, None) == -1               # pitch % 128
+    assert q(ctypes.c_void_p(4100), 0, 4, 64, 0, p, p, 128, p, None) == -3
+    assert q(p, 0, 4, 64, 0, ctypes.c_void_p(4104), None, 0, p, None) == -3

@@ -565,3 +565,28 @@ def test_fp8_model_matches_torch_fake_quant(variant):
     # fp8 really changes the result relative to the unquantised model
     l0, _ = oracle.forward_backward(cfg, p, tok, tgt, fp8=False)
     assert abs(l0 - loss) > 1e-6
+
+
+def test_round_bf16_matches_torch():
+    """Ties to even on exact halfway cases and on random values (library)."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    ties = x.view(np.uint32).copy()
+    ties[:5000] = (ties[:5000] & 0xFFFF0000) | 0x8000    # exactly halfway
+    x = ties.view(np.float32)
+    ref = torch.from_numpy(x.copy()).bfloat16().float().numpy()
+    np.testing.assert_array_equal(oracle.fp8.round_bf16(x), ref)
+
+
+def test_fp8_round_variant_only_touches_quantiser_inputs():
+    """fp8_round="bf16" changes an fp8 run but not an unquantised one."""
+    cfg = W.get("tiny").with_(fp8_linears=True)
+    _, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 3)
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    l0, g0 = oracle.forward_backward(cfg, p, tok, tgt, dtype=np.float32, fp8=False)
+    l1, g1 = oracle.forward_backward(cfg, p, tok, tgt, dtype=np.float32, fp8=False, fp8_round="bf16")
+    assert l0 == l1 and np.array_equal(g0, g1)
+    l2, _ = oracle.forward_backward(cfg, p, tok, tgt, dtype=np.float32)
+    l3, _ = oracle.forward_backward(cfg, p, tok, tgt, dtype=np.float32, fp8_round="bf16")
+    assert l2 != l3 and abs(l2 - l3) < 1e-2 * abs(l2)
