@@ -1,7 +1,7 @@
 """Throughput of the nanochat GPT forward+backward step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
-                    [--no-cpu-baseline] [--profile-site PREFIX]
+                    [--fp8 auto|on|off] [--no-cpu-baseline] [--roofline-kernel K]
 
 One step = one gpt_fwd_bwd call (loss + every parameter gradient) over one
 batch of seeded synthetic tokens, inputs already resident in HBM. Prints one
@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="d12")
+    ap.add_argument("--fp8", default="auto", choices=["auto", "on", "off"],
+                    help="block linears in fp8 (auto: as the workload defines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3)
     ap.add_argument("--roofline-kernel", default="wgrad", choices=sorted(ROOF_KERNELS),
@@ -144,6 +146,8 @@ def main():
     from decoder_only_pretraining_amd import binding as B
 
     w = W.get(args.config)
+    if args.fp8 != "auto":
+        w = w.with_(fp8_linears=args.fp8 == "on")
     total = param_total(w)
     params = W.gen_params(total, w.n_layer, W.weight_seed(w))
     tokens, targets = W.split_tokens(W.gen_tokens(w))
@@ -191,15 +195,18 @@ def main():
                 "avg_launch_ms": round(kern_ms / kern_n, 4),
                 "algorithmic_flop_per_launch": round(flops / kern_n)}
 
+    metric = METRIC if w.name == "d12" else METRIC.replace("d12", w.name)
     out = {
-        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 linears (e4m3/e5m2), bf16 elsewhere" if w.fp8_linears else "bf16",
         "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) weights)",
         "config": {"workload": f"{w.name}: {w.n_layer} layers, n_embd {w.n_embd}, heads "
                                f"{w.n_head}/{w.n_kv_head}, head_dim {w.head_dim}, MLP "
                                f"{w.mlp_hidden}, vocab {w.vocab}, seq {w.seq_len}, batch "
-                               f"{w.batch}, window {w.short_window}",
+                               f"{w.batch}, window {w.short_window}"
+                               + (", fp8 block linears" if w.fp8_linears else ""),
                    "seq_len": w.seq_len, "batch": w.batch, "tokens_per_step": ntok,
                    "parallelism": "none (1 GPU)"},
         "mfma_util_vs_bf16_peak": round(frac, 4),

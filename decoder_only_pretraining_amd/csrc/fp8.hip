@@ -63,10 +63,13 @@ __device__ __forceinline__ uint32_t cvt4(const float* v, float s, float fmax) {
 
 // max |x| per segment of (index mod period), atomically merged into the
 // segments' amax slots. n is a multiple of 8 and every segment boundary too.
+// Each block reduces through LDS and issues one atomic per segment: atomics
+// on one address serialise, so their number is kept to the block count.
 template <typename T>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const T* __restrict__ x, int64_t nv,
                                                        int64_t period, gpt::Segs sg,
                                                        uint32_t* __restrict__ amax) {
+  __shared__ float red[6][4];
   float m[6] = {0, 0, 0, 0, 0, 0};
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += stride) {
@@ -80,11 +83,18 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const T* __restrict__ x, 
     for (int j = 0; j < 6; ++j)
       if (j == k) m[j] = fmaxf(m[j], a);
   }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
     if (j >= sg.n) break;
     const float w = wave_max(m[j]);
-    if ((threadIdx.x & 63) == 0 && w > 0.0f) atomicMax(amax + sg.slot[j], __float_as_uint(w));
+    if (lane == 0) red[j][wave] = w;
+  }
+  __syncthreads();
+  if (threadIdx.x < sg.n) {
+    const int j = threadIdx.x;
+    const float w = fmaxf(fmaxf(red[j][0], red[j][1]), fmaxf(red[j][2], red[j][3]));
+    if (w > 0.0f) atomicMax(amax + sg.slot[j], __float_as_uint(w));
   }
 }
 
@@ -152,7 +162,7 @@ void launch_fp8_amax(const void* x, bool bf16_src, int64_t n, int64_t period, co
                      uint32_t* amax, hipStream_t s) {
   if (n <= 0) return;
   const int64_t nv = n / 8;
-  const unsigned blocks = (unsigned)std::min<int64_t>((nv + 255) / 256, 2048);
+  const unsigned blocks = (unsigned)std::min<int64_t>((nv + 255) / 256, 1024);
   if (bf16_src)
     hipLaunchKernelGGL(fp8_amax_kernel<bf16>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const bf16*>(x), nv, period, sg, amax);

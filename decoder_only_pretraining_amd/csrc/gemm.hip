@@ -43,6 +43,9 @@ struct PreRelu2 {  // ReLU^2 of the MLP hidden pre-activation
 // value(m, n, acc): per-element transform in the accumulator layout;
 // rowterm(value): the row-sum contribution (kRowSum epilogues only);
 // store4(m, n, v, cnt): write columns n .. n+cnt-1 of row m (cnt <= 4).
+// Epilogues that read another operand split the write into aux(m, n, cnt),
+// the load, and store4a(m, n, v, cnt, aux): the tiled kernel issues all
+// loads of a slab before any store, so their latencies overlap.
 // operator() is the element-wise form used by the fp32 kernel.
 template <typename T>
 __device__ __forceinline__ void put4(T* p, const f32x4& v, int cnt) {
@@ -79,8 +82,13 @@ template <class Derived>
 struct EpBase {
   static constexpr bool kRowSum = false;
   static constexpr bool kScalar = false;  // store1 with one column per lane
+  using Aux = NoAux;
   __device__ float value(int64_t, int64_t, float v) const { return v; }
   __device__ float rowterm(float) const { return 0.0f; }
+  __device__ NoAux aux(int64_t, int64_t, int) const { return {}; }
+  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const NoAux&) const {
+    static_cast<const Derived&>(*this).store4(m, n, v, cnt);
+  }
   __device__ float operator()(int64_t m, int64_t n, float acc) const {
     const Derived& d = static_cast<const Derived&>(*this);
     const float v = d.value(m, n, acc);
@@ -101,10 +109,15 @@ struct EpF32 : EpBase<EpF32> {
   float* C;
   int64_t ldc;
   int accumulate;
+  using Aux = f32x4;
+  __device__ f32x4 aux(int64_t m, int64_t n, int cnt) const {
+    return accumulate ? get4<float>(C + m * ldc + n, cnt) : f32x4{0, 0, 0, 0};
+  }
+  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const f32x4& old) const {
+    put4<float>(C + m * ldc + n, v + old, cnt);
+  }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
-    float* p = C + m * ldc + n;
-    if (accumulate) v += get4<float>(p, cnt);
-    put4<float>(p, v, cnt);
+    store4a(m, n, v, cnt, aux(m, n, cnt));
   }
 };
 struct EpAtomic : EpBase<EpAtomic> {  // C += acc with fp32 atomics (split-K partial sums)
@@ -120,8 +133,15 @@ struct EpResid : EpBase<EpResid> {  // C = R + acc (residual stream, fp32)
   const float* R;
   float* C;
   int64_t ldc;
+  using Aux = f32x4;
+  __device__ f32x4 aux(int64_t m, int64_t n, int cnt) const {
+    return get4<float>(R + m * ldc + n, cnt);
+  }
+  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const f32x4& r) const {
+    put4<float>(C + m * ldc + n, v + r, cnt);
+  }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
-    put4<float>(C + m * ldc + n, v + get4<float>(R + m * ldc + n, cnt), cnt);
+    store4a(m, n, v, cnt, aux(m, n, cnt));
   }
 };
 template <typename T>
@@ -144,12 +164,16 @@ struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {
   const T* H;
   T* C;
   int64_t ldc;
-  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
-    const f32x4 h = get4<T>(H + m * ldc + n, cnt);
+  using Aux = f32x4;
+  __device__ f32x4 aux(int64_t m, int64_t n, int cnt) const { return get4<T>(H + m * ldc + n, cnt); }
+  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const f32x4& h) const {
     f32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = 2.0f * sqrtf(h[j]) * v[j];
     put4<T>(C + m * ldc + n, o, cnt);
+  }
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    store4a(m, n, v, cnt, aux(m, n, cnt));
   }
 };
 template <typename T>
@@ -528,8 +552,10 @@ void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t l
 }
 
 void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-               const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, hipStream_t s) {
-  run_f8<2>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_f32(C, N, 0), to_deq(dq), s);
+               const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+               hipStream_t s) {
+  run_f8<2>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0),
+            to_deq(dq), s);
 }
 
 void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,

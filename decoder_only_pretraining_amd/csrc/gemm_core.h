@@ -226,13 +226,16 @@ __device__ __forceinline__ void mfma8(f32x16& acc, const Frag8& a, const Frag8& 
 }
 
 // Dequantisation of an fp8 product. NoDeq: bf16 products. Deq8: in segment
-// i of the M, N or K index (axis 0, 1, 2; at most 3 segments) the code sums
-// are multiplied by f_i = 1 / (s_a,i * s_b,i), s = fmax / amax (1 if amax is
-// 0 or not finite). Along K the accumulator is rescaled by f_old / f_new
-// where the segment changes, and by the last f at the end.
+// i of the M or N index (axis 0 or 1; at most 3 segments) the code sums are
+// multiplied by f_i = 1 / (s_a,i * s_b,i), s = fmax / amax (1 if amax is 0
+// or not finite). Scales that change along K are handled by the caller, one
+// product per K segment (rescaling the accumulators inside the main loop
+// would move them out of the accumulation registers).
 struct NoDeq {
   static constexpr bool kOn = false;
 };
+// Aux type of an epilogue that reads no operand besides the accumulators.
+struct NoAux {};
 struct Deq8 {
   static constexpr bool kOn = true;
   const uint32_t* amax;
@@ -298,15 +301,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // fp8: dequantisation factor of each segment; the K segment in progress
+  // fp8: dequantisation factor of each segment
   float fdq[3] = {1.0f, 1.0f, 1.0f};
-  int kseg = 0;
   if constexpr (F8) {
 #pragma unroll
     for (int i = 0; i < 3; ++i)
       if (i < dq.nseg)
         fdq[i] = 1.0f / (fp8_scale(dq.amax[dq.sa[i]], dq.fa) * fp8_scale(dq.amax[dq.sb[i]], dq.fb));
-    if (dq.axis == 2) kseg = dq.seg(2 * k_lo);
   }
 
   const int64_t nk = (k_hi - k_lo + BK - 1) / BK;
@@ -348,41 +349,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const int64_t kn = k_lo + (kt + 1) * BK;
     if (more) fetch(kn, cur ^ 1);
     if constexpr (F8) {
-      // 64-wide contraction slices; per-tensor scales may change along K
+      // 64-wide contraction slices. A 32-code fragment takes 8 VGPRs, so fragments are not double-
+      // buffered wholesale (that spills beside 256 accumulator registers):
+      // the B fragments of the next slice and the A fragment of the next
+      // row are read while the current row's MFMAs run.
       constexpr int KS = BK / 32;
-      Frag8 a[2][TM], b[2][TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) read_frag8<BM, BK>(a[0][i], As[cur], wm * (BM / 2) + i * 32, 0, lane);
+      Frag8 b[2][TN], a[2];
 #pragma unroll
       for (int j = 0; j < TN; ++j) read_frag8<BN, BK>(b[0][j], Bs[cur], wn * (BN / 2) + j * 32, 0, lane);
+      read_frag8<BM, BK>(a[0], As[cur], wm * (BM / 2), 0, lane);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int p = ks & 1;
-        if (ks + 1 < KS) {
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
-            read_frag8<BM, BK>(a[p ^ 1][i], As[cur], wm * (BM / 2) + i * 32, ks + 1, lane);
+        for (int i = 0; i < TM; ++i) {
+          const int q = i & 1;  // TM is even: row i of every slice uses a[i & 1]
+          if (i + 1 < TM) {
+            read_frag8<BM, BK>(a[q ^ 1], As[cur], wm * (BM / 2) + (i + 1) * 32, ks, lane);
+          } else if (ks + 1 < KS) {
+            read_frag8<BM, BK>(a[q ^ 1], As[cur], wm * (BM / 2), ks + 1, lane);
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            read_frag8<BN, BK>(b[p ^ 1][j], Bs[cur], wn * (BN / 2) + j * 32, ks + 1, lane);
-        }
-        if (dq.axis == 2) {
-          const int sg = dq.seg(2 * (k_lo + kt * BK) + 64 * ks);
-          if (sg != kseg) {
-            const float r = fdq[kseg] / fdq[sg];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-              for (int j = 0; j < TN; ++j) acc[i][j] *= r;
-            kseg = sg;
+            for (int j = 0; j < TN; ++j)
+              read_frag8<BN, BK>(b[p ^ 1][j], Bs[cur], wn * (BN / 2) + j * 32, ks + 1, lane);
           }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) mfma8<MODE>(acc[i][j], a[q], b[p][j]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) mfma8<MODE>(acc[i][j], a[p][i], b[p][j]);
-        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
     Frag<bf16> a[2][TM], b[2][TN];
@@ -419,6 +413,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   // the slab in LDS as fp32, then write it back with 4-column vectors.
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SP;
   const int64_t mw = m0 + wm * (BM / 2), nw = n0 + wn * WN;
+  // Epilogues that read another operand load it in chunks of CH vectors
+  // per lane, all loads of a chunk issued before its stores.
+  constexpr bool kAux = !std::is_same<typename EP::Aux, NoAux>::value;
+  constexpr int NVS = 32 * WN / 4 / 64;  // 4-column vectors per lane per slab
+  constexpr int CH = NVS % 8 == 0 ? 8 : NVS % 6 == 0 ? 6 : NVS % 4 == 0 ? 4 : NVS;
+  static_assert(NVS % CH == 0, "chunks must tile the slab");
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
       for (int j = 0; j < TN; ++j) {
         const int64_t n = nw + j * 32 + (lane & 31);
         float x = acc[i][j][e];
-        if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.axis == 1 ? dq.seg(n) : kseg];
+        if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(n)];
         const float v = ep.value(m, n, x);
         if (EP::kRowSum && m < M && n < N) rs += ep.rowterm(v);
         stage[r * SP + j * 32 + (lane & 31)] = v;
@@ -449,6 +449,28 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         const int r = v / WN, cc = v % WN;
         const int64_t m = mw + i * 32 + r, n = nw + cc;
         if (m < M && n < N) ep.store1(m, n, stage[r * SP + cc]);
+      }
+    } else if constexpr (kAux) {
+#pragma unroll
+      for (int c = 0; c < NVS; c += CH) {
+        typename EP::Aux ax[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+          const int v = lane + 64 * (c + t);
+          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+          const int64_t m = mw + i * 32 + r, n = nw + c4;
+          if (m < M && n < N) ax[t] = ep.aux(m, n, (int)min<int64_t>(4, N - n));
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+          const int v = lane + 64 * (c + t);
+          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+          const int64_t m = mw + i * 32 + r, n = nw + c4;
+          if (m < M && n < N) {
+            const f32x4 val = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
+            ep.store4a(m, n, val, (int)min<int64_t>(4, N - n), ax[t]);
+          }
+        }
       }
     } else {
 #pragma unroll

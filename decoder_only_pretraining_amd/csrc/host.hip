@@ -554,7 +554,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         site("fp8.quant", s, [&] { quant_tok(gu, true, Fh, one_seg(slot(l, 11)), FP8_E5M2, g8t); });
         site("gemm.fc.dgrad", s, [&] {
           gemm8_f32(N, C, Fh, q8, Fh, w8t(l, 2), P128(Fh), deq1(slot(l, 11), slot(l, 4), FP8_E5M2),
-                    gtmp, s);
+                    gtmp, false, s);
         });
         site("gemm.fc.wgrad", s, [&] {
           gemm8_wgrad(Fh, C, Nk, g8t, Np, LY8(l, P.l_x28t), Np,
@@ -598,10 +598,14 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         site("fp8.quant", s, [&] {
           quant_tok(gqkv, true, d.Qkv, segs3(d.Cq, d.Cq + d.Ckv, g0, g1, g2), FP8_E5M2, g8t);
         });
-        // the q, k and v gradients carry their own scales along the contraction
+        // the q, k and v gradients carry their own scales along the
+        // contraction: one product per segment, summed into gtmp
         site("gemm.qkv.dgrad", s, [&] {
-          gemm8_f32(N, d.C, d.Qkv, q8, d.Qkv, w8t(l, 0), P128(d.Qkv),
-                    deq3(2, g0, g1, g2, slot(l, 0), slot(l, 1), slot(l, 2), FP8_E5M2), gtmp, s);
+          const int64_t k0[3] = {0, d.Cq, d.Cq + d.Ckv}, kn[3] = {d.Cq, d.Ckv, d.Ckv};
+          const int ga8[3] = {g0, g1, g2};
+          for (int i = 0; i < 3; ++i)
+            gemm8_f32(N, d.C, kn[i], q8 + k0[i], d.Qkv, w8t(l, 0) + k0[i], P128(d.Qkv),
+                      deq1(ga8[i], slot(l, i), FP8_E5M2), gtmp, i > 0, s);
         });
         site("gemm.qkv.wgrad", s, [&] {
           const int x = slot(l, 6);

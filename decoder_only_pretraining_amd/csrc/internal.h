@@ -196,8 +196,8 @@ void launch_fp8_quant(const void* src, bool bf16_src, int64_t R, int64_t C, bool
                       const Segs& sg, const uint32_t* amax, int fmt, uint8_t* out, uint8_t* outT,
                       int64_t pitchT, hipStream_t s);
 
-// Dequantisation of an fp8 product: in segment i of the M, N or K index
-// (axis 0, 1, 2) the sum of code products is multiplied by
+// Dequantisation of an fp8 product: in segment i of the M or N index
+// (axis 0 or 1) the sum of code products is multiplied by
 // 1 / (s(amax[sa[i]], fa) * s(amax[sb[i]], fb)).
 struct Fp8Deq {
   const uint32_t* amax;
@@ -220,8 +220,10 @@ void gemm8_relu2(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
 void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                     const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const void* H, void* C,
                     hipStream_t s);
+// C (+)= the product (accumulate: add to C).
 void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-               const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, hipStream_t s);
+               const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+               hipStream_t s);
 // Weight gradient (K = tokens, split over workgroups with fp32 atomics when
 // that fills the machine); C (+)= the product.
 void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
