@@ -78,6 +78,14 @@ __device__ __forceinline__ f32x4 get4(const T* p, int cnt) {
   return r;
 }
 
+// sqrt of an activation: the hardware square root (about 1 ulp) for bf16
+// activations, the correctly rounded one for fp32.
+template <typename T>
+__device__ __forceinline__ float sqrt_act(float x) {
+  if constexpr (sizeof(T) == 2) return __builtin_amdgcn_sqrtf(x);
+  else return sqrtf(x);
+}
+
 template <class Derived>
 struct EpBase {
   static constexpr bool kRowSum = false;
@@ -169,7 +177,7 @@ struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {
   __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const f32x4& h) const {
     f32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = 2.0f * sqrtf(h[j]) * v[j];
+    for (int j = 0; j < 4; ++j) o[j] = 2.0f * sqrt_act<T>(h[j]) * v[j];
     put4<T>(C + m * ldc + n, o, cnt);
   }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
@@ -182,9 +190,18 @@ struct EpSoftcap : EpBase<EpSoftcap<T>> {  // c = cap * tanh(z / cap); row sums 
   T* C;
   int64_t ldc;
   float cap;
+  float k2;  // 2 log2(e) / cap
   // the stored (rounded) value, so the row sums match what the backward reads
   __device__ float value(int64_t, int64_t, float z) const {
-    return to_f(from_f<T>(cap * tanhf(z / cap)));
+    if constexpr (sizeof(T) == 2) {
+      // tanh(u) = 1 - 2 / (1 + e^(2u)) with the hardware exp2 and reciprocal
+      // (about 1 ulp each): the absolute error of c, ~cap * 2^-23, is far
+      // below the bf16 step of the stored value; saturates to +-cap
+      const float e = __builtin_amdgcn_exp2f(z * k2);
+      return to_f(from_f<T>(cap - (2.0f * cap) * __builtin_amdgcn_rcpf(1.0f + e)));
+    } else {
+      return cap * tanhf(z / cap);
+    }
   }
   __device__ float rowterm(float c) const { return __expf(c - cap); }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
@@ -240,6 +257,7 @@ EpSoftcap<T> mk_softcap(void* C, int64_t ld, float cap) {
   e.C = static_cast<T*>(C);
   e.ldc = ld;
   e.cap = cap;
+  e.k2 = 2.0f * 1.4426950408889634f / cap;
   return e;
 }
 
