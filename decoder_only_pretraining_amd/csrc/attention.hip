@@ -25,6 +25,9 @@
 // Blocks of the score matrix that lie wholly inside the causal window skip
 // the per-element mask.
 #include "device_common.h"
+#include "gemm_core.h"
+
+#include <type_traits>
 #include "internal.h"
 
 namespace gk {
@@ -265,6 +268,182 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
                       o[db][4 * g + 3] * inv);
       }
     if (hi == 0) lse2[(rb + t) * H + h] = m_i + log2f(l_i);
+  }
+}
+
+// ------------------------------------------------------------ forward, bf16
+// A workgroup of 8 wavefronts owns 256 queries of one head, 32 per
+// wavefront; two wavefronts share each SIMD so one's softmax arithmetic
+// overlaps the other's MFMAs. K/V tiles of 64 keys stream into three LDS
+// stages with direct global->LDS loads issued two tiles ahead by wavefronts
+// 0-3. K is kept as a swizzled K-major tile [key][d]; V as [key][d + 32]
+// for transposing fragment reads. The running max used for the
+// exponentials is raised only when a query's maximum grows by more than
+// 2^8 (then the output and sum are rescaled once for the wavefront);
+// probabilities up to 2^8 are exact enough in fp32 and bf16. Only tiles on
+// the causal diagonal or the window edge compute a mask. The linear block
+// id runs over (query tile, head, batch), latest (costliest) tiles first.
+template <int D>
+__global__ __launch_bounds__(512) void attn_fwd_tiled_kernel(const bf16* __restrict__ qkv,
+                                                             bf16* __restrict__ out,
+                                                             float* __restrict__ lse2, int T_,
+                                                             int H, int Hk, int W, int full,
+                                                             float c2, int nq, int nb) {
+  constexpr int BQ = 256, BKV = 64, S = 3;
+  constexpr float kTau = 8.0f;  // log2 of the largest unnormalised probability
+  using GK = TileGeom<BKV, D, true>;    // K tile: rows = keys, contraction = d
+  using GV = TileGeom<D, BKV, false>;   // V tile: [key][d + 32]
+  using LK = DirectLoader<BKV, D, true>;
+  using LV = DirectLoader<D, BKV, false>;
+  static_assert(LK::CHUNKS % 4 == 0 && LV::CHUNKS % 4 == 0, "whole chunks per loading wavefront");
+  constexpr int PER_WAVE = LK::CHUNKS / 4 + LV::CHUNKS / 4;  // loads per loading wavefront per tile
+  static_assert(PER_WAVE < 16, "vmcnt field");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[S][GK::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[S][GV::ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
+  const bool loader = wv < 4;
+  const int L = blockIdx.x;
+  const int qt = nq - 1 - L / (H * nb);
+  const int h = (L % (H * nb)) % H, b = (L % (H * nb)) / H;
+  const int j = h / (H / Hk);
+  const int Qkv = (H + 2 * Hk) * D;
+  const int64_t rb = (int64_t)b * T_;
+  const int t0 = qt * BQ, tw = t0 + wv * 32, t = tw + (lane & 31);
+  const bf16* kbase = qkv + (H + j) * D;
+  const bf16* vbase = qkv + (H + Hk + j) * D;
+
+  Frag<bf16> qf[D / 16];
+  load_row_frags<bf16, D>(qf, qkv + (rb + t) * Qkv + h * D, t < T_, lane);
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
+  float m_run = kNegInf, l_i = 0.0f;
+
+  const int first = ((full ? 0 : max(0, t0 - W)) / BKV) * BKV;
+  const int ntile = (min(T_, t0 + BQ) - first + BKV - 1) / BKV;
+  const int w_lo = full ? 0 : max(0, tw - W), w_hi = min(T_, tw + 32);
+  const unsigned wmax = full ? 0x7fffffffu : (unsigned)W;
+  auto issue = [&](int it) {
+    if (!loader) return;
+    const int64_t r0 = rb + first + (int64_t)it * BKV;
+    LK::issue(kbase, Qkv, r0, rb + T_, 0, D, Ks[it % S], wv, lane);
+    LV::issue(vbase, Qkv, 0, D, r0, rb + T_, Vs[it % S], wv, lane);
+  };
+#pragma unroll
+  for (int it = 0; it < S - 1; ++it)
+    if (it < ntile) issue(it);
+  if (ntile > 1 && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);  // tile 0 landed
+  else __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  // One tile; the stage buffer CUR is a compile-time index so every LDS
+  // address is a per-lane base plus an immediate offset.
+  auto tile = [&](int it, auto cur_c) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const int s0 = first + it * BKV;
+    if (it + S - 1 < ntile) issue(it + S - 1);
+    if (tw < T_ && s0 < w_hi && s0 + BKV > w_lo) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[sb][e] = 0.0f;
+        Frag<bf16> kf[2];
+        read_frag<BKV, D, true>(kf[0], Ks[CUR], sb * 32, 0, lane);
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          if (kc + 1 < D / 16) read_frag<BKV, D, true>(kf[(kc + 1) & 1], Ks[CUR], sb * 32, kc + 1, lane);
+          mfma(sacc[sb], kf[kc & 1], qf[kc]);
+        }
+      }
+      // all 64 keys visible to all 32 queries of the wavefront?
+      const bool interior = (s0 + BKV - 1 <= tw) && (full || tw + 31 - s0 <= W);
+      if (!interior) {
+        asm volatile("" ::: "memory");  // keep the mask on its own branch
+        // key s0 + sb*32 + r is visible iff 0 <= t - key <= W (unsigned compare)
+        const int u = t - s0 - 4 * hi;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = sb * 32 + (e >> 2) * 8 + (e & 3);
+            if ((unsigned)(u - r) > wmax) sacc[sb][e] = kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sacc[sb][e], sacc[sb][e + 1]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+      // raise the reference max only when a probability would exceed 2^tau
+      const bool need = mx > m_run + kTau;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        asm volatile("" ::: "memory");  // a real branch: the rescale is rare
+        const float m_new = need ? mx : m_run;
+        // 0 on a lane's first visible tile; 1 for lanes that keep their max
+        // (including lanes with no visible key yet: -inf - -inf is NaN)
+        const float alpha = need ? exp2_fast(m_run - m_new) : 1.0f;
+        l_i *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == kNegInf ? 0.0f : m_run;
+      float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = exp2_fast(fmaf(sacc[sb][e], c2, -m_use));
+          const float p1 = exp2_fast(fmaf(sacc[sb][e + 1], c2, -m_use));
+          sacc[sb][e] = p0;
+          sacc[sb][e + 1] = p1;
+          ps0 += p0;
+          ps1 += p1;
+        }
+      float ps = ps0 + ps1;
+      ps += __shfl_xor(ps, 32, 64);
+      l_i += ps;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<bf16> pf;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) frag_set(pf, jj, sacc[sb][8 * c + jj]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<bf16> vf;
+            frag_down<GV::PITCH>(vf, Vs[CUR], sb * 32 + 16 * c, db * 32, lane);
+            mfma(o[db], vf, pf);
+          }
+        }
+    }
+    // tile it + 1 landed (tile it + 2 may still be in flight)
+    if (it + S - 1 < ntile && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  };
+  static_assert(S == 3, "the tile loop is unrolled by the stage count");
+  for (int it = 0; it < ntile; it += S) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntile) tile(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < ntile) tile(it + 2, std::integral_constant<int, 2>{});
+  }
+  if (t < T_) {
+    const float inv = 1.0f / l_i;
+    bf16* op = out + (rb + t) * (H * D) + h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + g * 8 + hi * 4;
+        store_col4<bf16>(op + d, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
+                         o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      }
+    if (hi == 0) lse2[(rb + t) * H + h] = m_run + log2f(l_i);
   }
 }
 
@@ -540,9 +719,16 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
 template <typename T, int D>
 void fwd(const gpt::Dims& d, bool full, const void* qkv, void* out, float* lse, hipStream_t s) {
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
-  dim3 grid((unsigned)((d.T + 127) / 128), d.H, d.B);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(qkv),
-                     static_cast<T*>(out), lse, d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2);
+  if constexpr (sizeof(T) == 2) {
+    const int nq = (d.T + 255) / 256;
+    hipLaunchKernelGGL((attn_fwd_tiled_kernel<D>), dim3((unsigned)(nq * d.H * d.B)), dim3(512), 0,
+                       s, static_cast<const bf16*>(qkv), static_cast<bf16*>(out), lse, d.T, d.H,
+                       d.Hk, d.W, full ? 1 : 0, c2, nq, d.B);
+  } else {
+    dim3 grid((unsigned)((d.T + 127) / 128), d.H, d.B);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(qkv),
+                       static_cast<T*>(out), lse, d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2);
+  }
 }
 
 template <typename T, int D>

@@ -49,7 +49,11 @@ template <int FMT>
 __device__ __forceinline__ uint32_t cvt4(const float* v, float s, float fmax) {
   float c[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) c[j] = fminf(fmaxf(v[j] * s, -fmax), fmax);
+  for (int j = 0; j < 4; ++j) {
+    // saturate; a NaN input stays NaN (and converts to a NaN code)
+    const float x = v[j] * s;
+    c[j] = x > fmax ? fmax : (x < -fmax ? -fmax : x);
+  }
   int w;
   if constexpr (FMT == gpt::FP8_E4M3) {
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);

@@ -123,7 +123,7 @@ struct Loader {
 
 // Zero page for tile slots outside the matrix: lanes whose slot lies past
 // M, N or K copy zeros from here, so ragged K tails contribute nothing.
-__device__ __attribute__((aligned(256))) uint32_t g_zero_page[256];
+static __device__ __attribute__((aligned(256))) uint32_t g_zero_page[256];
 
 // Direct global->LDS stage loader (gfx950 global_load_lds, 16 bytes per
 // lane): one wavefront instruction fills a contiguous 1 KiB of LDS, lane l
