@@ -18,7 +18,9 @@
 // query-major pass recomputes S^T and dP^T and accumulates dQ^T. No atomics.
 //
 // Softmax works in base 2: the saved statistic is lse2 = log2(sum_s 2^(S*c))
-// with c = log2(e) / sqrt(D), so P = 2^(S*c - lse2).
+// with c = log2(e) / sqrt(D), so P = 2^(S*c - lse2). lse2 and delta are
+// stored [batch][head][token], so a run of queries of one head is
+// contiguous.
 //
 // All three kernels stream their tiles through two LDS buffers: the global
 // loads of the next tile are in flight while the current tile's MFMAs run.
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
         store_col4<T>(op + d, o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
                       o[db][4 * g + 3] * inv);
       }
-    if (hi == 0) lse2[(rb + t) * H + h] = m_i + log2f(l_i);
+    if (hi == 0) lse2[((int64_t)b * H + h) * T_ + t] = m_i + log2f(l_i);
   }
 }
 
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(512) void attn_fwd_tiled_kernel(const bf16* __restr
         store_col4<bf16>(op + d, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
                          o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
       }
-    if (hi == 0) lse2[(rb + t) * H + h] = m_run + log2f(l_i);
+    if (hi == 0) lse2[((int64_t)b * H + h) * T_ + t] = m_run + log2f(l_i);
   }
 }
 
@@ -452,12 +454,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ gO,
                                                          const T* __restrict__ O,
                                                          float* __restrict__ delta, int64_t NH,
-                                                         int D) {
+                                                         int D, int H, int T_) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (n, h) pair
+  // i runs over [batch][head][token], token fastest, like delta itself
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= NH) return;
+  const int64_t bh = i / T_, t = i % T_;
+  const int64_t row = ((bh / H) * T_ + t) * H + bh % H;  // (n, h) row of gO and O
   float s = 0.0f;
-  for (int d = lane; d < D; d += 64) s += to_f(gO[i * D + d]) * to_f(O[i * D + d]);
+  for (int d = lane; d < D; d += 64) s += to_f(gO[row * D + d]) * to_f(O[row * D + d]);
   s = wave_sum(s);
   if (lane == 0) delta[i] = s;
 }
@@ -505,8 +510,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
     dst.load(gO + h * D, rb + t0, T_ - t0, Cq, tid);
     if (tid < BQ2) {
       const bool ok = t0 + tid < T_;
-      st_l = ok ? lse2[(rb + t0 + tid) * H + h] : 0.0f;
-      st_d = ok ? delta[(rb + t0 + tid) * H + h] : 0.0f;
+      st_l = ok ? lse2[((int64_t)b * H + h) * T_ + t0 + tid] : 0.0f;
+      st_d = ok ? delta[((int64_t)b * H + h) * T_ + t0 + tid] : 0.0f;
     }
   };
   auto put = [&](int buf) {
@@ -627,8 +632,8 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
   Frag<T> qf[D / 16], df[D / 16];
   load_row_frags<T, D>(qf, qkv + (rb + t) * Qkv + h * D, tv, lane);
   load_row_frags<T, D>(df, gO + (rb + t) * Cq + h * D, tv, lane);
-  const float lt = tv ? lse2[(rb + t) * H + h] : 0.0f;
-  const float dt = tv ? delta[(rb + t) * H + h] : 0.0f;
+  const float lt = tv ? lse2[((int64_t)b * H + h) * T_ + t] : 0.0f;
+  const float dt = tv ? delta[((int64_t)b * H + h) * T_ + t] : 0.0f;
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -716,6 +721,373 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
   }
 }
 
+// ------------------------------------------------------------ backward, bf16
+// Tiles read both by rows (8 consecutive columns of one row, 16 bytes per
+// lane) and transposed (4 consecutive rows of one column, ds_read_b64_tr_b16)
+// are kept with row pitch D + 32 and the 16-byte granules of row t XOR-
+// permuted by (t >> 2) & 3. For a 16-lane row read (16 rows, one granule)
+// the pitch spreads rows over four bank offsets and the permutation over
+// the other four; for a 32-lane transposing read (4 rows, 4 granules of an
+// aligned group) the rows fall 8 bank pairs apart and the permutation stays
+// inside the group: neither pattern conflicts.
+template <int ROWS, int D>
+struct Dual {
+  static constexpr int PITCH = D + 32;
+  static constexpr int ELEMS = ROWS * PITCH;
+  static constexpr int CHUNKS = ELEMS * 2 / 1024;
+  static_assert(ELEMS * 2 % 1024 == 0 && CHUNKS % 4 == 0, "whole chunks per loading wavefront");
+  __device__ __forceinline__ static int off(int t, int col) {
+    return t * PITCH + ((((col >> 3) ^ ((t >> 2) & 3)) << 3) | (col & 7));
+  }
+  // Direct global->LDS fill by wavefronts 0-3: rows row0 .. row0 + ROWS - 1
+  // of a matrix with row stride ld (rows at or past rows_end read as zero).
+  __device__ __forceinline__ static void issue(const bf16* __restrict__ p, int64_t ld,
+                                               int64_t row0, int64_t rows_end, bf16* lds,
+                                               int wave, int lane) {
+#pragma unroll
+    for (int c = wave; c < CHUNKS; c += 4) {
+      const int o = c * 1024 + lane * 16;
+      const int t = o / (PITCH * 2), pg = (o % (PITCH * 2)) / 16;
+      const int gi = pg ^ ((t >> 2) & 3);
+      const bool ok = row0 + t < rows_end;
+      const bf16* src = ok ? p + (row0 + t) * ld + gi * 8
+                           : reinterpret_cast<const bf16*>(g_zero_page) + (lane & 15) * 8;
+      if (gi < D / 8)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)src,
+            (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(lds) + c * 1024), 16,
+            0, 0);
+    }
+  }
+  // 32 rows from row0, contraction slice kc (lane l: row row0 + l%32,
+  // columns 16 kc + 8 (l/32) .. +7)
+  __device__ __forceinline__ static void row_frag(Frag<bf16>& f, const bf16* lds, int row0, int kc,
+                                                  int lane) {
+    f.v = *reinterpret_cast<const bf16x8*>(lds + off(row0 + (lane & 31), kc * 16 + (lane >> 5) * 8));
+  }
+  // columns col0 .. col0 + 31 as rows of the operand, contraction rows in the
+  // accumulator slot order from kbase (see frag_down)
+  __device__ __forceinline__ static void tr_frag(Frag<bf16>& f, const bf16* lds, int kbase, int col0,
+                                                 int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int g16 = lane >> 4, L = lane & 15;
+    const int k0 = kbase + (g16 >> 1) * 4 + (L >> 2);
+    const int m = col0 + (g16 & 1) * 16 + (L & 3) * 4;
+    union {
+      struct { v4i16 a, b; } s;
+      bf16x8 v;
+    } u;
+    u.s.a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off(k0, m)));
+    u.s.b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + off(k0 + 8, m)));
+    f.v = u.v;
+  }
+};
+
+// 64 floats of lse2 and of delta for query rows t0 .. t0 + 63 of one head,
+// into st[0..63] and st[64..127]: 32 lanes of wavefront 0, 16 bytes each.
+// Reads may run up to 63 floats past the head's row (the regions carry a
+// 256-byte pad); those queries are masked.
+__device__ __forceinline__ void stats_issue(const float* __restrict__ lse2,
+                                            const float* __restrict__ delta, int64_t row,
+                                            float* st, int lane) {
+  if (lane < 32) {
+    const float* src = (lane < 16 ? lse2 : delta) + row + (lane & 15) * 4;
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)st, 16, 0, 0);
+  }
+}
+
+// dK, dV: a workgroup of 8 wavefronts owns 256 keys of one KV head (32 per
+// wavefront, K and V rows held as fragments) and walks the (query head of
+// the group, 64-query tile) steps that see them; Q, dO and the softmax
+// statistics stream through three LDS stages, two steps ahead.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
+    int full, float c2, float scale, int nkt, int nb) {
+  constexpr int BK2 = 32 * NW, BQ2 = 64, S = 3;
+  using DT = Dual<BQ2, D>;
+  constexpr int PER_WAVE = 2 * DT::CHUNKS / 4;  // Q and dO loads per loading wavefront
+  static_assert(PER_WAVE + 1 < 16, "vmcnt field");
+  __shared__ __attribute__((aligned(16))) bf16 Qs[S][DT::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[S][DT::ELEMS];
+  __shared__ __attribute__((aligned(16))) float st[S][2 * BQ2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
+  const bool loader = wv < 4;
+  const int L = blockIdx.x;
+  const int kt = L / (Hk * nb);  // early keys are seen by the most queries: first
+  const int j = (L % (Hk * nb)) % Hk, b = (L % (Hk * nb)) / Hk;
+  const int G = H / Hk;
+  const int Qkv = (H + 2 * Hk) * D, Cq = H * D;
+  const int64_t rb = (int64_t)b * T_;
+  const int s0 = kt * BK2, sw = s0 + wv * 32, s = sw + (lane & 31);
+
+  Frag<bf16> kf[D / 16], vf[D / 16];
+  load_row_frags<bf16, D>(kf, qkv + (rb + s) * Qkv + (H + j) * D, s < T_, lane);
+  load_row_frags<bf16, D>(vf, qkv + (rb + s) * Qkv + (H + Hk + j) * D, s < T_, lane);
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[i][e] = 0.0f;
+      dv[i][e] = 0.0f;
+    }
+  const unsigned wmax = full ? 0x7fffffffu : (unsigned)W;
+  const int q_first = (s0 / BQ2) * BQ2;
+  const int q_hi = full ? T_ : min(T_, s0 + BK2 + W);  // exclusive
+  const int nq = (q_hi - q_first + BQ2 - 1) / BQ2;
+  const int nstep = G * nq;
+  auto issue = [&](int step) {
+    if (!loader) return;
+    const int h = j * G + step / nq, t0 = q_first + (step % nq) * BQ2;
+    DT::issue(qkv + h * D, Qkv, rb + t0, rb + T_, Qs[step % S], wv, lane);
+    DT::issue(gO + h * D, Cq, rb + t0, rb + T_, dOs[step % S], wv, lane);
+    if (wv == 0) stats_issue(lse2, delta, ((int64_t)b * H + h) * T_ + t0, st[step % S], lane);
+  };
+  // this wavefront's loads of one step
+  auto wait_all_but_one = [&] {
+    if (wv == 0) __builtin_amdgcn_s_waitcnt(0x0f70 | (PER_WAVE + 1));
+    else if (loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+  };
+#pragma unroll
+  for (int st0 = 0; st0 < S - 1; ++st0)
+    if (st0 < nstep) issue(st0);
+  if (nstep > 1) wait_all_but_one();
+  else __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  auto step_fn = [&](int step, auto cur_c) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const int t0 = q_first + (step % nq) * BQ2;
+    if (step + S - 1 < nstep) issue(step + S - 1);
+    if (sw < T_) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int tlo = t0 + tb * 32;
+        // any (query, key) pair of this 32x32 block visible?
+        if (!(tlo < T_ && tlo + 31 >= sw && (full || tlo - (sw + 31) <= W))) continue;
+        const bool interior = tlo >= sw + 31 && (full || tlo + 31 - sw <= W) && tlo + 31 < T_;
+        f32x16 sa, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sa[e] = 0.0f;
+          dp[e] = 0.0f;
+        }
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          Frag<bf16> qa, da;
+          DT::row_frag(qa, Qs[CUR], tb * 32, kc, lane);
+          DT::row_frag(da, dOs[CUR], tb * 32, kc, lane);
+          mfma(sa, qa, kf[kc]);
+          mfma(dp, da, vf[kc]);
+        }
+        // accumulator rows t = tlo + 8 (e/4) + 4 hi + e%4: four consecutive
+        // rows per group g = e/4, so their statistics load as one vector
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int tl = tb * 32 + g * 8 + hi * 4;
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(&st[CUR][tl]);
+          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&st[CUR][BQ2 + tl]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * g + r;
+            const float p = exp2_fast(fmaf(sa[e], c2, -lv[r]));
+            sa[e] = p;
+            dp[e] = p * (dp[e] - dv4[r]);
+          }
+        }
+        if (!interior) {
+          asm volatile("" ::: "memory");  // keep the mask on its own branch
+          // query tq = t0 + tl + r sees key s iff tq < T and 0 <= tq - s <= W
+          const int u = t0 + tb * 32 + 4 * hi - s;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = (e >> 2) * 8 + (e & 3);
+            const bool vis = (unsigned)(u + r) <= wmax && t0 + tb * 32 + 4 * hi + r < T_;
+            if (!vis) {
+              sa[e] = 0.0f;
+              dp[e] = 0.0f;
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<bf16> pf, dsf;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            frag_set(pf, jj, sa[8 * c + jj]);
+            frag_set(dsf, jj, dp[8 * c + jj]);
+          }
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<bf16> doT, qT;
+            DT::tr_frag(doT, dOs[CUR], tb * 32 + 16 * c, db * 32, lane);
+            DT::tr_frag(qT, Qs[CUR], tb * 32 + 16 * c, db * 32, lane);
+            mfma(dv[db], doT, pf);
+            mfma(dk[db], qT, dsf);
+          }
+        }
+      }
+    }
+    if (step + S - 1 < nstep) wait_all_but_one();
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  };
+  static_assert(S == 3, "the step loop is unrolled by the stage count");
+  for (int step = 0; step < nstep; step += S) {
+    step_fn(step, std::integral_constant<int, 0>{});
+    if (step + 1 < nstep) step_fn(step + 1, std::integral_constant<int, 1>{});
+    if (step + 2 < nstep) step_fn(step + 2, std::integral_constant<int, 2>{});
+  }
+  if (s < T_) {
+    bf16* kp = gqkv + (rb + s) * Qkv + (H + j) * D;
+    bf16* vp = gqkv + (rb + s) * Qkv + (H + Hk + j) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + g * 8 + hi * 4;
+        store_col4<bf16>(kp + d, dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale,
+                         dk[db][4 * g + 2] * scale, dk[db][4 * g + 3] * scale);
+        store_col4<bf16>(vp + d, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2],
+                         dv[db][4 * g + 3]);
+      }
+  }
+}
+
+// dQ: a workgroup of 8 wavefronts owns 256 queries of one head (32 per
+// wavefront, Q and dO rows held as fragments) and walks the visible 64-key
+// tiles; K (read by rows and transposed) and V (read by rows) stream
+// through three LDS stages, two tiles ahead.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
+    int full, float c2, float scale, int nq, int nb) {
+  constexpr int BQ = 32 * NW, BKV = 64, S = 3;
+  using DK = Dual<BKV, D>;
+  using GV = TileGeom<BKV, D, true>;
+  using LV = DirectLoader<BKV, D, true>;
+  static_assert(LV::CHUNKS % 4 == 0, "whole chunks per loading wavefront");
+  constexpr int PER_WAVE = DK::CHUNKS / 4 + LV::CHUNKS / 4;
+  static_assert(PER_WAVE < 16, "vmcnt field");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[S][DK::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[S][GV::ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
+  const bool loader = wv < 4;
+  const int L = blockIdx.x;
+  const int qt = nq - 1 - L / (H * nb);
+  const int h = (L % (H * nb)) % H, b = (L % (H * nb)) / H;
+  const int j = h / (H / Hk);
+  const int Qkv = (H + 2 * Hk) * D, Cq = H * D;
+  const int64_t rb = (int64_t)b * T_;
+  const int t0 = qt * BQ, tw = t0 + wv * 32, t = tw + (lane & 31);
+  const bool tv = t < T_;
+  const bf16* kbase = qkv + (H + j) * D;
+  const bf16* vbase = qkv + (H + Hk + j) * D;
+
+  Frag<bf16> qf[D / 16], df[D / 16];
+  load_row_frags<bf16, D>(qf, qkv + (rb + t) * Qkv + h * D, tv, lane);
+  load_row_frags<bf16, D>(df, gO + (rb + t) * Cq + h * D, tv, lane);
+  const float lt = tv ? lse2[((int64_t)b * H + h) * T_ + t] : 0.0f;
+  const float dt = tv ? delta[((int64_t)b * H + h) * T_ + t] : 0.0f;
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[i][e] = 0.0f;
+  const unsigned wmax = full ? 0x7fffffffu : (unsigned)W;
+  const int first = ((full ? 0 : max(0, t0 - W)) / BKV) * BKV;
+  const int ntile = (min(T_, t0 + BQ) - first + BKV - 1) / BKV;
+  const int w_lo = full ? 0 : max(0, tw - W), w_hi = min(T_, tw + 32);
+  auto issue = [&](int it) {
+    if (!loader) return;
+    const int64_t r0 = rb + first + (int64_t)it * BKV;
+    DK::issue(kbase, Qkv, r0, rb + T_, Ks[it % S], wv, lane);
+    LV::issue(vbase, Qkv, r0, rb + T_, 0, D, Vs[it % S], wv, lane);
+  };
+#pragma unroll
+  for (int it = 0; it < S - 1; ++it)
+    if (it < ntile) issue(it);
+  if (ntile > 1 && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
+  else __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  auto tile = [&](int it, auto cur_c) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const int s0 = first + it * BKV;
+    if (it + S - 1 < ntile) issue(it + S - 1);
+    if (tw < T_ && s0 < w_hi && s0 + BKV > w_lo) {
+      const bool interior = (s0 + BKV - 1 <= tw) && (full || tw + 31 - s0 <= W);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        f32x16 sa, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sa[e] = 0.0f;
+          dp[e] = 0.0f;
+        }
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          Frag<bf16> ka, va;
+          DK::row_frag(ka, Ks[CUR], sb * 32, kc, lane);
+          read_frag<BKV, D, true>(va, Vs[CUR], sb * 32, kc, lane);
+          mfma(sa, ka, qf[kc]);
+          mfma(dp, va, df[kc]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2_fast(fmaf(sa[e], c2, -lt));
+          dp[e] = p * (dp[e] - dt);
+        }
+        if (!interior) {
+          asm volatile("" ::: "memory");  // keep the mask on its own branch
+          const int u = t - s0 - sb * 32 - 4 * hi;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = (e >> 2) * 8 + (e & 3);
+            if ((unsigned)(u - r) > wmax) dp[e] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          Frag<bf16> dsf;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) frag_set(dsf, jj, dp[8 * c + jj]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            Frag<bf16> kT;
+            DK::tr_frag(kT, Ks[CUR], sb * 32 + 16 * c, db * 32, lane);
+            mfma(dq[db], kT, dsf);
+          }
+        }
+      }
+    }
+    if (it + S - 1 < ntile && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
+    else __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  };
+  static_assert(S == 3, "the tile loop is unrolled by the stage count");
+  for (int it = 0; it < ntile; it += S) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntile) tile(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < ntile) tile(it + 2, std::integral_constant<int, 2>{});
+  }
+  if (tv) {
+    bf16* qp = gqkv + (rb + t) * Qkv + h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + g * 8 + hi * 4;
+        store_col4<bf16>(qp + d, dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale,
+                         dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale);
+      }
+  }
+}
+
 template <typename T, int D>
 void fwd(const gpt::Dims& d, bool full, const void* qkv, void* out, float* lse, hipStream_t s) {
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
@@ -736,6 +1108,19 @@ void bwd(const gpt::Dims& d, bool full, const void* qkv, const void* gO, const f
          const float* delta, void* gqkv, hipStream_t s) {
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   const float scale = 1.0f / sqrtf((float)D);
+  if constexpr (sizeof(T) == 2) {
+    constexpr int NW = 4;  // one wavefront per SIMD: the backward needs > 256 registers
+    const int nkt = (d.T + 32 * NW - 1) / (32 * NW), nq = (d.T + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((attn_bwd_kv_tiled_kernel<D, NW>), dim3((unsigned)(nkt * d.Hk * d.B)),
+                       dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
+                       static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
+                       d.Hk, d.W, full ? 1 : 0, c2, scale, nkt, d.B);
+    hipLaunchKernelGGL((attn_bwd_q_tiled_kernel<D, NW>), dim3((unsigned)(nq * d.H * d.B)),
+                       dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
+                       static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
+                       d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B);
+    return;
+  }
   dim3 gkv((unsigned)((d.T + 127) / 128), d.Hk, d.B);
   hipLaunchKernelGGL((attn_bwd_kv_kernel<T, D>), gkv, dim3(256), 0, s, static_cast<const T*>(qkv),
                      static_cast<const T*>(gO), lse, delta, static_cast<T*>(gqkv), d.T, d.H, d.Hk,
@@ -767,10 +1152,11 @@ void launch_attn_delta(const Dims& d, const void* gO, const void* O, float* delt
   dim3 grid((unsigned)((NH + 3) / 4));
   if (d.bf16)
     hipLaunchKernelGGL(attn_delta_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(gO),
-                       static_cast<const bf16*>(O), delta, NH, d.D);
+                       static_cast<const bf16*>(O), delta, NH, d.D, d.H, d.T);
   else
     hipLaunchKernelGGL(attn_delta_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(gO), static_cast<const float*>(O), delta, NH, d.D);
+                       static_cast<const float*>(gO), static_cast<const float*>(O), delta, NH, d.D,
+                       d.H, d.T);
 }
 
 void launch_attn_bwd(const Dims& d, bool full, const void* qkv, const void* gO, const float* lse,

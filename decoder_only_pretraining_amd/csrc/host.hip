@@ -204,7 +204,7 @@ Plan make_plan(const Dims& d) {
   p.l_rqk = ltake(N * (d.H + d.Hk) * 4);
   p.l_a = ltake(N * d.Hk * 4);
   p.l_attn = ltake(N * d.Cq * A);
-  p.l_lse = ltake(N * d.H * 4);
+  p.l_lse = ltake(N * d.H * 4 + 256);  // [B][H][T]; the pad covers 16-byte tile reads past T
   p.l_xmid = ltake(N * d.C * 4);
   p.l_xn2 = ltake(N * d.C * A);
   p.l_r2 = ltake(N * 4);
@@ -232,7 +232,7 @@ Plan make_plan(const Dims& d) {
   p.gtmp = take(N * d.C * 4);
   p.gO = take(N * d.Cq * A);
   p.gqkv = take(N * d.Qkv * A);
-  p.delta = take(N * d.H * 4);
+  p.delta = take(N * d.H * 4 + 256);  // [B][H][T], padded like lse
   p.ga = take(N * d.Hk * 4);
   p.lam_blocks = (int)((d.N + 3) / 4);
   p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
