@@ -73,7 +73,7 @@ ROOF_KERNELS = {
     "wgrad": dict(
         sites="gemm.qkv.wgrad,gemm.fc.wgrad,gemm.mp.wgrad,gemm.o.wgrad",
         desc="weight-gradient GEMMs of the blocks (split-K, fp32 atomics): "
-             "gemm_bf16_kernel<256, 192, 64, false, false, PreId, PreId, EpAtomic>",
+             "gemm_bf16_kernel<256, 192, 64, false, false, 0, PreId, PreId, EpAtomic, NoDeq>",
         flops=_wgrad_flops, pmc="profiles/gemm_wgrad_d12_pmc.txt"),
     "lm_fwd": dict(
         sites="gemm.lm.fwd", desc="lm_head GEMM + tanh softcap epilogue",
