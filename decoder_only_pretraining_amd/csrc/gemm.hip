@@ -62,6 +62,29 @@ __device__ __forceinline__ void put4(T* p, const f32x4& v, int cnt) {
     for (int j = 0; j < cnt; ++j) p[j] = from_f<T>(v[j]);
   }
 }
+// Four consecutive elements as stored (bf16 stays bf16 until used, so a
+// load in flight does not force a wait where it is issued).
+template <typename T>
+struct Raw4 {
+  using type = f32x4;
+};
+template <>
+struct Raw4<bf16> {
+  using type = bf16x4;
+};
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::type get4raw(const T* p, int cnt) {
+  using R = typename Raw4<T>::type;
+  if (cnt == 4) return *reinterpret_cast<const R*>(p);
+  R r{};
+  for (int j = 0; j < cnt; ++j) r[j] = p[j];
+  return r;
+}
+__device__ __forceinline__ f32x4 to_f4(const f32x4& v) { return v; }
+__device__ __forceinline__ f32x4 to_f4(const bf16x4& v) {
+  return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+               static_cast<float>(v[3])};
+}
 template <typename T>
 __device__ __forceinline__ f32x4 get4(const T* p, int cnt) {
   if (cnt == 4) {
@@ -172,9 +195,10 @@ struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {
   const T* H;
   T* C;
   int64_t ldc;
-  using Aux = f32x4;
-  __device__ f32x4 aux(int64_t m, int64_t n, int cnt) const { return get4<T>(H + m * ldc + n, cnt); }
-  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const f32x4& h) const {
+  using Aux = typename Raw4<T>::type;
+  __device__ Aux aux(int64_t m, int64_t n, int cnt) const { return get4raw<T>(H + m * ldc + n, cnt); }
+  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const Aux& hr) const {
+    const f32x4 h = to_f4(hr);
     f32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = 2.0f * sqrt_act<T>(h[j]) * v[j];

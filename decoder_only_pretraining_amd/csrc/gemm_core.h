@@ -248,6 +248,18 @@ struct Deq8 {
   }
 };
 
+// Scheduling groups for a main-loop slice: NR times (n MFMAs, one DS
+// read), n = MP or MP + 1 so that the MFMAs spread evenly over the reads.
+template <int R, int NR, int MP, int REM>
+__device__ __forceinline__ void interleave_mfma_ds() {
+  if constexpr (R < NR) {
+    constexpr int n = MP + (R < REM ? 1 : 0);
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x008, n, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                       // DS read
+    interleave_mfma_ds<R + 1, NR, MP, REM>();
+  }
+}
+
 template <int BM, int BN, int BK, bool AK, bool BKM, int MODE, class PA, class PB, class EP,
           class DQ>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
@@ -379,46 +391,94 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         }
       }
     } else {
-    Frag<bf16> a[2][TM], b[2][TN];
+      // Slice 0 is read in the order its MFMAs consume it (A row 0, the B
+      // columns, then the other A rows), one read at a time, so the first
+      // MFMAs wait for two reads, not eight; the reads of slice ks + 1 are
+      // interleaved with the MFMAs of slice ks.
+      constexpr int KS = BK / 16;
+      constexpr int NR = TM * (AK ? 1 : 2) + TN * (BKM ? 1 : 2);  // DS reads per slice
+      constexpr int NM = TM * TN;
+      Frag<bf16> a[2][TM], b[2][TN];
+      auto read_slice = [&](int q, int ks, auto ordered) {
+        read_frag<BM, BK, AK>(a[q][0], As[cur], wm * (BM / 2), ks, lane);
+        if constexpr (decltype(ordered)::value) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) read_frag<BM, BK, AK>(a[0][i], As[cur], wm * (BM / 2) + i * 32, 0, lane);
+        for (int j = 0; j < TN; ++j) {
+          read_frag<BN, BK, BKM>(b[q][j], Bs[cur], wn * (BN / 2) + j * 32, ks, lane);
+          if constexpr (decltype(ordered)::value) __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) read_frag<BN, BK, BKM>(b[0][j], Bs[cur], wn * (BN / 2) + j * 32, 0, lane);
+        for (int i = 1; i < TM; ++i) {
+          read_frag<BM, BK, AK>(a[q][i], As[cur], wm * (BM / 2) + i * 32, ks, lane);
+          if constexpr (decltype(ordered)::value) __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      read_slice(0, 0, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int p = ks & 1;
-      if (ks + 1 < BK / 16) {
+      for (int ks = 0; ks < KS; ++ks) {
+        const int p = ks & 1;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          read_frag<BM, BK, AK>(a[p ^ 1][i], As[cur], wm * (BM / 2) + i * 32, ks + 1, lane);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          read_frag<BN, BK, BKM>(b[p ^ 1][j], Bs[cur], wn * (BN / 2) + j * 32, ks + 1, lane);
+          for (int j = 0; j < TN; ++j) mfma(acc[i][j], a[p][i], b[p][j]);
+        if (ks + 1 < KS) {
+          read_slice(p ^ 1, ks + 1, std::false_type{});
+          interleave_mfma_ds<0, NR, NM / NR, NM % NR>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch reads ahead of the MFMAs
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) mfma(acc[i][j], a[p][i], b[p][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
     }
     if (more) place(kn, cur ^ 1);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): next stage's direct fills landed
     __syncthreads();
   }
 
+  const int64_t mw = m0 + wm * (BM / 2), nw = n0 + wn * WN;
+  if constexpr (EP::kScalar) {
+    // Scalar (atomic) epilogues write every accumulator straight from its
+    // MFMA layout: for one accumulator index, lanes 0-31 cover 32
+    // consecutive columns of one row and lanes 32-63 the same columns four
+    // rows further, as coalesced as a staged slab and without LDS traffic.
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = mw + i * 32 + acc_row(e, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t n = nw + j * 32 + (lane & 31);
+          float x = acc[i][j][e];
+          if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(n)];
+          if (m < M && n < N) ep.store1(m, n, ep.value(m, n, x));
+        }
+      }
+    return;
+  }
   // Epilogue, one 32-row slab of the wavefront tile at a time: transform
   // the accumulators in their MFMA layout (row sums for the softcap), stage
-  // the slab in LDS as fp32, then write it back with 4-column vectors.
+  // the slab in LDS as fp32, then write it back with 4-column vectors; all
+  // LDS reads of a slab are issued before its first global store.
+  // Epilogues that read another operand (residual, activation, old value)
+  // load it in half-slab chunks, one chunk ahead of its use, so the load
+  // latency overlaps the previous chunk's work.
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SP;
-  const int64_t mw = m0 + wm * (BM / 2), nw = n0 + wn * WN;
-  // Epilogues that read another operand load it in chunks of CH vectors
-  // per lane, all loads of a chunk issued before its stores.
   constexpr bool kAux = !std::is_same<typename EP::Aux, NoAux>::value;
   constexpr int NVS = 32 * WN / 4 / 64;  // 4-column vectors per lane per slab
-  constexpr int CH = NVS % 8 == 0 ? 8 : NVS % 6 == 0 ? 6 : NVS % 4 == 0 ? 4 : NVS;
-  static_assert(NVS % CH == 0, "chunks must tile the slab");
+  constexpr int NCH = 2, CV = NVS / NCH;  // aux chunks per slab, vectors per chunk
+  static_assert(NVS % NCH == 0, "aux chunks must tile the slab");
+  using AuxT = typename EP::Aux;
+  AuxT ax[kAux ? 2 : 1][kAux ? CV : 1];
+  auto load_aux = [&](int i, int c, AuxT* dst) {
+#pragma unroll
+    for (int t = 0; t < CV; ++t) {
+      const int v = lane + 64 * (c * CV + t);
+      const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+      const int64_t m = mw + i * 32 + r, n = nw + c4;
+      if (m < M && n < N) dst[t] = ep.aux(m, n, (int)min<int64_t>(4, N - n));
+    }
+  };
+  if constexpr (kAux) load_aux(0, 0, ax[0]);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -442,45 +502,41 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront
     __builtin_amdgcn_wave_barrier();
-    if constexpr (EP::kScalar) {
-      // one column per lane: consecutive lanes hit consecutive addresses
+    if constexpr (kAux) {
 #pragma unroll
-      for (int v = lane; v < 32 * WN; v += 64) {
-        const int r = v / WN, cc = v % WN;
-        const int64_t m = mw + i * 32 + r, n = nw + cc;
-        if (m < M && n < N) ep.store1(m, n, stage[r * SP + cc]);
-      }
-    } else if constexpr (kAux) {
+      for (int c = 0; c < NCH; ++c) {
+        const int g = i * NCH + c;  // chunk number within the tile
+        if (c + 1 < NCH) load_aux(i, c + 1, ax[(g + 1) & 1]);
+        else if (i + 1 < TM) load_aux(i + 1, 0, ax[(g + 1) & 1]);
+        f32x4 val[CV];
 #pragma unroll
-      for (int c = 0; c < NVS; c += CH) {
-        typename EP::Aux ax[CH];
-#pragma unroll
-        for (int t = 0; t < CH; ++t) {
-          const int v = lane + 64 * (c + t);
+        for (int t = 0; t < CV; ++t) {
+          const int v = lane + 64 * (c * CV + t);
           const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
-          const int64_t m = mw + i * 32 + r, n = nw + c4;
-          if (m < M && n < N) ax[t] = ep.aux(m, n, (int)min<int64_t>(4, N - n));
+          val[t] = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
         }
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-          const int v = lane + 64 * (c + t);
+        for (int t = 0; t < CV; ++t) {
+          const int v = lane + 64 * (c * CV + t);
           const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
           const int64_t m = mw + i * 32 + r, n = nw + c4;
-          if (m < M && n < N) {
-            const f32x4 val = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
-            ep.store4a(m, n, val, (int)min<int64_t>(4, N - n), ax[t]);
-          }
+          if (m < M && n < N) ep.store4a(m, n, val[t], (int)min<int64_t>(4, N - n), ax[g & 1][t]);
         }
       }
     } else {
+      f32x4 val[NVS];
 #pragma unroll
-      for (int v = lane; v < 32 * WN / 4; v += 64) {
+      for (int t = 0; t < NVS; ++t) {
+        const int v = lane + 64 * t;
+        const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+        val[t] = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
+      }
+#pragma unroll
+      for (int t = 0; t < NVS; ++t) {
+        const int v = lane + 64 * t;
         const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
         const int64_t m = mw + i * 32 + r, n = nw + c4;
-        if (m < M && n < N) {
-          const f32x4 val = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
-          ep.store4(m, n, val, (int)min<int64_t>(4, N - n));
-        }
+        if (m < M && n < N) ep.store4(m, n, val[t], (int)min<int64_t>(4, N - n));
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
