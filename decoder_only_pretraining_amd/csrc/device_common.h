@@ -32,12 +32,6 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
-// Sum over the 32 lanes of each half-wavefront (lanes 0-31 and 32-63).
-__device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 
 // ---------------------------------------------------------------------------
 // MFMA fragments. A 32x32 output tile is accumulated over 16-wide slices of

@@ -41,7 +41,6 @@ struct PreRelu2 {  // ReLU^2 of the MLP hidden pre-activation
 };
 // ------------------------------------------------------------ epilogues
 // value(m, n, acc): per-element transform in the accumulator layout;
-// rowterm(value): the row-sum contribution (kRowSum epilogues only);
 // store4(m, n, v, cnt): write columns n .. n+cnt-1 of row m (cnt <= 4).
 // Epilogues that read another operand split the write into aux(m, n, cnt),
 // the load, and store4a(m, n, v, cnt, aux): the tiled kernel issues all
@@ -111,20 +110,16 @@ __device__ __forceinline__ float sqrt_act(float x) {
 
 template <class Derived>
 struct EpBase {
-  static constexpr bool kRowSum = false;
   static constexpr bool kScalar = false;  // store1 with one column per lane
   using Aux = NoAux;
   __device__ float value(int64_t, int64_t, float v) const { return v; }
-  __device__ float rowterm(float) const { return 0.0f; }
   __device__ NoAux aux(int64_t, int64_t, int) const { return {}; }
   __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const NoAux&) const {
     static_cast<const Derived&>(*this).store4(m, n, v, cnt);
   }
-  __device__ float operator()(int64_t m, int64_t n, float acc) const {
+  __device__ void operator()(int64_t m, int64_t n, float acc) const {
     const Derived& d = static_cast<const Derived&>(*this);
-    const float v = d.value(m, n, acc);
-    d.store4(m, n, f32x4{v, 0, 0, 0}, 1);
-    return Derived::kRowSum ? d.rowterm(v) : 0.0f;
+    d.store4(m, n, f32x4{d.value(m, n, acc), 0, 0, 0}, 1);
   }
 };
 
@@ -209,25 +204,22 @@ struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {
   }
 };
 template <typename T>
-struct EpSoftcap : EpBase<EpSoftcap<T>> {  // c = cap * tanh(z / cap); row sums of exp(c - cap)
-  static constexpr bool kRowSum = true;
+struct EpSoftcap : EpBase<EpSoftcap<T>> {  // c = cap * tanh(z / cap)
   T* C;
   int64_t ldc;
   float cap;
   float k2;  // 2 log2(e) / cap
-  // the stored (rounded) value, so the row sums match what the backward reads
   __device__ float value(int64_t, int64_t, float z) const {
     if constexpr (sizeof(T) == 2) {
       // tanh(u) = 1 - 2 / (1 + e^(2u)) with the hardware exp2 and reciprocal
       // (about 1 ulp each): the absolute error of c, ~cap * 2^-23, is far
       // below the bf16 step of the stored value; saturates to +-cap
       const float e = __builtin_amdgcn_exp2f(z * k2);
-      return to_f(from_f<T>(cap - (2.0f * cap) * __builtin_amdgcn_rcpf(1.0f + e)));
+      return cap - (2.0f * cap) * __builtin_amdgcn_rcpf(1.0f + e);
     } else {
       return cap * tanhf(z / cap);
     }
   }
-  __device__ float rowterm(float c) const { return __expf(c - cap); }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
     put4<T>(C + m * ldc + n, v, cnt);
   }
@@ -360,7 +352,7 @@ template <typename T, int BM, int BN, int BK, bool AK, bool BKM, class PA, class
 __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int64_t lda,
                                                    const T* __restrict__ B, int64_t ldb,
                                                    int64_t M, int64_t N, int64_t K, PA pa,
-                                                   PB pb, EP ep, float* rowpart) {
+                                                   PB pb, EP ep) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int LDK = BK + VEC;
   constexpr int TM = BM / 64, TN = BN / 64;
@@ -427,15 +419,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int64_t m = m0 + wm * (BM / 2) + i * 32 + acc_row(e, lane);
-      float rs = 0.0f;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int64_t n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-        if (m < M && n < N) rs += ep(m, n, acc[i][j][e]);
-      }
-      if (EP::kRowSum) {
-        rs = half_sum(rs);
-        if ((lane & 31) == 0 && m < M) rowpart[m * (2 * gridDim.x) + blockIdx.x * 2 + wn] = rs;
+        if (m < M && n < N) ep(m, n, acc[i][j][e]);
       }
     }
   }
@@ -443,12 +430,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
 
 template <typename T, bool AK, bool BKM, class PA, class PB, class EP>
 void run_f32(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
-             int64_t K, PA pa, PB pb, EP ep, float* rowpart, hipStream_t s) {
+             int64_t K, PA pa, PB pb, EP ep, hipStream_t s) {
   constexpr int BM = 128, BN = 128, BK = 16;
   dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
                      static_cast<const T*>(A), lda, static_cast<const T*>(B), ldb, M, N, K, pa,
-                     pb, ep, rowpart);
+                     pb, ep);
 }
 
 // ------------------------------------------------------------ bf16 dispatch
@@ -457,9 +444,14 @@ struct Tile {
 };
 
 // Output tile for a product: the largest tile that still gives the 256 CUs
-// at least one full wave of workgroups.
-static Tile pick_tile(int64_t M, int64_t N) {
+// at least one full wave of workgroups. Short contractions (K <= 1024) with
+// 4 to 32 waves of 128 x 128 tiles take those instead: two such workgroups
+// share a CU, so one's epilogue overlaps the other's main loop (measured on
+// the d12 products with K = 768; the lm_head, with far more tiles, keeps
+// the larger tile).
+static Tile pick_tile(int64_t M, int64_t N, int64_t K) {
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (K <= 1024 && tiles(128, 128) >= 1024 && tiles(128, 128) <= 8192) return {128, 128};
   if (N % 256 == 0 && tiles(256, 256) >= 512) return {256, 256};
   if (N % 192 == 0 && tiles(256, 192) >= 256) return {256, 192};
   if (tiles(256, 128) >= 256) return {256, 128};
@@ -487,26 +479,26 @@ static int64_t pick_kchunk(int64_t tiles, int64_t K, int64_t min_chunk = 512) {
 
 template <int BM, int BN, bool AK, bool BKM, class PA, class PB, class EP>
 void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
-                 int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, float* rowsum, hipStream_t s) {
+                 int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const int splits = (int)((K + kchunk - 1) / kchunk);
   dim3 grid((unsigned)(tm * tn * std::max(splits, 1)));
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq>), grid, dim3(256),
                      0, s, static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M,
-                     N, K, kchunk, tm, tn, pa, pb, ep, rowsum, NoDeq{});
+                     N, K, kchunk, tm, tn, pa, pb, ep, NoDeq{});
 }
 
 template <bool AK, bool BKM, class PA, class PB, class EP>
 void run_bf16(Tile t, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
-              int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, float* rowsum, hipStream_t s) {
+              int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s) {
   if (t.bm == 256 && t.bn == 256)
-    launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
+    launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
   else if (t.bm == 256 && t.bn == 192)
-    launch_bf16<256, 192, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
+    launch_bf16<256, 192, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
   else if (t.bm == 256 && t.bn == 128)
-    launch_bf16<256, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
+    launch_bf16<256, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
   else
-    launch_bf16<128, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, rowsum, s);
+    launch_bf16<128, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
 }
 
 // ------------------------------------------------------------ fp8 dispatch
@@ -522,7 +514,7 @@ void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, true, true, MODE, PreId, PreId, EP, Deq8>), grid,
                      dim3(256), 0, s, reinterpret_cast<const bf16*>(A), lda / 2,
                      reinterpret_cast<const bf16*>(B), ldb / 2, M, N, Kp, kc, tm, tn, PreId{},
-                     PreId{}, ep, nullptr, dq);
+                     PreId{}, ep, dq);
 }
 
 template <int MODE, class EP>
@@ -569,7 +561,7 @@ static Deq8 to_deq(const Fp8Deq& q) {
 
 void gemm8_store(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                  const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s) {
-  const Tile t = pick_tile(M, N);
+  const Tile t = pick_tile(M, N, K);
   const Deq8 q = to_deq(dq);
   GPT_F8_DISPATCH(dq, (run_f8<1>(t, A, lda, B, ldb, M, N, K, K, mk_store<bf16>(C, N), q, s)),
                   (run_f8<2>(t, A, lda, B, ldb, M, N, K, K, mk_store<bf16>(C, N), q, s)));
@@ -578,25 +570,25 @@ void gemm8_store(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
 void gemm8_resid(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                  const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const float* R, float* C,
                  hipStream_t s) {
-  run_f8<1>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_resid(R, C, N), to_deq(dq), s);
+  run_f8<1>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_resid(R, C, N), to_deq(dq), s);
 }
 
 void gemm8_relu2(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                  const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s) {
-  run_f8<1>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_relu2<bf16>(C, N), to_deq(dq), s);
+  run_f8<1>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_relu2<bf16>(C, N), to_deq(dq), s);
 }
 
 void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                     const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const void* H, void* C,
                     hipStream_t s) {
-  run_f8<2>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_relu2bwd<bf16>(H, C, N), to_deq(dq),
+  run_f8<2>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_relu2bwd<bf16>(H, C, N), to_deq(dq),
             s);
 }
 
 void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
                hipStream_t s) {
-  run_f8<2>(pick_tile(M, N), A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0),
+  run_f8<2>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0),
             to_deq(dq), s);
 }
 
@@ -618,95 +610,85 @@ void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, true>(pick_tile(M, N), A, K, B, K, M, N, K, K, PreId{}, PreId{},
-                         mk_store<bf16>(C, N), nullptr, s);
+    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_store<bf16>(C, N), s);
   else
     run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
-                               mk_store<float>(C, N), nullptr, s);
+                               mk_store<float>(C, N), s);
 }
 
 void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    const float* R, float* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, true>(pick_tile(M, N), A, K, B, K, M, N, K, K, PreId{}, PreId{},
-                         mk_resid(R, C, N), nullptr, s);
+    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_resid(R, C, N), s);
   else
-    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_resid(R, C, N), nullptr,
-                               s);
+    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_resid(R, C, N), s);
 }
 
 void gemm_nt_relu2(const Dims& d, int64_t M, int N, int K, const void* A, const void* B, void* C,
                    hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, true>(pick_tile(M, N), A, K, B, K, M, N, K, K, PreId{}, PreId{},
-                         mk_relu2<bf16>(C, N), nullptr, s);
+    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_relu2<bf16>(C, N), s);
   else
-    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_relu2<float>(C, N),
-                               nullptr, s);
+    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_relu2<float>(C, N), s);
 }
 
-int gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                    void* C, float* rowpart, hipStream_t s) {
-  if (d.bf16) {
-    const Tile t = pick_tile(M, N);
-    run_bf16<true, true>(t, A, K, B, K, M, N, K, K, PreId{}, PreId{},
-                         mk_softcap<bf16>(C, N, d.cap), rowpart, s);
-    return 2 * (int)((N + t.bn - 1) / t.bn);
-  }
-  run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
-                             mk_softcap<float>(C, N, d.cap), rowpart, s);
-  return 2 * (int)((N + 127) / 128);
+void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                     void* C, hipStream_t s) {
+  if (d.bf16)
+    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+                         mk_softcap<bf16>(C, N, d.cap), s);
+  else
+    run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
+                               mk_softcap<float>(C, N, d.cap), s);
 }
 
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, false>(pick_tile(M, N), A, K, B, N, M, N, K, K, PreId{}, PreId{},
-                          mk_store<bf16>(C, N), nullptr, s);
+    run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+                          mk_store<bf16>(C, N), s);
   else
     run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{},
-                                mk_store<float>(C, N), nullptr, s);
+                                mk_store<float>(C, N), s);
 }
 
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                  float* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, false>(pick_tile(M, N), A, K, B, N, M, N, K, K, PreId{}, PreId{},
-                          mk_f32(C, N, 0), nullptr, s);
+    run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+                          mk_f32(C, N, 0), s);
   else
-    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), nullptr,
-                                s);
+    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
 }
 
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                       const void* U, void* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, false>(pick_tile(M, N), A, K, B, N, M, N, K, K, PreId{}, PreId{},
-                          mk_relu2bwd<bf16>(U, C, N),
-                          nullptr, s);
+    run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+                          mk_relu2bwd<bf16>(U, C, N), s);
   else
     run_f32<float, true, false>(
         A, K, B, N, M, N, K, PreId{}, PreId{},
-        mk_relu2bwd<float>(U, C, N), nullptr, s);
+        mk_relu2bwd<float>(U, C, N), s);
 }
 
 void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                         float* C, hipStream_t s) {
   if (d.bf16) {
-    const Tile t = pick_tile(M, N);
+    const Tile t = pick_tile(M, N, K);
     const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
     const int64_t kc = pick_kchunk(tiles, K, 4096);
     if (kc >= K) {
-      run_bf16<true, false>(t, A, K, B, N, M, N, K, K, PreId{}, PreId{}, mk_f32(C, N, 0), nullptr,
-                            s);
+      run_bf16<true, false>(t, A, K, B, N, M, N, K, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
       return;
     }
     launch_zero(C, M * N, s);
-    run_bf16<true, false>(t, A, K, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), nullptr,
-                          s);
+    run_bf16<true, false>(t, A, K, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), s);
   } else {
-    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), nullptr,
-                                s);
+    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
   }
 }
 
@@ -718,15 +700,14 @@ void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const 
     const int64_t kc = pick_kchunk(tiles, K);
     if (kc >= K) {  // one split: plain (accumulating) stores
       run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{},
-                             mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
+                             mk_f32(C, N, accumulate ? 1 : 0), s);
       return;
     }
     if (!accumulate) launch_zero(C, (int64_t)M * N, s);
-    run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), nullptr,
-                           s);
+    run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), s);
   } else {
     run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
-                                 mk_f32(C, N, accumulate ? 1 : 0), nullptr, s);
+                                 mk_f32(C, N, accumulate ? 1 : 0), s);
   }
 }
 

@@ -265,7 +265,7 @@ template <int BM, int BN, int BK, bool AK, bool BKM, int MODE, class PA, class P
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep,
-    float* rowpart, DQ dq) {
+    DQ dq) {
   static_assert(!PA::kActive && !PB::kActive, "direct LDS loads take operands as stored");
   constexpr bool F8 = MODE != 0;
   static_assert(!F8 || (AK && BKM), "fp8 products take K-major operands");
@@ -456,9 +456,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     return;
   }
   // Epilogue, one 32-row slab of the wavefront tile at a time: transform
-  // the accumulators in their MFMA layout (row sums for the softcap), stage
-  // the slab in LDS as fp32, then write it back with 4-column vectors; all
-  // LDS reads of a slab are issued before its first global store.
+  // the accumulators in their MFMA layout, stage the slab in LDS as fp32,
+  // then write it back with 4-column vectors; all LDS reads of a slab are
+  // issued before its first global store.
   // Epilogues that read another operand (residual, activation, old value)
   // load it in half-slab chunks, one chunk ahead of its use, so the load
   // latency overlaps the previous chunk's work.
@@ -485,19 +485,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     for (int e = 0; e < 16; ++e) {
       const int r = acc_row(e, lane);
       const int64_t m = mw + i * 32 + r;
-      float rs = 0.0f;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int64_t n = nw + j * 32 + (lane & 31);
         float x = acc[i][j][e];
         if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(n)];
-        const float v = ep.value(m, n, x);
-        if (EP::kRowSum && m < M && n < N) rs += ep.rowterm(v);
-        stage[r * SP + j * 32 + (lane & 31)] = v;
-      }
-      if (EP::kRowSum) {  // deterministic per-(tile, wavefront column) partials
-        rs = half_sum(rs);
-        if ((lane & 31) == 0 && m < M) rowpart[m * (2 * tiles_n) + tn * 2 + wn] = rs;
+        stage[r * SP + j * 32 + (lane & 31)] = ep.value(m, n, x);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront

@@ -221,8 +221,6 @@ Plan make_plan(const Dims& d) {
   p.xf = take(N * d.C * A);
   p.rf = take(N * 4);
   p.logits = take(N * d.V * A);
-  p.rowparts = d.V / 64;  // two partials per column tile of >= 128
-  p.rowpart = take(N * p.rowparts * 4);
   p.lossrow = take(N * 4);
   p.scalars = take(256);
   p.gx = take(N * d.C * 4);
@@ -487,15 +485,13 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   void* xf = W + P.xf;
   float* rf = reinterpret_cast<float*>(W + P.rf);
   void* logits = W + P.logits;
-  float* rowpart = reinterpret_cast<float*>(W + P.rowpart);
   float* lossrow = reinterpret_cast<float*>(W + P.lossrow);
   float* scalars = reinterpret_cast<float*>(W + P.scalars);
   launch_mix_norm(d, X(d.L), nullptr, nullptr, nullptr, nullptr, xf, rf, nullptr, nullptr, s);
-  int nparts = 0;
   launch_count_valid(d, targets, scalars, s);
-  site("gemm.lm.fwd", s, [&] { nparts = gemm_nt_softcap(d, N, d.V, d.C, xf, wmat(F.lm), logits, rowpart, s); });
+  site("gemm.lm.fwd", s, [&] { gemm_nt_softcap(d, N, d.V, d.C, xf, wmat(F.lm), logits, s); });
   // the loss; in a backward call the logits become the logit gradient g_z
-  site("loss", s, [&] { launch_loss(d, logits, targets, rowpart, nparts, scalars, lossrow, loss, backward, s); });
+  site("loss", s, [&] { launch_loss(d, logits, targets, scalars, lossrow, loss, backward, s); });
 
   if (backward) {
     const bool acc = d.accumulate;
@@ -727,8 +723,8 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
   const R global[] = {
       {"wc", P.wc, d.bf16 ? (P.rope - P.wc) : 0}, {"rope", P.rope, (size_t)d.T * d.D * 4},
       {"xin", P.xin, N * C * 4}, {"xf", P.xf, N * C * A}, {"rf", P.rf, N * 4},
-      {"logits", P.logits, N * d.V * A}, {"rowpart", P.rowpart, N * P.rowparts * 4},
-{"lossrow", P.lossrow, N * 4}, {"scalars", P.scalars, 256},
+      {"logits", P.logits, N * d.V * A}, {"lossrow", P.lossrow, N * 4},
+      {"scalars", P.scalars, 256},
       {"gx", P.gx, N * C * 4}, {"gxc", P.gxc, N * C * A}, {"gx0", P.gx0, N * C * 4},
       {"gu", P.gu, N * d.F * A}, {"gtmp", P.gtmp, N * C * 4}, {"gO", P.gO, N * d.Cq * A},
       {"gqkv", P.gqkv, N * d.Qkv * A}, {"delta", P.delta, N * d.H * 4},

@@ -43,8 +43,7 @@ struct Plan {
   // per layer, stride `layer_bytes`, starting at `layers`
   size_t layers, layer_bytes;
   size_t l_xn, l_r1, l_qkv, l_rqk, l_a, l_attn, l_lse, l_xmid, l_xn2, l_r2, l_u;
-  size_t xf, rf, logits, rowpart, lossrow, scalars;
-  int rowparts;         // max row-sum partials per token
+  size_t xf, rf, logits, lossrow, scalars;
   size_t gx, gxc, gx0, gu, gtmp, gO, gqkv, delta, ga, lam_part, veg_part;
   int lam_blocks, veg_splits;
   // fp8 linears only (0 bytes otherwise). Token-major code tensors that the
@@ -123,12 +122,11 @@ void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* par
                       int splits, float* gwg, hipStream_t s);
 // 1 / n_valid into scalars[0].
 void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipStream_t s);
-// Softcap cross-entropy loss from the stored logits and the per-tile row sums
-// of exp(c - cap) (nparts per token, summed in a fixed order); with `grad`
-// the logits are overwritten in place by the logit gradient of the mean loss.
-void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* rowpart,
-                 int nparts, const float* scalars, float* lossrow, float* loss, bool grad,
-                 hipStream_t s);
+// Softcap cross-entropy loss from the stored softcapped logits (row sums of
+// exp(c - cap) in a fixed order, one workgroup per token); with `grad` the
+// logits are overwritten in place by the logit gradient of the mean loss.
+void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* scalars,
+                 float* lossrow, float* loss, bool grad, hipStream_t s);
 void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t N, int C,
                       hipStream_t s);
 
@@ -144,10 +142,9 @@ void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const 
 // C = relu(A B^T)^2 (the MLP hidden activation)
 void gemm_nt_relu2(const Dims& d, int64_t M, int N, int K, const void* A, const void* B, void* C,
                    hipStream_t s);
-// Softcapped logits; row sums of exp(c - cap) as per-tile partials
-// rowpart[m * P + j], j < P; returns P.
-int gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                    void* C, float* rowpart, hipStream_t s);
+// Softcapped logits c = cap * tanh(A B^T / cap), stored in the activation type.
+void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
+                     void* C, hipStream_t s);
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s);
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,

@@ -429,60 +429,88 @@ __global__ __launch_bounds__(1024) void count_valid_kernel(const int32_t* __rest
   if (threadIdx.x == 0) scalars[0] = 1.0f / (float)(s_cnt[0] > 0 ? s_cnt[0] : 1);
 }
 
-// One wavefront per token. rowsum = fixed-order sum of the per-tile
-// partials of exp(c - cap); loss_n = cap + log(rowsum) - c[y] (0 if
-// ignored). With `grad`, the token's softcapped logits are then replaced in
-// place by the gradient of the mean loss w.r.t. the raw logits z:
+// One workgroup per token. Its softcapped logits c (|c| <= cap) are read
+// once: rowsum = sum_v exp(c_v - cap) in a fixed order (per-thread sums,
+// then the four wavefronts'), loss_n = cap + log(rowsum) - c[y] (0 if
+// ignored). With `grad`, the row is then replaced in place by the gradient
+// of the mean loss w.r.t. the raw logits z:
 //   (exp(c - cap) / rowsum - [v == y]) * (1 - (c / cap)^2) / n_valid.
 // |c| <= cap, so exp(c - cap) in [e^(-2 cap), 1] needs no running maximum.
+// The first RC 16-byte vectors per thread stay in registers between the
+// two passes; the rest of a longer row is read again.
 template <typename T>
+struct Vec16;
+template <>
+struct Vec16<bf16> {
+  using type = bf16x8;
+  static constexpr int n = 8;
+};
+template <>
+struct Vec16<float> {
+  using type = f32x4;
+  static constexpr int n = 4;
+};
+
+template <typename T, int RC>
 __global__ __launch_bounds__(256) void ce_rows_kernel(T* __restrict__ logits,
                                                       const int32_t* __restrict__ tgt,
-                                                      const float* __restrict__ part, int nparts,
                                                       const float* __restrict__ scalars,
-                                                      float* __restrict__ lossrow, int64_t N, int V,
-                                                      float cap, int grad) {
-  const int lane = threadIdx.x & 63;
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  float s = 0.0f;
-  for (int j = lane; j < nparts; j += 64) s += part[n * nparts + j];
-  s = wave_sum(s);
-  const int y = tgt[n];
+                                                      float* __restrict__ lossrow, int V, float cap,
+                                                      int grad) {
+  using VT = typename Vec16<T>::type;
+  constexpr int VEC = Vec16<T>::n;
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t n = blockIdx.x;
   T* row = logits + n * V;
-  float cy = 0.0f;
-  if (y >= 0) cy = to_f(row[y]);
-  if (lane == 0) lossrow[n] = y >= 0 ? cap + logf(s) - cy : 0.0f;
-  if (!grad) return;
-  const float inv = 1.0f / s, inv_nv = scalars[0], icap = 1.0f / cap;
-  constexpr int VEC = 16 / sizeof(T);
-  for (int v0 = lane * VEC; v0 < V; v0 += 64 * VEC) {
-    Frag<T> f;
-    frag_load(f, row + v0);  // 16 bytes
-    float e[VEC];
-    if constexpr (sizeof(T) == 2) {
+  const int nvec = V / VEC;
+  const int y = tgt[n];
+  const float cy = y >= 0 ? static_cast<float>(row[y]) : 0.0f;  // read before the row is rewritten
+  VT c[RC];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) e[j] = static_cast<float>(f.v[j]);
-    } else {
+  for (int r = 0; r < RC; ++r) {
+    const int v = tid + r * 256;
+    if (v < nvec) c[r] = reinterpret_cast<const VT*>(row)[v];
+  }
+  float s = 0.0f;
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) e[j] = f.lo[j];
-    }
+  for (int r = 0; r < RC; ++r) {
+    const int v = tid + r * 256;
+    if (v < nvec) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      const float c = e[j];
-      float p = y >= 0 ? __expf(c - cap) * inv : 0.0f;
-      if (v0 + j == y) p -= 1.0f;
-      const float q = c * icap;
-      e[j] = p * (1.0f - q * q) * inv_nv;
-    }
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) f.v[j] = static_cast<bf16>(e[j]);
-      *reinterpret_cast<bf16x8*>(row + v0) = f.v;
-    } else {
-      *reinterpret_cast<f32x4*>(row + v0) = f32x4{e[0], e[1], e[2], e[3]};
+      for (int j = 0; j < VEC; ++j) s += __expf(static_cast<float>(c[r][j]) - cap);
     }
   }
+  for (int v = tid + RC * 256; v < nvec; v += 256) {
+    const VT x = reinterpret_cast<const VT*>(row)[v];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) s += __expf(static_cast<float>(x[j]) - cap);
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[wv] = s;
+  __syncthreads();
+  s = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) lossrow[n] = y >= 0 ? cap + logf(s) - cy : 0.0f;
+  if (!grad) return;
+  const float inv = y >= 0 ? 1.0f / s : 0.0f, inv_nv = scalars[0], icap = 1.0f / cap;
+  auto gradv = [&](VT x, int v) {
+    VT o;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float cv = static_cast<float>(x[j]);
+      float p = __expf(cv - cap) * inv;
+      if (v * VEC + j == y) p -= 1.0f;
+      const float q = cv * icap;
+      o[j] = static_cast<T>(p * (1.0f - q * q) * inv_nv);
+    }
+    reinterpret_cast<VT*>(row)[v] = o;
+  };
+#pragma unroll
+  for (int r = 0; r < RC; ++r) {
+    const int v = tid + r * 256;
+    if (v < nvec) gradv(c[r], v);
+  }
+  for (int v = tid + RC * 256; v < nvec; v += 256) gradv(reinterpret_cast<const VT*>(row)[v], v);
 }
 
 // Mean over valid tokens: fixed-order reduction in double.
@@ -654,16 +682,14 @@ void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipSt
   hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(1024), 0, s, tgt, scalars, d.N);
 }
 
-void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* rowpart,
-                 int nparts, const float* scalars, float* lossrow, float* loss, bool grad,
-                 hipStream_t s) {
-  dim3 grid((unsigned)((d.N + 3) / 4));
+void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* scalars,
+                 float* lossrow, float* loss, bool grad, hipStream_t s) {
   if (d.bf16)
-    hipLaunchKernelGGL(ce_rows_kernel<bf16>, grid, dim3(256), 0, s, static_cast<bf16*>(logits),
-                       tgt, rowpart, nparts, scalars, lossrow, d.N, d.V, d.cap, grad ? 1 : 0);
+    hipLaunchKernelGGL((ce_rows_kernel<bf16, 16>), dim3((unsigned)d.N), dim3(256), 0, s,
+                       static_cast<bf16*>(logits), tgt, scalars, lossrow, d.V, d.cap, grad ? 1 : 0);
   else
-    hipLaunchKernelGGL(ce_rows_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(logits),
-                       tgt, rowpart, nparts, scalars, lossrow, d.N, d.V, d.cap, grad ? 1 : 0);
+    hipLaunchKernelGGL((ce_rows_kernel<float, 16>), dim3((unsigned)d.N), dim3(256), 0, s,
+                       static_cast<float*>(logits), tgt, scalars, lossrow, d.V, d.cap, grad ? 1 : 0);
   hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, lossrow, scalars, loss, d.N);
 }
 
