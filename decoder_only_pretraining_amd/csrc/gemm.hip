@@ -13,6 +13,8 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 
 namespace gk {
 
@@ -42,6 +44,7 @@ struct PreRelu2 {  // ReLU^2 of the MLP hidden pre-activation
 // ------------------------------------------------------------ epilogues
 // value(m, n, acc): per-element transform in the accumulator layout;
 // store4(m, n, v, cnt): write columns n .. n+cnt-1 of row m (cnt <= 4).
+// at_split(s): the epilogue of K split s (split-K partials).
 // Epilogues that read another operand split the write into aux(m, n, cnt),
 // the load, and store4a(m, n, v, cnt, aux): the tiled kernel issues all
 // loads of a slab before any store, so their latencies overlap.
@@ -110,8 +113,9 @@ __device__ __forceinline__ float sqrt_act(float x) {
 
 template <class Derived>
 struct EpBase {
-  static constexpr bool kScalar = false;  // store1 with one column per lane
   using Aux = NoAux;
+  // the epilogue of K split `split` (all splits write the same C by default)
+  __device__ Derived at_split(int) const { return static_cast<const Derived&>(*this); }
   __device__ float value(int64_t, int64_t, float v) const { return v; }
   __device__ NoAux aux(int64_t, int64_t, int) const { return {}; }
   __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const NoAux&) const {
@@ -146,13 +150,17 @@ struct EpF32 : EpBase<EpF32> {
     store4a(m, n, v, cnt, aux(m, n, cnt));
   }
 };
-struct EpAtomic : EpBase<EpAtomic> {  // C += acc with fp32 atomics (split-K partial sums)
-  static constexpr bool kScalar = true;
+struct EpPart : EpBase<EpPart> {  // split-K partials: split s writes C + s * stride
   float* C;
   int64_t ldc;
-  __device__ void store1(int64_t m, int64_t n, float v) const { atomicAdd(C + m * ldc + n, v); }
+  int64_t stride;
+  __device__ EpPart at_split(int split) const {
+    EpPart e = *this;
+    e.C += (int64_t)split * stride;
+    return e;
+  }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
-    for (int j = 0; j < cnt; ++j) store1(m, n + j, v[j]);
+    put4<float>(C + m * ldc + n, v, cnt);
   }
 };
 struct EpResid : EpBase<EpResid> {  // C = R + acc (residual stream, fp32)
@@ -239,10 +247,11 @@ inline EpF32 mk_f32(float* C, int64_t ld, int acc) {
   e.accumulate = acc;
   return e;
 }
-inline EpAtomic mk_atomic(float* C, int64_t ld) {
-  EpAtomic e;
-  e.C = C;
-  e.ldc = ld;
+inline EpPart mk_part(float* part, int64_t M, int64_t N) {
+  EpPart e;
+  e.C = part;
+  e.ldc = N;
+  e.stride = M * N;
   return e;
 }
 inline EpResid mk_resid(const float* R, float* C, int64_t ld) {
@@ -458,23 +467,84 @@ static Tile pick_tile(int64_t M, int64_t N, int64_t K) {
   return {128, 128};
 }
 
-// Tile for a weight gradient (split-K fills the machine instead).
+// Tile for a weight gradient. With a full wave of 256 x 256 tiles or more
+// the product runs unsplit and the tile with the fewest tile-area x waves
+// wins (the lm_head gradient: 2 waves of 256 x 192 beat 1.5 of 256 x 256).
+// Otherwise split-K fills the machine: 256 x 256 where the shape has at
+// least 16 of them, else 256 x 192 / 256 x 128 with as many, else 128 x 128
+// (measured on the d12 weight gradients with the partial-sum split-K below).
 static Tile pick_tile_wgrad(int64_t M, int64_t N) {
-  if (N % 192 == 0) return {256, 192};
-  if (N % 256 == 0 && M % 256 == 0) return {256, 256};
-  return {256, 128};
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(256, 256) >= 256) {
+    const Tile cand[3] = {{256, 256}, {256, 192}, {256, 128}};
+    Tile best = cand[0];
+    int64_t best_cost = -1;
+    for (const Tile& t : cand) {
+      if (N % t.bn != 0) continue;
+      const int64_t cost = (tiles(t.bm, t.bn) + 255) / 256 * t.bm * t.bn;
+      if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;
+    }
+    return best;
+  }
+  if (M % 256 == 0 && N % 256 == 0 && tiles(256, 256) >= 16) return {256, 256};
+  if (N % 192 == 0 && tiles(256, 192) >= 16) return {256, 192};
+  if (tiles(256, 128) >= 16) return {256, 128};
+  return {128, 128};
 }
 
-// K split for about one workgroup per CU (256): every extra split adds a
-// full pass of fp32 atomics over C, which costs more than the idle CUs of a
-// partly filled wave (measured on the d12 weight gradients). Chunks are
-// multiples of 64 and at least `min_chunk`.
-static int64_t pick_kchunk(int64_t tiles, int64_t K, int64_t min_chunk = 512) {
-  int64_t splits = std::max<int64_t>(1, (256 + tiles / 2) / tiles);
-  int64_t chunk = (K + splits - 1) / splits;
-  chunk = std::max<int64_t>(chunk, min_chunk);
-  chunk = (chunk + 63) / 64 * 64;
-  return std::min<int64_t>(chunk, (K + 63) / 64 * 64);
+// ------------------------------------------------------------ split-K
+// Long contractions over few output tiles are split along K for about one
+// workgroup per CU (256; two for 128 x 128 tiles, which fit two to a CU).
+// Each split writes its own fp32 partial of C and
+// splitk_reduce_kernel adds the partials in split order, so the result does
+// not depend on the order the workgroups run in. Chunks are multiples of
+// `unit` and at least `min_chunk` long.
+struct KSplit {
+  int64_t chunk, splits;
+};
+static KSplit plan_split(int64_t tiles, int64_t K, int64_t unit, int64_t min_chunk,
+                         int64_t target = 256) {
+  const int64_t want = std::max<int64_t>(1, (target + tiles / 2) / tiles);
+  int64_t chunk = std::max<int64_t>((K + want - 1) / want, min_chunk);
+  chunk = std::min<int64_t>((chunk + unit - 1) / unit * unit, (K + unit - 1) / unit * unit);
+  return {chunk, (K + chunk - 1) / chunk};
+}
+static int64_t tile_count(Tile t, int64_t M, int64_t N) {
+  return ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+}
+
+// C (+)= sum over s of part[s], s ascending; n4 = M * N / 4 vectors.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int64_t splits, int64_t n4,
+                                                            float* __restrict__ C,
+                                                            int accumulate) {
+  const f32x4* P = reinterpret_cast<const f32x4*>(part);
+  f32x4* Cv = reinterpret_cast<f32x4*>(C);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * 256) {
+    f32x4 v = accumulate ? Cv[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int64_t sp = 0; sp < splits; ++sp) v += P[sp * n4 + i];
+    Cv[i] = v;
+  }
+}
+
+static void splitk_reduce(const float* part, int64_t splits, int64_t M, int64_t N, float* C,
+                          bool accumulate, hipStream_t s) {
+  const int64_t n4 = M * N / 4;  // N is a multiple of 64
+  const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, splits, n4, C,
+                     accumulate ? 1 : 0);
+}
+
+// The partial region is sized by the plan from the *_part_bytes functions;
+// a call that needs more is a planning bug.
+static void check_part(int64_t need, int64_t cap) {
+  if (need > cap) {
+    std::fprintf(stderr, "gptstep: split-K partials need %lld bytes, plan holds %lld\n",
+                 (long long)need, (long long)cap);
+    std::abort();
+  }
 }
 
 template <int BM, int BN, bool AK, bool BKM, class PA, class PB, class EP>
@@ -592,19 +662,29 @@ void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
             to_deq(dq), s);
 }
 
+static int64_t wgrad_target(Tile t) { return t.bm == 128 ? 512 : 256; }
+static KSplit f8_wgrad_split(int64_t M, int64_t N, int64_t K) {
+  const Tile t = pick_tile_wgrad(M, N);
+  return plan_split(tile_count(t, M, N), K, 128, 1024, wgrad_target(t));  // K in codes
+}
+int64_t part_bytes_f8_wgrad(int64_t M, int64_t N, int64_t K) {
+  const KSplit ks = f8_wgrad_split(M, N, K);
+  return ks.splits > 1 ? ks.splits * M * N * 4 : 0;
+}
+
 void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                  const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
-                 hipStream_t s) {
+                 float* part, int64_t part_cap, hipStream_t s) {
   const Tile t = pick_tile_wgrad(M, N);
-  const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-  const int64_t kc = 2 * pick_kchunk(tiles, K / 2);  // in codes
+  const KSplit ks = f8_wgrad_split(M, N, K);
   const Deq8 q = to_deq(dq);
-  if (kc >= K) {
+  if (ks.splits == 1) {
     run_f8<2>(t, A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0), q, s);
     return;
   }
-  if (!accumulate) launch_zero(C, M * N, s);
-  run_f8<2>(t, A, lda, B, ldb, M, N, K, kc, mk_atomic(C, N), q, s);
+  check_part(part_bytes_f8_wgrad(M, N, K), part_cap);
+  run_f8<2>(t, A, lda, B, ldb, M, N, K, ks.chunk, mk_part(part, M, N), q, s);
+  splitk_reduce(part, ks.splits, M, N, C, accumulate, s);
 }
 
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
@@ -675,36 +755,57 @@ void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, con
         mk_relu2bwd<float>(U, C, N), s);
 }
 
+static KSplit nn_split(int64_t M, int64_t N, int64_t K) {
+  return plan_split(tile_count(pick_tile(M, N, K), M, N), K, 64, 4096);
+}
+int64_t part_bytes_nn_splitk(const Dims& d, int64_t M, int64_t N, int64_t K) {
+  if (!d.bf16) return 0;
+  const KSplit ks = nn_split(M, N, K);
+  return ks.splits > 1 ? ks.splits * M * N * 4 : 0;
+}
+
 void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                        float* C, hipStream_t s) {
+                        float* C, float* part, int64_t part_cap, hipStream_t s) {
   if (d.bf16) {
     const Tile t = pick_tile(M, N, K);
-    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-    const int64_t kc = pick_kchunk(tiles, K, 4096);
-    if (kc >= K) {
+    const KSplit ks = nn_split(M, N, K);
+    if (ks.splits == 1) {
       run_bf16<true, false>(t, A, K, B, N, M, N, K, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
       return;
     }
-    launch_zero(C, M * N, s);
-    run_bf16<true, false>(t, A, K, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), s);
+    check_part(part_bytes_nn_splitk(d, M, N, K), part_cap);
+    run_bf16<true, false>(t, A, K, B, N, M, N, K, ks.chunk, PreId{}, PreId{}, mk_part(part, M, N),
+                          s);
+    splitk_reduce(part, ks.splits, M, N, C, false, s);
   } else {
     run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
   }
 }
 
+static KSplit tn_split(int64_t M, int64_t N, int64_t K) {
+  const Tile t = pick_tile_wgrad(M, N);
+  return plan_split(tile_count(t, M, N), K, 64, 512, wgrad_target(t));
+}
+int64_t part_bytes_tn_wgrad(const Dims& d, int64_t M, int64_t N, int64_t K) {
+  if (!d.bf16) return 0;
+  const KSplit ks = tn_split(M, N, K);
+  return ks.splits > 1 ? ks.splits * M * N * 4 : 0;
+}
+
 void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
-                   float* C, bool accumulate, hipStream_t s) {
+                   float* C, bool accumulate, float* part, int64_t part_cap, hipStream_t s) {
   if (d.bf16) {
     const Tile t = pick_tile_wgrad(M, N);
-    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-    const int64_t kc = pick_kchunk(tiles, K);
-    if (kc >= K) {  // one split: plain (accumulating) stores
-      run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{},
+    const KSplit ks = tn_split(M, N, K);
+    if (ks.splits == 1) {  // one split: plain (accumulating) stores
+      run_bf16<false, false>(t, A, M, B, N, M, N, K, K, PreId{}, PreId{},
                              mk_f32(C, N, accumulate ? 1 : 0), s);
       return;
     }
-    if (!accumulate) launch_zero(C, (int64_t)M * N, s);
-    run_bf16<false, false>(t, A, M, B, N, M, N, K, kc, PreId{}, PreId{}, mk_atomic(C, N), s);
+    check_part(part_bytes_tn_wgrad(d, M, N, K), part_cap);
+    run_bf16<false, false>(t, A, M, B, N, M, N, K, ks.chunk, PreId{}, PreId{},
+                           mk_part(part, M, N), s);
+    splitk_reduce(part, ks.splits, M, N, C, accumulate, s);
   } else {
     run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
                                  mk_f32(C, N, accumulate ? 1 : 0), s);

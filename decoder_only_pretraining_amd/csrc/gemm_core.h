@@ -264,7 +264,7 @@ template <int BM, int BN, int BK, bool AK, bool BKM, int MODE, class PA, class P
           class DQ>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
-    int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep,
+    int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep_in,
     DQ dq) {
   static_assert(!PA::kActive && !PB::kActive, "direct LDS loads take operands as stored");
   constexpr bool F8 = MODE != 0;
@@ -295,6 +295,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   const int ntiles = tiles_m * tiles_n;
   const int split = pid / ntiles;
   pid -= split * ntiles;
+  const EP ep = ep_in.at_split(split);  // split-K products write per-split partials
   constexpr int GM = 8;
   const int group = pid / (GM * tiles_n);
   const int first_m = group * GM;
@@ -435,26 +436,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   }
 
   const int64_t mw = m0 + wm * (BM / 2), nw = n0 + wn * WN;
-  if constexpr (EP::kScalar) {
-    // Scalar (atomic) epilogues write every accumulator straight from its
-    // MFMA layout: for one accumulator index, lanes 0-31 cover 32
-    // consecutive columns of one row and lanes 32-63 the same columns four
-    // rows further, as coalesced as a staged slab and without LDS traffic.
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = mw + i * 32 + acc_row(e, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t n = nw + j * 32 + (lane & 31);
-          float x = acc[i][j][e];
-          if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(n)];
-          if (m < M && n < N) ep.store1(m, n, ep.value(m, n, x));
-        }
-      }
-    return;
-  }
   // Epilogue, one 32-row slab of the wavefront tile at a time: transform
   // the accumulators in their MFMA layout, stage the slab in LDS as fp32,
   // then write it back with 4-column vectors; all LDS reads of a slab are

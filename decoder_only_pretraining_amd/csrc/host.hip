@@ -236,6 +236,17 @@ Plan make_plan(const Dims& d) {
   p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
   p.veg_splits = 256;
   p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
+  {  // split-K partials: the largest over the step's split products
+    int64_t pb = std::max(part_bytes_nn_splitk(d, d.N, d.C, d.V),
+                          part_bytes_tn_wgrad(d, d.V, d.C, d.N));
+    const int64_t shapes[4][2] = {{d.Qkv, d.C}, {d.C, d.Cq}, {d.F, d.C}, {d.C, d.F}};
+    for (const auto& mn : shapes) {
+      pb = std::max(pb, part_bytes_tn_wgrad(d, mn[0], mn[1], d.N));
+      if (d.fp8) pb = std::max(pb, part_bytes_f8_wgrad(mn[0], mn[1], (d.N + 15) / 16 * 16));
+    }
+    p.part_bytes = pb;
+    p.part = take((size_t)pb);
+  }
   if (d.fp8) {
     auto P128 = [](int64_t x) { return (size_t)((x + 127) / 128 * 128); };
     const size_t C = d.C, Cq = d.Cq, F = d.F, Qkv = d.Qkv;
@@ -512,8 +523,10 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     float* lam_part = reinterpret_cast<float*>(W + P.lam_part);
     float* veg_part = reinterpret_cast<float*>(W + P.veg_part);
 
-    site("gemm.lm.dgrad", s, [&] { gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, s); });
-    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, s); });
+    float* part = reinterpret_cast<float*>(W + P.part);
+    const int64_t pcap = P.part_bytes;
+    site("gemm.lm.dgrad", s, [&] { gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, part, pcap, s); });
+    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, part, pcap, s); });
     NormBwdArgs nb{};
     nb.mode = NB_FINAL;
     nb.gin = gtmp;
@@ -545,7 +558,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         });
         site("gemm.mp.wgrad", s, [&] {
           gemm8_wgrad(C, Fh, Nk, g8t, Np, LY8(l, P.l_h8t), Np,
-                      deq1(slot(l, 10), slot(l, 9), FP8_E5M2), grads + F.mp[l], acc, s);
+                      deq1(slot(l, 10), slot(l, 9), FP8_E5M2), grads + F.mp[l], acc, part, pcap, s);
         });
         site("fp8.quant", s, [&] { quant_tok(gu, true, Fh, one_seg(slot(l, 11)), FP8_E5M2, g8t); });
         site("gemm.fc.dgrad", s, [&] {
@@ -554,13 +567,13 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         });
         site("gemm.fc.wgrad", s, [&] {
           gemm8_wgrad(Fh, C, Nk, g8t, Np, LY8(l, P.l_x28t), Np,
-                      deq1(slot(l, 11), slot(l, 8), FP8_E5M2), grads + F.fc[l], acc, s);
+                      deq1(slot(l, 11), slot(l, 8), FP8_E5M2), grads + F.fc[l], acc, part, pcap, s);
         });
       } else {
         site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s); });
-        site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, s); });
+        site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, part, pcap, s); });
         site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s); });
-        site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, s); });
+        site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, part, pcap, s); });
       }
       nb = NormBwdArgs{};
       nb.mode = NB_NORM2;
@@ -579,11 +592,11 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         });
         site("gemm.o.wgrad", s, [&] {
           gemm8_wgrad(d.C, d.Cq, Nk, g8t, Np, LY8(l, P.l_a8t), Np,
-                      deq1(slot(l, 12), slot(l, 7), FP8_E5M2), grads + F.o[l], acc, s);
+                      deq1(slot(l, 12), slot(l, 7), FP8_E5M2), grads + F.o[l], acc, part, pcap, s);
         });
       } else {
         site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s); });
-        site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, s); });
+        site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, part, pcap, s); });
       }
       site("attn.delta", s, [&] { launch_attn_delta(d, gO, att, delta, s); });
       site("attn.bwd", s, [&] { launch_attn_bwd(d, full, qkv, gO, lse, delta, gqkv, s); });
@@ -606,11 +619,11 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         site("gemm.qkv.wgrad", s, [&] {
           const int x = slot(l, 6);
           gemm8_wgrad(d.Qkv, d.C, Nk, g8t, Np, LY8(l, P.l_x8t), Np,
-                      deq3(0, g0, g1, g2, x, x, x, FP8_E5M2), grads + F.q[l], acc, s);
+                      deq3(0, g0, g1, g2, x, x, x, FP8_E5M2), grads + F.q[l], acc, part, pcap, s);
         });
       } else {
         site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s); });
-        site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, s); });
+        site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, part, pcap, s); });
       }
       if (ve) launch_veg_wgrad(d, ga, xn, veg_part, P.veg_splits, grads + F.veg[l], s);
       nb = NormBwdArgs{};
@@ -730,6 +743,7 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
       {"gqkv", P.gqkv, N * d.Qkv * A}, {"delta", P.delta, N * d.H * 4},
       {"ga", P.ga, N * d.Hk * 4}, {"lam_part", P.lam_part, (size_t)d.L * P.lam_blocks * 8},
       {"veg_part", P.veg_part, (size_t)P.veg_splits * d.Hk * C * 4},
+      {"part", P.part, (size_t)P.part_bytes},
       {"amax", P.amax, d.fp8 ? (size_t)16 * d.L * 4 : 0},
       {"w8", P.w8, d.fp8 ? P.w8_layer * d.L : 0},
       {"w8t", P.w8t, d.fp8 ? P.w8t_layer * d.L : 0},

@@ -44,6 +44,8 @@ struct Plan {
   size_t layers, layer_bytes;
   size_t l_xn, l_r1, l_qkv, l_rqk, l_a, l_attn, l_lse, l_xmid, l_xn2, l_r2, l_u;
   size_t xf, rf, logits, lossrow, scalars;
+  size_t part;           // split-K partials
+  int64_t part_bytes;
   size_t gx, gxc, gx0, gu, gtmp, gO, gqkv, delta, ga, lam_part, veg_part;
   int lam_blocks, veg_splits;
   // fp8 linears only (0 bytes otherwise). Token-major code tensors that the
@@ -152,13 +154,17 @@ void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const vo
 // C = (A B) * 2 sqrt(H): the MLP hidden gradient from h = relu(u)^2
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                       const void* H, void* C, hipStream_t s);
-// Like gemm_nn_f32 for a long contraction: K split across workgroups, C
-// zeroed and accumulated with fp32 atomics.
+// Split-K products: each K split writes an fp32 partial of C into `part`
+// (capacity part_cap bytes, at least what the matching *_part_bytes returns
+// for the shape) and the partials are added in split order.
+// Like gemm_nn_f32 for a long contraction.
 void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                        float* C, hipStream_t s);
+                        float* C, float* part, int64_t part_cap, hipStream_t s);
+int64_t part_bytes_nn_splitk(const Dims& d, int64_t M, int64_t N, int64_t K);
 // Weight gradients C[M][N] (+)= sum_k A[k][m] B[k][n].
 void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
-                   float* C, bool accumulate, hipStream_t s);
+                   float* C, bool accumulate, float* part, int64_t part_cap, hipStream_t s);
+int64_t part_bytes_tn_wgrad(const Dims& d, int64_t M, int64_t N, int64_t K);
 
 // ------------------------------------------------------------ fp8 linears
 // Per-tensor dynamic scaling: s = fmax / amax in fp32; codes are
@@ -221,10 +227,11 @@ void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t l
 void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
                hipStream_t s);
-// Weight gradient (K = tokens, split over workgroups with fp32 atomics when
-// that fills the machine); C (+)= the product.
+// Weight gradient (K = tokens, split over workgroups when that fills the
+// machine, partials as for gemm_tn_wgrad); C (+)= the product.
 void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                  const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
-                 hipStream_t s);
+                 float* part, int64_t part_cap, hipStream_t s);
+int64_t part_bytes_f8_wgrad(int64_t M, int64_t N, int64_t K);
 
 }  // namespace gpt
