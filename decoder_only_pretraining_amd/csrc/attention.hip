@@ -450,21 +450,27 @@ __global__ __launch_bounds__(512) void attn_fwd_tiled_kernel(const bf16* __restr
 }
 
 // ------------------------------------------------------------ delta
-template <typename T>
+// delta = rowsum(dO * O) per (batch, head, token), stored in that order
+// (token fastest). A row belongs to LP = D/8 lanes, 8 elements each.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ gO,
                                                          const T* __restrict__ O,
                                                          float* __restrict__ delta, int64_t NH,
-                                                         int D, int H, int T_) {
-  const int lane = threadIdx.x & 63;
-  // i runs over [batch][head][token], token fastest, like delta itself
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                         int H, int T_) {
+  constexpr int LP = D / 8;
+  const int q = threadIdx.x % LP;
+  const int64_t i = (int64_t)blockIdx.x * (256 / LP) + threadIdx.x / LP;
   if (i >= NH) return;
   const int64_t bh = i / T_, t = i % T_;
   const int64_t row = ((bh / H) * T_ + t) * H + bh % H;  // (n, h) row of gO and O
+  const T* g = gO + row * D + 8 * q;
+  const T* o = O + row * D + 8 * q;
   float s = 0.0f;
-  for (int d = lane; d < D; d += 64) s += to_f(gO[row * D + d]) * to_f(O[row * D + d]);
-  s = wave_sum(s);
-  if (lane == 0) delta[i] = s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += to_f(g[e]) * to_f(o[e]);
+#pragma unroll
+  for (int w = LP / 2; w > 0; w >>= 1) s += __shfl_xor(s, w, kWave);
+  if (q == 0) delta[i] = s;
 }
 
 // ------------------------------------------------------------ dK, dV
@@ -1149,14 +1155,19 @@ void launch_attn_fwd(const Dims& d, bool full, const void* qkv, void* out, float
 
 void launch_attn_delta(const Dims& d, const void* gO, const void* O, float* delta, hipStream_t s) {
   const int64_t NH = d.N * d.H;
-  dim3 grid((unsigned)((NH + 3) / 4));
-  if (d.bf16)
-    hipLaunchKernelGGL(attn_delta_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(gO),
-                       static_cast<const bf16*>(O), delta, NH, d.D, d.H, d.T);
-  else
-    hipLaunchKernelGGL(attn_delta_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(gO), static_cast<const float*>(O), delta, NH, d.D,
-                       d.H, d.T);
+  const int per = 256 / (d.D / 8);
+  dim3 grid((unsigned)((NH + per - 1) / per));
+#define GPT_DELTA(TY, DD)                                                                         \
+  hipLaunchKernelGGL((attn_delta_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<const TY*>(gO), \
+                     static_cast<const TY*>(O), delta, NH, d.H, d.T)
+  if (d.bf16) {
+    if (d.D == 128) GPT_DELTA(bf16, 128);
+    else GPT_DELTA(bf16, 64);
+  } else {
+    if (d.D == 128) GPT_DELTA(float, 128);
+    else GPT_DELTA(float, 64);
+  }
+#undef GPT_DELTA
 }
 
 void launch_attn_bwd(const Dims& d, bool full, const void* qkv, const void* gO, const float* lse,

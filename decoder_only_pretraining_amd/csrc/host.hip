@@ -234,7 +234,7 @@ Plan make_plan(const Dims& d) {
   p.ga = take(N * d.Hk * 4);
   p.lam_blocks = (int)((d.N + 3) / 4);
   p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
-  p.veg_splits = 256;
+  p.veg_splits = 512;
   p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
   {  // split-K partials: the largest over the step's split products
     int64_t pb = std::max(part_bytes_nn_splitk(d, d.N, d.C, d.V),

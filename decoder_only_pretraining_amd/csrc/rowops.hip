@@ -289,127 +289,188 @@ __global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __res
   }
 }
 
-// Gate weight gradient g_Wg[j][c] = sum_n ga[n][j] * xn[n][c]: per-split
-// partial sums, then a fixed-order sum over splits.
-template <typename T>
+// Gate weight gradient g_Wg[j][c] = sum_n ga[n][j] * xn[n][c]. Block b sums
+// the tokens [b * per, (b + 1) * per): thread (phase, column group) owns 8
+// consecutive columns and every NP-th token of the range; the phases are
+// then added in a fixed order and the block writes its partial. A second
+// kernel adds the partials in block order.
+template <typename T, int HK>
 __global__ __launch_bounds__(256) void veg_partial_kernel(const float* __restrict__ ga,
                                                           const T* __restrict__ xn,
                                                           float* __restrict__ part, int64_t N,
-                                                          int C, int hk, int splits) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int sp = blockIdx.y;
-  if (c >= C) return;
-  const int64_t per = (N + splits - 1) / splits;
-  const int64_t lo = sp * per, hi = lo + per < N ? lo + per : N;
-  float acc[16];
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  for (int64_t n = lo; n < hi; ++n) {
-    const float xv = to_f(xn[n * C + c]);
-    for (int j = 0; j < hk; ++j) acc[j] += ga[n * hk + j] * xv;
+                                                          int C, int hk, int64_t per) {
+  __shared__ float red[256 * 8];
+  const int CG = C / 8, NP = 256 / CG;  // column groups, token phases (C <= 2048)
+  const int cg = threadIdx.x % CG, ph = threadIdx.x / CG;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = lo + per < N ? lo + per : N;
+  float acc[HK][8];
+#pragma unroll
+  for (int j = 0; j < HK; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+  if (ph < NP) {
+#pragma unroll 4
+    for (int64_t n = lo + ph; n < hi; n += NP) {
+      const f32x4 x0 = load4<T>(xn + n * C + cg * 8), x1 = load4<T>(xn + n * C + cg * 8 + 4);
+#pragma unroll
+      for (int j = 0; j < HK; ++j) {
+        if (j < hk) {
+          const float g = ga[n * hk + j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[j][e] += g * x0[e];
+            acc[j][4 + e] += g * x1[e];
+          }
+        }
+      }
+    }
   }
-  for (int j = 0; j < hk; ++j) part[((int64_t)sp * hk + j) * C + c] = acc[j];
+#pragma unroll
+  for (int j = 0; j < HK; ++j) {  // constant indices keep acc in registers
+    if (j >= hk) break;            // uniform over the block
+    __syncthreads();
+    if (ph < NP) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[threadIdx.x * 8 + e] = acc[j][e];
+    }
+    __syncthreads();
+    if (ph == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[j][e];
+        for (int q = 1; q < NP; ++q) v += red[(q * CG + cg) * 8 + e];
+        part[((int64_t)blockIdx.x * hk + j) * C + cg * 8 + e] = v;
+      }
+    }
+  }
 }
 
+// Block b adds the partials of outputs 64b .. 64b+63: wavefront w takes the
+// splits w, w + 4, ..., then the four sums are added in wavefront order.
 __global__ __launch_bounds__(256) void veg_finalize_kernel(const float* __restrict__ part,
-                                                           float* __restrict__ g, int C, int hk,
-                                                           int splits, int accumulate) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= C * hk) return;
+                                                           float* __restrict__ g, int n, int splits,
+                                                           int accumulate) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
   float s = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) s += part[(int64_t)sp * hk * C + i];
-  g[i] = accumulate ? g[i] + s : s;
+  if (i < n) {
+#pragma unroll 8
+    for (int sp = w; sp < splits; sp += 4) s += part[(int64_t)sp * n + i];
+  }
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && i < n) {
+    const float v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    g[i] = accumulate ? g[i] + v : v;
+  }
 }
 
 // ------------------------------------------------------------ RoPE + QK-norm + VE
-// One block of 4 wavefronts per token. Head slots 0..H-1 are q heads,
-// H..H+Hk-1 k heads, H+Hk..H+2Hk-1 v heads (value-embedding layers only).
-// Lane p < D/2 owns the rotation pair (p, p + D/2).
-template <typename T>
+// Tasks: every (token, q or k head) pair, then (value-embedding layers) every
+// (token, v head) pair. A task belongs to LP = D/8 consecutive lanes; lane q
+// of it owns elements 4q .. 4q+3 and D/2 + 4q .. D/2 + 4q + 3, i.e. the
+// rotation pairs (p, p + D/2) for p = 4q .. 4q+3, and the group reduces
+// with LP-lane shuffles. Head slots 0..H-1 of a token's row are q heads,
+// H..H+Hk-1 k heads, H+Hk..H+2Hk-1 v heads.
+template <int LP>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = LP / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+// y = rope(x) (pairs rotated by t * theta_p), then y * r with
+// r = 1 / sqrt(mean(y^2) + eps), saved for the backward; v += sigmoid(a) * ve.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rqk,
                                                        const float* __restrict__ cs,
                                                        const float* __restrict__ a,
                                                        const float* __restrict__ ve,
-                                                       const int32_t* __restrict__ tok, int T_,
-                                                       int H, int Hk, int D, int Qkv, float eps) {
-  const int64_t n = blockIdx.x;
-  const int t = (int)(n % T_);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int h2 = D / 2;
-  const int nslots = H + Hk + (ve ? Hk : 0);
-  T* row = qkv + n * Qkv;
-  for (int sl = wv; sl < nslots; sl += 4) {
-    if (sl < H + Hk) {
-      T* hp = row + sl * D;  // k heads follow the q heads contiguously
-      float y1 = 0.0f, y2 = 0.0f;
-      if (lane < h2) {
-        const float c = cs[t * h2 + lane], s = cs[(int64_t)T_ * h2 + t * h2 + lane];
-        const float x1 = to_f(hp[lane]), x2 = to_f(hp[lane + h2]);
-        y1 = x1 * c - x2 * s;
-        y2 = x1 * s + x2 * c;
-      }
-      const float ss = wave_sum(y1 * y1 + y2 * y2);
-      const float r = 1.0f / sqrtf(ss / (float)D + eps);
-      if (lane < h2) {
-        hp[lane] = from_f<T>(y1 * r);
-        hp[lane + h2] = from_f<T>(y2 * r);
-      }
-      if (lane == 0) rqk[n * (H + Hk) + sl] = r;
-    } else {
-      const int j = sl - H - Hk;
-      T* vp = row + (H + Hk) * D + j * D;
-      const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
-      const float* er = ve + (int64_t)tok[n] * Hk * D + j * D;
-      for (int dd = lane; dd < D; dd += 64) vp[dd] = from_f<T>(to_f(vp[dd]) + g * er[dd]);
+                                                       const int32_t* __restrict__ tok, int64_t N,
+                                                       int T_, int H, int Hk, int Qkv, float eps) {
+  constexpr int H2 = D / 2, LP = D / 8;
+  const int q = threadIdx.x % LP;
+  const int64_t task = (int64_t)blockIdx.x * (256 / LP) + threadIdx.x / LP;
+  const int R = H + Hk;
+  const int64_t nrot = N * R;
+  if (task < nrot) {
+    const int64_t n = task / R;
+    const int sl = (int)(task % R), t = (int)(n % T_);
+    T* hp = qkv + n * Qkv + sl * D;  // k heads follow the q heads contiguously
+    const f32x4 x1 = load4<T>(hp + 4 * q), x2 = load4<T>(hp + H2 + 4 * q);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(cs + (int64_t)t * H2 + 4 * q);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(cs + ((int64_t)T_ + t) * H2 + 4 * q);
+    const f32x4 y1 = x1 * c - x2 * sn, y2 = x1 * sn + x2 * c;
+    const float ss = group_sum<LP>(dot4(y1, y1) + dot4(y2, y2));
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    store4<T>(hp + 4 * q, y1 * r);
+    store4<T>(hp + H2 + 4 * q, y2 * r);
+    if (q == 0) rqk[n * R + sl] = r;
+  } else if (ve && task - nrot < N * Hk) {
+    const int64_t n = (task - nrot) / Hk;
+    const int j = (int)((task - nrot) % Hk);
+    T* vp = qkv + n * Qkv + (R + j) * D;
+    const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
+    const float* er = ve + (int64_t)tok[n] * Hk * D + j * D;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int o = half * H2 + 4 * q;
+      store4<T>(vp + o, load4<T>(vp + o) + g * *reinterpret_cast<const f32x4*>(er + o));
     }
   }
 }
 
-template <typename T>
+// In place on the q / k / v gradient rows: through the QK-norm
+// (r * (g - y * mean(g * y)), y the saved normalised output) and the inverse
+// rotation; for v heads of value-embedding layers the table gradient
+// (atomic adds into the token's row) and the gate logit's gradient.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_bwd_kernel(
     T* __restrict__ gqkv, const T* __restrict__ qkv, const float* __restrict__ rqk,
     const float* __restrict__ cs, const float* __restrict__ a, const float* __restrict__ ve,
-    float* __restrict__ gve, float* __restrict__ ga, const int32_t* __restrict__ tok, int T_,
-    int H, int Hk, int D, int Qkv) {
-  const int64_t n = blockIdx.x;
-  const int t = (int)(n % T_);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int h2 = D / 2;
-  const int nslots = H + Hk + (ve ? Hk : 0);
-  T* grow = gqkv + n * Qkv;
-  const T* row = qkv + n * Qkv;
-  for (int sl = wv; sl < nslots; sl += 4) {
-    if (sl < H + Hk) {
-      T* gp = grow + sl * D;
-      const T* yp = row + sl * D;
-      float g1 = 0.0f, g2 = 0.0f, y1 = 0.0f, y2 = 0.0f;
-      if (lane < h2) {
-        g1 = to_f(gp[lane]);
-        g2 = to_f(gp[lane + h2]);
-        y1 = to_f(yp[lane]);
-        y2 = to_f(yp[lane + h2]);
-      }
-      const float dot = wave_sum(g1 * y1 + g2 * y2) / (float)D;
-      const float r = rqk[n * (H + Hk) + sl];
-      if (lane < h2) {
-        const float a1 = r * (g1 - y1 * dot), a2 = r * (g2 - y2 * dot);
-        const float c = cs[t * h2 + lane], s = cs[(int64_t)T_ * h2 + t * h2 + lane];
-        gp[lane] = from_f<T>(a1 * c + a2 * s);
-        gp[lane + h2] = from_f<T>(-a1 * s + a2 * c);
-      }
-    } else {
-      const int j = sl - H - Hk;
-      const T* gp = grow + (H + Hk) * D + j * D;
-      const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
-      const int64_t off = (int64_t)tok[n] * Hk * D + j * D;
-      float dot = 0.0f;
-      for (int dd = lane; dd < D; dd += 64) {
-        const float gv = to_f(gp[dd]);
-        dot += gv * ve[off + dd];
-        atomicAdd(gve + off + dd, g * gv);
-      }
-      dot = wave_sum(dot);
-      if (lane == 0) ga[n * Hk + j] = g * (1.0f - g) * dot;
+    float* __restrict__ gve, float* __restrict__ ga, const int32_t* __restrict__ tok, int64_t N,
+    int T_, int H, int Hk, int Qkv) {
+  constexpr int H2 = D / 2, LP = D / 8;
+  const int q = threadIdx.x % LP;
+  const int64_t task = (int64_t)blockIdx.x * (256 / LP) + threadIdx.x / LP;
+  const int R = H + Hk;
+  const int64_t nrot = N * R;
+  if (task < nrot) {
+    const int64_t n = task / R;
+    const int sl = (int)(task % R), t = (int)(n % T_);
+    T* gp = gqkv + n * Qkv + sl * D;
+    const T* yp = qkv + n * Qkv + sl * D;
+    const f32x4 g1 = load4<T>(gp + 4 * q), g2 = load4<T>(gp + H2 + 4 * q);
+    const f32x4 y1 = load4<T>(yp + 4 * q), y2 = load4<T>(yp + H2 + 4 * q);
+    const float dot = group_sum<LP>(dot4(g1, y1) + dot4(g2, y2)) / (float)D;
+    const float r = rqk[n * R + sl];
+    const f32x4 a1 = r * (g1 - y1 * dot), a2 = r * (g2 - y2 * dot);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(cs + (int64_t)t * H2 + 4 * q);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(cs + ((int64_t)T_ + t) * H2 + 4 * q);
+    store4<T>(gp + 4 * q, a1 * c + a2 * sn);
+    store4<T>(gp + H2 + 4 * q, a2 * c - a1 * sn);
+  } else if (ve && task - nrot < N * Hk) {
+    const int64_t n = (task - nrot) / Hk;
+    const int j = (int)((task - nrot) % Hk);
+    const T* gp = gqkv + n * Qkv + (R + j) * D;
+    const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
+    const int64_t off = (int64_t)tok[n] * Hk * D + j * D;
+    // elements q, q + LP, ...: the group's atomic adds of one instruction
+    // hit consecutive addresses
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int o = q + e * LP;
+      const float gv = to_f(gp[o]);
+      dot += gv * ve[off + o];
+      atomicAdd(gve + off + o, g * gv);
     }
+    dot = group_sum<LP>(dot);
+    if (q == 0) ga[n * Hk + j] = g * (1.0f - g) * dot;
   }
 }
 
@@ -642,40 +703,62 @@ void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, floa
 
 void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* part, int splits,
                       float* gwg, hipStream_t s) {
-  dim3 grid((unsigned)((d.C + 255) / 256), (unsigned)splits);
-  if (d.bf16)
-    hipLaunchKernelGGL(veg_partial_kernel<bf16>, grid, dim3(256), 0, s, ga,
-                       static_cast<const bf16*>(xn), part, d.N, d.C, d.Hk, splits);
-  else
-    hipLaunchKernelGGL(veg_partial_kernel<float>, grid, dim3(256), 0, s, ga,
-                       static_cast<const float*>(xn), part, d.N, d.C, d.Hk, splits);
-  hipLaunchKernelGGL(veg_finalize_kernel, dim3((unsigned)((d.C * d.Hk + 255) / 256)), dim3(256),
-                     0, s, part, gwg, d.C, d.Hk, splits, d.accumulate ? 1 : 0);
+  const int64_t per = (d.N + splits - 1) / splits;
+#define GPT_VEG(TY, HK)                                                                            \
+  hipLaunchKernelGGL((veg_partial_kernel<TY, HK>), dim3((unsigned)splits), dim3(256), 0, s, ga,    \
+                     static_cast<const TY*>(xn), part, d.N, d.C, d.Hk, per)
+  if (d.bf16) {
+    if (d.Hk <= 4) GPT_VEG(bf16, 4);
+    else if (d.Hk <= 8) GPT_VEG(bf16, 8);
+    else GPT_VEG(bf16, 16);
+  } else {
+    if (d.Hk <= 4) GPT_VEG(float, 4);
+    else if (d.Hk <= 8) GPT_VEG(float, 8);
+    else GPT_VEG(float, 16);
+  }
+#undef GPT_VEG
+  const int n = d.C * d.Hk;
+  hipLaunchKernelGGL(veg_finalize_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
+                     gwg, n, splits, d.accumulate ? 1 : 0);
+}
+
+static unsigned rope_blocks(const Dims& d, bool ve) {
+  const int64_t tasks = d.N * (d.H + d.Hk + (ve ? d.Hk : 0));
+  return (unsigned)((tasks + 256 / (d.D / 8) - 1) / (256 / (d.D / 8)));
 }
 
 void launch_rope_qk_ve_fwd(const Dims& d, void* qkv, float* rqk, const float* cs, const float* a,
                            const float* ve_table, const int32_t* tok, hipStream_t s) {
-  if (d.bf16)
-    hipLaunchKernelGGL(rope_fwd_kernel<bf16>, dim3((unsigned)d.N), dim3(256), 0, s,
-                       static_cast<bf16*>(qkv), rqk, cs, a, ve_table, tok, d.T, d.H, d.Hk, d.D,
-                       d.Qkv, d.eps);
-  else
-    hipLaunchKernelGGL(rope_fwd_kernel<float>, dim3((unsigned)d.N), dim3(256), 0, s,
-                       static_cast<float*>(qkv), rqk, cs, a, ve_table, tok, d.T, d.H, d.Hk, d.D,
-                       d.Qkv, d.eps);
+  const dim3 grid(rope_blocks(d, ve_table != nullptr));
+#define GPT_ROPE_F(TY, DD)                                                                        \
+  hipLaunchKernelGGL((rope_fwd_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<TY*>(qkv), rqk, \
+                     cs, a, ve_table, tok, d.N, d.T, d.H, d.Hk, d.Qkv, d.eps)
+  if (d.bf16) {
+    if (d.D == 128) GPT_ROPE_F(bf16, 128);
+    else GPT_ROPE_F(bf16, 64);
+  } else {
+    if (d.D == 128) GPT_ROPE_F(float, 128);
+    else GPT_ROPE_F(float, 64);
+  }
+#undef GPT_ROPE_F
 }
 
 void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const float* rqk,
                            const float* cs, const float* a, const float* ve_table,
                            float* gve_table, float* ga, const int32_t* tok, hipStream_t s) {
-  if (d.bf16)
-    hipLaunchKernelGGL(rope_bwd_kernel<bf16>, dim3((unsigned)d.N), dim3(256), 0, s,
-                       static_cast<bf16*>(gqkv), static_cast<const bf16*>(qkv), rqk, cs, a,
-                       ve_table, gve_table, ga, tok, d.T, d.H, d.Hk, d.D, d.Qkv);
-  else
-    hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3((unsigned)d.N), dim3(256), 0, s,
-                       static_cast<float*>(gqkv), static_cast<const float*>(qkv), rqk, cs, a,
-                       ve_table, gve_table, ga, tok, d.T, d.H, d.Hk, d.D, d.Qkv);
+  const dim3 grid(rope_blocks(d, ve_table != nullptr));
+#define GPT_ROPE_B(TY, DD)                                                                          \
+  hipLaunchKernelGGL((rope_bwd_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<TY*>(gqkv),       \
+                     static_cast<const TY*>(qkv), rqk, cs, a, ve_table, gve_table, ga, tok, d.N,    \
+                     d.T, d.H, d.Hk, d.Qkv)
+  if (d.bf16) {
+    if (d.D == 128) GPT_ROPE_B(bf16, 128);
+    else GPT_ROPE_B(bf16, 64);
+  } else {
+    if (d.D == 128) GPT_ROPE_B(float, 128);
+    else GPT_ROPE_B(float, 64);
+  }
+#undef GPT_ROPE_B
 }
 
 void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipStream_t s) {
