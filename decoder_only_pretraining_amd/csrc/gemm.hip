@@ -551,8 +551,8 @@ template <int BM, int BN, bool AK, bool BKM, class PA, class PB, class EP>
 void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
                  int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  const int splits = (int)((K + kchunk - 1) / kchunk);
-  dim3 grid((unsigned)(tm * tn * std::max(splits, 1)));
+  const int splits = K > 0 && kchunk > 0 ? (int)((K + kchunk - 1) / kchunk) : 1;
+  dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8));  // padded: see the kernel's tile order
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq>), grid, dim3(256),
                      0, s, static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M,
                      N, K, kchunk, tm, tn, pa, pb, ep, NoDeq{});
@@ -579,8 +579,8 @@ void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int
                int64_t K, int64_t kchunk, EP ep, const Deq8& dq, hipStream_t s) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const int64_t Kp = K / 2, kc = kchunk / 2;
-  const int splits = (int)((Kp + kc - 1) / kc);
-  dim3 grid((unsigned)(tm * tn * std::max(splits, 1)));
+  const int splits = Kp > 0 && kc > 0 ? (int)((Kp + kc - 1) / kc) : 1;
+  dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8));  // padded: see the kernel's tile order
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, true, true, MODE, PreId, PreId, EP, Deq8>), grid,
                      dim3(256), 0, s, reinterpret_cast<const bf16*>(A), lda / 2,
                      reinterpret_cast<const bf16*>(B), ldb / 2, M, N, Kp, kc, tm, tn, PreId{},
@@ -672,19 +672,19 @@ int64_t part_bytes_f8_wgrad(int64_t M, int64_t N, int64_t K) {
   return ks.splits > 1 ? ks.splits * M * N * 4 : 0;
 }
 
-void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
-                 float* part, int64_t part_cap, hipStream_t s) {
+SplitSum gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                     const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                     float* part, int64_t part_cap, hipStream_t s) {
   const Tile t = pick_tile_wgrad(M, N);
   const KSplit ks = f8_wgrad_split(M, N, K);
   const Deq8 q = to_deq(dq);
   if (ks.splits == 1) {
     run_f8<2>(t, A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0), q, s);
-    return;
+    return SplitSum{};
   }
   check_part(part_bytes_f8_wgrad(M, N, K), part_cap);
   run_f8<2>(t, A, lda, B, ldb, M, N, K, ks.chunk, mk_part(part, M, N), q, s);
-  splitk_reduce(part, ks.splits, M, N, C, accumulate, s);
+  return SplitSum{part, ks.splits, M, N, C, accumulate};
 }
 
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
@@ -764,22 +764,23 @@ int64_t part_bytes_nn_splitk(const Dims& d, int64_t M, int64_t N, int64_t K) {
   return ks.splits > 1 ? ks.splits * M * N * 4 : 0;
 }
 
-void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                        float* C, float* part, int64_t part_cap, hipStream_t s) {
+SplitSum gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A,
+                            const void* B, float* C, float* part, int64_t part_cap,
+                            hipStream_t s) {
   if (d.bf16) {
     const Tile t = pick_tile(M, N, K);
     const KSplit ks = nn_split(M, N, K);
     if (ks.splits == 1) {
       run_bf16<true, false>(t, A, K, B, N, M, N, K, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
-      return;
+      return SplitSum{};
     }
     check_part(part_bytes_nn_splitk(d, M, N, K), part_cap);
     run_bf16<true, false>(t, A, K, B, N, M, N, K, ks.chunk, PreId{}, PreId{}, mk_part(part, M, N),
                           s);
-    splitk_reduce(part, ks.splits, M, N, C, false, s);
-  } else {
-    run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
+    return SplitSum{part, ks.splits, M, N, C, false};
   }
+  run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
+  return SplitSum{};
 }
 
 static KSplit tn_split(int64_t M, int64_t N, int64_t K) {
@@ -792,24 +793,28 @@ int64_t part_bytes_tn_wgrad(const Dims& d, int64_t M, int64_t N, int64_t K) {
   return ks.splits > 1 ? ks.splits * M * N * 4 : 0;
 }
 
-void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
-                   float* C, bool accumulate, float* part, int64_t part_cap, hipStream_t s) {
+SplitSum gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
+                       float* C, bool accumulate, float* part, int64_t part_cap, hipStream_t s) {
   if (d.bf16) {
     const Tile t = pick_tile_wgrad(M, N);
     const KSplit ks = tn_split(M, N, K);
     if (ks.splits == 1) {  // one split: plain (accumulating) stores
       run_bf16<false, false>(t, A, M, B, N, M, N, K, K, PreId{}, PreId{},
                              mk_f32(C, N, accumulate ? 1 : 0), s);
-      return;
+      return SplitSum{};
     }
     check_part(part_bytes_tn_wgrad(d, M, N, K), part_cap);
     run_bf16<false, false>(t, A, M, B, N, M, N, K, ks.chunk, PreId{}, PreId{},
                            mk_part(part, M, N), s);
-    splitk_reduce(part, ks.splits, M, N, C, accumulate, s);
-  } else {
-    run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
-                                 mk_f32(C, N, accumulate ? 1 : 0), s);
+    return SplitSum{part, ks.splits, M, N, C, accumulate};
   }
+  run_f32<float, false, false>(A, M, B, N, M, N, K, PreId{}, PreId{},
+                               mk_f32(C, N, accumulate ? 1 : 0), s);
+  return SplitSum{};
+}
+
+void splitk_sum(const SplitSum& r, hipStream_t s) {
+  if (r.splits > 1) splitk_reduce(r.part, r.splits, r.M, r.N, r.C, r.accumulate, s);
 }
 
 }  // namespace gpt

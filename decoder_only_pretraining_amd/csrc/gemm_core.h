@@ -288,11 +288,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   // XCD-aware, grouped tile order. The linear id runs over (split, tile),
   // split-major; consecutive ids are dealt to the 8 XCDs in turn, so the id
   // is remapped to give each XCD a contiguous range: its co-resident
-  // workgroups then share one K range and neighbouring tiles in its L2.
-  int pid = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  // workgroups then share one K range and neighbouring tiles in its L2. The
+  // grid is padded to a multiple of 8; the padding workgroups exit here.
   const int ntiles = tiles_m * tiles_n;
+  const int nwork = ntiles * (K > 0 && kchunk > 0 ? (int)((K + kchunk - 1) / kchunk) : 1);
+  int pid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (pid >= nwork) return;
   const int split = pid / ntiles;
   pid -= split * ntiles;
   const EP ep = ep_in.at_split(split);  // split-K products write per-split partials

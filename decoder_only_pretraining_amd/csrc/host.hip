@@ -525,8 +525,12 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
 
     float* part = reinterpret_cast<float*>(W + P.part);
     const int64_t pcap = P.part_bytes;
-    site("gemm.lm.dgrad", s, [&] { gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, part, pcap, s); });
-    site("gemm.lm.wgrad", s, [&] { gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, part, pcap, s); });
+    SplitSum ssum;  // split-K partials still to be added into their gradient
+    auto sum_splits = [&] { site("splitk.sum", s, [&] { splitk_sum(ssum, s); }); };
+    site("gemm.lm.dgrad", s, [&] { ssum = gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, part, pcap, s); });
+    sum_splits();
+    site("gemm.lm.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, part, pcap, s); });
+    sum_splits();
     NormBwdArgs nb{};
     nb.mode = NB_FINAL;
     nb.gin = gtmp;
@@ -557,23 +561,27 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
                          deq1(slot(l, 10), slot(l, 5), FP8_E5M2), u, gu, s);
         });
         site("gemm.mp.wgrad", s, [&] {
-          gemm8_wgrad(C, Fh, Nk, g8t, Np, LY8(l, P.l_h8t), Np,
-                      deq1(slot(l, 10), slot(l, 9), FP8_E5M2), grads + F.mp[l], acc, part, pcap, s);
+          ssum = gemm8_wgrad(C, Fh, Nk, g8t, Np, LY8(l, P.l_h8t), Np,
+                             deq1(slot(l, 10), slot(l, 9), FP8_E5M2), grads + F.mp[l], acc, part, pcap, s);
         });
+        sum_splits();
         site("fp8.quant", s, [&] { quant_tok(gu, true, Fh, one_seg(slot(l, 11)), FP8_E5M2, g8t); });
         site("gemm.fc.dgrad", s, [&] {
           gemm8_f32(N, C, Fh, q8, Fh, w8t(l, 2), P128(Fh), deq1(slot(l, 11), slot(l, 4), FP8_E5M2),
                     gtmp, false, s);
         });
         site("gemm.fc.wgrad", s, [&] {
-          gemm8_wgrad(Fh, C, Nk, g8t, Np, LY8(l, P.l_x28t), Np,
-                      deq1(slot(l, 11), slot(l, 8), FP8_E5M2), grads + F.fc[l], acc, part, pcap, s);
+          ssum = gemm8_wgrad(Fh, C, Nk, g8t, Np, LY8(l, P.l_x28t), Np,
+                             deq1(slot(l, 11), slot(l, 8), FP8_E5M2), grads + F.fc[l], acc, part, pcap, s);
         });
+        sum_splits();
       } else {
         site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s); });
-        site("gemm.mp.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, part, pcap, s); });
+        site("gemm.mp.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, part, pcap, s); });
+        sum_splits();
         site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s); });
-        site("gemm.fc.wgrad", s, [&] { gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, part, pcap, s); });
+        site("gemm.fc.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, part, pcap, s); });
+        sum_splits();
       }
       nb = NormBwdArgs{};
       nb.mode = NB_NORM2;
@@ -591,12 +599,14 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
                       deq1(slot(l, 12), slot(l, 3), FP8_E5M2), gO, s);
         });
         site("gemm.o.wgrad", s, [&] {
-          gemm8_wgrad(d.C, d.Cq, Nk, g8t, Np, LY8(l, P.l_a8t), Np,
-                      deq1(slot(l, 12), slot(l, 7), FP8_E5M2), grads + F.o[l], acc, part, pcap, s);
+          ssum = gemm8_wgrad(d.C, d.Cq, Nk, g8t, Np, LY8(l, P.l_a8t), Np,
+                             deq1(slot(l, 12), slot(l, 7), FP8_E5M2), grads + F.o[l], acc, part, pcap, s);
         });
+        sum_splits();
       } else {
         site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s); });
-        site("gemm.o.wgrad", s, [&] { gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, part, pcap, s); });
+        site("gemm.o.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, part, pcap, s); });
+        sum_splits();
       }
       site("attn.delta", s, [&] { launch_attn_delta(d, gO, att, delta, s); });
       site("attn.bwd", s, [&] { launch_attn_bwd(d, full, qkv, gO, lse, delta, gqkv, s); });
@@ -618,12 +628,14 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         });
         site("gemm.qkv.wgrad", s, [&] {
           const int x = slot(l, 6);
-          gemm8_wgrad(d.Qkv, d.C, Nk, g8t, Np, LY8(l, P.l_x8t), Np,
-                      deq3(0, g0, g1, g2, x, x, x, FP8_E5M2), grads + F.q[l], acc, part, pcap, s);
+          ssum = gemm8_wgrad(d.Qkv, d.C, Nk, g8t, Np, LY8(l, P.l_x8t), Np,
+                             deq3(0, g0, g1, g2, x, x, x, FP8_E5M2), grads + F.q[l], acc, part, pcap, s);
         });
+        sum_splits();
       } else {
         site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s); });
-        site("gemm.qkv.wgrad", s, [&] { gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, part, pcap, s); });
+        site("gemm.qkv.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, part, pcap, s); });
+        sum_splits();
       }
       if (ve) launch_veg_wgrad(d, ga, xn, veg_part, P.veg_splits, grads + F.veg[l], s);
       nb = NormBwdArgs{};

@@ -156,14 +156,24 @@ void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, con
                       const void* H, void* C, hipStream_t s);
 // Split-K products: each K split writes an fp32 partial of C into `part`
 // (capacity part_cap bytes, at least what the matching *_part_bytes returns
-// for the shape) and the partials are added in split order.
+// for the shape); the returned SplitSum, passed to splitk_sum, adds the
+// partials into C in split order (nothing to do when the product ran
+// unsplit and wrote C itself).
+struct SplitSum {
+  const float* part = nullptr;
+  int64_t splits = 0, M = 0, N = 0;
+  float* C = nullptr;
+  bool accumulate = false;
+};
+void splitk_sum(const SplitSum& r, hipStream_t s);
 // Like gemm_nn_f32 for a long contraction.
-void gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                        float* C, float* part, int64_t part_cap, hipStream_t s);
+SplitSum gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A,
+                            const void* B, float* C, float* part, int64_t part_cap,
+                            hipStream_t s);
 int64_t part_bytes_nn_splitk(const Dims& d, int64_t M, int64_t N, int64_t K);
 // Weight gradients C[M][N] (+)= sum_k A[k][m] B[k][n].
-void gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
-                   float* C, bool accumulate, float* part, int64_t part_cap, hipStream_t s);
+SplitSum gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,
+                       float* C, bool accumulate, float* part, int64_t part_cap, hipStream_t s);
 int64_t part_bytes_tn_wgrad(const Dims& d, int64_t M, int64_t N, int64_t K);
 
 // ------------------------------------------------------------ fp8 linears
@@ -229,9 +239,9 @@ void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                hipStream_t s);
 // Weight gradient (K = tokens, split over workgroups when that fills the
 // machine, partials as for gemm_tn_wgrad); C (+)= the product.
-void gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
-                 float* part, int64_t part_cap, hipStream_t s);
+SplitSum gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                     const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                     float* part, int64_t part_cap, hipStream_t s);
 int64_t part_bytes_f8_wgrad(int64_t M, int64_t N, int64_t K);
 
 }  // namespace gpt
