@@ -137,6 +137,45 @@ struct DirectLoader {
   using Geo = TileGeom<ROWS, BK, KMAJ>;
   static constexpr int BYTES = Geo::ELEMS * 2;
   static constexpr int CHUNKS = (BYTES + 1023) / 1024;
+  static constexpr int NJ = (CHUNKS + 3) / 4;  // instructions per loading wavefront and stage
+
+  // Streaming form: the byte offset of each of this lane's slots from the
+  // tile's first element (row / column mn0 and k0 of the operand) is computed
+  // once, so a stage fill costs one 64-bit add and one M0 update per
+  // instruction; ~0u marks a slot with nothing to load (MN-major row
+  // padding, or past the tile). Only for stages that lie inside K; rows or
+  // columns past MN read the last one instead (the products of those never
+  // reach a stored output).
+  uint32_t off[NJ];
+  __device__ __forceinline__ void init(int64_t ld, int64_t mn0, int64_t MN, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int o = (wave + 4 * q) * 1024 + lane * 16;
+      if (KMAJ) {
+        const int r = o / (BK * 2), pg = (o % (BK * 2)) / 16;
+        const int g = pg ^ ((r / Geo::RPS) & (Geo::G - 1));
+        const int64_t mn = min(mn0 + r, MN - 1);
+        off[q] = o < BYTES ? (uint32_t)(((mn - mn0) * ld + g * 8) * 2) : ~0u;
+      } else {
+        const int r = o / (Geo::PITCH * 2), cb = o % (Geo::PITCH * 2);
+        const int64_t mn = min(mn0 + cb / 2, MN - 8);
+        off[q] = (o < BYTES && cb < ROWS * 2) ? (uint32_t)((r * ld + (mn - mn0)) * 2) : ~0u;
+      }
+    }
+  }
+  // tile = the operand at (mn0, k0): p + mn0 * ld + k0 (K-major) or
+  // p + k0 * ld + mn0 (MN-major)
+  __device__ __forceinline__ void issue_fast(const bf16* tile, bf16* lds, int wave) const {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int c = wave + 4 * q;
+      if (c < CHUNKS && off[q] != ~0u)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(reinterpret_cast<const char*>(tile) + off[q]),
+            (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(lds) + c * 1024), 16,
+            0, 0);
+    }
+  }
   __device__ __forceinline__ static void issue(const bf16* __restrict__ p, int64_t ld, int64_t mn0,
                                                int64_t MN, int64_t k0, int64_t khi, bf16* lds,
                                                int wave, int lane) {
