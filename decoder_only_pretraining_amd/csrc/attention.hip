@@ -756,11 +756,7 @@ struct Dual {
       const bool ok = row0 + t < rows_end;
       const bf16* src = ok ? p + (row0 + t) * ld + gi * 8
                            : reinterpret_cast<const bf16*>(g_zero_page) + (lane & 15) * 8;
-      if (gi < D / 8)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)src,
-            (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(lds) + c * 1024), 16,
-            0, 0);
+      if (gi < D / 8) lds_fill16(src, lds_addr(lds) + c * 1024);
     }
   }
   // 32 rows from row0, contraction slice kc (lane l: row row0 + l%32,
@@ -797,8 +793,7 @@ __device__ __forceinline__ void stats_issue(const float* __restrict__ lse2,
                                             float* st, int lane) {
   if (lane < 32) {
     const float* src = (lane < 16 ? lse2 : delta) + row + (lane & 15) * 4;
-    __builtin_amdgcn_global_load_lds((const void*)src,
-                                     (__attribute__((address_space(3))) void*)st, 16, 0, 0);
+    lds_fill16(src, lds_addr(st));
   }
 }
 

@@ -85,6 +85,32 @@ __device__ __forceinline__ float fp8_scale(uint32_t bits, float fmax) {
   return (a > 0.0f && a <= 3.402823466e38f) ? __fdiv_rn(fmax, a) : 1.0f;
 }
 
+// Direct global->LDS copy, 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's bytes land at LDS byte address lds + 16 l, lds being uniform over the
+// wavefront (it goes to M0). Written as inline assembly, not with the
+// builtin: for the builtin the compiler records an LDS write that it cannot
+// tell apart from the buffer being read, and puts a wait for every fill in
+// flight (vmcnt(0)) before the next LDS read, which serialises the prefetch
+// of the next stage with the reads of the current one. Here the compiler
+// sees no LDS write, so the caller waits (vmcnt) and synchronises before the
+// filled buffer is read. The copy has no register result.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// source: one 64-bit address per lane
+__device__ __forceinline__ void lds_fill16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// source: a base address uniform over the wavefront plus a 32-bit byte
+// offset per lane
+__device__ __forceinline__ void lds_fill16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
 // Output row (within a 32x32 tile) of accumulator element e for lane l.
 __device__ __forceinline__ int acc_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
 

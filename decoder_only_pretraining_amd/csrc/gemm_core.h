@@ -169,11 +169,7 @@ struct DirectLoader {
 #pragma unroll
     for (int q = 0; q < NJ; ++q) {
       const int c = wave + 4 * q;
-      if (c < CHUNKS && off[q] != ~0u)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(reinterpret_cast<const char*>(tile) + off[q]),
-            (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(lds) + c * 1024), 16,
-            0, 0);
+      if (c < CHUNKS && off[q] != ~0u) lds_fill16(tile, off[q], lds_addr(lds) + c * 1024);
     }
   }
   __device__ __forceinline__ static void issue(const bf16* __restrict__ p, int64_t ld, int64_t mn0,
@@ -198,11 +194,7 @@ struct DirectLoader {
       const bool ok = (mn < MN) && (k < khi);
       const bf16* src = ok ? (KMAJ ? p + mn * ld + k : p + k * ld + mn)
                            : reinterpret_cast<const bf16*>(g_zero_page) + (lane & 15) * 8;
-      if (slot)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)src,
-            (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(lds) + c * 1024), 16,
-            0, 0);
+      if (slot) lds_fill16(src, lds_addr(lds) + c * 1024);
     }
   }
 };
@@ -481,81 +473,99 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   // then write it back with 4-column vectors; all LDS reads of a slab are
   // issued before its first global store.
   // Epilogues that read another operand (residual, activation, old value)
-  // load it in half-slab chunks, one chunk ahead of its use, so the load
-  // latency overlaps the previous chunk's work.
+  // load a whole slab of it at a time, a slab ahead where the registers
+  // allow (two slab buffers of at most 64 VGPRs), else right after the
+  // current slab's values are stored: the epilogue's time goes to the
+  // latency of these loads, and a wavefront has only a few of them in
+  // flight otherwise.
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SP;
   constexpr bool kAux = !std::is_same<typename EP::Aux, NoAux>::value;
   constexpr int NVS = 32 * WN / 4 / 64;  // 4-column vectors per lane per slab
-  constexpr int NCH = 2, CV = NVS / NCH;  // aux chunks per slab, vectors per chunk
-  static_assert(NVS % NCH == 0, "aux chunks must tile the slab");
+  constexpr int NCH = 2, CV = NVS / NCH;  // staged values are read in half slabs
+  static_assert(NVS % NCH == 0, "value chunks must tile the slab");
   using AuxT = typename EP::Aux;
-  AuxT ax[kAux ? 2 : 1][kAux ? CV : 1];
-  auto load_aux = [&](int i, int c, AuxT* dst) {
-#pragma unroll
-    for (int t = 0; t < CV; ++t) {
-      const int v = lane + 64 * (c * CV + t);
-      const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
-      const int64_t m = mw + i * 32 + r, n = nw + c4;
-      if (m < M && n < N) dst[t] = ep.aux(m, n, (int)min<int64_t>(4, N - n));
-    }
-  };
-  if constexpr (kAux) load_aux(0, 0, ax[0]);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = acc_row(e, lane);
-      const int64_t m = mw + i * 32 + r;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = nw + j * 32 + (lane & 31);
-        float x = acc[i][j][e];
-        if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(n)];
-        stage[r * SP + j * 32 + (lane & 31)] = ep.value(m, n, x);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront
-    __builtin_amdgcn_wave_barrier();
-    if constexpr (kAux) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int g = i * NCH + c;  // chunk number within the tile
-        if (c + 1 < NCH) load_aux(i, c + 1, ax[(g + 1) & 1]);
-        else if (i + 1 < TM) load_aux(i + 1, 0, ax[(g + 1) & 1]);
-        f32x4 val[CV];
-#pragma unroll
-        for (int t = 0; t < CV; ++t) {
-          const int v = lane + 64 * (c * CV + t);
-          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
-          val[t] = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
-        }
-#pragma unroll
-        for (int t = 0; t < CV; ++t) {
-          const int v = lane + 64 * (c * CV + t);
-          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
-          const int64_t m = mw + i * 32 + r, n = nw + c4;
-          if (m < M && n < N) ep.store4a(m, n, val[t], (int)min<int64_t>(4, N - n), ax[g & 1][t]);
-        }
-      }
-    } else {
-      f32x4 val[NVS];
-#pragma unroll
-      for (int t = 0; t < NVS; ++t) {
-        const int v = lane + 64 * t;
-        const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
-        val[t] = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
-      }
+  constexpr int AUXR = kAux ? (int)(sizeof(AuxT) / 4) : 0;  // VGPRs per aux vector
+  constexpr int NB = (kAux && 2 * NVS * AUXR <= 64 && TM > 1) ? 2 : 1;
+  // A tile wholly inside C takes the branch-free form: every 4-column vector
+  // is whole and in range (per-vector range checks put each aux load on its
+  // own branch, and the loads then issue one at a time).
+  auto epilogue = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    auto in_range = [&](int64_t m, int64_t n) { return FULL || (m < M && n < N); };
+    auto count = [&](int64_t n) { return FULL ? 4 : (int)min<int64_t>(4, N - n); };
+    AuxT ax[kAux ? NB : 1][kAux ? NVS : 1];
+    auto load_aux = [&](int i, AuxT* dst) {
 #pragma unroll
       for (int t = 0; t < NVS; ++t) {
         const int v = lane + 64 * t;
         const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
         const int64_t m = mw + i * 32 + r, n = nw + c4;
-        if (m < M && n < N) ep.store4(m, n, val[t], (int)min<int64_t>(4, N - n));
+        if (in_range(m, n)) dst[t] = ep.aux(m, n, count(n));
       }
+    };
+    if constexpr (kAux) load_aux(0, ax[0]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (kAux && NB == 2)
+        if (i + 1 < TM) load_aux(i + 1, ax[(i + 1) % NB]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = acc_row(e, lane);
+        const int64_t m = mw + i * 32 + r;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t n = nw + j * 32 + (lane & 31);
+          float x = acc[i][j][e];
+          if constexpr (F8) x *= fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(n)];
+          stage[r * SP + j * 32 + (lane & 31)] = ep.value(m, n, x);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront
+      __builtin_amdgcn_wave_barrier();
+      if constexpr (kAux) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          f32x4 val[CV];
+#pragma unroll
+          for (int t = 0; t < CV; ++t) {
+            const int v = lane + 64 * (c * CV + t);
+            const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+            val[t] = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
+          }
+#pragma unroll
+          for (int t = 0; t < CV; ++t) {
+            const int v = lane + 64 * (c * CV + t);
+            const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+            const int64_t m = mw + i * 32 + r, n = nw + c4;
+            if (in_range(m, n)) ep.store4a(m, n, val[t], count(n), ax[i % NB][c * CV + t]);
+          }
+        }
+        if constexpr (NB == 1)
+          if (i + 1 < TM) load_aux(i + 1, ax[0]);
+      } else {
+        f32x4 val[NVS];
+#pragma unroll
+        for (int t = 0; t < NVS; ++t) {
+          const int v = lane + 64 * t;
+          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+          val[t] = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
+        }
+#pragma unroll
+        for (int t = 0; t < NVS; ++t) {
+          const int v = lane + 64 * t;
+          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+          const int64_t m = mw + i * 32 + r, n = nw + c4;
+          if (in_range(m, n)) ep.store4(m, n, val[t], count(n));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-  }
+  };
+  if (m0 + BM <= M && n0 + BN <= N)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 }  // namespace gk
