@@ -759,6 +759,31 @@ struct Dual {
       if (gi < D / 8) lds_fill16(src, lds_addr(lds) + c * 1024);
     }
   }
+  // Streaming form for tiles wholly inside the matrix: this lane's byte
+  // offset from the tile's first element for each of its chunks (~0u for a
+  // slot in the row padding), computed once; a fill is then one load per
+  // chunk from a wavefront-uniform base.
+  static constexpr int NJ = CHUNKS / 4;
+  struct Offs {
+    uint32_t o[NJ];
+  };
+  __device__ __forceinline__ static Offs offsets(int64_t ld, int wave, int lane) {
+    Offs f;
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int o = (wave + 4 * q) * 1024 + lane * 16;
+      const int t = o / (PITCH * 2), pg = (o % (PITCH * 2)) / 16;
+      const int gi = pg ^ ((t >> 2) & 3);
+      f.o[q] = gi < D / 8 ? (uint32_t)((t * ld + gi * 8) * 2) : ~0u;
+    }
+    return f;
+  }
+  __device__ __forceinline__ static void issue_fast(const bf16* tile, const Offs& f, bf16* lds,
+                                                    int wave) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q)
+      if (f.o[q] != ~0u) lds_fill16(tile, f.o[q], lds_addr(lds) + (wave + 4 * q) * 1024);
+  }
   // 32 rows from row0, contraction slice kc (lane l: row row0 + l%32,
   // columns 16 kc + 8 (l/32) .. +7)
   __device__ __forceinline__ static void row_frag(Frag<bf16>& f, const bf16* lds, int row0, int kc,
@@ -801,7 +826,7 @@ __device__ __forceinline__ void stats_issue(const float* __restrict__ lse2,
 // wavefront, K and V rows held as fragments) and walks the (query head of
 // the group, 64-query tile) steps that see them; Q, dO and the softmax
 // statistics stream through three LDS stages, two steps ahead.
-template <int D, int NW>
+template <int D, int NW, bool ALIGNED>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
     const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
@@ -813,7 +838,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Qs[S][DT::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 dOs[S][DT::ELEMS];
   __shared__ __attribute__((aligned(16))) float st[S][2 * BQ2];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches and fill bases scalar
   const bool loader = wv < 4;
   const int L = blockIdx.x;
   const int kt = L / (Hk * nb);  // early keys are seen by the most queries: first
@@ -839,11 +865,22 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
   const int q_hi = full ? T_ : min(T_, s0 + BK2 + W);  // exclusive
   const int nq = (q_hi - q_first + BQ2 - 1) / BQ2;
   const int nstep = G * nq;
+  // T a multiple of 64: every query tile lies inside the sequence
+  typename DT::Offs oq, od;
+  if (ALIGNED && loader) {
+    oq = DT::offsets(Qkv, wv, lane);
+    od = DT::offsets(Cq, wv, lane);
+  }
   auto issue = [&](int step) {
     if (!loader) return;
     const int h = j * G + step / nq, t0 = q_first + (step % nq) * BQ2;
-    DT::issue(qkv + h * D, Qkv, rb + t0, rb + T_, Qs[step % S], wv, lane);
-    DT::issue(gO + h * D, Cq, rb + t0, rb + T_, dOs[step % S], wv, lane);
+    if constexpr (ALIGNED) {
+      DT::issue_fast(qkv + (rb + t0) * Qkv + h * D, oq, Qs[step % S], wv);
+      DT::issue_fast(gO + (rb + t0) * Cq + h * D, od, dOs[step % S], wv);
+    } else {
+      DT::issue(qkv + h * D, Qkv, rb + t0, rb + T_, Qs[step % S], wv, lane);
+      DT::issue(gO + h * D, Cq, rb + t0, rb + T_, dOs[step % S], wv, lane);
+    }
     if (wv == 0) stats_issue(lse2, delta, ((int64_t)b * H + h) * T_ + t0, st[step % S], lane);
   };
   // this wavefront's loads of one step
@@ -862,73 +899,102 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
     constexpr int CUR = decltype(cur_c)::value;
     const int t0 = q_first + (step % nq) * BQ2;
     if (step + S - 1 < nstep) issue(step + S - 1);
-    if (sw < T_) {
+    // P and dS of the 32-query block tb from its scores and dP (in place)
+    auto softgrad = [&](f32x16& sa, f32x16& dp, int tb) {
+      // accumulator rows t = t0 + 32 tb + 8 (e/4) + 4 hi + e%4: four
+      // consecutive rows per group g = e/4, so their statistics load as one
+      // vector
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int tlo = t0 + tb * 32;
-        // any (query, key) pair of this 32x32 block visible?
-        if (!(tlo < T_ && tlo + 31 >= sw && (full || tlo - (sw + 31) <= W))) continue;
-        const bool interior = tlo >= sw + 31 && (full || tlo + 31 - sw <= W) && tlo + 31 < T_;
-        f32x16 sa, dp;
+      for (int g = 0; g < 4; ++g) {
+        const int tl = tb * 32 + g * 8 + hi * 4;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&st[CUR][tl]);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&st[CUR][BQ2 + tl]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          const float p = exp2_fast(fmaf(sa[e], c2, -lv[r]));
+          sa[e] = p;
+          dp[e] = p * (dp[e] - dv4[r]);
+        }
+      }
+    };
+    // dV += P^T dO and dK += dS^T Q over the block's 32 queries
+    auto accumulate = [&](const f32x16& sa, const f32x16& dp, int tb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag<bf16> pf, dsf;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          frag_set(pf, jj, sa[8 * c + jj]);
+          frag_set(dsf, jj, dp[8 * c + jj]);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          Frag<bf16> doT, qT;
+          DT::tr_frag(doT, dOs[CUR], tb * 32 + 16 * c, db * 32, lane);
+          DT::tr_frag(qT, Qs[CUR], tb * 32 + 16 * c, db * 32, lane);
+          mfma(dv[db], doT, pf);
+          mfma(dk[db], qT, dsf);
+        }
+      }
+    };
+    // any (query, key) pair of the step visible to this wavefront's keys?
+    if (sw < T_ && t0 + 63 >= sw && (full || t0 - (sw + 31) <= W)) {
+      // The scores and dP of the step's two 32-query blocks are formed
+      // together: four independent accumulation chains, fragments read one
+      // k-slice ahead. A block on the causal diagonal or the window edge is
+      // masked on its own branch (a block with nothing visible is computed
+      // and masked whole: it occurs only next to the diagonal or the edge).
+      f32x16 sa[2], dp[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          sa[e] = 0.0f;
-          dp[e] = 0.0f;
+          sa[tb][e] = 0.0f;
+          dp[tb][e] = 0.0f;
         }
+      Frag<bf16> qa[2][2], da[2][2];
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          Frag<bf16> qa, da;
-          DT::row_frag(qa, Qs[CUR], tb * 32, kc, lane);
-          DT::row_frag(da, dOs[CUR], tb * 32, kc, lane);
-          mfma(sa, qa, kf[kc]);
-          mfma(dp, da, vf[kc]);
-        }
-        // accumulator rows t = tlo + 8 (e/4) + 4 hi + e%4: four consecutive
-        // rows per group g = e/4, so their statistics load as one vector
+      for (int tb = 0; tb < 2; ++tb) {
+        DT::row_frag(qa[0][tb], Qs[CUR], tb * 32, 0, lane);
+        DT::row_frag(da[0][tb], dOs[CUR], tb * 32, 0, lane);
+      }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int tl = tb * 32 + g * 8 + hi * 4;
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(&st[CUR][tl]);
-          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&st[CUR][BQ2 + tl]);
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const int p = kc & 1;
+        if (kc + 1 < D / 16) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * g + r;
-            const float p = exp2_fast(fmaf(sa[e], c2, -lv[r]));
-            sa[e] = p;
-            dp[e] = p * (dp[e] - dv4[r]);
+          for (int tb = 0; tb < 2; ++tb) {
+            DT::row_frag(qa[p ^ 1][tb], Qs[CUR], tb * 32, kc + 1, lane);
+            DT::row_frag(da[p ^ 1][tb], dOs[CUR], tb * 32, kc + 1, lane);
           }
         }
-        if (!interior) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          mfma(sa[tb], qa[p][tb], kf[kc]);
+          mfma(dp[tb], da[p][tb], vf[kc]);
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        softgrad(sa[tb], dp[tb], tb);
+        const int tlo = t0 + tb * 32;
+        if (!(tlo >= sw + 31 && (full || tlo + 31 - sw <= W) && tlo + 31 < T_)) {
           asm volatile("" ::: "memory");  // keep the mask on its own branch
-          // query tq = t0 + tl + r sees key s iff tq < T and 0 <= tq - s <= W
-          const int u = t0 + tb * 32 + 4 * hi - s;
+          // query tq = tlo + 8 (e/4) + 4 hi + e%4 sees key s iff tq < T and
+          // 0 <= tq - s <= W
+          const int u = tlo + 4 * hi - s;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int r = (e >> 2) * 8 + (e & 3);
-            const bool vis = (unsigned)(u + r) <= wmax && t0 + tb * 32 + 4 * hi + r < T_;
+            const bool vis = (unsigned)(u + r) <= wmax && tlo + 4 * hi + r < T_;
             if (!vis) {
-              sa[e] = 0.0f;
-              dp[e] = 0.0f;
+              sa[tb][e] = 0.0f;
+              dp[tb][e] = 0.0f;
             }
           }
         }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          Frag<bf16> pf, dsf;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            frag_set(pf, jj, sa[8 * c + jj]);
-            frag_set(dsf, jj, dp[8 * c + jj]);
-          }
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            Frag<bf16> doT, qT;
-            DT::tr_frag(doT, dOs[CUR], tb * 32 + 16 * c, db * 32, lane);
-            DT::tr_frag(qT, Qs[CUR], tb * 32 + 16 * c, db * 32, lane);
-            mfma(dv[db], doT, pf);
-            mfma(dk[db], qT, dsf);
-          }
-        }
+        accumulate(sa[tb], dp[tb], tb);
       }
     }
     if (step + S - 1 < nstep) wait_all_but_one();
@@ -961,7 +1027,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
 // wavefront, Q and dO rows held as fragments) and walks the visible 64-key
 // tiles; K (read by rows and transposed) and V (read by rows) stream
 // through three LDS stages, two tiles ahead.
-template <int D, int NW>
+template <int D, int NW, bool ALIGNED>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
     const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
@@ -1003,11 +1069,23 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
   const int first = ((full ? 0 : max(0, t0 - W)) / BKV) * BKV;
   const int ntile = (min(T_, t0 + BQ) - first + BKV - 1) / BKV;
   const int w_lo = full ? 0 : max(0, tw - W), w_hi = min(T_, tw + 32);
+  // T a multiple of 64: every key tile lies inside the sequence
+  typename DK::Offs ok;
+  LV lv;
+  if (ALIGNED && loader) {
+    ok = DK::offsets(Qkv, wv, lane);
+    lv.init(Qkv, 0, 1 << 30, wv, lane);
+  }
   auto issue = [&](int it) {
     if (!loader) return;
     const int64_t r0 = rb + first + (int64_t)it * BKV;
-    DK::issue(kbase, Qkv, r0, rb + T_, Ks[it % S], wv, lane);
-    LV::issue(vbase, Qkv, r0, rb + T_, 0, D, Vs[it % S], wv, lane);
+    if constexpr (ALIGNED) {
+      DK::issue_fast(kbase + r0 * Qkv, ok, Ks[it % S], wv);
+      lv.issue_fast(vbase + r0 * Qkv, Vs[it % S], wv);
+    } else {
+      DK::issue(kbase, Qkv, r0, rb + T_, Ks[it % S], wv, lane);
+      LV::issue(vbase, Qkv, r0, rb + T_, 0, D, Vs[it % S], wv, lane);
+    }
   };
 #pragma unroll
   for (int it = 0; it < S - 1; ++it)
@@ -1116,14 +1194,21 @@ void bwd(const gpt::Dims& d, bool full, const void* qkv, const void* gO, const f
   if constexpr (sizeof(T) == 2) {
     constexpr int NW = 4;  // one wavefront per SIMD: the backward needs > 256 registers
     const int nkt = (d.T + 32 * NW - 1) / (32 * NW), nq = (d.T + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((attn_bwd_kv_tiled_kernel<D, NW>), dim3((unsigned)(nkt * d.Hk * d.B)),
-                       dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
-                       static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
-                       d.Hk, d.W, full ? 1 : 0, c2, scale, nkt, d.B);
-    hipLaunchKernelGGL((attn_bwd_q_tiled_kernel<D, NW>), dim3((unsigned)(nq * d.H * d.B)),
-                       dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
-                       static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
-                       d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B);
+#define GPT_ATTN_BWD(AL)                                                                          \
+  hipLaunchKernelGGL((attn_bwd_kv_tiled_kernel<D, NW, AL>), dim3((unsigned)(nkt * d.Hk * d.B)),    \
+                     dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),                           \
+                     static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H, \
+                     d.Hk, d.W, full ? 1 : 0, c2, scale, nkt, d.B);                                \
+  hipLaunchKernelGGL((attn_bwd_q_tiled_kernel<D, NW, AL>), dim3((unsigned)(nq * d.H * d.B)),       \
+                     dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),                           \
+                     static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H, \
+                     d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B)
+    if (d.T % 64 == 0) {
+      GPT_ATTN_BWD(true);
+    } else {
+      GPT_ATTN_BWD(false);
+    }
+#undef GPT_ATTN_BWD
     return;
   }
   dim3 gkv((unsigned)((d.T + 127) / 128), d.Hk, d.B);
