@@ -784,6 +784,43 @@ struct Dual {
     for (int q = 0; q < NJ; ++q)
       if (f.o[q] != ~0u) lds_fill16(tile, f.o[q], lds_addr(lds) + (wave + 4 * q) * 1024);
   }
+  // Lane offsets (elements) of the two read patterns. For rows row0 a
+  // multiple of 16 the permutation (t >> 2) & 3 depends on the lane alone,
+  // and it changes only the low two bits of a granule index, so a read's
+  // address is one of two lane offsets plus a constant: row fragments use
+  // r[kc & 1] + 32 (kc / 2) + row0 PITCH, transposed fragments (kbase a
+  // multiple of 16, col0 of 32) tr[0 or 1] + kbase PITCH + col0.
+  struct Lane {
+    int r[2], tr[2];
+  };
+  __device__ __forceinline__ static Lane lane_offsets(int lane) {
+    Lane q;
+    q.r[0] = off(lane & 31, (lane >> 5) * 8);
+    q.r[1] = off(lane & 31, 16 + (lane >> 5) * 8);
+    const int g16 = lane >> 4, L = lane & 15;
+    const int k0 = (g16 >> 1) * 4 + (L >> 2), m = (g16 & 1) * 16 + (L & 3) * 4;
+    q.tr[0] = off(k0, m);
+    q.tr[1] = off(k0 + 8, m);
+    return q;
+  }
+  __device__ __forceinline__ static void row_frag(Frag<bf16>& f, const bf16* lds, const Lane& q,
+                                                  int row0, int kc) {
+    f.v = *reinterpret_cast<const bf16x8*>(lds + q.r[kc & 1] + (kc >> 1) * 32 + row0 * PITCH);
+  }
+  __device__ __forceinline__ static void tr_frag(Frag<bf16>& f, const bf16* lds, const Lane& q,
+                                                 int kbase, int col0) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    union {
+      struct { v4i16 a, b; } s;
+      bf16x8 v;
+    } u;
+    u.s.a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(lds + q.tr[0] + kbase * PITCH + col0));
+    u.s.b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(lds + q.tr[1] + kbase * PITCH + col0));
+    f.v = u.v;
+  }
   // 32 rows from row0, contraction slice kc (lane l: row row0 + l%32,
   // columns 16 kc + 8 (l/32) .. +7)
   __device__ __forceinline__ static void row_frag(Frag<bf16>& f, const bf16* lds, int row0, int kc,
@@ -849,6 +886,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
   const int64_t rb = (int64_t)b * T_;
   const int s0 = kt * BK2, sw = s0 + wv * 32, s = sw + (lane & 31);
 
+  const typename DT::Lane lo = DT::lane_offsets(lane);
   Frag<bf16> kf[D / 16], vf[D / 16];
   load_row_frags<bf16, D>(kf, qkv + (rb + s) * Qkv + (H + j) * D, s < T_, lane);
   load_row_frags<bf16, D>(vf, qkv + (rb + s) * Qkv + (H + Hk + j) * D, s < T_, lane);
@@ -931,8 +969,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           Frag<bf16> doT, qT;
-          DT::tr_frag(doT, dOs[CUR], tb * 32 + 16 * c, db * 32, lane);
-          DT::tr_frag(qT, Qs[CUR], tb * 32 + 16 * c, db * 32, lane);
+          DT::tr_frag(doT, dOs[CUR], lo, tb * 32 + 16 * c, db * 32);
+          DT::tr_frag(qT, Qs[CUR], lo, tb * 32 + 16 * c, db * 32);
           mfma(dv[db], doT, pf);
           mfma(dk[db], qT, dsf);
         }
@@ -956,8 +994,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
       Frag<bf16> qa[2][2], da[2][2];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        DT::row_frag(qa[0][tb], Qs[CUR], tb * 32, 0, lane);
-        DT::row_frag(da[0][tb], dOs[CUR], tb * 32, 0, lane);
+        DT::row_frag(qa[0][tb], Qs[CUR], lo, tb * 32, 0);
+        DT::row_frag(da[0][tb], dOs[CUR], lo, tb * 32, 0);
       }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
@@ -965,8 +1003,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
         if (kc + 1 < D / 16) {
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
-            DT::row_frag(qa[p ^ 1][tb], Qs[CUR], tb * 32, kc + 1, lane);
-            DT::row_frag(da[p ^ 1][tb], dOs[CUR], tb * 32, kc + 1, lane);
+            DT::row_frag(qa[p ^ 1][tb], Qs[CUR], lo, tb * 32, kc + 1);
+            DT::row_frag(da[p ^ 1][tb], dOs[CUR], lo, tb * 32, kc + 1);
           }
         }
 #pragma unroll
@@ -1055,6 +1093,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
   const bf16* kbase = qkv + (H + j) * D;
   const bf16* vbase = qkv + (H + Hk + j) * D;
 
+  const typename DK::Lane lo = DK::lane_offsets(lane);
   Frag<bf16> qf[D / 16], df[D / 16];
   load_row_frags<bf16, D>(qf, qkv + (rb + t) * Qkv + h * D, tv, lane);
   load_row_frags<bf16, D>(df, gO + (rb + t) * Cq + h * D, tv, lane);
@@ -1099,26 +1138,45 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
     if (it + S - 1 < ntile) issue(it + S - 1);
     if (tw < T_ && s0 < w_hi && s0 + BKV > w_lo) {
       const bool interior = (s0 + BKV - 1 <= tw) && (full || tw + 31 - s0 <= W);
+      // The scores and dP of the tile's two 32-key blocks are formed
+      // together: four independent accumulation chains, fragments read one
+      // k-slice ahead.
+      f32x16 sa[2], dp[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sa[sb][e] = 0.0f;
+          dp[sb][e] = 0.0f;
+        }
+      Frag<bf16> ka[2][2], va[2][2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        f32x16 sa, dp;
+        DK::row_frag(ka[0][sb], Ks[CUR], lo, sb * 32, 0);
+        read_frag<BKV, D, true>(va[0][sb], Vs[CUR], sb * 32, 0, lane);
+      }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sa[e] = 0.0f;
-          dp[e] = 0.0f;
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const int p = kc & 1;
+        if (kc + 1 < D / 16) {
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            DK::row_frag(ka[p ^ 1][sb], Ks[CUR], lo, sb * 32, kc + 1);
+            read_frag<BKV, D, true>(va[p ^ 1][sb], Vs[CUR], sb * 32, kc + 1, lane);
+          }
         }
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          Frag<bf16> ka, va;
-          DK::row_frag(ka, Ks[CUR], sb * 32, kc, lane);
-          read_frag<BKV, D, true>(va, Vs[CUR], sb * 32, kc, lane);
-          mfma(sa, ka, qf[kc]);
-          mfma(dp, va, df[kc]);
+        for (int sb = 0; sb < 2; ++sb) {
+          mfma(sa[sb], ka[p][sb], qf[kc]);
+          mfma(dp[sb], va[p][sb], df[kc]);
         }
+      }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2_fast(fmaf(sa[e], c2, -lt));
-          dp[e] = p * (dp[e] - dt);
+          const float p = exp2_fast(fmaf(sa[sb][e], c2, -lt));
+          dp[sb][e] = p * (dp[sb][e] - dt);
         }
         if (!interior) {
           asm volatile("" ::: "memory");  // keep the mask on its own branch
@@ -1126,18 +1184,18 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int r = (e >> 2) * 8 + (e & 3);
-            if ((unsigned)(u - r) > wmax) dp[e] = 0.0f;
+            if ((unsigned)(u - r) > wmax) dp[sb][e] = 0.0f;
           }
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           Frag<bf16> dsf;
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) frag_set(dsf, jj, dp[8 * c + jj]);
+          for (int jj = 0; jj < 8; ++jj) frag_set(dsf, jj, dp[sb][8 * c + jj]);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             Frag<bf16> kT;
-            DK::tr_frag(kT, Ks[CUR], sb * 32 + 16 * c, db * 32, lane);
+            DK::tr_frag(kT, Ks[CUR], lo, sb * 32 + 16 * c, db * 32);
             mfma(dq[db], kT, dsf);
           }
         }

@@ -726,8 +726,11 @@ void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, cons
 }
 
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                   void* C, hipStream_t s) {
-  if (d.bf16)
+                   void* C, hipStream_t s, const void* Bt) {
+  if (d.bf16 && Bt)
+    run_bf16<true, true>(pick_tile(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
+                         mk_store<bf16>(C, N), s);
+  else if (d.bf16)
     run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
                           mk_store<bf16>(C, N), s);
   else
@@ -736,8 +739,11 @@ void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const 
 }
 
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                 float* C, hipStream_t s) {
-  if (d.bf16)
+                 float* C, hipStream_t s, const void* Bt) {
+  if (d.bf16 && Bt)
+    run_bf16<true, true>(pick_tile(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
+                         mk_f32(C, N, 0), s);
+  else if (d.bf16)
     run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
                           mk_f32(C, N, 0), s);
   else
@@ -745,8 +751,11 @@ void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const vo
 }
 
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                      const void* U, void* C, hipStream_t s) {
-  if (d.bf16)
+                      const void* U, void* C, hipStream_t s, const void* Bt) {
+  if (d.bf16 && Bt)
+    run_bf16<true, true>(pick_tile(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
+                         mk_relu2bwd<bf16>(U, C, N), s);
+  else if (d.bf16)
     run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
                           mk_relu2bwd<bf16>(U, C, N), s);
   else
@@ -766,17 +775,26 @@ int64_t part_bytes_nn_splitk(const Dims& d, int64_t M, int64_t N, int64_t K) {
 
 SplitSum gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A,
                             const void* B, float* C, float* part, int64_t part_cap,
-                            hipStream_t s) {
+                            hipStream_t s, const void* Bt) {
   if (d.bf16) {
     const Tile t = pick_tile(M, N, K);
     const KSplit ks = nn_split(M, N, K);
-    if (ks.splits == 1) {
-      run_bf16<true, false>(t, A, K, B, N, M, N, K, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
-      return SplitSum{};
+    const int64_t chunk = ks.splits == 1 ? K : ks.chunk;
+    if (ks.splits > 1) check_part(part_bytes_nn_splitk(d, M, N, K), part_cap);
+    if (Bt) {
+      if (ks.splits == 1)
+        run_bf16<true, true>(t, A, K, Bt, K, M, N, K, chunk, PreId{}, PreId{}, mk_f32(C, N, 0), s);
+      else
+        run_bf16<true, true>(t, A, K, Bt, K, M, N, K, chunk, PreId{}, PreId{}, mk_part(part, M, N),
+                             s);
+    } else {
+      if (ks.splits == 1)
+        run_bf16<true, false>(t, A, K, B, N, M, N, K, chunk, PreId{}, PreId{}, mk_f32(C, N, 0), s);
+      else
+        run_bf16<true, false>(t, A, K, B, N, M, N, K, chunk, PreId{}, PreId{}, mk_part(part, M, N),
+                              s);
     }
-    check_part(part_bytes_nn_splitk(d, M, N, K), part_cap);
-    run_bf16<true, false>(t, A, K, B, N, M, N, K, ks.chunk, PreId{}, PreId{}, mk_part(part, M, N),
-                          s);
+    if (ks.splits == 1) return SplitSum{};
     return SplitSum{part, ks.splits, M, N, C, false};
   }
   run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);

@@ -188,6 +188,7 @@ Plan make_plan(const Dims& d) {
     }
   }
   p.wc = take(d.bf16 ? (size_t)n_elems * 2 : 0);
+  p.wct = take(d.bf16 ? (size_t)n_elems * 2 : 0);
   p.rope = take((size_t)d.T * d.D * 4);
   p.x = take((size_t)(d.L + 1) * N * d.C * 4);
   p.xin = take(N * d.C * 4);
@@ -326,14 +327,25 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   // compute-dtype weights: a mirror of params with the same element offsets
   const char* wc = d.bf16 ? W + P.wc : reinterpret_cast<const char*>(params);
   auto wmat = [&](int64_t off) { return static_cast<const void*>(wc + off * A); };
+  // bf16: transposed copies of the linear weights, so the input-gradient
+  // products run with both operands K-major (nullptr: not kept)
+  auto wmatT = [&](int64_t off) -> const void* {
+    return d.bf16 ? static_cast<const void*>(W + P.wct + off * 2) : nullptr;
+  };
   if (d.bf16) {
     std::vector<CastSeg> segs;
-    for (int l = 0; l < d.L; ++l) {
-      if (!d.fp8) segs.push_back({F.q[l], F.mp[l] + (int64_t)d.C * d.F - F.q[l]});  // q k v o fc mp
+    for (int l = 0; l < d.L; ++l)
       if (F.veg[l] >= 0) segs.push_back({F.veg[l], (int64_t)d.Hk * d.C});
+    if (!segs.empty()) launch_cast(params, W + P.wc, segs, s);
+    if (!d.fp8) {
+      std::vector<int64_t> q(d.L), o(d.L), fc(d.L), mp(d.L);
+      for (int l = 0; l < d.L; ++l) q[l] = F.q[l], o[l] = F.o[l], fc[l] = F.fc[l], mp[l] = F.mp[l];
+      launch_cast_t(params, W + P.wc, W + P.wct, q, d.Qkv, d.C, s);
+      launch_cast_t(params, W + P.wc, W + P.wct, o, d.C, d.Cq, s);
+      launch_cast_t(params, W + P.wc, W + P.wct, fc, d.F, d.C, s);
+      launch_cast_t(params, W + P.wc, W + P.wct, mp, d.C, d.F, s);
     }
-    segs.push_back({F.lm, (int64_t)d.V * d.C});
-    launch_cast(params, W + P.wc, segs, s);
+    launch_cast_t(params, W + P.wc, W + P.wct, {F.lm}, d.V, d.C, s);
   }
   float* cs = reinterpret_cast<float*>(W + P.rope);
   launch_rope_table(cs, d.T, d.D, d.theta, s);
@@ -527,7 +539,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     const int64_t pcap = P.part_bytes;
     SplitSum ssum;  // split-K partials still to be added into their gradient
     auto sum_splits = [&] { site("splitk.sum", s, [&] { splitk_sum(ssum, s); }); };
-    site("gemm.lm.dgrad", s, [&] { ssum = gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, part, pcap, s); });
+    site("gemm.lm.dgrad", s, [&] { ssum = gemm_nn_f32_splitk(d, N, d.C, d.V, logits, wmat(F.lm), gtmp, part, pcap, s, wmatT(F.lm)); });
     sum_splits();
     site("gemm.lm.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, part, pcap, s); });
     sum_splits();
@@ -576,10 +588,10 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         });
         sum_splits();
       } else {
-        site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s); });
+        site("gemm.mp.dgrad", s, [&] { gemm_nn_relu2bwd(d, N, d.F, d.C, gxc, wmat(F.mp[l]), u, gu, s, wmatT(F.mp[l])); });
         site("gemm.mp.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.C, d.F, N, gxc, u, grads + F.mp[l], acc, part, pcap, s); });
         sum_splits();
-        site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s); });
+        site("gemm.fc.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.F, gu, wmat(F.fc[l]), gtmp, s, wmatT(F.fc[l])); });
         site("gemm.fc.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.F, d.C, N, gu, xn2, grads + F.fc[l], acc, part, pcap, s); });
         sum_splits();
       }
@@ -604,7 +616,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         });
         sum_splits();
       } else {
-        site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s); });
+        site("gemm.o.dgrad", s, [&] { gemm_nn_store(d, N, d.Cq, d.C, gxc, wmat(F.o[l]), gO, s, wmatT(F.o[l])); });
         site("gemm.o.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.C, d.Cq, N, gxc, att, grads + F.o[l], acc, part, pcap, s); });
         sum_splits();
       }
@@ -633,7 +645,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         });
         sum_splits();
       } else {
-        site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s); });
+        site("gemm.qkv.dgrad", s, [&] { gemm_nn_f32(d, N, d.C, d.Qkv, gqkv, wmat(F.q[l]), gtmp, s, wmatT(F.q[l])); });
         site("gemm.qkv.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.Qkv, d.C, N, gqkv, xn, grads + F.q[l], acc, part, pcap, s); });
         sum_splits();
       }
@@ -746,7 +758,8 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
     return GPT_OK;
   }
   const R global[] = {
-      {"wc", P.wc, d.bf16 ? (P.rope - P.wc) : 0}, {"rope", P.rope, (size_t)d.T * d.D * 4},
+      {"wc", P.wc, d.bf16 ? (P.wct - P.wc) : 0}, {"wct", P.wct, d.bf16 ? (P.rope - P.wct) : 0},
+      {"rope", P.rope, (size_t)d.T * d.D * 4},
       {"xin", P.xin, N * C * 4}, {"xf", P.xf, N * C * A}, {"rf", P.rf, N * 4},
       {"logits", P.logits, N * d.V * A}, {"lossrow", P.lossrow, N * 4},
       {"scalars", P.scalars, 256},

@@ -37,6 +37,8 @@ std::vector<TensorInfo> param_layout(const gpt_config& c);
 // Workspace plan: byte offsets of every region (all 256-byte aligned).
 struct Plan {
   size_t wc;            // compute-dtype mirror of params (bf16 only)
+  size_t wct;           // bf16 transposed mirror of the linear weights (same element
+                        // offsets; a [rows][cols] weight is stored [cols][rows])
   size_t rope;          // fp32 cos [T][D/2], sin [T][D/2]
   size_t x;             // fp32 [(L+1)][N][C] residual stream per layer boundary
   size_t xin;           // fp32 [N][C] scratch
@@ -69,6 +71,10 @@ struct CastSeg {
   int64_t off, n;
 };
 void launch_cast(const float* src, void* dst, const std::vector<CastSeg>& segs, hipStream_t s);
+// bf16 casts of the [rows][cols] fp32 matrices at offsets `offs` into dst and
+// their transposes into dstT (same element offsets)
+void launch_cast_t(const float* src, void* dst, void* dstT, const std::vector<int64_t>& offs,
+                   int rows, int cols, hipStream_t s);
 void launch_zero(float* p, int64_t n, hipStream_t s);
 void launch_rope_table(float* cs, int T, int D, float theta, hipStream_t s);
 void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C, hipStream_t s);
@@ -147,13 +153,15 @@ void gemm_nt_relu2(const Dims& d, int64_t M, int N, int K, const void* A, const 
 // Softcapped logits c = cap * tanh(A B^T / cap), stored in the activation type.
 void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                      void* C, hipStream_t s);
+// The nn products take an optional Bt = B^T ([N][K], bf16): with it the
+// product runs with both operands K-major (direct LDS fills).
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                   void* C, hipStream_t s);
+                   void* C, hipStream_t s, const void* Bt = nullptr);
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                 float* C, hipStream_t s);
+                 float* C, hipStream_t s, const void* Bt = nullptr);
 // C = (A B) * 2 sqrt(H): the MLP hidden gradient from h = relu(u)^2
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
-                      const void* H, void* C, hipStream_t s);
+                      const void* H, void* C, hipStream_t s, const void* Bt = nullptr);
 // Split-K products: each K split writes an fp32 partial of C into `part`
 // (capacity part_cap bytes, at least what the matching *_part_bytes returns
 // for the shape); the returned SplitSum, passed to splitk_sum, adds the
@@ -169,7 +177,7 @@ void splitk_sum(const SplitSum& r, hipStream_t s);
 // Like gemm_nn_f32 for a long contraction.
 SplitSum gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* A,
                             const void* B, float* C, float* part, int64_t part_cap,
-                            hipStream_t s);
+                            hipStream_t s, const void* Bt = nullptr);
 int64_t part_bytes_nn_splitk(const Dims& d, int64_t M, int64_t N, int64_t K);
 // Weight gradients C[M][N] (+)= sum_k A[k][m] B[k][n].
 SplitSum gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, const void* B,

@@ -34,6 +34,68 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ src
   }
 }
 
+// Cast of weight matrices [rows][cols] (fp32, at offsets off[z]) to the
+// compute-dtype mirror, plus a transposed mirror [cols][rows] for the
+// products that contract over a weight's rows (input gradients). One 64 x 64
+// tile per workgroup, transposed through LDS; both stores are 16 or 8 bytes
+// per lane along rows of their own matrix.
+struct CastTTable {
+  int64_t off[64];
+  int rows, cols;
+};
+__global__ __launch_bounds__(256) void cast_t_kernel(const float* __restrict__ src,
+                                                     bf16* __restrict__ dst,
+                                                     bf16* __restrict__ dstT, CastTTable t) {
+  __shared__ float tile[64][65];
+  const int tid = threadIdx.x;
+  const int64_t off = t.off[blockIdx.z];
+  const int R = t.rows, Cc = t.cols;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const float* a = src + off;
+  // rows r0 + tid / 16 + 16 i, columns c0 + 4 (tid % 16) .. + 3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = tid / 16 + 16 * i, c = (tid % 16) * 4;
+    f32x4 v = {0, 0, 0, 0};
+    if (r0 + r < R) {
+      if (c0 + c + 3 < Cc) {
+        v = *reinterpret_cast<const f32x4*>(a + (int64_t)(r0 + r) * Cc + c0 + c);
+      } else {
+        for (int j = 0; j < 4; ++j)
+          if (c0 + c + j < Cc) v[j] = a[(int64_t)(r0 + r) * Cc + c0 + c + j];
+      }
+      bf16* o = dst + off + (int64_t)(r0 + r) * Cc + c0 + c;
+      if (c0 + c + 3 < Cc) {
+        bf16x4 w;
+        for (int j = 0; j < 4; ++j) w[j] = static_cast<bf16>(v[j]);
+        *reinterpret_cast<bf16x4*>(o) = w;
+      } else {
+        for (int j = 0; j < 4; ++j)
+          if (c0 + c + j < Cc) o[j] = static_cast<bf16>(v[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[r][c + j] = v[j];
+  }
+  __syncthreads();
+  // transposed: rows c0 + tid / 8 + 32 i, columns r0 + 8 (tid % 8) .. + 7
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid / 8 + 32 * i, r = (tid % 8) * 8;
+    if (c0 + c >= Cc) continue;
+    bf16* o = dstT + off + (int64_t)(c0 + c) * R + r0 + r;
+    if (r0 + r + 7 < R) {
+      bf16x8 w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = static_cast<bf16>(tile[r + j][c]);
+      *reinterpret_cast<bf16x8*>(o) = w;
+    } else {
+      for (int j = 0; j < 8; ++j)
+        if (r0 + r + j < R) o[j] = static_cast<bf16>(tile[r + j][c]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -612,6 +674,20 @@ void launch_cast(const float* src, void* dst, const std::vector<CastSeg>& segs, 
     }
     dim3 grid(std::min<unsigned>(blocks_for(mx, 256 * 8), 1024), t.nseg);
     hipLaunchKernelGGL(cast_kernel, grid, dim3(256), 0, s, src, static_cast<bf16*>(dst), t);
+  }
+}
+
+void launch_cast_t(const float* src, void* dst, void* dstT, const std::vector<int64_t>& offs,
+                   int rows, int cols, hipStream_t s) {
+  for (size_t base = 0; base < offs.size(); base += 64) {
+    CastTTable t{};
+    const int n = (int)std::min<size_t>(64, offs.size() - base);
+    for (int i = 0; i < n; ++i) t.off[i] = offs[base + i];
+    t.rows = rows;
+    t.cols = cols;
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)n);
+    hipLaunchKernelGGL(cast_t_kernel, grid, dim3(256), 0, s, src, static_cast<bf16*>(dst),
+                       static_cast<bf16*>(dstT), t);
   }
 }
 

@@ -129,7 +129,8 @@ int gpt_workspace_size(const gpt_config* cfg, size_t* bytes);
  *   "xf"   act  [N, C]   final RMSNorm output
  *   "logits" act [N, V]  softcapped logits after gpt_fwd; after gpt_fwd_bwd
  *                        the gradient of the loss w.r.t. the raw logits
- * Scratch (layout only): "wc", "rope", "xin", "rf", "lossrow", "scalars",
+ * Scratch (layout only): "wc", "wct" (bf16 weight mirror and its per-matrix
+ * transposes; 0 bytes for fp32), "rope", "xin", "rf", "lossrow", "scalars",
  * "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga", "lam_part",
  * "veg_part", "part" (split-K partials; 0 bytes when no product is split);
  * per layer "r1", "rqk", "a", "lse", "r2". With fp8_linears = 1 also "amax", "w8", "w8t", "q8", "g8t" and per
