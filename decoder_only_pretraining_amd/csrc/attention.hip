@@ -1013,9 +1013,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
           mfma(dp[tb], da[p][tb], vf[kc]);
         }
       }
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        softgrad(sa[tb], dp[tb], tb);
+      auto mask = [&](int tb) {
         const int tlo = t0 + tb * 32;
         if (!(tlo >= sw + 31 && (full || tlo + 31 - sw <= W) && tlo + 31 < T_)) {
           asm volatile("" ::: "memory");  // keep the mask on its own branch
@@ -1032,8 +1030,22 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
             }
           }
         }
-        accumulate(sa[tb], dp[tb], tb);
+      };
+      softgrad(sa[0], dp[0], 0);
+      mask(0);
+      // the second block's softmax gradient (VALU) is interleaved with the
+      // first block's dK / dV products (MFMA): one wavefront per SIMD, so
+      // only its own instruction stream can fill the MFMA shadow
+      accumulate(sa[0], dp[0], 0);
+      softgrad(sa[1], dp[1], 1);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
       }
+      mask(1);
+      accumulate(sa[1], dp[1], 1);
     }
     if (step + S - 1 < nstep) wait_all_but_one();
     else __builtin_amdgcn_s_waitcnt(0x0f70);
