@@ -1077,12 +1077,13 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
 // wavefront, Q and dO rows held as fragments) and walks the visible 64-key
 // tiles; K (read by rows and transposed) and V (read by rows) stream
 // through three LDS stages, two tiles ahead.
-template <int D, int NW, bool ALIGNED>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
+template <int D, int NW, bool ALIGNED, int S>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(S == 2 ? 2 : 1, S == 2 ? 2 : 1))) void attn_bwd_q_tiled_kernel(
     const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
     const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
     int full, float c2, float scale, int nq, int nb) {
-  constexpr int BQ = 32 * NW, BKV = 64, S = 3;
+  constexpr int BQ = 32 * NW, BKV = 64;
+  static_assert(S == 2 || S == 3, "two or three stages");
   using DK = Dual<BKV, D>;
   using GV = TileGeom<BKV, D, true>;
   using LV = DirectLoader<BKV, D, true>;
@@ -1141,7 +1142,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
 #pragma unroll
   for (int it = 0; it < S - 1; ++it)
     if (it < ntile) issue(it);
-  if (ntile > 1 && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
+  if (S == 3 && ntile > 1 && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
   else __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
   auto tile = [&](int it, auto cur_c) {
@@ -1213,15 +1214,16 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_q_tiled_kernel(
         }
       }
     }
-    if (it + S - 1 < ntile && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
+    if (S == 3 && it + S - 1 < ntile && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
     else __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   };
-  static_assert(S == 3, "the tile loop is unrolled by the stage count");
+  // the tile loop is unrolled by the stage count
   for (int it = 0; it < ntile; it += S) {
     tile(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntile) tile(it + 1, std::integral_constant<int, 1>{});
-    if (it + 2 < ntile) tile(it + 2, std::integral_constant<int, 2>{});
+    if constexpr (S == 3)
+      if (it + 2 < ntile) tile(it + 2, std::integral_constant<int, 2 % S>{});
   }
   if (tv) {
     bf16* qp = gqkv + (rb + t) * Qkv + h * D;
@@ -1262,14 +1264,17 @@ void bwd(const gpt::Dims& d, bool full, const void* qkv, const void* gO, const f
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   const float scale = 1.0f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
-    constexpr int NW = 4;  // one wavefront per SIMD: the backward needs > 256 registers
+    // 4 wavefronts per workgroup. The dK/dV pass needs > 256 registers (one
+    // wavefront per SIMD); the dQ pass fits 256 with two LDS stages when T is
+    // a multiple of 64, so two of its workgroups share a CU.
+    constexpr int NW = 4;
     const int nkt = (d.T + 32 * NW - 1) / (32 * NW), nq = (d.T + 32 * NW - 1) / (32 * NW);
 #define GPT_ATTN_BWD(AL)                                                                          \
   hipLaunchKernelGGL((attn_bwd_kv_tiled_kernel<D, NW, AL>), dim3((unsigned)(nkt * d.Hk * d.B)),    \
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),                           \
                      static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H, \
                      d.Hk, d.W, full ? 1 : 0, c2, scale, nkt, d.B);                                \
-  hipLaunchKernelGGL((attn_bwd_q_tiled_kernel<D, NW, AL>), dim3((unsigned)(nq * d.H * d.B)),       \
+  hipLaunchKernelGGL((attn_bwd_q_tiled_kernel<D, NW, AL, AL ? 2 : 3>), dim3((unsigned)(nq * d.H * d.B)), \
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),                           \
                      static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H, \
                      d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B)
