@@ -237,6 +237,8 @@ Plan make_plan(const Dims& d) {
   p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
   p.veg_splits = 512;
   p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
+  p.vegrow = take(N * d.Ckv * 4);  // every model has a value-embedding layer (the last)
+  p.tlink = take(2 * N * 4);
   {  // split-K partials: the largest over the step's split products
     int64_t pb = std::max(part_bytes_nn_splitk(d, d.N, d.C, d.V),
                           part_bytes_tn_wgrad(d, d.V, d.C, d.N));
@@ -523,6 +525,9 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       for (int l = 0; l < d.L; ++l)
         if (F.ve[l] >= 0) launch_zero(grads + F.ve[l], (int64_t)d.V * d.Ckv, s);
     }
+    float* vegrow = reinterpret_cast<float*>(W + P.vegrow);
+    int32_t* tlink = reinterpret_cast<int32_t*>(W + P.tlink);
+    launch_token_links(tokens, N, tlink, s);
     float* gx = reinterpret_cast<float*>(W + P.gx);
     void* gxc = d.bf16 ? static_cast<void*>(W + P.gxc) : static_cast<void*>(gx);
     float* gx0 = reinterpret_cast<float*>(W + P.gx0);
@@ -623,7 +628,8 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       site("attn.delta", s, [&] { launch_attn_delta(d, gO, att, delta, s); });
       site("attn.bwd", s, [&] { launch_attn_bwd(d, full, qkv, gO, lse, delta, gqkv, s); });
       launch_rope_qk_ve_bwd(d, gqkv, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr,
-                            ve ? grads + F.ve[l] : nullptr, ga, tokens, s);
+                            ve ? vegrow : nullptr, ga, tokens, s);
+      if (ve) launch_rows_to_table(vegrow, d.Ckv, tokens, tlink, N, grads + F.ve[l], s);
       if (d.fp8) {
         const int g0 = slot(l, 13), g1 = slot(l, 14), g2 = slot(l, 15);
         site("fp8.quant", s, [&] {
@@ -668,7 +674,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       nb.lam_part = lam_part + (size_t)l * P.lam_blocks * 2;
       launch_norm_bwd(d, nb, s);
     }
-    site("embed.bwd", s, [&] { launch_embed_bwd(gx0, tokens, grads + F.wte, N, d.C, s); });
+    site("embed.bwd", s, [&] { launch_rows_to_table(gx0, d.C, tokens, tlink, N, grads + F.wte, s); });
     for (int l = 0; l < d.L; ++l)
       launch_lambda_finalize(d, lam_part + (size_t)l * P.lam_blocks * 2, P.lam_blocks,
                              grads + F.lr + l, grads + F.l0 + l, s);
@@ -768,6 +774,7 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
       {"gqkv", P.gqkv, N * d.Qkv * A}, {"delta", P.delta, N * d.H * 4},
       {"ga", P.ga, N * d.Hk * 4}, {"lam_part", P.lam_part, (size_t)d.L * P.lam_blocks * 8},
       {"veg_part", P.veg_part, (size_t)P.veg_splits * d.Hk * C * 4},
+      {"vegrow", P.vegrow, N * (size_t)d.Ckv * 4}, {"tlink", P.tlink, 2 * N * 4},
       {"part", P.part, (size_t)P.part_bytes},
       {"amax", P.amax, d.fp8 ? (size_t)16 * d.L * 4 : 0},
       {"w8", P.w8, d.fp8 ? P.w8_layer * d.L : 0},

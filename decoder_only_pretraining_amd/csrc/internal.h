@@ -49,6 +49,8 @@ struct Plan {
   size_t part;           // split-K partials
   int64_t part_bytes;
   size_t gx, gxc, gx0, gu, gtmp, gO, gqkv, delta, ga, lam_part, veg_part;
+  size_t vegrow;         // fp32 [N][Hk*D] per-position value-embedding gradient rows
+  size_t tlink;          // int32 [2 N] token links of the embedding-table gradients
   int lam_blocks, veg_splits;
   // fp8 linears only (0 bytes otherwise). Token-major code tensors that the
   // weight gradients contract over are stored transposed, [features][Np],
@@ -91,7 +93,15 @@ void launch_rope_qk_ve_fwd(const Dims& d, void* qkv, float* rqk, const float* cs
                            hipStream_t s);
 void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const float* rqk,
                            const float* cs, const float* a, const float* ve_table,
-                           float* gve_table, float* ga, const int32_t* tok, hipStream_t s);
+                           float* gve_rows, float* ga, const int32_t* tok, hipStream_t s);
+// Embedding-table gradients tab[tok[n]][:] += g[n][:] over n < N (g [N][W]
+// fp32): within each chunk of 128 positions the rows sharing a token id are
+// summed in position order first, then one fp32 atomic add per (id,
+// column). launch_token_links builds the per-call links (int32 [2 N]) from
+// the tokens.
+void launch_token_links(const int32_t* tok, int64_t N, int32_t* link, hipStream_t s);
+void launch_rows_to_table(const float* g, int W, const int32_t* tok, const int32_t* link,
+                          int64_t N, float* tab, hipStream_t s);
 
 void launch_attn_fwd(const Dims& d, bool full, const void* qkv, void* out, float* lse,
                      hipStream_t s);
@@ -135,8 +145,6 @@ void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipSt
 // logits are overwritten in place by the logit gradient of the mean loss.
 void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* scalars,
                  float* lossrow, float* loss, bool grad, hipStream_t s);
-void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t N, int C,
-                      hipStream_t s);
 
 // ------------------------------------------------------------ GEMMs
 // Shapes: C[M][N] = sum_k A(m,k) B(n,k).

@@ -127,13 +127,58 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wt
   for (int c = threadIdx.x; c < C / 4; c += blockDim.x) o[c] = s[c];
 }
 
-__global__ __launch_bounds__(256) void embed_bwd_kernel(const float* __restrict__ gx0,
-                                                        const int32_t* __restrict__ tok,
-                                                        float* __restrict__ gwte, int C) {
+// ------------------------------------------------------------ embedding-table gradients
+// tab[tok[n]][:] += g[n][:] for the rows g of N positions. Frequent token
+// ids would serialise per-position atomic adds on one table row, so the
+// positions are cut into chunks of kChunk and, in each chunk, the first
+// position holding an id (its leader) sums the rows of all the chunk's
+// positions with that id, in position order, and makes the one atomic add
+// per column. The links (leader flag, next position of the same id in the
+// chunk) depend only on the tokens and are built once per call.
+constexpr int kChunk = 128;
+
+// link[n] = next position of tok[n]'s id in n's chunk (-1: none);
+// link[N + n] = 1 if n is the first of its id in its chunk, else 0
+__global__ __launch_bounds__(kChunk) void token_links_kernel(const int32_t* __restrict__ tok,
+                                                             int64_t N, int32_t* __restrict__ link) {
+  __shared__ int32_t ids[kChunk];
+  const int t = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * kChunk;
+  const int cnt = (int)min<int64_t>(kChunk, N - n0);
+  ids[t] = t < cnt ? tok[n0 + t] : -1;
+  __syncthreads();
+  if (t >= cnt) return;
+  const int my = ids[t];
+  int first = 1, next = -1;
+  for (int k = 0; k < t; ++k)
+    if (ids[k] == my) {
+      first = 0;
+      break;
+    }
+  for (int k = t + 1; k < cnt; ++k)
+    if (ids[k] == my) {
+      next = k;
+      break;
+    }
+  link[n0 + t] = next >= 0 ? (int32_t)(n0 + next) : -1;
+  link[N + n0 + t] = first;
+}
+
+// One workgroup per position; only leaders work (the test is uniform over
+// the workgroup). Columns are strided over the threads, so the member row
+// reads and the atomic adds are contiguous across a wavefront.
+__global__ __launch_bounds__(256) void rows_to_table_kernel(const float* __restrict__ g, int W,
+                                                            const int32_t* __restrict__ tok,
+                                                            const int32_t* __restrict__ link,
+                                                            int64_t N, float* __restrict__ tab) {
   const int64_t n = blockIdx.x;
-  const int64_t row = tok[n];
-  for (int c = threadIdx.x; c < C; c += blockDim.x)
-    atomicAdd(gwte + row * C + c, gx0[n * C + c]);
+  if (!link[N + n]) return;
+  float* dst = tab + (int64_t)tok[n] * W;
+  for (int f = threadIdx.x; f < W; f += 256) {
+    float acc = g[n * W + f];
+    for (int k = link[n]; k >= 0; k = link[k]) acc += g[(int64_t)k * W + f];
+    atomicAdd(dst + f, acc);
+  }
 }
 
 // ------------------------------------------------------------ mix + RMSNorm
@@ -488,13 +533,13 @@ __global__ __launch_bounds__(256) void rope_fwd_kernel(T* __restrict__ qkv, floa
 
 // In place on the q / k / v gradient rows: through the QK-norm
 // (r * (g - y * mean(g * y)), y the saved normalised output) and the inverse
-// rotation; for v heads of value-embedding layers the table gradient
-// (atomic adds into the token's row) and the gate logit's gradient.
+// rotation; for v heads of value-embedding layers the per-position rows of
+// the table gradient and the gate logit's gradient.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_bwd_kernel(
     T* __restrict__ gqkv, const T* __restrict__ qkv, const float* __restrict__ rqk,
     const float* __restrict__ cs, const float* __restrict__ a, const float* __restrict__ ve,
-    float* __restrict__ gve, float* __restrict__ ga, const int32_t* __restrict__ tok, int64_t N,
+    float* __restrict__ rows, float* __restrict__ ga, const int32_t* __restrict__ tok, int64_t N,
     int T_, int H, int Hk, int Qkv) {
   constexpr int H2 = D / 2, LP = D / 8;
   const int q = threadIdx.x % LP;
@@ -521,15 +566,16 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(
     const T* gp = gqkv + n * Qkv + (R + j) * D;
     const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
     const int64_t off = (int64_t)tok[n] * Hk * D + j * D;
-    // elements q, q + LP, ...: the group's atomic adds of one instruction
-    // hit consecutive addresses
+    // position n's row of the table gradient (added to the table per token
+    // id by rows_to_table_kernel)
+    float* rp = rows + n * Hk * D + j * D;
     float dot = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int o = q + e * LP;
-      const float gv = to_f(gp[o]);
-      dot += gv * ve[off + o];
-      atomicAdd(gve + off + o, g * gv);
+    for (int e = 0; e < 2; ++e) {
+      const int o = 4 * q + e * H2;
+      const f32x4 gv = load4<T>(gp + o);
+      dot += dot4(gv, *reinterpret_cast<const f32x4*>(ve + off + o));
+      *reinterpret_cast<f32x4*>(rp + o) = g * gv;
     }
     dot = group_sum<LP>(dot);
     if (q == 0) ga[n * Hk + j] = g * (1.0f - g) * dot;
@@ -708,11 +754,6 @@ void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, in
   hipLaunchKernelGGL(embed_kernel, dim3((unsigned)N), dim3(256), 0, s, wte, tok, x0, N, C);
 }
 
-void launch_embed_bwd(const float* gx0, const int32_t* tok, float* gwte, int64_t N, int C,
-                      hipStream_t s) {
-  hipLaunchKernelGGL(embed_bwd_kernel, dim3((unsigned)N), dim3(256), 0, s, gx0, tok, gwte, C);
-}
-
 template <typename T, int NC>
 static void mix_norm_nc(const Dims& d, const float* x, const float* x0, const float* lam_r,
                         const float* lam_0, float* xin_out, void* y, float* r, const float* wg,
@@ -821,11 +862,11 @@ void launch_rope_qk_ve_fwd(const Dims& d, void* qkv, float* rqk, const float* cs
 
 void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const float* rqk,
                            const float* cs, const float* a, const float* ve_table,
-                           float* gve_table, float* ga, const int32_t* tok, hipStream_t s) {
+                           float* gve_rows, float* ga, const int32_t* tok, hipStream_t s) {
   const dim3 grid(rope_blocks(d, ve_table != nullptr));
 #define GPT_ROPE_B(TY, DD)                                                                          \
   hipLaunchKernelGGL((rope_bwd_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<TY*>(gqkv),       \
-                     static_cast<const TY*>(qkv), rqk, cs, a, ve_table, gve_table, ga, tok, d.N,    \
+                     static_cast<const TY*>(qkv), rqk, cs, a, ve_table, gve_rows, ga, tok, d.N,     \
                      d.T, d.H, d.Hk, d.Qkv)
   if (d.bf16) {
     if (d.D == 128) GPT_ROPE_B(bf16, 128);
@@ -835,6 +876,17 @@ void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const flo
     else GPT_ROPE_B(float, 64);
   }
 #undef GPT_ROPE_B
+}
+
+void launch_token_links(const int32_t* tok, int64_t N, int32_t* link, hipStream_t s) {
+  hipLaunchKernelGGL(token_links_kernel, dim3((unsigned)((N + kChunk - 1) / kChunk)), dim3(kChunk),
+                     0, s, tok, N, link);
+}
+
+void launch_rows_to_table(const float* g, int W, const int32_t* tok, const int32_t* link,
+                          int64_t N, float* tab, hipStream_t s) {
+  hipLaunchKernelGGL(rows_to_table_kernel, dim3((unsigned)N), dim3(256), 0, s, g, W, tok, link, N,
+                     tab);
 }
 
 void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipStream_t s) {

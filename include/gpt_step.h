@@ -132,7 +132,9 @@ int gpt_workspace_size(const gpt_config* cfg, size_t* bytes);
  * Scratch (layout only): "wc", "wct" (bf16 weight mirror and its per-matrix
  * transposes; 0 bytes for fp32), "rope", "xin", "rf", "lossrow", "scalars",
  * "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga", "lam_part",
- * "veg_part", "part" (split-K partials; 0 bytes when no product is split);
+ * "veg_part", "part" (split-K partials; 0 bytes when no product is split),
+ * "vegrow" (per-position value-embedding gradient rows, fp32 [N, Hk*D]),
+ * "tlink" (int32 [2N] token links of the embedding-table gradients);
  * per layer "r1", "rqk", "a", "lse", "r2". With fp8_linears = 1 also "amax", "w8", "w8t", "q8", "g8t" and per
  * layer "x8t", "a8t", "x28t", "h8t" (fp8 codes; 0 bytes otherwise).
  * All regions are disjoint. `layer` is ignored for global regions.

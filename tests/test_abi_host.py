@@ -115,7 +115,7 @@ def test_entry_points_reject_bad_pointers_before_any_launch():
 
 GLOBAL_REGIONS = ["wc", "wct", "rope", "xin", "xf", "rf", "logits", "lossrow",
                   "scalars", "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga",
-                  "lam_part", "veg_part", "part", "amax", "w8", "w8t", "q8", "g8t"]
+                  "lam_part", "veg_part", "vegrow", "tlink", "part", "amax", "w8", "w8t", "q8", "g8t"]
 LAYER_REGIONS = ["xn", "r1", "qkv", "rqk", "a", "attn", "lse", "xmid", "xn2", "r2", "h",
                  "x8t", "a8t", "x28t", "h8t"]
 
