@@ -235,7 +235,7 @@ Plan make_plan(const Dims& d) {
   p.ga = take(N * d.Hk * 4);
   p.lam_blocks = (int)((d.N + 3) / 4);
   p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
-  p.veg_splits = 512;
+  p.veg_splits = veg_splits(d.N);
   p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
   p.vegrow = take(N * d.Ckv * 4);  // every model has a value-embedding layer (the last)
   p.tlink = take(2 * N * 4);

@@ -136,6 +136,8 @@ void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s);
 
 void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
                             float* g_l0, hipStream_t s);
+// splits: veg_splits(N) (each split takes at most 64 tokens)
+int veg_splits(int64_t N);
 void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* part,
                       int splits, float* gwg, hipStream_t s);
 // 1 / n_valid into scalars[0].

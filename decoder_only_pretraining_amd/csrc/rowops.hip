@@ -397,36 +397,52 @@ __global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __res
 }
 
 // Gate weight gradient g_Wg[j][c] = sum_n ga[n][j] * xn[n][c]. Block b sums
-// the tokens [b * per, (b + 1) * per): thread (phase, column group) owns 8
-// consecutive columns and every NP-th token of the range; the phases are
-// then added in a fixed order and the block writes its partial. A second
-// kernel adds the partials in block order.
+// the tokens [b * per, (b + 1) * per), per <= kVegPer: thread (phase,
+// column group) owns 8 consecutive columns and every NP-th token of the
+// range; the phases are then added in a fixed order and the block writes
+// its partial. A second kernel adds the partials in block order.
+constexpr int kVegPer = 64;
 template <typename T, int HK>
 __global__ __launch_bounds__(256) void veg_partial_kernel(const float* __restrict__ ga,
                                                           const T* __restrict__ xn,
                                                           float* __restrict__ part, int64_t N,
                                                           int C, int hk, int64_t per) {
   __shared__ float red[256 * 8];
+  __shared__ float gs[kVegPer * HK];  // the block's gate gradients, staged once
   const int CG = C / 8, NP = 256 / CG;  // column groups, token phases (C <= 2048)
   const int cg = threadIdx.x % CG, ph = threadIdx.x / CG;
   const int64_t lo = (int64_t)blockIdx.x * per, hi = lo + per < N ? lo + per : N;
+  for (int64_t i = threadIdx.x; i < (hi - lo) * hk; i += 256) gs[i] = ga[lo * hk + i];
+  __syncthreads();
   float acc[HK][8];
 #pragma unroll
   for (int j = 0; j < HK; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
   if (ph < NP) {
-#pragma unroll 4
-    for (int64_t n = lo + ph; n < hi; n += NP) {
-      const f32x4 x0 = load4<T>(xn + n * C + cg * 8), x1 = load4<T>(xn + n * C + cg * 8 + 4);
+    // eight tokens' loads are issued before their products
+    for (int64_t nb = lo + ph; nb < hi; nb += 8 * NP) {
+      f32x4 xa[8], xb[8];
 #pragma unroll
-      for (int j = 0; j < HK; ++j) {
-        if (j < hk) {
-          const float g = ga[n * hk + j];
+      for (int q = 0; q < 8; ++q) {
+        const int64_t n = min(nb + q * NP, hi - 1);
+        xa[q] = load4<T>(xn + n * C + cg * 8);
+        xb[q] = load4<T>(xn + n * C + cg * 8 + 4);
+      }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[j][e] += g * x0[e];
-            acc[j][4 + e] += g * x1[e];
+      for (int q = 0; q < 8; ++q) {
+        const int64_t n = nb + q * NP;
+        if (n < hi) {
+#pragma unroll
+          for (int j = 0; j < HK; ++j) {
+            if (j < hk) {
+              const float g = gs[(n - lo) * hk + j];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                acc[j][e] += g * xa[q][e];
+                acc[j][4 + e] += g * xb[q][e];
+              }
+            }
           }
         }
       }
@@ -462,7 +478,7 @@ __global__ __launch_bounds__(256) void veg_finalize_kernel(const float* __restri
   const int i = blockIdx.x * 64 + lane;
   float s = 0.0f;
   if (i < n) {
-#pragma unroll 8
+#pragma unroll 16
     for (int sp = w; sp < splits; sp += 4) s += part[(int64_t)sp * n + i];
   }
   red[w][lane] = s;
@@ -818,9 +834,11 @@ void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, floa
                      g_l0, d.accumulate ? 1 : 0);
 }
 
+int veg_splits(int64_t N) { return (int)std::max<int64_t>(256, (N + kVegPer - 1) / kVegPer); }
+
 void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* part, int splits,
                       float* gwg, hipStream_t s) {
-  const int64_t per = (d.N + splits - 1) / splits;
+  const int64_t per = (d.N + splits - 1) / splits;  // <= kVegPer with splits = veg_splits(N)
 #define GPT_VEG(TY, HK)                                                                            \
   hipLaunchKernelGGL((veg_partial_kernel<TY, HK>), dim3((unsigned)splits), dim3(256), 0, s, ga,    \
                      static_cast<const TY*>(xn), part, d.N, d.C, d.Hk, per)
