@@ -253,19 +253,30 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
       store4<T>(y + n * C + c4 * 4, v[i]);
     }
   }
-  if (wg) {  // gate logits from the rounded norm output, one KV head at a time
-    for (int j = 0; j < hk; ++j) {
-      float dot = 0.0f;
+  if (wg) {  // gate logits from the rounded norm output, four KV heads at a time
+    for (int j0 = 0; j0 < hk; j0 += 4) {
+      float dot[4];
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c4 = lane + i * 64;
-        if (c4 < C4) {
-          const f32x4 w = reinterpret_cast<const f32x4*>(wg + (int64_t)j * C)[c4];
-          dot += v[i][0] * w[0] + v[i][1] * w[1] + v[i][2] * w[2] + v[i][3] * w[3];
+      for (int q = 0; q < 4; ++q) {
+        const int j = min(j0 + q, hk - 1);  // past hk: a valid row, result unused
+        dot[q] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c4 = lane + i * 64;
+          if (c4 < C4) {
+            const f32x4 w = reinterpret_cast<const f32x4*>(wg + (int64_t)j * C)[c4];
+            dot[q] += v[i][0] * w[0] + v[i][1] * w[1] + v[i][2] * w[2] + v[i][3] * w[3];
+          }
         }
       }
-      dot = wave_sum(dot);
-      if (lane == 0) a[n * hk + j] = dot;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dot[q] += __shfl_xor(dot[q], o, kWave);
+      if (lane == 0)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (j0 + q < hk) a[n * hk + j0 + q] = dot[q];
     }
   }
 }
@@ -297,12 +308,28 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(gpt::NormBwdArgs p, int64
       if (c4 < C4) g[i] = reinterpret_cast<const f32x4*>(p.gin + n * C)[c4];
     }
     if (norm1 && p.ga) {  // the value-embedding gate's share: g += sum_j ga[j] * wg[j]
-      for (int j = 0; j < hk; ++j) {
-        const float gj = p.ga[n * hk + j];
+      for (int j0 = 0; j0 < hk; j0 += 4) {  // four KV heads' loads at a time
+        float gj[4];
+        f32x4 w[4][NC];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          const int c4 = lane + i * 64;
-          if (c4 < C4) g[i] += gj * reinterpret_cast<const f32x4*>(p.wg + (int64_t)j * C)[c4];
+        for (int q = 0; q < 4; ++q) {
+          const int j = min(j0 + q, hk - 1);  // past hk: a valid row, not used
+          gj[q] = p.ga[n * hk + j];
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const int c4 = lane + i * 64;
+            if (c4 < C4) w[q][i] = reinterpret_cast<const f32x4*>(p.wg + (int64_t)j * C)[c4];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (j0 + q < hk) {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+              const int c4 = lane + i * 64;
+              if (c4 < C4) g[i] += gj[q] * w[q][i];
+            }
+          }
         }
       }
     }
