@@ -675,9 +675,9 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       launch_norm_bwd(d, nb, s);
     }
     site("embed.bwd", s, [&] { launch_rows_to_table(gx0, d.C, tokens, tlink, N, grads + F.wte, s); });
-    for (int l = 0; l < d.L; ++l)
-      launch_lambda_finalize(d, lam_part + (size_t)l * P.lam_blocks * 2, P.lam_blocks,
-                             grads + F.lr + l, grads + F.l0 + l, s);
+    // every layer's lambda gradients in one launch (layer l's partials at
+    // lam_part + l * 2 * lam_blocks)
+    launch_lambda_finalize(d, lam_part, P.lam_blocks, grads + F.lr, grads + F.l0, s);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));

@@ -134,6 +134,8 @@ struct NormBwdArgs {
 };
 void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s);
 
+// The lambda gradients of all d.L layers: layer l's nblk partial pairs at
+// lam_part + 2 l nblk, outputs g_lr[l], g_l0[l].
 void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
                             float* g_l0, hipStream_t s);
 // splits: veg_splits(N) (each split takes at most 64 tokens)

@@ -396,11 +396,17 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(gpt::NormBwdArgs p, int64
   }
 }
 
-// Per-layer lambda gradients: fixed-order sums of the per-block partials.
-__global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __restrict__ part,
-                                                              int nblk, float* g_lr, float* g_l0,
+// Per-layer lambda gradients: fixed-order sums of the per-block partials;
+// workgroup l takes layer l (partials at part + l * stride, outputs g_lr[l],
+// g_l0[l]).
+__global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __restrict__ part_all,
+                                                              int nblk, int64_t stride,
+                                                              float* g_lr_all, float* g_l0_all,
                                                               int accumulate) {
   __shared__ double red[2][256];
+  const float* part = part_all + (int64_t)blockIdx.x * stride;
+  float* g_lr = g_lr_all + blockIdx.x;
+  float* g_l0 = g_l0_all + blockIdx.x;
   double a = 0.0, b = 0.0;
   for (int i = threadIdx.x; i < nblk; i += 256) {
     a += part[2 * i];
@@ -857,8 +863,8 @@ void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s) {
 
 void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
                             float* g_l0, hipStream_t s) {
-  hipLaunchKernelGGL(lambda_finalize_kernel, dim3(1), dim3(256), 0, s, lam_part, nblk, g_lr,
-                     g_l0, d.accumulate ? 1 : 0);
+  hipLaunchKernelGGL(lambda_finalize_kernel, dim3((unsigned)d.L), dim3(256), 0, s, lam_part, nblk,
+                     (int64_t)nblk * 2, g_lr, g_l0, d.accumulate ? 1 : 0);
 }
 
 int veg_splits(int64_t N) { return (int)std::max<int64_t>(256, (N + kVegPer - 1) / kVegPer); }
