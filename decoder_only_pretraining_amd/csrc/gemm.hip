@@ -458,6 +458,31 @@ struct Tile {
 // share a CU, so one's epilogue overlaps the other's main loop (measured on
 // the d12 products with K = 768; the lm_head, with far more tiles, keeps
 // the larger tile).
+// bf16 products: among the 256-row tiles whose width divides N and that
+// give at least one full wave (256 workgroups), the one with the fewest
+// waves x tile area (a ragged last wave costs a whole wave); ties go to the
+// wider tile. Measured on the d12 shapes (16384 rows, K = 768): N = 3072 runs
+// 100 us as 256 x 256 against 111 as 128 x 128, N = 2304 85 us as 256 x 192
+// (256 x 256 leaves a quarter wave) against 89, N = 768 35 us as 256 x 192.
+static Tile pick_tile_bf16(int64_t M, int64_t N, int64_t K) {
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  const Tile cand[2] = {{256, 256}, {256, 192}};
+  Tile best{0, 0};
+  int64_t best_cost = -1;
+  for (const Tile& t : cand) {
+    if (N % t.bn != 0 || tiles(t.bm, t.bn) < 256) continue;
+    const int64_t cost = (tiles(t.bm, t.bn) + 255) / 256 * t.bm * t.bn;
+    if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;
+  }
+  if (best_cost >= 0) return best;
+  (void)K;
+  if (tiles(256, 128) >= 256) return {256, 128};
+  return {128, 128};
+}
+
+// fp8 products: 128 x 128 for short contractions with 4-32 waves of such
+// tiles, else the largest 256-row tile with enough tiles (measured on the
+// d26 shapes before the bf16 rule above).
 static Tile pick_tile(int64_t M, int64_t N, int64_t K) {
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (K <= 1024 && tiles(128, 128) >= 1024 && tiles(128, 128) <= 8192) return {128, 128};
@@ -692,7 +717,7 @@ SplitSum gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t 
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, true>(pick_tile_bf16(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
                          mk_store<bf16>(C, N), s);
   else
     run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
@@ -702,7 +727,7 @@ void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const 
 void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    const float* R, float* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, true>(pick_tile_bf16(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
                          mk_resid(R, C, N), s);
   else
     run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_resid(R, C, N), s);
@@ -711,7 +736,7 @@ void gemm_nt_resid(const Dims& d, int64_t M, int N, int K, const void* A, const 
 void gemm_nt_relu2(const Dims& d, int64_t M, int N, int K, const void* A, const void* B, void* C,
                    hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, true>(pick_tile_bf16(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
                          mk_relu2<bf16>(C, N), s);
   else
     run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{}, mk_relu2<float>(C, N), s);
@@ -720,7 +745,7 @@ void gemm_nt_relu2(const Dims& d, int64_t M, int N, int K, const void* A, const 
 void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                      void* C, hipStream_t s) {
   if (d.bf16)
-    run_bf16<true, true>(pick_tile(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, true>(pick_tile_bf16(M, N, K), A, K, B, K, M, N, K, K, PreId{}, PreId{},
                          mk_softcap<bf16>(C, N, d.cap), s);
   else
     run_f32<float, true, true>(A, K, B, K, M, N, K, PreId{}, PreId{},
@@ -730,10 +755,10 @@ void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, cons
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s, const void* Bt) {
   if (d.bf16 && Bt)
-    run_bf16<true, true>(pick_tile(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, true>(pick_tile_bf16(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
                          mk_store<bf16>(C, N), s);
   else if (d.bf16)
-    run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, false>(pick_tile_bf16(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
                           mk_store<bf16>(C, N), s);
   else
     run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{},
@@ -743,10 +768,10 @@ void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const 
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                  float* C, hipStream_t s, const void* Bt) {
   if (d.bf16 && Bt)
-    run_bf16<true, true>(pick_tile(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, true>(pick_tile_bf16(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
                          mk_f32(C, N, 0), s);
   else if (d.bf16)
-    run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, false>(pick_tile_bf16(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
                           mk_f32(C, N, 0), s);
   else
     run_f32<float, true, false>(A, K, B, N, M, N, K, PreId{}, PreId{}, mk_f32(C, N, 0), s);
@@ -755,10 +780,10 @@ void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const vo
 void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                       const void* U, void* C, hipStream_t s, const void* Bt) {
   if (d.bf16 && Bt)
-    run_bf16<true, true>(pick_tile(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, true>(pick_tile_bf16(M, N, K), A, K, Bt, K, M, N, K, K, PreId{}, PreId{},
                          mk_relu2bwd<bf16>(U, C, N), s);
   else if (d.bf16)
-    run_bf16<true, false>(pick_tile(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
+    run_bf16<true, false>(pick_tile_bf16(M, N, K), A, K, B, N, M, N, K, K, PreId{}, PreId{},
                           mk_relu2bwd<bf16>(U, C, N), s);
   else
     run_f32<float, true, false>(
@@ -767,7 +792,7 @@ void gemm_nn_relu2bwd(const Dims& d, int64_t M, int N, int K, const void* A, con
 }
 
 static KSplit nn_split(int64_t M, int64_t N, int64_t K) {
-  return plan_split(tile_count(pick_tile(M, N, K), M, N), K, 64, 4096);
+  return plan_split(tile_count(pick_tile_bf16(M, N, K), M, N), K, 64, 4096);
 }
 int64_t part_bytes_nn_splitk(const Dims& d, int64_t M, int64_t N, int64_t K) {
   if (!d.bf16) return 0;
@@ -779,7 +804,7 @@ SplitSum gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* 
                             const void* B, float* C, float* part, int64_t part_cap,
                             hipStream_t s, const void* Bt) {
   if (d.bf16) {
-    const Tile t = pick_tile(M, N, K);
+    const Tile t = pick_tile_bf16(M, N, K);
     const KSplit ks = nn_split(M, N, K);
     const int64_t chunk = ks.splits == 1 ? K : ks.chunk;
     if (ks.splits > 1) check_part(part_bytes_nn_splitk(d, M, N, K), part_cap);
