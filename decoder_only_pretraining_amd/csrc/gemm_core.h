@@ -172,11 +172,12 @@ struct DirectLoader {
       if (c < CHUNKS && off[q] != ~0u) lds_fill16(tile, off[q], lds_addr(lds) + c * 1024);
     }
   }
+  // `nw` loading wavefronts take the chunks wave, wave + nw, ...
   __device__ __forceinline__ static void issue(const bf16* __restrict__ p, int64_t ld, int64_t mn0,
                                                int64_t MN, int64_t k0, int64_t khi, bf16* lds,
-                                               int wave, int lane) {
+                                               int wave, int lane, int nw = 4) {
 #pragma unroll
-    for (int c = wave; c < CHUNKS; c += 4) {
+    for (int c = wave; c < CHUNKS; c += nw) {
       const int o = c * 1024 + lane * 16;  // byte offset of this lane's slot
       int64_t mn, k;
       bool slot = o < BYTES;
@@ -291,9 +292,13 @@ __device__ __forceinline__ void interleave_mfma_ds() {
   }
 }
 
+// NW = 4: wavefronts in a 2 x 2 grid, one per SIMD. NW = 8 (bf16, both
+// operands K-major): a 4 x 2 grid of (BM/4) x (BN/2) wavefront tiles, two
+// wavefronts per SIMD, so one's LDS reads and waits overlap the other's
+// MFMAs (half the accumulators per wavefront, more fragment reads per MFMA).
 template <int BM, int BN, int BK, bool AK, bool BKM, int MODE, class PA, class PB, class EP,
-          class DQ>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(
+          class DQ, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep_in,
     DQ dq) {
@@ -301,13 +306,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   constexpr bool F8 = MODE != 0;
   static_assert(!F8 || (AK && BKM), "fp8 products take K-major operands");
   static_assert(F8 == DQ::kOn, "fp8 products need a dequantisation");
+  static_assert(NW == 4 || (NW == 8 && AK && BKM && !F8), "8 wavefronts: bf16, K-major operands");
   using GA = TileGeom<BM, BK, AK>;
   using GB = TileGeom<BN, BK, BKM>;
-  constexpr int TM = BM / 64, TN = BN / 64;
+  constexpr int WGM = NW / 2;            // wavefront rows of the block grid
+  constexpr int WM = BM / WGM;           // wavefront tile rows
+  constexpr int TM = WM / 32, TN = BN / 64;
+  static_assert(TM >= 1 && WM % 32 == 0, "wavefront tile rows");
   constexpr int WN = BN / 2;
   constexpr int SP = WN + 4;  // epilogue staging row pitch (floats)
   constexpr int MAIN_BYTES = 2 * (GA::ELEMS + GB::ELEMS) * 2;
-  constexpr int STAGE_BYTES = 4 * 32 * SP * 4;
+  constexpr int STAGE_BYTES = NW * 32 * SP * 4;
   __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES];
   bf16 (*As)[GA::ELEMS] = reinterpret_cast<bf16 (*)[GA::ELEMS]>(smem);
   bf16 (*Bs)[GB::ELEMS] = reinterpret_cast<bf16 (*)[GB::ELEMS]>(smem + 2 * GA::ELEMS * 2);
@@ -366,8 +375,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   Loader<BN, BK, BKM> rb;
   auto fetch = [&](int64_t k0, int buf) {
     if constexpr (kDirect) {
-      DA::issue(A, lda, m0, M, k0, k_hi, As[buf], wave, lane);
-      DB::issue(B, ldb, n0, N, k0, k_hi, Bs[buf], wave, lane);
+      DA::issue(A, lda, m0, M, k0, k_hi, As[buf], wave, lane, NW);
+      DB::issue(B, ldb, n0, N, k0, k_hi, Bs[buf], wave, lane, NW);
     } else {
       ra.load(A, lda, m0, M, k0, k_hi, tid);
       rb.load(B, ldb, n0, N, k0, k_hi, tid);
@@ -402,7 +411,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
       Frag8 b[2][TN], a[2];
 #pragma unroll
       for (int j = 0; j < TN; ++j) read_frag8<BN, BK>(b[0][j], Bs[cur], wn * (BN / 2) + j * 32, 0, lane);
-      read_frag8<BM, BK>(a[0], As[cur], wm * (BM / 2), 0, lane);
+      read_frag8<BM, BK>(a[0], As[cur], wm * WM, 0, lane);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int p = ks & 1;
@@ -410,9 +419,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         for (int i = 0; i < TM; ++i) {
           const int q = i & 1;  // TM is even: row i of every slice uses a[i & 1]
           if (i + 1 < TM) {
-            read_frag8<BM, BK>(a[q ^ 1], As[cur], wm * (BM / 2) + (i + 1) * 32, ks, lane);
+            read_frag8<BM, BK>(a[q ^ 1], As[cur], wm * WM + (i + 1) * 32, ks, lane);
           } else if (ks + 1 < KS) {
-            read_frag8<BM, BK>(a[q ^ 1], As[cur], wm * (BM / 2), ks + 1, lane);
+            read_frag8<BM, BK>(a[q ^ 1], As[cur], wm * WM, ks + 1, lane);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
               read_frag8<BN, BK>(b[p ^ 1][j], Bs[cur], wn * (BN / 2) + j * 32, ks + 1, lane);
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
       constexpr int NM = TM * TN;
       Frag<bf16> a[2][TM], b[2][TN];
       auto read_slice = [&](int q, int ks, auto ordered) {
-        read_frag<BM, BK, AK>(a[q][0], As[cur], wm * (BM / 2), ks, lane);
+        read_frag<BM, BK, AK>(a[q][0], As[cur], wm * WM, ks, lane);
         if constexpr (decltype(ordered)::value) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -442,7 +451,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         }
 #pragma unroll
         for (int i = 1; i < TM; ++i) {
-          read_frag<BM, BK, AK>(a[q][i], As[cur], wm * (BM / 2) + i * 32, ks, lane);
+          read_frag<BM, BK, AK>(a[q][i], As[cur], wm * WM + i * 32, ks, lane);
           if constexpr (decltype(ordered)::value) __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -467,7 +476,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     __syncthreads();
   }
 
-  const int64_t mw = m0 + wm * (BM / 2), nw = n0 + wn * WN;
+  const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
   // Epilogue, one 32-row slab of the wavefront tile at a time: transform
   // the accumulators in their MFMA layout, stage the slab in LDS as fp32,
   // then write it back with 4-column vectors; all LDS reads of a slab are
@@ -485,7 +494,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
   static_assert(NVS % NCH == 0, "value chunks must tile the slab");
   using AuxT = typename EP::Aux;
   constexpr int AUXR = kAux ? (int)(sizeof(AuxT) / 4) : 0;  // VGPRs per aux vector
-  constexpr int NB = (kAux && 2 * NVS * AUXR <= 64 && TM > 1) ? 2 : 1;
+  constexpr int NB = (kAux && NW == 4 && 2 * NVS * AUXR <= 64 && TM > 1) ? 2 : 1;
   // A tile wholly inside C takes the branch-free form: every 4-column vector
   // is whole and in range (per-vector range checks put each aux load on its
   // own branch, and the loads then issue one at a time).
