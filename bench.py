@@ -73,8 +73,8 @@ ROOF_KERNELS = {
     "wgrad": dict(
         sites="gemm.qkv.wgrad,gemm.fc.wgrad,gemm.mp.wgrad,gemm.o.wgrad",
         desc="weight-gradient GEMMs of the blocks, split-K partial sums (their reduction, "
-             "splitk_reduce_kernel, is timed apart): gemm_bf16_kernel<256 or 128, 256 or 128, 64, "
-             "false, false, 0, PreId, PreId, EpPart, NoDeq>",
+             "splitk_reduce_kernel, is timed apart): gemm_bf16_kernel<256, 256, 64, false, false, 0, "
+             "PreId, PreId, EpPart, NoDeq, 8> (8 wavefronts) and <128, 128, ..., EpPart, NoDeq, 4>",
         flops=_wgrad_flops, pmc="profiles/gemm_wgrad_d12_pmc.txt"),
     "lm_fwd": dict(
         sites="gemm.lm.fwd", desc="lm_head GEMM + tanh softcap epilogue",

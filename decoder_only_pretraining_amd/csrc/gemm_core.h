@@ -61,17 +61,20 @@ struct TileGeom {
   }
 };
 
-template <int ROWS, int BK, bool KMAJ>
+// Register-staged stage fill by NTHR threads (NV 16-byte vectors each).
+template <int ROWS, int BK, bool KMAJ, int NTHR = 256>
 struct Loader {
   using Geo = TileGeom<ROWS, BK, KMAJ>;
-  U128 raw[Geo::NV];
-  bool ok[Geo::NV];
+  static constexpr int NV = ROWS * BK / 8 / NTHR;
+  static_assert(NV >= 1 && ROWS * BK / 8 % NTHR == 0, "whole vectors per thread");
+  U128 raw[NV];
+  bool ok[NV];
 
   __device__ __forceinline__ void load(const bf16* __restrict__ p, int64_t ld, int64_t mn0,
                                        int64_t MN, int64_t k0, int64_t khi, int tid) {
 #pragma unroll
-    for (int i = 0; i < Geo::NV; ++i) {
-      const int v = tid + i * 256;
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + i * NTHR;
       int64_t mn, k;
       if (KMAJ) {
         mn = mn0 + v / Geo::G;
@@ -92,8 +95,8 @@ struct Loader {
   __device__ __forceinline__ void store(bf16* lds, int64_t mn0, int64_t k0, int tid,
                                         const PRE& pre) {
 #pragma unroll
-    for (int i = 0; i < Geo::NV; ++i) {
-      const int v = tid + i * 256;
+    for (int i = 0; i < NV; ++i) {
+      const int v = tid + i * NTHR;
       if (PRE::kActive && ok[i]) {
         bf16* e = reinterpret_cast<bf16*>(&raw[i]);
         int64_t mn, k;
@@ -292,10 +295,10 @@ __device__ __forceinline__ void interleave_mfma_ds() {
   }
 }
 
-// NW = 4: wavefronts in a 2 x 2 grid, one per SIMD. NW = 8 (bf16, both
-// operands K-major): a 4 x 2 grid of (BM/4) x (BN/2) wavefront tiles, two
-// wavefronts per SIMD, so one's LDS reads and waits overlap the other's
-// MFMAs (half the accumulators per wavefront, more fragment reads per MFMA).
+// NW = 4: wavefronts in a 2 x 2 grid, one per SIMD. NW = 8 (bf16): a 4 x 2
+// grid of (BM/4) x (BN/2) wavefront tiles, two wavefronts per SIMD, so one's
+// LDS reads and waits overlap the other's MFMAs (half the accumulators per
+// wavefront, more fragment reads per MFMA).
 template <int BM, int BN, int BK, bool AK, bool BKM, int MODE, class PA, class PB, class EP,
           class DQ, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
   constexpr bool F8 = MODE != 0;
   static_assert(!F8 || (AK && BKM), "fp8 products take K-major operands");
   static_assert(F8 == DQ::kOn, "fp8 products need a dequantisation");
-  static_assert(NW == 4 || (NW == 8 && AK && BKM && !F8), "8 wavefronts: bf16, K-major operands");
+  static_assert(NW == 4 || (NW == 8 && !F8), "8 wavefronts: bf16 products");
   using GA = TileGeom<BM, BK, AK>;
   using GB = TileGeom<BN, BK, BKM>;
   constexpr int WGM = NW / 2;            // wavefront rows of the block grid
@@ -371,8 +374,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
   constexpr bool kDirect = AK && BKM;
   using DA = DirectLoader<BM, BK, AK>;
   using DB = DirectLoader<BN, BK, BKM>;
-  Loader<BM, BK, AK> ra;
-  Loader<BN, BK, BKM> rb;
+  Loader<BM, BK, AK, 64 * NW> ra;
+  Loader<BN, BK, BKM, 64 * NW> rb;
   auto fetch = [&](int64_t k0, int buf) {
     if constexpr (kDirect) {
       DA::issue(A, lda, m0, M, k0, k_hi, As[buf], wave, lane, NW);
