@@ -24,12 +24,15 @@ Pages cited (by title and section):
 Functions whose result the pages do not fix, and how each is pinned, are
 listed in ``oracle/model.py``'s module docstring. The gate form of the value
 embedding is "parity unpinned" with respect to the pages (one reading of a
-sentence that names a gate but not its form).
+sentence that names a gate but not its form). The same holds for the two
+model variants: the Smear gate's form and the Backout layer are readings of
+the additions page's notes (stated in ``oracle/model.py``); the tests pin the
+oracle's arithmetic for them, not the readings.
 """
 from .model import (  # noqa: F401
     layer_is_full, layer_has_ve, layout, param_offsets, unpack,
     rms_fwd, rms_bwd, rope_tables, rope_fwd, rope_bwd, attention_fwd,
     attention_bwd, softcap_ce_fwd_bwd, forward_backward, forward_loss,
-    visible, model_flops_per_token,
+    visible, model_flops_per_token, smear_fwd, smear_bwd, backout_layer,
 )
 from . import fp8  # noqa: F401

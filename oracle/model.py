@@ -38,6 +38,21 @@ Nanochatåœ¨nanoGPTä¹‹ä¸Šçš„æ–°å¢žåŠŸèƒ½; "overview" = nanochat â€” æž¶æž„ä¸ŽåŽŸç
 * Cross-entropy averaged over targets that are not -1 (overview section 4,
   the -1 ignore index).
 * Attention scale 1/sqrt(D).
+
+Model variants (workload flags ``smear`` and ``backout``; "additions",
+feature table rows Smear and Backout and the notes on them):
+
+* Smear: x <- x + sigmoid(gate(x)) * x_prev at the embedding. Readings:
+  gate is a bias-free linear map C -> 1 ("smear_gate" [1, C]) of the
+  current token's embedding; x_prev is the previous token's embedding in
+  the same sequence (before smearing); position 0 of a sequence has no
+  previous token and is left unchanged; the smeared embedding is the x0
+  the blocks mix in.
+* Backout: the residual stream is cached at the middle layer and
+  lambda * x_backout is subtracted before the final norm. Readings: the
+  cached stream is the one entering layer L // 2 (after the first L // 2
+  blocks); lambda is one learnable scalar ("backout_lambda" [1]); its
+  initial value (the table's "half") is the caller's.
 """
 from __future__ import annotations
 
@@ -82,7 +97,12 @@ def layout(cfg):
                 (f"l{l}.fc", (F, C)), (f"l{l}.mp", (C, F))]
         if layer_has_ve(l, L):
             out += [(f"l{l}.ve", (V, Hk * D)), (f"l{l}.veg", (Hk, C))]
-    out += [("lm_head", (V, C)), ("resid_lambdas", (L,)), ("x0_lambdas", (L,))]
+    out += [("lm_head", (V, C))]
+    if getattr(cfg, "smear", False):
+        out += [("smear_gate", (1, C))]
+    if getattr(cfg, "backout", False):
+        out += [("backout_lambda", (1,))]
+    out += [("resid_lambdas", (L,)), ("x0_lambdas", (L,))]
     return out
 
 
@@ -278,6 +298,43 @@ def _sigmoid(a):
     return 1.0 / (1.0 + np.exp(-a))
 
 
+def smear_fwd(e, w, B, T):
+    """Smear ("additions" notes on Smear), readings as in the header:
+    x0[b, t] = e[b, t] + sigmoid(e[b, t] . w) * e[b, t - 1] for t >= 1 and
+    x0[b, 0] = e[b, 0]. e [B*T, C], w [1, C]. Returns x0 [B*T, C] and the
+    gate values s [B, T] (s[:, 0] = 0: no gate there)."""
+    C = e.shape[-1]
+    e3 = e.reshape(B, T, C)
+    s = np.zeros((B, T), dtype=e.dtype)
+    s[:, 1:] = _sigmoid(e3[:, 1:] @ w.reshape(C))
+    x0 = e3.copy()
+    x0[:, 1:] += s[:, 1:, None] * e3[:, :-1]
+    return x0.reshape(B * T, C), s
+
+
+def smear_bwd(gx0, e, w, s, B, T):
+    """Gradients of smear_fwd: (g_e [B*T, C], g_w [1, C]).
+    Through x_prev: g_e[t - 1] += s[t] g[t]. Through the gate:
+    dL/dz[t] = s[t] (1 - s[t]) <g[t], e[t - 1]>, z[t] = e[t] . w, so
+    g_e[t] += dL/dz[t] w and g_w += dL/dz[t] e[t]."""
+    C = e.shape[-1]
+    g3 = gx0.reshape(B, T, C)
+    e3 = e.reshape(B, T, C)
+    ge = g3.copy()
+    ge[:, :-1] += s[:, 1:, None] * g3[:, 1:]
+    gs = np.sum(g3[:, 1:] * e3[:, :-1], axis=-1, dtype=np.float64).astype(e.dtype)
+    gz = s[:, 1:] * (1 - s[:, 1:]) * gs
+    ge[:, 1:] += gz[..., None] * w.reshape(1, 1, C)
+    gw = gz.reshape(-1).astype(np.float64) @ e3[:, 1:].reshape(-1, C).astype(np.float64)
+    return ge.reshape(B * T, C), gw.reshape(1, C)
+
+
+def backout_layer(L: int) -> int:
+    """Backout caches the residual stream entering this layer (the middle
+    one; "additions" notes on Backout, reading in the header)."""
+    return L // 2
+
+
 # --------------------------------------------------------------------------
 # The step
 # --------------------------------------------------------------------------
@@ -389,7 +446,14 @@ def forward_backward(cfg, params, tokens, targets, dtype=np.float64,
     L = cfg.n_layer
     cos, sin = rope_tables(T, cfg.head_dim, cfg.rope_theta)
 
-    x0 = P["wte"].astype(dt)[tok.reshape(-1)]                  # [N, C]
+    smear = getattr(cfg, "smear", False)
+    backout = getattr(cfg, "backout", False)
+    e = P["wte"].astype(dt)[tok.reshape(-1)]                   # [N, C]
+    if smear:
+        wsm = P["smear_gate"].astype(dt)
+        x0, sg = smear_fwd(e, wsm, B, T)
+    else:
+        x0 = e
     xs = []
     x = x0
     acts = {}
@@ -398,24 +462,37 @@ def forward_backward(cfg, params, tokens, targets, dtype=np.float64,
         x, c = _layer_fwd(l, cfg, P, x, x0, tok, cos, sin, lin, dt)
         if return_acts:
             acts[l] = c
-    xf, rf = rms_fwd(x, cfg.norm_eps)
+    mid = backout_layer(L)
+    if backout:
+        lb = dt.type(P["backout_lambda"][0])
+        xb = x - lb * xs[mid]
+    else:
+        xb = x
+    xf, rf = rms_fwd(xb, cfg.norm_eps)
     Wlm = P["lm_head"].astype(dt)
     z = xf @ Wlm.T
     loss, gz, cz = softcap_ce_fwd_bwd(z, tgt, cfg.softcap)
     if return_acts:
-        acts["final"] = dict(x=x, xf=xf, rf=rf, c=cz, gz=gz)
+        acts["final"] = dict(x=x, xb=xb, xf=xf, rf=rf, c=cz, gz=gz, x0=x0)
     del z, cz
     G["lm_head"][...] = gz.T @ xf
-    gx = rms_bwd(gz @ Wlm, xf, rf)
+    gx = rms_bwd(gz @ Wlm, xf, rf)               # w.r.t. the final norm input
     del gz
+    if backout:
+        G["backout_lambda"][0] = -np.sum(gx * xs[mid], dtype=np.float64)
+        gbo = -lb * gx                            # joins the stream entering layer mid
     gx0 = np.zeros_like(x0)
     for l in reversed(range(L)):
         _, c = _layer_fwd(l, cfg, P, xs[l], x0, tok, cos, sin, lin, dt)
         c["x0"] = x0
         gx, g0 = _layer_bwd(l, cfg, P, c, gx, tok, cos, sin, lin, dt, G)
         gx0 += g0
+        if backout and l == mid:
+            gx = gx + gbo
         del c
     gx0 += gx                                     # layer 0 reads x = x0
+    if smear:
+        gx0, G["smear_gate"][...] = smear_bwd(gx0, e, wsm, sg, B, T)
     np.add.at(G["wte"], tok.reshape(-1), gx0)
     if return_acts:
         return loss, grads, acts
@@ -432,9 +509,15 @@ def forward_loss(cfg, params, tokens, targets, dtype=np.float64, fp8=None, fp8_r
     B, T = tok.shape
     cos, sin = rope_tables(T, cfg.head_dim, cfg.rope_theta)
     x0 = P["wte"].astype(dt)[tok.reshape(-1)]
+    if getattr(cfg, "smear", False):
+        x0, _ = smear_fwd(x0, P["smear_gate"].astype(dt), B, T)
     x = x0
+    xs = []
     for l in range(cfg.n_layer):
+        xs.append(x)
         x, _ = _layer_fwd(l, cfg, P, x, x0, tok, cos, sin, lin, dt)
+    if getattr(cfg, "backout", False):
+        x = x - dt.type(P["backout_lambda"][0]) * xs[backout_layer(cfg.n_layer)]
     xf, _ = rms_fwd(x, cfg.norm_eps)
     z = xf @ P["lm_head"].astype(dt).T
     loss, _, _ = softcap_ce_fwd_bwd(z, np.asarray(targets).reshape(-1), cfg.softcap)
@@ -448,7 +531,7 @@ def model_flops_per_token(cfg):
     L, T, W = cfg.n_layer, cfg.seq_len, cfg.short_window
     n_mat = sum(int(np.prod(s)) for n, s in layout(cfg)
                 if n.split(".")[-1] in ("q", "k", "v", "o", "fc", "mp", "veg")
-                or n == "lm_head")
+                or n in ("lm_head", "smear_gate"))
     kbar = 0.0
     for l in range(L):
         if layer_is_full(l, L):

@@ -386,8 +386,16 @@ def _torch_model_loss(cfg, params, tok, tgt, linear=F.linear):
         return torch.cat([a * cs - b * sn, a * sn + b * cs], -1)
 
     x0 = F.embedding(tk, Pt["wte"])
+    if getattr(cfg, "smear", False):
+        # previous token's embedding, zero at position 0 (gate output unused there)
+        prev = torch.cat([torch.zeros_like(x0[:, :1]), x0[:, :-1]], 1)
+        gate = torch.sigmoid(F.linear(x0, Pt["smear_gate"]))
+        x0 = x0 + gate * prev
     x = x0
+    cached = None
     for l in range(L):
+        if l == L // 2:
+            cached = x
         x = Pt["resid_lambdas"][l] * x + Pt["x0_lambdas"][l] * x0
         xn = F.rms_norm(x, (C,), eps=eps)
         q = linear(xn, Pt[f"l{l}.q"]).view(B, T, H, D)
@@ -409,19 +417,30 @@ def _torch_model_loss(cfg, params, tok, tgt, linear=F.linear):
         x = x + linear(y.transpose(1, 2).reshape(B, T, H * D), Pt[f"l{l}.o"])
         x = x + linear(F.relu(linear(F.rms_norm(x, (C,), eps=eps), Pt[f"l{l}.fc"])).square(),
                        Pt[f"l{l}.mp"])
+    if getattr(cfg, "backout", False):
+        x = x - Pt["backout_lambda"][0] * cached
     z = F.linear(F.rms_norm(x, (C,), eps=eps), Pt["lm_head"])
     c = cfg.softcap * torch.tanh(z / cfg.softcap)
     return F.cross_entropy(c.view(B * T, -1), torch.from_numpy(tgt).long().view(-1),
                            ignore_index=-1)
 
 
-@pytest.mark.parametrize("variant", ["tiny", "tiny_gqa_ignore"])
+@pytest.mark.parametrize("variant", ["tiny", "tiny_gqa_ignore", "smear_backout",
+                                     "smear_backout_L3"])
 def test_full_model_matches_torch_autograd(variant):
     cfg = W.get("tiny")
     if variant == "tiny_gqa_ignore":
         cfg = cfg.with_(n_head=4, n_kv_head=2, head_dim=32, n_layer=4, short_window=5)
+    if variant.startswith("smear_backout"):
+        cfg = cfg.with_(smear=True, backout=True)
+    if variant == "smear_backout_L3":
+        cfg = cfg.with_(n_layer=3, seq_len=20)
     offs, total = oracle.param_offsets(cfg)
     p = W.gen_params(total, cfg.n_layer, 21).astype(np.float64)
+    if cfg.smear:
+        p[offs["smear_gate"][0]:][:cfg.n_embd] *= 50     # gates away from 1/2
+    if cfg.backout:
+        p[offs["backout_lambda"][0]] = 0.5
     tok, tgt = W.split_tokens(W.gen_tokens(cfg))
     if variant == "tiny_gqa_ignore":
         tgt = tgt.copy()
@@ -590,3 +609,149 @@ def test_fp8_round_variant_only_touches_quantiser_inputs():
     l2, _ = oracle.forward_backward(cfg, p, tok, tgt, dtype=np.float32)
     l3, _ = oracle.forward_backward(cfg, p, tok, tgt, dtype=np.float32, fp8_round="bf16")
     assert l2 != l3 and abs(l2 - l3) < 1e-2 * abs(l2)
+
+
+# ---------------------------------------------------------------- Smear / Backout
+
+def _variant_params(cfg, base_cfg, p_base, w_smear=None, lam_b=None):
+    """Parameters of a variant config: the base tensors copied by name, the
+    variant's own tensors set from the arguments."""
+    offs_v, total_v = oracle.param_offsets(cfg)
+    offs_b, _ = oracle.param_offsets(base_cfg)
+    p = np.zeros(total_v)
+    for name, (o, s) in offs_b.items():
+        n = int(np.prod(s))
+        p[offs_v[name][0]:offs_v[name][0] + n] = p_base[o:o + n]
+    if "smear_gate" in offs_v:
+        o = offs_v["smear_gate"][0]
+        p[o:o + cfg.n_embd] = w_smear
+    if "backout_lambda" in offs_v:
+        p[offs_v["backout_lambda"][0]] = lam_b
+    return p
+
+
+def test_variant_layout():
+    base = W.get("tiny")
+    cfg = base.with_(smear=True, backout=True)
+    offs, total = oracle.param_offsets(cfg)
+    assert total == 590_084 + 128 + 1
+    assert offs["smear_gate"] == (offs["lm_head"][0] + 512 * 128, (1, 128))
+    assert offs["backout_lambda"] == (offs["smear_gate"][0] + 128, (1,))
+    assert offs["resid_lambdas"][0] == offs["backout_lambda"][0] + 1
+    assert [n for n, _ in oracle.layout(cfg)][-2:] == ["resid_lambdas", "x0_lambdas"]
+    assert oracle.backout_layer(12) == 6 and oracle.backout_layer(1) == 0
+
+
+def test_smear_closed_form():
+    """With w = 0 every gate is 1/2: x0[t] = e[t] + e[t-1] / 2 for t >= 1,
+    x0[0] = e[0] (no previous token)."""
+    cfg = W.get("tiny").with_(smear=True)
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 4).astype(np.float64)
+    o = offs["smear_gate"][0]
+    p[o:o + cfg.n_embd] = 0
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    _, _, acts = oracle.forward_backward(cfg, p, tok, tgt, return_acts=True)
+    wte = oracle.unpack(cfg, p)["wte"]
+    e = wte[tok]                                          # [B, T, C]
+    want = e.copy()
+    want[:, 1:] += 0.5 * e[:, :-1]
+    np.testing.assert_allclose(acts[0]["x"].reshape(e.shape), want, rtol=0, atol=1e-15)
+
+
+def test_smear_single_position_is_base_model():
+    """seq_len 1: no token has a predecessor, so Smear changes nothing (loss
+    and every shared gradient equal the base model's; the gate's is 0)."""
+    base = W.get("tiny").with_(seq_len=1, batch=6)
+    cfg = base.with_(smear=True)
+    _, tb = oracle.param_offsets(base)
+    pb = W.gen_params(tb, base.n_layer, 8).astype(np.float64)
+    pv = _variant_params(cfg, base, pb, w_smear=np.linspace(-3, 3, base.n_embd))
+    tok, tgt = W.split_tokens(W.gen_tokens(base.with_(seq_len=2)))
+    tok, tgt = tok[:, :1].copy(), tgt[:, :1].copy()
+    lb, gb = oracle.forward_backward(base, pb, tok, tgt)
+    lv, gv = oracle.forward_backward(cfg, pv, tok, tgt)
+    assert lv == lb
+    offs_v, _ = oracle.param_offsets(cfg)
+    for name, (o, s) in oracle.param_offsets(base)[0].items():
+        n = int(np.prod(s))
+        np.testing.assert_array_equal(gv[offs_v[name][0]:offs_v[name][0] + n], gb[o:o + n])
+    o = offs_v["smear_gate"][0]
+    assert not np.any(gv[o:o + cfg.n_embd])
+
+
+def test_backout_zero_lambda_is_base_model():
+    base = W.get("tiny")
+    cfg = base.with_(backout=True)
+    _, tb = oracle.param_offsets(base)
+    pb = W.gen_params(tb, base.n_layer, 9).astype(np.float64)
+    pv = _variant_params(cfg, base, pb, lam_b=0.0)
+    tok, tgt = W.split_tokens(W.gen_tokens(base))
+    lb, gb = oracle.forward_backward(base, pb, tok, tgt)
+    lv, gv = oracle.forward_backward(cfg, pv, tok, tgt)
+    assert lv == lb
+    offs_v, _ = oracle.param_offsets(cfg)
+    for name, (o, s) in oracle.param_offsets(base)[0].items():
+        n = int(np.prod(s))
+        np.testing.assert_allclose(gv[offs_v[name][0]:offs_v[name][0] + n], gb[o:o + n],
+                                   rtol=0, atol=1e-15)
+    assert gv[offs_v["backout_lambda"][0]] != 0
+
+
+def test_backout_identity_blocks_closed_form():
+    """o = mp = 0: the stream after k blocks is a_k * x0 with
+    a_k = lr_k a_{k-1} + l0_k, a_0 = 1. With 3 layers the cached stream is
+    the one entering layer 1 (a_1 x0), so the final norm sees
+    (a_3 - lambda a_1) x0; the loss then follows from torch routines."""
+    cfg = W.get("tiny").with_(n_layer=3, backout=True)
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 12).astype(np.float64) * 10
+    P = oracle.unpack(cfg, p)
+    for l in range(cfg.n_layer):
+        P[f"l{l}.o"][...] = 0
+        P[f"l{l}.mp"][...] = 0
+    lr, l0 = [0.7, 1.3, 0.9], [0.2, 0.5, -0.4]
+    P["resid_lambdas"][...] = lr
+    P["x0_lambdas"][...] = l0
+    P["backout_lambda"][...] = 0.75
+    a = [1.0]
+    for k in range(3):
+        a.append(lr[k] * a[-1] + l0[k])
+    coef = a[3] - 0.75 * a[1]
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    loss = oracle.forward_loss(cfg, p, tok, tgt)
+    x0 = torch.from_numpy(P["wte"][tok.reshape(-1)])
+    xf = F.rms_norm(coef * x0, (cfg.n_embd,), eps=2.0 ** -23)
+    z = xf @ torch.from_numpy(P["lm_head"]).T
+    ref = F.cross_entropy(15 * torch.tanh(z / 15), torch.from_numpy(tgt.reshape(-1)).long())
+    assert abs(loss - ref.item()) < 1e-12
+
+
+def test_finite_differences_smear_backout():
+    """Central differences on the two variant tensors (every smear-gate
+    entry, lambda), the lambdas and 8 entries of every other tensor."""
+    cfg = W.get("tiny").with_(smear=True, backout=True, n_layer=3, seq_len=24)
+    offs, total = oracle.param_offsets(cfg)
+    p = W.gen_params(total, cfg.n_layer, 31).astype(np.float64)
+    o = offs["smear_gate"][0]
+    p[o:o + cfg.n_embd] *= 50
+    p[offs["backout_lambda"][0]] = 0.5
+    tok, tgt = W.split_tokens(W.gen_tokens(cfg))
+    _, g = oracle.forward_backward(cfg, p, tok, tgt)
+    rng = np.random.default_rng(3)
+    idx = list(range(o, o + cfg.n_embd, 7)) + [offs["backout_lambda"][0]]
+    for name, (oo, s) in offs.items():
+        n = int(np.prod(s))
+        if name.endswith("lambdas"):
+            idx += [oo + i for i in range(n)]
+        elif name not in ("smear_gate", "backout_lambda"):
+            idx += list(oo + rng.choice(n, size=min(8, n), replace=False))
+    used = np.unique(tok)
+    ow = offs["wte"][0]
+    idx += list(ow + rng.choice(used, 12) * cfg.n_embd + rng.integers(0, cfg.n_embd, 12))
+    h = 1e-5
+    for i in idx:
+        pp = p.copy(); pp[i] += h
+        pm = p.copy(); pm[i] -= h
+        fd = (oracle.forward_loss(cfg, pp, tok, tgt) - oracle.forward_loss(cfg, pm, tok, tgt)) / (2 * h)
+        assert abs(fd - g[i]) <= 1e-6 * max(abs(g[i]), 1e-4), (i, fd, g[i])

@@ -41,6 +41,10 @@ class Workload:
     rope_theta: float = 10000.0
     norm_eps: float = 2.0 ** -23
     softcap: float = 15.0
+    # model variants of the nanochat additions page (notes on Smear and
+    # Backout); off in the configurations below
+    smear: bool = False
+    backout: bool = False
 
     @property
     def tokens_per_call(self) -> int:
