@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(PKG, "libgptstep.so")
 GPT_ABI_VERSION = 1
 GPT_DT_F32, GPT_DT_BF16 = 0, 1
 GPT_F_ACCUMULATE = 1
+GPT_F_SMEAR = 2
+GPT_F_BACKOUT = 4
 
 STATUS = {0: "GPT_OK", -1: "GPT_E_INVAL", -2: "GPT_E_NULLPTR", -3: "GPT_E_ALIGN",
           -4: "GPT_E_WORKSPACE", -5: "GPT_E_UNSUPPORTED", -6: "GPT_E_HIP"}
@@ -96,7 +98,12 @@ def _check(fn, st):
 
 
 def make_config(w, flags: int = 0, **over) -> GptConfig:
-    """GptConfig from a workload description (attribute access)."""
+    """GptConfig from a workload description (attribute access). The model
+    variant flags follow the description's ``smear`` / ``backout``."""
+    if getattr(w, "smear", False):
+        flags |= GPT_F_SMEAR
+    if getattr(w, "backout", False):
+        flags |= GPT_F_BACKOUT
     f = dict(abi_version=GPT_ABI_VERSION, n_layer=w.n_layer, n_embd=w.n_embd,
              n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
              mlp_hidden=w.mlp_hidden, vocab=w.vocab, seq_len=w.seq_len, batch=w.batch,

@@ -102,6 +102,9 @@ Dims make_dims(const gpt_config& c) {
   d.eps = c.norm_eps;
   d.cap = c.softcap;
   d.accumulate = (c.flags & GPT_F_ACCUMULATE) != 0;
+  d.smear = (c.flags & GPT_F_SMEAR) != 0;
+  d.backout = (c.flags & GPT_F_BACKOUT) != 0;
+  d.mid = d.L / 2;
   return d;
 }
 
@@ -129,7 +132,8 @@ static int validate(const gpt_config* c) {
   if (c->compute_dtype != GPT_DT_F32 && c->compute_dtype != GPT_DT_BF16)
     return fail(GPT_E_INVAL, "compute_dtype %d unknown", c->compute_dtype);
   if (c->fp8_linears != 0 && c->fp8_linears != 1) return fail(GPT_E_INVAL, "fp8_linears must be 0 or 1");
-  if (c->flags & ~GPT_F_ACCUMULATE) return fail(GPT_E_INVAL, "unknown flag bits 0x%x", c->flags);
+  if (c->flags & ~(GPT_F_ACCUMULATE | GPT_F_SMEAR | GPT_F_BACKOUT))
+    return fail(GPT_E_INVAL, "unknown flag bits 0x%x", c->flags);
   if (!(std::isfinite(c->rope_theta) && c->rope_theta > 1.0f))
     return fail(GPT_E_INVAL, "rope_theta must be finite and > 1");
   if (!(std::isfinite(c->norm_eps) && c->norm_eps > 0.0f)) return fail(GPT_E_INVAL, "norm_eps must be > 0");
@@ -162,6 +166,8 @@ std::vector<TensorInfo> param_layout(const gpt_config& c) {
     }
   }
   add("lm_head", d.V, d.C);
+  if (d.smear) add("smear_gate", 1, d.C);
+  if (d.backout) add("backout_lambda", 1, 1);
   add("resid_lambdas", d.L, 1);
   add("x0_lambdas", d.L, 1);
   return v;
@@ -181,7 +187,7 @@ Plan make_plan(const Dims& d) {
   int64_t n_elems = 0;
   {
     // total parameter count, same walk as param_layout
-    n_elems = (int64_t)d.V * d.C * 2 + 2 * d.L;
+    n_elems = (int64_t)d.V * d.C * 2 + 2 * d.L + (d.smear ? d.C : 0) + (d.backout ? 1 : 0);
     for (int l = 0; l < d.L; ++l) {
       n_elems += (int64_t)d.Qkv * d.C + (int64_t)d.C * d.Cq + 2 * (int64_t)d.F * d.C;
       if (layer_ve(l, d.L)) n_elems += (int64_t)d.V * d.Ckv + (int64_t)d.Hk * d.C;
@@ -234,11 +240,13 @@ Plan make_plan(const Dims& d) {
   p.delta = take(N * d.H * 4 + 256);  // [B][H][T], padded like lse
   p.ga = take(N * d.Hk * 4);
   p.lam_blocks = (int)((d.N + 3) / 4);
-  p.lam_part = take((size_t)d.L * p.lam_blocks * 2 * 4);
+  // one slot per layer, and one for the final norm's mix under Backout
+  p.lam_part = take((size_t)(d.L + (d.backout ? 1 : 0)) * p.lam_blocks * 2 * 4);
   p.veg_splits = veg_splits(d.N);
   p.veg_part = take((size_t)p.veg_splits * d.Hk * d.C * 4);
   p.vegrow = take(N * d.Ckv * 4);  // every model has a value-embedding layer (the last)
   p.tlink = take(2 * N * 4);
+  p.sgate = take(d.smear ? N * 4 : 0);
   {  // split-K partials: the largest over the step's split products
     int64_t pb = std::max(part_bytes_nn_splitk(d, d.N, d.C, d.V),
                           part_bytes_tn_wgrad(d, d.V, d.C, d.N));
@@ -269,7 +277,7 @@ Plan make_plan(const Dims& d) {
 }
 
 struct Offs {
-  int64_t wte, lm, lr, l0;
+  int64_t wte, lm, lr, l0, sm = -1, bo = -1;
   std::vector<int64_t> q, o, fc, mp, ve, veg;
 };
 
@@ -288,6 +296,8 @@ static Offs offsets(const gpt_config& c) {
     else if (n == "lm_head") f.lm = t.offset;
     else if (n == "resid_lambdas") f.lr = t.offset;
     else if (n == "x0_lambdas") f.l0 = t.offset;
+    else if (n == "smear_gate") f.sm = t.offset;
+    else if (n == "backout_lambda") f.bo = t.offset;
     else {
       const size_t dot = n.find('.');
       const int l = std::stoi(n.substr(1, dot - 1));
@@ -454,7 +464,13 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     });
   }
 
-  site("embed.fwd", s, [&] { launch_embed(params + F.wte, tokens, X(0), N, d.C, s); });
+  float* sgate = reinterpret_cast<float*>(W + P.sgate);
+  site("embed.fwd", s, [&] {
+    if (d.smear)
+      launch_smear_embed(d, params + F.wte, tokens, params + F.sm, X(0), sgate, s);
+    else
+      launch_embed(params + F.wte, tokens, X(0), N, d.C, s);
+  });
   for (int l = 0; l < d.L; ++l) {
     const bool ve = layer_ve(l, d.L), full = layer_full(l, d.L);
     void* xn = LY(l, P.l_xn);
@@ -512,7 +528,15 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   void* logits = W + P.logits;
   float* lossrow = reinterpret_cast<float*>(W + P.lossrow);
   float* scalars = reinterpret_cast<float*>(W + P.scalars);
-  launch_mix_norm(d, X(d.L), nullptr, nullptr, nullptr, nullptr, xf, rf, nullptr, nullptr, s);
+  // Backout: the final norm reads x - lambda * x_mid, a mix with weights
+  // (1, -lambda) kept in scalars[4], scalars[5]
+  float* bo_w = scalars + 4;
+  if (d.backout) {
+    launch_backout_weights(params + F.bo, bo_w, s);
+    launch_mix_norm(d, X(d.L), X(d.mid), bo_w, bo_w + 1, nullptr, xf, rf, nullptr, nullptr, s);
+  } else {
+    launch_mix_norm(d, X(d.L), nullptr, nullptr, nullptr, nullptr, xf, rf, nullptr, nullptr, s);
+  }
   launch_count_valid(d, targets, scalars, s);
   site("gemm.lm.fwd", s, [&] { gemm_nt_softcap(d, N, d.V, d.C, xf, wmat(F.lm), logits, s); });
   // the loss; in a backward call the logits become the logit gradient g_z
@@ -548,13 +572,28 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     sum_splits();
     site("gemm.lm.wgrad", s, [&] { ssum = gemm_tn_wgrad(d, d.V, d.C, N, logits, xf, grads + F.lm, acc, part, pcap, s); });
     sum_splits();
+    // Backout's share of the gradient w.r.t. x_mid, -lambda * g, is held in
+    // the forward's xin scratch until the backward reaches layer d.mid
+    float* gbo = reinterpret_cast<float*>(W + P.xin);
     NormBwdArgs nb{};
-    nb.mode = NB_FINAL;
     nb.gin = gtmp;
-    nb.ysrc = X(d.L);
     nb.r = rf;
     nb.gx = gx;
     nb.gxc = d.bf16 ? gxc : nullptr;
+    if (d.backout) {  // the final norm as a mix of x and x_mid with weights (1, -lambda)
+      nb.mode = NB_NORM1;
+      nb.gx_first = 1;
+      nb.x = X(d.L);
+      nb.x0 = X(d.mid);
+      nb.lam_r = bo_w;
+      nb.lam_0 = bo_w + 1;
+      nb.gx0 = gbo;
+      nb.gx0_first = 1;
+      nb.lam_part = lam_part + (size_t)d.L * P.lam_blocks * 2;
+    } else {
+      nb.mode = NB_FINAL;
+      nb.ysrc = X(d.L);
+    }
     launch_norm_bwd(d, nb, s);
     for (int l = d.L - 1; l >= 0; --l) {
       const bool ve = layer_ve(l, d.L), full = layer_full(l, d.L);
@@ -672,12 +711,25 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       nb.gx0_first = l == d.L - 1;
       nb.last_layer0 = l == 0;
       nb.lam_part = lam_part + (size_t)l * P.lam_blocks * 2;
+      nb.gadd = d.backout && l == d.mid ? gbo : nullptr;
       launch_norm_bwd(d, nb, s);
     }
-    site("embed.bwd", s, [&] { launch_rows_to_table(gx0, d.C, tokens, tlink, N, grads + F.wte, s); });
+    site("embed.bwd", s, [&] {
+      if (d.smear) {  // dL/dx0 -> dL/de (into gtmp) and the smear gate's gradient
+        launch_smear_bwd(d, gx0, params + F.wte, tokens, params + F.sm, sgate, gtmp, veg_part,
+                         P.veg_splits, grads + F.sm, s);
+        launch_rows_to_table(gtmp, d.C, tokens, tlink, N, grads + F.wte, s);
+      } else {
+        launch_rows_to_table(gx0, d.C, tokens, tlink, N, grads + F.wte, s);
+      }
+    });
     // every layer's lambda gradients in one launch (layer l's partials at
     // lam_part + l * 2 * lam_blocks)
-    launch_lambda_finalize(d, lam_part, P.lam_blocks, grads + F.lr, grads + F.l0, s);
+    launch_lambda_finalize(d, lam_part, P.lam_blocks, grads + F.lr, grads + F.l0, s, d.L);
+    // Backout: dL/dlambda = -sum g * x_mid (the second sum of the final mix's slot)
+    if (d.backout)
+      launch_lambda_finalize(d, lam_part + (size_t)d.L * P.lam_blocks * 2, P.lam_blocks, nullptr,
+                             grads + F.bo, s, 1, -1.0f);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
@@ -772,9 +824,10 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
       {"gx", P.gx, N * C * 4}, {"gxc", P.gxc, N * C * A}, {"gx0", P.gx0, N * C * 4},
       {"gu", P.gu, N * d.F * A}, {"gtmp", P.gtmp, N * C * 4}, {"gO", P.gO, N * d.Cq * A},
       {"gqkv", P.gqkv, N * d.Qkv * A}, {"delta", P.delta, N * d.H * 4},
-      {"ga", P.ga, N * d.Hk * 4}, {"lam_part", P.lam_part, (size_t)d.L * P.lam_blocks * 8},
+      {"ga", P.ga, N * d.Hk * 4}, {"lam_part", P.lam_part, (size_t)(d.L + (d.backout ? 1 : 0)) * P.lam_blocks * 8},
       {"veg_part", P.veg_part, (size_t)P.veg_splits * d.Hk * C * 4},
       {"vegrow", P.vegrow, N * (size_t)d.Ckv * 4}, {"tlink", P.tlink, 2 * N * 4},
+      {"sgate", P.sgate, d.smear ? N * 4 : 0},
       {"part", P.part, (size_t)P.part_bytes},
       {"amax", P.amax, d.fp8 ? (size_t)16 * d.L * 4 : 0},
       {"w8", P.w8, d.fp8 ? P.w8_layer * d.L : 0},

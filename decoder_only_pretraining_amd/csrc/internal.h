@@ -22,6 +22,9 @@ struct Dims {
   int act_bytes;    // 2 (bf16) or 4 (fp32)
   float theta, eps, cap;
   bool accumulate;
+  bool smear;       // Smear at the embedding (GPT_F_SMEAR)
+  bool backout;     // Backout before the final norm (GPT_F_BACKOUT)
+  int mid;          // Backout caches the stream entering this layer (L / 2)
 };
 
 Dims make_dims(const gpt_config& c);
@@ -51,6 +54,7 @@ struct Plan {
   size_t gx, gxc, gx0, gu, gtmp, gO, gqkv, delta, ga, lam_part, veg_part;
   size_t vegrow;         // fp32 [N][Hk*D] per-position value-embedding gradient rows
   size_t tlink;          // int32 [2 N] token links of the embedding-table gradients
+  size_t sgate;          // fp32 [N] Smear gate values (0 bytes without Smear)
   int lam_blocks, veg_splits;
   // fp8 linears only (0 bytes otherwise). Token-major code tensors that the
   // weight gradients contract over are stored transposed, [features][Np],
@@ -80,6 +84,18 @@ void launch_cast_t(const float* src, void* dst, void* dstT, const std::vector<in
 void launch_zero(float* p, int64_t n, hipStream_t s);
 void launch_rope_table(float* cs, int T, int D, float theta, hipStream_t s);
 void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C, hipStream_t s);
+// Smear: x0[n] = e[n] + sigmoid(<e[n], w>) e[n-1] (t >= 1), e[n] = wte[tok[n]];
+// the gate values go to sig (fp32 [N], 0 at t = 0).
+void launch_smear_embed(const Dims& d, const float* wte, const int32_t* tok, const float* w,
+                        float* x0, float* sig, hipStream_t s);
+// Smear backward: ge (fp32 [N][C]) = dL/de from g = dL/dx0, and the gate
+// weight gradient gw [C] (written, or added to with d.accumulate) through
+// `waves` fixed-order partials in part (fp32 [waves][C]).
+void launch_smear_bwd(const Dims& d, const float* g, const float* wte, const int32_t* tok,
+                      const float* w, const float* sig, float* ge, float* part, int waves,
+                      float* gw, hipStream_t s);
+// out[0] = 1, out[1] = -lam[0] (device scalars)
+void launch_backout_weights(const float* lam, float* out, hipStream_t s);
 
 // rows of x (fp32 [N][C]): if x0 != nullptr, xin = lr*x + l0*x0 (written to
 // xin_out if non-null) else xin = x; y = rms(xin) (act), r (fp32 [N]).
@@ -131,13 +147,16 @@ struct NormBwdArgs {
   int gx0_first;        // gx0 = ... instead of +=
   int last_layer0;      // layer 0: add the final gx into gx0
   float* lam_part;      // fp32 [blocks][2]
+  const float* gadd;    // fp32 [N][C] added to the gradient w.r.t. x, or null
+  int gx_first;         // NB_NORM1: gx is written without reading it
 };
 void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s);
 
-// The lambda gradients of all d.L layers: layer l's nblk partial pairs at
-// lam_part + 2 l nblk, outputs g_lr[l], g_l0[l].
+// The lambda gradients of `layers` layers: layer l's nblk partial pairs at
+// lam_part + 2 l nblk, outputs scale * sums into g_lr[l] (skipped if g_lr is
+// null) and g_l0[l].
 void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
-                            float* g_l0, hipStream_t s);
+                            float* g_l0, hipStream_t s, int layers, float scale = 1.0f);
 // splits: veg_splits(N) (each split takes at most 64 tokens)
 int veg_splits(int64_t N);
 void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* part,

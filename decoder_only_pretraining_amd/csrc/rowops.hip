@@ -127,6 +127,148 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wt
   for (int c = threadIdx.x; c < C / 4; c += blockDim.x) o[c] = s[c];
 }
 
+// ------------------------------------------------------------ Smear
+// Smear at the embedding ("Nanochat在nanoGPT之上的新增功能", feature table
+// row Smear and its note): x0[n] = e[n] + sigmoid(<e[n], w>) * e[n - 1] with
+// e[n] = wte[tok[n]], for positions t = n mod T >= 1; x0[n] = e[n] at t = 0.
+// One wavefront per row; the gate value (0 at t = 0) is kept for the
+// backward.
+template <int NC>
+__global__ __launch_bounds__(256) void smear_embed_kernel(const float* __restrict__ wte,
+                                                          const int32_t* __restrict__ tok,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ x0,
+                                                          float* __restrict__ sig, int64_t N,
+                                                          int T, int C) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int C4 = C / 4;
+  const bool has_prev = (n % T) != 0;  // uniform over the wavefront
+  const f32x4* e = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n] * C);
+  f32x4* o = reinterpret_cast<f32x4*>(x0 + n * C);
+  if (!has_prev) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (lane + i * 64 < C4) o[lane + i * 64] = e[lane + i * 64];
+    if (lane == 0) sig[n] = 0.0f;
+    return;
+  }
+  const f32x4* ep = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n - 1] * C);
+  f32x4 ev[NC], pv[NC];
+  float dot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) {
+      ev[i] = e[c4];
+      pv[i] = ep[c4];
+      const f32x4 wv = reinterpret_cast<const f32x4*>(w)[c4];
+      dot += ev[i][0] * wv[0] + ev[i][1] * wv[1] + ev[i][2] * wv[2] + ev[i][3] * wv[3];
+    }
+  }
+  dot = wave_sum(dot);
+  const float g = 1.0f / (1.0f + expf(-dot));
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) o[c4] = ev[i] + g * pv[i];
+  }
+  if (lane == 0) sig[n] = g;
+}
+
+// Backward of the smear, from g = dL/dx0 [N][C]:
+//   ge[n] = g[n] + sig[n+1] g[n+1]          (n+1 in the same sequence)
+//             + dz[n] w,  dz[n] = sig[n] (1 - sig[n]) <g[n], e[n-1]>  (t >= 1)
+//   g_w  += dz[n] e[n].
+// Wavefront k of the grid takes the rows [k per, (k+1) per) and writes its
+// g_w partial to part[k][C] (waves past `waves` write nothing); the
+// partials are then added in wavefront order.
+template <int NC>
+__global__ __launch_bounds__(256) void smear_bwd_kernel(const float* __restrict__ g,
+                                                        const float* __restrict__ wte,
+                                                        const int32_t* __restrict__ tok,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ sig,
+                                                        float* __restrict__ ge,
+                                                        float* __restrict__ part, int64_t N,
+                                                        int T, int C, int waves, int64_t per) {
+  const int lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= waves) return;
+  const int C4 = C / 4;
+  f32x4 wv[NC], acc[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c4 = lane + i * 64;
+    acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (c4 < C4) wv[i] = reinterpret_cast<const f32x4*>(w)[c4];
+  }
+  const int64_t n0 = (int64_t)k * per, n1 = min(N, n0 + per);
+  for (int64_t n = n0; n < n1; ++n) {
+    const int t = (int)(n % T);
+    f32x4 gv[NC], out[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) out[i] = gv[i] = reinterpret_cast<const f32x4*>(g + n * C)[c4];
+    }
+    if (t + 1 < T) {
+      const float sn = sig[n + 1];
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c4 = lane + i * 64;
+        if (c4 < C4) out[i] += sn * reinterpret_cast<const f32x4*>(g + (n + 1) * C)[c4];
+      }
+    }
+    if (t > 0) {
+      const f32x4* ep = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n - 1] * C);
+      const f32x4* e = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n] * C);
+      f32x4 ev[NC];
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c4 = lane + i * 64;
+        if (c4 < C4) {
+          const f32x4 pv = ep[c4];
+          ev[i] = e[c4];
+          dot += gv[i][0] * pv[0] + gv[i][1] * pv[1] + gv[i][2] * pv[2] + gv[i][3] * pv[3];
+        }
+      }
+      dot = wave_sum(dot);
+      const float sn = sig[n];
+      const float dz = sn * (1.0f - sn) * dot;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c4 = lane + i * 64;
+        if (c4 < C4) {
+          out[i] += dz * wv[i];
+          acc[i] += dz * ev[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) reinterpret_cast<f32x4*>(ge + n * C)[c4] = out[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c4 = lane + i * 64;
+    if (c4 < C4) reinterpret_cast<f32x4*>(part + (int64_t)k * C)[c4] = acc[i];
+  }
+}
+
+// The final norm's mix weights under Backout: out[0] = 1 (the stream),
+// out[1] = -lambda (the cached stream).
+__global__ void backout_weights_kernel(const float* __restrict__ lam, float* __restrict__ out) {
+  if (threadIdx.x == 0) {
+    out[0] = 1.0f;
+    out[1] = -lam[0];
+  }
+}
+
 // ------------------------------------------------------------ embedding-table gradients
 // tab[tok[n]][:] += g[n][:] for the rows g of N positions. Frequent token
 // ids would serialise per-position atomic adds on one table row, so the
@@ -354,18 +496,21 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(gpt::NormBwdArgs p, int64
       const int c4 = lane + i * 64;
       if (c4 < C4) {
         f32x4 gx = r * (g[i] - yv[i] * dot);
-        if (p.mode != gpt::NB_FINAL) gx += reinterpret_cast<const f32x4*>(p.gx + n * C)[c4];
+        if (p.mode != gpt::NB_FINAL && !p.gx_first)
+          gx += reinterpret_cast<const f32x4*>(p.gx + n * C)[c4];
         if (norm1) {
           // gx is now the gradient w.r.t. xin = lr * x + l0 * x0
           const f32x4 xv = reinterpret_cast<const f32x4*>(p.x + n * C)[c4];
           const f32x4 zv = reinterpret_cast<const f32x4*>(p.x0 + n * C)[c4];
           s_lr += gx[0] * xv[0] + gx[1] * xv[1] + gx[2] * xv[2] + gx[3] * xv[3];
           s_l0 += gx[0] * zv[0] + gx[1] * zv[1] + gx[2] * zv[2] + gx[3] * zv[3];
+          f32x4 gr = lr * gx;  // w.r.t. the block input x
+          if (p.gadd) gr += reinterpret_cast<const f32x4*>(p.gadd + n * C)[c4];
           f32x4 g0 = l0 * gx;
-          if (p.last_layer0) g0 += lr * gx;
+          if (p.last_layer0) g0 += gr;
           if (!p.gx0_first) g0 += reinterpret_cast<const f32x4*>(p.gx0 + n * C)[c4];
           reinterpret_cast<f32x4*>(p.gx0 + n * C)[c4] = g0;
-          gx = lr * gx;
+          gx = gr;
         }
         if (!(norm1 && p.last_layer0)) {
           reinterpret_cast<f32x4*>(p.gx + n * C)[c4] = gx;
@@ -402,10 +547,10 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(gpt::NormBwdArgs p, int64
 __global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __restrict__ part_all,
                                                               int nblk, int64_t stride,
                                                               float* g_lr_all, float* g_l0_all,
-                                                              int accumulate) {
+                                                              int accumulate, float scale) {
   __shared__ double red[2][256];
   const float* part = part_all + (int64_t)blockIdx.x * stride;
-  float* g_lr = g_lr_all + blockIdx.x;
+  float* g_lr = g_lr_all ? g_lr_all + blockIdx.x : nullptr;
   float* g_l0 = g_l0_all + blockIdx.x;
   double a = 0.0, b = 0.0;
   for (int i = threadIdx.x; i < nblk; i += 256) {
@@ -423,8 +568,8 @@ __global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __res
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const float va = (float)red[0][0], vb = (float)red[1][0];
-    *g_lr = accumulate ? *g_lr + va : va;
+    const float va = (float)(scale * red[0][0]), vb = (float)(scale * red[1][0]);
+    if (g_lr) *g_lr = accumulate ? *g_lr + va : va;
     *g_l0 = accumulate ? *g_l0 + vb : vb;
   }
 }
@@ -862,9 +1007,49 @@ void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s) {
 }
 
 void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
-                            float* g_l0, hipStream_t s) {
-  hipLaunchKernelGGL(lambda_finalize_kernel, dim3((unsigned)d.L), dim3(256), 0, s, lam_part, nblk,
-                     (int64_t)nblk * 2, g_lr, g_l0, d.accumulate ? 1 : 0);
+                            float* g_l0, hipStream_t s, int layers, float scale) {
+  hipLaunchKernelGGL(lambda_finalize_kernel, dim3((unsigned)layers), dim3(256), 0, s, lam_part,
+                     nblk, (int64_t)nblk * 2, g_lr, g_l0, d.accumulate ? 1 : 0, scale);
+}
+
+void launch_smear_embed(const Dims& d, const float* wte, const int32_t* tok, const float* w,
+                        float* x0, float* sig, hipStream_t s) {
+  const dim3 grid((unsigned)((d.N + 3) / 4));
+  const int nc = (d.C + 255) / 256;
+#define SM_CALL(NC)                                                                             \
+  hipLaunchKernelGGL(smear_embed_kernel<NC>, grid, dim3(256), 0, s, wte, tok, w, x0, sig, d.N, \
+                     d.T, d.C)
+  if (nc <= 1) SM_CALL(1);
+  else if (nc == 2) SM_CALL(2);
+  else if (nc == 3) SM_CALL(3);
+  else if (nc <= 4) SM_CALL(4);
+  else if (nc <= 6) SM_CALL(6);
+  else SM_CALL(8);
+#undef SM_CALL
+}
+
+void launch_smear_bwd(const Dims& d, const float* g, const float* wte, const int32_t* tok,
+                      const float* w, const float* sig, float* ge, float* part, int waves,
+                      float* gw, hipStream_t s) {
+  const int64_t per = (d.N + waves - 1) / waves;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  const int nc = (d.C + 255) / 256;
+#define SB_CALL(NC)                                                                               \
+  hipLaunchKernelGGL(smear_bwd_kernel<NC>, grid, dim3(256), 0, s, g, wte, tok, w, sig, ge, part, \
+                     d.N, d.T, d.C, waves, per)
+  if (nc <= 1) SB_CALL(1);
+  else if (nc == 2) SB_CALL(2);
+  else if (nc == 3) SB_CALL(3);
+  else if (nc <= 4) SB_CALL(4);
+  else if (nc <= 6) SB_CALL(6);
+  else SB_CALL(8);
+#undef SB_CALL
+  hipLaunchKernelGGL(veg_finalize_kernel, dim3((unsigned)((d.C + 63) / 64)), dim3(256), 0, s,
+                     part, gw, d.C, waves, d.accumulate ? 1 : 0);
+}
+
+void launch_backout_weights(const float* lam, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(backout_weights_kernel, dim3(1), dim3(64), 0, s, lam, out);
 }
 
 int veg_splits(int64_t N) { return (int)std::max<int64_t>(256, (N + kVegPer - 1) / kVegPer); }

@@ -50,7 +50,17 @@ enum { GPT_DT_F32 = 0, GPT_DT_BF16 = 1 };
 
 /* flags */
 enum {
-  GPT_F_ACCUMULATE = 1     /* grads += new grads instead of grads = new grads */
+  GPT_F_ACCUMULATE = 1,    /* grads += new grads instead of grads = new grads */
+  /* Model variants of the additions page (feature table rows Smear and
+   * Backout, and the notes on them). Readings where the page is silent:
+   * Smear: x0[b,t] = e[b,t] + sigmoid(<e[b,t], smear_gate>) * e[b,t-1] for
+   *   t >= 1 and x0[b,0] = e[b,0], e = wte[tokens] (the gate is a bias-free
+   *   linear map C -> 1 of the current token's embedding; x0 is the stream
+   *   entering layer 0 and the one every block mixes in).
+   * Backout: the final norm reads x - backout_lambda * x_mid, where x_mid
+   *   is the residual stream entering layer n_layer / 2. */
+  GPT_F_SMEAR = 2,
+  GPT_F_BACKOUT = 4
 };
 
 /*
@@ -97,11 +107,12 @@ int gpt_config_validate(const gpt_config* cfg);
  *   per layer l: l.q [H*D, C], l.k [Hk*D, C], l.v [Hk*D, C], l.o [C, H*D],
  *                l.fc [F, C], l.mp [C, F], and on value-embedding layers
  *                l.ve [V, Hk*D], l.veg [Hk, C];
- *   lm_head [V, C]; resid_lambdas [L]; x0_lambdas [L].
+ *   lm_head [V, C]; with GPT_F_SMEAR smear_gate [1, C]; with GPT_F_BACKOUT
+ *   backout_lambda [1]; resid_lambdas [L]; x0_lambdas [L].
  * Linear weights are [out, in] (y = x W^T). Names are "wte", "l3.q", ...
  * gpt_param_count: number of tensors and total element count.
  * gpt_param_info: tensor i's name (NUL-terminated, < 64 bytes), element
- * offset, rows and cols (cols = 1 for the lambda vectors).
+ * offset, rows and cols (cols = 1 for the lambda vectors and backout_lambda).
  */
 int gpt_param_count(const gpt_config* cfg, int64_t* n_tensors, int64_t* n_elems);
 int gpt_param_info(const gpt_config* cfg, int64_t i, char name[64],
@@ -134,7 +145,8 @@ int gpt_workspace_size(const gpt_config* cfg, size_t* bytes);
  * "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga", "lam_part",
  * "veg_part", "part" (split-K partials; 0 bytes when no product is split),
  * "vegrow" (per-position value-embedding gradient rows, fp32 [N, Hk*D]),
- * "tlink" (int32 [2N] token links of the embedding-table gradients);
+ * "tlink" (int32 [2N] token links of the embedding-table gradients),
+ * "sgate" (fp32 [N] Smear gate values; 0 bytes without GPT_F_SMEAR);
  * per layer "r1", "rqk", "a", "lse", "r2". With fp8_linears = 1 also "amax", "w8", "w8t", "q8", "g8t" and per
  * layer "x8t", "a8t", "x28t", "h8t" (fp8 codes; 0 bytes otherwise).
  * All regions are disjoint. `layer` is ignored for global regions.

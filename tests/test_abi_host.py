@@ -35,9 +35,14 @@ def test_abi_version():
     assert B.lib().gpt_abi_version() == B.GPT_ABI_VERSION
 
 
-@pytest.mark.parametrize("name", list(W.CONFIGS))
+VARIANTS = {"tiny_smear": W.get("tiny").with_(smear=True),
+            "tiny_backout": W.get("tiny").with_(backout=True),
+            "d12_smear_backout": W.get("d12").with_(smear=True, backout=True)}
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS) + list(VARIANTS))
 def test_layout_matches_oracle(name):
-    w = W.get(name)
+    w = VARIANTS[name] if name in VARIANTS else W.get(name)
     cfg = B.make_config(w, fp8_linears=0)
     lay = B.param_layout(cfg)
     ref = [(n, o, s) for n, (o, s) in oracle.param_offsets(w)[0].items()]
@@ -73,6 +78,8 @@ def test_validation_errors():
     assert B.validate(B.make_config(w, fp8_linears=1)) == -1
     assert "bf16" in B.lib().gpt_last_error().decode()
     assert B.validate(B.make_config(w, fp8_linears=1, compute_dtype=B.GPT_DT_BF16)) == 0
+    # the model-variant flags are known bits
+    assert B.validate(B.make_config(w, flags=B.GPT_F_SMEAR | B.GPT_F_BACKOUT | 1)) == 0
     assert B.lib().gpt_config_validate(None) == -2
 
 
@@ -115,16 +122,18 @@ def test_entry_points_reject_bad_pointers_before_any_launch():
 
 GLOBAL_REGIONS = ["wc", "wct", "rope", "xin", "xf", "rf", "logits", "lossrow",
                   "scalars", "gx", "gxc", "gx0", "gu", "gtmp", "gO", "gqkv", "delta", "ga",
-                  "lam_part", "veg_part", "vegrow", "tlink", "part", "amax", "w8", "w8t", "q8", "g8t"]
+                  "lam_part", "veg_part", "vegrow", "tlink", "sgate", "part", "amax", "w8", "w8t", "q8", "g8t"]
 LAYER_REGIONS = ["xn", "r1", "qkv", "rqk", "a", "attn", "lse", "xmid", "xn2", "r2", "h",
                  "x8t", "a8t", "x28t", "h8t"]
 
 
 @pytest.mark.parametrize("name,fp8", [("tiny", 0), ("d12", 0), ("d12_gqa", 0), ("d26", 0),
-                                      ("d26", 1), ("small_fp8", 1)])
+                                      ("d26", 1), ("small_fp8", 1), ("d12_smear_backout", 0)])
 def test_workspace_regions_disjoint(name, fp8):
-    w = W.get(name) if name != "small_fp8" else W.get("d12").with_(
+    w = W.get(name) if name not in ("small_fp8", "d12_smear_backout") else W.get("d12").with_(
         n_layer=3, seq_len=200, batch=1, vocab=1024, fp8_linears=True)
+    if name == "d12_smear_backout":
+        w = VARIANTS[name]
     cfg = B.make_config(w, fp8_linears=fp8)
     ws = B.workspace_size(cfg)
     N, Np = w.batch * w.seq_len, (w.batch * w.seq_len + 127) // 128 * 128
@@ -145,6 +154,11 @@ def test_workspace_regions_disjoint(name, fp8):
     for (n1, o1, b1), (n2, o2, b2) in zip(spans, spans[1:]):
         assert o1 + b1 <= o2, (n1, n2)
     assert all(o % 256 == 0 for _, o, _ in spans)
+    N_sg = B.workspace_region(cfg, "sgate", 0)[1]
+    assert N_sg == (4 * N if getattr(w, "smear", False) else 0)
+    lam = B.workspace_region(cfg, "lam_part", 0)[1]
+    slots = w.n_layer + (1 if getattr(w, "backout", False) else 0)
+    assert lam >= slots * ((N + 3) // 4) * 2 * 4
     assert spans[-1][1] + spans[-1][2] <= ws
 
 
