@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
                     [--fp8 auto|on|off] [--no-cpu-baseline] [--roofline-kernel K]
+                    [--smear] [--backout]
 
 One step = one gpt_fwd_bwd call (loss + every parameter gradient) over one
 batch of seeded synthetic tokens, inputs already resident in HBM. Prints one
@@ -45,7 +46,7 @@ def model_flops_per_token(w) -> float:
     C, H, Hk, D, F, V, L = (w.n_embd, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden,
                             w.vocab, w.n_layer)
     T, Wn = w.seq_len, w.short_window
-    n_mat = V * C
+    n_mat = V * C + (C if w.smear else 0)
     kbar = 0.0
     for l in range(L):
         n_mat += (H + 2 * Hk) * D * C + C * H * D + 2 * F * C
@@ -61,7 +62,7 @@ def model_flops_per_token(w) -> float:
 
 # Kernels the roofline figure can be taken for: the launch sites that run
 # it (timed with HIP events on the call's stream) and the algorithmic FLOPs
-# of those launches in one step.
+# (MFMA-bound) or HBM bytes (bandwidth-bound) of those launches in one step.
 def _wgrad_flops(w):
     N = w.batch * w.seq_len
     C, Cq, Qkv, F = (w.n_embd, w.n_head * w.head_dim,
@@ -79,13 +80,19 @@ ROOF_KERNELS = {
     "lm_fwd": dict(
         sites="gemm.lm.fwd", desc="lm_head GEMM + tanh softcap epilogue",
         flops=lambda w: 2.0 * w.batch * w.seq_len * w.vocab * w.n_embd, pmc=None),
+    # the embedding gather (with --smear: the fused smear, which reads the
+    # current and the previous token's rows and writes the mixed row)
+    "embed_fwd": dict(
+        sites="embed.fwd", bound="hbm",
+        desc="embedding gather (smear_embed_kernel with --smear, else embed_kernel)",
+        bytes=lambda w: (12.0 if w.smear else 8.0) * w.n_embd * w.batch * w.seq_len, pmc=None),
 }
 
 
 def param_total(w) -> int:
     C, H, Hk, D, F, V, L = (w.n_embd, w.n_head, w.n_kv_head, w.head_dim, w.mlp_hidden,
                             w.vocab, w.n_layer)
-    n = 2 * V * C + 2 * L
+    n = 2 * V * C + 2 * L + (C if w.smear else 0) + (1 if w.backout else 0)
     for l in range(L):
         n += (H + 2 * Hk) * D * C + C * H * D + 2 * F * C
         if _ve(l, L):
@@ -122,6 +129,9 @@ def main():
     ap.add_argument("--fp8", default="auto", choices=["auto", "on", "off"],
                     help="block linears in fp8 (auto: as the workload defines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--smear", action="store_true", help="the Smear model variant")
+    ap.add_argument("--backout", action="store_true",
+                    help="the Backout model variant (lambda 0.5)")
     ap.add_argument("--cpu-rows", type=int, default=3)
     ap.add_argument("--roofline-kernel", default="wgrad", choices=sorted(ROOF_KERNELS),
                     help="kernel whose launches are timed with HIP events for the roofline")
@@ -149,8 +159,12 @@ def main():
     w = W.get(args.config)
     if args.fp8 != "auto":
         w = w.with_(fp8_linears=args.fp8 == "on")
+    w = w.with_(smear=args.smear, backout=args.backout)
     total = param_total(w)
     params = W.gen_params(total, w.n_layer, W.weight_seed(w))
+    if w.backout:  # the additions page's table: Backout subtracts half
+        lay = {n: o for n, o, _, _ in B.param_layout(B.make_config(w))}
+        params[lay["backout_lambda"]] = 0.5
     tokens, targets = W.split_tokens(W.gen_tokens(w))
     step = B.Step(w, params, tokens, targets, device="cuda:0")
     stream = torch.cuda.current_stream()
@@ -182,11 +196,20 @@ def main():
     frac = tps * mflop / PEAK_BF16_FLOPS
 
     roof = None
-    if kern_n > 0:
+    if kern_n > 0 and roof_k.get("bound", "mfma") == "hbm":
+        nbytes = roof_k["bytes"](w) * args.steps
+        achieved = nbytes / (kern_ms / 1e3) / 1e9
+        roof = {"kernel": roof_k["desc"], "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                "frac": round(achieved / (PEAK_HBM_BYTES / 1e9), 4),
+                "traffic": None, "launches": kern_n,
+                "avg_launch_ms": round(kern_ms / kern_n, 4),
+                "algorithmic_bytes_per_launch": round(nbytes / kern_n)}
+    elif kern_n > 0:
         flops = roof_k["flops"](w) * args.steps
         achieved = flops / (kern_ms / 1e3) / 1e12
         traffic = None
-        if roof_k["pmc"] and w.name == "d12":
+        if roof_k["pmc"] and w.name == "d12" and not (w.smear or w.backout):
             from decoder_only_pretraining_amd.profiling import traffic_for
             traffic = traffic_for(os.path.join(ROOT, roof_k["pmc"]))
         roof = {"kernel": roof_k["desc"], "bound": "mfma", "achieved": round(achieved, 1),
@@ -207,7 +230,9 @@ def main():
                                f"{w.n_head}/{w.n_kv_head}, head_dim {w.head_dim}, MLP "
                                f"{w.mlp_hidden}, vocab {w.vocab}, seq {w.seq_len}, batch "
                                f"{w.batch}, window {w.short_window}"
-                               + (", fp8 block linears" if w.fp8_linears else ""),
+                               + (", fp8 block linears" if w.fp8_linears else "")
+                               + (", smear" if w.smear else "")
+                               + (", backout (lambda 0.5)" if w.backout else ""),
                    "seq_len": w.seq_len, "batch": w.batch, "tokens_per_step": ntok,
                    "parallelism": "none (1 GPU)"},
         "mfma_util_vs_bf16_peak": round(frac, 4),

@@ -716,8 +716,9 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     }
     site("embed.bwd", s, [&] {
       if (d.smear) {  // dL/dx0 -> dL/de (into gtmp) and the smear gate's gradient
+        // its partials (smear_blocks(N) <= veg_splits rows of C) reuse veg_part
         launch_smear_bwd(d, gx0, params + F.wte, tokens, params + F.sm, sgate, gtmp, veg_part,
-                         P.veg_splits, grads + F.sm, s);
+                         grads + F.sm, s);
         launch_rows_to_table(gtmp, d.C, tokens, tlink, N, grads + F.wte, s);
       } else {
         launch_rows_to_table(gx0, d.C, tokens, tlink, N, grads + F.wte, s);

@@ -90,10 +90,11 @@ void launch_smear_embed(const Dims& d, const float* wte, const int32_t* tok, con
                         float* x0, float* sig, hipStream_t s);
 // Smear backward: ge (fp32 [N][C]) = dL/de from g = dL/dx0, and the gate
 // weight gradient gw [C] (written, or added to with d.accumulate) through
-// `waves` fixed-order partials in part (fp32 [waves][C]).
+// smear_blocks(N) fixed-order partials in part (fp32 [smear_blocks(N)][C]).
+int smear_blocks(int64_t N);
 void launch_smear_bwd(const Dims& d, const float* g, const float* wte, const int32_t* tok,
-                      const float* w, const float* sig, float* ge, float* part, int waves,
-                      float* gw, hipStream_t s);
+                      const float* w, const float* sig, float* ge, float* part, float* gw,
+                      hipStream_t s);
 // out[0] = 1, out[1] = -lam[0] (device scalars)
 void launch_backout_weights(const float* lam, float* out, hipStream_t s);
 

@@ -181,9 +181,13 @@ __global__ __launch_bounds__(256) void smear_embed_kernel(const float* __restric
 //   ge[n] = g[n] + sig[n+1] g[n+1]          (n+1 in the same sequence)
 //             + dz[n] w,  dz[n] = sig[n] (1 - sig[n]) <g[n], e[n-1]>  (t >= 1)
 //   g_w  += dz[n] e[n].
-// Wavefront k of the grid takes the rows [k per, (k+1) per) and writes its
-// g_w partial to part[k][C] (waves past `waves` write nothing); the
-// partials are then added in wavefront order.
+// A workgroup takes kSmearRows consecutive rows, 16 per wavefront in groups
+// of 4 whose gradient and embedding rows are loaded together (row n needs
+// g[n], g[n+1], e[n-1], e[n]: 5 + 5 row loads per group of 4). The g_w
+// terms are summed in registers, then over the 4 wavefronts in LDS, and the
+// workgroup writes its partial part[blockIdx][C]; the partials are added in
+// workgroup order afterwards.
+constexpr int kSmearRows = 64;
 template <int NC>
 __global__ __launch_bounds__(256) void smear_bwd_kernel(const float* __restrict__ g,
                                                         const float* __restrict__ wte,
@@ -192,72 +196,81 @@ __global__ __launch_bounds__(256) void smear_bwd_kernel(const float* __restrict_
                                                         const float* __restrict__ sig,
                                                         float* __restrict__ ge,
                                                         float* __restrict__ part, int64_t N,
-                                                        int T, int C, int waves, int64_t per) {
-  const int lane = threadIdx.x & 63;
-  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (k >= waves) return;
+                                                        int T, int C) {
+  constexpr int RG = 4, GROUPS = kSmearRows / 4 / RG;
+  __shared__ f32x4 red[4][NC * 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int C4 = C / 4;
-  f32x4 wv[NC], acc[NC];
+  f32x4 wgt[NC], acc[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const int c4 = lane + i * 64;
     acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (c4 < C4) wv[i] = reinterpret_cast<const f32x4*>(w)[c4];
+    wgt[i] = acc[i];
+    if (c4 < C4) wgt[i] = reinterpret_cast<const f32x4*>(w)[c4];
   }
-  const int64_t n0 = (int64_t)k * per, n1 = min(N, n0 + per);
-  for (int64_t n = n0; n < n1; ++n) {
-    const int t = (int)(n % T);
-    f32x4 gv[NC], out[NC];
+  const int64_t base = (int64_t)blockIdx.x * kSmearRows + wv * (kSmearRows / 4);
+  for (int gi = 0; gi < GROUPS; ++gi) {
+    const int64_t n0 = base + gi * RG;
+    if (n0 >= N) break;  // uniform over the wavefront
+    f32x4 G[RG + 1][NC], E[RG + 1][NC];  // G[j] = g[n0 + j], E[j] = e[n0 - 1 + j]
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c4 = lane + i * 64;
-      if (c4 < C4) out[i] = gv[i] = reinterpret_cast<const f32x4*>(g + n * C)[c4];
-    }
-    if (t + 1 < T) {
-      const float sn = sig[n + 1];
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c4 = lane + i * 64;
-        if (c4 < C4) out[i] += sn * reinterpret_cast<const f32x4*>(g + (n + 1) * C)[c4];
-      }
-    }
-    if (t > 0) {
-      const f32x4* ep = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n - 1] * C);
-      const f32x4* e = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n] * C);
-      f32x4 ev[NC];
-      float dot = 0.0f;
+    for (int j = 0; j <= RG; ++j) {
+      const int64_t n = n0 + j, m = n0 - 1 + j;
+      const f32x4* gr = reinterpret_cast<const f32x4*>(g + (n < N ? n : 0) * C);
+      const f32x4* er = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[m >= 0 && m < N ? m : 0] * C);
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
         const int c4 = lane + i * 64;
         if (c4 < C4) {
-          const f32x4 pv = ep[c4];
-          ev[i] = e[c4];
-          dot += gv[i][0] * pv[0] + gv[i][1] * pv[1] + gv[i][2] * pv[2] + gv[i][3] * pv[3];
-        }
-      }
-      dot = wave_sum(dot);
-      const float sn = sig[n];
-      const float dz = sn * (1.0f - sn) * dot;
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const int c4 = lane + i * 64;
-        if (c4 < C4) {
-          out[i] += dz * wv[i];
-          acc[i] += dz * ev[i];
+          G[j][i] = gr[c4];
+          E[j][i] = er[c4];
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int c4 = lane + i * 64;
-      if (c4 < C4) reinterpret_cast<f32x4*>(ge + n * C)[c4] = out[i];
+    for (int j = 0; j < RG; ++j) {
+      const int64_t n = n0 + j;
+      if (n < N) {
+        const int t = (int)(n % T);
+        f32x4 out[NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) out[i] = G[j][i];
+        if (t + 1 < T) {  // n + 1 < N: same sequence
+          const float sn1 = sig[n + 1];
+#pragma unroll
+          for (int i = 0; i < NC; ++i) out[i] += sn1 * G[j + 1][i];
+        }
+        if (t > 0) {
+          float dot = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NC; ++i)
+            if (lane + i * 64 < C4)
+              dot += G[j][i][0] * E[j][i][0] + G[j][i][1] * E[j][i][1] +
+                     G[j][i][2] * E[j][i][2] + G[j][i][3] * E[j][i][3];
+          dot = wave_sum(dot);
+          const float sn = sig[n];
+          const float dz = sn * (1.0f - sn) * dot;
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            out[i] += dz * wgt[i];
+            acc[i] += dz * E[j + 1][i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int c4 = lane + i * 64;
+          if (c4 < C4) reinterpret_cast<f32x4*>(ge + n * C)[c4] = out[i];
+        }
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c4 = lane + i * 64;
-    if (c4 < C4) reinterpret_cast<f32x4*>(part + (int64_t)k * C)[c4] = acc[i];
-  }
+  for (int i = 0; i < NC; ++i) red[wv][i * 64 + lane] = acc[i];
+  __syncthreads();
+  for (int c4 = threadIdx.x; c4 < C4; c4 += 256)
+    reinterpret_cast<f32x4*>(part + (int64_t)blockIdx.x * C)[c4] =
+        ((red[0][c4] + red[1][c4]) + red[2][c4]) + red[3][c4];
 }
 
 // The final norm's mix weights under Backout: out[0] = 1 (the stream),
@@ -580,6 +593,8 @@ __global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __res
 // range; the phases are then added in a fixed order and the block writes
 // its partial. A second kernel adds the partials in block order.
 constexpr int kVegPer = 64;
+// the smear partials (one per kSmearRows rows) fit the gate-weight partial buffer
+static_assert(kSmearRows >= kVegPer, "smear partials exceed the veg partial rows");
 template <typename T, int HK>
 __global__ __launch_bounds__(256) void veg_partial_kernel(const float* __restrict__ ga,
                                                           const T* __restrict__ xn,
@@ -1029,14 +1044,14 @@ void launch_smear_embed(const Dims& d, const float* wte, const int32_t* tok, con
 }
 
 void launch_smear_bwd(const Dims& d, const float* g, const float* wte, const int32_t* tok,
-                      const float* w, const float* sig, float* ge, float* part, int waves,
-                      float* gw, hipStream_t s) {
-  const int64_t per = (d.N + waves - 1) / waves;
-  const dim3 grid((unsigned)((waves + 3) / 4));
+                      const float* w, const float* sig, float* ge, float* part, float* gw,
+                      hipStream_t s) {
+  const int nblk = smear_blocks(d.N);
+  const dim3 grid((unsigned)nblk);
   const int nc = (d.C + 255) / 256;
 #define SB_CALL(NC)                                                                               \
   hipLaunchKernelGGL(smear_bwd_kernel<NC>, grid, dim3(256), 0, s, g, wte, tok, w, sig, ge, part, \
-                     d.N, d.T, d.C, waves, per)
+                     d.N, d.T, d.C)
   if (nc <= 1) SB_CALL(1);
   else if (nc == 2) SB_CALL(2);
   else if (nc == 3) SB_CALL(3);
@@ -1045,8 +1060,10 @@ void launch_smear_bwd(const Dims& d, const float* g, const float* wte, const int
   else SB_CALL(8);
 #undef SB_CALL
   hipLaunchKernelGGL(veg_finalize_kernel, dim3((unsigned)((d.C + 63) / 64)), dim3(256), 0, s,
-                     part, gw, d.C, waves, d.accumulate ? 1 : 0);
+                     part, gw, d.C, nblk, d.accumulate ? 1 : 0);
 }
+
+int smear_blocks(int64_t N) { return (int)((N + kSmearRows - 1) / kSmearRows); }
 
 void launch_backout_weights(const float* lam, float* out, hipStream_t s) {
   hipLaunchKernelGGL(backout_weights_kernel, dim3(1), dim3(64), 0, s, lam, out);

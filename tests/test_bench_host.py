@@ -1,0 +1,18 @@
+"""The benchmark's own size and FLOP accounting agrees with the oracle's
+parameter layout and model-FLOP count (no GPU)."""
+import pytest
+
+import bench
+import oracle
+import workloads as W
+
+CASES = [W.get(n) for n in W.CONFIGS] + [
+    W.get("d12").with_(smear=True), W.get("d12").with_(backout=True),
+    W.get("tiny").with_(smear=True, backout=True)]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: f"{w.name}-{int(w.smear)}{int(w.backout)}")
+def test_param_total_and_flops_match_oracle(w):
+    assert bench.param_total(w) == oracle.param_offsets(w)[1]
+    assert bench.model_flops_per_token(w) == pytest.approx(oracle.model_flops_per_token(w),
+                                                           rel=1e-12)
