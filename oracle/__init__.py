@@ -36,3 +36,4 @@ from .model import (  # noqa: F401
     visible, model_flops_per_token, smear_fwd, smear_bwd, backout_layer,
 )
 from . import fp8  # noqa: F401
+from . import decode  # noqa: F401

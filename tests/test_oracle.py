@@ -755,3 +755,58 @@ def test_finite_differences_smear_backout():
         pm = p.copy(); pm[i] -= h
         fd = (oracle.forward_loss(cfg, pp, tok, tgt) - oracle.forward_loss(cfg, pm, tok, tgt)) / (2 * h)
         assert abs(fd - g[i]) <= 1e-6 * max(abs(g[i]), 1e-4), (i, fd, g[i])
+
+
+# ---------------------------------------------------------------- decode attention
+
+def _decode_case(B=3, H=4, Hk=2, D=16, Tmax=40, seed=0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, D))
+    k = rng.standard_normal((B, Tmax, Hk, D))
+    v = rng.standard_normal((B, Tmax, Hk, D))
+    seqlen = rng.integers(1, Tmax + 1, B)
+    return q, k, v, seqlen
+
+
+@pytest.mark.parametrize("window", [None, 0, 5, 100])
+def test_decode_attention_matches_sdpa(window):
+    """Against torch SDPA (float64) on the cached rows, with the window as
+    an explicit boolean mask."""
+    q, k, v, seqlen = _decode_case(seed=1)
+    out = oracle.decode.decode_attention(q, k, v, seqlen, window)
+    B, H, D = q.shape
+    G = H // k.shape[2]
+    for b in range(B):
+        t = int(seqlen[b]) - 1
+        s = np.arange(k.shape[1])
+        mask = s <= t
+        if window is not None:
+            mask &= (t - s) <= window
+        kb = torch.from_numpy(k[b]).transpose(0, 1).repeat_interleave(G, 0)   # [H, Tmax, D]
+        vb = torch.from_numpy(v[b]).transpose(0, 1).repeat_interleave(G, 0)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[:, None, :], kb, vb,
+                                             attn_mask=torch.from_numpy(mask)[None, None, :])
+        np.testing.assert_allclose(out[b], ref[:, 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_decode_attention_brute_force_and_invariants():
+    q, k, v, seqlen = _decode_case(B=2, H=2, Hk=1, D=4, Tmax=6, seed=2)
+    seqlen = np.array([6, 3])
+    out = oracle.decode.decode_attention(q, k, v, seqlen, window=2)
+    # brute force with scalar loops: sequence 0 sees positions 3, 4, 5
+    for h in range(2):
+        w = [math.exp(sum(q[0, h, d] * k[0, s, 0, d] for d in range(4)) / 2.0) for s in (3, 4, 5)]
+        ref = [sum(w[i] * v[0, s, 0, d] for i, s in enumerate((3, 4, 5))) / sum(w)
+               for d in range(4)]
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-12)
+    # one visible key: the output is that value row
+    one = oracle.decode.decode_attention(q, k, v, np.array([6, 3]), window=0)
+    np.testing.assert_array_equal(one[0], np.repeat(v[0, 5], 2, 0).reshape(2, 4))
+    # a window at least as long as the sequence is the full causal case
+    np.testing.assert_allclose(oracle.decode.decode_attention(q, k, v, seqlen, 10),
+                               oracle.decode.decode_attention(q, k, v, seqlen, None), rtol=0,
+                               atol=0)
+    # equal value rows: the output is that row whatever the scores
+    v2 = np.broadcast_to(v[:, :1], v.shape)
+    o2 = oracle.decode.decode_attention(q, k, v2, seqlen, None)
+    np.testing.assert_allclose(o2[1, 0], v[1, 0, 0], rtol=1e-12)
