@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
                     [--fp8 auto|on|off] [--no-cpu-baseline] [--roofline-kernel K]
                     [--smear] [--backout]
+    python bench.py --decode [--steps K] [--warmup W]
 
 One step = one gpt_fwd_bwd call (loss + every parameter gradient) over one
 batch of seeded synthetic tokens, inputs already resident in HBM. Prints one
@@ -120,6 +121,76 @@ def cpu_baseline(w, params, tokens, targets, rows: int):
                       f"{w.name} workload, one fp32 forward+backward, {dt:.1f} s"}
 
 
+def decode_bench(args):
+    """KV-cache decode attention of the d12 model: one step = the attention
+    of all 12 layers for one new token in each of 16 sequences whose caches
+    hold 2048 positions (short-window layers read the last 513 positions,
+    the full layers all 2048). Each layer has its own cache, so the step
+    reads 1.2 GB from HBM rather than from the memory-side cache."""
+    import torch
+    from decoder_only_pretraining_amd import binding as B
+    w = W.get("d12")
+    Bs, H, Hk, D, T, L = 16, w.n_head, w.n_kv_head, w.head_dim, w.seq_len, w.n_layer
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    dev = "cuda:0"
+    wins = [-1 if _full(l, L) else w.short_window for l in range(L)]
+    q = [torch.randn(Bs, H, D, device=dev, generator=g).to(torch.bfloat16) for _ in range(L)]
+    kc = [torch.randn(Bs, T, Hk, D, device=dev, generator=g).to(torch.bfloat16) for _ in range(L)]
+    vc = [torch.randn(Bs, T, Hk, D, device=dev, generator=g).to(torch.bfloat16) for _ in range(L)]
+    out = [torch.empty_like(x) for x in q]
+    seqlen = torch.full((Bs,), T, dtype=torch.int32, device=dev)
+    ws = torch.zeros(max(B.decode_attn_workspace(Bs, H, Hk, D, T, wn) for wn in wins),
+                     dtype=torch.uint8, device=dev)  # chunk counters start at zero
+
+    def step():
+        stream = torch.cuda.current_stream()
+        for l in range(L):
+            B.decode_attn(q[l], kc[l], vc[l], seqlen, out[l], ws, wins[l], stream)
+
+    # the 24 launches of a step are captured once into a HIP graph, so the
+    # timing sees the kernels rather than the host's per-call overhead; the
+    # replays must reproduce the eager outputs bit for bit
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in out]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    assert all(torch.equal(e, o) for e, o in zip(eager, out)), "graph replay differs from eager"
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    assert all(torch.equal(e, o) for e, o in zip(eager, out)), "graph replay differs from eager"
+    ms = a.elapsed_time(b) / args.steps
+    # algorithmic bytes: visible K and V rows, q read, out written
+    kv = sum(Bs * Hk * (T if wn < 0 else min(T, wn + 1)) * D * 2 * 2 for wn in wins)
+    nbytes = kv + L * 2 * Bs * H * D * 2
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "KV-cache decode attention read rate, d12 (12 layers), 16 sequences x 2048 "
+                  "cached positions", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) q and caches)",
+        "config": {"workload": "d12 decode attention: 16 sequences, 2048 cached positions, "
+                               "heads 6/6, head_dim 128, 9 window-512 layers + 3 full",
+                   "tokens_per_step": Bs},
+        "decode_tokens_per_s_attention_only": round(Bs / (ms / 1e3), 1),
+        "roofline": {"kernel": "decode_attn_partial_kernel<128, 1> (chunk states, the last "
+                               "chunk of each sequence and KV head combines)",
+                     "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_BYTES / 1e9,
+                     "unit": "GB/s", "frac": round(gbs / (PEAK_HBM_BYTES / 1e9), 4),
+                     "traffic": None, "launches": L * args.steps,
+                     "algorithmic_bytes_per_step": nbytes}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +201,8 @@ def main():
                     help="block linears in fp8 (auto: as the workload defines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--smear", action="store_true", help="the Smear model variant")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the KV-cache decode attention instead of the training step")
     ap.add_argument("--backout", action="store_true",
                     help="the Backout model variant (lambda 0.5)")
     ap.add_argument("--cpu-rows", type=int, default=3)
@@ -152,6 +225,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is "
               "not part of this library", file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        decode_bench(args)
+        return
 
     import torch
     from decoder_only_pretraining_amd import binding as B

@@ -25,7 +25,8 @@ STATUS = {0: "GPT_OK", -1: "GPT_E_INVAL", -2: "GPT_E_NULLPTR", -3: "GPT_E_ALIGN"
 EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_param_info",
            "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region", "gpt_fwd_bwd",
            "gpt_fwd", "gpt_fp8_quantize", "gpt_status_string", "gpt_last_error",
-           "gpt_profile_begin", "gpt_profile_end"]
+           "gpt_profile_begin", "gpt_profile_end", "gpt_decode_attn_workspace",
+           "gpt_decode_attn"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -75,6 +76,9 @@ def lib():
                               c.c_void_p, c.c_size_t, c.c_void_p]
         L.gpt_fp8_quantize.argtypes = [c.c_void_p, c.c_int32, c.c_int64, c.c_int64, c.c_int32,
                                        c.c_void_p, c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p]
+        L.gpt_decode_attn_workspace.argtypes = [c.c_int32] * 6 + [P(c.c_size_t)]
+        L.gpt_decode_attn.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6 + [c.c_size_t,
+                                                                             c.c_void_p]
         L.gpt_status_string.restype = c.c_char_p
         L.gpt_status_string.argtypes = [c.c_int]
         L.gpt_last_error.restype = c.c_char_p
@@ -84,7 +88,8 @@ def lib():
         L.gpt_profile_end.restype = c.c_int
         for name in ("gpt_config_validate", "gpt_param_count", "gpt_param_info",
                      "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region",
-                     "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize"):
+                     "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize", "gpt_decode_attn_workspace",
+                     "gpt_decode_attn"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -195,6 +200,27 @@ def fp8_quantize(src, fmt, codes=None, codes_t=None, pitch_t=0, amax=None, strea
     st = lib().gpt_fp8_quantize(src.data_ptr(), dt, rows, cols, fmt, ptr(codes), ptr(codes_t),
                                 pitch_t, ptr(amax), _stream_ptr(stream))
     _check("gpt_fp8_quantize", st)
+
+
+def decode_attn_workspace(batch, n_head, n_kv_head, head_dim, max_len, window) -> int:
+    n = ctypes.c_size_t()
+    _check("gpt_decode_attn_workspace",
+           lib().gpt_decode_attn_workspace(batch, n_head, n_kv_head, head_dim, max_len, window,
+                                           ctypes.byref(n)))
+    return n.value
+
+
+def decode_attn(q, k_cache, v_cache, seqlen, out, workspace, window=-1, stream=None):
+    """Decode attention (gpt_decode_attn) on device tensors: q, out bf16
+    [B, H, D]; caches bf16 [B, Tmax, Hk, D]; seqlen int32 [B]; workspace a
+    device tensor of at least decode_attn_workspace(...) bytes."""
+    B, H, D = q.shape
+    _, Tmax, Hk, _ = k_cache.shape
+    st = lib().gpt_decode_attn(B, H, Hk, D, Tmax, window, q.data_ptr(), k_cache.data_ptr(),
+                               v_cache.data_ptr(), seqlen.data_ptr(), out.data_ptr(),
+                               workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    _check("gpt_decode_attn", st)
 
 
 def profile_begin(site_prefix: str):

@@ -906,6 +906,53 @@ int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t c
   return GPT_OK;
 }
 
+static int decode_validate(int32_t B, int32_t H, int32_t Hk, int32_t D, int32_t Tmax,
+                           int32_t window) {
+  if (B < 1 || B > 65535) return fail(GPT_E_INVAL, "batch %d not in [1, 65535]", B);
+  if (D != 64 && D != 128) return fail(GPT_E_INVAL, "head_dim %d: need 64 or 128", D);
+  if (H < 1 || Hk < 1 || H % Hk || H / Hk > 8 || Hk > 65535)
+    return fail(GPT_E_INVAL, "n_head %d / n_kv_head %d: need n_kv_head dividing n_head, at most 8 "
+                "query heads per KV head", H, Hk);
+  if (Tmax < 1 || (int64_t)B * Tmax * Hk * D > ((int64_t)1 << 40))
+    return fail(GPT_E_INVAL, "cache length %d out of range", Tmax);
+  if (window < -1) return fail(GPT_E_INVAL, "window %d: need >= 0, or -1 for full context", window);
+  return GPT_OK;
+}
+
+int gpt_decode_attn_workspace(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                              int32_t max_len, int32_t window, size_t* bytes) {
+  g_err[0] = 0;
+  const int st = decode_validate(batch, n_head, n_kv_head, head_dim, max_len, window);
+  if (st) return st;
+  if (!bytes) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  *bytes = decode_workspace_bytes(batch, n_head, n_kv_head, head_dim, max_len, window);
+  return GPT_OK;
+}
+
+int gpt_decode_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                    int32_t max_len, int32_t window, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* seqlen, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const int st = decode_validate(batch, n_head, n_kv_head, head_dim, max_len, window);
+  if (st) return st;
+  const size_t need = decode_workspace_bytes(batch, n_head, n_kv_head, head_dim, max_len, window);
+  if (!q || !k_cache || !v_cache || !seqlen || !out || (need && !workspace))
+    return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seqlen, 4) || !aligned(workspace, 256))
+    return fail(GPT_E_ALIGN, "q, caches and out need 16-byte alignment, seqlen 4, workspace 256");
+  if (workspace_bytes < need)
+    return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  launch_decode_attn(batch, n_head, n_kv_head, head_dim, max_len, window, q, k_cache, v_cache,
+                     seqlen, out, workspace, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
+  return GPT_OK;
+}
+
 const char* gpt_status_string(int status) {
   switch (status) {
     case GPT_OK: return "ok";

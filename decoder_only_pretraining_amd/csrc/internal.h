@@ -170,6 +170,16 @@ void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipSt
 void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* scalars,
                  float* lossrow, float* loss, bool grad, hipStream_t s);
 
+// Decode attention over a KV cache (decode.hip): chunks per (sequence, KV
+// head), workspace bytes (fp32 chunk states; 0 when there is one chunk), and
+// the launch (q, out bf16 [B][H][D]; k, v bf16 [B][Tmax][Hk][D]; seqlen
+// int32 [B], clamped to [1, Tmax]).
+int decode_splits(int Tmax, int window);
+size_t decode_workspace_bytes(int B, int H, int Hk, int D, int Tmax, int window);
+void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const void* q,
+                        const void* k, const void* v, const int32_t* seqlen, void* out,
+                        void* workspace, hipStream_t s);
+
 // ------------------------------------------------------------ GEMMs
 // Shapes: C[M][N] = sum_k A(m,k) B(n,k).
 // "nt": A [M][K], B [N][K] (both contraction-contiguous).

@@ -206,6 +206,41 @@ int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t c
                      uint32_t* amax, void* stream);
 
 /*
+ * Decode attention over a KV cache: the attention step of generating one
+ * token per sequence with a pre-allocated cache ("Nanochat在nanoGPT之上的新增
+ * 功能", inference engine: KV cache, batch-1 prefill then the cache copied
+ * per sample; "nanochat — 架构与原理", section 5: flash attention with a KV
+ * cache). For sequence b the newest token sits at position
+ * t = seqlen[b] - 1 (its k and v already written into the cache); query
+ * head h reads KV head h / (n_head / n_kv_head) and attends the positions s
+ * with max(0, t - window) <= s <= t (window = -1: 0 <= s <= t), with the
+ * model's softmax(q k^T / sqrt(head_dim)) (additions page, notes on GQA
+ * and the sliding window):
+ *   out[b][h] = sum_s softmax_s(q[b][h] . k[b][s][h'] / sqrt(D)) v[b][s][h'].
+ *   q        (device) bf16 [batch, n_head, head_dim] (after RoPE and QK-norm)
+ *   k_cache, v_cache (device) bf16 [batch, max_len, n_kv_head, head_dim];
+ *            rows at positions >= seqlen[b] are not read
+ *   seqlen   (device) int32 [batch]; values are clamped to [1, max_len]
+ *   out      (device) bf16 [batch, n_head, head_dim], written
+ *   workspace (device) >= gpt_decode_attn_workspace bytes (may be NULL when
+ *            that is 0): fp32 chunk states. The visible keys of each
+ *            (sequence, KV head) are split into chunks of 128 positions
+ *            whose states a second kernel combines in chunk order (one
+ *            chunk, max_len or window + 1 <= 128: no workspace). Calls that
+ *            share a workspace must not overlap.
+ * head_dim 64 or 128; n_head a multiple of n_kv_head with at most 8 query
+ * heads per KV head; window >= -1. q, caches and out 16-byte aligned,
+ * seqlen 4, workspace 256. Validation errors return before anything is
+ * enqueued; the work is enqueued on `stream`.
+ */
+int gpt_decode_attn_workspace(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                              int32_t max_len, int32_t window, size_t* bytes);
+int gpt_decode_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                    int32_t max_len, int32_t window, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* seqlen, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * Host only; measurement support. After gpt_profile_begin(prefixes), every
  * kernel launch of gpt_fwd_bwd / gpt_fwd whose launch-site name starts with
  * one of the comma-separated `prefixes` is bracketed by two HIP events

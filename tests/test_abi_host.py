@@ -176,3 +176,25 @@ def test_fp8_quantize_rejects_bad_arguments_before_any_launch():
     assert q(p, 0, 4, 64, 0, p, p, 100, p, None) == -1               # pitch % 128
     assert q(ctypes.c_void_p(4100), 0, 4, 64, 0, p, p, 128, p, None) == -3
     assert q(p, 0, 4, 64, 0, ctypes.c_void_p(4104), None, 0, p, None) == -3
+
+
+def test_decode_attn_validation_and_workspace():
+    L = B.lib()
+    # chunks of 128 visible positions per (sequence, KV head); one chunk: none
+    assert B.decode_attn_workspace(16, 6, 6, 128, 2048, -1) == 16 * 6 * 16 * 130 * 4
+    assert B.decode_attn_workspace(16, 6, 6, 128, 2048, 512) == 16 * 6 * 5 * 130 * 4
+    assert B.decode_attn_workspace(2, 8, 2, 64, 3000, -1) == 2 * 8 * 24 * 66 * 4
+    assert B.decode_attn_workspace(2, 4, 1, 64, 10, 0) == 0
+    assert B.decode_attn_workspace(2, 4, 1, 64, 128, -1) == 0
+    n = ctypes.c_size_t()
+    for bad in [(0, 6, 6, 128, 64, -1), (2, 6, 4, 128, 64, -1), (2, 18, 2, 128, 64, -1),
+                (2, 6, 6, 96, 64, -1), (2, 6, 6, 128, 0, -1), (2, 6, 6, 128, 64, -2)]:
+        assert L.gpt_decode_attn_workspace(*bad, ctypes.byref(n)) == -1, bad
+    p = ctypes.c_void_p(256)
+    ws = B.decode_attn_workspace(2, 6, 6, 128, 1024, -1)
+    assert ws > 0
+    assert L.gpt_decode_attn(2, 6, 6, 128, 1024, -1, p, p, p, p, p, None, ws, None) == -2
+    assert L.gpt_decode_attn(2, 6, 6, 128, 64, -1, None, p, p, p, p, p, ws, None) == -2
+    assert L.gpt_decode_attn(2, 6, 6, 128, 64, -1, ctypes.c_void_p(264), p, p, p, p, p, ws,
+                             None) == -3
+    assert L.gpt_decode_attn(2, 6, 6, 128, 1024, -1, p, p, p, p, p, p, ws - 1, None) == -4
