@@ -46,3 +46,21 @@ def decode_attention(q, k, v, seqlen, window=None):
             p = np.exp(s - s.max())
             out[b, h] = (p / p.sum()) @ vv
     return out
+
+
+def kv_cache_append(qkv, pos, k_cache, v_cache, n_head, n_kv_head, head_dim):
+    """Write the k and v rows of n_new tokens per sequence into the caches
+    (in place): qkv [B * n_new, (H + 2 Hk) D] holds, per token, the q heads,
+    then the k heads, then the v heads (the layout of the model's fused QKV
+    product); token i of sequence b goes to position pos[b] + i. Positions
+    outside the cache are not written."""
+    H, Hk, D = n_head, n_kv_head, head_dim
+    B, Tmax = k_cache.shape[:2]
+    n_new = qkv.shape[0] // B
+    for b in range(B):
+        for i in range(n_new):
+            p = int(pos[b]) + i
+            if 0 <= p < Tmax:
+                row = qkv[b * n_new + i]
+                k_cache[b, p] = row[H * D:(H + Hk) * D].reshape(Hk, D)
+                v_cache[b, p] = row[(H + Hk) * D:(H + 2 * Hk) * D].reshape(Hk, D)

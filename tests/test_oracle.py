@@ -810,3 +810,24 @@ def test_decode_attention_brute_force_and_invariants():
     v2 = np.broadcast_to(v[:, :1], v.shape)
     o2 = oracle.decode.decode_attention(q, k, v2, seqlen, None)
     np.testing.assert_allclose(o2[1, 0], v[1, 0, 0], rtol=1e-12)
+
+
+def test_kv_cache_append_by_hand():
+    """Every written element checked against the qkv column it comes from,
+    element by element; rows outside [0, max_len) are left alone."""
+    B, n_new, H, Hk, D, Tmax = 2, 3, 4, 2, 8, 5
+    qkv = np.arange(B * n_new * (H + 2 * Hk) * D, dtype=np.float64).reshape(B * n_new, -1)
+    k = np.full((B, Tmax, Hk, D), -1.0)
+    v = np.full((B, Tmax, Hk, D), -2.0)
+    pos = np.array([1, 4])                   # sequence 1: only its first new token fits
+    oracle.decode.kv_cache_append(qkv, pos, k, v, H, Hk, D)
+    for b in range(B):
+        for p in range(Tmax):
+            i = p - pos[b]
+            for j in range(Hk):
+                for d in range(D):
+                    if 0 <= i < n_new:
+                        assert k[b, p, j, d] == qkv[b * n_new + i, H * D + j * D + d]
+                        assert v[b, p, j, d] == qkv[b * n_new + i, (H + Hk) * D + j * D + d]
+                    else:
+                        assert k[b, p, j, d] == -1.0 and v[b, p, j, d] == -2.0
