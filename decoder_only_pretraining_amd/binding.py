@@ -26,7 +26,7 @@ EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_par
            "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region", "gpt_fwd_bwd",
            "gpt_fwd", "gpt_fp8_quantize", "gpt_status_string", "gpt_last_error",
            "gpt_profile_begin", "gpt_profile_end", "gpt_decode_attn_workspace",
-           "gpt_decode_attn"]
+           "gpt_decode_attn", "gpt_kv_cache_append"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -79,6 +79,7 @@ def lib():
         L.gpt_decode_attn_workspace.argtypes = [c.c_int32] * 6 + [P(c.c_size_t)]
         L.gpt_decode_attn.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6 + [c.c_size_t,
                                                                              c.c_void_p]
+        L.gpt_kv_cache_append.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 5
         L.gpt_status_string.restype = c.c_char_p
         L.gpt_status_string.argtypes = [c.c_int]
         L.gpt_last_error.restype = c.c_char_p
@@ -89,7 +90,7 @@ def lib():
         for name in ("gpt_config_validate", "gpt_param_count", "gpt_param_info",
                      "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region",
                      "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize", "gpt_decode_attn_workspace",
-                     "gpt_decode_attn"):
+                     "gpt_decode_attn", "gpt_kv_cache_append"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -221,6 +222,16 @@ def decode_attn(q, k_cache, v_cache, seqlen, out, workspace, window=-1, stream=N
                                workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check("gpt_decode_attn", st)
+
+
+def kv_cache_append(qkv, pos, k_cache, v_cache, n_head, stream=None):
+    """gpt_kv_cache_append on device tensors: qkv bf16 [B * n_new, (H + 2 Hk) D],
+    pos int32 [B], caches bf16 [B, Tmax, Hk, D]."""
+    B, Tmax, Hk, D = k_cache.shape
+    n_new = qkv.shape[0] // B
+    st = lib().gpt_kv_cache_append(B, n_new, n_head, Hk, D, Tmax, qkv.data_ptr(), pos.data_ptr(),
+                                   k_cache.data_ptr(), v_cache.data_ptr(), _stream_ptr(stream))
+    _check("gpt_kv_cache_append", st)
 
 
 def profile_begin(site_prefix: str):

@@ -184,6 +184,32 @@ __global__ __launch_bounds__(D) void decode_attn_combine_kernel(const float* __r
   out[bh * D + threadIdx.x] = static_cast<bf16>(A / L);
 }
 
+// KV-cache append: token i of sequence b (qkv row b * n_new + i) goes to
+// position pos[b] + i; one thread per 16-byte vector of its k and v heads.
+// Positions outside [0, Tmax) are skipped.
+__global__ __launch_bounds__(256) void kv_cache_append_kernel(
+    const bf16* __restrict__ qkv, const int32_t* __restrict__ pos, bf16* __restrict__ kc,
+    bf16* __restrict__ vc, int B, int n_new, int H, int Hk, int D, int Tmax) {
+  const int per_head = D / 8;
+  const int64_t per_tok = (int64_t)2 * Hk * per_head;  // k vectors, then v vectors
+  const int64_t total = (int64_t)B * n_new * per_tok;
+  const int64_t row_w = (int64_t)(H + 2 * Hk) * D;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < total;
+       x += (int64_t)gridDim.x * 256) {
+    const int64_t tokrow = x / per_tok;  // b * n_new + i
+    const int r = (int)(x % per_tok);
+    const int b = (int)(tokrow / n_new), i = (int)(tokrow % n_new);
+    const int p = pos[b] + i;
+    if (p < 0 || p >= Tmax) continue;
+    const bool is_v = r >= Hk * per_head;
+    const int rr = is_v ? r - Hk * per_head : r;  // head * per_head + vector
+    const bf16x8 val = *reinterpret_cast<const bf16x8*>(
+        qkv + tokrow * row_w + (int64_t)(H + (is_v ? Hk : 0)) * D + (int64_t)rr * 8);
+    bf16* dst = is_v ? vc : kc;
+    *reinterpret_cast<bf16x8*>(dst + ((int64_t)b * Tmax + p) * Hk * D + (int64_t)rr * 8) = val;
+  }
+}
+
 }  // namespace gk
 
 namespace gpt {
@@ -238,6 +264,15 @@ void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const
   }
 #undef DEC_G
 #undef DEC_P
+}
+
+void launch_kv_cache_append(int B, int n_new, int H, int Hk, int D, int Tmax, const void* qkv,
+                            const int32_t* pos, void* k, void* v, hipStream_t s) {
+  const int64_t total = (int64_t)B * n_new * 2 * Hk * (D / 8);
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(gk::kv_cache_append_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const bf16*>(qkv), pos, static_cast<bf16*>(k),
+                     static_cast<bf16*>(v), B, n_new, H, Hk, D, Tmax);
 }
 
 }  // namespace gpt

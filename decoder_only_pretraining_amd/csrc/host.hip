@@ -953,6 +953,26 @@ int gpt_decode_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t he
   return GPT_OK;
 }
 
+int gpt_kv_cache_append(int32_t batch, int32_t n_new, int32_t n_head, int32_t n_kv_head,
+                        int32_t head_dim, int32_t max_len, const void* qkv, const int32_t* pos,
+                        void* k_cache, void* v_cache, void* stream) {
+  g_err[0] = 0;
+  const int st = decode_validate(batch, n_head, n_kv_head, head_dim, max_len, -1);
+  if (st) return st;
+  if (n_new < 1 || (int64_t)batch * n_new > ((int64_t)1 << 26))
+    return fail(GPT_E_INVAL, "n_new %d: need >= 1 and batch * n_new <= 2^26", n_new);
+  if (!qkv || !pos || !k_cache || !v_cache) return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+  if (!aligned(qkv, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pos, 4))
+    return fail(GPT_E_ALIGN, "qkv and caches need 16-byte alignment, pos 4");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  launch_kv_cache_append(batch, n_new, n_head, n_kv_head, head_dim, max_len, qkv, pos, k_cache,
+                         v_cache, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
+  return GPT_OK;
+}
+
 const char* gpt_status_string(int status) {
   switch (status) {
     case GPT_OK: return "ok";

@@ -176,6 +176,10 @@ void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* s
 // int32 [B], clamped to [1, Tmax]).
 int decode_splits(int Tmax, int window);
 size_t decode_workspace_bytes(int B, int H, int Hk, int D, int Tmax, int window);
+// KV-cache append from fused QKV rows (bf16 [B * n_new][(H + 2Hk) D]) to
+// positions pos[b] + i of the caches (bf16 [B][Tmax][Hk][D]).
+void launch_kv_cache_append(int B, int n_new, int H, int Hk, int D, int Tmax, const void* qkv,
+                            const int32_t* pos, void* k, void* v, hipStream_t s);
 void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const void* q,
                         const void* k, const void* v, const int32_t* seqlen, void* out,
                         void* workspace, hipStream_t s);

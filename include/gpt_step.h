@@ -241,6 +241,26 @@ int gpt_decode_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t he
                     size_t workspace_bytes, void* stream);
 
 /*
+ * KV-cache append: writes the k and v rows of n_new tokens per sequence into
+ * the caches gpt_decode_attn reads (prefill: the prompt's rows after a
+ * forward; decode: the new token's). qkv holds one row per token, row
+ * b * n_new + i for token i of sequence b, laid out as the model's fused
+ * QKV product output: H query heads, then Hk key heads, then Hk value
+ * heads, head_dim each (gpt_fwd leaves it, after RoPE, QK-norm and the
+ * value embedding, in the per-layer workspace region "qkv").
+ *   qkv      (device) bf16 [batch * n_new, (n_head + 2 n_kv_head) * head_dim]
+ *   pos      (device) int32 [batch]: cache position of each sequence's first
+ *            new token; token i goes to pos[b] + i, and rows falling outside
+ *            [0, max_len) are not written
+ *   k_cache, v_cache (device) bf16 [batch, max_len, n_kv_head, head_dim]
+ * Same size rules as gpt_decode_attn (window not used); n_new >= 1. qkv and
+ * caches 16-byte aligned, pos 4. Enqueued on `stream`.
+ */
+int gpt_kv_cache_append(int32_t batch, int32_t n_new, int32_t n_head, int32_t n_kv_head,
+                        int32_t head_dim, int32_t max_len, const void* qkv, const int32_t* pos,
+                        void* k_cache, void* v_cache, void* stream);
+
+/*
  * Host only; measurement support. After gpt_profile_begin(prefixes), every
  * kernel launch of gpt_fwd_bwd / gpt_fwd whose launch-site name starts with
  * one of the comma-separated `prefixes` is bracketed by two HIP events

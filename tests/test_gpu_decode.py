@@ -1,4 +1,5 @@
-"""Parity of the KV-cache decode attention (gpt_decode_attn) with the CPU
+"""Parity of the KV-cache decode attention (gpt_decode_attn) and the cache
+append (gpt_kv_cache_append) with the CPU
 oracle (oracle/decode.py) on seeded bf16 inputs.
 
 Both sides read the same bf16 values; the oracle computes in float64. The
@@ -91,3 +92,61 @@ def test_decode_attention_clamps_seqlen_and_repeats_exactly():
     B.decode_attn(qd, kd, vd, sd, out, ws, -1)
     torch.cuda.synchronize()
     assert torch.equal(first, out)
+
+
+def test_kv_cache_append_matches_oracle():
+    """Bit-exact against the oracle's append, with positions that run past
+    the cache end and one that starts before it."""
+    import torch
+    B_, n_new, H, Hk, D, Tmax = 3, 5, 6, 2, 128, 40
+    rng = np.random.default_rng(11)
+    qkv = _bf16(rng.standard_normal((B_ * n_new, (H + 2 * Hk) * D)))
+    pos = np.array([0, 37, -2], dtype=np.int32)
+    k0 = _bf16(rng.standard_normal((B_, Tmax, Hk, D)))
+    v0 = _bf16(rng.standard_normal((B_, Tmax, Hk, D)))
+    kd, vd = k0.cuda(), v0.cuda()
+    B.kv_cache_append(qkv.cuda(), torch.from_numpy(pos).cuda(), kd, vd, H)
+    torch.cuda.synchronize()
+    kr, vr = k0.float().numpy(), v0.float().numpy()
+    oracle.decode.kv_cache_append(qkv.float().numpy(), pos, kr, vr, H, Hk, D)
+    np.testing.assert_array_equal(kd.float().cpu().numpy(), kr)
+    np.testing.assert_array_equal(vd.float().cpu().numpy(), vr)
+
+
+def test_prefill_then_decode_matches_the_forward_attention():
+    """Prefill through the training forward: the per-layer qkv rows of a
+    bf16 forward, appended to a cache, then decode attention for each
+    sequence's last token, equal the forward's attention output at that
+    token (both bf16; two roundings and different summation orders:
+    |a - b| <= 2^-7 |b| + 2e-3), on a short-window and a full layer."""
+    import torch
+    import workloads as W
+    from tests.gpu_common import inputs
+    w = W.get("d12").with_(name="prefill", n_layer=4, seq_len=300, batch=3, short_window=75,
+                           vocab=2048, n_kv_head=2)
+    p, tok, tgt = inputs(w, 61, 62)
+    step = B.Step(w, p, tok, tgt)
+    step.forward()
+    torch.cuda.synchronize()
+    H, Hk, D, T, N = w.n_head, w.n_kv_head, w.head_dim, w.seq_len, w.batch * w.seq_len
+    Tmax = T + 20
+    for layer in (0, 3):                      # layer 0 short-window, layer 3 full
+        window = -1 if oracle.layer_is_full(layer, w.n_layer) else w.short_window
+        qkv = step.region("qkv", layer).view(torch.bfloat16).view(N, (H + 2 * Hk) * D)
+        attn = step.region("attn", layer).view(torch.bfloat16).view(N, H * D)
+        kc = torch.zeros(w.batch, Tmax, Hk, D, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        pos = torch.zeros(w.batch, dtype=torch.int32, device="cuda")
+        B.kv_cache_append(qkv, pos, kc, vc, H)
+        last = torch.arange(w.batch, device="cuda") * T + T - 1
+        q = qkv[last, :H * D].reshape(w.batch, H, D).contiguous()
+        out = torch.empty_like(q)
+        ws = torch.empty(max(B.decode_attn_workspace(w.batch, H, Hk, D, Tmax, window), 1),
+                         dtype=torch.uint8, device="cuda")
+        seqlen = torch.full((w.batch,), T, dtype=torch.int32, device="cuda")
+        B.decode_attn(q, kc, vc, seqlen, out, ws, window)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().reshape(w.batch, H * D)
+        ref = attn[last].float().cpu().numpy()
+        assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2e-3), (
+            layer, float(np.abs(got - ref).max()))
