@@ -101,6 +101,16 @@ def param_total(w) -> int:
     return n
 
 
+def _cpu_cores() -> int:
+    """Threads of the host's BLAS pool (what the oracle's NumPy products use)."""
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        return int(max((i.get("num_threads", 0) for i in info), default=os.cpu_count()))
+    except Exception:  # pragma: no cover
+        return int(os.cpu_count())
+
+
 def cpu_baseline(w, params, tokens, targets, rows: int):
     """The oracle (unchanged) on the first `rows` batch rows of the same
     inputs: tokens/s of its fwd+bwd, on the host's cores."""
@@ -109,13 +119,7 @@ def cpu_baseline(w, params, tokens, targets, rows: int):
     t0 = time.perf_counter()
     oracle.forward_backward(sub, params, tokens[:rows], targets[:rows], dtype=np.float32)
     dt = time.perf_counter() - t0
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max((i.get("num_threads", 0) for i in info), default=os.cpu_count())
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    return {"value": rows * w.seq_len / dt, "unit": "tokens/s", "cores": int(cores),
+    return {"value": rows * w.seq_len / dt, "unit": "tokens/s", "cores": _cpu_cores(),
             "kind": "oracle",
             "sample": f"{rows} of {w.batch} batch rows ({rows * w.seq_len} tokens) of the "
                       f"{w.name} workload, one fp32 forward+backward, {dt:.1f} s"}
@@ -173,6 +177,19 @@ def decode_bench(args):
     kv = sum(Bs * Hk * (T if wn < 0 else min(T, wn + 1)) * D * 2 * 2 for wn in wins)
     nbytes = kv + L * 2 * Bs * H * D * 2
     gbs = nbytes / (ms / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:  # the oracle on the same inputs, all 12 layers
+        import oracle  # test infrastructure: only the CPU-baseline legs use it
+        host = [(x.float().cpu().numpy(), y.float().cpu().numpy(), z.float().cpu().numpy())
+                for x, y, z in zip(q, kc, vc)]
+        sl = seqlen.cpu().numpy()
+        t0 = time.perf_counter()
+        for (qh, kh, vh), wn in zip(host, wins):
+            oracle.decode.decode_attention(qh, kh, vh, sl, None if wn < 0 else wn)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": _cpu_cores(),
+               "kind": "oracle", "sample": f"the whole step (12 layers, {Bs} sequences), float64 "
+                                           f"NumPy, {dt:.2f} s"}
     print(json.dumps({
         "metric": "KV-cache decode attention read rate, d12 (12 layers), 16 sequences x 2048 "
                   "cached positions", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
@@ -183,12 +200,13 @@ def decode_bench(args):
                                "heads 6/6, head_dim 128, 9 window-512 layers + 3 full",
                    "tokens_per_step": Bs},
         "decode_tokens_per_s_attention_only": round(Bs / (ms / 1e3), 1),
-        "roofline": {"kernel": "decode_attn_partial_kernel<128, 1> (chunk states, the last "
-                               "chunk of each sequence and KV head combines)",
+        "roofline": {"kernel": "decode_attn_kernel<128, 1, 4> (chunks of 128 cached positions) "
+                               "+ decode_attn_combine_kernel<128>",
                      "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_BYTES / 1e9,
                      "unit": "GB/s", "frac": round(gbs / (PEAK_HBM_BYTES / 1e9), 4),
-                     "traffic": None, "launches": L * args.steps,
-                     "algorithmic_bytes_per_step": nbytes}}), flush=True)
+                     "traffic": None, "launches": 2 * L * args.steps,
+                     "algorithmic_bytes_per_step": nbytes},
+        "cpu_baseline": cpu}), flush=True)
 
 
 def main():
