@@ -37,3 +37,4 @@ from .model import (  # noqa: F401
 )
 from . import fp8  # noqa: F401
 from . import decode  # noqa: F401
+from . import optim  # noqa: F401

@@ -831,3 +831,79 @@ def test_kv_cache_append_by_hand():
                         assert v[b, p, j, d] == qkv[b * n_new + i, (H + Hk) * D + j * D + d]
                     else:
                         assert k[b, p, j, d] == -1.0 and v[b, p, j, d] == -2.0
+
+
+# ---------------------------------------------------------------- MuonAdamW
+
+def test_adamw_matches_torch():
+    rng = np.random.default_rng(5)
+    p0 = rng.standard_normal(50)
+    p = p0.copy(); m = np.zeros(50); v = np.zeros(50)
+    pt = torch.tensor(p0, requires_grad=True)
+    opt = torch.optim.AdamW([pt], lr=0.3, betas=(0.8, 0.95), eps=1e-10, weight_decay=0.1)
+    for t in range(1, 5):
+        g = rng.standard_normal(50)
+        oracle.optim.adamw_update(p, g, m, v, 0.3, t, 0.8, 0.95, 1e-10, wd=0.1)
+        pt.grad = torch.from_numpy(g.copy())
+        opt.step()
+        np.testing.assert_allclose(p, pt.detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+def _polar(Mx):
+    U, _, Vt = np.linalg.svd(Mx, full_matrices=False)
+    return U @ Vt
+
+
+@pytest.mark.parametrize("shape", [(8, 8), (6, 20), (20, 6)])
+def test_newton_schulz_cubic_converges_to_polar_factor(shape):
+    """With the cubic coefficients (1.5, -0.5, 0) the iteration converges to
+    the orthogonal polar factor U V^T of the SVD G = U S V^T."""
+    rng = np.random.default_rng(6)
+    U, _ = np.linalg.qr(rng.standard_normal((shape[0], min(shape))))
+    V, _ = np.linalg.qr(rng.standard_normal((shape[1], min(shape))))
+    G = U @ np.diag(np.linspace(1.0, 3.0, min(shape))) @ V.T      # condition number 3
+    X = oracle.optim.newton_schulz(G, 1.5, -0.5, 0.0, 60)
+    np.testing.assert_allclose(X, _polar(G), atol=1e-10)
+
+
+def test_newton_schulz_quintic_keeps_singular_vectors():
+    """The default quintic iteration maps every singular value of a
+    well-spread spectrum into a band around 1 and keeps the singular
+    vectors: U^T X V is diagonal with entries in (0.6, 1.3)."""
+    rng = np.random.default_rng(7)
+    U, _ = np.linalg.qr(rng.standard_normal((16, 16)))
+    V, _ = np.linalg.qr(rng.standard_normal((48, 16)))
+    G = U @ np.diag(np.geomspace(0.05, 5.0, 16)) @ V.T
+    d = oracle.optim.DEFAULTS
+    X = oracle.optim.newton_schulz(G, d["ns_a"], d["ns_b"], d["ns_c"], d["ns_steps"])
+    D = U.T @ X @ V
+    assert np.abs(D - np.diag(np.diag(D))).max() < 1e-10
+    assert np.all(np.diag(D) > 0.6) and np.all(np.diag(D) < 1.3)
+
+
+def test_muon_two_steps_closed_form():
+    """Orthogonal gradients Q1 then Q2, Nesterov momentum mu, many cubic NS
+    steps: the second update direction is the polar factor of
+    (1 + mu) Q2 + mu^2 Q1, the first is Q1; tall matrices get
+    sqrt(rows / cols)."""
+    rng = np.random.default_rng(8)
+    Q1, _ = np.linalg.qr(rng.standard_normal((12, 4)))
+    Q2, _ = np.linalg.qr(rng.standard_normal((12, 4)))
+    p0 = rng.standard_normal((12, 4))
+    p, buf = p0.copy(), np.zeros((12, 4))
+    mu, lr, wd = 0.9, 0.1, 0.2
+    oracle.optim.muon_update(p, Q1, buf, lr, mu, True, wd, 1.5, -0.5, 0.0, 80)
+    oracle.optim.muon_update(p, Q2, buf, lr, mu, True, wd, 1.5, -0.5, 0.0, 80)
+    s = np.sqrt(12 / 4)
+    want = (p0 * (1 - lr * wd) - lr * s * Q1) * (1 - lr * wd) - lr * s * _polar((1 + mu) * Q2 + mu * mu * Q1)
+    np.testing.assert_allclose(p, want, atol=1e-9)
+
+
+def test_optimizer_groups():
+    cfg = W.get("tiny").with_(smear=True, backout=True)
+    g = {n: oracle.optim.group(n) for n in oracle.param_offsets(cfg)[0]}
+    assert g["l0.q"] == g["l1.mp"] == ("muon", "lr_matrix")
+    assert g["wte"] == g["l1.ve"] == ("adamw", "lr_embed")
+    assert g["lm_head"] == ("adamw", "lr_unembed")
+    assert g["resid_lambdas"] == g["l1.veg"] == g["smear_gate"] == g["backout_lambda"] == \
+        ("adamw", "lr_scalar")
