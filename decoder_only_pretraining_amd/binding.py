@@ -26,7 +26,8 @@ EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_par
            "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region", "gpt_fwd_bwd",
            "gpt_fwd", "gpt_fp8_quantize", "gpt_status_string", "gpt_last_error",
            "gpt_profile_begin", "gpt_profile_end", "gpt_decode_attn_workspace",
-           "gpt_decode_attn", "gpt_kv_cache_append"]
+           "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
+           "gpt_optimizer_step"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -40,6 +41,14 @@ class GptConfig(ctypes.Structure):
                 ("fp8_linears", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float),
                 ("softcap", ctypes.c_float)]
+
+
+class OptimHparams(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+                ("nesterov", ctypes.c_int32)] + [
+        (n, ctypes.c_float) for n in ("lr_matrix", "lr_scalar", "lr_embed", "lr_unembed",
+                                      "lr_mult", "weight_decay", "beta1", "beta2", "eps",
+                                      "momentum", "ns_a", "ns_b", "ns_c")]
 
 
 class GptError(RuntimeError):
@@ -80,6 +89,9 @@ def lib():
         L.gpt_decode_attn.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6 + [c.c_size_t,
                                                                              c.c_void_p]
         L.gpt_kv_cache_append.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 5
+        L.gpt_optim_workspace_size.argtypes = [P(GptConfig), P(c.c_size_t)]
+        L.gpt_optimizer_step.argtypes = [P(GptConfig), P(OptimHparams)] + [c.c_void_p] * 4 + [
+            c.c_size_t, c.c_void_p]
         L.gpt_status_string.restype = c.c_char_p
         L.gpt_status_string.argtypes = [c.c_int]
         L.gpt_last_error.restype = c.c_char_p
@@ -90,7 +102,8 @@ def lib():
         for name in ("gpt_config_validate", "gpt_param_count", "gpt_param_info",
                      "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region",
                      "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize", "gpt_decode_attn_workspace",
-                     "gpt_decode_attn", "gpt_kv_cache_append"):
+                     "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
+                     "gpt_optimizer_step"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -232,6 +245,23 @@ def kv_cache_append(qkv, pos, k_cache, v_cache, n_head, stream=None):
     st = lib().gpt_kv_cache_append(B, n_new, n_head, Hk, D, Tmax, qkv.data_ptr(), pos.data_ptr(),
                                    k_cache.data_ptr(), v_cache.data_ptr(), _stream_ptr(stream))
     _check("gpt_kv_cache_append", st)
+
+
+def optim_workspace_size(cfg) -> int:
+    n = ctypes.c_size_t()
+    _check("gpt_optim_workspace_size", lib().gpt_optim_workspace_size(ctypes.byref(cfg),
+                                                                      ctypes.byref(n)))
+    return n.value
+
+
+def optimizer_step(cfg, hp: OptimHparams, params, grads, state, workspace, stream=None):
+    """gpt_optimizer_step on device tensors (fp32 params, grads, state [2 n];
+    workspace uint8)."""
+    st = lib().gpt_optimizer_step(ctypes.byref(cfg), ctypes.byref(hp), params.data_ptr(),
+                                  grads.data_ptr(), state.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream_ptr(stream))
+    _check("gpt_optimizer_step", st)
 
 
 def profile_begin(site_prefix: str):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgptstep.so")
-SOURCES = ["host.hip", "rowops.hip", "gemm.hip", "attention.hip", "fp8.hip", "decode.hip"]
+SOURCES = ["host.hip", "rowops.hip", "gemm.hip", "attention.hip", "fp8.hip", "decode.hip", "optim.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -973,6 +973,70 @@ int gpt_kv_cache_append(int32_t batch, int32_t n_new, int32_t n_head, int32_t n_
   return GPT_OK;
 }
 
+int gpt_optim_workspace_size(const gpt_config* cfg, size_t* bytes) {
+  g_err[0] = 0;
+  const int st = validate(cfg);
+  if (st) return st;
+  if (!bytes) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  *bytes = make_optim_plan(make_dims(*cfg)).total;
+  return GPT_OK;
+}
+
+int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float* params,
+                       const float* grads, float* state, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_err[0] = 0;
+  const int st = validate(cfg);
+  if (st) return st;
+  if (!hp || !params || !grads || !state || !workspace)
+    return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+  if (!aligned(params, 256) || !aligned(grads, 256) || !aligned(state, 256) ||
+      !aligned(workspace, 256))
+    return fail(GPT_E_ALIGN, "params, grads, state and workspace need 256-byte alignment");
+  if (hp->step < 1 || hp->ns_steps < 0 || hp->ns_steps > 100 || (hp->nesterov != 0 && hp->nesterov != 1))
+    return fail(GPT_E_INVAL, "step >= 1, ns_steps in [0, 100] and nesterov 0/1 required");
+  const float fl[] = {hp->lr_matrix, hp->lr_scalar, hp->lr_embed, hp->lr_unembed, hp->lr_mult,
+                      hp->weight_decay, hp->beta1, hp->beta2, hp->eps, hp->momentum,
+                      hp->ns_a, hp->ns_b, hp->ns_c};
+  for (float f : fl)
+    if (!std::isfinite(f)) return fail(GPT_E_INVAL, "hyper-parameters must be finite");
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+    return fail(GPT_E_INVAL, "betas must lie in [0, 1)");
+  const Dims d = make_dims(*cfg);
+  const OptimPlan o = make_optim_plan(d);
+  if (workspace_bytes < o.total)
+    return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, o.total);
+  int64_t n_elems = 0;
+  const std::vector<TensorInfo> lay = param_layout(*cfg);
+  for (const auto& t : lay) n_elems = std::max(n_elems, t.offset + t.rows * t.cols);
+  float* m = state;
+  float* v = state + n_elems;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  for (const auto& t : lay) {
+    const std::string& n = t.name;
+    const size_t dot = n.find('.');
+    const std::string leaf = dot == std::string::npos ? n : n.substr(dot + 1);
+    float* p = params + t.offset;
+    const float* g = grads + t.offset;
+    const int64_t cnt = t.rows * t.cols;
+    if (leaf == "q" || leaf == "k" || leaf == "v" || leaf == "o" || leaf == "fc" || leaf == "mp") {
+      launch_muon(d, o, workspace, p, g, m + t.offset, (int)t.rows, (int)t.cols,
+                  hp->lr_matrix * hp->lr_mult, hp->weight_decay, hp->momentum, hp->nesterov,
+                  hp->ns_a, hp->ns_b, hp->ns_c, hp->ns_steps, s);
+    } else {
+      const float lr = n == "wte" || leaf == "ve" ? hp->lr_embed
+                       : n == "lm_head"            ? hp->lr_unembed
+                                                   : hp->lr_scalar;
+      launch_adamw(p, g, m + t.offset, v + t.offset, cnt, lr * hp->lr_mult, hp->beta1, hp->beta2,
+                   hp->eps, hp->step, s);
+    }
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
+  return GPT_OK;
+}
+
 const char* gpt_status_string(int status) {
   switch (status) {
     case GPT_OK: return "ok";

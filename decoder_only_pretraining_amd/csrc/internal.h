@@ -184,6 +184,19 @@ void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const
                         const void* k, const void* v, const int32_t* seqlen, void* out,
                         void* workspace, hipStream_t s);
 
+// MuonAdamW (optim.hip). Workspace for the Newton-Schulz iteration of the
+// largest block matrix: workgroup partials + the norm scalar, X and Y
+// [r][k], A and A A [r][r] (compute dtype; r <= k the matrix's sides).
+struct OptimPlan {
+  size_t part, x, y, a, aa, total;
+};
+OptimPlan make_optim_plan(const Dims& d);
+void launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float b1,
+                  float b2, float eps, int step, hipStream_t s);
+void launch_muon(const Dims& d, const OptimPlan& o, void* workspace, float* p, const float* g,
+                 float* buf, int rows, int cols, float lr, float wd, float mu, int nesterov,
+                 float a, float b, float c, int steps, hipStream_t s);
+
 // ------------------------------------------------------------ GEMMs
 // Shapes: C[M][N] = sum_k A(m,k) B(n,k).
 // "nt": A [M][K], B [N][K] (both contraction-contiguous).

@@ -261,6 +261,55 @@ int gpt_kv_cache_append(int32_t batch, int32_t n_new, int32_t n_head, int32_t n_
                         void* k_cache, void* v_cache, void* stream);
 
 /*
+ * MuonAdamW optimizer step ("NanoChat基础训练报告", optimizer block: Muon for
+ * the matrices, AdamW for the rest; matrix rate 0.02, scalar 0.5, embedding
+ * 0.3, unembedding 0.008, weight decay 0.28, a warmup / decay schedule;
+ * "Nanochat在nanoGPT之上的新增功能", notes on Muon: momentum, then
+ * Newton-Schulz orthogonalisation). The pages give neither the Newton-Schulz
+ * coefficients nor the step count nor the Adam betas: they are fields here.
+ * Groups (fixed by the library):
+ *   Muon, rate lr_matrix: l.q, l.k, l.v, l.o, l.fc, l.mp of every layer;
+ *     buf <- momentum buf + g; u = g + momentum buf (nesterov) or buf;
+ *     X = u / (||u||_F + 1e-7), rows <= cols orientation (tall matrices
+ *     transposed); ns_steps times X <- a X + (b A + c A^2) X, A = X X^T, in
+ *     the compute dtype; p <- p (1 - lr weight_decay) - lr
+ *     sqrt(max(1, rows / cols)) X.
+ *   AdamW (no weight decay; bias-corrected with `step`): wte and l.ve at
+ *     lr_embed, lm_head at lr_unembed, every other tensor (lambdas, l.veg,
+ *     smear_gate, backout_lambda) at lr_scalar.
+ * Every rate is multiplied by lr_mult (the caller's schedule).
+ */
+typedef struct gpt_optim_hparams {
+  int32_t step;            /* 1, 2, ...: AdamW bias correction            */
+  int32_t ns_steps;        /* Newton-Schulz iterations, [0, 100]           */
+  int32_t nesterov;        /* 0 | 1                                        */
+  float lr_matrix, lr_scalar, lr_embed, lr_unembed, lr_mult;
+  float weight_decay;      /* Muon matrices                                */
+  float beta1, beta2, eps; /* AdamW, betas in [0, 1)                       */
+  float momentum;          /* Muon                                         */
+  float ns_a, ns_b, ns_c;  /* Newton-Schulz coefficients                   */
+} gpt_optim_hparams;
+
+/* Host only. Bytes of device workspace gpt_optimizer_step needs. */
+int gpt_optim_workspace_size(const gpt_config* cfg, size_t* bytes);
+
+/*
+ * One optimizer step, in place.
+ *   params (device) fp32 [n_elems], canonical layout; updated.
+ *   grads  (device) fp32 [n_elems]; read only.
+ *   state  (device) fp32 [2 * n_elems]: first n_elems the AdamW first moment
+ *          or the Muon momentum buffer, then the AdamW second moment; zero
+ *          before step 1; updated.
+ *   workspace (device) >= gpt_optim_workspace_size bytes; scratch.
+ * params, grads, state and workspace 256-byte aligned. Validation errors
+ * return before anything is enqueued; the work is enqueued on `stream`.
+ * Concurrent calls need distinct workspaces.
+ */
+int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float* params,
+                       const float* grads, float* state, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * Host only; measurement support. After gpt_profile_begin(prefixes), every
  * kernel launch of gpt_fwd_bwd / gpt_fwd whose launch-site name starts with
  * one of the comma-separated `prefixes` is bracketed by two HIP events

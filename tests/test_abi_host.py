@@ -198,3 +198,27 @@ def test_decode_attn_validation_and_workspace():
     assert L.gpt_decode_attn(2, 6, 6, 128, 64, -1, ctypes.c_void_p(264), p, p, p, p, p, ws,
                              None) == -3
     assert L.gpt_decode_attn(2, 6, 6, 128, 1024, -1, p, p, p, p, p, p, ws - 1, None) == -4
+
+
+def test_optimizer_validation():
+    w = W.get("tiny")
+    cfg = B.make_config(w)
+    L = B.lib()
+    ws = B.optim_workspace_size(cfg)
+    assert ws > 0
+    p = ctypes.c_void_p(256)
+    good = dict(step=1, ns_steps=5, nesterov=1, lr_matrix=0.02, lr_scalar=0.5, lr_embed=0.3,
+                lr_unembed=0.008, lr_mult=1.0, weight_decay=0.28, beta1=0.9, beta2=0.999,
+                eps=1e-8, momentum=0.95, ns_a=3.4445, ns_b=-4.775, ns_c=2.0315)
+    for kw in [dict(step=0), dict(ns_steps=-1), dict(nesterov=2), dict(beta1=1.0),
+               dict(beta2=-0.1), dict(lr_matrix=float("nan"))]:
+        hp = B.OptimHparams(**dict(good, **kw))
+        assert L.gpt_optimizer_step(ctypes.byref(cfg), ctypes.byref(hp), p, p, p, p, ws,
+                                    None) == -1, kw
+    hp = B.OptimHparams(**good)
+    assert L.gpt_optimizer_step(ctypes.byref(cfg), ctypes.byref(hp), p, p, p, p, ws - 1,
+                                None) == -4
+    assert L.gpt_optimizer_step(ctypes.byref(cfg), ctypes.byref(hp), None, p, p, p, ws,
+                                None) == -2
+    assert L.gpt_optimizer_step(ctypes.byref(cfg), ctypes.byref(hp), ctypes.c_void_p(260), p, p,
+                                p, ws, None) == -3
