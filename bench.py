@@ -4,6 +4,7 @@
                     [--fp8 auto|on|off] [--no-cpu-baseline] [--roofline-kernel K]
                     [--smear] [--backout]
     python bench.py --decode [--steps K] [--warmup W]
+    python bench.py --optimizer [--steps K] [--warmup W]
 
 One step = one gpt_fwd_bwd call (loss + every parameter gradient) over one
 batch of seeded synthetic tokens, inputs already resident in HBM. Prints one
@@ -209,6 +210,69 @@ def decode_bench(args):
         "cpu_baseline": cpu}), flush=True)
 
 
+def optimizer_bench(args):
+    """The full d12 training step of the pages: 4 accumulated fwd+bwd calls
+    of 16,384 tokens (65,536 tokens) and one MuonAdamW step (default
+    hyper-parameters of the library's oracle description: the pages' rates,
+    5 Newton-Schulz steps); also the optimizer step alone."""
+    import torch
+    from decoder_only_pretraining_amd import binding as B
+    w = W.get("d12")
+    total = param_total(w)
+    params = W.gen_params(total, w.n_layer, W.weight_seed(w))
+    tokens, targets = W.split_tokens(W.gen_tokens(w))
+    step = B.Step(w, params, tokens, targets, flags=B.GPT_F_ACCUMULATE, device="cuda:0")
+    state = torch.zeros(2 * total, dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(B.optim_workspace_size(step.cfg), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def hp(t):
+        return B.OptimHparams(step=t, ns_steps=5, nesterov=1, lr_matrix=0.02, lr_scalar=0.5,
+                              lr_embed=0.3, lr_unembed=0.008, lr_mult=1.0, weight_decay=0.28,
+                              beta1=0.9, beta2=0.999, eps=1e-8, momentum=0.95, ns_a=3.4445,
+                              ns_b=-4.7750, ns_c=2.0315)
+
+    t = 0
+
+    def full_step():
+        nonlocal t
+        t += 1
+        step.grads.zero_()
+        for _ in range(4):
+            step.run(stream)
+        B.optimizer_step(step.cfg, hp(t), step.params, step.grads, state, ws, stream)
+
+    for _ in range(args.warmup):
+        full_step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        full_step()
+    ev[1].record(stream)
+    ev[2].record(stream)
+    for _ in range(args.steps):
+        t += 1
+        B.optimizer_step(step.cfg, hp(t), step.params, step.grads, state, ws, stream)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    full_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    opt_ms = ev[2].elapsed_time(ev[3]) / args.steps
+    loss = float(step.loss.item())
+    assert np.isfinite(loss), loss
+    ntok = 4 * w.batch * w.seq_len
+    print(json.dumps({
+        "metric": "full training step tokens/sec (4 x 16,384-token fwd+bwd + MuonAdamW), d12 "
+                  "seq2048, 1 GPU", "value": round(ntok / (full_ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(full_ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) weights)",
+        "config": {"workload": "d12, 65,536 tokens per optimizer step (4 accumulated calls)",
+                   "tokens_per_step": ntok},
+        "optimizer_ms": round(opt_ms, 3),
+        "context": {"pages_rtx4070_full_step_ms": 1177}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +283,8 @@ def main():
                     help="block linears in fp8 (auto: as the workload defines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--smear", action="store_true", help="the Smear model variant")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="time the full step with MuonAdamW (4 accumulated calls + optimizer)")
     ap.add_argument("--decode", action="store_true",
                     help="time the KV-cache decode attention instead of the training step")
     ap.add_argument("--backout", action="store_true",
@@ -246,6 +312,9 @@ def main():
 
     if args.decode:
         decode_bench(args)
+        return
+    if args.optimizer:
+        optimizer_bench(args)
         return
 
     import torch
