@@ -251,13 +251,14 @@ def optimizer_bench(args):
         full_step()
     ev[1].record(stream)
     ev[2].record(stream)
-    for _ in range(args.steps):
+    for _ in range(args.optimizer_alone_steps):
         t += 1
         B.optimizer_step(step.cfg, hp(t), step.params, step.grads, state, ws, stream)
     ev[3].record(stream)
     torch.cuda.synchronize()
     full_ms = ev[0].elapsed_time(ev[1]) / args.steps
-    opt_ms = ev[2].elapsed_time(ev[3]) / args.steps
+    opt_ms = (ev[2].elapsed_time(ev[3]) / args.optimizer_alone_steps
+              if args.optimizer_alone_steps else None)
     loss = float(step.loss.item())
     assert np.isfinite(loss), loss
     ntok = 4 * w.batch * w.seq_len
@@ -269,7 +270,7 @@ def optimizer_bench(args):
         "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) weights)",
         "config": {"workload": "d12, 65,536 tokens per optimizer step (4 accumulated calls)",
                    "tokens_per_step": ntok},
-        "optimizer_ms": round(opt_ms, 3),
+        "optimizer_ms": None if opt_ms is None else round(opt_ms, 3),
         "context": {"pages_rtx4070_full_step_ms": 1177}}), flush=True)
 
 
@@ -285,6 +286,8 @@ def main():
     ap.add_argument("--smear", action="store_true", help="the Smear model variant")
     ap.add_argument("--optimizer", action="store_true",
                     help="time the full step with MuonAdamW (4 accumulated calls + optimizer)")
+    ap.add_argument("--optimizer-alone-steps", type=int, default=10,
+                    help="with --optimizer: optimizer steps timed on their own after the full steps")
     ap.add_argument("--decode", action="store_true",
                     help="time the KV-cache decode attention instead of the training step")
     ap.add_argument("--backout", action="store_true",

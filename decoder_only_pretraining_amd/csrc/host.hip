@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <map>
 #include <mutex>
 
 #include "internal.h"
@@ -1013,6 +1014,31 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
   float* v = state + n_elems;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  // side streams and events of this device, created once (default priority)
+  struct Side {
+    hipStream_t st[kOptStreams];
+    hipEvent_t ev[kOptStreams + 1];
+  };
+  static std::mutex side_mu;
+  static std::map<int, Side> sides;
+  std::lock_guard<std::mutex> lock(side_mu);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GPT_E_HIP, "hipGetDevice failed");
+  auto it = sides.find(dev);
+  if (it == sides.end()) {
+    Side sd{};
+    for (int i = 0; i < kOptStreams; ++i)
+      if (hipStreamCreateWithFlags(&sd.st[i], hipStreamNonBlocking) != hipSuccess)
+        return fail(GPT_E_HIP, "hipStreamCreateWithFlags failed");
+    for (int i = 0; i <= kOptStreams; ++i)
+      if (hipEventCreateWithFlags(&sd.ev[i], hipEventDisableTiming) != hipSuccess)
+        return fail(GPT_E_HIP, "hipEventCreateWithFlags failed");
+    it = sides.emplace(dev, sd).first;
+  }
+  const Side& sd = it->second;
+  (void)hipEventRecord(sd.ev[kOptStreams], s);  // fork
+  for (int i = 0; i < kOptStreams; ++i) (void)hipStreamWaitEvent(sd.st[i], sd.ev[kOptStreams], 0);
+  int next = 0;
   for (const auto& t : lay) {
     const std::string& n = t.name;
     const size_t dot = n.find('.');
@@ -1021,9 +1047,11 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
     const float* g = grads + t.offset;
     const int64_t cnt = t.rows * t.cols;
     if (leaf == "q" || leaf == "k" || leaf == "v" || leaf == "o" || leaf == "fc" || leaf == "mp") {
-      launch_muon(d, o, workspace, p, g, m + t.offset, (int)t.rows, (int)t.cols,
-                  hp->lr_matrix * hp->lr_mult, hp->weight_decay, hp->momentum, hp->nesterov,
-                  hp->ns_a, hp->ns_b, hp->ns_c, hp->ns_steps, s);
+      const int k = next++ % kOptStreams;  // matrix -> side stream and buffer set
+      launch_muon(d, o, static_cast<char*>(workspace) + k * o.set_bytes, p, g, m + t.offset,
+                  (int)t.rows, (int)t.cols, hp->lr_matrix * hp->lr_mult, hp->weight_decay,
+                  hp->momentum, hp->nesterov, hp->ns_a, hp->ns_b, hp->ns_c, hp->ns_steps,
+                  sd.st[k]);
     } else {
       const float lr = n == "wte" || leaf == "ve" ? hp->lr_embed
                        : n == "lm_head"            ? hp->lr_unembed
@@ -1031,6 +1059,10 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
       launch_adamw(p, g, m + t.offset, v + t.offset, cnt, lr * hp->lr_mult, hp->beta1, hp->beta2,
                    hp->eps, hp->step, s);
     }
+  }
+  for (int i = 0; i < kOptStreams; ++i) {  // join
+    (void)hipEventRecord(sd.ev[i], sd.st[i]);
+    (void)hipStreamWaitEvent(s, sd.ev[i], 0);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));

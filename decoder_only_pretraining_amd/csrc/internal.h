@@ -184,11 +184,16 @@ void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const
                         const void* k, const void* v, const int32_t* seqlen, void* out,
                         void* workspace, hipStream_t s);
 
-// MuonAdamW (optim.hip). Workspace for the Newton-Schulz iteration of the
-// largest block matrix: workgroup partials + the norm scalar, X and Y
-// [r][k], A and A A [r][r] (compute dtype; r <= k the matrix's sides).
+// MuonAdamW (optim.hip). Workspace: kOptStreams buffer sets, each sized for
+// the Newton-Schulz iteration of the largest block matrix: workgroup
+// partials + the norm scalar, X and Y [r][k], A and A A [r][r] (compute
+// dtype; r <= k the matrix's sides).
+constexpr int kOptStreams = 8;  // side streams of the Muon matrices
 struct OptimPlan {
-  size_t part, x, y, a, aa, total;
+  size_t part, x, y, a, aa;  // offsets inside one buffer set
+  size_t set_bytes;
+  int sets;
+  size_t total;
 };
 OptimPlan make_optim_plan(const Dims& d);
 void launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float b1,

@@ -11,7 +11,10 @@
 // per Newton-Schulz step three products on the GEMM core (A = X X^T,
 // A A, (b A + c A A) X, A being symmetric so it serves as its own
 // transpose) and two element-wise passes, and a last pass applying
-// p <- p (1 - lr wd) - lr sqrt(max(1, rows / cols)) X.
+// p <- p (1 - lr wd) - lr sqrt(max(1, rows / cols)) X. The block matrices
+// are small products (768 x 768 x 768 at d12 fills 36 of 256 CUs), so the
+// matrices are spread over kOptStreams side streams, each with its own set
+// of buffers, forked from and joined back to the caller's stream.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -125,6 +128,7 @@ static unsigned ew_blocks(int64_t n) {
 }
 
 OptimPlan make_optim_plan(const Dims& d) {
+  // one buffer set per side stream
   OptimPlan o{};
   const int64_t mats[4][2] = {{d.Cq, d.C}, {d.Ckv, d.C}, {d.C, d.Cq}, {d.F, d.C}};
   int64_t max_rc = (int64_t)d.C * d.F, max_r = 0;
@@ -145,7 +149,9 @@ OptimPlan make_optim_plan(const Dims& d) {
   off += al((size_t)max_r * max_r * A);
   o.aa = off;
   off += al((size_t)max_r * max_r * A);
-  o.total = off;
+  o.set_bytes = off;
+  o.sets = kOptStreams;
+  o.total = off * kOptStreams;
   return o;
 }
 
