@@ -116,6 +116,8 @@ struct EpBase {
   using Aux = NoAux;
   // the epilogue of K split `split` (all splits write the same C by default)
   __device__ Derived at_split(int) const { return static_cast<const Derived&>(*this); }
+  // the epilogue of batch entry `b` (batched launches only)
+  __device__ Derived at_batch(int) const { return static_cast<const Derived&>(*this); }
   __device__ float value(int64_t, int64_t, float v) const { return v; }
   __device__ NoAux aux(int64_t, int64_t, int) const { return {}; }
   __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const NoAux&) const {
@@ -131,6 +133,12 @@ template <typename T>
 struct EpStore : EpBase<EpStore<T>> {
   T* C;
   int64_t ldc;
+  int64_t bstride;  // elements between the C of consecutive batch entries
+  __device__ EpStore at_batch(int b) const {
+    EpStore e = *this;
+    e.C += (int64_t)b * bstride;
+    return e;
+  }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
     put4<T>(C + m * ldc + n, v, cnt);
   }
@@ -238,6 +246,7 @@ EpStore<T> mk_store(void* C, int64_t ld) {
   EpStore<T> e;
   e.C = static_cast<T*>(C);
   e.ldc = ld;
+  e.bstride = 0;
   return e;
 }
 inline EpF32 mk_f32(float* C, int64_t ld, int acc) {
@@ -578,27 +587,41 @@ static void check_part(int64_t need, int64_t cap) {
 // measured 4-10% faster than 4 on the d12 products); the others 4.
 template <int BM, int BN, bool AK, bool BKM, class PA, class PB, class EP>
 void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
-                 int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s) {
+                 int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s, int batch = 1,
+                 int64_t sA = 0, int64_t sB = 0) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const int splits = K > 0 && kchunk > 0 ? (int)((K + kchunk - 1) / kchunk) : 1;
-  dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8));  // padded: see the kernel's tile order
+  // padded to a multiple of 8: see the kernel's tile order; y: batch entries
+  dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8), (unsigned)batch);
   constexpr int NW = BM == 256 ? 8 : 4;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq, NW>), grid,
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(A), lda,
-                     static_cast<const bf16*>(B), ldb, M, N, K, kchunk, tm, tn, pa, pb, ep, NoDeq{});
+                     static_cast<const bf16*>(B), ldb, M, N, K, kchunk, tm, tn, pa, pb, ep, NoDeq{},
+                     sA, sB);
 }
 
 template <bool AK, bool BKM, class PA, class PB, class EP>
 void run_bf16(Tile t, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
-              int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s) {
+              int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s, int batch = 1,
+              int64_t sA = 0, int64_t sB = 0) {
   if (t.bm == 256 && t.bn == 256)
-    launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
+    launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
   else if (t.bm == 256 && t.bn == 192)
-    launch_bf16<256, 192, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
+    launch_bf16<256, 192, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
   else if (t.bm == 256 && t.bn == 128)
-    launch_bf16<256, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
+    launch_bf16<256, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
   else
-    launch_bf16<128, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s);
+    launch_bf16<128, 128, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
+}
+
+// Tile of a batched product: the bf16 rule applied to the whole batch's
+// tile count (a batch of small products fills the machine together).
+static Tile pick_tile_batched(int batch, int64_t M, int64_t N) {
+  auto tiles = [&](int bm, int bn) { return batch * ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (N % 256 == 0 && tiles(256, 256) >= 256) return {256, 256};
+  if (N % 192 == 0 && tiles(256, 192) >= 256) return {256, 192};
+  if (tiles(256, 128) >= 256) return {256, 128};
+  return {128, 128};
 }
 
 // ------------------------------------------------------------ fp8 dispatch
@@ -614,7 +637,7 @@ void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, true, true, MODE, PreId, PreId, EP, Deq8>), grid,
                      dim3(256), 0, s, reinterpret_cast<const bf16*>(A), lda / 2,
                      reinterpret_cast<const bf16*>(B), ldb / 2, M, N, Kp, kc, tm, tn, PreId{},
-                     PreId{}, ep, dq);
+                     PreId{}, ep, dq, (int64_t)0, (int64_t)0);
 }
 
 template <int MODE, class EP>
@@ -863,6 +886,45 @@ SplitSum gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, co
 
 void splitk_sum(const SplitSum& r, hipStream_t s) {
   if (r.splits > 1) splitk_reduce(r.part, r.splits, r.M, r.N, r.C, r.accumulate, s);
+}
+
+}  // namespace gpt
+
+namespace gpt {
+using namespace gk;
+
+void gemm_nt_store_batched(const Dims& d, int batch, int64_t M, int N, int K, const void* A,
+                           int64_t sA, const void* B, int64_t sB, void* C, int64_t sC,
+                           hipStream_t s) {
+  if (d.bf16) {
+    EpStore<bf16> ep = mk_store<bf16>(C, N);
+    ep.bstride = sC;
+    run_bf16<true, true>(pick_tile_batched(batch, M, N), A, K, B, K, M, N, K, K, PreId{},
+                         PreId{}, ep, s, batch, sA, sB);
+  } else {
+    const size_t A4 = 4;
+    for (int b = 0; b < batch; ++b)
+      gemm_nt_store(d, M, N, K, static_cast<const char*>(A) + b * sA * A4,
+                    static_cast<const char*>(B) + b * sB * A4, static_cast<char*>(C) + b * sC * A4,
+                    s);
+  }
+}
+
+void gemm_nn_store_batched(const Dims& d, int batch, int64_t M, int N, int K, const void* A,
+                           int64_t sA, const void* B, int64_t sB, void* C, int64_t sC,
+                           hipStream_t s) {
+  if (d.bf16) {
+    EpStore<bf16> ep = mk_store<bf16>(C, N);
+    ep.bstride = sC;
+    run_bf16<true, false>(pick_tile_batched(batch, M, N), A, K, B, N, M, N, K, K, PreId{},
+                          PreId{}, ep, s, batch, sA, sB);
+  } else {
+    const size_t A4 = 4;
+    for (int b = 0; b < batch; ++b)
+      gemm_nn_store(d, M, N, K, static_cast<const char*>(A) + b * sA * A4,
+                    static_cast<const char*>(B) + b * sB * A4, static_cast<char*>(C) + b * sC * A4,
+                    s);
+  }
 }
 
 }  // namespace gpt

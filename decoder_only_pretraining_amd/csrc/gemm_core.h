@@ -304,7 +304,7 @@ template <int BM, int BN, int BK, bool AK, bool BKM, int MODE, class PA, class P
 __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, PA pa, PB pb, EP ep_in,
-    DQ dq) {
+    DQ dq, int64_t bsA, int64_t bsB) {
   static_assert(!PA::kActive && !PB::kActive, "direct LDS loads take operands as stored");
   constexpr bool F8 = MODE != 0;
   static_assert(!F8 || (AK && BKM), "fp8 products take K-major operands");
@@ -339,7 +339,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
   if (pid >= nwork) return;
   const int split = pid / ntiles;
   pid -= split * ntiles;
-  const EP ep = ep_in.at_split(split);  // split-K products write per-split partials
+  // batched products: gridDim.y independent problems, operands bsA / bsB
+  // elements apart, the epilogue's own stride for C
+  A += (int64_t)blockIdx.y * bsA;
+  B += (int64_t)blockIdx.y * bsB;
+  // split-K products write per-split partials
+  const EP ep = ep_in.at_split(split).at_batch((int)blockIdx.y);
   constexpr int GM = 8;
   const int group = pid / (GM * tiles_n);
   const int first_m = group * GM;

@@ -979,7 +979,7 @@ int gpt_optim_workspace_size(const gpt_config* cfg, size_t* bytes) {
   const int st = validate(cfg);
   if (st) return st;
   if (!bytes) return fail(GPT_E_NULLPTR, "output pointer is NULL");
-  *bytes = make_optim_plan(make_dims(*cfg)).total;
+  *bytes = make_optim_plan(*cfg).total;
   return GPT_OK;
 }
 
@@ -1004,7 +1004,7 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
   if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
     return fail(GPT_E_INVAL, "betas must lie in [0, 1)");
   const Dims d = make_dims(*cfg);
-  const OptimPlan o = make_optim_plan(d);
+  const OptimPlan o = make_optim_plan(*cfg);
   if (workspace_bytes < o.total)
     return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, o.total);
   int64_t n_elems = 0;
@@ -1014,55 +1014,22 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
   float* v = state + n_elems;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  // side streams and events of this device, created once (default priority)
-  struct Side {
-    hipStream_t st[kOptStreams];
-    hipEvent_t ev[kOptStreams + 1];
-  };
-  static std::mutex side_mu;
-  static std::map<int, Side> sides;
-  std::lock_guard<std::mutex> lock(side_mu);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(GPT_E_HIP, "hipGetDevice failed");
-  auto it = sides.find(dev);
-  if (it == sides.end()) {
-    Side sd{};
-    for (int i = 0; i < kOptStreams; ++i)
-      if (hipStreamCreateWithFlags(&sd.st[i], hipStreamNonBlocking) != hipSuccess)
-        return fail(GPT_E_HIP, "hipStreamCreateWithFlags failed");
-    for (int i = 0; i <= kOptStreams; ++i)
-      if (hipEventCreateWithFlags(&sd.ev[i], hipEventDisableTiming) != hipSuccess)
-        return fail(GPT_E_HIP, "hipEventCreateWithFlags failed");
-    it = sides.emplace(dev, sd).first;
-  }
-  const Side& sd = it->second;
-  (void)hipEventRecord(sd.ev[kOptStreams], s);  // fork
-  for (int i = 0; i < kOptStreams; ++i) (void)hipStreamWaitEvent(sd.st[i], sd.ev[kOptStreams], 0);
-  int next = 0;
+  // Muon: the block matrices, batched by shape
+  launch_muon_groups(d, muon_groups(*cfg), o, workspace, params, grads, m,
+                     hp->lr_matrix * hp->lr_mult, hp->weight_decay, hp->momentum, hp->nesterov,
+                     hp->ns_a, hp->ns_b, hp->ns_c, hp->ns_steps, s);
+  // AdamW: every other tensor
   for (const auto& t : lay) {
     const std::string& n = t.name;
     const size_t dot = n.find('.');
     const std::string leaf = dot == std::string::npos ? n : n.substr(dot + 1);
-    float* p = params + t.offset;
-    const float* g = grads + t.offset;
-    const int64_t cnt = t.rows * t.cols;
-    if (leaf == "q" || leaf == "k" || leaf == "v" || leaf == "o" || leaf == "fc" || leaf == "mp") {
-      const int k = next++ % kOptStreams;  // matrix -> side stream and buffer set
-      launch_muon(d, o, static_cast<char*>(workspace) + k * o.set_bytes, p, g, m + t.offset,
-                  (int)t.rows, (int)t.cols, hp->lr_matrix * hp->lr_mult, hp->weight_decay,
-                  hp->momentum, hp->nesterov, hp->ns_a, hp->ns_b, hp->ns_c, hp->ns_steps,
-                  sd.st[k]);
-    } else {
-      const float lr = n == "wte" || leaf == "ve" ? hp->lr_embed
-                       : n == "lm_head"            ? hp->lr_unembed
-                                                   : hp->lr_scalar;
-      launch_adamw(p, g, m + t.offset, v + t.offset, cnt, lr * hp->lr_mult, hp->beta1, hp->beta2,
-                   hp->eps, hp->step, s);
-    }
-  }
-  for (int i = 0; i < kOptStreams; ++i) {  // join
-    (void)hipEventRecord(sd.ev[i], sd.st[i]);
-    (void)hipStreamWaitEvent(s, sd.ev[i], 0);
+    if (leaf == "q" || leaf == "k" || leaf == "v" || leaf == "o" || leaf == "fc" || leaf == "mp")
+      continue;
+    const float lr = n == "wte" || leaf == "ve" ? hp->lr_embed
+                     : n == "lm_head"            ? hp->lr_unembed
+                                                 : hp->lr_scalar;
+    launch_adamw(params + t.offset, grads + t.offset, m + t.offset, v + t.offset,
+                 t.rows * t.cols, lr * hp->lr_mult, hp->beta1, hp->beta2, hp->eps, hp->step, s);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));

@@ -184,23 +184,26 @@ void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const
                         const void* k, const void* v, const int32_t* seqlen, void* out,
                         void* workspace, hipStream_t s);
 
-// MuonAdamW (optim.hip). Workspace: kOptStreams buffer sets, each sized for
-// the Newton-Schulz iteration of the largest block matrix: workgroup
-// partials + the norm scalar, X and Y [r][k], A and A A [r][r] (compute
-// dtype; r <= k the matrix's sides).
-constexpr int kOptStreams = 8;  // side streams of the Muon matrices
-struct OptimPlan {
-  size_t part, x, y, a, aa;  // offsets inside one buffer set
-  size_t set_bytes;
-  int sets;
-  size_t total;
+// MuonAdamW (optim.hip). The Muon matrices grouped by their wide shape
+// r x k (r <= k): element offsets and whether each is stored tall (k x r).
+struct MuonGroup {
+  int r, k;
+  std::vector<int64_t> off;
+  std::vector<int> tall;
 };
-OptimPlan make_optim_plan(const Dims& d);
+std::vector<MuonGroup> muon_groups(const gpt_config& c);
+// Workspace: per-matrix norm partials and scales, then X and Y [nm][r][k],
+// A and A A [nm][r][r] (compute dtype) for the largest batch of a group.
+struct OptimPlan {
+  size_t part, scal, x, y, a, aa, total;
+};
+OptimPlan make_optim_plan(const gpt_config& c);
 void launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float b1,
                   float b2, float eps, int step, hipStream_t s);
-void launch_muon(const Dims& d, const OptimPlan& o, void* workspace, float* p, const float* g,
-                 float* buf, int rows, int cols, float lr, float wd, float mu, int nesterov,
-                 float a, float b, float c, int steps, hipStream_t s);
+void launch_muon_groups(const Dims& d, const std::vector<MuonGroup>& groups, const OptimPlan& o,
+                        void* workspace, float* params, const float* grads, float* buf, float lr,
+                        float wd, float mu, int nesterov, float a, float b, float c, int steps,
+                        hipStream_t s);
 
 // ------------------------------------------------------------ GEMMs
 // Shapes: C[M][N] = sum_k A(m,k) B(n,k).
@@ -221,6 +224,15 @@ void gemm_nt_softcap(const Dims& d, int64_t M, int N, int K, const void* A, cons
 // product runs with both operands K-major (direct LDS fills).
 void gemm_nn_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                    void* C, hipStream_t s, const void* Bt = nullptr);
+// `batch` independent products in the compute dtype, operands and outputs
+// sA / sB / sC elements apart: nt C_b = A_b B_b^T (A [M][K], B [N][K]);
+// nn C_b = A_b B_b (A [M][K], B [K][N]).
+void gemm_nt_store_batched(const Dims& d, int batch, int64_t M, int N, int K, const void* A,
+                           int64_t sA, const void* B, int64_t sB, void* C, int64_t sC,
+                           hipStream_t s);
+void gemm_nn_store_batched(const Dims& d, int batch, int64_t M, int N, int K, const void* A,
+                           int64_t sA, const void* B, int64_t sB, void* C, int64_t sC,
+                           hipStream_t s);
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                  float* C, hipStream_t s, const void* Bt = nullptr);
 // C = (A B) * 2 sqrt(H): the MLP hidden gradient from h = relu(u)^2

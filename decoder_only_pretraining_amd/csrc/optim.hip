@@ -4,17 +4,18 @@
 // the six block linears of every layer, AdamW on everything else.
 //
 // AdamW is one HBM-bound pass per tensor (p, g, m, v read, p, m, v written).
-// Muon runs per matrix: a momentum pass that also sums the squares of the
+// Muon runs per group of equal-shaped matrices: a momentum pass that also sums the squares of the
 // update in fixed-order workgroup partials, a single-workgroup sum giving
 // 1 / (||u||_F + 1e-7), a pass writing X = u / ||u|| in the compute dtype
 // in the wide orientation (rows <= cols; tall matrices transposed), then
 // per Newton-Schulz step three products on the GEMM core (A = X X^T,
 // A A, (b A + c A A) X, A being symmetric so it serves as its own
 // transpose) and two element-wise passes, and a last pass applying
-// p <- p (1 - lr wd) - lr sqrt(max(1, rows / cols)) X. The block matrices
-// are small products (768 x 768 x 768 at d12 fills 36 of 256 CUs), so the
-// matrices are spread over kOptStreams side streams, each with its own set
-// of buffers, forked from and joined back to the caller's stream.
+// p <- p (1 - lr wd) - lr sqrt(max(1, rows / cols)) X. One product of a
+// block matrix is small (768 x 768 x 768 at d12 fills 36 of 256 CUs), so
+// the matrices of equal shape (in the wide orientation) run as one group:
+// every pass above is one launch over up to 64 matrices (a table of their
+// offsets; the products are batched GEMMs).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -23,8 +24,6 @@
 #include "internal.h"
 
 namespace gk {
-
-constexpr int kOptBlocks = 512;  // partial sums of the momentum pass
 
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
                                                     const float* __restrict__ g,
@@ -41,13 +40,26 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
   }
 }
 
-// buf <- mu buf + g; partial sums of u^2, u = g + mu buf (Nesterov) or buf,
-// one per workgroup (grid-stride, then a fixed-order reduction in LDS).
-__global__ __launch_bounds__(256) void muon_momentum_kernel(const float* __restrict__ g,
-                                                            float* __restrict__ buf, int64_t n,
-                                                            float mu, int nesterov,
+// The Muon matrices of one group share their wide shape r x k (r <= k);
+// entry y of a launch's table is a matrix: its element offset in params /
+// grads / the momentum buffer and whether it is stored tall (k x r).
+constexpr int kMaxMats = 64;   // matrices per batched launch
+constexpr int kMomBlocks = 64;  // momentum-pass workgroups per matrix
+struct MatTable {
+  int64_t off[kMaxMats];
+  int32_t tall[kMaxMats];
+};
+
+// buf <- mu buf + g; per-workgroup partial sums of u^2 (u = g + mu buf,
+// Nesterov, or buf) in a fixed order: part[y][blockIdx.x].
+__global__ __launch_bounds__(256) void muon_momentum_kernel(const float* __restrict__ g0,
+                                                            float* __restrict__ buf0,
+                                                            MatTable T, int64_t n, float mu,
+                                                            int nesterov,
                                                             float* __restrict__ part) {
   __shared__ float red[256];
+  const float* g = g0 + T.off[blockIdx.y];
+  float* buf = buf0 + T.off[blockIdx.y];
   float ss = 0.0f;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const float gi = g[i];
@@ -62,39 +74,38 @@ __global__ __launch_bounds__(256) void muon_momentum_kernel(const float* __restr
     if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+  if (threadIdx.x == 0) part[blockIdx.y * gridDim.x + blockIdx.x] = red[0];
 }
 
-// scal[0] = 1 / (sqrt(sum of the partials) + 1e-7)
-__global__ __launch_bounds__(256) void muon_norm_kernel(const float* __restrict__ part, int n,
-                                                        float* __restrict__ scal) {
-  __shared__ double red[256];
-  double s = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) s += part[i];
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) scal[0] = (float)(1.0 / (sqrt(red[0]) + 1e-7));
+// scal[y] = 1 / (sqrt(sum of matrix y's partials) + 1e-7), one workgroup each
+__global__ __launch_bounds__(64) void muon_norm_kernel(const float* __restrict__ part,
+                                                       float* __restrict__ scal) {
+  double s = part[blockIdx.x * kMomBlocks + threadIdx.x];  // kMomBlocks == 64 lanes
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (threadIdx.x == 0) scal[blockIdx.x] = (float)(1.0 / (sqrt(s) + 1e-7));
 }
 
-// X = u * scal[0] in the wide orientation: X [rows][cols] or, transposed,
-// X [cols][rows]; u recomputed from g and the updated buffer.
+// X[y] = u * scal[y] in the wide orientation [r][k] (a tall matrix, stored
+// [k][r], is transposed); u recomputed from g and the updated buffer.
 template <typename T>
-__global__ __launch_bounds__(256) void muon_to_x_kernel(const float* __restrict__ g,
-                                                        const float* __restrict__ buf, int rows,
-                                                        int cols, float mu, int nesterov,
-                                                        int transpose,
+__global__ __launch_bounds__(256) void muon_to_x_kernel(const float* __restrict__ g0,
+                                                        const float* __restrict__ buf0,
+                                                        MatTable Tb, int r, int k, float mu,
+                                                        int nesterov,
                                                         const float* __restrict__ scal,
-                                                        T* __restrict__ X) {
-  const int64_t n = (int64_t)rows * cols;
-  const float inv = scal[0];
+                                                        T* __restrict__ X0) {
+  const int y = blockIdx.y;
+  const float* g = g0 + Tb.off[y];
+  const float* buf = buf0 + Tb.off[y];
+  T* X = X0 + (int64_t)y * r * k;
+  const int tall = Tb.tall[y];
+  const int cols = tall ? r : k;  // the stored matrix's row length
+  const int64_t n = (int64_t)r * k;
+  const float inv = scal[y];
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const float u = nesterov ? g[i] + mu * buf[i] : buf[i];
-    const int64_t r = i / cols, c = i % cols;
-    X[transpose ? c * rows + r : i] = from_f<T>(u * inv);
+    const int64_t a = i / cols, c = i % cols;  // stored [a][c]
+    X[tall ? c * k + a : i] = from_f<T>(u * inv);
   }
 }
 
@@ -106,16 +117,21 @@ __global__ __launch_bounds__(256) void axpby_kernel(T* __restrict__ y, const T* 
     y[i] = from_f<T>(alpha * to_f(y[i]) + beta * to_f(x[i]));
 }
 
-// p <- p * decay - step * X (X in the wide orientation, see muon_to_x_kernel)
+// p <- p * decay - lr * sqrt(max(1, rows / cols)) * X[y] (back in p's layout)
 template <typename T>
-__global__ __launch_bounds__(256) void muon_apply_kernel(float* __restrict__ p,
-                                                         const T* __restrict__ X, int rows,
-                                                         int cols, int transpose, float decay,
-                                                         float step) {
-  const int64_t n = (int64_t)rows * cols;
+__global__ __launch_bounds__(256) void muon_apply_kernel(float* __restrict__ p0,
+                                                         const T* __restrict__ X0, MatTable Tb,
+                                                         int r, int k, float decay, float lr) {
+  const int y = blockIdx.y;
+  float* p = p0 + Tb.off[y];
+  const T* X = X0 + (int64_t)y * r * k;
+  const int tall = Tb.tall[y];
+  const int cols = tall ? r : k;
+  const float step = lr * (tall ? sqrtf((float)k / (float)r) : 1.0f);
+  const int64_t n = (int64_t)r * k;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / cols, c = i % cols;
-    p[i] = p[i] * decay - step * to_f(X[transpose ? c * rows + r : i]);
+    const int64_t a = i / cols, c = i % cols;
+    p[i] = p[i] * decay - step * to_f(X[tall ? c * k + a : i]);
   }
 }
 
@@ -127,31 +143,52 @@ static unsigned ew_blocks(int64_t n) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4096));
 }
 
-OptimPlan make_optim_plan(const Dims& d) {
-  // one buffer set per side stream
-  OptimPlan o{};
-  const int64_t mats[4][2] = {{d.Cq, d.C}, {d.Ckv, d.C}, {d.C, d.Cq}, {d.F, d.C}};
-  int64_t max_rc = (int64_t)d.C * d.F, max_r = 0;
-  for (const auto& m : mats) {
-    max_rc = std::max(max_rc, m[0] * m[1]);
-    max_r = std::max(max_r, std::min(m[0], m[1]));
+std::vector<MuonGroup> muon_groups(const gpt_config& c) {
+  std::vector<MuonGroup> out;
+  for (const auto& t : param_layout(c)) {
+    const size_t dot = t.name.find('.');
+    if (dot == std::string::npos) continue;
+    const std::string leaf = t.name.substr(dot + 1);
+    if (!(leaf == "q" || leaf == "k" || leaf == "v" || leaf == "o" || leaf == "fc" || leaf == "mp"))
+      continue;
+    const int r = (int)std::min(t.rows, t.cols), k = (int)std::max(t.rows, t.cols);
+    auto it = std::find_if(out.begin(), out.end(),
+                           [&](const MuonGroup& g) { return g.r == r && g.k == k; });
+    if (it == out.end()) {
+      out.push_back(MuonGroup{r, k, {}, {}});
+      it = out.end() - 1;
+    }
+    it->off.push_back(t.offset);
+    it->tall.push_back(t.rows > t.cols ? 1 : 0);
   }
+  return out;
+}
+
+OptimPlan make_optim_plan(const gpt_config& c) {
+  const Dims d = make_dims(c);
   const size_t A = (size_t)d.act_bytes;
+  size_t xb = 0, ab = 0;
+  for (const auto& g : muon_groups(c)) {
+    const size_t nm = std::min<size_t>(g.off.size(), gk::kMaxMats);
+    xb = std::max(xb, nm * g.r * g.k * A);
+    ab = std::max(ab, nm * g.r * g.r * A);
+  }
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  OptimPlan o{};
   size_t off = 0;
   o.part = off;
-  off += al((size_t)gk::kOptBlocks * 4 + 64);
+  off += al((size_t)gk::kMaxMats * gk::kMomBlocks * 4);
+  o.scal = off;
+  off += al((size_t)gk::kMaxMats * 4);
   o.x = off;
-  off += al((size_t)max_rc * A);
+  off += al(xb);
   o.y = off;
-  off += al((size_t)max_rc * A);
+  off += al(xb);
   o.a = off;
-  off += al((size_t)max_r * max_r * A);
+  off += al(ab);
   o.aa = off;
-  off += al((size_t)max_r * max_r * A);
-  o.set_bytes = off;
-  o.sets = kOptStreams;
-  o.total = off * kOptStreams;
+  off += al(ab);
+  o.total = off;
   return o;
 }
 
@@ -163,45 +200,57 @@ void launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float
 }
 
 template <typename T>
-static void muon_typed(const Dims& d, const OptimPlan& o, char* ws, float* p, const float* g,
-                       float* buf, int rows, int cols, float lr, float wd, float mu, int nesterov,
-                       float a, float b, float c, int steps, hipStream_t s) {
-  const int64_t n = (int64_t)rows * cols;
+static void muon_chunk(const Dims& d, const OptimPlan& o, char* ws, const gk::MatTable& tb,
+                       int nm, int r, int k, float* params, const float* grads, float* buf,
+                       float lr, float wd, float mu, int nesterov, float a, float b, float c,
+                       int steps, hipStream_t s) {
   float* part = reinterpret_cast<float*>(ws + o.part);
-  float* scal = part + gk::kOptBlocks;
+  float* scal = reinterpret_cast<float*>(ws + o.scal);
   T* X = reinterpret_cast<T*>(ws + o.x);
   T* Y = reinterpret_cast<T*>(ws + o.y);
   T* Am = reinterpret_cast<T*>(ws + o.a);
   T* AA = reinterpret_cast<T*>(ws + o.aa);
-  const int tr = rows > cols ? 1 : 0;
-  const int r = tr ? cols : rows, k = tr ? rows : cols;  // X is [r][k], r <= k
-  hipLaunchKernelGGL(gk::muon_momentum_kernel, dim3(gk::kOptBlocks), dim3(256), 0, s, g, buf, n,
-                     mu, nesterov, part);
-  hipLaunchKernelGGL(gk::muon_norm_kernel, dim3(1), dim3(256), 0, s, part, gk::kOptBlocks, scal);
-  hipLaunchKernelGGL(gk::muon_to_x_kernel<T>, dim3(ew_blocks(n)), dim3(256), 0, s, g, buf, rows,
-                     cols, mu, nesterov, tr, scal, X);
+  const int64_t n = (int64_t)r * k, nr = (int64_t)r * r;
+  const unsigned per = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 64));
+  hipLaunchKernelGGL(gk::muon_momentum_kernel, dim3(gk::kMomBlocks, nm), dim3(256), 0, s, grads,
+                     buf, tb, n, mu, nesterov, part);
+  hipLaunchKernelGGL(gk::muon_norm_kernel, dim3(nm), dim3(64), 0, s, part, scal);
+  hipLaunchKernelGGL(gk::muon_to_x_kernel<T>, dim3(per, nm), dim3(256), 0, s, grads, buf, tb, r, k,
+                     mu, nesterov, scal, X);
   for (int it = 0; it < steps; ++it) {
-    gemm_nt_store(d, r, r, k, X, X, Am, s);   // A = X X^T
-    gemm_nt_store(d, r, r, r, Am, Am, AA, s); // A A (A symmetric)
-    hipLaunchKernelGGL(gk::axpby_kernel<T>, dim3(ew_blocks((int64_t)r * r)), dim3(256), 0, s, Am,
-                       AA, (int64_t)r * r, b, c);  // B = b A + c A A
-    gemm_nn_store(d, r, k, r, Am, X, Y, s);   // Y = B X
-    hipLaunchKernelGGL(gk::axpby_kernel<T>, dim3(ew_blocks(n)), dim3(256), 0, s, X, Y, n, a,
-                       1.0f);                  // X = a X + Y
+    gemm_nt_store_batched(d, nm, r, r, k, X, n, X, n, Am, nr, s);     // A = X X^T
+    gemm_nt_store_batched(d, nm, r, r, r, Am, nr, Am, nr, AA, nr, s); // A A (A symmetric)
+    hipLaunchKernelGGL(gk::axpby_kernel<T>, dim3(ew_blocks(nm * nr)), dim3(256), 0, s, Am, AA,
+                       nm * nr, b, c);                                  // b A + c A A
+    gemm_nn_store_batched(d, nm, r, k, r, Am, nr, X, n, Y, n, s);      // (b A + c A A) X
+    hipLaunchKernelGGL(gk::axpby_kernel<T>, dim3(ew_blocks(nm * n)), dim3(256), 0, s, X, Y,
+                       nm * n, a, 1.0f);                                // X = a X + ...
   }
-  const float scale = std::sqrt(std::max(1.0f, (float)rows / (float)cols));
-  hipLaunchKernelGGL(gk::muon_apply_kernel<T>, dim3(ew_blocks(n)), dim3(256), 0, s, p, X, rows,
-                     cols, tr, 1.0f - lr * wd, lr * scale);
+  hipLaunchKernelGGL(gk::muon_apply_kernel<T>, dim3(per, nm), dim3(256), 0, s, params, X, tb, r,
+                     k, 1.0f - lr * wd, lr);
 }
 
-void launch_muon(const Dims& d, const OptimPlan& o, void* workspace, float* p, const float* g,
-                 float* buf, int rows, int cols, float lr, float wd, float mu, int nesterov,
-                 float a, float b, float c, int steps, hipStream_t s) {
+void launch_muon_groups(const Dims& d, const std::vector<MuonGroup>& groups, const OptimPlan& o,
+                        void* workspace, float* params, const float* grads, float* buf, float lr,
+                        float wd, float mu, int nesterov, float a, float b, float c, int steps,
+                        hipStream_t s) {
   char* ws = static_cast<char*>(workspace);
-  if (d.bf16)
-    muon_typed<bf16>(d, o, ws, p, g, buf, rows, cols, lr, wd, mu, nesterov, a, b, c, steps, s);
-  else
-    muon_typed<float>(d, o, ws, p, g, buf, rows, cols, lr, wd, mu, nesterov, a, b, c, steps, s);
+  for (const auto& g : groups) {
+    for (size_t i0 = 0; i0 < g.off.size(); i0 += gk::kMaxMats) {
+      const int nm = (int)std::min<size_t>(gk::kMaxMats, g.off.size() - i0);
+      gk::MatTable tb{};
+      for (int y = 0; y < nm; ++y) {
+        tb.off[y] = g.off[i0 + y];
+        tb.tall[y] = g.tall[i0 + y];
+      }
+      if (d.bf16)
+        muon_chunk<bf16>(d, o, ws, tb, nm, g.r, g.k, params, grads, buf, lr, wd, mu, nesterov, a,
+                         b, c, steps, s);
+      else
+        muon_chunk<float>(d, o, ws, tb, nm, g.r, g.k, params, grads, buf, lr, wd, mu, nesterov,
+                          a, b, c, steps, s);
+    }
+  }
 }
 
 }  // namespace gpt

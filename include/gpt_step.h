@@ -302,12 +302,8 @@ int gpt_optim_workspace_size(const gpt_config* cfg, size_t* bytes);
  *          before step 1; updated.
  *   workspace (device) >= gpt_optim_workspace_size bytes; scratch.
  * params, grads, state and workspace 256-byte aligned. Validation errors
- * return before anything is enqueued; the work is enqueued on `stream`:
- * the Muon matrices run on 8 library-owned side streams of the current
- * device (created on the first call, default priority, kept until the
- * process ends) that wait for `stream` at the start of the call and that
- * `stream` waits for at its end, so the call orders like one enqueued
- * operation on `stream`. Calls are serialised on the host; concurrent
+ * return before anything is enqueued; the work is enqueued on `stream`
+ * (the Muon matrices of equal shape run as batched launches). Concurrent
  * calls need distinct workspaces.
  */
 int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float* params,
