@@ -99,14 +99,14 @@ __global__ __launch_bounds__(256) void muon_to_x_kernel(const float* __restrict_
   const float* buf = buf0 + Tb.off[y];
   T* X = X0 + (int64_t)y * r * k;
   const int tall = Tb.tall[y];
-  const int cols = tall ? r : k;  // the stored matrix's row length
-  const int64_t n = (int64_t)r * k;
+  const int rows = tall ? k : r, cols = tall ? r : k;  // the stored matrix
   const float inv = scal[y];
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const float u = nesterov ? g[i] + mu * buf[i] : buf[i];
-    const int64_t a = i / cols, c = i % cols;  // stored [a][c]
-    X[tall ? c * k + a : i] = from_f<T>(u * inv);
-  }
+  for (int a = blockIdx.x; a < rows; a += gridDim.x)  // stored row a, no index division
+    for (int c = threadIdx.x; c < cols; c += 256) {
+      const int64_t i = (int64_t)a * cols + c;
+      const float u = nesterov ? g[i] + mu * buf[i] : buf[i];
+      X[tall ? (int64_t)c * k + a : i] = from_f<T>(u * inv);
+    }
 }
 
 // y = alpha * y + beta * x (element-wise, compute dtype)
@@ -126,13 +126,13 @@ __global__ __launch_bounds__(256) void muon_apply_kernel(float* __restrict__ p0,
   float* p = p0 + Tb.off[y];
   const T* X = X0 + (int64_t)y * r * k;
   const int tall = Tb.tall[y];
-  const int cols = tall ? r : k;
+  const int rows = tall ? k : r, cols = tall ? r : k;
   const float step = lr * (tall ? sqrtf((float)k / (float)r) : 1.0f);
-  const int64_t n = (int64_t)r * k;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t a = i / cols, c = i % cols;
-    p[i] = p[i] * decay - step * to_f(X[tall ? c * k + a : i]);
-  }
+  for (int a = blockIdx.x; a < rows; a += gridDim.x)
+    for (int c = threadIdx.x; c < cols; c += 256) {
+      const int64_t i = (int64_t)a * cols + c;
+      p[i] = p[i] * decay - step * to_f(X[tall ? (int64_t)c * k + a : i]);
+    }
 }
 
 }  // namespace gk
