@@ -25,6 +25,29 @@
 
 namespace gk {
 
+// four elements per thread and iteration (16-byte aligned tensors whose
+// length is a multiple of 4)
+__global__ __launch_bounds__(256) void adamw4_kernel(float* __restrict__ p,
+                                                     const float* __restrict__ g,
+                                                     float* __restrict__ m, float* __restrict__ v,
+                                                     int64_t n4, float lr, float b1, float b2,
+                                                     float eps, float c1, float c2) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const f32x4 gi = reinterpret_cast<const f32x4*>(g)[i];
+    f32x4 mi = reinterpret_cast<f32x4*>(m)[i], vi = reinterpret_cast<f32x4*>(v)[i];
+    f32x4 pi = reinterpret_cast<f32x4*>(p)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mi[e] = b1 * mi[e] + (1.0f - b1) * gi[e];
+      vi[e] = b2 * vi[e] + (1.0f - b2) * gi[e] * gi[e];
+      pi[e] -= lr * (mi[e] / c1) / (sqrtf(vi[e] / c2) + eps);
+    }
+    reinterpret_cast<f32x4*>(m)[i] = mi;
+    reinterpret_cast<f32x4*>(v)[i] = vi;
+    reinterpret_cast<f32x4*>(p)[i] = pi;
+  }
+}
+
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
                                                     const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
@@ -98,14 +121,28 @@ __global__ __launch_bounds__(256) void muon_to_x_kernel(const float* __restrict_
   const float* g = g0 + Tb.off[y];
   const float* buf = buf0 + Tb.off[y];
   T* X = X0 + (int64_t)y * r * k;
-  const int tall = Tb.tall[y];
-  const int rows = tall ? k : r, cols = tall ? r : k;  // the stored matrix
   const float inv = scal[y];
-  for (int a = blockIdx.x; a < rows; a += gridDim.x)  // stored row a, no index division
-    for (int c = threadIdx.x; c < cols; c += 256) {
-      const int64_t i = (int64_t)a * cols + c;
+  if (Tb.tall[y]) {  // stored [k][r]: 64 x 64 tiles through LDS, both sides coalesced
+    __shared__ float tile[64][65];
+    const int tr = r / 64, tk = k / 64;  // r and k are multiples of 64
+    for (int t = blockIdx.x; t < tr * tk; t += gridDim.x) {
+      const int a0 = (t / tr) * 64, c0 = (t % tr) * 64;  // stored rows a0.., cols c0..
+      for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int64_t i = (int64_t)(a0 + e / 64) * r + c0 + e % 64;
+        tile[e / 64][e % 64] = (nesterov ? g[i] + mu * buf[i] : buf[i]) * inv;
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < 64 * 64; e += 256)  // X row c0 + e / 64, col a0 + e % 64
+        X[(int64_t)(c0 + e / 64) * k + a0 + e % 64] = from_f<T>(tile[e % 64][e / 64]);
+      __syncthreads();
+    }
+    return;
+  }
+  for (int a = blockIdx.x; a < r; a += gridDim.x)  // stored [r][k], row by row
+    for (int c = threadIdx.x; c < k; c += 256) {
+      const int64_t i = (int64_t)a * k + c;
       const float u = nesterov ? g[i] + mu * buf[i] : buf[i];
-      X[tall ? (int64_t)c * k + a : i] = from_f<T>(u * inv);
+      X[i] = from_f<T>(u * inv);
     }
 }
 
@@ -125,13 +162,27 @@ __global__ __launch_bounds__(256) void muon_apply_kernel(float* __restrict__ p0,
   const int y = blockIdx.y;
   float* p = p0 + Tb.off[y];
   const T* X = X0 + (int64_t)y * r * k;
-  const int tall = Tb.tall[y];
-  const int rows = tall ? k : r, cols = tall ? r : k;
-  const float step = lr * (tall ? sqrtf((float)k / (float)r) : 1.0f);
-  for (int a = blockIdx.x; a < rows; a += gridDim.x)
-    for (int c = threadIdx.x; c < cols; c += 256) {
-      const int64_t i = (int64_t)a * cols + c;
-      p[i] = p[i] * decay - step * to_f(X[tall ? (int64_t)c * k + a : i]);
+  if (Tb.tall[y]) {  // p stored [k][r], X [r][k]: 64 x 64 tiles through LDS
+    __shared__ float tile[64][65];
+    const float step = lr * sqrtf((float)k / (float)r);
+    const int tr = r / 64, tk = k / 64;
+    for (int t = blockIdx.x; t < tr * tk; t += gridDim.x) {
+      const int a0 = (t / tr) * 64, c0 = (t % tr) * 64;
+      for (int e = threadIdx.x; e < 64 * 64; e += 256)  // X rows c0.., cols a0..
+        tile[e / 64][e % 64] = to_f(X[(int64_t)(c0 + e / 64) * k + a0 + e % 64]);
+      __syncthreads();
+      for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int64_t i = (int64_t)(a0 + e / 64) * r + c0 + e % 64;
+        p[i] = p[i] * decay - step * tile[e % 64][e / 64];
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  for (int a = blockIdx.x; a < r; a += gridDim.x)
+    for (int c = threadIdx.x; c < k; c += 256) {
+      const int64_t i = (int64_t)a * k + c;
+      p[i] = p[i] * decay - lr * to_f(X[i]);
     }
 }
 
@@ -195,8 +246,13 @@ OptimPlan make_optim_plan(const gpt_config& c) {
 void launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float b1,
                   float b2, float eps, int step, hipStream_t s) {
   const float c1 = 1.0f - std::pow(b1, (float)step), c2 = 1.0f - std::pow(b2, (float)step);
-  hipLaunchKernelGGL(gk::adamw_kernel, dim3(ew_blocks(n)), dim3(256), 0, s, p, g, m, v, n, lr, b1,
-                     b2, eps, c1, c2);
+  const bool vec = n % 4 == 0 && ((uintptr_t)p | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(gk::adamw4_kernel, dim3(ew_blocks(n / 4)), dim3(256), 0, s, p, g, m, v,
+                       n / 4, lr, b1, b2, eps, c1, c2);
+  else
+    hipLaunchKernelGGL(gk::adamw_kernel, dim3(ew_blocks(n)), dim3(256), 0, s, p, g, m, v, n, lr,
+                       b1, b2, eps, c1, c2);
 }
 
 template <typename T>
