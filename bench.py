@@ -233,13 +233,18 @@ def optimizer_bench(args):
                               ns_b=-4.7750, ns_c=2.0315)
 
     t = 0
+    # micro-batches 2-4 see the same weights: they keep the bf16 weight
+    # mirrors the first call converted
+    reuse = B.make_config(w, B.GPT_F_ACCUMULATE | B.GPT_F_REUSE_WEIGHTS)
 
     def full_step():
         nonlocal t
         t += 1
         step.grads.zero_()
-        for _ in range(4):
-            step.run(stream)
+        step.run(stream)
+        for _ in range(3):
+            B.fwd_bwd(reuse, step.params, step.tokens, step.targets, step.loss, step.grads,
+                      step.workspace, stream)
         B.optimizer_step(step.cfg, hp(t), step.params, step.grads, state, ws, stream)
 
     for _ in range(args.warmup):

@@ -18,6 +18,7 @@ GPT_DT_F32, GPT_DT_BF16 = 0, 1
 GPT_F_ACCUMULATE = 1
 GPT_F_SMEAR = 2
 GPT_F_BACKOUT = 4
+GPT_F_REUSE_WEIGHTS = 8
 
 STATUS = {0: "GPT_OK", -1: "GPT_E_INVAL", -2: "GPT_E_NULLPTR", -3: "GPT_E_ALIGN",
           -4: "GPT_E_WORKSPACE", -5: "GPT_E_UNSUPPORTED", -6: "GPT_E_HIP"}

@@ -106,6 +106,7 @@ Dims make_dims(const gpt_config& c) {
   d.smear = (c.flags & GPT_F_SMEAR) != 0;
   d.backout = (c.flags & GPT_F_BACKOUT) != 0;
   d.mid = d.L / 2;
+  d.reuse_weights = (c.flags & GPT_F_REUSE_WEIGHTS) != 0;
   return d;
 }
 
@@ -133,7 +134,7 @@ static int validate(const gpt_config* c) {
   if (c->compute_dtype != GPT_DT_F32 && c->compute_dtype != GPT_DT_BF16)
     return fail(GPT_E_INVAL, "compute_dtype %d unknown", c->compute_dtype);
   if (c->fp8_linears != 0 && c->fp8_linears != 1) return fail(GPT_E_INVAL, "fp8_linears must be 0 or 1");
-  if (c->flags & ~(GPT_F_ACCUMULATE | GPT_F_SMEAR | GPT_F_BACKOUT))
+  if (c->flags & ~(GPT_F_ACCUMULATE | GPT_F_SMEAR | GPT_F_BACKOUT | GPT_F_REUSE_WEIGHTS))
     return fail(GPT_E_INVAL, "unknown flag bits 0x%x", c->flags);
   if (!(std::isfinite(c->rope_theta) && c->rope_theta > 1.0f))
     return fail(GPT_E_INVAL, "rope_theta must be finite and > 1");
@@ -345,7 +346,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   auto wmatT = [&](int64_t off) -> const void* {
     return d.bf16 ? static_cast<const void*>(W + P.wct + off * 2) : nullptr;
   };
-  if (d.bf16) {
+  if (d.bf16 && !d.reuse_weights) {
     std::vector<CastSeg> segs;
     for (int l = 0; l < d.L; ++l)
       if (F.veg[l] >= 0) segs.push_back({F.veg[l], (int64_t)d.Hk * d.C});

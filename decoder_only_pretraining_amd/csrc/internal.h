@@ -25,6 +25,7 @@ struct Dims {
   bool smear;       // Smear at the embedding (GPT_F_SMEAR)
   bool backout;     // Backout before the final norm (GPT_F_BACKOUT)
   int mid;          // Backout caches the stream entering this layer (L / 2)
+  bool reuse_weights;  // GPT_F_REUSE_WEIGHTS: keep the workspace's bf16 weight mirrors
 };
 
 Dims make_dims(const gpt_config& c);

@@ -60,7 +60,13 @@ enum {
    * Backout: the final norm reads x - backout_lambda * x_mid, where x_mid
    *   is the residual stream entering layer n_layer / 2. */
   GPT_F_SMEAR = 2,
-  GPT_F_BACKOUT = 4
+  GPT_F_BACKOUT = 4,
+  /* The previous call on this workspace had the same params (same values,
+   * e.g. the micro-batches of one optimizer step): its bf16 weight mirrors
+   * in the workspace are reused instead of converted again from the fp32
+   * params (fp8 weight codes are still made each call). Undefined results
+   * if the params or the workspace changed since. */
+  GPT_F_REUSE_WEIGHTS = 8
 };
 
 /*

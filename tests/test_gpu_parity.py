@@ -102,6 +102,31 @@ def test_repeatable():
         assert rel <= 1e-6, name
 
 
+def test_reused_weight_mirrors_give_the_same_step():
+    """GPT_F_REUSE_WEIGHTS on the call after one with the same params and
+    workspace: the bf16 mirrors left by the first call are what a fresh
+    conversion would write, so loss and gradients are bit-identical."""
+    import torch
+    w = SMALL_BF16
+    p, tok, tgt = inputs(w, 33, 34)
+    step = B.Step(w, p, tok, tgt)
+    step.run()
+    torch.cuda.synchronize()
+    l1, g1 = step.loss.item(), step.grads.cpu().numpy().copy()
+    cfg = B.make_config(w, B.GPT_F_REUSE_WEIGHTS)
+    B.fwd_bwd(cfg, step.params, step.tokens, step.targets, step.loss, step.grads, step.workspace)
+    torch.cuda.synchronize()
+    assert step.loss.item() == l1
+    g2 = step.grads.cpu().numpy()
+    offs = oracle.param_offsets(w)[0]
+    for name, (o, s) in offs.items():   # tables take fp32 atomics: order-dependent sums
+        n = int(np.prod(s))
+        if name == "wte" or name.endswith(".ve"):
+            assert per_tensor(w, g2, g1)[name][0] <= 1e-6, name
+        else:
+            assert np.array_equal(g2[o:o + n], g1[o:o + n]), name
+
+
 SMALL_BF16 = W.get("d12").with_(name="small_bf16", n_layer=4, seq_len=300, batch=2,
                                 short_window=75, vocab=2048)
 SMALL_BF16_GQA = SMALL_BF16.with_(name="small_bf16_gqa", n_kv_head=2, seq_len=256, batch=3,
