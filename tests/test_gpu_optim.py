@@ -73,8 +73,12 @@ def test_fp32_optimizer_parity(name):
         assert _rel(vg[sl], vo[sl]) <= 1e-4, tname
 
 
-def test_bf16_optimizer_parity_d12_widths():
-    w = W.get("d12").with_(name="opt_bf16", n_layer=2, vocab=2048)
+@pytest.mark.parametrize("base", ["d12", "d26"])
+def test_bf16_optimizer_parity_d12_widths(base):
+    """d12 widths (768 / 3072: 256 x 256 batched tiles) and d26 widths
+    (1664 / 6656, fp8 linears in the model: 256 x 128 tiles, the
+    Newton-Schulz products in bf16 all the same)."""
+    w = W.get(base).with_(name=f"opt_{base}", n_layer=2 if base == "d12" else 1, vocab=2048)
     p0, pg, po, mg, mo, vg, vo = _run(w, 2, 23)
     worst = {}
     for tname, (o, s) in oracle.param_offsets(w)[0].items():
