@@ -186,6 +186,29 @@ struct EpResid : EpBase<EpResid> {  // C = R + acc (residual stream, fp32)
     store4a(m, n, v, cnt, aux(m, n, cnt));
   }
 };
+// C = alpha R + beta acc (R and C alike, same leading dimension); batched
+// launches step R and C by bstride elements per entry
+template <typename T>
+struct EpLin : EpBase<EpLin<T>> {
+  const T* R;
+  T* C;
+  int64_t ldc, bstride;
+  float alpha, beta;
+  using Aux = f32x4;
+  __device__ EpLin at_batch(int b) const {
+    EpLin e = *this;
+    e.R += (int64_t)b * bstride;
+    e.C += (int64_t)b * bstride;
+    return e;
+  }
+  __device__ f32x4 aux(int64_t m, int64_t n, int cnt) const { return get4<T>(R + m * ldc + n, cnt); }
+  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const f32x4& r) const {
+    put4<T>(C + m * ldc + n, alpha * r + beta * v, cnt);
+  }
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+    store4a(m, n, v, cnt, aux(m, n, cnt));
+  }
+};
 template <typename T>
 struct EpRelu2 : EpBase<EpRelu2<T>> {  // C = relu(acc)^2 (the MLP hidden activation h)
   T* C;
@@ -924,6 +947,49 @@ void gemm_nn_store_batched(const Dims& d, int batch, int64_t M, int N, int K, co
       gemm_nn_store(d, M, N, K, static_cast<const char*>(A) + b * sA * A4,
                     static_cast<const char*>(B) + b * sB * A4, static_cast<char*>(C) + b * sC * A4,
                     s);
+  }
+}
+
+}  // namespace gpt
+
+namespace gpt {
+using namespace gk;
+
+template <typename T>
+static EpLin<T> mk_lin(const void* R, void* C, int64_t ld, int64_t bstride, float alpha,
+                       float beta) {
+  EpLin<T> e;
+  e.R = static_cast<const T*>(R);
+  e.C = static_cast<T*>(C);
+  e.ldc = ld;
+  e.bstride = bstride;
+  e.alpha = alpha;
+  e.beta = beta;
+  return e;
+}
+
+void gemm_lin_batched(const Dims& d, bool nn, int batch, int64_t M, int N, int K, const void* A,
+                      int64_t sA, const void* B, int64_t sB, const void* R, void* C, int64_t sC,
+                      float alpha, float beta, hipStream_t s) {
+  if (d.bf16) {
+    const EpLin<bf16> ep = mk_lin<bf16>(R, C, N, sC, alpha, beta);
+    if (nn)
+      run_bf16<true, false>(pick_tile_batched(batch, M, N), A, K, B, N, M, N, K, K, PreId{},
+                            PreId{}, ep, s, batch, sA, sB);
+    else
+      run_bf16<true, true>(pick_tile_batched(batch, M, N), A, K, B, K, M, N, K, K, PreId{},
+                           PreId{}, ep, s, batch, sA, sB);
+    return;
+  }
+  for (int b = 0; b < batch; ++b) {  // fp32: one product per entry
+    const float* Ab = static_cast<const float*>(A) + b * sA;
+    const float* Bb = static_cast<const float*>(B) + b * sB;
+    const EpLin<float> ep = mk_lin<float>(static_cast<const float*>(R) + b * sC,
+                                          static_cast<float*>(C) + b * sC, N, 0, alpha, beta);
+    if (nn)
+      run_f32<float, true, false>(Ab, K, Bb, N, M, N, K, PreId{}, PreId{}, ep, s);
+    else
+      run_f32<float, true, true>(Ab, K, Bb, K, M, N, K, PreId{}, PreId{}, ep, s);
   }
 }
 

@@ -234,6 +234,11 @@ void gemm_nt_store_batched(const Dims& d, int batch, int64_t M, int N, int K, co
 void gemm_nn_store_batched(const Dims& d, int batch, int64_t M, int N, int K, const void* A,
                            int64_t sA, const void* B, int64_t sB, void* C, int64_t sC,
                            hipStream_t s);
+// Batched C_b = alpha R_b + beta (A_b op(B_b)) with R_b, C_b [M][N] sC apart;
+// op: B_b^T (B [N][K], nn = false) or B_b (B [K][N], nn = true).
+void gemm_lin_batched(const Dims& d, bool nn, int batch, int64_t M, int N, int K, const void* A,
+                      int64_t sA, const void* B, int64_t sB, const void* R, void* C, int64_t sC,
+                      float alpha, float beta, hipStream_t s);
 void gemm_nn_f32(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,
                  float* C, hipStream_t s, const void* Bt = nullptr);
 // C = (A B) * 2 sqrt(H): the MLP hidden gradient from h = relu(u)^2

@@ -8,9 +8,10 @@
 // update in fixed-order workgroup partials, a single-workgroup sum giving
 // 1 / (||u||_F + 1e-7), a pass writing X = u / ||u|| in the compute dtype
 // in the wide orientation (rows <= cols; tall matrices transposed), then
-// per Newton-Schulz step three products on the GEMM core (A = X X^T,
-// A A, (b A + c A A) X, A being symmetric so it serves as its own
-// transpose) and two element-wise passes, and a last pass applying
+// per Newton-Schulz step three products on the GEMM core: A = X X^T, then
+// b A + c A A and a X + (b A + c A A) X, the linear combinations formed in
+// the product epilogues (A is symmetric, so it serves as its own
+// transpose), and a last pass applying
 // p <- p (1 - lr wd) - lr sqrt(max(1, rows / cols)) X. One product of a
 // block matrix is small (768 x 768 x 768 at d12 fills 36 of 256 CUs), so
 // the matrices of equal shape (in the wide orientation) run as one group:
@@ -19,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <utility>
 
 #include "device_common.h"
 #include "internal.h"
@@ -146,14 +148,6 @@ __global__ __launch_bounds__(256) void muon_to_x_kernel(const float* __restrict_
     }
 }
 
-// y = alpha * y + beta * x (element-wise, compute dtype)
-template <typename T>
-__global__ __launch_bounds__(256) void axpby_kernel(T* __restrict__ y, const T* __restrict__ x,
-                                                    int64_t n, float alpha, float beta) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    y[i] = from_f<T>(alpha * to_f(y[i]) + beta * to_f(x[i]));
-}
-
 // p <- p * decay - lr * sqrt(max(1, rows / cols)) * X[y] (back in p's layout)
 template <typename T>
 __global__ __launch_bounds__(256) void muon_apply_kernel(float* __restrict__ p0,
@@ -274,13 +268,12 @@ static void muon_chunk(const Dims& d, const OptimPlan& o, char* ws, const gk::Ma
   hipLaunchKernelGGL(gk::muon_to_x_kernel<T>, dim3(per, nm), dim3(256), 0, s, grads, buf, tb, r, k,
                      mu, nesterov, scal, X);
   for (int it = 0; it < steps; ++it) {
-    gemm_nt_store_batched(d, nm, r, r, k, X, n, X, n, Am, nr, s);     // A = X X^T
-    gemm_nt_store_batched(d, nm, r, r, r, Am, nr, Am, nr, AA, nr, s); // A A (A symmetric)
-    hipLaunchKernelGGL(gk::axpby_kernel<T>, dim3(ew_blocks(nm * nr)), dim3(256), 0, s, Am, AA,
-                       nm * nr, b, c);                                  // b A + c A A
-    gemm_nn_store_batched(d, nm, r, k, r, Am, nr, X, n, Y, n, s);      // (b A + c A A) X
-    hipLaunchKernelGGL(gk::axpby_kernel<T>, dim3(ew_blocks(nm * n)), dim3(256), 0, s, X, Y,
-                       nm * n, a, 1.0f);                                // X = a X + ...
+    gemm_nt_store_batched(d, nm, r, r, k, X, n, X, n, Am, nr, s);  // A = X X^T
+    // Bm = b A + c A A (A symmetric: its own transpose), into AA
+    gemm_lin_batched(d, false, nm, r, r, r, Am, nr, Am, nr, Am, AA, nr, b, c, s);
+    // a X + Bm X, into Y; Y is the next X
+    gemm_lin_batched(d, true, nm, r, k, r, AA, nr, X, n, X, Y, n, a, 1.0f, s);
+    std::swap(X, Y);
   }
   hipLaunchKernelGGL(gk::muon_apply_kernel<T>, dim3(per, nm), dim3(256), 0, s, params, X, tb, r,
                      k, 1.0f - lr * wd, lr);
