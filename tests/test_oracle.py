@@ -907,3 +907,85 @@ def test_optimizer_groups():
     assert g["lm_head"] == ("adamw", "lr_unembed")
     assert g["resid_lambdas"] == g["l1.veg"] == g["smear_gate"] == g["backout_lambda"] == \
         ("adamw", "lr_scalar")
+
+
+def test_optimizer_step_matches_torch_groups_and_muon_closed_form():
+    """The assembled MuonAdamW step (oracle.optim.optimizer_step) over three
+    steps on the small config with Smear and Backout, a schedule multiplier
+    0.7 and weight decay 0.28 (report, optimizer and schedule blocks):
+      * AdamW tensors equal torch.optim.AdamW run with one param group per
+        rate (embedding rate for wte and the value-embedding tables,
+        unembedding rate for lm_head, scalar rate for the rest), each rate
+        times the multiplier, and no weight decay;
+      * Muon tensors follow a closed form: every step's gradient is
+        U diag(s_t) V^T with fixed orthonormal U, V and s_t in [1, 3], so the
+        momentum buffer is mu buf + g and the Nesterov update u = g + mu buf
+        share U, V, and the orthogonalised update is exactly U V^T (cubic
+        Newton-Schulz, run to convergence); p <- p (1 - lr wd) - lr
+        sqrt(max(1, rows / cols)) U V^T.
+    Decay on an AdamW tensor, a dropped multiplier, a wrong rate key or a
+    wrong step counter each fail this test."""
+    cfg = W.get("tiny").with_(smear=True, backout=True)
+    names, total = oracle.param_offsets(cfg)
+    rng = np.random.default_rng(11)
+    p = rng.standard_normal(total) * 0.1
+    m = np.zeros(total)
+    v = np.zeros(total)
+    hp = dict(lr_mult=0.7, weight_decay=0.28, ns_a=1.5, ns_b=-0.5, ns_c=0.0, ns_steps=60,
+              momentum=0.9, nesterov=True, beta1=0.85, beta2=0.99, eps=1e-9)
+    d = dict(oracle.optim.DEFAULTS, **hp)
+    lay = {n: (o, shp) for n, (o, shp) in names.items()}
+    rate_key = {"wte": "lr_embed", "lm_head": "lr_unembed"}
+    muon, groups = [], {"lr_embed": [], "lr_unembed": [], "lr_scalar": []}
+    tparams = {}
+    for n, (o, shp) in lay.items():
+        leaf = n.split(".")[-1]
+        if leaf in ("q", "k", "v", "o", "fc", "mp"):
+            muon.append(n)
+            continue
+        key = "lr_embed" if leaf == "ve" else rate_key.get(n, "lr_scalar")
+        t = torch.tensor(p[o:o + int(np.prod(shp))].copy(), requires_grad=True)
+        tparams[n] = t
+        groups[key].append(t)
+    opt = torch.optim.AdamW([dict(params=ps, lr=d[k] * 0.7) for k, ps in groups.items() if ps],
+                            betas=(0.85, 0.99), eps=1e-9, weight_decay=0.0)
+    # fixed singular vectors per Muon matrix
+    UV = {}
+    for n in muon:
+        o, (r, c) = lay[n]
+        k = min(r, c)
+        U, _ = np.linalg.qr(rng.standard_normal((r, k)))
+        V, _ = np.linalg.qr(rng.standard_normal((c, k)))
+        UV[n] = (U, V, k)
+    want = {n: p[lay[n][0]:lay[n][0] + int(np.prod(lay[n][1]))].reshape(lay[n][1]).copy()
+            for n in muon}
+    want_buf = {n: np.zeros(lay[n][1]) for n in muon}
+    lr_m = d["lr_matrix"] * 0.7
+    for t in range(1, 4):
+        g = rng.standard_normal(total) * 0.01
+        for n in muon:
+            o, shp = lay[n]
+            U, V, k = UV[n]
+            G = U @ np.diag(rng.uniform(1.0, 3.0, k)) @ V.T
+            g[o:o + G.size] = G.ravel()
+            want_buf[n] = 0.9 * want_buf[n] + G
+            scale = max(1.0, shp[0] / shp[1]) ** 0.5
+            want[n] = want[n] * (1 - lr_m * 0.28) - lr_m * scale * (U @ V.T)
+        oracle.optim.optimizer_step(cfg, p, g, m, v, t, **hp)
+        for n, tp in tparams.items():
+            o = lay[n][0]
+            tp.grad = torch.from_numpy(g[o:o + tp.numel()].copy())
+        opt.step()
+    for n, tp in tparams.items():
+        o = lay[n][0]
+        sl = slice(o, o + tp.numel())
+        np.testing.assert_allclose(p[sl], tp.detach().numpy(), rtol=1e-11, atol=1e-12, err_msg=n)
+        st = opt.state[tp]
+        np.testing.assert_allclose(m[sl], st["exp_avg"].numpy(), rtol=1e-11, atol=1e-14, err_msg=n)
+        np.testing.assert_allclose(v[sl], st["exp_avg_sq"].numpy(), rtol=1e-11, atol=1e-16,
+                                   err_msg=n)
+    for n in muon:
+        o, shp = lay[n]
+        sl = slice(o, o + int(np.prod(shp)))
+        np.testing.assert_allclose(p[sl].reshape(shp), want[n], atol=1e-9, err_msg=n)
+        np.testing.assert_allclose(m[sl].reshape(shp), want_buf[n], atol=1e-12, err_msg=n)
