@@ -616,6 +616,14 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
   const int splits = K > 0 && kchunk > 0 ? (int)((K + kchunk - 1) / kchunk) : 1;
   // padded to a multiple of 8: see the kernel's tile order; y: batch entries
   dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8), (unsigned)batch);
+  if constexpr (BM == 256 && AK && BKM && !PA::kActive && !PB::kActive) {
+    if (K % 64 == 0 && (splits == 1 || kchunk % 64 == 0)) {
+      hipLaunchKernelGGL((gemm_kmaj_kernel<BN, EP>), grid, dim3(512), 0, s,
+                         static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M, N,
+                         K, splits == 1 ? K : kchunk, tm, tn, ep, sA, sB);
+      return;
+    }
+  }
   constexpr int NW = BM == 256 ? 8 : 4;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq, NW>), grid,
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(A), lda,

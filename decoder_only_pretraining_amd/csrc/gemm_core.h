@@ -585,4 +585,235 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
     epilogue(std::false_type{});
 }
 
+
+// ---------------------------------------------------------------- K-major bf16 products
+// Both operands K-major, bf16, K and the K chunk multiples of 64: 256-row
+// tiles, 8 wavefronts in a 4 x 2 grid (wavefront tile 64 x BN/2), two LDS
+// stages of 64-deep slabs filled straight from global memory.
+//
+// Schedule of one stage (four 16-wide slices). The fragments of slice s + 1
+// are read while the MFMAs of slice s run. Before the last slice every
+// wavefront waits for its own fills of the next stage and its own reads of
+// this stage, then the workgroup synchronises: the next stage is now
+// readable and this stage's buffer is free, so the fills of the stage after
+// next are issued into it at once, and the last slice's MFMAs (whose
+// fragments are already in registers) overlap the reads of the next
+// stage's first slice. The barrier thus falls where every wavefront still
+// has a whole slice of MFMAs queued, not at a point where all of them would
+// first have to read LDS.
+//
+// The MFMA takes the B fragment as its first operand, so an accumulator
+// block holds C^T: lane l owns row m = l % 32 and the four consecutive
+// columns n = 8 (e / 4) + 4 (l / 32) + e % 4, e = 4g .. 4g + 3. The epilogue
+// stages them with one 16-byte LDS write per group.
+template <int ROWS>
+struct KmajFill {
+  static constexpr int CHUNKS = ROWS * 128 / 1024;  // 1 KiB LDS chunks of a stage
+  static constexpr int NJ = CHUNKS / 8;             // per wavefront (8 wavefronts)
+  static_assert(CHUNKS % 8 == 0, "whole chunks per wavefront");
+  uint32_t off[NJ];
+  // byte offset of each of this lane's slots from the tile origin (row mn0,
+  // column k0); rows past MN read row MN - 1 (their products are never stored)
+  __device__ __forceinline__ void init(int64_t ld, int64_t mn0, int64_t MN, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int o = (wave + 8 * q) * 1024 + lane * 16;
+      const int r = o / 128, pg = (o % 128) / 16;
+      const int g = pg ^ ((r / 2) & 7);
+      const int64_t mn = min(mn0 + r, MN - 1);
+      off[q] = (uint32_t)(((mn - mn0) * ld + g * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16* tile, uint32_t lds, int wave) const {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) lds_fill16(tile, off[q], lds + (wave + 8 * q) * 1024);
+  }
+};
+
+template <int BN, class EP>
+__global__ __launch_bounds__(512) void gemm_kmaj_kernel(
+    const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
+    int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, EP ep_in, int64_t bsA,
+    int64_t bsB) {
+  constexpr int BM = 256, NW = 8, KS = 4;
+  constexpr int WM = BM / 4, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int AEL = BM * 64, BEL = BN * 64;  // elements per stage
+  constexpr int SP = WN + 4;                   // epilogue staging row pitch (floats)
+  constexpr int MAIN_BYTES = 2 * (AEL + BEL) * 2;
+  constexpr int STAGE_BYTES = NW * 32 * SP * 4;
+  __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES];
+  const bf16* As = reinterpret_cast<const bf16*>(smem);
+  const bf16* Bs = reinterpret_cast<const bf16*>(smem + 2 * AEL * 2);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, hi = lane >> 5;
+
+  // tile order as in gemm_bf16_kernel: split-major, XCD-contiguous, groups
+  // of 8 tile rows
+  const int ntiles = tiles_m * tiles_n;
+  const int nwork = ntiles * (int)((K + kchunk - 1) / kchunk);
+  int pid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (pid >= nwork) return;
+  const int split = pid / ntiles;
+  pid -= split * ntiles;
+  A += (int64_t)blockIdx.y * bsA;
+  B += (int64_t)blockIdx.y * bsB;
+  const EP ep = ep_in.at_split(split).at_batch((int)blockIdx.y);
+  constexpr int GM = 8;
+  const int group = pid / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % (GM * tiles_n)) % gsize;
+  const int tn = (pid % (GM * tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t k_lo = (int64_t)split * kchunk;
+  const int nk = (int)((min(K, k_lo + kchunk) - k_lo) / 64);
+
+  KmajFill<BM> fa;
+  KmajFill<BN> fb;
+  fa.init(lda, m0, M, wave, lane);
+  fb.init(ldb, n0, N, wave, lane);
+  const bf16* Ab = A + m0 * lda + k_lo;
+  const bf16* Bb = B + n0 * ldb + k_lo;
+  const uint32_t la = lds_addr(As), lb = lds_addr(Bs);
+  auto fill = [&](int kt, int buf) {
+    fa.issue(Ab + (int64_t)kt * 64, la + buf * AEL * 2, wave);
+    fb.issue(Bb + (int64_t)kt * 64, lb + buf * BEL * 2, wave);
+  };
+  auto kswz = [](int r, int g) { return r * 64 + ((g ^ ((r >> 1) & 7)) << 3); };
+  auto fragA = [&](Frag<bf16>& f, int buf, int i, int ks) {
+    f.v = *reinterpret_cast<const bf16x8*>(As + buf * AEL + kswz(wm * WM + i * 32 + r32, 2 * ks + hi));
+  };
+  auto fragB = [&](Frag<bf16>& f, int buf, int j, int ks) {
+    f.v = *reinterpret_cast<const bf16x8*>(Bs + buf * BEL + kswz(wn * WN + j * 32 + r32, 2 * ks + hi));
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  if (nk > 0) {
+    fill(0, 0);
+    if (nk > 1) {
+      fill(1, 1);
+      // vmcnt(fills of one stage): this wavefront's fills of stage 0 landed
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (KmajFill<BM>::NJ + KmajFill<BN>::NJ));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+    }
+  }
+  __syncthreads();
+  Frag<bf16> a[2][TM], b[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fragA(a[0][i], 0, i, 0);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fragB(b[0][j], 0, j, 0);
+  constexpr int NR = TM + TN, NM = TM * TN;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int p = ks & 1;
+      if (ks == KS - 1) {
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        __syncthreads();
+        if (kt + 2 < nk) fill(kt + 2, cur);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[p][j].v, a[p][i].v, acc[i][j], 0, 0, 0);
+      // the next slice: of this stage, or the next stage's first (after the
+      // last stage these reads are stale and unused)
+      const int rb = ks + 1 < KS ? cur : cur ^ 1, rs = ks + 1 < KS ? ks + 1 : 0;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fragA(a[p ^ 1][i], rb, i, rs);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fragB(b[p ^ 1][j], rb, j, rs);
+      interleave_mfma_ds<0, NR, NM / NR, NM % NR>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __syncthreads();                     // the stage buffers become the epilogue's staging area
+
+  // Epilogue, one 32-row slab of the wavefront tile at a time (see
+  // gemm_bf16_kernel): transform, stage in LDS as fp32, write back in
+  // 4-column vectors; operand-reading epilogues load a slab of the operand
+  // ahead of its stores.
+  const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SP;
+  constexpr bool kAux = !std::is_same<typename EP::Aux, NoAux>::value;
+  constexpr int NVS = 32 * WN / 4 / 64;
+  constexpr int NCH = 2, CV = NVS / NCH;
+  static_assert(NVS % NCH == 0, "value chunks must tile the slab");
+  using AuxT = typename EP::Aux;
+  auto epilogue = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    auto in_range = [&](int64_t m, int64_t n) { return FULL || (m < M && n < N); };
+    auto count = [&](int64_t n) { return FULL ? 4 : (int)min<int64_t>(4, N - n); };
+    AuxT ax[kAux ? NVS : 1];
+    auto load_aux = [&](int i) {
+#pragma unroll
+      for (int t = 0; t < NVS; ++t) {
+        const int v = lane + 64 * t;
+        const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+        const int64_t m = mw + i * 32 + r, n = nw + c4;
+        if (in_range(m, n)) ax[t] = ep.aux(m, n, count(n));
+      }
+    };
+    if constexpr (kAux) load_aux(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = mw + i * 32 + r32;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = j * 32 + 8 * g + 4 * hi;
+          f32x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = ep.value(m, nw + nl + t, acc[i][j][4 * g + t]);
+          *reinterpret_cast<f32x4*>(stage + r32 * SP + nl) = v;
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        f32x4 val[CV];
+#pragma unroll
+        for (int t = 0; t < CV; ++t) {
+          const int v = lane + 64 * (c * CV + t);
+          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+          val[t] = *reinterpret_cast<const f32x4*>(stage + r * SP + c4);
+        }
+#pragma unroll
+        for (int t = 0; t < CV; ++t) {
+          const int v = lane + 64 * (c * CV + t);
+          const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
+          const int64_t mm = mw + i * 32 + r, n = nw + c4;
+          if (in_range(mm, n)) {
+            if constexpr (kAux) ep.store4a(mm, n, val[t], count(n), ax[c * CV + t]);
+            else ep.store4(mm, n, val[t], count(n));
+          }
+        }
+      }
+      if constexpr (kAux)
+        if (i + 1 < TM) load_aux(i + 1);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  if (m0 + BM <= M && n0 + BN <= N)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
+}
+
 }  // namespace gk
