@@ -13,22 +13,26 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgptstep.so")
 
-GPT_ABI_VERSION = 1
+GPT_ABI_VERSION = 2
 GPT_DT_F32, GPT_DT_BF16 = 0, 1
 GPT_F_ACCUMULATE = 1
-GPT_F_SMEAR = 2
-GPT_F_BACKOUT = 4
-GPT_F_REUSE_WEIGHTS = 8
+GPT_F_EMBED_NORM = 2
+GPT_F_CHECK_FINITE = 4
+GPT_F_CHECK_INPUTS = 8
+GPT_F_SMEAR = 16
+GPT_F_BACKOUT = 32
+GPT_F_REUSE_WEIGHTS = 64
 
 STATUS = {0: "GPT_OK", -1: "GPT_E_INVAL", -2: "GPT_E_NULLPTR", -3: "GPT_E_ALIGN",
-          -4: "GPT_E_WORKSPACE", -5: "GPT_E_UNSUPPORTED", -6: "GPT_E_HIP"}
+          -4: "GPT_E_WORKSPACE", -5: "GPT_E_UNSUPPORTED", -6: "GPT_E_HIP",
+          -7: "GPT_E_NONFINITE"}
 
 EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_param_info",
            "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region", "gpt_fwd_bwd",
            "gpt_fwd", "gpt_fp8_quantize", "gpt_status_string", "gpt_last_error",
            "gpt_profile_begin", "gpt_profile_end", "gpt_decode_attn_workspace",
            "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
-           "gpt_optimizer_step"]
+           "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -93,6 +97,8 @@ def lib():
         L.gpt_optim_workspace_size.argtypes = [P(GptConfig), P(c.c_size_t)]
         L.gpt_optimizer_step.argtypes = [P(GptConfig), P(OptimHparams)] + [c.c_void_p] * 4 + [
             c.c_size_t, c.c_void_p]
+        L.gpt_debug_launches.argtypes = [c.c_int64, c.c_int32]
+        L.gpt_debug_launch_count.argtypes = [P(c.c_int64)]
         L.gpt_status_string.restype = c.c_char_p
         L.gpt_status_string.argtypes = [c.c_int]
         L.gpt_last_error.restype = c.c_char_p
@@ -104,7 +110,7 @@ def lib():
                      "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region",
                      "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize", "gpt_decode_attn_workspace",
                      "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
-                     "gpt_optimizer_step"):
+                     "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -263,6 +269,20 @@ def optimizer_step(cfg, hp: OptimHparams, params, grads, state, workspace, strea
                                   workspace.numel() * workspace.element_size(),
                                   _stream_ptr(stream))
     _check("gpt_optimizer_step", st)
+
+
+def debug_launches(fail_at: int = -1, dry_run: bool = False):
+    """Fault injection / dry run of the calling thread's later calls
+    (gpt_debug_launches): launch number `fail_at` fails (< 0: none);
+    dry_run counts the launch sequence without launching."""
+    _check("gpt_debug_launches", lib().gpt_debug_launches(fail_at, 1 if dry_run else 0))
+
+
+def debug_launch_count() -> int:
+    """Launches issued (or counted) by the thread's last entry-point call."""
+    n = ctypes.c_int64()
+    _check("gpt_debug_launch_count", lib().gpt_debug_launch_count(ctypes.byref(n)))
+    return n.value
 
 
 def profile_begin(site_prefix: str):

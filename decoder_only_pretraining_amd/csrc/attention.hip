@@ -1244,16 +1244,16 @@ void fwd(const gpt::Dims& d, bool full, const void* qkv, void* out, float* lse, 
   if constexpr (sizeof(T) == 2) {
     const int nq = (d.T + 255) / 256;
     if (d.T % 64 == 0)
-      hipLaunchKernelGGL((attn_fwd_tiled_kernel<D, true>), dim3((unsigned)(nq * d.H * d.B)),
+      GK_LAUNCH((attn_fwd_tiled_kernel<D, true>), dim3((unsigned)(nq * d.H * d.B)),
                          dim3(512), 0, s, static_cast<const bf16*>(qkv), static_cast<bf16*>(out),
                          lse, d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2, nq, d.B);
     else
-      hipLaunchKernelGGL((attn_fwd_tiled_kernel<D, false>), dim3((unsigned)(nq * d.H * d.B)),
+      GK_LAUNCH((attn_fwd_tiled_kernel<D, false>), dim3((unsigned)(nq * d.H * d.B)),
                          dim3(512), 0, s, static_cast<const bf16*>(qkv), static_cast<bf16*>(out),
                          lse, d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2, nq, d.B);
   } else {
     dim3 grid((unsigned)((d.T + 127) / 128), d.H, d.B);
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(qkv),
+    GK_LAUNCH((attn_fwd_kernel<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(qkv),
                        static_cast<T*>(out), lse, d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2);
   }
 }
@@ -1270,11 +1270,11 @@ void bwd(const gpt::Dims& d, bool full, const void* qkv, const void* gO, const f
     constexpr int NW = 4;
     const int nkt = (d.T + 32 * NW - 1) / (32 * NW), nq = (d.T + 32 * NW - 1) / (32 * NW);
 #define GPT_ATTN_BWD(AL)                                                                          \
-  hipLaunchKernelGGL((attn_bwd_kv_tiled_kernel<D, NW, AL>), dim3((unsigned)(nkt * d.Hk * d.B)),    \
+  GK_LAUNCH((attn_bwd_kv_tiled_kernel<D, NW, AL>), dim3((unsigned)(nkt * d.Hk * d.B)),    \
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),                           \
                      static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H, \
                      d.Hk, d.W, full ? 1 : 0, c2, scale, nkt, d.B);                                \
-  hipLaunchKernelGGL((attn_bwd_q_tiled_kernel<D, NW, AL, AL ? 2 : 3>), dim3((unsigned)(nq * d.H * d.B)), \
+  GK_LAUNCH((attn_bwd_q_tiled_kernel<D, NW, AL, AL ? 2 : 3>), dim3((unsigned)(nq * d.H * d.B)), \
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),                           \
                      static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H, \
                      d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B)
@@ -1287,11 +1287,11 @@ void bwd(const gpt::Dims& d, bool full, const void* qkv, const void* gO, const f
     return;
   }
   dim3 gkv((unsigned)((d.T + 127) / 128), d.Hk, d.B);
-  hipLaunchKernelGGL((attn_bwd_kv_kernel<T, D>), gkv, dim3(256), 0, s, static_cast<const T*>(qkv),
+  GK_LAUNCH((attn_bwd_kv_kernel<T, D>), gkv, dim3(256), 0, s, static_cast<const T*>(qkv),
                      static_cast<const T*>(gO), lse, delta, static_cast<T*>(gqkv), d.T, d.H, d.Hk,
                      d.W, full ? 1 : 0, c2, scale);
   dim3 gq((unsigned)((d.T + 127) / 128), d.H, d.B);
-  hipLaunchKernelGGL((attn_bwd_q_kernel<T, D>), gq, dim3(256), 0, s, static_cast<const T*>(qkv),
+  GK_LAUNCH((attn_bwd_q_kernel<T, D>), gq, dim3(256), 0, s, static_cast<const T*>(qkv),
                      static_cast<const T*>(gO), lse, delta, static_cast<T*>(gqkv), d.T, d.H, d.Hk,
                      d.W, full ? 1 : 0, c2, scale);
 }
@@ -1317,7 +1317,7 @@ void launch_attn_delta(const Dims& d, const void* gO, const void* O, float* delt
   const int per = 256 / (d.D / 8);
   dim3 grid((unsigned)((NH + per - 1) / per));
 #define GPT_DELTA(TY, DD)                                                                         \
-  hipLaunchKernelGGL((attn_delta_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<const TY*>(gO), \
+  GK_LAUNCH((attn_delta_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<const TY*>(gO), \
                      static_cast<const TY*>(O), delta, NH, d.H, d.T)
   if (d.bf16) {
     if (d.D == 128) GPT_DELTA(bf16, 128);

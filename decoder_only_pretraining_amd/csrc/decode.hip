@@ -238,7 +238,7 @@ void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const
   bf16* op = static_cast<bf16*>(out);
   float* part = static_cast<float*>(workspace);
 #define DEC_P(DD, GG)                                                                        \
-  hipLaunchKernelGGL((gk::decode_attn_kernel<DD, GG>), grid, dim3(gk::kDecWaves * 64), 0, s,     \
+  GK_LAUNCH((gk::decode_attn_kernel<DD, GG>), grid, dim3(gk::kDecWaves * 64), 0, s,     \
                      qp, kp, vp, seqlen, part, op, H, Hk, Tmax, window, S, chunk)
 #define DEC_G(DD)                      \
   switch (G) {                         \
@@ -254,12 +254,12 @@ void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const
   if (D == 128) {
     DEC_G(128);
     if (S > 1)
-      hipLaunchKernelGGL(gk::decode_attn_combine_kernel<128>, dim3((unsigned)(B * H)), dim3(128),
+      GK_LAUNCH(gk::decode_attn_combine_kernel<128>, dim3((unsigned)(B * H)), dim3(128),
                          0, s, part, op, S);
   } else {
     DEC_G(64);
     if (S > 1)
-      hipLaunchKernelGGL(gk::decode_attn_combine_kernel<64>, dim3((unsigned)(B * H)), dim3(64), 0,
+      GK_LAUNCH(gk::decode_attn_combine_kernel<64>, dim3((unsigned)(B * H)), dim3(64), 0,
                          s, part, op, S);
   }
 #undef DEC_G
@@ -270,7 +270,7 @@ void launch_kv_cache_append(int B, int n_new, int H, int Hk, int D, int Tmax, co
                             const int32_t* pos, void* k, void* v, hipStream_t s) {
   const int64_t total = (int64_t)B * n_new * 2 * Hk * (D / 8);
   const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL(gk::kv_cache_append_kernel, dim3(blocks), dim3(256), 0, s,
+  GK_LAUNCH(gk::kv_cache_append_kernel, dim3(blocks), dim3(256), 0, s,
                      static_cast<const bf16*>(qkv), pos, static_cast<bf16*>(k),
                      static_cast<bf16*>(v), B, n_new, H, Hk, D, Tmax);
 }

@@ -168,10 +168,10 @@ void launch_fp8_amax(const void* x, bool bf16_src, int64_t n, int64_t period, co
   const int64_t nv = n / 8;
   const unsigned blocks = (unsigned)std::min<int64_t>((nv + 255) / 256, 1024);
   if (bf16_src)
-    hipLaunchKernelGGL(fp8_amax_kernel<bf16>, dim3(blocks), dim3(256), 0, s,
+    GK_LAUNCH(fp8_amax_kernel<bf16>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const bf16*>(x), nv, period, sg, amax);
   else
-    hipLaunchKernelGGL(fp8_amax_kernel<float>, dim3(blocks), dim3(256), 0, s,
+    GK_LAUNCH(fp8_amax_kernel<float>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const float*>(x), nv, period, sg, amax);
 }
 
@@ -183,7 +183,7 @@ void launch_fp8_quant(const void* src, bool bf16_src, int64_t R, int64_t C, bool
   dim3 grid((unsigned)(C / 64), (unsigned)((rows + 127) / 128));
   const float fm = fmax_of(fmt);
 #define GPT_QUANT(T, F)                                                                        \
-  hipLaunchKernelGGL((fp8_quant_kernel<T, F>), grid, dim3(256), 0, s, static_cast<const T*>(src), \
+  GK_LAUNCH((fp8_quant_kernel<T, F>), grid, dim3(256), 0, s, static_cast<const T*>(src), \
                      R, C, seg_rows ? 1 : 0, sg, amax, fm, out, outT, pitchT)
   if (bf16_src) {
     if (fmt == FP8_E4M3) GPT_QUANT(bf16, FP8_E4M3);

@@ -474,7 +474,7 @@ void run_f32(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, 
              int64_t K, PA pa, PB pb, EP ep, hipStream_t s) {
   constexpr int BM = 128, BN = 128, BK = 16;
   dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
+  GK_LAUNCH((gemm_kernel<T, BM, BN, BK, AK, BKM, PA, PB, EP>), grid, dim3(256), 0, s,
                      static_cast<const T*>(A), lda, static_cast<const T*>(B), ldb, M, N, K, pa,
                      pb, ep);
 }
@@ -592,18 +592,19 @@ static void splitk_reduce(const float* part, int64_t splits, int64_t M, int64_t 
                           bool accumulate, hipStream_t s) {
   const int64_t n4 = M * N / 4;  // N is a multiple of 64
   const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, splits, n4, C,
+  GK_LAUNCH(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, splits, n4, C,
                      accumulate ? 1 : 0);
 }
 
-// The partial region is sized by the plan from the *_part_bytes functions;
-// a call that needs more is a planning bug.
-static void check_part(int64_t need, int64_t cap) {
-  if (need > cap) {
-    std::fprintf(stderr, "gptstep: split-K partials need %lld bytes, plan holds %lld\n",
-                 (long long)need, (long long)cap);
-    std::abort();
-  }
+// The partial region is sized by the plan from the *_part_bytes functions
+// (and the entry point checks that before enqueueing anything); a product
+// that would still need more is not launched: the call's launch state
+// records an error, so no later launch is enqueued and the entry point
+// returns GPT_E_HIP.
+static bool check_part(int64_t need, int64_t cap) {
+  if (need <= cap) return true;
+  ::gpt::launch_state().err = hipErrorInvalidValue;
+  return false;
 }
 
 // Products with 256-row tiles run 8 wavefronts per workgroup (two per SIMD,
@@ -618,14 +619,14 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
   dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8), (unsigned)batch);
   if constexpr (BM == 256 && AK && BKM && !PA::kActive && !PB::kActive) {
     if (K % 64 == 0 && (splits == 1 || kchunk % 64 == 0)) {
-      hipLaunchKernelGGL((gemm_kmaj_kernel<BN, EP>), grid, dim3(512), 0, s,
+      GK_LAUNCH((gemm_kmaj_kernel<BN, EP>), grid, dim3(512), 0, s,
                          static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M, N,
                          K, splits == 1 ? K : kchunk, tm, tn, ep, sA, sB);
       return;
     }
   }
   constexpr int NW = BM == 256 ? 8 : 4;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq, NW>), grid,
+  GK_LAUNCH((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq, NW>), grid,
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(A), lda,
                      static_cast<const bf16*>(B), ldb, M, N, K, kchunk, tm, tn, pa, pb, ep, NoDeq{},
                      sA, sB);
@@ -665,7 +666,7 @@ void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int
   const int64_t Kp = K / 2, kc = kchunk / 2;
   const int splits = Kp > 0 && kc > 0 ? (int)((Kp + kc - 1) / kc) : 1;
   dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8));  // padded: see the kernel's tile order
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 64, true, true, MODE, PreId, PreId, EP, Deq8>), grid,
+  GK_LAUNCH((gemm_bf16_kernel<BM, BN, 64, true, true, MODE, PreId, PreId, EP, Deq8>), grid,
                      dim3(256), 0, s, reinterpret_cast<const bf16*>(A), lda / 2,
                      reinterpret_cast<const bf16*>(B), ldb / 2, M, N, Kp, kc, tm, tn, PreId{},
                      PreId{}, ep, dq, (int64_t)0, (int64_t)0);
@@ -766,7 +767,7 @@ SplitSum gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t 
     run_f8<2>(t, A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0), q, s);
     return SplitSum{};
   }
-  check_part(part_bytes_f8_wgrad(M, N, K), part_cap);
+  if (!check_part(part_bytes_f8_wgrad(M, N, K), part_cap)) return SplitSum{};
   run_f8<2>(t, A, lda, B, ldb, M, N, K, ks.chunk, mk_part(part, M, N), q, s);
   return SplitSum{part, ks.splits, M, N, C, accumulate};
 }
@@ -864,7 +865,7 @@ SplitSum gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* 
     const Tile t = pick_tile_bf16(M, N, K);
     const KSplit ks = nn_split(M, N, K);
     const int64_t chunk = ks.splits == 1 ? K : ks.chunk;
-    if (ks.splits > 1) check_part(part_bytes_nn_splitk(d, M, N, K), part_cap);
+    if (ks.splits > 1 && !check_part(part_bytes_nn_splitk(d, M, N, K), part_cap)) return SplitSum{};
     if (Bt) {
       if (ks.splits == 1)
         run_bf16<true, true>(t, A, K, Bt, K, M, N, K, chunk, PreId{}, PreId{}, mk_f32(C, N, 0), s);
@@ -905,7 +906,7 @@ SplitSum gemm_tn_wgrad(const Dims& d, int M, int N, int64_t K, const void* A, co
                              mk_f32(C, N, accumulate ? 1 : 0), s);
       return SplitSum{};
     }
-    check_part(part_bytes_tn_wgrad(d, M, N, K), part_cap);
+    if (!check_part(part_bytes_tn_wgrad(d, M, N, K), part_cap)) return SplitSum{};
     run_bf16<false, false>(t, A, M, B, N, M, N, K, ks.chunk, PreId{}, PreId{},
                            mk_part(part, M, N), s);
     return SplitSum{part, ks.splits, M, N, C, accumulate};

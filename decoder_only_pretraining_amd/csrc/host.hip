@@ -23,6 +23,41 @@ static int fail(int status, const char* fmt, ...) {
   return status;
 }
 
+// ---------------------------------------------------------------- launches
+static thread_local LaunchState g_launch;
+LaunchState& launch_state() { return g_launch; }
+void launch_reset() {
+  g_launch.err = hipSuccess;
+  g_launch.injected = false;
+  g_launch.issued = 0;
+  if (!g_launch.dry) (void)hipGetLastError();  // drop an error left by earlier work
+}
+bool launch_begin() {
+  LaunchState& st = g_launch;
+  if (st.err != hipSuccess) return false;
+  if (st.fail_at >= 0 && st.issued == st.fail_at) {
+    st.err = hipErrorLaunchFailure;
+    st.injected = true;
+    return false;
+  }
+  ++st.issued;
+  return !st.dry;
+}
+void launch_end() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess && g_launch.err == hipSuccess) g_launch.err = e;
+}
+// status of the current call's launches: GPT_OK or GPT_E_HIP with the detail
+static int launch_status() {
+  const LaunchState& st = g_launch;
+  if (st.err == hipSuccess) return GPT_OK;
+  if (st.injected)
+    return fail(GPT_E_HIP, "HIP: injected launch failure at launch %lld (nothing later enqueued)",
+                (long long)st.issued);
+  return fail(GPT_E_HIP, "HIP: %s at launch %lld (nothing later enqueued)", hipGetErrorString(st.err),
+              (long long)st.issued);
+}
+
 // ---------------------------------------------------------------- profiling
 // When enabled, every launch whose site name starts with the chosen prefix is
 // bracketed by two HIP events recorded on the launch stream. Events come from
@@ -107,6 +142,8 @@ Dims make_dims(const gpt_config& c) {
   d.backout = (c.flags & GPT_F_BACKOUT) != 0;
   d.mid = d.L / 2;
   d.reuse_weights = (c.flags & GPT_F_REUSE_WEIGHTS) != 0;
+  d.check_finite = (c.flags & GPT_F_CHECK_FINITE) != 0;
+  d.check_inputs = (c.flags & GPT_F_CHECK_INPUTS) != 0;
   return d;
 }
 
@@ -134,7 +171,8 @@ static int validate(const gpt_config* c) {
   if (c->compute_dtype != GPT_DT_F32 && c->compute_dtype != GPT_DT_BF16)
     return fail(GPT_E_INVAL, "compute_dtype %d unknown", c->compute_dtype);
   if (c->fp8_linears != 0 && c->fp8_linears != 1) return fail(GPT_E_INVAL, "fp8_linears must be 0 or 1");
-  if (c->flags & ~(GPT_F_ACCUMULATE | GPT_F_SMEAR | GPT_F_BACKOUT | GPT_F_REUSE_WEIGHTS))
+  if (c->flags & ~(GPT_F_ACCUMULATE | GPT_F_EMBED_NORM | GPT_F_CHECK_FINITE | GPT_F_CHECK_INPUTS |
+                   GPT_F_SMEAR | GPT_F_BACKOUT | GPT_F_REUSE_WEIGHTS))
     return fail(GPT_E_INVAL, "unknown flag bits 0x%x", c->flags);
   if (!(std::isfinite(c->rope_theta) && c->rope_theta > 1.0f))
     return fail(GPT_E_INVAL, "rope_theta must be finite and > 1");
@@ -142,6 +180,8 @@ static int validate(const gpt_config* c) {
   if (!(std::isfinite(c->softcap) && c->softcap > 0.0f)) return fail(GPT_E_INVAL, "softcap must be > 0");
   if (c->fp8_linears && c->compute_dtype != GPT_DT_BF16)
     return fail(GPT_E_INVAL, "fp8 linears need bf16 compute");
+  if (c->flags & GPT_F_EMBED_NORM)
+    return fail(GPT_E_UNSUPPORTED, "GPT_F_EMBED_NORM: no embedding norm is built into this library");
   return GPT_OK;
 }
 
@@ -333,10 +373,47 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   if (workspace_bytes < P.total)
     return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, P.total);
   const Offs F = offsets(*cfg);
+  // the split-K partial region holds every split product of the step (a
+  // shortfall would be a planning error of this library)
+  {
+    int64_t need = std::max(part_bytes_nn_splitk(d, d.N, d.C, d.V), part_bytes_tn_wgrad(d, d.V, d.C, d.N));
+    const int64_t shapes[4][2] = {{d.Qkv, d.C}, {d.C, d.Cq}, {d.F, d.C}, {d.C, d.F}};
+    for (const auto& mn : shapes) {
+      need = std::max(need, part_bytes_tn_wgrad(d, mn[0], mn[1], d.N));
+      if (d.fp8) need = std::max(need, part_bytes_f8_wgrad(mn[0], mn[1], (d.N + 15) / 16 * 16));
+    }
+    if (need > P.part_bytes)
+      return fail(GPT_E_WORKSPACE, "internal: split-K partials need %lld bytes, the plan holds %lld",
+                  (long long)need, (long long)P.part_bytes);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  launch_reset();
 
   char* W = static_cast<char*>(workspace);
+  // debug flags in the scalars region: [8], [9] id checks, [10] finiteness
+  uint32_t* dbg = reinterpret_cast<uint32_t*>(W + P.scalars) + 8;
+  // device values of the debug checks, after an internal synchronisation
+  auto read_flags = [&](uint32_t* host, const uint32_t* dev, int n) -> int {
+    if (launch_state().dry) {
+      for (int i = 0; i < n; ++i) host[i] = 0;
+      return GPT_OK;
+    }
+    int st2 = launch_status();
+    if (st2) return st2;
+    hipError_t e = hipMemcpyAsync(host, dev, n * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s (debug check)", hipGetErrorString(e));
+    return GPT_OK;
+  };
+  if (d.check_inputs) {
+    launch_check_ids(tokens, targets, d.N, d.V, dbg, s);
+    uint32_t bad[2];
+    const int st2 = read_flags(bad, dbg, 2);
+    if (st2) return st2;
+    if (bad[0] || bad[1])
+      return fail(GPT_E_INVAL, "%u token ids outside [0, %d), %u targets outside [-1, %d)", bad[0],
+                  d.V, bad[1], d.V);
+  }
   const size_t A = (size_t)d.act_bytes;
   // compute-dtype weights: a mirror of params with the same element offsets
   const char* wc = d.bf16 ? W + P.wc : reinterpret_cast<const char*>(params);
@@ -471,7 +548,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     if (d.smear)
       launch_smear_embed(d, params + F.wte, tokens, params + F.sm, X(0), sgate, s);
     else
-      launch_embed(params + F.wte, tokens, X(0), N, d.C, s);
+      launch_embed(params + F.wte, tokens, X(0), N, d.C, d.V, s);
   });
   for (int l = 0; l < d.L; ++l) {
     const bool ve = layer_ve(l, d.L), full = layer_full(l, d.L);
@@ -670,7 +747,7 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       site("attn.bwd", s, [&] { launch_attn_bwd(d, full, qkv, gO, lse, delta, gqkv, s); });
       launch_rope_qk_ve_bwd(d, gqkv, qkv, rqk, cs, a, ve ? params + F.ve[l] : nullptr,
                             ve ? vegrow : nullptr, ga, tokens, s);
-      if (ve) launch_rows_to_table(vegrow, d.Ckv, tokens, tlink, N, grads + F.ve[l], s);
+      if (ve) launch_rows_to_table(vegrow, d.Ckv, tokens, tlink, N, grads + F.ve[l], d.V, s);
       if (d.fp8) {
         const int g0 = slot(l, 13), g1 = slot(l, 14), g2 = slot(l, 15);
         site("fp8.quant", s, [&] {
@@ -721,9 +798,9 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         // its partials (smear_blocks(N) <= veg_splits rows of C) reuse veg_part
         launch_smear_bwd(d, gx0, params + F.wte, tokens, params + F.sm, sgate, gtmp, veg_part,
                          grads + F.sm, s);
-        launch_rows_to_table(gtmp, d.C, tokens, tlink, N, grads + F.wte, s);
+        launch_rows_to_table(gtmp, d.C, tokens, tlink, N, grads + F.wte, d.V, s);
       } else {
-        launch_rows_to_table(gx0, d.C, tokens, tlink, N, grads + F.wte, s);
+        launch_rows_to_table(gx0, d.C, tokens, tlink, N, grads + F.wte, d.V, s);
       }
     });
     // every layer's lambda gradients in one launch (layer l's partials at
@@ -734,9 +811,22 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
       launch_lambda_finalize(d, lam_part + (size_t)d.L * P.lam_blocks * 2, P.lam_blocks, nullptr,
                              grads + F.bo, s, 1, -1.0f);
   }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
-  return GPT_OK;
+  if (d.check_finite) {
+    launch_zero(reinterpret_cast<float*>(dbg + 2), 1, s);
+    launch_check_finite(loss, 1, dbg + 2, s);
+    if (backward) {
+      int64_t n_elems = 0;
+      for (const auto& t : param_layout(*cfg)) n_elems = std::max(n_elems, t.offset + t.rows * t.cols);
+      launch_check_finite(grads, n_elems, dbg + 2, s);
+    }
+    uint32_t bad = 0;
+    const int st2 = read_flags(&bad, dbg + 2, 1);
+    if (st2) return st2;
+    if (bad)
+      return fail(GPT_E_NONFINITE, backward ? "the loss or a gradient is NaN or infinite"
+                                            : "the loss is NaN or infinite");
+  }
+  return launch_status();
 }
 
 }  // namespace gpt
@@ -897,15 +987,13 @@ int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t c
       !aligned(amax, 4))
     return fail(GPT_E_ALIGN, "src, codes, codes_t need 16-byte alignment, amax 4");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  launch_reset();
   const bool bf = src_dtype == GPT_DT_BF16;
   const Segs sg = one_seg(0);
   launch_zero(reinterpret_cast<float*>(amax), 1, s);
   launch_fp8_amax(src, bf, rows * cols, rows * cols, sg, amax, s);
   launch_fp8_quant(src, bf, rows, cols, false, sg, amax, fmt, codes, codes_t, pitch_t, s);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
-  return GPT_OK;
+  return launch_status();
 }
 
 static int decode_validate(int32_t B, int32_t H, int32_t Hk, int32_t D, int32_t Tmax,
@@ -947,12 +1035,10 @@ int gpt_decode_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t he
   if (workspace_bytes < need)
     return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  launch_reset();
   launch_decode_attn(batch, n_head, n_kv_head, head_dim, max_len, window, q, k_cache, v_cache,
                      seqlen, out, workspace, s);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
-  return GPT_OK;
+  return launch_status();
 }
 
 int gpt_kv_cache_append(int32_t batch, int32_t n_new, int32_t n_head, int32_t n_kv_head,
@@ -967,12 +1053,10 @@ int gpt_kv_cache_append(int32_t batch, int32_t n_new, int32_t n_head, int32_t n_
   if (!aligned(qkv, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pos, 4))
     return fail(GPT_E_ALIGN, "qkv and caches need 16-byte alignment, pos 4");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  launch_reset();
   launch_kv_cache_append(batch, n_new, n_head, n_kv_head, head_dim, max_len, qkv, pos, k_cache,
                          v_cache, s);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
-  return GPT_OK;
+  return launch_status();
 }
 
 int gpt_optim_workspace_size(const gpt_config* cfg, size_t* bytes) {
@@ -1014,7 +1098,7 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
   float* m = state;
   float* v = state + n_elems;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  launch_reset();
   // Muon: the block matrices, batched by shape
   launch_muon_groups(d, muon_groups(*cfg), o, workspace, params, grads, m,
                      hp->lr_matrix * hp->lr_mult, hp->weight_decay, hp->momentum, hp->nesterov,
@@ -1032,9 +1116,7 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
     launch_adamw(params + t.offset, grads + t.offset, m + t.offset, v + t.offset,
                  t.rows * t.cols, lr * hp->lr_mult, hp->beta1, hp->beta2, hp->eps, hp->step, s);
   }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
-  return GPT_OK;
+  return launch_status();
 }
 
 const char* gpt_status_string(int status) {
@@ -1046,11 +1128,28 @@ const char* gpt_status_string(int status) {
     case GPT_E_WORKSPACE: return "workspace too small";
     case GPT_E_UNSUPPORTED: return "unsupported configuration";
     case GPT_E_HIP: return "HIP runtime error";
+    case GPT_E_NONFINITE: return "non-finite loss or gradient";
     default: return "unknown status";
   }
 }
 
 const char* gpt_last_error(void) { return g_err; }
+
+int gpt_debug_launches(int64_t fail_at, int32_t dry_run) {
+  g_err[0] = 0;
+  if (dry_run != 0 && dry_run != 1) return fail(GPT_E_INVAL, "dry_run must be 0 or 1");
+  LaunchState& st = launch_state();
+  st.fail_at = fail_at < 0 ? -1 : fail_at;
+  st.dry = dry_run != 0;
+  return GPT_OK;
+}
+
+int gpt_debug_launch_count(int64_t* issued) {
+  // a query: the last call's error text is left as it is
+  if (!issued) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  *issued = launch_state().issued;
+  return GPT_OK;
+}
 
 int gpt_profile_begin(const char* site_prefix) {
   g_err[0] = 0;

@@ -12,6 +12,38 @@
 
 namespace gpt {
 
+// ------------------------------------------------------------ launches
+// Every kernel launch of an entry point goes through GK_LAUNCH, which keeps
+// per-thread bookkeeping for the current call: the first launch error
+// (hipGetLastError right after the launch) is recorded and every later
+// launch of the call is skipped, so nothing is enqueued after a failure.
+// Test support (gpt_debug_launches): a launch index at which a failure is
+// injected instead of launching, and a dry run that counts the launch
+// sequence without launching anything.
+struct LaunchState {
+  hipError_t err = hipSuccess;  // first error of the current call
+  bool injected = false;        // err came from the fault-injection switch
+  int64_t issued = 0;           // launches issued (or counted, in a dry run)
+  int64_t fail_at = -1;         // inject a failure at this launch index (< 0: never)
+  bool dry = false;             // count launches, launch nothing
+};
+LaunchState& launch_state();
+// start of an entry point call: clears the error and the count
+void launch_reset();
+// before a launch: false if it must be skipped (earlier error, injected
+// failure, dry run)
+bool launch_begin();
+// after a launch: record hipGetLastError
+void launch_end();
+
+#define GK_LAUNCH(...)                      \
+  do {                                       \
+    if (::gpt::launch_begin()) {             \
+      hipLaunchKernelGGL(__VA_ARGS__);       \
+      ::gpt::launch_end();                   \
+    }                                        \
+  } while (0)
+
 struct Dims {
   int L, C, H, Hk, D, F, V, T, B, W;
   int64_t N;        // tokens per call = B * T
@@ -26,6 +58,8 @@ struct Dims {
   bool backout;     // Backout before the final norm (GPT_F_BACKOUT)
   int mid;          // Backout caches the stream entering this layer (L / 2)
   bool reuse_weights;  // GPT_F_REUSE_WEIGHTS: keep the workspace's bf16 weight mirrors
+  bool check_finite;   // GPT_F_CHECK_FINITE
+  bool check_inputs;   // GPT_F_CHECK_INPUTS
 };
 
 Dims make_dims(const gpt_config& c);
@@ -83,8 +117,16 @@ void launch_cast(const float* src, void* dst, const std::vector<CastSeg>& segs, 
 void launch_cast_t(const float* src, void* dst, void* dstT, const std::vector<int64_t>& offs,
                    int rows, int cols, hipStream_t s);
 void launch_zero(float* p, int64_t n, hipStream_t s);
+// Debug checks. check_ids: out[0] = number of token ids outside [0, V),
+// out[1] = number of targets outside [-1, V) (one workgroup; writes both).
+// check_finite: flag |= 1 if any of x[0 .. n) is NaN or infinite (flag must
+// be zero before the first call).
+void launch_check_ids(const int32_t* tok, const int32_t* tgt, int64_t N, int V, uint32_t* out,
+                      hipStream_t s);
+void launch_check_finite(const float* x, int64_t n, uint32_t* flag, hipStream_t s);
 void launch_rope_table(float* cs, int T, int D, float theta, hipStream_t s);
-void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C, hipStream_t s);
+void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C, int V,
+                  hipStream_t s);
 // Smear: x0[n] = e[n] + sigmoid(<e[n], w>) e[n-1] (t >= 1), e[n] = wte[tok[n]];
 // the gate values go to sig (fp32 [N], 0 at t = 0).
 void launch_smear_embed(const Dims& d, const float* wte, const int32_t* tok, const float* w,
@@ -119,7 +161,7 @@ void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const flo
 // the tokens.
 void launch_token_links(const int32_t* tok, int64_t N, int32_t* link, hipStream_t s);
 void launch_rows_to_table(const float* g, int W, const int32_t* tok, const int32_t* link,
-                          int64_t N, float* tab, hipStream_t s);
+                          int64_t N, float* tab, int V, hipStream_t s);
 
 void launch_attn_fwd(const Dims& d, bool full, const void* qkv, void* out, float* lse,
                      hipStream_t s);

@@ -242,10 +242,10 @@ void launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float
   const float c1 = 1.0f - std::pow(b1, (float)step), c2 = 1.0f - std::pow(b2, (float)step);
   const bool vec = n % 4 == 0 && ((uintptr_t)p | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) % 16 == 0;
   if (vec)
-    hipLaunchKernelGGL(gk::adamw4_kernel, dim3(ew_blocks(n / 4)), dim3(256), 0, s, p, g, m, v,
+    GK_LAUNCH(gk::adamw4_kernel, dim3(ew_blocks(n / 4)), dim3(256), 0, s, p, g, m, v,
                        n / 4, lr, b1, b2, eps, c1, c2);
   else
-    hipLaunchKernelGGL(gk::adamw_kernel, dim3(ew_blocks(n)), dim3(256), 0, s, p, g, m, v, n, lr,
+    GK_LAUNCH(gk::adamw_kernel, dim3(ew_blocks(n)), dim3(256), 0, s, p, g, m, v, n, lr,
                        b1, b2, eps, c1, c2);
 }
 
@@ -262,10 +262,10 @@ static void muon_chunk(const Dims& d, const OptimPlan& o, char* ws, const gk::Ma
   T* AA = reinterpret_cast<T*>(ws + o.aa);
   const int64_t n = (int64_t)r * k, nr = (int64_t)r * r;
   const unsigned per = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 64));
-  hipLaunchKernelGGL(gk::muon_momentum_kernel, dim3(gk::kMomBlocks, nm), dim3(256), 0, s, grads,
+  GK_LAUNCH(gk::muon_momentum_kernel, dim3(gk::kMomBlocks, nm), dim3(256), 0, s, grads,
                      buf, tb, n, mu, nesterov, part);
-  hipLaunchKernelGGL(gk::muon_norm_kernel, dim3(nm), dim3(64), 0, s, part, scal);
-  hipLaunchKernelGGL(gk::muon_to_x_kernel<T>, dim3(per, nm), dim3(256), 0, s, grads, buf, tb, r, k,
+  GK_LAUNCH(gk::muon_norm_kernel, dim3(nm), dim3(64), 0, s, part, scal);
+  GK_LAUNCH(gk::muon_to_x_kernel<T>, dim3(per, nm), dim3(256), 0, s, grads, buf, tb, r, k,
                      mu, nesterov, scal, X);
   for (int it = 0; it < steps; ++it) {
     gemm_nt_store_batched(d, nm, r, r, k, X, n, X, n, Am, nr, s);  // A = X X^T
@@ -275,7 +275,7 @@ static void muon_chunk(const Dims& d, const OptimPlan& o, char* ws, const gk::Ma
     gemm_lin_batched(d, true, nm, r, k, r, AA, nr, X, n, X, Y, n, a, 1.0f, s);
     std::swap(X, Y);
   }
-  hipLaunchKernelGGL(gk::muon_apply_kernel<T>, dim3(per, nm), dim3(256), 0, s, params, X, tb, r,
+  GK_LAUNCH(gk::muon_apply_kernel<T>, dim3(per, nm), dim3(256), 0, s, params, X, tb, r,
                      k, 1.0f - lr * wd, lr);
 }
 

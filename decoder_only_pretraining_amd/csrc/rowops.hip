@@ -117,12 +117,19 @@ __global__ void rope_table_kernel(float* __restrict__ cs, int T, int D, double t
 }
 
 // ------------------------------------------------------------ embedding
+// Row `id` of a [V][W] table, or a row of zeros for an id outside [0, V):
+// such ids violate the call's precondition, and every table access goes
+// through here so that they never read outside the table (W <= 2048).
+static __device__ __attribute__((aligned(16))) float g_zero_row[2048];
+__device__ __forceinline__ const float* table_row(const float* tab, int32_t id, int V, int W) {
+  return (uint32_t)id < (uint32_t)V ? tab + (int64_t)id * W : g_zero_row;
+}
+
 __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wte,
                                                     const int32_t* __restrict__ tok,
-                                                    float* __restrict__ x0, int64_t N, int C) {
+                                                    float* __restrict__ x0, int64_t N, int C, int V) {
   const int64_t n = blockIdx.x;
-  const int64_t row = tok[n];
-  const f32x4* s = reinterpret_cast<const f32x4*>(wte + row * C);
+  const f32x4* s = reinterpret_cast<const f32x4*>(table_row(wte, tok[n], V, C));
   f32x4* o = reinterpret_cast<f32x4*>(x0 + n * C);
   for (int c = threadIdx.x; c < C / 4; c += blockDim.x) o[c] = s[c];
 }
@@ -139,13 +146,13 @@ __global__ __launch_bounds__(256) void smear_embed_kernel(const float* __restric
                                                           const float* __restrict__ w,
                                                           float* __restrict__ x0,
                                                           float* __restrict__ sig, int64_t N,
-                                                          int T, int C) {
+                                                          int T, int C, int V) {
   const int lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
   const int C4 = C / 4;
   const bool has_prev = (n % T) != 0;  // uniform over the wavefront
-  const f32x4* e = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n] * C);
+  const f32x4* e = reinterpret_cast<const f32x4*>(table_row(wte, tok[n], V, C));
   f32x4* o = reinterpret_cast<f32x4*>(x0 + n * C);
   if (!has_prev) {
 #pragma unroll
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(256) void smear_embed_kernel(const float* __restric
     if (lane == 0) sig[n] = 0.0f;
     return;
   }
-  const f32x4* ep = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[n - 1] * C);
+  const f32x4* ep = reinterpret_cast<const f32x4*>(table_row(wte, tok[n - 1], V, C));
   f32x4 ev[NC], pv[NC];
   float dot = 0.0f;
 #pragma unroll
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(256) void smear_bwd_kernel(const float* __restrict_
                                                         const float* __restrict__ sig,
                                                         float* __restrict__ ge,
                                                         float* __restrict__ part, int64_t N,
-                                                        int T, int C) {
+                                                        int T, int C, int V) {
   constexpr int RG = 4, GROUPS = kSmearRows / 4 / RG;
   __shared__ f32x4 red[4][NC * 64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256) void smear_bwd_kernel(const float* __restrict_
     for (int j = 0; j <= RG; ++j) {
       const int64_t n = n0 + j, m = n0 - 1 + j;
       const f32x4* gr = reinterpret_cast<const f32x4*>(g + (n < N ? n : 0) * C);
-      const f32x4* er = reinterpret_cast<const f32x4*>(wte + (int64_t)tok[m >= 0 && m < N ? m : 0] * C);
+      const f32x4* er = reinterpret_cast<const f32x4*>(table_row(wte, tok[m >= 0 && m < N ? m : 0], V, C));
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
         const int c4 = lane + i * 64;
@@ -325,9 +332,12 @@ __global__ __launch_bounds__(kChunk) void token_links_kernel(const int32_t* __re
 __global__ __launch_bounds__(256) void rows_to_table_kernel(const float* __restrict__ g, int W,
                                                             const int32_t* __restrict__ tok,
                                                             const int32_t* __restrict__ link,
-                                                            int64_t N, float* __restrict__ tab) {
+                                                            int64_t N, float* __restrict__ tab,
+                                                            int V) {
   const int64_t n = blockIdx.x;
-  if (!link[N + n]) return;
+  // only leaders work; an id outside [0, V) (and so its whole link chain)
+  // has no table row
+  if (!link[N + n] || (uint32_t)tok[n] >= (uint32_t)V) return;
   float* dst = tab + (int64_t)tok[n] * W;
   for (int f = threadIdx.x; f < W; f += 256) {
     float acc = g[n * W + f];
@@ -707,7 +717,8 @@ __global__ __launch_bounds__(256) void rope_fwd_kernel(T* __restrict__ qkv, floa
                                                        const float* __restrict__ a,
                                                        const float* __restrict__ ve,
                                                        const int32_t* __restrict__ tok, int64_t N,
-                                                       int T_, int H, int Hk, int Qkv, float eps) {
+                                                       int T_, int H, int Hk, int Qkv, float eps,
+                                                       int V) {
   constexpr int H2 = D / 2, LP = D / 8;
   const int q = threadIdx.x % LP;
   const int64_t task = (int64_t)blockIdx.x * (256 / LP) + threadIdx.x / LP;
@@ -731,7 +742,7 @@ __global__ __launch_bounds__(256) void rope_fwd_kernel(T* __restrict__ qkv, floa
     const int j = (int)((task - nrot) % Hk);
     T* vp = qkv + n * Qkv + (R + j) * D;
     const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
-    const float* er = ve + (int64_t)tok[n] * Hk * D + j * D;
+    const float* er = table_row(ve, tok[n], V, Hk * D) + j * D;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int o = half * H2 + 4 * q;
@@ -749,7 +760,7 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(
     T* __restrict__ gqkv, const T* __restrict__ qkv, const float* __restrict__ rqk,
     const float* __restrict__ cs, const float* __restrict__ a, const float* __restrict__ ve,
     float* __restrict__ rows, float* __restrict__ ga, const int32_t* __restrict__ tok, int64_t N,
-    int T_, int H, int Hk, int Qkv) {
+    int T_, int H, int Hk, int Qkv, int V) {
   constexpr int H2 = D / 2, LP = D / 8;
   const int q = threadIdx.x % LP;
   const int64_t task = (int64_t)blockIdx.x * (256 / LP) + threadIdx.x / LP;
@@ -774,7 +785,7 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(
     const int j = (int)((task - nrot) % Hk);
     const T* gp = gqkv + n * Qkv + (R + j) * D;
     const float g = 1.0f / (1.0f + __expf(-a[n * Hk + j]));
-    const int64_t off = (int64_t)tok[n] * Hk * D + j * D;
+    const float* vrow = table_row(ve, tok[n], V, Hk * D) + j * D;
     // position n's row of the table gradient (added to the table per token
     // id by rows_to_table_kernel)
     float* rp = rows + n * Hk * D + j * D;
@@ -783,7 +794,7 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(
     for (int e = 0; e < 2; ++e) {
       const int o = 4 * q + e * H2;
       const f32x4 gv = load4<T>(gp + o);
-      dot += dot4(gv, *reinterpret_cast<const f32x4*>(ve + off + o));
+      dot += dot4(gv, *reinterpret_cast<const f32x4*>(vrow + o));
       *reinterpret_cast<f32x4*>(rp + o) = g * gv;
     }
     dot = group_sum<LP>(dot);
@@ -794,10 +805,13 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(
 // ------------------------------------------------------------ loss
 // 1 / n_valid (scalars[0]) from the targets; one block.
 __global__ __launch_bounds__(1024) void count_valid_kernel(const int32_t* __restrict__ tgt,
-                                                           float* __restrict__ scalars, int64_t N) {
+                                                           float* __restrict__ scalars, int64_t N,
+                                                           int V) {
   __shared__ int s_cnt[1024];
   int cnt = 0;
-  for (int64_t n = threadIdx.x; n < N; n += 1024) cnt += tgt[n] >= 0 ? 1 : 0;
+  // a target counts iff it lies in [0, V): -1 (and, off the precondition,
+  // any other id outside the vocabulary) is ignored
+  for (int64_t n = threadIdx.x; n < N; n += 1024) cnt += (uint32_t)tgt[n] < (uint32_t)V ? 1 : 0;
   s_cnt[threadIdx.x] = cnt;
   __syncthreads();
   for (int s = 512; s > 0; s >>= 1) {
@@ -843,7 +857,8 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(T* __restrict__ logits,
   T* row = logits + n * V;
   const int nvec = V / VEC;
   const int y = tgt[n];
-  const float cy = y >= 0 ? static_cast<float>(row[y]) : 0.0f;  // read before the row is rewritten
+  const bool valid = (uint32_t)y < (uint32_t)V;  // ignored: -1, or off-precondition ids
+  const float cy = valid ? static_cast<float>(row[y]) : 0.0f;  // read before the row is rewritten
   VT c[RC];
 #pragma unroll
   for (int r = 0; r < RC; ++r) {
@@ -868,9 +883,9 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(T* __restrict__ logits,
   if (lane == 0) red[wv] = s;
   __syncthreads();
   s = (red[0] + red[1]) + (red[2] + red[3]);
-  if (tid == 0) lossrow[n] = y >= 0 ? cap + logf(s) - cy : 0.0f;
+  if (tid == 0) lossrow[n] = valid ? cap + logf(s) - cy : 0.0f;
   if (!grad) return;
-  const float inv = y >= 0 ? 1.0f / s : 0.0f, inv_nv = scalars[0], icap = 1.0f / cap;
+  const float inv = valid ? 1.0f / s : 0.0f, inv_nv = scalars[0], icap = 1.0f / cap;
   auto gradv = [&](VT x, int v) {
     VT o;
 #pragma unroll
@@ -928,7 +943,7 @@ void launch_cast(const float* src, void* dst, const std::vector<CastSeg>& segs, 
       mx = std::max(mx, t.seg[i].n);
     }
     dim3 grid(std::min<unsigned>(blocks_for(mx, 256 * 8), 1024), t.nseg);
-    hipLaunchKernelGGL(cast_kernel, grid, dim3(256), 0, s, src, static_cast<bf16*>(dst), t);
+    GK_LAUNCH(cast_kernel, grid, dim3(256), 0, s, src, static_cast<bf16*>(dst), t);
   }
 }
 
@@ -941,33 +956,80 @@ void launch_cast_t(const float* src, void* dst, void* dstT, const std::vector<in
     t.rows = rows;
     t.cols = cols;
     dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)n);
-    hipLaunchKernelGGL(cast_t_kernel, grid, dim3(256), 0, s, src, static_cast<bf16*>(dst),
+    GK_LAUNCH(cast_t_kernel, grid, dim3(256), 0, s, src, static_cast<bf16*>(dst),
                        static_cast<bf16*>(dstT), t);
   }
 }
 
 void launch_zero(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return;
-  hipLaunchKernelGGL(zero_kernel, dim3(std::min<unsigned>(blocks_for(n, 256 * 4), 8192)),
+  GK_LAUNCH(zero_kernel, dim3(std::min<unsigned>(blocks_for(n, 256 * 4), 8192)),
                      dim3(256), 0, s, p, n);
 }
 
 void launch_rope_table(float* cs, int T, int D, float theta, hipStream_t s) {
   const int64_t n = (int64_t)T * (D / 2);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, cs, T, D,
+  GK_LAUNCH(rope_table_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, cs, T, D,
                      (double)theta);
 }
 
-void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C,
+// ------------------------------------------------------------ debug checks
+__global__ __launch_bounds__(1024) void check_ids_kernel(const int32_t* __restrict__ tok,
+                                                         const int32_t* __restrict__ tgt,
+                                                         int64_t N, int V, uint32_t* out) {
+  __shared__ uint32_t s_bad[2][16];
+  uint32_t bt = 0, by = 0;
+  for (int64_t n = threadIdx.x; n < N; n += 1024) {
+    bt += (uint32_t)tok[n] >= (uint32_t)V ? 1u : 0u;
+    const int32_t y = tgt[n];
+    by += (y < -1 || y >= V) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    bt += __shfl_xor(bt, o, 64);
+    by += __shfl_xor(by, o, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_bad[0][w] = bt;
+    s_bad[1][w] = by;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    uint32_t t = 0;
+    for (int k = 0; k < 16; ++k) t += s_bad[threadIdx.x][k];
+    out[threadIdx.x] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void check_finite_kernel(const float* __restrict__ x, int64_t n,
+                                                           uint32_t* flag) {
+  uint32_t bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    bad |= (__float_as_uint(x[i]) & 0x7f800000u) == 0x7f800000u ? 1u : 0u;
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1u);
+}
+
+void launch_check_ids(const int32_t* tok, const int32_t* tgt, int64_t N, int V, uint32_t* out,
+                      hipStream_t s) {
+  GK_LAUNCH(check_ids_kernel, dim3(1), dim3(1024), 0, s, tok, tgt, N, V, out);
+}
+
+void launch_check_finite(const float* x, int64_t n, uint32_t* flag, hipStream_t s) {
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+  GK_LAUNCH(check_finite_kernel, dim3(blocks), dim3(256), 0, s, x, n, flag);
+}
+
+void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, int C, int V,
                   hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)N), dim3(256), 0, s, wte, tok, x0, N, C);
+  GK_LAUNCH(embed_kernel, dim3((unsigned)N), dim3(256), 0, s, wte, tok, x0, N, C, V);
 }
 
 template <typename T, int NC>
 static void mix_norm_nc(const Dims& d, const float* x, const float* x0, const float* lam_r,
                         const float* lam_0, float* xin_out, void* y, float* r, const float* wg,
                         float* a, hipStream_t s) {
-  hipLaunchKernelGGL((mix_norm_kernel<T, NC>), dim3((unsigned)((d.N + 3) / 4)), dim3(256), 0, s,
+  GK_LAUNCH((mix_norm_kernel<T, NC>), dim3((unsigned)((d.N + 3) / 4)), dim3(256), 0, s,
                      x, x0, lam_r, lam_0, xin_out, static_cast<T*>(y), r, wg, a, d.N, d.C, d.Hk,
                      d.eps);
 }
@@ -1007,7 +1069,7 @@ void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((d.N + 3) / 4));
   NormBwdArgs b = a;
   b.gxc_bf16 = d.bf16 ? 1 : 0;
-#define NB_CALL(NC) hipLaunchKernelGGL(norm_bwd_kernel<NC>, grid, dim3(256), 0, s, b, d.N, d.C, d.Hk)
+#define NB_CALL(NC) GK_LAUNCH(norm_bwd_kernel<NC>, grid, dim3(256), 0, s, b, d.N, d.C, d.Hk)
   switch ((d.C + 255) / 256) {
     case 1: NB_CALL(1); break;
     case 2: NB_CALL(2); break;
@@ -1023,7 +1085,7 @@ void launch_norm_bwd(const Dims& d, const NormBwdArgs& a, hipStream_t s) {
 
 void launch_lambda_finalize(const Dims& d, const float* lam_part, int nblk, float* g_lr,
                             float* g_l0, hipStream_t s, int layers, float scale) {
-  hipLaunchKernelGGL(lambda_finalize_kernel, dim3((unsigned)layers), dim3(256), 0, s, lam_part,
+  GK_LAUNCH(lambda_finalize_kernel, dim3((unsigned)layers), dim3(256), 0, s, lam_part,
                      nblk, (int64_t)nblk * 2, g_lr, g_l0, d.accumulate ? 1 : 0, scale);
 }
 
@@ -1032,8 +1094,8 @@ void launch_smear_embed(const Dims& d, const float* wte, const int32_t* tok, con
   const dim3 grid((unsigned)((d.N + 3) / 4));
   const int nc = (d.C + 255) / 256;
 #define SM_CALL(NC)                                                                             \
-  hipLaunchKernelGGL(smear_embed_kernel<NC>, grid, dim3(256), 0, s, wte, tok, w, x0, sig, d.N, \
-                     d.T, d.C)
+  GK_LAUNCH(smear_embed_kernel<NC>, grid, dim3(256), 0, s, wte, tok, w, x0, sig, d.N, \
+                     d.T, d.C, d.V)
   if (nc <= 1) SM_CALL(1);
   else if (nc == 2) SM_CALL(2);
   else if (nc == 3) SM_CALL(3);
@@ -1050,8 +1112,8 @@ void launch_smear_bwd(const Dims& d, const float* g, const float* wte, const int
   const dim3 grid((unsigned)nblk);
   const int nc = (d.C + 255) / 256;
 #define SB_CALL(NC)                                                                               \
-  hipLaunchKernelGGL(smear_bwd_kernel<NC>, grid, dim3(256), 0, s, g, wte, tok, w, sig, ge, part, \
-                     d.N, d.T, d.C)
+  GK_LAUNCH(smear_bwd_kernel<NC>, grid, dim3(256), 0, s, g, wte, tok, w, sig, ge, part, \
+                     d.N, d.T, d.C, d.V)
   if (nc <= 1) SB_CALL(1);
   else if (nc == 2) SB_CALL(2);
   else if (nc == 3) SB_CALL(3);
@@ -1059,14 +1121,14 @@ void launch_smear_bwd(const Dims& d, const float* g, const float* wte, const int
   else if (nc <= 6) SB_CALL(6);
   else SB_CALL(8);
 #undef SB_CALL
-  hipLaunchKernelGGL(veg_finalize_kernel, dim3((unsigned)((d.C + 63) / 64)), dim3(256), 0, s,
+  GK_LAUNCH(veg_finalize_kernel, dim3((unsigned)((d.C + 63) / 64)), dim3(256), 0, s,
                      part, gw, d.C, nblk, d.accumulate ? 1 : 0);
 }
 
 int smear_blocks(int64_t N) { return (int)((N + kSmearRows - 1) / kSmearRows); }
 
 void launch_backout_weights(const float* lam, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(backout_weights_kernel, dim3(1), dim3(64), 0, s, lam, out);
+  GK_LAUNCH(backout_weights_kernel, dim3(1), dim3(64), 0, s, lam, out);
 }
 
 int veg_splits(int64_t N) { return (int)std::max<int64_t>(256, (N + kVegPer - 1) / kVegPer); }
@@ -1075,7 +1137,7 @@ void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* par
                       float* gwg, hipStream_t s) {
   const int64_t per = (d.N + splits - 1) / splits;  // <= kVegPer with splits = veg_splits(N)
 #define GPT_VEG(TY, HK)                                                                            \
-  hipLaunchKernelGGL((veg_partial_kernel<TY, HK>), dim3((unsigned)splits), dim3(256), 0, s, ga,    \
+  GK_LAUNCH((veg_partial_kernel<TY, HK>), dim3((unsigned)splits), dim3(256), 0, s, ga,    \
                      static_cast<const TY*>(xn), part, d.N, d.C, d.Hk, per)
   if (d.bf16) {
     if (d.Hk <= 4) GPT_VEG(bf16, 4);
@@ -1088,7 +1150,7 @@ void launch_veg_wgrad(const Dims& d, const float* ga, const void* xn, float* par
   }
 #undef GPT_VEG
   const int n = d.C * d.Hk;
-  hipLaunchKernelGGL(veg_finalize_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
+  GK_LAUNCH(veg_finalize_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
                      gwg, n, splits, d.accumulate ? 1 : 0);
 }
 
@@ -1101,8 +1163,8 @@ void launch_rope_qk_ve_fwd(const Dims& d, void* qkv, float* rqk, const float* cs
                            const float* ve_table, const int32_t* tok, hipStream_t s) {
   const dim3 grid(rope_blocks(d, ve_table != nullptr));
 #define GPT_ROPE_F(TY, DD)                                                                        \
-  hipLaunchKernelGGL((rope_fwd_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<TY*>(qkv), rqk, \
-                     cs, a, ve_table, tok, d.N, d.T, d.H, d.Hk, d.Qkv, d.eps)
+  GK_LAUNCH((rope_fwd_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<TY*>(qkv), rqk, \
+                     cs, a, ve_table, tok, d.N, d.T, d.H, d.Hk, d.Qkv, d.eps, d.V)
   if (d.bf16) {
     if (d.D == 128) GPT_ROPE_F(bf16, 128);
     else GPT_ROPE_F(bf16, 64);
@@ -1118,9 +1180,9 @@ void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const flo
                            float* gve_rows, float* ga, const int32_t* tok, hipStream_t s) {
   const dim3 grid(rope_blocks(d, ve_table != nullptr));
 #define GPT_ROPE_B(TY, DD)                                                                          \
-  hipLaunchKernelGGL((rope_bwd_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<TY*>(gqkv),       \
+  GK_LAUNCH((rope_bwd_kernel<TY, DD>), grid, dim3(256), 0, s, static_cast<TY*>(gqkv),       \
                      static_cast<const TY*>(qkv), rqk, cs, a, ve_table, gve_rows, ga, tok, d.N,     \
-                     d.T, d.H, d.Hk, d.Qkv)
+                     d.T, d.H, d.Hk, d.Qkv, d.V)
   if (d.bf16) {
     if (d.D == 128) GPT_ROPE_B(bf16, 128);
     else GPT_ROPE_B(bf16, 64);
@@ -1132,29 +1194,29 @@ void launch_rope_qk_ve_bwd(const Dims& d, void* gqkv, const void* qkv, const flo
 }
 
 void launch_token_links(const int32_t* tok, int64_t N, int32_t* link, hipStream_t s) {
-  hipLaunchKernelGGL(token_links_kernel, dim3((unsigned)((N + kChunk - 1) / kChunk)), dim3(kChunk),
+  GK_LAUNCH(token_links_kernel, dim3((unsigned)((N + kChunk - 1) / kChunk)), dim3(kChunk),
                      0, s, tok, N, link);
 }
 
 void launch_rows_to_table(const float* g, int W, const int32_t* tok, const int32_t* link,
-                          int64_t N, float* tab, hipStream_t s) {
-  hipLaunchKernelGGL(rows_to_table_kernel, dim3((unsigned)N), dim3(256), 0, s, g, W, tok, link, N,
-                     tab);
+                          int64_t N, float* tab, int V, hipStream_t s) {
+  GK_LAUNCH(rows_to_table_kernel, dim3((unsigned)N), dim3(256), 0, s, g, W, tok, link, N,
+                     tab, V);
 }
 
 void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipStream_t s) {
-  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(1024), 0, s, tgt, scalars, d.N);
+  GK_LAUNCH(count_valid_kernel, dim3(1), dim3(1024), 0, s, tgt, scalars, d.N, d.V);
 }
 
 void launch_loss(const Dims& d, void* logits, const int32_t* tgt, const float* scalars,
                  float* lossrow, float* loss, bool grad, hipStream_t s) {
   if (d.bf16)
-    hipLaunchKernelGGL((ce_rows_kernel<bf16, 16>), dim3((unsigned)d.N), dim3(256), 0, s,
+    GK_LAUNCH((ce_rows_kernel<bf16, 16>), dim3((unsigned)d.N), dim3(256), 0, s,
                        static_cast<bf16*>(logits), tgt, scalars, lossrow, d.V, d.cap, grad ? 1 : 0);
   else
-    hipLaunchKernelGGL((ce_rows_kernel<float, 16>), dim3((unsigned)d.N), dim3(256), 0, s,
+    GK_LAUNCH((ce_rows_kernel<float, 16>), dim3((unsigned)d.N), dim3(256), 0, s,
                        static_cast<float*>(logits), tgt, scalars, lossrow, d.V, d.cap, grad ? 1 : 0);
-  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, lossrow, scalars, loss, d.N);
+  GK_LAUNCH(loss_kernel, dim3(1), dim3(1024), 0, s, lossrow, scalars, loss, d.N);
 }
 
 }  // namespace gpt

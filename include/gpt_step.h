@@ -34,16 +34,17 @@
 extern "C" {
 #endif
 
-#define GPT_ABI_VERSION 1
+#define GPT_ABI_VERSION 2
 
 typedef enum gpt_status {
   GPT_OK = 0,
-  GPT_E_INVAL = -1,        /* a config field or size is out of range        */
+  GPT_E_INVAL = -1,        /* a config field, size or (checked) input is out of range */
   GPT_E_NULLPTR = -2,      /* a required pointer is NULL                     */
   GPT_E_ALIGN = -3,        /* a pointer breaks the alignment rule below      */
   GPT_E_WORKSPACE = -4,    /* workspace smaller than gpt_workspace_size      */
   GPT_E_UNSUPPORTED = -5,  /* valid model, but not built into this library   */
-  GPT_E_HIP = -6           /* the HIP runtime reported an error              */
+  GPT_E_HIP = -6,          /* the HIP runtime reported an error              */
+  GPT_E_NONFINITE = -7     /* GPT_F_CHECK_FINITE: the loss or a gradient is not finite */
 } gpt_status;
 
 enum { GPT_DT_F32 = 0, GPT_DT_BF16 = 1 };
@@ -51,6 +52,21 @@ enum { GPT_DT_F32 = 0, GPT_DT_BF16 = 1 };
 /* flags */
 enum {
   GPT_F_ACCUMULATE = 1,    /* grads += new grads instead of grads = new grads */
+  /* An RMSNorm of the token embedding before the first block. The pages
+   * place RMSNorm only before attention, before the MLP and before lm_head
+   * (nanochat additions page, feature table), so the library does not
+   * build it: a config that sets this bit is GPT_E_UNSUPPORTED. */
+  GPT_F_EMBED_NORM = 2,
+  /* Debug checks, each reported after an internal hipStreamSynchronize of
+   * `stream` (so the call is no longer asynchronous):
+   * CHECK_FINITE: after the step, the loss (and with gpt_fwd_bwd every
+   *   gradient) is checked on the device; GPT_E_NONFINITE if any is NaN or
+   *   infinite (the outputs are written all the same).
+   * CHECK_INPUTS: before anything else is enqueued, token ids are checked
+   *   to lie in [0, vocab) and targets in [-1, vocab); GPT_E_INVAL if not,
+   *   with nothing else enqueued. */
+  GPT_F_CHECK_FINITE = 4,
+  GPT_F_CHECK_INPUTS = 8,
   /* Model variants of the additions page (feature table rows Smear and
    * Backout, and the notes on them). Readings where the page is silent:
    * Smear: x0[b,t] = e[b,t] + sigmoid(<e[b,t], smear_gate>) * e[b,t-1] for
@@ -59,14 +75,14 @@ enum {
    *   entering layer 0 and the one every block mixes in).
    * Backout: the final norm reads x - backout_lambda * x_mid, where x_mid
    *   is the residual stream entering layer n_layer / 2. */
-  GPT_F_SMEAR = 2,
-  GPT_F_BACKOUT = 4,
+  GPT_F_SMEAR = 16,
+  GPT_F_BACKOUT = 32,
   /* The previous call on this workspace had the same params (same values,
    * e.g. the micro-batches of one optimizer step): its bf16 weight mirrors
    * in the workspace are reused instead of converted again from the fp32
    * params (fp8 weight codes are still made each call). Undefined results
    * if the params or the workspace changed since. */
-  GPT_F_REUSE_WEIGHTS = 8
+  GPT_F_REUSE_WEIGHTS = 64
 };
 
 /*
@@ -175,9 +191,16 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
  *   workspace (device) >= gpt_workspace_size bytes; scratch, contents
  *             undefined after the call.
  * Alignment: params, grads and workspace 256-byte aligned; tokens, targets
- * and loss 4-byte aligned. Out-of-range token ids are a precondition
- * violation (not checked). Concurrent calls need distinct workspaces,
+ * and loss 4-byte aligned. Concurrent calls need distinct workspaces,
  * grads and loss buffers.
+ * Ids out of range are a precondition violation, reported only with
+ * GPT_F_CHECK_INPUTS; without it they never make a kernel touch memory
+ * outside its buffers: a token id outside [0, vocab) embeds as a zero row
+ * (no table row is read or receives a gradient), and a target outside
+ * [0, vocab) is ignored like -1.
+ * Errors: validation errors return before anything is enqueued; if a
+ * kernel launch fails, no later launch of the call is enqueued and the call
+ * returns GPT_E_HIP (detail in gpt_last_error).
  */
 int gpt_fwd_bwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
                 const int32_t* targets, float* loss, float* grads,
@@ -334,6 +357,21 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
  */
 int gpt_profile_begin(const char* site_prefix);
 int gpt_profile_end(double* total_ms, int64_t* launches);
+
+/*
+ * Host only; test support for the error path. For the calling thread's
+ * later entry-point calls: fail_at >= 0 makes launch number fail_at
+ * (0-based) of each call fail as if the HIP runtime had refused it (it is
+ * not launched, nor is any later launch of the call, and the call returns
+ * GPT_E_HIP); fail_at < 0 turns this off. dry_run = 1 counts the launch
+ * sequence without launching anything (device pointers are then never
+ * used, and the debug checks' synchronisations are skipped), so the host
+ * logic of a call can run on a machine without a GPU. Both default to off.
+ * gpt_debug_launch_count gives the number of launches the thread's last
+ * entry-point call issued (counted, in a dry run).
+ */
+int gpt_debug_launches(int64_t fail_at, int32_t dry_run);
+int gpt_debug_launch_count(int64_t* issued);
 
 /* Static text for a status code. */
 const char* gpt_status_string(int status);

@@ -69,7 +69,7 @@ def test_validation_errors():
     bad = [dict(abi_version=7), dict(n_layer=0), dict(n_embd=100), dict(head_dim=96),
            dict(n_kv_head=3), dict(n_head=3, n_kv_head=2), dict(mlp_hidden=100),
            dict(vocab=500), dict(seq_len=0), dict(batch=0), dict(short_window=-1),
-           dict(compute_dtype=5), dict(flags=16), dict(rope_theta=0.5), dict(norm_eps=0.0),
+           dict(compute_dtype=5), dict(flags=128), dict(rope_theta=0.5), dict(norm_eps=0.0),
            dict(softcap=-1.0), dict(fp8_linears=2), dict(n_kv_head=32, n_head=32)]
     for kw in bad:
         assert B.validate(B.make_config(w, **kw)) == -1, kw
@@ -78,8 +78,13 @@ def test_validation_errors():
     assert B.validate(B.make_config(w, fp8_linears=1)) == -1
     assert "bf16" in B.lib().gpt_last_error().decode()
     assert B.validate(B.make_config(w, fp8_linears=1, compute_dtype=B.GPT_DT_BF16)) == 0
-    # the model-variant flags are known bits
+    # the model-variant, debug and reuse flags are known bits
     assert B.validate(B.make_config(w, flags=B.GPT_F_SMEAR | B.GPT_F_BACKOUT | 1)) == 0
+    assert B.validate(B.make_config(w, flags=B.GPT_F_CHECK_FINITE | B.GPT_F_CHECK_INPUTS |
+                                    B.GPT_F_REUSE_WEIGHTS)) == 0
+    # the embedding norm is a known bit that this library does not build
+    assert B.validate(B.make_config(w, flags=B.GPT_F_EMBED_NORM)) == -5
+    assert "EMBED_NORM" in B.lib().gpt_last_error().decode()
     assert B.lib().gpt_config_validate(None) == -2
 
 
@@ -222,3 +227,84 @@ def test_optimizer_validation():
                                 None) == -2
     assert L.gpt_optimizer_step(ctypes.byref(cfg), ctypes.byref(hp), ctypes.c_void_p(260), p, p,
                                 p, ws, None) == -3
+
+
+# ---------------------------------------------------------------- launch sequence
+# Dry runs (gpt_debug_launches): the host logic of an entry point runs and
+# counts its launches without launching anything, so none of these tests
+# needs a GPU; fake device pointers are never dereferenced.
+
+@pytest.fixture
+def dry():
+    B.debug_launches(-1, True)
+    yield
+    B.debug_launches(-1, False)
+
+
+def _fake(n=7):
+    return [ctypes.c_void_p(1 << 20) for _ in range(n)]
+
+
+def _fwd_bwd(cfg):
+    p = _fake()
+    ws = B.workspace_size(cfg)
+    return B.lib().gpt_fwd_bwd(ctypes.byref(cfg), p[0], p[1], p[2], p[3], p[4], p[5], ws, None)
+
+
+def _fwd(cfg):
+    p = _fake()
+    ws = B.workspace_size(cfg)
+    return B.lib().gpt_fwd(ctypes.byref(cfg), p[0], p[1], p[2], p[3], p[4], ws, None)
+
+
+CASES = {"tiny": W.get("tiny"), "d12": W.get("d12"), "d12_gqa": W.get("d12_gqa"),
+         "d26_fp8": W.get("d26"), "d12_smear_backout": VARIANTS["d12_smear_backout"]}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_dry_run_counts_the_launch_sequence(dry, name):
+    cfg = B.make_config(CASES[name])
+    assert _fwd_bwd(cfg) == 0
+    n_step = B.debug_launch_count()
+    assert _fwd_bwd(cfg) == 0 and B.debug_launch_count() == n_step   # deterministic
+    assert _fwd(cfg) == 0
+    n_fwd = B.debug_launch_count()
+    assert 0 < n_fwd < n_step
+    # the debug checks add their own launches: the id check (one), the
+    # finiteness check (a flag clear and one pass over the loss, one over the
+    # gradients in a backward call)
+    assert _fwd_bwd(B.make_config(CASES[name], B.GPT_F_CHECK_INPUTS)) == 0
+    assert B.debug_launch_count() == n_step + 1
+    assert _fwd_bwd(B.make_config(CASES[name], B.GPT_F_CHECK_FINITE)) == 0
+    assert B.debug_launch_count() == n_step + 3
+    assert _fwd(B.make_config(CASES[name], B.GPT_F_CHECK_FINITE)) == 0
+    assert B.debug_launch_count() == n_fwd + 2
+
+
+@pytest.mark.parametrize("name", ["tiny", "d12", "d26_fp8"])
+def test_injected_launch_failure_stops_the_sequence(name):
+    cfg = B.make_config(CASES[name])
+    B.debug_launches(-1, True)
+    try:
+        assert _fwd_bwd(cfg) == 0
+        n_step = B.debug_launch_count()
+        for k in sorted({0, 1, 7, n_step // 2, n_step - 1}):
+            B.debug_launches(k, True)
+            st = _fwd_bwd(cfg)
+            assert st == -6, (k, st)                       # GPT_E_HIP
+            assert B.debug_launch_count() == k             # nothing after the failed launch
+            msg = B.lib().gpt_last_error().decode()
+            assert "injected" in msg and f"launch {k}" in msg
+        B.debug_launches(n_step, True)                     # past the last launch: no failure
+        assert _fwd_bwd(cfg) == 0 and B.debug_launch_count() == n_step
+        # the other entry points report it the same way
+        B.debug_launches(0, True)
+        p = _fake()
+        assert B.lib().gpt_fp8_quantize(p[0], 1, 4, 64, 0, p[1], None, 0, p[2], None) == -6
+        assert B.debug_launch_count() == 0
+        ws = B.decode_attn_workspace(2, 6, 6, 128, 1024, -1)
+        assert B.lib().gpt_decode_attn(2, 6, 6, 128, 1024, -1, p[0], p[1], p[2], p[3], p[4],
+                                       p[5], ws, None) == -6
+    finally:
+        B.debug_launches(-1, False)
+    assert B.lib().gpt_debug_launches(0, 2) == -1
