@@ -32,7 +32,8 @@ EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_par
            "gpt_fwd", "gpt_fp8_quantize", "gpt_status_string", "gpt_last_error",
            "gpt_profile_begin", "gpt_profile_end", "gpt_decode_attn_workspace",
            "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
-           "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count"]
+           "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
+           "gpt_decode_attn_noalloc"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -94,6 +95,7 @@ def lib():
         L.gpt_decode_attn.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6 + [c.c_size_t,
                                                                              c.c_void_p]
         L.gpt_kv_cache_append.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 5
+        L.gpt_decode_attn_noalloc.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6
         L.gpt_optim_workspace_size.argtypes = [P(GptConfig), P(c.c_size_t)]
         L.gpt_optimizer_step.argtypes = [P(GptConfig), P(OptimHparams)] + [c.c_void_p] * 4 + [
             c.c_size_t, c.c_void_p]
@@ -110,7 +112,8 @@ def lib():
                      "gpt_layer_info", "gpt_workspace_size", "gpt_workspace_region",
                      "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize", "gpt_decode_attn_workspace",
                      "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
-                     "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count"):
+                     "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
+                     "gpt_decode_attn_noalloc"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -242,6 +245,17 @@ def decode_attn(q, k_cache, v_cache, seqlen, out, workspace, window=-1, stream=N
                                workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check("gpt_decode_attn", st)
+
+
+def decode_attn_noalloc(q, k_cache, v_cache, seqlen, out, window=-1, stream=None):
+    """gpt_decode_attn_noalloc: decode_attn with the library's static scratch
+    instead of a workspace (for callers that cannot allocate)."""
+    B, H, D = q.shape
+    _, Tmax, Hk, _ = k_cache.shape
+    st = lib().gpt_decode_attn_noalloc(B, H, Hk, D, Tmax, window, q.data_ptr(),
+                                       k_cache.data_ptr(), v_cache.data_ptr(), seqlen.data_ptr(),
+                                       out.data_ptr(), _stream_ptr(stream))
+    _check("gpt_decode_attn_noalloc", st)
 
 
 def kv_cache_append(qkv, pos, k_cache, v_cache, n_head, stream=None):

@@ -23,6 +23,8 @@
 // the combine kernel.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -212,7 +214,44 @@ __global__ __launch_bounds__(256) void kv_cache_append_kernel(
 
 }  // namespace gk
 
+namespace gk {
+
+// Scratch of the no-allocation entry point (gpt_decode_attn_noalloc): the
+// chunk states of one call live in this file-scope device array instead of
+// a caller's workspace. Each GPU the library runs on holds its own copy
+// until the process ends. In host code `dec_scratch` names a host-side
+// stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress (decode_scratch below) and only that address is
+// passed to kernels.
+constexpr size_t kDecScratchBytes = (size_t)4 << 20;
+static __device__ __attribute__((aligned(256))) float dec_scratch[kDecScratchBytes / sizeof(float)];
+
+}  // namespace gk
+
 namespace gpt {
+
+size_t decode_scratch_capacity() { return gk::kDecScratchBytes; }
+
+// Device address of the current GPU's copy of dec_scratch, looked up once
+// per device (with that device current) and kept.
+hipError_t decode_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(gk::dec_scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 // Chunks per (sequence, KV head) for the longest visible range.
 int decode_splits(int Tmax, int window) {

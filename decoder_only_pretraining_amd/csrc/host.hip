@@ -1041,6 +1041,33 @@ int gpt_decode_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t he
   return launch_status();
 }
 
+int gpt_decode_attn_noalloc(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                            int32_t max_len, int32_t window, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* seqlen, void* out, void* stream) {
+  g_err[0] = 0;
+  const int st = decode_validate(batch, n_head, n_kv_head, head_dim, max_len, window);
+  if (st) return st;
+  const size_t need = decode_workspace_bytes(batch, n_head, n_kv_head, head_dim, max_len, window);
+  if (need > decode_scratch_capacity())
+    return fail(GPT_E_WORKSPACE, "chunk states need %zu bytes; the static scratch holds %zu", need,
+                decode_scratch_capacity());
+  if (!q || !k_cache || !v_cache || !seqlen || !out)
+    return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seqlen, 4))
+    return fail(GPT_E_ALIGN, "q, caches and out need 16-byte alignment, seqlen 4");
+  void* scratch = nullptr;
+  if (need) {
+    const hipError_t e = decode_scratch(&scratch);
+    if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s (scratch address)", hipGetErrorString(e));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_reset();
+  launch_decode_attn(batch, n_head, n_kv_head, head_dim, max_len, window, q, k_cache, v_cache,
+                     seqlen, out, scratch, s);
+  return launch_status();
+}
+
 int gpt_kv_cache_append(int32_t batch, int32_t n_new, int32_t n_head, int32_t n_kv_head,
                         int32_t head_dim, int32_t max_len, const void* qkv, const int32_t* pos,
                         void* k_cache, void* v_cache, void* stream) {

@@ -223,6 +223,10 @@ size_t decode_workspace_bytes(int B, int H, int Hk, int D, int Tmax, int window)
 // positions pos[b] + i of the caches (bf16 [B][Tmax][Hk][D]).
 void launch_kv_cache_append(int B, int n_new, int H, int Hk, int D, int Tmax, const void* qkv,
                             const int32_t* pos, void* k, void* v, hipStream_t s);
+// The no-allocation variant's scratch: its capacity in bytes, and the
+// current GPU's device address of it (looked up once per device).
+size_t decode_scratch_capacity();
+hipError_t decode_scratch(void** out);
 void launch_decode_attn(int B, int H, int Hk, int D, int Tmax, int window, const void* q,
                         const void* k, const void* v, const int32_t* seqlen, void* out,
                         void* workspace, hipStream_t s);

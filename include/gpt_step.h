@@ -270,6 +270,26 @@ int gpt_decode_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t he
                     size_t workspace_bytes, void* stream);
 
 /*
+ * gpt_decode_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, rules and results as
+ * gpt_decode_attn, minus the workspace: the chunk states live in a static
+ * 4 MiB scratch array inside the library, one copy per GPU, held until the
+ * process ends (its device address is looked up on the first call on each
+ * device). Calls whose chunk states need more (gpt_decode_attn_workspace
+ * above 4 MiB: batch * n_head * chunks above 8,065 at head_dim 128, above
+ * 15,887 at head_dim 64; chunks = ceil(min(max_len, window + 1) / 128))
+ * return GPT_E_WORKSPACE before anything is enqueued. The call allocates and frees nothing. Every call on a GPU
+ * shares that GPU's scratch, so calls that overlap on one GPU (on
+ * different streams, or from different threads) race; calls ordered on one
+ * stream do not. Each call writes every chunk state it reads, so nothing
+ * left by an earlier call is used.
+ */
+int gpt_decode_attn_noalloc(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                            int32_t max_len, int32_t window, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* seqlen, void* out, void* stream);
+
+/*
  * KV-cache append: writes the k and v rows of n_new tokens per sequence into
  * the caches gpt_decode_attn reads (prefill: the prompt's rows after a
  * forward; decode: the new token's). qkv holds one row per token, row
