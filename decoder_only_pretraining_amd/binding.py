@@ -33,7 +33,7 @@ EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_par
            "gpt_profile_begin", "gpt_profile_end", "gpt_decode_attn_workspace",
            "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
            "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
-           "gpt_decode_attn_noalloc"]
+           "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -96,6 +96,8 @@ def lib():
                                                                              c.c_void_p]
         L.gpt_kv_cache_append.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 5
         L.gpt_decode_attn_noalloc.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6
+        L.gpt_attn_fwd.argtypes = [P(GptConfig), c.c_int32] + [c.c_void_p] * 4
+        L.gpt_attn_bwd.argtypes = [P(GptConfig), c.c_int32] + [c.c_void_p] * 7
         L.gpt_optim_workspace_size.argtypes = [P(GptConfig), P(c.c_size_t)]
         L.gpt_optimizer_step.argtypes = [P(GptConfig), P(OptimHparams)] + [c.c_void_p] * 4 + [
             c.c_size_t, c.c_void_p]
@@ -113,7 +115,7 @@ def lib():
                      "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize", "gpt_decode_attn_workspace",
                      "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
                      "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
-                     "gpt_decode_attn_noalloc"):
+                     "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -210,6 +212,22 @@ def fwd(cfg, params, tokens, targets, loss, workspace, stream=None):
                        targets.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
                        workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check("gpt_fwd", st)
+
+
+def attn_fwd(cfg, full, qkv, out, lse2, stream=None):
+    """gpt_attn_fwd on device tensors: qkv [N, (H + 2 Hk) D], out [N, H D]
+    (compute dtype), lse2 fp32 of B H T + 64 elements."""
+    st = lib().gpt_attn_fwd(ctypes.byref(cfg), int(full), qkv.data_ptr(), out.data_ptr(),
+                            lse2.data_ptr(), _stream_ptr(stream))
+    _check("gpt_attn_fwd", st)
+
+
+def attn_bwd(cfg, full, qkv, out, g_out, lse2, delta, g_qkv, stream=None):
+    """gpt_attn_bwd on device tensors (delta: fp32 scratch like lse2)."""
+    st = lib().gpt_attn_bwd(ctypes.byref(cfg), int(full), qkv.data_ptr(), out.data_ptr(),
+                            g_out.data_ptr(), lse2.data_ptr(), delta.data_ptr(), g_qkv.data_ptr(),
+                            _stream_ptr(stream))
+    _check("gpt_attn_bwd", st)
 
 
 def fp8_quantize(src, fmt, codes=None, codes_t=None, pitch_t=0, amax=None, stream=None):

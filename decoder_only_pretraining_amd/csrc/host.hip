@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 
@@ -968,6 +969,43 @@ int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
             const int32_t* targets, float* loss, void* workspace, size_t workspace_bytes,
             void* stream) {
   return run(cfg, params, tokens, targets, loss, nullptr, workspace, workspace_bytes, stream, false);
+}
+
+static int attn_args(const gpt_config* cfg, int32_t full, std::initializer_list<const void*> ptrs) {
+  int st = validate(cfg);
+  if (st == GPT_E_UNSUPPORTED) st = GPT_OK;  // flags that only the full step reads
+  if (st) return st;
+  if (full != 0 && full != 1) return fail(GPT_E_INVAL, "full must be 0 or 1");
+  for (const void* p : ptrs) {
+    if (!p) return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+    if (!aligned(p, 16)) return fail(GPT_E_ALIGN, "every pointer needs 16-byte alignment");
+  }
+  return GPT_OK;
+}
+
+int gpt_attn_fwd(const gpt_config* cfg, int32_t full, const void* qkv, void* out, float* lse2,
+                 void* stream) {
+  g_err[0] = 0;
+  const int st = attn_args(cfg, full, {qkv, out, lse2});
+  if (st) return st;
+  const Dims d = make_dims(*cfg);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_reset();
+  launch_attn_fwd(d, full != 0, qkv, out, lse2, s);
+  return launch_status();
+}
+
+int gpt_attn_bwd(const gpt_config* cfg, int32_t full, const void* qkv, const void* out,
+                 const void* g_out, const float* lse2, float* delta, void* g_qkv, void* stream) {
+  g_err[0] = 0;
+  const int st = attn_args(cfg, full, {qkv, out, g_out, lse2, delta, g_qkv});
+  if (st) return st;
+  const Dims d = make_dims(*cfg);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_reset();
+  launch_attn_delta(d, g_out, out, delta, s);
+  launch_attn_bwd(d, full != 0, qkv, g_out, lse2, delta, g_qkv, s);
+  return launch_status();
 }
 
 int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,

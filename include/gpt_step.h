@@ -212,6 +212,40 @@ int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The attention step of one layer on its own (the kernels gpt_fwd_bwd runs
+ * for F5 and its backward), for tests of the step and for reuse: causal
+ * GQA softmax attention with the layer's window ("Nanochat在nanoGPT之上的新增
+ * 功能", feature table and notes: GQA, SSSL sliding window, last layer full):
+ *   y[b,t,h] = sum_s softmax_s(q[b,t,h] . k[b,s,h'] / sqrt(D)) v[b,s,h'],
+ * h' = h / (n_head / n_kv_head), over keys s <= t with (full or
+ * t - s <= short_window). Sizes, window and dtype come from cfg (n_embd,
+ * mlp_hidden, vocab, n_layer, flags and fp8_linears are not used).
+ *   qkv   (device) act [batch * seq_len, (H + 2 Hk) * D]: q heads, k heads,
+ *         v heads of each token (head-major columns), as the QK-norm and the
+ *         value embedding leave them. bf16: q and k rows must have an RMS
+ *         over head_dim of at most 1 (up to bf16 rounding), which the
+ *         parameter-free QK-norm guarantees; the kernels take their softmax
+ *         reference from that bound.
+ *   out   (device) act [batch * seq_len, H * D], written (gpt_attn_fwd).
+ *   lse2  (device) fp32 [batch, H, seq_len] + 64 elements of padding:
+ *         log2 of each query's softmax denominator, written by
+ *         gpt_attn_fwd, read by gpt_attn_bwd.
+ *   g_out (device) act [batch * seq_len, H * D]: dL/dy.
+ *   delta (device) fp32 [batch, H, seq_len] + 64 elements of padding:
+ *         scratch, rowsum(g_out * out) per query.
+ *   g_qkv (device) act [batch * seq_len, (H + 2 Hk) * D], written: dL/dq,
+ *         dL/dk, dL/dv (k and v gradients summed over the query heads that
+ *         share them).
+ *   full  1: full causal context, 0: the short window.
+ * act = the compute dtype; every pointer 16-byte aligned. Validation errors
+ * return before anything is enqueued; the work is enqueued on `stream`.
+ */
+int gpt_attn_fwd(const gpt_config* cfg, int32_t full, const void* qkv, void* out, float* lse2,
+                 void* stream);
+int gpt_attn_bwd(const gpt_config* cfg, int32_t full, const void* qkv, const void* out,
+                 const void* g_out, const float* lse2, float* delta, void* g_qkv, void* stream);
+
+/*
  * Dynamic per-tensor fp8 quantisation of a row-major matrix: the operation
  * applied to every operand of the six block linears when fp8_linears = 1
  * (additions page, feature table: dynamic per-tensor fp8, e4m3 / e5m2;
