@@ -33,7 +33,8 @@ EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_par
            "gpt_profile_begin", "gpt_profile_end", "gpt_decode_attn_workspace",
            "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
            "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
-           "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd"]
+           "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd", "gpt_fp8_gemm_workspace",
+           "gpt_fp8_gemm"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -47,6 +48,12 @@ class GptConfig(ctypes.Structure):
                 ("fp8_linears", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float),
                 ("softcap", ctypes.c_float)]
+
+
+class Fp8Scales(ctypes.Structure):
+    _fields_ = [("axis", ctypes.c_int32), ("nseg", ctypes.c_int32),
+                ("end", ctypes.c_int64 * 2), ("slot_a", ctypes.c_int32 * 3),
+                ("slot_b", ctypes.c_int32 * 3)]
 
 
 class OptimHparams(ctypes.Structure):
@@ -98,6 +105,12 @@ def lib():
         L.gpt_decode_attn_noalloc.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6
         L.gpt_attn_fwd.argtypes = [P(GptConfig), c.c_int32] + [c.c_void_p] * 4
         L.gpt_attn_bwd.argtypes = [P(GptConfig), c.c_int32] + [c.c_void_p] * 7
+        L.gpt_fp8_gemm_workspace.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64,
+                                             P(c.c_size_t)]
+        L.gpt_fp8_gemm.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64, c.c_void_p,
+                                   c.c_int64, c.c_int32, c.c_void_p, c.c_int64, c.c_void_p,
+                                   P(Fp8Scales), c.c_int32, c.c_void_p, c.c_void_p, c.c_size_t,
+                                   c.c_void_p]
         L.gpt_optim_workspace_size.argtypes = [P(GptConfig), P(c.c_size_t)]
         L.gpt_optimizer_step.argtypes = [P(GptConfig), P(OptimHparams)] + [c.c_void_p] * 4 + [
             c.c_size_t, c.c_void_p]
@@ -115,7 +128,8 @@ def lib():
                      "gpt_fwd_bwd", "gpt_fwd", "gpt_fp8_quantize", "gpt_decode_attn_workspace",
                      "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
                      "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
-                     "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd"):
+                     "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd",
+                     "gpt_fp8_gemm_workspace", "gpt_fp8_gemm"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -242,6 +256,22 @@ def fp8_quantize(src, fmt, codes=None, codes_t=None, pitch_t=0, amax=None, strea
     st = lib().gpt_fp8_quantize(src.data_ptr(), dt, rows, cols, fmt, ptr(codes), ptr(codes_t),
                                 pitch_t, ptr(amax), _stream_ptr(stream))
     _check("gpt_fp8_quantize", st)
+
+
+def fp8_gemm(wgrad, A, lda, fmt_a, B, ldb, amax, scales, C, M, N, K, accumulate=False,
+             stream=None):
+    """gpt_fp8_gemm on device tensors (A, B uint8 codes, amax int32 slots, C
+    fp32 [M, N]); allocates the weight-gradient partials itself."""
+    import torch
+    n = ctypes.c_size_t()
+    _check("gpt_fp8_gemm_workspace", lib().gpt_fp8_gemm_workspace(int(wgrad), M, N, K,
+                                                                  ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=C.device)
+    st = lib().gpt_fp8_gemm(int(wgrad), M, N, K, A.data_ptr(), lda, fmt_a, B.data_ptr(), ldb,
+                            amax.data_ptr(), ctypes.byref(scales), int(accumulate), C.data_ptr(),
+                            ws.data_ptr(), n.value, _stream_ptr(stream))
+    _check("gpt_fp8_gemm", st)
+    return ws
 
 
 def decode_attn_workspace(batch, n_head, n_kv_head, head_dim, max_len, window) -> int:

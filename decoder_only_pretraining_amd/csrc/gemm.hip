@@ -747,6 +747,13 @@ void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
             to_deq(dq), s);
 }
 
+// An fp8 product with an fp32 output on the step's code paths: the plain
+// product (format of A picks e4m3 x e4m3 or e5m2 x e4m3), or the
+// weight-gradient product (split-K partials, then the fixed-order sum).
+SplitSum gemm8_product(bool wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                       const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                       float* part, int64_t part_cap, hipStream_t s);
+
 static int64_t wgrad_target(Tile t) { return t.bm == 128 ? 512 : 256; }
 static KSplit f8_wgrad_split(int64_t M, int64_t N, int64_t K) {
   const Tile t = pick_tile_wgrad(M, N);
@@ -770,6 +777,18 @@ SplitSum gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t 
   if (!check_part(part_bytes_f8_wgrad(M, N, K), part_cap)) return SplitSum{};
   run_f8<2>(t, A, lda, B, ldb, M, N, K, ks.chunk, mk_part(part, M, N), q, s);
   return SplitSum{part, ks.splits, M, N, C, accumulate};
+}
+
+SplitSum gemm8_product(bool wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                       const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                       float* part, int64_t part_cap, hipStream_t s) {
+  if (wgrad) return gemm8_wgrad(M, N, K, A, lda, B, ldb, dq, C, accumulate, part, part_cap, s);
+  const Tile t = pick_tile(M, N, K);
+  const Deq8 q = to_deq(dq);
+  const EpF32 ep = mk_f32(C, N, accumulate ? 1 : 0);
+  GPT_F8_DISPATCH(dq, (run_f8<1>(t, A, lda, B, ldb, M, N, K, K, ep, q, s)),
+                  (run_f8<2>(t, A, lda, B, ldb, M, N, K, K, ep, q, s)));
+  return SplitSum{};
 }
 
 void gemm_nt_store(const Dims& d, int64_t M, int N, int K, const void* A, const void* B,

@@ -1034,6 +1034,70 @@ int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t c
   return launch_status();
 }
 
+static int fp8_gemm_sizes(int32_t wgrad, int64_t M, int64_t N, int64_t K) {
+  if (wgrad != 0 && wgrad != 1) return fail(GPT_E_INVAL, "wgrad must be 0 or 1");
+  if (M < 1 || N < 1 || N % 4 || K < 16 || K % 16 || M > (1 << 24) || N > (1 << 24) ||
+      K > ((int64_t)1 << 30))
+    return fail(GPT_E_INVAL, "M %lld / N %lld / K %lld: need M >= 1, N a multiple of 4, K a multiple of 16",
+                (long long)M, (long long)N, (long long)K);
+  return GPT_OK;
+}
+
+int gpt_fp8_gemm_workspace(int32_t wgrad, int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  g_err[0] = 0;
+  const int st = fp8_gemm_sizes(wgrad, M, N, K);
+  if (st) return st;
+  if (!bytes) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  *bytes = wgrad ? (size_t)part_bytes_f8_wgrad(M, N, K) : 0;
+  return GPT_OK;
+}
+
+int gpt_fp8_gemm(int32_t wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 int32_t fmt_a, const uint8_t* B, int64_t ldb, const uint32_t* amax,
+                 const gpt_fp8_scales* sc, int32_t accumulate, float* C, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int st = fp8_gemm_sizes(wgrad, M, N, K);
+  if (st) return st;
+  if (fmt_a != FP8_E4M3 && fmt_a != FP8_E5M2) return fail(GPT_E_INVAL, "fmt_a %d unknown", fmt_a);
+  if (accumulate != 0 && accumulate != 1) return fail(GPT_E_INVAL, "accumulate must be 0 or 1");
+  if (lda < K || ldb < K || lda % 16 || ldb % 16)
+    return fail(GPT_E_INVAL, "lda %lld / ldb %lld: need multiples of 16, >= K", (long long)lda,
+                (long long)ldb);
+  if (!A || !B || !amax || !sc || !C) return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+  if (sc->axis != 0 && sc->axis != 1) return fail(GPT_E_INVAL, "scales.axis must be 0 or 1");
+  if (sc->nseg < 1 || sc->nseg > 3) return fail(GPT_E_INVAL, "scales.nseg must be 1, 2 or 3");
+  if (sc->nseg == 3 && sc->end[1] < sc->end[0]) return fail(GPT_E_INVAL, "scales.end must ascend");
+  for (int i = 0; i < sc->nseg; ++i)
+    if (sc->slot_a[i] < 0 || sc->slot_b[i] < 0) return fail(GPT_E_INVAL, "amax slots must be >= 0");
+  const size_t need = wgrad ? (size_t)part_bytes_f8_wgrad(M, N, K) : 0;
+  if (need && !workspace) return fail(GPT_E_NULLPTR, "workspace is NULL");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(amax, 4) ||
+      (need && !aligned(workspace, 256)))
+    return fail(GPT_E_ALIGN, "A, B, C need 16-byte alignment, amax 4, workspace 256");
+  if (workspace_bytes < need)
+    return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  Fp8Deq q{};
+  q.amax = amax;
+  q.axis = sc->axis;
+  q.nseg = sc->nseg;
+  q.end[0] = sc->nseg > 1 ? sc->end[0] : INT64_MAX;
+  q.end[1] = sc->nseg > 2 ? sc->end[1] : INT64_MAX;
+  q.end[2] = INT64_MAX;
+  for (int i = 0; i < 3; ++i) {
+    q.sa[i] = sc->slot_a[i < sc->nseg ? i : 0];
+    q.sb[i] = sc->slot_b[i < sc->nseg ? i : 0];
+  }
+  q.fa = fmt_a;
+  q.fb = FP8_E4M3;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch_reset();
+  const SplitSum r = gemm8_product(wgrad != 0, M, N, K, A, lda, B, ldb, q, C, accumulate != 0,
+                                   static_cast<float*>(workspace), (int64_t)workspace_bytes, s);
+  splitk_sum(r, s);
+  return launch_status();
+}
+
 static int decode_validate(int32_t B, int32_t H, int32_t Hk, int32_t D, int32_t Tmax,
                            int32_t window) {
   if (B < 1 || B > 65535) return fail(GPT_E_INVAL, "batch %d not in [1, 65535]", B);

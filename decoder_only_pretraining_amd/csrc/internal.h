@@ -379,5 +379,13 @@ SplitSum gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t 
                      const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
                      float* part, int64_t part_cap, hipStream_t s);
 int64_t part_bytes_f8_wgrad(int64_t M, int64_t N, int64_t K);
+// One fp8 product with an fp32 output C [M][N] (+)= ... on the step's code
+// paths: wgrad = the weight-gradient product (split-K partials in part,
+// at least part_bytes_f8_wgrad(M, N, K) bytes); else the plain product with
+// A's format from dq.fa. Returns the split sum still to be added
+// (splitk_sum).
+SplitSum gemm8_product(bool wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                       const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                       float* part, int64_t part_cap, hipStream_t s);
 
 }  // namespace gpt

@@ -269,6 +269,45 @@ int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t c
                      uint32_t* amax, void* stream);
 
 /*
+ * One product of the fp8 block linears on given codes, with an fp32
+ * output (test support: it pins the fp8 MFMA arithmetic apart from the
+ * quantiser). "Nanochat在nanoGPT之上的新增功能", feature table: dynamic
+ * per-tensor fp8, e4m3 / e5m2; "nanochat — 架构与原理", section 4: the
+ * dequantisation after each scaled matmul.
+ *   C[m][n] (+)= f(m, n) * sum_k a(A[m][k]) b(B[n][k])
+ * with a, b the values of the byte codes (A in fmt_a, B in e4m3), both
+ * operands K-major (A [M][lda], B [N][ldb]), and f = 1 / (s_a * s_b) of the
+ * segment that (m, n) falls in: the segments cut the M (axis 0) or N
+ * (axis 1) index at end[0] and end[1] (nseg of them), segment i takes the
+ * amax slots slot_a[i] and slot_b[i] of `amax` (uint32 bit patterns of
+ * fp32 amax values, as gpt_fp8_quantize writes them), and
+ * s = fmax / amax in fp32 (1 if amax is 0 or not finite; fmax 448 for
+ * e4m3, 57344 for e5m2). Scales that change along K are handled by the
+ * caller: one call per K segment, the later ones with accumulate = 1.
+ *   wgrad = 0: the product the step runs for forward and input-gradient
+ *     linears; wgrad = 1: the weight-gradient product (K = tokens, split
+ *     over workgroups with fp32 partials in `workspace`, then summed in a
+ *     fixed order), which needs gpt_fp8_gemm_workspace bytes (0 for the
+ *     plain product; workspace may then be NULL).
+ *   C (device) fp32 [M][N], written (accumulate = 0) or added to.
+ * K, lda, ldb multiples of 16 with lda, ldb >= K; N a multiple of 4;
+ * A, B, C 16-byte aligned, amax 4, workspace 256. Validation errors return
+ * before anything is enqueued; the work is enqueued on `stream`.
+ */
+typedef struct gpt_fp8_scales {
+  int32_t axis;        /* 0: segments of the M index, 1: of the N index    */
+  int32_t nseg;        /* 1, 2 or 3                                         */
+  int64_t end[2];      /* exclusive ends of segments 0 and 1 (ascending)    */
+  int32_t slot_a[3];   /* amax slot of A in segment i                       */
+  int32_t slot_b[3];   /* amax slot of B in segment i                       */
+} gpt_fp8_scales;
+int gpt_fp8_gemm_workspace(int32_t wgrad, int64_t M, int64_t N, int64_t K, size_t* bytes);
+int gpt_fp8_gemm(int32_t wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                 int32_t fmt_a, const uint8_t* B, int64_t ldb, const uint32_t* amax,
+                 const gpt_fp8_scales* scales, int32_t accumulate, float* C, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
  * Decode attention over a KV cache: the attention step of generating one
  * token per sequence with a pre-allocated cache ("Nanochat在nanoGPT之上的新增
  * 功能", inference engine: KV cache, batch-1 prefill then the cache copied
