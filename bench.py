@@ -29,6 +29,7 @@ import numpy as np  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA (published)
+PEAK_FP8_FLOPS = 5.0e15       # MI355X dense fp8 MFMA (published)
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E (published)
 METRIC = "train tokens/sec (fwd+bwd) d12 seq2048, 1 GPU; MFMA util vs bf16 peak"
 
@@ -72,6 +73,18 @@ def _wgrad_flops(w):
     return w.n_layer * 2.0 * N * (Qkv * C + 2 * F * C + C * Cq)
 
 
+def _block_linear_flops(w):
+    """The six block linears' forward, input-gradient and weight-gradient
+    products of one step (2 FLOPs per multiply-add, 3 products each)."""
+    N = w.batch * w.seq_len
+    C, Cq, Qkv, F = (w.n_embd, w.n_head * w.head_dim,
+                     (w.n_head + 2 * w.n_kv_head) * w.head_dim, w.mlp_hidden)
+    return w.n_layer * 3 * 2.0 * N * (Qkv * C + 2 * F * C + C * Cq)
+
+
+_BLOCK_SITES = ",".join(f"gemm.{m}.{k}" for m in ("qkv", "o", "fc", "mp")
+                        for k in ("fwd", "dgrad", "wgrad"))
+
 ROOF_KERNELS = {
     "wgrad": dict(
         sites="gemm.qkv.wgrad,gemm.fc.wgrad,gemm.mp.wgrad,gemm.o.wgrad",
@@ -79,6 +92,12 @@ ROOF_KERNELS = {
              "splitk_reduce_kernel, is timed apart): gemm_bf16_kernel<256, 256, 64, false, false, 0, "
              "PreId, PreId, EpPart, NoDeq, 8> (8 wavefronts) and <128, 128, ..., EpPart, NoDeq, 4>",
         flops=_wgrad_flops, pmc="profiles/gemm_wgrad_d12_pmc.txt"),
+    # every product of the block linears (with fp8 linears: the fp8 MFMA
+    # products, against the fp8 peak; their quantisation is timed apart)
+    "block_gemm": dict(
+        sites=_BLOCK_SITES, desc="the block linears' products (forward, input gradient, weight "
+                                 "gradient; split-K sums timed apart)",
+        flops=_block_linear_flops, pmc=None, fp8_peak=True),
     "lm_fwd": dict(
         sites="gemm.lm.fwd", desc="lm_head GEMM + tanh softcap epilogue",
         flops=lambda w: 2.0 * w.batch * w.seq_len * w.vocab * w.n_embd, pmc=None),
@@ -145,7 +164,7 @@ def decode_bench(args):
     out = [torch.empty_like(x) for x in q]
     seqlen = torch.full((Bs,), T, dtype=torch.int32, device=dev)
     ws = torch.zeros(max(B.decode_attn_workspace(Bs, H, Hk, D, T, wn) for wn in wins),
-                     dtype=torch.uint8, device=dev)  # chunk counters start at zero
+                     dtype=torch.uint8, device=dev)  # chunk states, written before read
 
     def step():
         stream = torch.cuda.current_stream()
@@ -345,19 +364,22 @@ def main():
         step.run(stream)
     torch.cuda.synchronize()
 
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event before every step and one after the last, on the step's
+    # stream: the whole timed region and each step's time
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     roof_k = ROOF_KERNELS[args.roofline_kernel]
     B.profile_begin(roof_k["sites"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i].record(stream)
         step.run(stream)
-    stop.record(stream)
+    ev[args.steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms, kern_n = B.profile_end()
-    gpu_ms = start.elapsed_time(stop)
+    gpu_ms = ev[0].elapsed_time(ev[args.steps])
+    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     loss = float(step.loss.item())
     assert np.isfinite(loss), loss
@@ -384,9 +406,12 @@ def main():
         if roof_k["pmc"] and w.name == "d12" and not (w.smear or w.backout):
             from decoder_only_pretraining_amd.profiling import traffic_for
             traffic = traffic_for(os.path.join(ROOT, roof_k["pmc"]))
-        roof = {"kernel": roof_k["desc"], "bound": "mfma", "achieved": round(achieved, 1),
-                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                "frac": round(achieved / (PEAK_BF16_FLOPS / 1e12), 4),
+        peak = PEAK_FP8_FLOPS if (roof_k.get("fp8_peak") and w.fp8_linears) else PEAK_BF16_FLOPS
+        roof = {"kernel": roof_k["desc"] + (" in fp8 (e4m3 / e5m2 MFMA)" if peak == PEAK_FP8_FLOPS
+                                            else ""),
+                "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": peak / 1e12, "unit": "TFLOP/s",
+                "frac": round(achieved / (peak / 1e12), 4),
                 "traffic": traffic, "launches": kern_n,
                 "avg_launch_ms": round(kern_ms / kern_n, 4),
                 "algorithmic_flop_per_launch": round(flops / kern_n)}
@@ -395,6 +420,9 @@ def main():
     out = {
         "metric": metric, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_median": round(float(np.median(per_step)), 3),
+        "ms_per_step_p10": round(float(np.percentile(per_step, 10)), 3),
+        "ms_per_step_p90": round(float(np.percentile(per_step, 90)), 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8 linears (e4m3/e5m2), bf16 elsewhere" if w.fp8_linears else "bf16",
         "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) weights)",
