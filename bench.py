@@ -307,6 +307,9 @@ def main():
     ap.add_argument("--fp8", default="auto", choices=["auto", "on", "off"],
                     help="block linears in fp8 (auto: as the workload defines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="enqueue every launch of each call (default: the call's launch sequence "
+                         "is captured once into a HIP graph and replayed, GPT_F_GRAPH)")
     ap.add_argument("--smear", action="store_true", help="the Smear model variant")
     ap.add_argument("--optimizer", action="store_true",
                     help="time the full step with MuonAdamW (4 accumulated calls + optimizer)")
@@ -357,18 +360,28 @@ def main():
         lay = {n: o for n, o, _, _ in B.param_layout(B.make_config(w))}
         params[lay["backout_lambda"]] = 0.5
     tokens, targets = W.split_tokens(W.gen_tokens(w))
-    step = B.Step(w, params, tokens, targets, device="cuda:0")
-    stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
+    graph = not args.no_graph
+    step = B.Step(w, params, tokens, targets, flags=B.GPT_F_GRAPH if graph else 0,
+                  device="cuda:0")
+    # a stream of its own (a HIP graph cannot be captured on the null stream),
+    # after the uploads on the default stream have finished
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    roof_k = ROOF_KERNELS[args.roofline_kernel]
+    for _ in range(args.warmup):   # with the graph: the first call captures it
         step.run(stream)
     torch.cuda.synchronize()
+    # eager launches: the dominant kernel's launches are bracketed by HIP
+    # events on the call's stream inside the timed region; with the graph
+    # they are timed the same way over eager steps right after it (same
+    # buffers and stream; a kernel's duration does not depend on how it was
+    # enqueued)
+    if not graph:
+        B.profile_begin(roof_k["sites"])
 
     # one event before every step and one after the last, on the step's
     # stream: the whole timed region and each step's time
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    roof_k = ROOF_KERNELS[args.roofline_kernel]
-    B.profile_begin(roof_k["sites"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -377,8 +390,13 @@ def main():
     ev[args.steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms, kern_n = B.profile_end()
     gpu_ms = ev[0].elapsed_time(ev[args.steps])
+    steps_timed = args.steps if not graph else min(args.steps, 10)
+    if graph:
+        B.profile_begin(roof_k["sites"])
+        for _ in range(steps_timed):
+            step.run(stream)
+    kern_ms, kern_n = B.profile_end()
     per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     loss = float(step.loss.item())
@@ -391,16 +409,18 @@ def main():
 
     roof = None
     if kern_n > 0 and roof_k.get("bound", "mfma") == "hbm":
-        nbytes = roof_k["bytes"](w) * args.steps
+        nbytes = roof_k["bytes"](w) * steps_timed
         achieved = nbytes / (kern_ms / 1e3) / 1e9
         roof = {"kernel": roof_k["desc"], "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                 "frac": round(achieved / (PEAK_HBM_BYTES / 1e9), 4),
                 "traffic": None, "launches": kern_n,
+                "timed_over": f"{steps_timed} eager steps " + ("after the timed region" if graph
+                                                                else "of the timed region"),
                 "avg_launch_ms": round(kern_ms / kern_n, 4),
                 "algorithmic_bytes_per_launch": round(nbytes / kern_n)}
     elif kern_n > 0:
-        flops = roof_k["flops"](w) * args.steps
+        flops = roof_k["flops"](w) * steps_timed
         achieved = flops / (kern_ms / 1e3) / 1e12
         traffic = None
         if roof_k["pmc"] and w.name == "d12" and not (w.smear or w.backout):
@@ -413,6 +433,8 @@ def main():
                 "peak": peak / 1e12, "unit": "TFLOP/s",
                 "frac": round(achieved / (peak / 1e12), 4),
                 "traffic": traffic, "launches": kern_n,
+                "timed_over": f"{steps_timed} eager steps " + ("after the timed region" if graph
+                                                                else "of the timed region"),
                 "avg_launch_ms": round(kern_ms / kern_n, 4),
                 "algorithmic_flop_per_launch": round(flops / kern_n)}
 
@@ -435,6 +457,7 @@ def main():
                                + (", backout (lambda 0.5)" if w.backout else ""),
                    "seq_len": w.seq_len, "batch": w.batch, "tokens_per_step": ntok,
                    "parallelism": "none (1 GPU)"},
+        "launch": "HIP graph replay of the call (GPT_F_GRAPH)" if graph else "eager",
         "mfma_util_vs_bf16_peak": round(frac, 4),
         "model_mflop_per_token": round(mflop / 1e6, 3),
         "loss": round(loss, 5),

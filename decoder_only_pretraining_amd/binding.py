@@ -22,6 +22,7 @@ GPT_F_CHECK_INPUTS = 8
 GPT_F_SMEAR = 16
 GPT_F_BACKOUT = 32
 GPT_F_REUSE_WEIGHTS = 64
+GPT_F_GRAPH = 128
 
 STATUS = {0: "GPT_OK", -1: "GPT_E_INVAL", -2: "GPT_E_NULLPTR", -3: "GPT_E_ALIGN",
           -4: "GPT_E_WORKSPACE", -5: "GPT_E_UNSUPPORTED", -6: "GPT_E_HIP",
@@ -34,7 +35,7 @@ EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_par
            "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
            "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
            "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd", "gpt_fp8_gemm_workspace",
-           "gpt_fp8_gemm"]
+           "gpt_fp8_gemm", "gpt_graph_cache_clear"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -105,6 +106,7 @@ def lib():
         L.gpt_decode_attn_noalloc.argtypes = [c.c_int32] * 6 + [c.c_void_p] * 6
         L.gpt_attn_fwd.argtypes = [P(GptConfig), c.c_int32] + [c.c_void_p] * 4
         L.gpt_attn_bwd.argtypes = [P(GptConfig), c.c_int32] + [c.c_void_p] * 7
+        L.gpt_graph_cache_clear.argtypes = []
         L.gpt_fp8_gemm_workspace.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64,
                                              P(c.c_size_t)]
         L.gpt_fp8_gemm.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64, c.c_void_p,
@@ -129,7 +131,7 @@ def lib():
                      "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
                      "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
                      "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd",
-                     "gpt_fp8_gemm_workspace", "gpt_fp8_gemm"):
+                     "gpt_fp8_gemm_workspace", "gpt_fp8_gemm", "gpt_graph_cache_clear"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")

@@ -173,7 +173,7 @@ static int validate(const gpt_config* c) {
     return fail(GPT_E_INVAL, "compute_dtype %d unknown", c->compute_dtype);
   if (c->fp8_linears != 0 && c->fp8_linears != 1) return fail(GPT_E_INVAL, "fp8_linears must be 0 or 1");
   if (c->flags & ~(GPT_F_ACCUMULATE | GPT_F_EMBED_NORM | GPT_F_CHECK_FINITE | GPT_F_CHECK_INPUTS |
-                   GPT_F_SMEAR | GPT_F_BACKOUT | GPT_F_REUSE_WEIGHTS))
+                   GPT_F_SMEAR | GPT_F_BACKOUT | GPT_F_REUSE_WEIGHTS | GPT_F_GRAPH))
     return fail(GPT_E_INVAL, "unknown flag bits 0x%x", c->flags);
   if (!(std::isfinite(c->rope_theta) && c->rope_theta > 1.0f))
     return fail(GPT_E_INVAL, "rope_theta must be finite and > 1");
@@ -830,6 +830,93 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
   return launch_status();
 }
 
+// ---------------------------------------------------------------- graph cache
+// GPT_F_GRAPH: one instantiated HIP graph per distinct argument set (the
+// key holds the config and every pointer), least recently used dropped past
+// kMaxGraphs.
+struct GraphCache {
+  std::mutex mu;
+  std::map<std::string, hipGraphExec_t> exec;
+  std::vector<std::string> lru;  // most recent last
+};
+static GraphCache g_graphs;
+static constexpr size_t kMaxGraphs = 64;
+
+static int graph_cache_clear() {
+  std::lock_guard<std::mutex> lk(g_graphs.mu);
+  if (g_graphs.exec.empty()) return GPT_OK;
+  const hipError_t e = hipDeviceSynchronize();
+  for (auto& kv : g_graphs.exec) (void)hipGraphExecDestroy(kv.second);
+  g_graphs.exec.clear();
+  g_graphs.lru.clear();
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s (graph cache)", hipGetErrorString(e));
+  return GPT_OK;
+}
+
+static int run_cached(const gpt_config* cfg, const float* params, const int32_t* tokens,
+                      const int32_t* targets, float* loss, float* grads, void* workspace,
+                      size_t workspace_bytes, void* stream, bool backward) {
+  if (!cfg || !(cfg->flags & GPT_F_GRAPH) || launch_state().dry || g_prof.on)
+    return run(cfg, params, tokens, targets, loss, grads, workspace, workspace_bytes, stream,
+               backward);
+  g_err[0] = 0;
+  if (!stream) return fail(GPT_E_INVAL, "GPT_F_GRAPH needs a stream other than the null stream");
+  if (cfg->flags & (GPT_F_CHECK_FINITE | GPT_F_CHECK_INPUTS))
+    return fail(GPT_E_INVAL, "GPT_F_GRAPH cannot be combined with the debug checks");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s", hipGetErrorString(e));
+  struct {
+    gpt_config cfg;
+    const void* ptr[7];
+    size_t ws;
+    int dev, backward;
+  } key;
+  std::memset(&key, 0, sizeof key);
+  key.cfg = *cfg;
+  const void* ptrs[7] = {params, tokens, targets, loss, grads, workspace, nullptr};
+  for (int i = 0; i < 7; ++i) key.ptr[i] = ptrs[i];
+  key.ws = workspace_bytes;
+  key.dev = dev;
+  key.backward = backward ? 1 : 0;
+  const std::string k(reinterpret_cast<const char*>(&key), sizeof key);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lk(g_graphs.mu);
+  auto it = g_graphs.exec.find(k);
+  if (it == g_graphs.exec.end()) {
+    // capture: validation errors return before any launch, so the capture
+    // is then empty and dropped
+    e = hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s (begin capture)", hipGetErrorString(e));
+    const int st = run(cfg, params, tokens, targets, loss, grads, workspace, workspace_bytes,
+                       stream, backward);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(s, &graph);
+    if (st) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return st;
+    }
+    if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s (end capture)", hipGetErrorString(e));
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s (instantiate)", hipGetErrorString(e));
+    if (g_graphs.exec.size() >= kMaxGraphs) {  // drop the least recently used
+      (void)hipDeviceSynchronize();
+      (void)hipGraphExecDestroy(g_graphs.exec[g_graphs.lru.front()]);
+      g_graphs.exec.erase(g_graphs.lru.front());
+      g_graphs.lru.erase(g_graphs.lru.begin());
+    }
+    it = g_graphs.exec.emplace(k, ex).first;
+  } else {
+    g_graphs.lru.erase(std::find(g_graphs.lru.begin(), g_graphs.lru.end(), k));
+  }
+  g_graphs.lru.push_back(k);
+  e = hipGraphLaunch(it->second, s);
+  if (e != hipSuccess) return fail(GPT_E_HIP, "HIP: %s (graph launch)", hipGetErrorString(e));
+  return GPT_OK;
+}
+
 }  // namespace gpt
 
 using namespace gpt;
@@ -962,13 +1049,20 @@ int gpt_workspace_region(const gpt_config* cfg, const char* name, int32_t layer,
 int gpt_fwd_bwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
                 const int32_t* targets, float* loss, float* grads, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  return run(cfg, params, tokens, targets, loss, grads, workspace, workspace_bytes, stream, true);
+  return run_cached(cfg, params, tokens, targets, loss, grads, workspace, workspace_bytes, stream,
+                    true);
 }
 
 int gpt_fwd(const gpt_config* cfg, const float* params, const int32_t* tokens,
             const int32_t* targets, float* loss, void* workspace, size_t workspace_bytes,
             void* stream) {
-  return run(cfg, params, tokens, targets, loss, nullptr, workspace, workspace_bytes, stream, false);
+  return run_cached(cfg, params, tokens, targets, loss, nullptr, workspace, workspace_bytes, stream,
+                    false);
+}
+
+int gpt_graph_cache_clear(void) {
+  g_err[0] = 0;
+  return graph_cache_clear();
 }
 
 static int attn_args(const gpt_config* cfg, int32_t full, std::initializer_list<const void*> ptrs) {

@@ -82,7 +82,20 @@ enum {
    * in the workspace are reused instead of converted again from the fp32
    * params (fp8 weight codes are still made each call). Undefined results
    * if the params or the workspace changed since. */
-  GPT_F_REUSE_WEIGHTS = 64
+  GPT_F_REUSE_WEIGHTS = 64,
+  /* HIP-graph cache of gpt_fwd_bwd / gpt_fwd: the first call with a given
+   * set of arguments (the config, every pointer, workspace_bytes, the
+   * current device) captures its launch sequence on `stream` into a HIP
+   * graph, which that call and every later call with the same arguments
+   * replays with one hipGraphLaunch on their `stream` (so the host's
+   * per-launch overhead and the gaps between launches go). Buffer contents
+   * may change between calls; the pointers may not. `stream` must not be
+   * the null stream; not with GPT_F_CHECK_FINITE or GPT_F_CHECK_INPUTS
+   * (GPT_E_INVAL). Calls run eagerly (nothing captured or replayed) while
+   * gpt_profile_begin is active and in a dry run. At most 64 graphs are
+   * kept (the least recently used one is dropped after a device
+   * synchronisation); gpt_graph_cache_clear drops them all. */
+  GPT_F_GRAPH = 128
 };
 
 /*
@@ -446,7 +459,8 @@ int gpt_optimizer_step(const gpt_config* cfg, const gpt_optim_hparams* hp, float
  * (amax + codes of an activation or gradient).
  * gpt_profile_end waits for the recorded events, returns the summed
  * kernel time in milliseconds and the number of bracketed launches, and
- * stops recording. Process-wide state: not for concurrent callers.
+ * stops recording. Process-wide state: not for concurrent callers. While
+ * it is active, calls with GPT_F_GRAPH run eagerly.
  */
 int gpt_profile_begin(const char* site_prefix);
 int gpt_profile_end(double* total_ms, int64_t* launches);
@@ -465,6 +479,10 @@ int gpt_profile_end(double* total_ms, int64_t* launches);
  */
 int gpt_debug_launches(int64_t fail_at, int32_t dry_run);
 int gpt_debug_launch_count(int64_t* issued);
+
+/* Drops every cached HIP graph (GPT_F_GRAPH) after synchronising the
+ * device; host only. */
+int gpt_graph_cache_clear(void);
 
 /* Static text for a status code. */
 const char* gpt_status_string(int status);
