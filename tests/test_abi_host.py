@@ -69,7 +69,7 @@ def test_validation_errors():
     bad = [dict(abi_version=7), dict(n_layer=0), dict(n_embd=100), dict(head_dim=96),
            dict(n_kv_head=3), dict(n_head=3, n_kv_head=2), dict(mlp_hidden=100),
            dict(vocab=500), dict(seq_len=0), dict(batch=0), dict(short_window=-1),
-           dict(compute_dtype=5), dict(flags=128), dict(rope_theta=0.5), dict(norm_eps=0.0),
+           dict(compute_dtype=5), dict(flags=256), dict(rope_theta=0.5), dict(norm_eps=0.0),
            dict(softcap=-1.0), dict(fp8_linears=2), dict(n_kv_head=32, n_head=32)]
     for kw in bad:
         assert B.validate(B.make_config(w, **kw)) == -1, kw
