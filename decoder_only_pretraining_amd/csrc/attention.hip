@@ -1073,6 +1073,181 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
   }
 }
 
+// dK, dV with two workgroups per CU (T a multiple of 32): a workgroup of 4
+// wavefronts owns 128 keys of one KV head, 32 per wavefront (its K rows held
+// as fragments; the workgroup's V rows staged once in LDS, XOR-swizzled, and
+// read by rows for dP), and walks the (query head of the group, 32-query
+// tile) steps that see them; Q, dO and the softmax statistics stream through
+// two LDS stages, one step ahead. Against attn_bwd_kv_tiled_kernel (64-query
+// steps, K and V in registers, three stages) a wavefront needs at most 256
+// registers and the workgroup 73 KB of LDS, so two workgroups share a CU
+// and each SIMD runs two wavefronts: one's softmax-gradient arithmetic and
+// LDS waits overlap the other's MFMAs. The arithmetic of a (query, key)
+// pair is the same as in that kernel.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_kv2_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
+    int full, float c2, float scale, int nkt, int nb) {
+  constexpr int BK2 = 128, BQ2 = 32;
+  using DT = Dual<64, D>;                     // layout of the Q / dO tiles (32 of its rows)
+  constexpr int PITCH = DT::PITCH, QEL = BQ2 * PITCH, QCH = QEL * 2 / 1024;
+  static_assert(QEL * 2 % 1024 == 0, "whole 1 KiB chunks per tile");
+  using GV = TileGeom<BK2, D, true>;
+  using LV = DirectLoader<BK2, D, true>;
+  __shared__ __attribute__((aligned(16))) bf16 Vs[GV::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][QEL];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[2][QEL];
+  __shared__ __attribute__((aligned(16))) float st[2][2 * BQ2];
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L = blockIdx.x;
+  const int kt = L / (Hk * nb);  // early keys are seen by the most queries: first
+  const int j = (L % (Hk * nb)) % Hk, b = (L % (Hk * nb)) / Hk;
+  const int G = H / Hk;
+  const int Qkv = (H + 2 * Hk) * D, Cq = H * D;
+  const int64_t rb = (int64_t)b * T_;
+  const int s0 = kt * BK2, sw = s0 + wv * 32, s = sw + (lane & 31);
+
+  const typename DT::Lane lo = DT::lane_offsets(lane);
+  Frag<bf16> kf[D / 16];
+  load_row_frags<bf16, D>(kf, qkv + (rb + s) * Qkv + (H + j) * D, s < T_, lane);
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[i][e] = 0.0f;
+      dv[i][e] = 0.0f;
+    }
+  const unsigned wmax = full ? 0x7fffffffu : (unsigned)W;
+  const int q_hi = full ? T_ : min(T_, s0 + BK2 + W);  // exclusive; queries start at s0
+  const int nq = (q_hi - s0 + BQ2 - 1) / BQ2;
+  const int nstep = G * nq;
+  // a 32-row tile of rows row0.. of a matrix with row stride ld into the
+  // Dual layout (chunks dealt to the 4 wavefronts in turn; slots in the row
+  // padding are not filled); every row lies inside the sequence
+  auto fill_tile = [&](const bf16* p, int64_t ld, int64_t row0, bf16* lds) {
+    for (int c = wv; c < QCH; c += 4) {
+      const int o = c * 1024 + lane * 16;
+      const int t = o / (PITCH * 2), pg = (o % (PITCH * 2)) / 16;
+      const int gi = pg ^ ((t >> 2) & 3);
+      if (gi < D / 8) lds_fill16(p + (row0 + t) * ld + gi * 8, lds_addr(lds) + c * 1024);
+    }
+  };
+  auto issue = [&](int step) {
+    const int h = j * G + step / nq, t0 = s0 + (step % nq) * BQ2;
+    fill_tile(qkv + h * D, Qkv, rb + t0, Qs[step & 1]);
+    fill_tile(gO + h * D, Cq, rb + t0, dOs[step & 1]);
+    if (wv == 0 && lane < 16) {  // 32 floats of lse2, then 32 of delta
+      const int64_t row = ((int64_t)b * H + h) * T_ + t0;
+      const float* src = (lane < 8 ? lse2 : delta) + row + (lane & 7) * 4;
+      lds_fill16(src, lds_addr(st[step & 1]) + lane * 16);
+    }
+  };
+  LV::issue(qkv + (H + Hk + j) * D, Qkv, rb + s0, rb + T_, 0, D, Vs, wv, lane, 4);
+  if (nstep > 0) issue(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+  auto step_fn = [&](int step, auto cur_c) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const int t0 = s0 + (step % nq) * BQ2;
+    if (step + 1 < nstep) issue(step + 1);
+    if (sw < T_ && t0 + 31 >= sw && (full || t0 - (sw + 31) <= W)) {
+      // S = Q K^T and dP = dO V^T of the 32 queries x 32 keys, fragments
+      // read one k-slice ahead
+      f32x16 sa, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sa[e] = 0.0f;
+        dp[e] = 0.0f;
+      }
+      Frag<bf16> qa[2], da[2], va[2];
+      DT::row_frag(qa[0], Qs[CUR], lo, 0, 0);
+      DT::row_frag(da[0], dOs[CUR], lo, 0, 0);
+      read_frag<BK2, D, true>(va[0], Vs, wv * 32, 0, lane);
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const int p = kc & 1;
+        if (kc + 1 < D / 16) {
+          DT::row_frag(qa[p ^ 1], Qs[CUR], lo, 0, kc + 1);
+          DT::row_frag(da[p ^ 1], dOs[CUR], lo, 0, kc + 1);
+          read_frag<BK2, D, true>(va[p ^ 1], Vs, wv * 32, kc + 1, lane);
+        }
+        mfma(sa, qa[p], kf[kc]);
+        mfma(dp, da[p], va[p]);
+      }
+      // P and dS in place: accumulator rows t0 + 8 (e/4) + 4 hi + e%4 are
+      // queries, so each group of four reads one vector of statistics
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int tl = g * 8 + hi * 4;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&st[CUR][tl]);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&st[CUR][BQ2 + tl]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          const float pr = exp2_fast(fmaf(sa[e], c2, -lv[r]));
+          sa[e] = pr;
+          dp[e] = pr * (dp[e] - dv4[r]);
+        }
+      }
+      if (!(t0 >= sw + 31 && (full || t0 + 31 - sw <= W))) {
+        asm volatile("" ::: "memory");  // keep the mask on its own branch
+        // query t0 + 8 (e/4) + 4 hi + e%4 sees key s iff 0 <= t - s <= W
+        const int u = t0 + 4 * hi - s;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = (e >> 2) * 8 + (e & 3);
+          if ((unsigned)(u + r) > wmax) {
+            sa[e] = 0.0f;
+            dp[e] = 0.0f;
+          }
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q over the 32 queries (two 16-query
+      // slices in the accumulator's row order)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag<bf16> pf, dsf;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          frag_set(pf, jj, sa[8 * c + jj]);
+          frag_set(dsf, jj, dp[8 * c + jj]);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          Frag<bf16> doT, qT;
+          DT::tr_frag(doT, dOs[CUR], lo, 16 * c, db * 32);
+          DT::tr_frag(qT, Qs[CUR], lo, 16 * c, db * 32);
+          mfma(dv[db], doT, pf);
+          mfma(dk[db], qT, dsf);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next step's tiles landed
+    __syncthreads();
+  };
+  for (int step = 0; step < nstep; step += 2) {
+    step_fn(step, std::integral_constant<int, 0>{});
+    if (step + 1 < nstep) step_fn(step + 1, std::integral_constant<int, 1>{});
+  }
+  if (s < T_) {
+    bf16* kp = gqkv + (rb + s) * Qkv + (H + j) * D;
+    bf16* vp = gqkv + (rb + s) * Qkv + (H + Hk + j) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + g * 8 + hi * 4;
+        store_col4<bf16>(kp + d, dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale,
+                         dk[db][4 * g + 2] * scale, dk[db][4 * g + 3] * scale);
+        store_col4<bf16>(vp + d, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2],
+                         dv[db][4 * g + 3]);
+      }
+  }
+}
+
 // dQ: a workgroup of 8 wavefronts owns 256 queries of one head (32 per
 // wavefront, Q and dO rows held as fragments) and walks the visible 64-key
 // tiles; K (read by rows and transposed) and V (read by rows) stream
@@ -1278,6 +1453,26 @@ void bwd(const gpt::Dims& d, bool full, const void* qkv, const void* gO, const f
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),                           \
                      static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H, \
                      d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B)
+    if constexpr (D == 128) {
+      if (d.T % 32 == 0) {
+        const int nkt2 = (d.T + 127) / 128;
+        GK_LAUNCH((attn_bwd_kv2_kernel<D>), dim3((unsigned)(nkt2 * d.Hk * d.B)), dim3(256), 0, s,
+                  static_cast<const bf16*>(qkv), static_cast<const bf16*>(gO), lse, delta,
+                  static_cast<bf16*>(gqkv), d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2, scale, nkt2,
+                  d.B);
+        if (d.T % 64 == 0)
+          GK_LAUNCH((attn_bwd_q_tiled_kernel<D, NW, true, 2>), dim3((unsigned)(nq * d.H * d.B)),
+                    dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
+                    static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
+                    d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B);
+        else
+          GK_LAUNCH((attn_bwd_q_tiled_kernel<D, NW, false, 3>), dim3((unsigned)(nq * d.H * d.B)),
+                    dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
+                    static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
+                    d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B);
+        return;
+      }
+    }
     if (d.T % 64 == 0) {
       GPT_ATTN_BWD(true);
     } else {
