@@ -1124,35 +1124,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int q_hi = full ? T_ : min(T_, s0 + BK2 + W);  // exclusive; queries start at s0
   const int nq = (q_hi - s0 + BQ2 - 1) / BQ2;
   const int nstep = G * nq;
-  // a 32-row tile of rows row0.. of a matrix with row stride ld into the
-  // Dual layout (chunks dealt to the 4 wavefronts in turn; slots in the row
-  // padding are not filled); every row lies inside the sequence
-  auto fill_tile = [&](const bf16* p, int64_t ld, int64_t row0, bf16* lds) {
-    for (int c = wv; c < QCH; c += 4) {
-      const int o = c * 1024 + lane * 16;
-      const int t = o / (PITCH * 2), pg = (o % (PITCH * 2)) / 16;
+  // Fills of a 32-row tile into the Dual layout: the 1 KiB chunks are dealt
+  // to the 4 wavefronts in turn (chunk wv + 4 q); each lane's byte offset
+  // from the tile's first element is computed once per matrix (~0u: a slot
+  // in the row padding), so a fill is one load per chunk from a
+  // wavefront-uniform base. Every row lies inside the sequence.
+  constexpr int NQC = (QCH + 3) / 4;
+  auto tile_offs = [&](int64_t ld, uint32_t (&o)[NQC]) {
+#pragma unroll
+    for (int q = 0; q < NQC; ++q) {
+      const int c = wv + 4 * q;
+      const int ob = c * 1024 + lane * 16;
+      const int t = ob / (PITCH * 2), pg = (ob % (PITCH * 2)) / 16;
       const int gi = pg ^ ((t >> 2) & 3);
-      if (gi < D / 8) lds_fill16(p + (row0 + t) * ld + gi * 8, lds_addr(lds) + c * 1024);
+      o[q] = (c < QCH && gi < D / 8) ? (uint32_t)((t * ld + gi * 8) * 2) : ~0u;
     }
   };
-  auto issue = [&](int step) {
-    const int h = j * G + step / nq, t0 = s0 + (step % nq) * BQ2;
-    fill_tile(qkv + h * D, Qkv, rb + t0, Qs[step & 1]);
-    fill_tile(gO + h * D, Cq, rb + t0, dOs[step & 1]);
+  uint32_t oq[NQC], od[NQC];
+  tile_offs(Qkv, oq);
+  tile_offs(Cq, od);
+  auto fill_tile = [&](const bf16* tile, const uint32_t (&o)[NQC], bf16* lds) {
+#pragma unroll
+    for (int q = 0; q < NQC; ++q)
+      if (o[q] != ~0u) lds_fill16(tile, o[q], lds_addr(lds) + (wv + 4 * q) * 1024);
+  };
+  // the step after (h, qi): the query tiles of one head, then the next head
+  int ih = 0, iq = 0;  // head index in the group and query tile of the next fill
+  auto issue = [&](int buf) {
+    const int h = j * G + ih, t0 = s0 + iq * BQ2;
+    fill_tile(qkv + (rb + t0) * Qkv + h * D, oq, Qs[buf]);
+    fill_tile(gO + (rb + t0) * Cq + h * D, od, dOs[buf]);
     if (wv == 0 && lane < 16) {  // 32 floats of lse2, then 32 of delta
       const int64_t row = ((int64_t)b * H + h) * T_ + t0;
       const float* src = (lane < 8 ? lse2 : delta) + row + (lane & 7) * 4;
-      lds_fill16(src, lds_addr(st[step & 1]) + lane * 16);
+      lds_fill16(src, lds_addr(st[buf]) + lane * 16);
+    }
+    if (++iq == nq) {
+      iq = 0;
+      ++ih;
     }
   };
   LV::issue(qkv + (H + Hk + j) * D, Qkv, rb + s0, rb + T_, 0, D, Vs, wv, lane, 4);
   if (nstep > 0) issue(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
+  int cq = 0;  // query tile of the current step
   auto step_fn = [&](int step, auto cur_c) {
     constexpr int CUR = decltype(cur_c)::value;
-    const int t0 = s0 + (step % nq) * BQ2;
-    if (step + 1 < nstep) issue(step + 1);
+    const int t0 = s0 + cq * BQ2;
+    if (++cq == nq) cq = 0;
+    if (step + 1 < nstep) issue(CUR ^ 1);
     if (sw < T_ && t0 + 31 >= sw && (full || t0 - (sw + 31) <= W)) {
       // S = Q K^T and dP = dO V^T of the 32 queries x 32 keys, fragments
       // read one k-slice ahead
