@@ -35,7 +35,7 @@ EXPORTS = ["gpt_abi_version", "gpt_config_validate", "gpt_param_count", "gpt_par
            "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
            "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
            "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd", "gpt_fp8_gemm_workspace",
-           "gpt_fp8_gemm", "gpt_graph_cache_clear"]
+           "gpt_fp8_gemm", "gpt_graph_cache_clear", "gpt_bf16_gemm_workspace", "gpt_bf16_gemm"]
 FP8_E4M3, FP8_E5M2 = 0, 1
 
 
@@ -113,6 +113,11 @@ def lib():
                                    c.c_int64, c.c_int32, c.c_void_p, c.c_int64, c.c_void_p,
                                    P(Fp8Scales), c.c_int32, c.c_void_p, c.c_void_p, c.c_size_t,
                                    c.c_void_p]
+        L.gpt_bf16_gemm_workspace.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64,
+                                              P(c.c_size_t)]
+        L.gpt_bf16_gemm.argtypes = [c.c_int32, c.c_int64, c.c_int64, c.c_int64, c.c_void_p,
+                                    c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_size_t,
+                                    c.c_void_p]
         L.gpt_optim_workspace_size.argtypes = [P(GptConfig), P(c.c_size_t)]
         L.gpt_optimizer_step.argtypes = [P(GptConfig), P(OptimHparams)] + [c.c_void_p] * 4 + [
             c.c_size_t, c.c_void_p]
@@ -131,7 +136,8 @@ def lib():
                      "gpt_decode_attn", "gpt_kv_cache_append", "gpt_optim_workspace_size",
                      "gpt_optimizer_step", "gpt_debug_launches", "gpt_debug_launch_count",
                      "gpt_decode_attn_noalloc", "gpt_attn_fwd", "gpt_attn_bwd",
-                     "gpt_fp8_gemm_workspace", "gpt_fp8_gemm", "gpt_graph_cache_clear"):
+                     "gpt_fp8_gemm_workspace", "gpt_fp8_gemm", "gpt_graph_cache_clear",
+                     "gpt_bf16_gemm_workspace", "gpt_bf16_gemm"):
             getattr(L, name).restype = c.c_int
         if L.gpt_abi_version() != GPT_ABI_VERSION:
             raise RuntimeError("libgptstep.so ABI version mismatch")
@@ -273,6 +279,23 @@ def fp8_gemm(wgrad, A, lda, fmt_a, B, ldb, amax, scales, C, M, N, K, accumulate=
                             amax.data_ptr(), ctypes.byref(scales), int(accumulate), C.data_ptr(),
                             ws.data_ptr(), n.value, _stream_ptr(stream))
     _check("gpt_fp8_gemm", st)
+    return ws
+
+
+GEMM_NT, GEMM_NT_SPLITK, GEMM_WGRAD = 0, 1, 2
+
+
+def bf16_gemm(kind, A, B, C, M, N, K, accumulate=False, stream=None):
+    """gpt_bf16_gemm on device tensors (A, B bf16, C fp32 [M, N]); allocates
+    the split-K partials itself and returns them."""
+    import torch
+    n = ctypes.c_size_t()
+    _check("gpt_bf16_gemm_workspace", lib().gpt_bf16_gemm_workspace(kind, M, N, K,
+                                                                    ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=C.device)
+    st = lib().gpt_bf16_gemm(kind, M, N, K, A.data_ptr(), B.data_ptr(), int(accumulate),
+                             C.data_ptr(), ws.data_ptr(), n.value, _stream_ptr(stream))
+    _check("gpt_bf16_gemm", st)
     return ws
 
 

@@ -1192,6 +1192,77 @@ int gpt_fp8_gemm(int32_t wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* 
   return launch_status();
 }
 
+// The bf16 products of the step on their own: the K-major product of the
+// forward and input-gradient GEMMs with an fp32 result, its split-K form for
+// long contractions, and the weight-gradient product (split-K partials
+// summed in split order), each with the tile and split plan the step uses.
+static int bf16_gemm_sizes(int32_t kind, int64_t M, int64_t N, int64_t K) {
+  if (kind < 0 || kind > 2) return fail(GPT_E_INVAL, "kind %d: need 0, 1 or 2", kind);
+  if (M < 1 || M > (1 << 24) || N < 64 || N % 64 || N > (1 << 24))
+    return fail(GPT_E_INVAL, "M %lld / N %lld: need M >= 1, N a multiple of 64", (long long)M,
+                (long long)N);
+  if (kind == 2) {
+    if (M % 64 || K < 1 || K > ((int64_t)1 << 30))
+      return fail(GPT_E_INVAL, "weight gradient M %lld / K %lld: need M a multiple of 64, K >= 1",
+                  (long long)M, (long long)K);
+  } else if (K < 64 || K % 64 || K > ((int64_t)1 << 30)) {
+    return fail(GPT_E_INVAL, "K %lld: need a multiple of 64", (long long)K);
+  }
+  return GPT_OK;
+}
+
+static int64_t bf16_gemm_need(int32_t kind, int64_t M, int64_t N, int64_t K) {
+  Dims d{};
+  d.bf16 = true;
+  if (kind == 1) return part_bytes_nn_splitk(d, M, N, K);
+  if (kind == 2) return part_bytes_tn_wgrad(d, M, N, K);
+  return 0;
+}
+
+int gpt_bf16_gemm_workspace(int32_t kind, int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  g_err[0] = 0;
+  const int st = bf16_gemm_sizes(kind, M, N, K);
+  if (st) return st;
+  if (!bytes) return fail(GPT_E_NULLPTR, "output pointer is NULL");
+  *bytes = (size_t)bf16_gemm_need(kind, M, N, K);
+  return GPT_OK;
+}
+
+int gpt_bf16_gemm(int32_t kind, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                  int32_t accumulate, float* C, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  g_err[0] = 0;
+  const int st = bf16_gemm_sizes(kind, M, N, K);
+  if (st) return st;
+  if (accumulate != 0 && accumulate != 1) return fail(GPT_E_INVAL, "accumulate must be 0 or 1");
+  if (accumulate && kind != 2)
+    return fail(GPT_E_INVAL, "accumulate: only the weight-gradient product (kind 2) adds into C");
+  if (!A || !B || !C) return fail(GPT_E_NULLPTR, "a required pointer is NULL");
+  const size_t need = (size_t)bf16_gemm_need(kind, M, N, K);
+  if (need && !workspace) return fail(GPT_E_NULLPTR, "workspace is NULL");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || (need && !aligned(workspace, 256)))
+    return fail(GPT_E_ALIGN, "A, B, C need 16-byte alignment, workspace 256");
+  if (workspace_bytes < need)
+    return fail(GPT_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  Dims d{};
+  d.bf16 = true;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(workspace);
+  launch_reset();
+  if (kind == 0) {
+    gemm_nn_f32(d, M, (int)N, (int)K, A, nullptr, C, s, B);
+  } else if (kind == 1) {
+    splitk_sum(gemm_nn_f32_splitk(d, M, (int)N, (int)K, A, nullptr, C, part,
+                                  (int64_t)workspace_bytes, s, B),
+               s);
+  } else {
+    splitk_sum(gemm_tn_wgrad(d, (int)M, (int)N, K, A, B, C, accumulate != 0, part,
+                             (int64_t)workspace_bytes, s),
+               s);
+  }
+  return launch_status();
+}
+
 static int decode_validate(int32_t B, int32_t H, int32_t Hk, int32_t D, int32_t Tmax,
                            int32_t window) {
   if (B < 1 || B > 65535) return fail(GPT_E_INVAL, "batch %d not in [1, 65535]", B);

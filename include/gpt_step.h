@@ -321,6 +321,33 @@ int gpt_fp8_gemm(int32_t wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* 
                  size_t workspace_bytes, void* stream);
 
 /*
+ * The bf16 products of the step on their own, for element-wise tests of the
+ * GEMM core (each runs the tiles, K-major or transposing operand paths and
+ * split plan that the step uses for a product of that shape; the products
+ * are the linear maps of the model, "Nanochat在nanoGPT之上的新增功能",
+ * section 1 table: bias-free linears, untied lm_head):
+ *   kind 0: C[M][N] = sum_k A[m][k] B[n][k]; A [M][K], B [N][K], both
+ *           contraction-contiguous (the forward products, and the input
+ *           gradients on the transposed weight copy);
+ *   kind 1: the same product for a long contraction (the lm_head input
+ *           gradient), split over K into fp32 partials added in split order
+ *           when the plan splits it (gpt_bf16_gemm_workspace bytes);
+ *   kind 2: C[M][N] (+)= sum_k A[k][m] B[k][n]; A [K][M], B [K][N] with K
+ *           the tokens (the weight gradients), split over K as the step
+ *           plans it, partials added in split order.
+ *   A, B (device) bf16; C (device) fp32 [M][N], written (accumulate = 0) or,
+ *   for kind 2 only, added to (accumulate = 1).
+ * M >= 1 and N a multiple of 64; kinds 0 and 1: K a multiple of 64; kind 2:
+ * M a multiple of 64, K >= 1. A, B, C 16-byte aligned, workspace 256 (may be
+ * NULL when gpt_bf16_gemm_workspace reports 0). Validation errors return
+ * before anything is enqueued; the work is enqueued on `stream`.
+ */
+int gpt_bf16_gemm_workspace(int32_t kind, int64_t M, int64_t N, int64_t K, size_t* bytes);
+int gpt_bf16_gemm(int32_t kind, int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                  int32_t accumulate, float* C, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
  * Decode attention over a KV cache: the attention step of generating one
  * token per sequence with a pre-allocated cache ("Nanochat在nanoGPT之上的新增
  * 功能", inference engine: KV cache, batch-1 prefill then the cache copied

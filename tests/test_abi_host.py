@@ -183,6 +183,23 @@ def test_fp8_quantize_rejects_bad_arguments_before_any_launch():
     assert q(p, 0, 4, 64, 0, ctypes.c_void_p(4104), None, 0, p, None) == -3
 
 
+def test_bf16_gemm_rejects_bad_arguments_before_any_launch():
+    L = B.lib()
+    p = ctypes.c_void_p(4096)
+    n = ctypes.c_size_t()
+    g = L.gpt_bf16_gemm
+    assert L.gpt_bf16_gemm_workspace(3, 64, 64, 64, ctypes.byref(n)) == -1   # kind
+    assert L.gpt_bf16_gemm_workspace(0, 64, 96, 64, ctypes.byref(n)) == -1   # N % 64
+    assert L.gpt_bf16_gemm_workspace(0, 64, 64, 32, ctypes.byref(n)) == -1   # K % 64
+    assert L.gpt_bf16_gemm_workspace(2, 96, 64, 5, ctypes.byref(n)) == -1    # wgrad M % 64
+    assert L.gpt_bf16_gemm_workspace(0, 64, 64, 64, None) == -2
+    assert g(0, 64, 64, 64, None, p, 0, p, None, 0, None) == -2
+    assert g(0, 64, 64, 64, p, p, 1, p, None, 0, None) == -1                 # accumulate, kind 0
+    assert g(0, 64, 64, 64, ctypes.c_void_p(4100), p, 0, p, None, 0, None) == -3
+    assert L.gpt_bf16_gemm_workspace(2, 3072, 768, 16384, ctypes.byref(n)) == 0 and n.value > 0
+    assert g(2, 3072, 768, 16384, p, p, 0, p, p, n.value - 1, None) == -4
+
+
 def test_decode_attn_validation_and_workspace():
     L = B.lib()
     # chunks of 128 visible positions per (sequence, KV head); one chunk: none

@@ -1,0 +1,149 @@
+"""The bf16 products of the step on their own (gpt_bf16_gemm), element by
+element against the exact float64 product of the same bf16 values. The
+model's linears are bias-free matrix products ("Nanochat在nanoGPT之上的新增
+功能", section 1 table: no biases, untied lm_head), so the reference is the
+product's definition: C[m][n] = sum_k a_k b_k.
+
+Bound, from the arithmetic: a product of two bf16 values is exact in fp32,
+and fp32 accumulation of the K products (in MFMA blocks, then over split-K
+partials added in split order) rounds at most K + splits times, so
+  |C - C_ref| <= 2^-24 (K + 2 + splits) sum_k |a_k b_k|
+plus 2^-24 |C0| when the weight-gradient product adds into C0.
+
+Each shape also runs on small integer values (|a|, |b| <= 4): every
+product and every partial sum is then an integer below 2^24, exact in fp32
+in any order, so the result must equal the exact product bit for bit — a
+dropped or repeated contraction chunk, a wrong tile offset or a transposed
+operand cannot hide inside the rounding bound.
+
+Shapes: the d12 step's products at full size (16,384 tokens: forward and
+input-gradient GEMMs as kind 0, the lm_head input gradient's 32,768-long
+contraction as kind 1, the weight gradients over 16,384 tokens as kind 2),
+checked on every column of one sampled row per 256-row block (and the
+first and last rows), after C was filled with NaN so
+an element the kernels never write fails; plus ragged shapes that end
+inside tiles, checked in full."""
+import numpy as np
+import pytest
+
+from decoder_only_pretraining_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(rng, shape, ints=False):
+    """N(0, 1) values rounded to bf16, or integers in [-4, 4]: (device tensor,
+    float64 copy)."""
+    import torch
+    v = (rng.integers(-4, 5, size=shape).astype(np.float32) if ints
+         else rng.standard_normal(shape, dtype=np.float32))
+    x = torch.from_numpy(v).bfloat16()
+    return x.cuda(), x.float().numpy().astype(np.float64)
+
+
+def _check(got, ref, absum, K, splits, what, c0=None, exact=False):
+    if exact:
+        assert np.all(np.isfinite(got)), (what, "unwritten or non-finite output")
+        diff = np.nonzero(got.astype(np.float64) != ref)
+        assert diff[0].size == 0, (what, "differs from the exact product at", diff[0][0],
+                                   diff[1][0], float(got[diff][0]), float(ref[diff][0]))
+        return
+    bound = 2.0 ** -24 * (K + 2 + splits) * absum
+    if c0 is not None:
+        bound = bound + 2.0 ** -24 * np.abs(c0)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(np.isfinite(got)), (what, "unwritten or non-finite output")
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (what, float(err[worst]), float(bound[worst]), worst)
+
+
+def _rows(rng, M, full_below=512):
+    """Every row of a small output; otherwise the first and last row and one
+    random row in each block of 256 rows (every row tile of the product)."""
+    if M <= full_below:
+        return np.arange(M)
+    starts = np.arange(0, M, 256)
+    pick = np.minimum(starts + rng.integers(0, 256, size=starts.size), M - 1)
+    return np.unique(np.concatenate([pick, [0, M - 1]]))
+
+
+def _splits(kind, M, N, K):
+    """Upper bound on the number of K splits (the workspace holds one fp32
+    partial of C per split)."""
+    import ctypes
+    n = ctypes.c_size_t()
+    assert B.lib().gpt_bf16_gemm_workspace(kind, M, N, K, ctypes.byref(n)) == 0
+    return max(1, n.value // (M * N * 4))
+
+
+NT = [(16384, 768, 2304, "QKV input gradient"), (16384, 3072, 768, "c_fc forward"),
+      (16384, 768, 768, "o-proj forward"), (16384, 2304, 768, "QKV forward"),
+      (300, 192, 512, "ragged"), (77, 64, 64, "one tile, ragged")]
+
+
+@pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
+@pytest.mark.parametrize("M,N,K,what", NT)
+def test_bf16_nt_product(M, N, K, what, ints):
+    import torch
+    rng = np.random.default_rng(7000 + M + N + K + ints)
+    A, A64 = _bf16(rng, (M, K), ints)
+    Bm, B64 = _bf16(rng, (N, K), ints)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    B.bf16_gemm(B.GEMM_NT, A, Bm, C, M, N, K)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    rows = _rows(rng, M)
+    _check(got[rows], A64[rows] @ B64.T, np.abs(A64[rows]) @ np.abs(B64).T, K, 0,
+           f"nt {what}", exact=ints)
+    assert np.all(np.isfinite(got)), "an output element was not written"
+
+
+@pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
+@pytest.mark.parametrize("M,N,K", [(2048, 768, 32768), (300, 128, 8192), (256, 64, 4096)])
+def test_bf16_long_contraction(M, N, K, ints):
+    import torch
+    rng = np.random.default_rng(7100 + M + N + K + ints)
+    A, A64 = _bf16(rng, (M, K), ints)
+    Bm, B64 = _bf16(rng, (N, K), ints)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    B.bf16_gemm(B.GEMM_NT_SPLITK, A, Bm, C, M, N, K)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    rows = _rows(rng, M)
+    _check(got[rows], A64[rows] @ B64.T, np.abs(A64[rows]) @ np.abs(B64).T, K,
+           _splits(B.GEMM_NT_SPLITK, M, N, K), "long contraction", exact=ints)
+    assert np.all(np.isfinite(got))
+
+
+WG = [(2304, 768, 16384, False), (3072, 768, 16384, False), (768, 3072, 16384, False),
+      (768, 768, 16384, True), (192, 128, 300, False), (192, 128, 300, True), (64, 64, 1, True)]
+
+
+@pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
+@pytest.mark.parametrize("M,N,K,acc", WG)
+def test_bf16_weight_gradient(M, N, K, acc, ints):
+    import torch
+    rng = np.random.default_rng(7200 + M + N + K + acc + 2 * ints)
+    A, A64 = _bf16(rng, (K, M), ints)
+    Bm, B64 = _bf16(rng, (K, N), ints)
+    if acc:
+        c0 = (rng.integers(-100, 101, size=(M, N)).astype(np.float32) if ints
+              else rng.standard_normal((M, N), dtype=np.float32))
+        C = torch.from_numpy(c0).cuda()
+    else:
+        c0 = None
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    B.bf16_gemm(B.GEMM_WGRAD, A, Bm, C, M, N, K, accumulate=acc)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    rows = _rows(rng, M, 256)
+    ref = A64[:, rows].T @ B64
+    absum = np.abs(A64[:, rows]).T @ np.abs(B64)
+    base = None
+    if acc:
+        base = c0[rows].astype(np.float64)
+        ref = ref + base
+    _check(got[rows], ref, absum, K, _splits(B.GEMM_WGRAD, M, N, K), "weight gradient", base,
+           exact=ints)
+    assert np.all(np.isfinite(got))
+
