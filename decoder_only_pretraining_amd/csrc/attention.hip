@@ -1084,24 +1084,35 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_kv_tiled_kernel(
 // and each SIMD runs two wavefronts: one's softmax-gradient arithmetic and
 // LDS waits overlap the other's MFMAs. The arithmetic of a (query, key)
 // pair is the same as in that kernel.
+// LDS of one dK/dV workgroup: the V rows, two stages of Q and dO tiles and
+// their statistics.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_kv2_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
-    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
-    int full, float c2, float scale, int nkt, int nb) {
-  constexpr int BK2 = 128, BQ2 = 32;
+struct Kv2Lds {
+  static constexpr int BK2 = 128, BQ2 = 32;
+  static constexpr int QEL = BQ2 * Dual<64, D>::PITCH;
+  static constexpr int V_BYTES = (TileGeom<BK2, D, true>::ELEMS * 2 + 15) / 16 * 16;
+  static constexpr int Q_OFF = V_BYTES, DO_OFF = Q_OFF + 2 * QEL * 2, ST_OFF = DO_OFF + 2 * QEL * 2;
+  static constexpr int BYTES = ST_OFF + 2 * 2 * BQ2 * 4;
+};
+
+// Workgroup L of the dK/dV pass (see attn_bwd_kv2_kernel), on the LDS `smem`.
+template <int D>
+__device__ __forceinline__ void attn_bwd_kv2_body(
+    char* smem, int L, const bf16* __restrict__ qkv, const bf16* __restrict__ gO,
+    const float* __restrict__ lse2, const float* __restrict__ delta, bf16* __restrict__ gqkv,
+    int T_, int H, int Hk, int W, int full, float c2, float scale, int nb) {
+  using LY = Kv2Lds<D>;
+  constexpr int BK2 = LY::BK2, BQ2 = LY::BQ2;
   using DT = Dual<64, D>;                     // layout of the Q / dO tiles (32 of its rows)
-  constexpr int PITCH = DT::PITCH, QEL = BQ2 * PITCH, QCH = QEL * 2 / 1024;
+  constexpr int PITCH = DT::PITCH, QEL = LY::QEL, QCH = QEL * 2 / 1024;
   static_assert(QEL * 2 % 1024 == 0, "whole 1 KiB chunks per tile");
-  using GV = TileGeom<BK2, D, true>;
   using LV = DirectLoader<BK2, D, true>;
-  __shared__ __attribute__((aligned(16))) bf16 Vs[GV::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][QEL];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[2][QEL];
-  __shared__ __attribute__((aligned(16))) float st[2][2 * BQ2];
+  bf16* const Vs = reinterpret_cast<bf16*>(smem);
+  bf16(*const Qs)[QEL] = reinterpret_cast<bf16(*)[QEL]>(smem + LY::Q_OFF);
+  bf16(*const dOs)[QEL] = reinterpret_cast<bf16(*)[QEL]>(smem + LY::DO_OFF);
+  float(*const st)[2 * BQ2] = reinterpret_cast<float(*)[2 * BQ2]>(smem + LY::ST_OFF);
   const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int L = blockIdx.x;
   const int kt = L / (Hk * nb);  // early keys are seen by the most queries: first
   const int j = (L % (Hk * nb)) % Hk, b = (L % (Hk * nb)) / Hk;
   const int G = H / Hk;
@@ -1269,16 +1280,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_kv2_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
+    int full, float c2, float scale, int nb) {
+  __shared__ __attribute__((aligned(16))) char smem[Kv2Lds<D>::BYTES];
+  attn_bwd_kv2_body<D>(smem, (int)blockIdx.x, qkv, gO, lse2, delta, gqkv, T_, H, Hk, W, full, c2,
+                       scale, nb);
+}
+
+
 // dQ: a workgroup of 8 wavefronts owns 256 queries of one head (32 per
 // wavefront, Q and dO rows held as fragments) and walks the visible 64-key
 // tiles; K (read by rows and transposed) and V (read by rows) stream
 // through three LDS stages, two tiles ahead.
+// LDS of one dQ workgroup: S stages of V and K tiles.
+template <int D, int S>
+struct QLds {
+  static constexpr int BKV = 64;
+  static constexpr int K_ELEMS = Dual<BKV, D>::ELEMS, V_ELEMS = TileGeom<BKV, D, true>::ELEMS;
+  static constexpr int K_OFF = (S * V_ELEMS * 2 + 15) / 16 * 16;
+  static constexpr int BYTES = K_OFF + S * K_ELEMS * 2;
+};
+
+// Workgroup L of the dQ pass (see attn_bwd_q_tiled_kernel), on the LDS `smem`.
 template <int D, int NW, bool ALIGNED, int S>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(S == 2 ? 2 : 1, S == 2 ? 2 : 1))) void attn_bwd_q_tiled_kernel(
-    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
-    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
-    int full, float c2, float scale, int nq, int nb) {
-  constexpr int BQ = 32 * NW, BKV = 64;
+__device__ __forceinline__ void attn_bwd_q_body(
+    char* smem, int L, const bf16* __restrict__ qkv, const bf16* __restrict__ gO,
+    const float* __restrict__ lse2, const float* __restrict__ delta, bf16* __restrict__ gqkv,
+    int T_, int H, int Hk, int W, int full, float c2, float scale, int nq, int nb) {
+  constexpr int BQ = 32 * NW, BKV = QLds<D, S>::BKV;
   static_assert(S == 2 || S == 3, "two or three stages");
   using DK = Dual<BKV, D>;
   using GV = TileGeom<BKV, D, true>;
@@ -1286,12 +1318,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(S == 2 
   static_assert(LV::CHUNKS % 4 == 0, "whole chunks per loading wavefront");
   constexpr int PER_WAVE = DK::CHUNKS / 4 + LV::CHUNKS / 4;
   static_assert(PER_WAVE < 16, "vmcnt field");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[S][DK::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[S][GV::ELEMS];
+  bf16(*const Vs)[GV::ELEMS] = reinterpret_cast<bf16(*)[GV::ELEMS]>(smem);
+  bf16(*const Ks)[DK::ELEMS] = reinterpret_cast<bf16(*)[DK::ELEMS]>(smem + QLds<D, S>::K_OFF);
   const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS fill addresses in SGPRs
   const bool loader = wv < 4;
-  const int L = blockIdx.x;
   const int qt = nq - 1 - L / (H * nb);
   const int h = (L % (H * nb)) % H, b = (L % (H * nb)) / H;
   const int j = h / (H / Hk);
@@ -1434,6 +1465,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(S == 2 
   }
 }
 
+template <int D, int NW, bool ALIGNED, int S>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(S == 2 ? 2 : 1, S == 2 ? 2 : 1))) void attn_bwd_q_tiled_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
+    int full, float c2, float scale, int nq, int nb) {
+  __shared__ __attribute__((aligned(16))) char smem[QLds<D, S>::BYTES];
+  attn_bwd_q_body<D, NW, ALIGNED, S>(smem, (int)blockIdx.x, qkv, gO, lse2, delta, gqkv, T_, H, Hk,
+                                     W, full, c2, scale, nq, nb);
+}
+
+// Both backward passes in one launch (head_dim 128, T a multiple of 64):
+// workgroups 0 .. nkv - 1 run the dK/dV pass, the rest the dQ pass. The two
+// passes read the same inputs and write disjoint outputs, and both fit two
+// workgroups per CU; in one grid the shorter dQ workgroups fill the CU slots
+// the dK/dV workgroups leave (a d12 layer has 768 of each against 512
+// slots, which as separate launches both end on a half-empty round).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_pair_kernel(
+    const bf16* __restrict__ qkv, const bf16* __restrict__ gO, const float* __restrict__ lse2,
+    const float* __restrict__ delta, bf16* __restrict__ gqkv, int T_, int H, int Hk, int W,
+    int full, float c2, float scale, int nkv, int nq, int nb) {
+  constexpr int BYTES = Kv2Lds<D>::BYTES > QLds<D, 2>::BYTES ? Kv2Lds<D>::BYTES : QLds<D, 2>::BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[BYTES];
+  const int L = (int)blockIdx.x;
+  if (L < nkv)
+    attn_bwd_kv2_body<D>(smem, L, qkv, gO, lse2, delta, gqkv, T_, H, Hk, W, full, c2, scale, nb);
+  else
+    attn_bwd_q_body<D, 4, true, 2>(smem, L - nkv, qkv, gO, lse2, delta, gqkv, T_, H, Hk, W, full,
+                                   c2, scale, nq, nb);
+}
+
+
 template <typename T, int D>
 void fwd(const gpt::Dims& d, bool full, const void* qkv, void* out, float* lse, hipStream_t s) {
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
@@ -1477,20 +1540,21 @@ void bwd(const gpt::Dims& d, bool full, const void* qkv, const void* gO, const f
     if constexpr (D == 128) {
       if (d.T % 32 == 0) {
         const int nkt2 = (d.T + 127) / 128;
-        GK_LAUNCH((attn_bwd_kv2_kernel<D>), dim3((unsigned)(nkt2 * d.Hk * d.B)), dim3(256), 0, s,
+        const int nkv = nkt2 * d.Hk * d.B;
+        if (d.T % 64 == 0) {
+          GK_LAUNCH((attn_bwd_pair_kernel<D>), dim3((unsigned)(nkv + nq * d.H * d.B)), dim3(256), 0,
+                    s, static_cast<const bf16*>(qkv), static_cast<const bf16*>(gO), lse, delta,
+                    static_cast<bf16*>(gqkv), d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2, scale, nkv,
+                    nq, d.B);
+          return;
+        }
+        GK_LAUNCH((attn_bwd_kv2_kernel<D>), dim3((unsigned)nkv), dim3(256), 0, s,
                   static_cast<const bf16*>(qkv), static_cast<const bf16*>(gO), lse, delta,
-                  static_cast<bf16*>(gqkv), d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2, scale, nkt2,
-                  d.B);
-        if (d.T % 64 == 0)
-          GK_LAUNCH((attn_bwd_q_tiled_kernel<D, NW, true, 2>), dim3((unsigned)(nq * d.H * d.B)),
-                    dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
-                    static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
-                    d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B);
-        else
-          GK_LAUNCH((attn_bwd_q_tiled_kernel<D, NW, false, 3>), dim3((unsigned)(nq * d.H * d.B)),
-                    dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
-                    static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
-                    d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B);
+                  static_cast<bf16*>(gqkv), d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2, scale, d.B);
+        GK_LAUNCH((attn_bwd_q_tiled_kernel<D, NW, false, 3>), dim3((unsigned)(nq * d.H * d.B)),
+                  dim3(64 * NW), 0, s, static_cast<const bf16*>(qkv),
+                  static_cast<const bf16*>(gO), lse, delta, static_cast<bf16*>(gqkv), d.T, d.H,
+                  d.Hk, d.W, full ? 1 : 0, c2, scale, nq, d.B);
         return;
       }
     }
