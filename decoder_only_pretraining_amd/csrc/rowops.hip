@@ -326,23 +326,56 @@ __global__ __launch_bounds__(kChunk) void token_links_kernel(const int32_t* __re
   link[N + n0 + t] = first;
 }
 
-// One workgroup per position; only leaders work (the test is uniform over
-// the workgroup). Columns are strided over the threads, so the member row
-// reads and the atomic adds are contiguous across a wavefront.
+// One workgroup per (chunk, slice of CW columns): the chunk's rows of the
+// slice are staged in LDS with every load in flight at once (a
+// workgroup per position, walking the links through global memory, waited
+// on one dependent load per member), then each leader's sum is formed from
+// LDS in position order, the leaders dealt alternately to the two halves
+// of the workgroup, each thread owning one column.
+template <int CW>
 __global__ __launch_bounds__(256) void rows_to_table_kernel(const float* __restrict__ g, int W,
                                                             const int32_t* __restrict__ tok,
                                                             const int32_t* __restrict__ link,
                                                             int64_t N, float* __restrict__ tab,
                                                             int V) {
-  const int64_t n = blockIdx.x;
-  // only leaders work; an id outside [0, V) (and so its whole link chain)
-  // has no table row
-  if (!link[N + n] || (uint32_t)tok[n] >= (uint32_t)V) return;
-  float* dst = tab + (int64_t)tok[n] * W;
-  for (int f = threadIdx.x; f < W; f += 256) {
-    float acc = g[n * W + f];
-    for (int k = link[n]; k >= 0; k = link[k]) acc += g[(int64_t)k * W + f];
-    atomicAdd(dst + f, acc);
+  static_assert(256 % CW == 0 && kChunk * CW / 4 % 256 == 0, "whole vectors per thread");
+  __shared__ __attribute__((aligned(16))) float rows[kChunk][CW];
+  __shared__ int32_t ids[kChunk], nxt[kChunk], lead[kChunk];
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * kChunk;
+  const int cnt = (int)min<int64_t>(kChunk, N - n0);
+  const int c0 = blockIdx.y * CW;
+  if (tid < cnt) {
+    ids[tid] = tok[n0 + tid];
+    const int32_t nx = link[n0 + tid];
+    nxt[tid] = nx >= 0 ? (int32_t)(nx - n0) : -1;
+    lead[tid] = link[N + n0 + tid];
+  }
+  constexpr int VPR = CW / 4, NV = kChunk * VPR / 256;  // 16-byte vectors per row, per thread
+  f32x4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = tid + 256 * i, r = e / VPR, c4 = (e % VPR) * 4;
+    if (r < cnt) v[i] = *reinterpret_cast<const f32x4*>(g + (n0 + r) * W + c0 + c4);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = tid + 256 * i, r = e / VPR, c4 = (e % VPR) * 4;
+    if (r < cnt) *reinterpret_cast<f32x4*>(&rows[r][c4]) = v[i];
+  }
+  __syncthreads();
+  constexpr int HALVES = 256 / CW;
+  const int col = tid % CW, half = tid / CW;
+  int k = 0;  // leaders seen so far
+  for (int p = 0; p < cnt; ++p) {
+    if (!lead[p]) continue;
+    const int mine = (k++ % HALVES) == half;
+    const int32_t id = ids[p];
+    // an id outside [0, V) (and so its whole link chain) has no table row
+    if (!mine || (uint32_t)id >= (uint32_t)V) continue;
+    float acc = rows[p][col];
+    for (int q = nxt[p]; q >= 0; q = nxt[q]) acc += rows[q][col];
+    atomicAdd(tab + (int64_t)id * W + c0 + col, acc);
   }
 }
 
@@ -1200,8 +1233,13 @@ void launch_token_links(const int32_t* tok, int64_t N, int32_t* link, hipStream_
 
 void launch_rows_to_table(const float* g, int W, const int32_t* tok, const int32_t* link,
                           int64_t N, float* tab, int V, hipStream_t s) {
-  GK_LAUNCH(rows_to_table_kernel, dim3((unsigned)N), dim3(256), 0, s, g, W, tok, link, N,
-                     tab, V);
+  const unsigned chunks = (unsigned)((N + kChunk - 1) / kChunk);
+  if (W % 128 == 0)
+    GK_LAUNCH(rows_to_table_kernel<128>, dim3(chunks, (unsigned)(W / 128)), dim3(256), 0, s, g,
+              W, tok, link, N, tab, V);
+  else  // W is a multiple of 64
+    GK_LAUNCH(rows_to_table_kernel<64>, dim3(chunks, (unsigned)(W / 64)), dim3(256), 0, s, g, W,
+              tok, link, N, tab, V);
 }
 
 void launch_count_valid(const Dims& d, const int32_t* tgt, float* scalars, hipStream_t s) {
