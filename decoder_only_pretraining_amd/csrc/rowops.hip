@@ -327,29 +327,34 @@ __global__ __launch_bounds__(kChunk) void token_links_kernel(const int32_t* __re
 }
 
 // One workgroup per (chunk, slice of CW columns): the chunk's rows of the
-// slice are staged in LDS with every load in flight at once (a
-// workgroup per position, walking the links through global memory, waited
-// on one dependent load per member), then each leader's sum is formed from
-// LDS in position order, the leaders dealt alternately to the two halves
-// of the workgroup, each thread owning one column.
+// slice are staged in LDS with every load in flight at once, the chunk's
+// leaders are listed in position order (a ballot over the first 128
+// threads), and the 256 / CW groups of threads take every (256 / CW)-th
+// leader, each thread one column: its sum formed from LDS in position
+// order, then one atomic add. (A single scan over all positions by every
+// thread, and a workgroup per position walking the links in global
+// memory, each spent their time waiting on dependent loads.)
 template <int CW>
 __global__ __launch_bounds__(256) void rows_to_table_kernel(const float* __restrict__ g, int W,
                                                             const int32_t* __restrict__ tok,
                                                             const int32_t* __restrict__ link,
                                                             int64_t N, float* __restrict__ tab,
                                                             int V) {
-  static_assert(256 % CW == 0 && kChunk * CW / 4 % 256 == 0, "whole vectors per thread");
+  static_assert(256 % CW == 0 && kChunk * CW / 4 % 256 == 0 && kChunk == 128,
+                "whole vectors per thread; two wavefronts list the leaders");
   __shared__ __attribute__((aligned(16))) float rows[kChunk][CW];
-  __shared__ int32_t ids[kChunk], nxt[kChunk], lead[kChunk];
-  const int tid = threadIdx.x;
+  __shared__ int32_t ids[kChunk], nxt[kChunk], leaders[kChunk];
+  __shared__ int nlead0, nlead;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t n0 = (int64_t)blockIdx.x * kChunk;
   const int cnt = (int)min<int64_t>(kChunk, N - n0);
   const int c0 = blockIdx.y * CW;
+  int is_lead = 0;
   if (tid < cnt) {
     ids[tid] = tok[n0 + tid];
     const int32_t nx = link[n0 + tid];
     nxt[tid] = nx >= 0 ? (int32_t)(nx - n0) : -1;
-    lead[tid] = link[N + n0 + tid];
+    is_lead = link[N + n0 + tid];
   }
   constexpr int VPR = CW / 4, NV = kChunk * VPR / 256;  // 16-byte vectors per row, per thread
   f32x4 v[NV];
@@ -358,21 +363,27 @@ __global__ __launch_bounds__(256) void rows_to_table_kernel(const float* __restr
     const int e = tid + 256 * i, r = e / VPR, c4 = (e % VPR) * 4;
     if (r < cnt) v[i] = *reinterpret_cast<const f32x4*>(g + (n0 + r) * W + c0 + c4);
   }
+  // leaders in position order: positions 0-63 are wavefront 0's lanes,
+  // 64-127 wavefront 1's
+  const uint64_t bal = __ballot(is_lead);
+  const int below = __popcll(bal & ((1ull << lane) - 1ull));
+  if (tid == 63) nlead0 = __popcll(bal);
+  __syncthreads();
+  if (tid < 128 && is_lead) leaders[(tid < 64 ? 0 : nlead0) + below] = tid;
+  if (tid == 127) nlead = nlead0 + __popcll(bal);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = tid + 256 * i, r = e / VPR, c4 = (e % VPR) * 4;
     if (r < cnt) *reinterpret_cast<f32x4*>(&rows[r][c4]) = v[i];
   }
   __syncthreads();
-  constexpr int HALVES = 256 / CW;
-  const int col = tid % CW, half = tid / CW;
-  int k = 0;  // leaders seen so far
-  for (int p = 0; p < cnt; ++p) {
-    if (!lead[p]) continue;
-    const int mine = (k++ % HALVES) == half;
+  constexpr int GROUPS = 256 / CW;
+  const int col = tid % CW, grp = tid / CW;
+  for (int k = grp; k < nlead; k += GROUPS) {
+    const int p = leaders[k];
     const int32_t id = ids[p];
     // an id outside [0, V) (and so its whole link chain) has no table row
-    if (!mine || (uint32_t)id >= (uint32_t)V) continue;
+    if ((uint32_t)id >= (uint32_t)V) continue;
     float acc = rows[p][col];
     for (int q = nxt[p]; q >= 0; q = nxt[q]) acc += rows[q][col];
     atomicAdd(tab + (int64_t)id * W + c0 + col, acc);
