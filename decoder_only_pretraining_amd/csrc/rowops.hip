@@ -424,68 +424,80 @@ __device__ __forceinline__ f32x4 round4(const f32x4& v, bf16) {
   return r;
 }
 
-template <typename T, int NC>
+// One wavefront per row. With gate weights (STAGED) the workgroup first
+// stages them in LDS (hk x C floats, dynamic) and its wavefronts then take
+// rows in a grid-stride loop, so the weights are read from L2 once per
+// workgroup rather than once per row; weights past 64 KB are read from
+// global memory per row.
+template <typename T, int NC, bool STAGED = false>
 __global__ __launch_bounds__(256) void mix_norm_kernel(
     const float* __restrict__ x, const float* __restrict__ x0, const float* __restrict__ lam_r,
     const float* __restrict__ lam_0, float* __restrict__ xin_out, T* __restrict__ y,
     float* __restrict__ r_out, const float* __restrict__ wg, float* __restrict__ a, int64_t N,
     int C, int hk, float eps) {
+  extern __shared__ f32x4 wgs[];  // hk * C / 4 vectors, with gate weights only
   const int lane = threadIdx.x & 63;
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
   const int C4 = C / 4;
+  if (STAGED) {
+    for (int i = threadIdx.x; i < hk * C4; i += 256) wgs[i] = reinterpret_cast<const f32x4*>(wg)[i];
+    __syncthreads();
+  }
+  const f32x4* wsrc = STAGED ? wgs : reinterpret_cast<const f32x4*>(wg);
   const float lr = x0 ? lam_r[0] : 1.0f, l0 = x0 ? lam_0[0] : 0.0f;
-  f32x4 v[NC];
-  float ss = 0.0f;
+  for (int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); n < N;
+       n += (int64_t)gridDim.x * 4) {
+    f32x4 v[NC];
+    float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c4 = lane + i * 64;
-    if (c4 < C4) {
-      f32x4 xv = reinterpret_cast<const f32x4*>(x + n * C)[c4];
-      if (x0) {
-        const f32x4 zv = reinterpret_cast<const f32x4*>(x0 + n * C)[c4];
-        xv = lr * xv + l0 * zv;
-        if (xin_out) reinterpret_cast<f32x4*>(xin_out + n * C)[c4] = xv;
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+        f32x4 xv = reinterpret_cast<const f32x4*>(x + n * C)[c4];
+        if (x0) {
+          const f32x4 zv = reinterpret_cast<const f32x4*>(x0 + n * C)[c4];
+          xv = lr * xv + l0 * zv;
+          if (xin_out) reinterpret_cast<f32x4*>(xin_out + n * C)[c4] = xv;
+        }
+        v[i] = xv;
+        ss += xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3];
       }
-      v[i] = xv;
-      ss += xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3];
     }
-  }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)C + eps);
-  if (lane == 0) r_out[n] = r;
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)C + eps);
+    if (lane == 0) r_out[n] = r;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c4 = lane + i * 64;
-    if (c4 < C4) {
-      v[i] = round4(v[i] * r, T{});
-      store4<T>(y + n * C + c4 * 4, v[i]);
+    for (int i = 0; i < NC; ++i) {
+      const int c4 = lane + i * 64;
+      if (c4 < C4) {
+        v[i] = round4(v[i] * r, T{});
+        store4<T>(y + n * C + c4 * 4, v[i]);
+      }
     }
-  }
-  if (wg) {  // gate logits from the rounded norm output, four KV heads at a time
-    for (int j0 = 0; j0 < hk; j0 += 4) {
-      float dot[4];
+    if (wg) {  // gate logits from the rounded norm output, four KV heads at a time
+      for (int j0 = 0; j0 < hk; j0 += 4) {
+        float dot[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = min(j0 + q, hk - 1);  // past hk: a valid row, result unused
-        dot[q] = 0.0f;
+        for (int q = 0; q < 4; ++q) {
+          const int j = min(j0 + q, hk - 1);  // past hk: a valid row, result unused
+          dot[q] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          const int c4 = lane + i * 64;
-          if (c4 < C4) {
-            const f32x4 w = reinterpret_cast<const f32x4*>(wg + (int64_t)j * C)[c4];
-            dot[q] += v[i][0] * w[0] + v[i][1] * w[1] + v[i][2] * w[2] + v[i][3] * w[3];
+          for (int i = 0; i < NC; ++i) {
+            const int c4 = lane + i * 64;
+            if (c4 < C4) {
+              const f32x4 w = wsrc[j * C4 + c4];
+              dot[q] += v[i][0] * w[0] + v[i][1] * w[1] + v[i][2] * w[2] + v[i][3] * w[3];
+            }
           }
         }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dot[q] += __shfl_xor(dot[q], o, kWave);
+        if (lane == 0)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (j0 + q < hk) a[n * hk + j0 + q] = dot[q];
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dot[q] += __shfl_xor(dot[q], o, kWave);
-      if (lane == 0)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (j0 + q < hk) a[n * hk + j0 + q] = dot[q];
     }
   }
 }
@@ -1073,9 +1085,16 @@ template <typename T, int NC>
 static void mix_norm_nc(const Dims& d, const float* x, const float* x0, const float* lam_r,
                         const float* lam_0, float* xin_out, void* y, float* r, const float* wg,
                         float* a, hipStream_t s) {
-  GK_LAUNCH((mix_norm_kernel<T, NC>), dim3((unsigned)((d.N + 3) / 4)), dim3(256), 0, s,
-                     x, x0, lam_r, lam_0, xin_out, static_cast<T*>(y), r, wg, a, d.N, d.C, d.Hk,
-                     d.eps);
+  const int64_t rows4 = (d.N + 3) / 4;
+  const size_t lds = (size_t)d.Hk * d.C * 4;
+  if (wg && lds <= 65536) {  // fewer workgroups, each staging the gate weights once
+    GK_LAUNCH((mix_norm_kernel<T, NC, true>), dim3((unsigned)std::min<int64_t>(rows4, 1024)),
+              dim3(256), lds, s, x, x0, lam_r, lam_0, xin_out, static_cast<T*>(y), r, wg, a, d.N,
+              d.C, d.Hk, d.eps);
+    return;
+  }
+  GK_LAUNCH((mix_norm_kernel<T, NC, false>), dim3((unsigned)rows4), dim3(256), 0, s, x, x0, lam_r,
+            lam_0, xin_out, static_cast<T*>(y), r, wg, a, d.N, d.C, d.Hk, d.eps);
 }
 
 void launch_mix_norm(const Dims& d, const float* x, const float* x0, const float* lam_r,
