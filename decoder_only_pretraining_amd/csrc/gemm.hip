@@ -666,6 +666,19 @@ void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int
   const int64_t Kp = K / 2, kc = kchunk / 2;
   const int splits = Kp > 0 && kc > 0 ? (int)((Kp + kc - 1) / kc) : 1;
   dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8));  // padded: see the kernel's tile order
+  // The K-major kernel's fp8 mode (8 wavefronts, direct fills); at 256
+  // columns the epilogues that read an fp32 operand do not fit its 256
+  // registers and stay on the 4-wavefront kernel.
+  constexpr bool kKmaj = BM == 256 && !(BN == 256 && (std::is_same<EP, EpResid>::value ||
+                                                      std::is_same<EP, EpF32>::value));
+  if constexpr (kKmaj) {
+    if (Kp % 64 == 0 && (splits == 1 || kc % 64 == 0)) {
+      GK_LAUNCH((gemm_kmaj_kernel<BN, EP, MODE, Deq8>), grid, dim3(512), 0, s,
+                reinterpret_cast<const bf16*>(A), lda / 2, reinterpret_cast<const bf16*>(B),
+                ldb / 2, M, N, Kp, splits == 1 ? Kp : kc, tm, tn, ep, (int64_t)0, (int64_t)0, dq);
+      return;
+    }
+  }
   GK_LAUNCH((gemm_bf16_kernel<BM, BN, 64, true, true, MODE, PreId, PreId, EP, Deq8>), grid,
                      dim3(256), 0, s, reinterpret_cast<const bf16*>(A), lda / 2,
                      reinterpret_cast<const bf16*>(B), ldb / 2, M, N, Kp, kc, tm, tn, PreId{},

@@ -260,6 +260,14 @@ __device__ __forceinline__ void mfma8(f32x16& acc, const Frag8& a, const Frag8& 
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, acc, FA, 0, 0, 0, 0, 0);
 }
 
+// The same with the B fragment first (the K-major kernel's C^T accumulator
+// layout): the operand formats swap places.
+template <int MODE>
+__device__ __forceinline__ void mfma8_bt(f32x16& acc, const Frag8& b, const Frag8& a) {
+  constexpr int FA = MODE == 2 ? 1 : 0;
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b.v, a.v, acc, 0, FA, 0, 0, 0, 0);
+}
+
 // Dequantisation of an fp8 product. NoDeq: bf16 products. Deq8: in segment
 // i of the M or N index (axis 0 or 1; at most 3 segments) the code sums are
 // multiplied by f_i = 1 / (s_a,i * s_b,i), s = fmax / amax (1 if amax is 0
@@ -630,12 +638,21 @@ struct KmajFill {
   }
 };
 
-template <int BN, class EP>
+//
+// fp8 mode (MODE 1: e4m3 x e4m3, 2: e5m2 x e4m3; DQ = Deq8): the operands
+// are codes handled as 2-byte units (K, the leading dimensions and the K
+// chunk in units), so tiles, fills and LDS layout are unchanged; a 64-unit
+// stage holds 128 codes per row and is consumed by two 64-code slices of
+// v_mfma_f32_32x32x64_f8f6f4 (a fragment: 32 codes of one row per lane, two
+// 16-byte reads), and the epilogue dequantises by segment.
+template <int BN, class EP, int MODE = 0, class DQ = NoDeq>
 __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, EP ep_in, int64_t bsA,
-    int64_t bsB) {
-  constexpr int BM = 256, NW = 8, KS = 4;
+    int64_t bsB, DQ dq = DQ{}) {
+  constexpr bool F8 = MODE != 0;
+  static_assert(F8 == DQ::kOn, "fp8 products need a dequantisation");
+  constexpr int BM = 256, NW = 8, KS = F8 ? 2 : 4;
   constexpr int WM = BM / 4, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int AEL = BM * 64, BEL = BN * 64;  // elements per stage
   constexpr int SP = WN + 4;                   // epilogue staging row pitch (floats)
@@ -688,6 +705,20 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
   auto fragB = [&](Frag<bf16>& f, int buf, int j, int ks) {
     f.v = *reinterpret_cast<const bf16x8*>(Bs + buf * BEL + kswz(wn * WN + j * 32 + r32, 2 * ks + hi));
   };
+  // fp8: 32 codes of row r for 64-code slice ks: granules 4 ks + 2 hi, + 1
+  auto frag8 = [&](Frag8& f, const bf16* base, int r, int ks) {
+    const U128 lo = *reinterpret_cast<const U128*>(base + kswz(r, 4 * ks + 2 * hi));
+    const U128 up = *reinterpret_cast<const U128*>(base + kswz(r, 4 * ks + 2 * hi + 1));
+    f.v = i32x8{(int)lo.w[0], (int)lo.w[1], (int)lo.w[2], (int)lo.w[3],
+                (int)up.w[0], (int)up.w[1], (int)up.w[2], (int)up.w[3]};
+  };
+  float fdq[3] = {1.0f, 1.0f, 1.0f};
+  if constexpr (F8) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (i < dq.nseg)
+        fdq[i] = 1.0f / (fp8_scale(dq.amax[dq.sa[i]], dq.fa) * fp8_scale(dq.amax[dq.sb[i]], dq.fb));
+  }
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -708,36 +739,68 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     }
   }
   __syncthreads();
-  Frag<bf16> a[2][TM], b[2][TN];
+  if constexpr (F8) {
+    // two 64-code slices per stage; the fragments of slice s + 1 (of this
+    // stage, or the next stage's first) are read while slice s's MFMAs run
+    Frag8 a[2][TM], b[2][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) fragA(a[0][i], 0, i, 0);
+    for (int i = 0; i < TM; ++i) frag8(a[0][i], As, wm * WM + i * 32 + r32, 0);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) fragB(b[0][j], 0, j, 0);
-  constexpr int NR = TM + TN, NM = TM * TN;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+    for (int j = 0; j < TN; ++j) frag8(b[0][j], Bs, wn * WN + j * 32 + r32, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int p = ks & 1;
-      if (ks == KS - 1) {
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-        __syncthreads();
-        if (kt + 2 < nk) fill(kt + 2, cur);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int p = ks & 1;
+        if (ks == KS - 1) {
+          __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+          __syncthreads();
+          if (kt + 2 < nk) fill(kt + 2, cur);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) mfma8_bt<MODE>(acc[i][j], b[p][j], a[p][i]);
+        const int rb = ks + 1 < KS ? cur : cur ^ 1, rs = ks + 1 < KS ? ks + 1 : 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) frag8(a[p ^ 1][i], As + rb * AEL, wm * WM + i * 32 + r32, rs);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) frag8(b[p ^ 1][j], Bs + rb * BEL, wn * WN + j * 32 + r32, rs);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+  } else {
+    Frag<bf16> a[2][TM], b[2][TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) fragA(a[0][i], 0, i, 0);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[p][j].v, a[p][i].v, acc[i][j], 0, 0, 0);
-      // the next slice: of this stage, or the next stage's first (after the
-      // last stage these reads are stale and unused)
-      const int rb = ks + 1 < KS ? cur : cur ^ 1, rs = ks + 1 < KS ? ks + 1 : 0;
+    for (int j = 0; j < TN; ++j) fragB(b[0][j], 0, j, 0);
+    constexpr int NR = TM + TN, NM = TM * TN;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fragA(a[p ^ 1][i], rb, i, rs);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int p = ks & 1;
+        if (ks == KS - 1) {
+          __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+          __syncthreads();
+          if (kt + 2 < nk) fill(kt + 2, cur);
+        }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fragB(b[p ^ 1][j], rb, j, rs);
-      interleave_mfma_ds<0, NR, NM / NR, NM % NR>();
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[p][j].v, a[p][i].v, acc[i][j], 0, 0, 0);
+        // the next slice: of this stage, or the next stage's first (after the
+        // last stage these reads are stale and unused)
+        const int rb = ks + 1 < KS ? cur : cur ^ 1, rs = ks + 1 < KS ? ks + 1 : 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fragA(a[p ^ 1][i], rb, i, rs);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fragB(b[p ^ 1][j], rb, j, rs);
+        interleave_mfma_ds<0, NR, NM / NR, NM % NR>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -778,8 +841,13 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
         for (int g = 0; g < 4; ++g) {
           const int nl = j * 32 + 8 * g + 4 * hi;
           f32x4 v;
+          // fp8: one dequantisation factor per 4-column group (segment
+          // bounds are multiples of 4)
+          float f = 1.0f;
+          if constexpr (F8) f = fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(nw + nl)];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = ep.value(m, nw + nl + t, acc[i][j][4 * g + t]);
+          for (int t = 0; t < 4; ++t)
+            v[t] = ep.value(m, nw + nl + t, F8 ? acc[i][j][4 * g + t] * f : acc[i][j][4 * g + t]);
           *reinterpret_cast<f32x4*>(stage + r32 * SP + nl) = v;
         }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront
