@@ -768,9 +768,32 @@ SplitSum gemm8_product(bool wgrad, int64_t M, int64_t N, int64_t K, const uint8_
                        float* part, int64_t part_cap, hipStream_t s);
 
 static int64_t wgrad_target(Tile t) { return t.bm == 128 ? 512 : 256; }
+
+// K splits of an fp8 weight gradient (K in codes, chunks multiples of 128):
+// the count s in 1..8 with the least modelled time, where a split product
+// takes ceil(tiles * s / 256) waves of one workgroup per CU, each as long as
+// its chunk, and every split beyond one adds an fp32 partial of C written
+// and read back. Work is priced in MFMA flops at ~40% of a CU's fp8 rate
+// (7.8 TFLOP/s, as measured in these products) against partial bytes at
+// ~5 TB/s of HBM: 1.56 flops per byte. (A 6656 x 1664 gradient over 16,384
+// tokens: 338 tiles of 256 x 128 take 2 waves unsplit, 4 waves of a third
+// of K in 3 splits.)
 static KSplit f8_wgrad_split(int64_t M, int64_t N, int64_t K) {
   const Tile t = pick_tile_wgrad(M, N);
-  return plan_split(tile_count(t, M, N), K, 128, 1024, wgrad_target(t));  // K in codes
+  const int64_t tiles = tile_count(t, M, N);
+  const int64_t units = (K + 127) / 128;
+  KSplit best{K, 1};
+  double best_cost = -1.0;
+  for (int64_t sp = 1; sp <= 8 && sp <= units; ++sp) {
+    const int64_t chunk = (units + sp - 1) / sp * 128;
+    const int64_t splits = (K + chunk - 1) / chunk;
+    if (splits != sp) continue;
+    const double waves = (double)((tiles * splits + 255) / 256);
+    double cost = waves * (double)chunk * t.bm * t.bn * 2.0;
+    if (splits > 1) cost += 1.56 * (double)splits * M * N * 8.0;
+    if (best_cost < 0 || cost < best_cost) best = KSplit{splits > 1 ? chunk : K, splits}, best_cost = cost;
+  }
+  return best;
 }
 int64_t part_bytes_f8_wgrad(int64_t M, int64_t N, int64_t K) {
   const KSplit ks = f8_wgrad_split(M, N, K);

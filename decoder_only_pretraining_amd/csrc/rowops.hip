@@ -8,6 +8,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <mutex>
+
 namespace gk {
 
 
@@ -425,12 +427,13 @@ __device__ __forceinline__ f32x4 round4(const f32x4& v, bf16) {
 }
 
 // One wavefront per row. With gate weights (STAGED) the workgroup first
-// stages them in LDS (hk x C floats, dynamic) and its wavefronts then take
-// rows in a grid-stride loop, so the weights are read from L2 once per
-// workgroup rather than once per row; weights past 64 KB are read from
-// global memory per row.
-template <typename T, int NC, bool STAGED = false>
-__global__ __launch_bounds__(256) void mix_norm_kernel(
+// stages them in LDS (hk x C floats, dynamic) and its NT / 64 wavefronts
+// then take rows in a grid-stride loop, so the weights are read from L2
+// once per workgroup rather than once per row. Up to 64 KB of weights the
+// workgroups have 256 threads; larger ones (up to the device's LDS per
+// workgroup) have 1024, one workgroup per CU sharing one copy.
+template <typename T, int NC, bool STAGED = false, int NT = 256>
+__global__ __launch_bounds__(NT) void mix_norm_kernel(
     const float* __restrict__ x, const float* __restrict__ x0, const float* __restrict__ lam_r,
     const float* __restrict__ lam_0, float* __restrict__ xin_out, T* __restrict__ y,
     float* __restrict__ r_out, const float* __restrict__ wg, float* __restrict__ a, int64_t N,
@@ -438,14 +441,15 @@ __global__ __launch_bounds__(256) void mix_norm_kernel(
   extern __shared__ f32x4 wgs[];  // hk * C / 4 vectors, with gate weights only
   const int lane = threadIdx.x & 63;
   const int C4 = C / 4;
+  constexpr int RW = NT / 64;  // rows in flight per workgroup
   if (STAGED) {
-    for (int i = threadIdx.x; i < hk * C4; i += 256) wgs[i] = reinterpret_cast<const f32x4*>(wg)[i];
+    for (int i = threadIdx.x; i < hk * C4; i += NT) wgs[i] = reinterpret_cast<const f32x4*>(wg)[i];
     __syncthreads();
   }
   const f32x4* wsrc = STAGED ? wgs : reinterpret_cast<const f32x4*>(wg);
   const float lr = x0 ? lam_r[0] : 1.0f, l0 = x0 ? lam_0[0] : 0.0f;
-  for (int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); n < N;
-       n += (int64_t)gridDim.x * 4) {
+  for (int64_t n = (int64_t)blockIdx.x * RW + (threadIdx.x >> 6); n < N;
+       n += (int64_t)gridDim.x * RW) {
     f32x4 v[NC];
     float ss = 0.0f;
 #pragma unroll
@@ -1081,6 +1085,25 @@ void launch_embed(const float* wte, const int32_t* tok, float* x0, int64_t N, in
   GK_LAUNCH(embed_kernel, dim3((unsigned)N), dim3(256), 0, s, wte, tok, x0, N, C, V);
 }
 
+// LDS bytes a workgroup may allocate on the current device (looked up once
+// per device; 64 KB if the query fails).
+static int max_lds_per_block() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 65536;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        v < 65536)
+      v = 65536;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
 template <typename T, int NC>
 static void mix_norm_nc(const Dims& d, const float* x, const float* x0, const float* lam_r,
                         const float* lam_0, float* xin_out, void* y, float* r, const float* wg,
@@ -1091,6 +1114,12 @@ static void mix_norm_nc(const Dims& d, const float* x, const float* x0, const fl
     GK_LAUNCH((mix_norm_kernel<T, NC, true>), dim3((unsigned)std::min<int64_t>(rows4, 1024)),
               dim3(256), lds, s, x, x0, lam_r, lam_0, xin_out, static_cast<T*>(y), r, wg, a, d.N,
               d.C, d.Hk, d.eps);
+    return;
+  }
+  if (wg && lds <= (size_t)max_lds_per_block()) {  // one 1024-thread workgroup per CU
+    GK_LAUNCH((mix_norm_kernel<T, NC, true, 1024>),
+              dim3((unsigned)std::min<int64_t>((d.N + 15) / 16, 256)), dim3(1024), lds, s, x, x0,
+              lam_r, lam_0, xin_out, static_cast<T*>(y), r, wg, a, d.N, d.C, d.Hk, d.eps);
     return;
   }
   GK_LAUNCH((mix_norm_kernel<T, NC, false>), dim3((unsigned)rows4), dim3(256), 0, s, x, x0, lam_r,

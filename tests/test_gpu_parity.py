@@ -133,10 +133,18 @@ SMALL_BF16_GQA = SMALL_BF16.with_(name="small_bf16_gqa", n_kv_head=2, seq_len=25
                                   short_window=64)
 
 
-@pytest.mark.parametrize("w", [SMALL_BF16, SMALL_BF16_GQA], ids=lambda w: w.name)
+# d26 widths in bf16: 13 KV heads x 1664 fp32 gate weights (86.5 KB) take
+# the mix/norm kernel's 1024-thread path, which stages them in one LDS copy
+# per CU; layer 1 (the last) carries value embeddings.
+SMALL_D26W = W.get("d26").with_(name="small_d26w", n_layer=2, seq_len=200, batch=2,
+                                short_window=50, vocab=2048, fp8_linears=False)
+
+
+@pytest.mark.parametrize("w", [SMALL_BF16, SMALL_BF16_GQA, SMALL_D26W], ids=lambda w: w.name)
 def test_bf16_parity_small(w):
-    """The bf16 kernels at d12 widths (C 768, D 128, F 3072) on a short
-    sequence, against the float64 oracle."""
+    """The bf16 kernels at d12 widths (C 768, D 128, F 3072) and d26 widths
+    (C 1664, 13 heads, F 6656) on a short sequence, against the float64
+    oracle."""
     p, tok, tgt = inputs(w, 31, 32)
     lo, go = oracle.forward_backward(w, p.astype(np.float64), tok, tgt)
     lg, gg, _ = gpu_step(w, p, tok, tgt)
