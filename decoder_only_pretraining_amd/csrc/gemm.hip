@@ -685,6 +685,18 @@ void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int
                      PreId{}, ep, dq, (int64_t)0, (int64_t)0);
 }
 
+// The K-major kernel with scales cut along K (one unsplit launch; K and the
+// segment ends multiples of 128 codes, checked by the caller).
+template <int BN, int MODE>
+void launch_f8_kseg(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M,
+                    int64_t N, int64_t K, EpF32 ep, const Deq8K& dq, hipStream_t s) {
+  const int tm = (int)((M + 255) / 256), tn = (int)((N + BN - 1) / BN);
+  GK_LAUNCH((gemm_kmaj_kernel<BN, EpF32, MODE, Deq8K>), dim3((unsigned)((tm * tn + 7) / 8 * 8)),
+            dim3(512), 0, s, reinterpret_cast<const bf16*>(A), lda / 2,
+            reinterpret_cast<const bf16*>(B), ldb / 2, M, N, K / 2, K / 2, tm, tn, ep, (int64_t)0,
+            (int64_t)0, dq);
+}
+
 template <int MODE, class EP>
 void run_f8(Tile t, const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M,
             int64_t N, int64_t K, int64_t kchunk, EP ep, const Deq8& dq, hipStream_t s) {
@@ -758,6 +770,60 @@ void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                hipStream_t s) {
   run_f8<2>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_f32(C, N, accumulate ? 1 : 0),
             to_deq(dq), s);
+}
+
+// An fp8 product with scales that change along K (the q, k and v segments
+// of the attention input gradient's contraction, each with its own
+// output-gradient and weight scale): one launch of the K-major kernel,
+// which rescales its accumulators where a segment ends, when the tile is
+// 256 rows, not 256 columns (those fp32 epilogues run on the 4-wavefront
+// kernel), K and the segment ends are multiples of 128 codes; otherwise one
+// accumulating product per segment.
+SplitSum gemm8_product(bool wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                       const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                       float* part, int64_t part_cap, hipStream_t s);
+
+static bool f8_kseg_fused(int64_t M, int64_t N, int64_t K, const Fp8Deq& dq) {
+  const Tile t = pick_tile(M, N, K);
+  if (t.bm != 256 || (t.bn != 192 && t.bn != 128) || K % 128) return false;
+  for (int i = 0; i + 1 < dq.nseg; ++i)
+    if (dq.end[i] % 128 || dq.end[i] > K) return false;
+  return true;
+}
+
+void gemm8_f32_kseg(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                    const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                    hipStream_t s) {
+  if (f8_kseg_fused(M, N, K, dq)) {
+    Deq8K q;
+    static_cast<Deq8&>(q) = to_deq(dq);
+    q.axis = 2;
+    const EpF32 ep = mk_f32(C, N, accumulate ? 1 : 0);
+    const Tile t = pick_tile(M, N, K);
+    if (t.bn == 192)
+      GPT_F8_DISPATCH(dq, (launch_f8_kseg<192, 1>(A, lda, B, ldb, M, N, K, ep, q, s)),
+                      (launch_f8_kseg<192, 2>(A, lda, B, ldb, M, N, K, ep, q, s)));
+    else
+      GPT_F8_DISPATCH(dq, (launch_f8_kseg<128, 1>(A, lda, B, ldb, M, N, K, ep, q, s)),
+                      (launch_f8_kseg<128, 2>(A, lda, B, ldb, M, N, K, ep, q, s)));
+    return;
+  }
+  int64_t k0 = 0;
+  bool first = true;
+  for (int i = 0; i < dq.nseg; ++i) {
+    const int64_t k1 = i + 1 < dq.nseg ? std::min<int64_t>(dq.end[i], K) : K;
+    if (k1 > k0) {
+      Fp8Deq one = dq;
+      one.axis = 0;
+      one.nseg = 1;
+      one.sa[0] = dq.sa[i];
+      one.sb[0] = dq.sb[i];
+      gemm8_product(false, M, N, k1 - k0, A + k0, lda, B + k0, ldb, one, C, accumulate || !first,
+                    nullptr, 0, s);
+      first = false;
+    }
+    k0 = std::max(k0, k1);
+  }
 }
 
 // An fp8 product with an fp32 output on the step's code paths: the plain

@@ -276,19 +276,25 @@ __device__ __forceinline__ void mfma8_bt(f32x16& acc, const Frag8& b, const Frag
 // would move them out of the accumulation registers).
 struct NoDeq {
   static constexpr bool kOn = false;
+  static constexpr bool kKseg = false;
 };
 // Aux type of an epilogue that reads no operand besides the accumulators.
 struct NoAux {};
 struct Deq8 {
   static constexpr bool kOn = true;
+  static constexpr bool kKseg = false;
   const uint32_t* amax;
-  int axis, nseg;
+  int axis, nseg;  // axis 0: segments of M, 1: of N (Deq8K: of K, in codes)
   int64_t end[2];
   int sa[3], sb[3];
   float fa, fb;
   __device__ __forceinline__ int seg(int64_t i) const {
     return (nseg > 1 && i >= end[0]) + (nseg > 2 && i >= end[1]);
   }
+};
+// fp8 scales cut along the contraction (the K-major kernel only).
+struct Deq8K : Deq8 {
+  static constexpr bool kKseg = true;
 };
 
 // Scheduling groups for a main-loop slice: NR times (n MFMAs, one DS
@@ -719,6 +725,13 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
       if (i < dq.nseg)
         fdq[i] = 1.0f / (fp8_scale(dq.amax[dq.sa[i]], dq.fa) * fp8_scale(dq.amax[dq.sb[i]], dq.fb));
   }
+  auto fsel = [&](int i) { return i == 0 ? fdq[0] : (i == 1 ? fdq[1] : fdq[2]); };
+  // fp8 scales along K (axis 2; segment ends on 128-code stages): the
+  // accumulators hold the sum in units of the current segment's factor, are
+  // multiplied by f_prev / f_next where a stage opens the next segment, and
+  // the epilogue applies the factor of the last segment
+  int kseg = 0;
+  if constexpr (DQ::kKseg) kseg = dq.seg(k_lo * 2);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -749,6 +762,19 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     for (int j = 0; j < TN; ++j) frag8(b[0][j], Bs, wn * WN + j * 32 + r32, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
+      if (DQ::kKseg && kt > 0) {
+        const int sg = dq.seg((k_lo + (int64_t)kt * 64) * 2);
+        if (sg != kseg) {
+          const float rr = fsel(kseg) / fsel(sg);
+          kseg = sg;
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[i][j][e] *= rr;
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int p = ks & 1;
@@ -844,7 +870,10 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
           // fp8: one dequantisation factor per 4-column group (segment
           // bounds are multiples of 4)
           float f = 1.0f;
-          if constexpr (F8) f = fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(nw + nl)];
+          if constexpr (DQ::kKseg)
+            f = fsel(kseg);
+          else if constexpr (F8)
+            f = fdq[dq.axis == 0 ? dq.seg(m) : dq.seg(nw + nl)];
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             v[t] = ep.value(m, nw + nl + t, F8 ? acc[i][j][4 * g + t] * f : acc[i][j][4 * g + t]);

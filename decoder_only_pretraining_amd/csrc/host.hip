@@ -755,13 +755,11 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
           quant_tok(gqkv, true, d.Qkv, segs3(d.Cq, d.Cq + d.Ckv, g0, g1, g2), FP8_E5M2, g8t);
         });
         // the q, k and v gradients carry their own scales along the
-        // contraction: one product per segment, summed into gtmp
+        // contraction (K segments)
         site("gemm.qkv.dgrad", s, [&] {
-          const int64_t k0[3] = {0, d.Cq, d.Cq + d.Ckv}, kn[3] = {d.Cq, d.Ckv, d.Ckv};
-          const int ga8[3] = {g0, g1, g2};
-          for (int i = 0; i < 3; ++i)
-            gemm8_f32(N, d.C, kn[i], q8 + k0[i], d.Qkv, w8t(l, 0) + k0[i], P128(d.Qkv),
-                      deq1(ga8[i], slot(l, i), FP8_E5M2), gtmp, i > 0, s);
+          gemm8_f32_kseg(N, d.C, d.Qkv, q8, d.Qkv, w8t(l, 0), P128(d.Qkv),
+                         deq3(2, g0, g1, g2, slot(l, 0), slot(l, 1), slot(l, 2), FP8_E5M2), gtmp,
+                         false, s);
         });
         site("gemm.qkv.wgrad", s, [&] {
           const int x = slot(l, 6);
@@ -1159,9 +1157,16 @@ int gpt_fp8_gemm(int32_t wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* 
     return fail(GPT_E_INVAL, "lda %lld / ldb %lld: need multiples of 16, >= K", (long long)lda,
                 (long long)ldb);
   if (!A || !B || !amax || !sc || !C) return fail(GPT_E_NULLPTR, "a required pointer is NULL");
-  if (sc->axis != 0 && sc->axis != 1) return fail(GPT_E_INVAL, "scales.axis must be 0 or 1");
+  if (sc->axis < 0 || sc->axis > 2) return fail(GPT_E_INVAL, "scales.axis must be 0, 1 or 2");
   if (sc->nseg < 1 || sc->nseg > 3) return fail(GPT_E_INVAL, "scales.nseg must be 1, 2 or 3");
   if (sc->nseg == 3 && sc->end[1] < sc->end[0]) return fail(GPT_E_INVAL, "scales.end must ascend");
+  if (sc->axis == 2) {
+    if (wgrad) return fail(GPT_E_INVAL, "scales along K (axis 2) need wgrad = 0");
+    for (int i = 0; i + 1 < sc->nseg; ++i)
+      if (sc->end[i] < 0 || sc->end[i] > K || sc->end[i] % 16)
+        return fail(GPT_E_INVAL, "scales.end[%d] = %lld: along K, need a multiple of 16 in [0, K]",
+                    i, (long long)sc->end[i]);
+  }
   for (int i = 0; i < sc->nseg; ++i)
     if (sc->slot_a[i] < 0 || sc->slot_b[i] < 0) return fail(GPT_E_INVAL, "amax slots must be >= 0");
   const size_t need = wgrad ? (size_t)part_bytes_f8_wgrad(M, N, K) : 0;
@@ -1186,6 +1191,10 @@ int gpt_fp8_gemm(int32_t wgrad, int64_t M, int64_t N, int64_t K, const uint8_t* 
   q.fb = FP8_E4M3;
   hipStream_t s = static_cast<hipStream_t>(stream);
   launch_reset();
+  if (q.axis == 2) {
+    gemm8_f32_kseg(M, N, K, A, lda, B, ldb, q, C, accumulate != 0, s);
+    return launch_status();
+  }
   const SplitSum r = gemm8_product(wgrad != 0, M, N, K, A, lda, B, ldb, q, C, accumulate != 0,
                                    static_cast<float*>(workspace), (int64_t)workspace_bytes, s);
   splitk_sum(r, s);

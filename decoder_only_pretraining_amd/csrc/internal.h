@@ -373,6 +373,12 @@ void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t l
 void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
                hipStream_t s);
+// The same with scales that change along K (dq.axis 2: segments of the
+// contraction cut at dq.end, in codes, multiples of 16): C (+)= sum over
+// segments i of f_i * (A_i B_i^T).
+void gemm8_f32_kseg(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                    const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,
+                    hipStream_t s);
 // Weight gradient (K = tokens, split over workgroups when that fills the
 // machine, partials as for gemm_tn_wgrad); C (+)= the product.
 SplitSum gemm8_wgrad(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,

@@ -295,8 +295,13 @@ int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t c
  * amax slots slot_a[i] and slot_b[i] of `amax` (uint32 bit patterns of
  * fp32 amax values, as gpt_fp8_quantize writes them), and
  * s = fmax / amax in fp32 (1 if amax is 0 or not finite; fmax 448 for
- * e4m3, 57344 for e5m2). Scales that change along K are handled by the
- * caller: one call per K segment, the later ones with accumulate = 1.
+ * e4m3, 57344 for e5m2). With axis 2 (wgrad = 0 only) the segments cut the
+ * contraction instead (ends multiples of 16, at most K):
+ *   C[m][n] (+)= sum over segments i of f_i * sum_{k in segment i} a b,
+ * as the step's attention input gradient runs it (its q, k and v parts
+ * carry their own scales); one launch that rescales its accumulators at
+ * the segment ends when the tile plan allows (K and the ends multiples of
+ * 128), else one product per segment.
  *   wgrad = 0: the product the step runs for forward and input-gradient
  *     linears; wgrad = 1: the weight-gradient product (K = tokens, split
  *     over workgroups with fp32 partials in `workspace`, then summed in a
@@ -308,7 +313,7 @@ int gpt_fp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t c
  * before anything is enqueued; the work is enqueued on `stream`.
  */
 typedef struct gpt_fp8_scales {
-  int32_t axis;        /* 0: segments of the M index, 1: of the N index    */
+  int32_t axis;        /* 0: segments of M, 1: of N, 2: of K (wgrad = 0)   */
   int32_t nseg;        /* 1, 2 or 3                                         */
   int64_t end[2];      /* exclusive ends of segments 0 and 1 (ascending)    */
   int32_t slot_a[3];   /* amax slot of A in segment i                       */

@@ -200,6 +200,27 @@ def test_bf16_gemm_rejects_bad_arguments_before_any_launch():
     assert g(2, 3072, 768, 16384, p, p, 0, p, p, n.value - 1, None) == -4
 
 
+def test_fp8_gemm_k_segments_rejected_before_any_launch():
+    """Scales along K (axis 2) are for the plain product only, with segment
+    ends that are multiples of 16 within K; anything else returns
+    GPT_E_INVAL before a launch (the pointers here are never dereferenced)."""
+    L = B.lib()
+    p = ctypes.c_void_p(1 << 20)
+    g = L.gpt_fp8_gemm
+
+    def sc(axis, ends, n):
+        s = B.Fp8Scales()
+        s.axis, s.nseg = axis, n
+        for i, e in enumerate(ends):
+            s.end[i] = e
+        return s
+
+    for wgrad, s in [(1, sc(2, [32], 2)), (0, sc(2, [40], 2)), (0, sc(2, [80], 2)),
+                     (0, sc(2, [-16], 2)), (0, sc(2, [48, 32], 3)), (0, sc(3, [], 1))]:
+        assert g(wgrad, 64, 64, 64, p, 64, 0, p, 64, p, ctypes.byref(s), 0, p, None, 0,
+                 None) == -1, (wgrad, s.axis, list(s.end))
+
+
 def test_decode_attn_validation_and_workspace():
     L = B.lib()
     # chunks of 128 visible positions per (sequence, KV head); one chunk: none

@@ -18,10 +18,13 @@ The three products of the c_q / c_k / c_v linears at d26 widths (C 1664,
            (segments of the output columns);
   dgrad    dx = g W: e5m2 x e4m3, one call per q / k / v segment of the
            contraction (separate output-gradient scales), accumulating;
+           and the same as one call with the scales cut along K (axis 2),
+           as the step runs it;
   wgrad    dW = g^T x: e5m2 x e4m3 on the transposed codes (tokens as the
            contraction, zero-padded), split over workgroups, separate
            gradient scales per output-row segment.
-Token counts 4096 (two sequences) and 300 (ragged)."""
+Token counts 5120 (enough 256-row tiles for the K-major kernel's single-launch
+K-segment form of dgrad) and 300 (ragged: one product per segment)."""
 import numpy as np
 import pytest
 
@@ -86,7 +89,7 @@ def _check(got, ref, absum, what):
     assert np.linalg.norm(ref) > 0
 
 
-@pytest.mark.parametrize("ntok", [4096, 300])
+@pytest.mark.parametrize("ntok", [5120, 300])
 def test_fp8_products_against_exact_dequantised(ntok):
     import torch
     rng = np.random.default_rng(ntok)
@@ -144,6 +147,19 @@ def test_fp8_products_against_exact_dequantised(ntok):
     torch.cuda.synchronize()
     _check(dx.cpu().numpy().astype(np.float64), ref, 2.0 ** -24 * (K + 2) * absum, "dgrad")
 
+    # the same contraction in one call with scales along K: the codes of the
+    # three gradients side by side [ntok][QKV], the transposed weights
+    # [C][QKV]; besides the K + 2 roundings of the accumulation, each of the
+    # two rescales at a segment end (f_prev / f_next, itself rounded) adds two
+    g8cat = torch.cat(g8, dim=1).contiguous()
+    wcat = torch.cat([wt[i][:, :n] for i, n in enumerate((CQ, CKV, CKV))], dim=1).contiguous()
+    dxk = torch.full((ntok, C), float("nan"), dtype=torch.float32, device=dev)
+    B.fp8_gemm(0, g8cat, QKV, B.FP8_E5M2, wcat, QKV, Q.amax,
+               _scales(2, [CQ, CQ + CKV], [4, 5, 6], [1, 2, 3]), dxk, ntok, C, QKV)
+    torch.cuda.synchronize()
+    _check(dxk.cpu().numpy().astype(np.float64), ref, 2.0 ** -24 * (K + 2 + 4) * absum,
+           "dgrad, K segments")
+
     # wgrad: dW = g^T x on the transposed codes, gradient scales by row segment
     dW = torch.full((QKV, C), float("nan"), dtype=torch.float32, device=dev)
     ws = B.fp8_gemm(1, g8t, Np, B.FP8_E5M2, x8t, Np, Q.amax,
@@ -160,11 +176,11 @@ def test_fp8_products_against_exact_dequantised(ntok):
 
     # a weight gradient of 1664 x 1664 (the attention output projection's
     # shape): few enough output tiles that the contraction over tokens is
-    # split over workgroups at 4096 tokens (fp32 partials, fixed-order sum)
+    # split over workgroups at 5120 tokens (fp32 partials, fixed-order sum)
     import ctypes
     n = ctypes.c_size_t()
     assert B.lib().gpt_fp8_gemm_workspace(1, CQ, C, Nk, ctypes.byref(n)) == 0
-    assert (n.value > 0) == (ntok >= 4096)
+    assert (n.value > 0) == (ntok >= 5120)
     dW2 = torch.full((CQ, C), float("nan"), dtype=torch.float32, device=dev)
     ws = B.fp8_gemm(1, g8t, Np, B.FP8_E5M2, x8t, Np, Q.amax, _scales(0, [], [4], [0]), dW2,
                     CQ, C, Nk)
@@ -187,8 +203,14 @@ def test_fp8_gemm_rejects_bad_arguments():
     assert g(0, 64, 64, 64, p, 32, 0, p, 64, p, ctypes.byref(sc), 0, p, None, 0, None) == -1
     assert g(0, 64, 64, 64, p, 64, 5, p, 64, p, ctypes.byref(sc), 0, p, None, 0, None) == -1
     assert g(0, 64, 64, 64, None, 64, 0, p, 64, p, ctypes.byref(sc), 0, p, None, 0, None) == -2
-    bad = _scales(2, [], [0], [0])
+    bad = _scales(3, [], [0], [0])
     assert g(0, 64, 64, 64, p, 64, 0, p, 64, p, ctypes.byref(bad), 0, p, None, 0, None) == -1
+    kseg = _scales(2, [32], [0, 1], [0, 1])
+    assert g(1, 64, 64, 64, p, 64, 0, p, 64, p, ctypes.byref(kseg), 0, p, None, 0, None) == -1
+    kseg = _scales(2, [40], [0, 1], [0, 1])                    # end not a multiple of 16
+    assert g(0, 64, 64, 64, p, 64, 0, p, 64, p, ctypes.byref(kseg), 0, p, None, 0, None) == -1
+    kseg = _scales(2, [80], [0, 1], [0, 1])                    # end past K
+    assert g(0, 64, 64, 64, p, 64, 0, p, 64, p, ctypes.byref(kseg), 0, p, None, 0, None) == -1
     n = ctypes.c_size_t()
     assert L.gpt_fp8_gemm_workspace(1, 1664, 1664, 16384, ctypes.byref(n)) == 0 and n.value > 0
     assert g(1, 1664, 1664, 16384, p, 16384, 1, p, 16384, p, ctypes.byref(sc), 0, p, p,
