@@ -76,9 +76,7 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const T* __restrict__ x, 
   __shared__ float red[6][4];
   float m[6] = {0, 0, 0, 0, 0, 0};
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += stride) {
-    float e[8];
-    load8(x + v * 8, e);
+  auto take = [&](int64_t v, const float* e) {
     float a = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(e[j]));
@@ -86,6 +84,20 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const T* __restrict__ x, 
 #pragma unroll
     for (int j = 0; j < 6; ++j)
       if (j == k) m[j] = fmaxf(m[j], a);
+  };
+  // four vectors in flight per thread, then the remainder one at a time
+  int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; v + 3 * stride < nv; v += 4 * stride) {
+    float e[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8(x + (v + u * stride) * 8, e[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) take(v + u * stride, e[u]);
+  }
+  for (; v < nv; v += stride) {
+    float e[8];
+    load8(x + v * 8, e);
+    take(v, e);
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll

@@ -711,21 +711,32 @@ __global__ __launch_bounds__(256) void veg_partial_kernel(const float* __restric
       }
     }
   }
+  // fully unrolled with constant indices (no early exit), so acc stays in
+  // registers; j < hk is uniform over the block
 #pragma unroll
-  for (int j = 0; j < HK; ++j) {  // constant indices keep acc in registers
-    if (j >= hk) break;            // uniform over the block
-    __syncthreads();
-    if (ph < NP) {
+  for (int j = 0; j < HK; ++j) {
+    if (j < hk) {
+      if (NP == 1) {  // one token phase (C > 1024): nothing to add across threads
+        if (ph == 0) {
+          float* dst = part + ((int64_t)blockIdx.x * hk + j) * C + cg * 8;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[j][4], acc[j][5], acc[j][6], acc[j][7]};
+        }
+        continue;
+      }
+      __syncthreads();
+      if (ph < NP) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[threadIdx.x * 8 + e] = acc[j][e];
-    }
-    __syncthreads();
-    if (ph == 0) {
+        for (int e = 0; e < 8; ++e) red[threadIdx.x * 8 + e] = acc[j][e];
+      }
+      __syncthreads();
+      if (ph == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[j][e];
-        for (int q = 1; q < NP; ++q) v += red[(q * CG + cg) * 8 + e];
-        part[((int64_t)blockIdx.x * hk + j) * C + cg * 8 + e] = v;
+        for (int e = 0; e < 8; ++e) {
+          float v = acc[j][e];
+          for (int q = 1; q < NP; ++q) v += red[(q * CG + cg) * 8 + e];
+          part[((int64_t)blockIdx.x * hk + j) * C + cg * 8 + e] = v;
+        }
       }
     }
   }
