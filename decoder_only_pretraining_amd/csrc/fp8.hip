@@ -70,10 +70,10 @@ __device__ __forceinline__ uint32_t cvt4(const float* v, float s, float fmax) {
 // Each block reduces through LDS and issues one atomic per segment: atomics
 // on one address serialise, so their number is kept to the block count.
 template <typename T>
-__global__ __launch_bounds__(256) void fp8_amax_kernel(const T* __restrict__ x, int64_t nv,
+__global__ __launch_bounds__(1024) void fp8_amax_kernel(const T* __restrict__ x, int64_t nv,
                                                        int64_t period, gpt::Segs sg,
                                                        uint32_t* __restrict__ amax) {
-  __shared__ float red[6][4];
+  __shared__ float red[6][16];
   float m[6] = {0, 0, 0, 0, 0, 0};
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   auto take = [&](int64_t v, const float* e) {
@@ -109,7 +109,9 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const T* __restrict__ x, 
   __syncthreads();
   if (threadIdx.x < sg.n) {
     const int j = threadIdx.x;
-    const float w = fmaxf(fmaxf(red[j][0], red[j][1]), fmaxf(red[j][2], red[j][3]));
+    float w = red[j][0];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) w = fmaxf(w, red[j][q]);
     if (w > 0.0f) atomicMax(amax + sg.slot[j], __float_as_uint(w));
   }
 }
@@ -178,12 +180,13 @@ void launch_fp8_amax(const void* x, bool bf16_src, int64_t n, int64_t period, co
                      uint32_t* amax, hipStream_t s) {
   if (n <= 0) return;
   const int64_t nv = n / 8;
-  const unsigned blocks = (unsigned)std::min<int64_t>((nv + 255) / 256, 1024);
+  // one 1024-thread block per CU at most: few atomics on the slots
+  const unsigned blocks = (unsigned)std::min<int64_t>((nv + 1023) / 1024, 256);
   if (bf16_src)
-    GK_LAUNCH(fp8_amax_kernel<bf16>, dim3(blocks), dim3(256), 0, s,
+    GK_LAUNCH(fp8_amax_kernel<bf16>, dim3(blocks), dim3(1024), 0, s,
                        static_cast<const bf16*>(x), nv, period, sg, amax);
   else
-    GK_LAUNCH(fp8_amax_kernel<float>, dim3(blocks), dim3(256), 0, s,
+    GK_LAUNCH(fp8_amax_kernel<float>, dim3(blocks), dim3(1024), 0, s,
                        static_cast<const float*>(x), nv, period, sg, amax);
 }
 
