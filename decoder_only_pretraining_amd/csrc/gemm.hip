@@ -114,6 +114,10 @@ __device__ __forceinline__ float sqrt_act(float x) {
 template <class Derived>
 struct EpBase {
   using Aux = NoAux;
+  // kAmax: the epilogue also returns max |stored value| of each store
+  // (store4m / store4am) and the kernel merges the block's maximum into
+  // *amax (when non-null) as the bits of a non-negative float
+  static constexpr bool kAmax = false;
   // the epilogue of K split `split` (all splits write the same C by default)
   __device__ Derived at_split(int) const { return static_cast<const Derived&>(*this); }
   // the epilogue of batch entry `b` (batched launches only)
@@ -211,36 +215,55 @@ struct EpLin : EpBase<EpLin<T>> {
 };
 template <typename T>
 struct EpRelu2 : EpBase<EpRelu2<T>> {  // C = relu(acc)^2 (the MLP hidden activation h)
+  static constexpr bool kAmax = true;
   T* C;
   int64_t ldc;
-  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
+  uint32_t* amax;  // max |C| (fp8 quantiser's amax slot), or null
+  __device__ float store4m(int64_t m, int64_t n, f32x4 v, int cnt) const {
     f32x4 o;
+    float mx = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float r = fmaxf(v[j], 0.0f);
       o[j] = r * r;
+      if (j < cnt) mx = fmaxf(mx, o[j]);
     }
     put4<T>(C + m * ldc + n, o, cnt);
+    return mx;
   }
+  __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const { (void)store4m(m, n, v, cnt); }
+  // the stored maximum: rounding to T is monotone, so max |round(o)| = round(max |o|)
+  __device__ float amax_of(float mx) const { return static_cast<float>(from_f<T>(mx)); }
 };
 template <typename T>
 struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {
   // g_u = g_h * d/du relu(u)^2 = g_h * 2 relu(u), with relu(u) = sqrt(h)
+  static constexpr bool kAmax = true;
   const T* H;
   T* C;
   int64_t ldc;
+  uint32_t* amax;  // max |C| (fp8 quantiser's amax slot), or null
   using Aux = typename Raw4<T>::type;
   __device__ Aux aux(int64_t m, int64_t n, int cnt) const { return get4raw<T>(H + m * ldc + n, cnt); }
-  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const Aux& hr) const {
+  __device__ float store4am(int64_t m, int64_t n, f32x4 v, int cnt, const Aux& hr) const {
     const f32x4 h = to_f4(hr);
     f32x4 o;
+    float mx = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = 2.0f * sqrt_act<T>(h[j]) * v[j];
+    for (int j = 0; j < 4; ++j) {
+      o[j] = 2.0f * sqrt_act<T>(h[j]) * v[j];
+      if (j < cnt) mx = fmaxf(mx, fabsf(o[j]));
+    }
     put4<T>(C + m * ldc + n, o, cnt);
+    return mx;
+  }
+  __device__ void store4a(int64_t m, int64_t n, f32x4 v, int cnt, const Aux& hr) const {
+    (void)store4am(m, n, v, cnt, hr);
   }
   __device__ void store4(int64_t m, int64_t n, f32x4 v, int cnt) const {
     store4a(m, n, v, cnt, aux(m, n, cnt));
   }
+  __device__ float amax_of(float mx) const { return static_cast<float>(from_f<T>(mx)); }
 };
 template <typename T>
 struct EpSoftcap : EpBase<EpSoftcap<T>> {  // c = cap * tanh(z / cap)
@@ -294,18 +317,20 @@ inline EpResid mk_resid(const float* R, float* C, int64_t ld) {
   return e;
 }
 template <typename T>
-EpRelu2<T> mk_relu2(void* C, int64_t ld) {
+EpRelu2<T> mk_relu2(void* C, int64_t ld, uint32_t* amax = nullptr) {
   EpRelu2<T> e;
   e.C = static_cast<T*>(C);
   e.ldc = ld;
+  e.amax = amax;
   return e;
 }
 template <typename T>
-EpRelu2Bwd<T> mk_relu2bwd(const void* H, void* C, int64_t ld) {
+EpRelu2Bwd<T> mk_relu2bwd(const void* H, void* C, int64_t ld, uint32_t* amax = nullptr) {
   EpRelu2Bwd<T> e;
   e.H = static_cast<const T*>(H);
   e.C = static_cast<T*>(C);
   e.ldc = ld;
+  e.amax = amax;
   return e;
 }
 template <typename T>
@@ -754,15 +779,17 @@ void gemm8_resid(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
 }
 
 void gemm8_relu2(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s) {
-  run_f8<1>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_relu2<bf16>(C, N), to_deq(dq), s);
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, uint32_t* amax_c,
+                 hipStream_t s) {
+  run_f8<1>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_relu2<bf16>(C, N, amax_c),
+            to_deq(dq), s);
 }
 
 void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                     const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const void* H, void* C,
-                    hipStream_t s) {
-  run_f8<2>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_relu2bwd<bf16>(H, C, N), to_deq(dq),
-            s);
+                    uint32_t* amax_c, hipStream_t s) {
+  run_f8<2>(pick_tile(M, N, K), A, lda, B, ldb, M, N, K, K, mk_relu2bwd<bf16>(H, C, N, amax_c),
+            to_deq(dq), s);
 }
 
 void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,

@@ -280,6 +280,31 @@ struct NoDeq {
 };
 // Aux type of an epilogue that reads no operand besides the accumulators.
 struct NoAux {};
+
+// Epilogues with kAmax also return max |stored value| per store (store4m,
+// store4am); the block's maximum, rounded as stored (amax_of), is merged
+// into *ep.amax with one integer atomic max (non-negative floats order like
+// their bits) when that pointer is set.
+template <class EP, class = void>
+struct EpAmax : std::false_type {};
+template <class EP>
+struct EpAmax<EP, std::void_t<decltype(EP::kAmax)>> : std::integral_constant<bool, EP::kAmax> {};
+
+template <class EP>
+__device__ __forceinline__ void amax_merge(const EP& ep, float mx) {
+  if (ep.amax == nullptr) return;  // uniform over the block
+  __shared__ float red[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  mx = wave_max(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = red[0];
+    for (int q = 1; q < (int)(blockDim.x >> 6); ++q) v = fmaxf(v, red[q]);
+    v = ep.amax_of(v);
+    if (v > 0.0f) atomicMax(ep.amax, __float_as_uint(v));
+  }
+}
 struct Deq8 {
   static constexpr bool kOn = true;
   static constexpr bool kKseg = false;
@@ -520,6 +545,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
   // A tile wholly inside C takes the branch-free form: every 4-column vector
   // is whole and in range (per-vector range checks put each aux load on its
   // own branch, and the loads then issue one at a time).
+  float amx = 0.0f;  // max |stored value| of this thread (kAmax epilogues)
   auto epilogue = [&](auto full_c) {
     constexpr bool FULL = decltype(full_c)::value;
     auto in_range = [&](int64_t m, int64_t n) { return FULL || (m < M && n < N); };
@@ -568,7 +594,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
             const int v = lane + 64 * (c * CV + t);
             const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
             const int64_t m = mw + i * 32 + r, n = nw + c4;
-            if (in_range(m, n)) ep.store4a(m, n, val[t], count(n), ax[i % NB][c * CV + t]);
+            if (in_range(m, n)) {
+              if constexpr (EpAmax<EP>::value)
+                amx = fmaxf(amx, ep.store4am(m, n, val[t], count(n), ax[i % NB][c * CV + t]));
+              else
+                ep.store4a(m, n, val[t], count(n), ax[i % NB][c * CV + t]);
+            }
           }
         }
         if constexpr (NB == 1)
@@ -586,7 +617,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
           const int v = lane + 64 * t;
           const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
           const int64_t m = mw + i * 32 + r, n = nw + c4;
-          if (in_range(m, n)) ep.store4(m, n, val[t], count(n));
+          if (in_range(m, n)) {
+            if constexpr (EpAmax<EP>::value)
+              amx = fmaxf(amx, ep.store4m(m, n, val[t], count(n)));
+            else
+              ep.store4(m, n, val[t], count(n));
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -597,6 +633,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(
     epilogue(std::true_type{});
   else
     epilogue(std::false_type{});
+  if constexpr (EpAmax<EP>::value) amax_merge(ep, amx);
 }
 
 
@@ -843,6 +880,7 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
   constexpr int NCH = 2, CV = NVS / NCH;
   static_assert(NVS % NCH == 0, "value chunks must tile the slab");
   using AuxT = typename EP::Aux;
+  float amx = 0.0f;  // max |stored value| of this thread (kAmax epilogues)
   auto epilogue = [&](auto full_c) {
     constexpr bool FULL = decltype(full_c)::value;
     auto in_range = [&](int64_t m, int64_t n) { return FULL || (m < M && n < N); };
@@ -896,8 +934,17 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
           const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
           const int64_t mm = mw + i * 32 + r, n = nw + c4;
           if (in_range(mm, n)) {
-            if constexpr (kAux) ep.store4a(mm, n, val[t], count(n), ax[c * CV + t]);
-            else ep.store4(mm, n, val[t], count(n));
+            if constexpr (kAux) {
+              if constexpr (EpAmax<EP>::value)
+                amx = fmaxf(amx, ep.store4am(mm, n, val[t], count(n), ax[c * CV + t]));
+              else
+                ep.store4a(mm, n, val[t], count(n), ax[c * CV + t]);
+            } else {
+              if constexpr (EpAmax<EP>::value)
+                amx = fmaxf(amx, ep.store4m(mm, n, val[t], count(n)));
+              else
+                ep.store4(mm, n, val[t], count(n));
+            }
           }
         }
       }
@@ -911,6 +958,7 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     epilogue(std::true_type{});
   else
     epilogue(std::false_type{});
+  if constexpr (EpAmax<EP>::value) amax_merge(ep, amx);
 }
 
 }  // namespace gk

@@ -515,6 +515,10 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     launch_fp8_amax(src, bf, N * cols, cols, sg, amax, s);
     launch_fp8_quant(src, bf, N, cols, false, sg, amax, fmt, q8, backward ? outT : nullptr, Np, s);
   };
+  // codes of a tensor whose producer already merged its amax into the slot
+  auto quant_only = [&](const void* src, int64_t cols, const Segs& sg, int fmt, uint8_t* outT) {
+    launch_fp8_quant(src, true, N, cols, false, sg, amax, fmt, q8, backward ? outT : nullptr, Np, s);
+  };
   if (d.fp8) {
     launch_zero(reinterpret_cast<float*>(amax), 16 * d.L, s);
     site("fp8.weights", s, [&] {
@@ -591,9 +595,10 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
     if (d.fp8) {
       site("fp8.quant", s, [&] { quant_tok(xn2, true, d.C, one_seg(slot(l, 8)), FP8_E4M3, LY8(l, P.l_x28t)); });
       site("gemm.fc.fwd", s, [&] {
-        gemm8_relu2(N, d.F, d.C, q8, d.C, w8(l, 2), d.C, deq1(slot(l, 8), slot(l, 4), FP8_E4M3), u, s);
+        gemm8_relu2(N, d.F, d.C, q8, d.C, w8(l, 2), d.C, deq1(slot(l, 8), slot(l, 4), FP8_E4M3), u,
+                    amax + slot(l, 9), s);
       });
-      site("fp8.quant", s, [&] { quant_tok(u, true, d.F, one_seg(slot(l, 9)), FP8_E4M3, LY8(l, P.l_h8t)); });
+      site("fp8.quant", s, [&] { quant_only(u, d.F, one_seg(slot(l, 9)), FP8_E4M3, LY8(l, P.l_h8t)); });
       site("gemm.mp.fwd", s, [&] {
         gemm8_resid(N, d.C, d.F, q8, d.F, w8(l, 3), d.F, deq1(slot(l, 9), slot(l, 5), FP8_E4M3),
                     xmid, X(l + 1), s);
@@ -694,14 +699,14 @@ static int run(const gpt_config* cfg, const float* params, const int32_t* tokens
         site("fp8.quant", s, [&] { quant_tok(gxc, true, C, one_seg(slot(l, 10)), FP8_E5M2, g8t); });
         site("gemm.mp.dgrad", s, [&] {
           gemm8_relu2bwd(N, Fh, C, q8, C, w8t(l, 3), P128(C),
-                         deq1(slot(l, 10), slot(l, 5), FP8_E5M2), u, gu, s);
+                         deq1(slot(l, 10), slot(l, 5), FP8_E5M2), u, gu, amax + slot(l, 11), s);
         });
         site("gemm.mp.wgrad", s, [&] {
           ssum = gemm8_wgrad(C, Fh, Nk, g8t, Np, LY8(l, P.l_h8t), Np,
                              deq1(slot(l, 10), slot(l, 9), FP8_E5M2), grads + F.mp[l], acc, part, pcap, s);
         });
         sum_splits();
-        site("fp8.quant", s, [&] { quant_tok(gu, true, Fh, one_seg(slot(l, 11)), FP8_E5M2, g8t); });
+        site("fp8.quant", s, [&] { quant_only(gu, Fh, one_seg(slot(l, 11)), FP8_E5M2, g8t); });
         site("gemm.fc.dgrad", s, [&] {
           gemm8_f32(N, C, Fh, q8, Fh, w8t(l, 2), P128(Fh), deq1(slot(l, 11), slot(l, 4), FP8_E5M2),
                     gtmp, false, s);

@@ -364,11 +364,15 @@ void gemm8_store(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
 void gemm8_resid(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                  const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const float* R, float* C,
                  hipStream_t s);
+// The two activation products also merge max |C| (the stored bf16 values)
+// into *amax_c when it is non-null: the amax the fp8 quantiser of C needs,
+// without a separate pass over C.
 void gemm8_relu2(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, hipStream_t s);
+                 const uint8_t* B, int64_t ldb, const Fp8Deq& dq, void* C, uint32_t* amax_c,
+                 hipStream_t s);
 void gemm8_relu2bwd(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                     const uint8_t* B, int64_t ldb, const Fp8Deq& dq, const void* H, void* C,
-                    hipStream_t s);
+                    uint32_t* amax_c, hipStream_t s);
 // C (+)= the product (accumulate: add to C).
 void gemm8_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                const uint8_t* B, int64_t ldb, const Fp8Deq& dq, float* C, bool accumulate,

@@ -121,3 +121,24 @@ def test_fp8_step_parity(w):
     # the fp8 mode really ran: the unquantised model differs beyond the bar
     l_plain = oracle.forward_loss(w, p, tok, tgt, dtype=np.float32, fp8=False)
     assert abs(l_plain - lo) > 0 and abs(lg - lo) < abs(lg - l_plain) + 1e-3 * abs(lo)
+
+
+@pytest.mark.parametrize("w", [SMALL_FP8, MID_FP8], ids=lambda w: w.name)
+def test_fused_amax_is_the_tensor_max(w):
+    """The c_fc product merges max |h| into h's amax slot, and the mlp c_proj
+    input-gradient product max |g_u| into g_u's, inside their epilogues (no
+    separate pass over the tensor). Each slot must hold exactly the largest
+    magnitude of the bf16 tensor it describes, the value a pass over that
+    tensor computes. small_fp8's products take the 4-wavefront kernel
+    (128 x 128 tiles), mid_fp8's the K-major one (256 x 256)."""
+    import torch
+    p, tok, tgt = inputs(w, 51, 52)
+    _, _, step = gpu_step(w, p, tok, tgt)
+    amax = step.region("amax").view(torch.int32).cpu().numpy().view(np.float32)
+    n = w.batch * w.seq_len
+    for l in range(w.n_layer):
+        h = step.region("h", l).view(torch.bfloat16).float().cpu().numpy()[:n * w.mlp_hidden]
+        assert amax[16 * l + 9] == np.max(np.abs(h)) > 0, l
+    # the g_u buffer is reused by every layer's backward; layer 0's is last
+    gu = step.region("gu").view(torch.bfloat16).float().cpu().numpy()[:n * w.mlp_hidden]
+    assert amax[11] == np.max(np.abs(gu)) > 0
