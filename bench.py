@@ -89,8 +89,9 @@ ROOF_KERNELS = {
     "wgrad": dict(
         sites="gemm.qkv.wgrad,gemm.fc.wgrad,gemm.mp.wgrad,gemm.o.wgrad",
         desc="weight-gradient GEMMs of the blocks, split-K partial sums (their reduction, "
-             "splitk_reduce_kernel, is timed apart): gemm_bf16_kernel<256, 256, 64, false, false, 0, "
-             "PreId, PreId, EpPart, NoDeq, 8> (8 wavefronts) and <128, 128, ..., EpPart, NoDeq, 4>",
+             "splitk_reduce_kernel, is timed apart): gemm_kmaj_kernel<256, EpPart, 0, NoDeq, true> "
+             "(token-major operands, direct LDS fills, 8 wavefronts) and gemm_bf16_kernel<128, 128, "
+             "..., EpPart, NoDeq, 4>",
         flops=_wgrad_flops, pmc="profiles/gemm_wgrad_d12_pmc.txt"),
     # every product of the block linears (with fp8 linears: the fp8 MFMA
     # products, against the fp8 peak; their quantisation is timed apart)

@@ -650,6 +650,19 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
       return;
     }
   }
+  // both operands token-major (the weight gradients): the same kernel with
+  // padded row-major stages and transposing fragment reads; the direct fills
+  // move 16 aligned bytes along M or N
+  if constexpr (BM == 256 && !AK && !BKM && !PA::kActive && !PB::kActive) {
+    const bool aligned16 = ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    if (K % 64 == 0 && (splits == 1 || kchunk % 64 == 0) && M >= 8 && N >= 8 && M % 8 == 0 &&
+        N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && sA % 8 == 0 && sB % 8 == 0 && aligned16) {
+      GK_LAUNCH((gemm_kmaj_kernel<BN, EP, 0, NoDeq, true>), grid, dim3(512), 0, s,
+                static_cast<const bf16*>(A), lda, static_cast<const bf16*>(B), ldb, M, N, K,
+                splits == 1 ? K : kchunk, tm, tn, ep, sA, sB);
+      return;
+    }
+  }
   constexpr int NW = BM == 256 ? 8 : 4;
   GK_LAUNCH((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq, NW>), grid,
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(A), lda,

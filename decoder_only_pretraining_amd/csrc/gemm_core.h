@@ -681,6 +681,42 @@ struct KmajFill {
   }
 };
 
+// Token-major (MN-major) stage of 64 contraction rows for the same kernel
+// (TNL): LDS row k holds the ROWS output-index elements of contraction row
+// k0 + k, with a pitch of ROWS + 32 elements, so the four rows a transposing
+// fragment read touches start 64 bytes apart in the bank space and the
+// gfx950 ds_read_b64_tr_b16 reads are conflict-free (see read_frag). A 1 KiB
+// fill chunk runs across row ends; its lanes that land in a row's padding
+// load that row's first 16 bytes again (never read back), so every lane of a
+// fill takes part and no lane mask is needed. Columns past MN read the last
+// 8 (their products are never stored).
+template <int ROWS>
+struct TnFill {
+  static constexpr int PITCH = ROWS + 32;
+  static constexpr int BYTES = 64 * PITCH * 2;
+  static constexpr int CHUNKS = BYTES / 1024;
+  static constexpr int NJ = (CHUNKS + 7) / 8;  // per wavefront (8 wavefronts; the last may idle)
+  static_assert(BYTES % 1024 == 0, "whole chunks per stage");
+  uint32_t off[NJ];
+  // byte offset of each of this lane's slots from the tile origin (contraction
+  // row k0, column mn0)
+  __device__ __forceinline__ void init(int64_t ld, int64_t mn0, int64_t MN, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int o = (wave + 8 * q) * 1024 + lane * 16;
+      const int r = o / (PITCH * 2), cb = o % (PITCH * 2);
+      const int col = cb < ROWS * 2 ? cb / 2 : 0;
+      const int64_t mn = min(mn0 + col, MN - 8);
+      off[q] = (uint32_t)(((int64_t)r * ld + (mn - mn0)) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16* tile, uint32_t lds, int wave) const {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q)
+      if (wave + 8 * q < CHUNKS) lds_fill16(tile, off[q], lds + (wave + 8 * q) * 1024);
+  }
+};
+
 //
 // fp8 mode (MODE 1: e4m3 x e4m3, 2: e5m2 x e4m3; DQ = Deq8): the operands
 // are codes handled as 2-byte units (K, the leading dimensions and the K
@@ -688,16 +724,25 @@ struct KmajFill {
 // stage holds 128 codes per row and is consumed by two 64-code slices of
 // v_mfma_f32_32x32x64_f8f6f4 (a fragment: 32 codes of one row per lane, two
 // 16-byte reads), and the epilogue dequantises by segment.
-template <int BN, class EP, int MODE = 0, class DQ = NoDeq>
+//
+// TNL: both operands token-major instead (the weight gradients: A(m, k) at
+// A[k * lda + m], B(n, k) at B[k * ldb + n]), bf16 only. The stages hold
+// TnFill's padded row-major tiles and the fragments are read with the
+// transposing LDS load (read_frag), which yields the same register layout,
+// so the schedule and the epilogue are unchanged.
+template <int BN, class EP, int MODE = 0, class DQ = NoDeq, bool TNL = false>
 __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B, int64_t ldb, int64_t M,
     int64_t N, int64_t K, int64_t kchunk, int tiles_m, int tiles_n, EP ep_in, int64_t bsA,
     int64_t bsB, DQ dq = DQ{}) {
   constexpr bool F8 = MODE != 0;
   static_assert(F8 == DQ::kOn, "fp8 products need a dequantisation");
+  static_assert(!(TNL && F8), "token-major operands: bf16 only");
   constexpr int BM = 256, NW = 8, KS = F8 ? 2 : 4;
   constexpr int WM = BM / 4, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-  constexpr int AEL = BM * 64, BEL = BN * 64;  // elements per stage
+  // elements per stage
+  constexpr int AEL = TNL ? TnFill<BM>::BYTES / 2 : BM * 64;
+  constexpr int BEL = TNL ? TnFill<BN>::BYTES / 2 : BN * 64;
   constexpr int SP = WN + 4;                   // epilogue staging row pitch (floats)
   constexpr int MAIN_BYTES = 2 * (AEL + BEL) * 2;
   constexpr int STAGE_BYTES = NW * 32 * SP * 4;
@@ -730,23 +775,30 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
   const int64_t k_lo = (int64_t)split * kchunk;
   const int nk = (int)((min(K, k_lo + kchunk) - k_lo) / 64);
 
-  KmajFill<BM> fa;
-  KmajFill<BN> fb;
+  std::conditional_t<TNL, TnFill<BM>, KmajFill<BM>> fa;
+  std::conditional_t<TNL, TnFill<BN>, KmajFill<BN>> fb;
   fa.init(lda, m0, M, wave, lane);
   fb.init(ldb, n0, N, wave, lane);
-  const bf16* Ab = A + m0 * lda + k_lo;
-  const bf16* Bb = B + n0 * ldb + k_lo;
+  const bf16* Ab = TNL ? A + k_lo * lda + m0 : A + m0 * lda + k_lo;
+  const bf16* Bb = TNL ? B + k_lo * ldb + n0 : B + n0 * ldb + k_lo;
+  const int64_t sta = TNL ? 64 * lda : 64, stb = TNL ? 64 * ldb : 64;  // per stage
   const uint32_t la = lds_addr(As), lb = lds_addr(Bs);
   auto fill = [&](int kt, int buf) {
-    fa.issue(Ab + (int64_t)kt * 64, la + buf * AEL * 2, wave);
-    fb.issue(Bb + (int64_t)kt * 64, lb + buf * BEL * 2, wave);
+    fa.issue(Ab + (int64_t)kt * sta, la + buf * AEL * 2, wave);
+    fb.issue(Bb + (int64_t)kt * stb, lb + buf * BEL * 2, wave);
   };
   auto kswz = [](int r, int g) { return r * 64 + ((g ^ ((r >> 1) & 7)) << 3); };
   auto fragA = [&](Frag<bf16>& f, int buf, int i, int ks) {
-    f.v = *reinterpret_cast<const bf16x8*>(As + buf * AEL + kswz(wm * WM + i * 32 + r32, 2 * ks + hi));
+    if constexpr (TNL)
+      read_frag<BM, 64, false>(f, As + buf * AEL, wm * WM + i * 32, ks, lane);
+    else
+      f.v = *reinterpret_cast<const bf16x8*>(As + buf * AEL + kswz(wm * WM + i * 32 + r32, 2 * ks + hi));
   };
   auto fragB = [&](Frag<bf16>& f, int buf, int j, int ks) {
-    f.v = *reinterpret_cast<const bf16x8*>(Bs + buf * BEL + kswz(wn * WN + j * 32 + r32, 2 * ks + hi));
+    if constexpr (TNL)
+      read_frag<BN, 64, false>(f, Bs + buf * BEL, wn * WN + j * 32, ks, lane);
+    else
+      f.v = *reinterpret_cast<const bf16x8*>(Bs + buf * BEL + kswz(wn * WN + j * 32 + r32, 2 * ks + hi));
   };
   // fp8: 32 codes of row r for 64-code slice ks: granules 4 ks + 2 hi, + 1
   auto frag8 = [&](Frag8& f, const bf16* base, int r, int ks) {
@@ -783,7 +835,11 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     if (nk > 1) {
       fill(1, 1);
       // vmcnt(fills of one stage): this wavefront's fills of stage 0 landed
-      __builtin_amdgcn_s_waitcnt(0x0f70 | (KmajFill<BM>::NJ + KmajFill<BN>::NJ));
+      // (token-major stages: the count differs between wavefronts, so all)
+      if constexpr (TNL)
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+      else
+        __builtin_amdgcn_s_waitcnt(0x0f70 | (KmajFill<BM>::NJ + KmajFill<BN>::NJ));
     } else {
       __builtin_amdgcn_s_waitcnt(0x0f70);
     }
@@ -838,7 +894,8 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     for (int i = 0; i < TM; ++i) fragA(a[0][i], 0, i, 0);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fragB(b[0][j], 0, j, 0);
-    constexpr int NR = TM + TN, NM = TM * TN;
+    // LDS read instructions per slice: one per fragment, two for transposing reads
+    constexpr int NR = (TNL ? 2 : 1) * (TM + TN), NM = TM * TN;
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
 #pragma unroll
