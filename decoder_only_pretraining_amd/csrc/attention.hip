@@ -288,13 +288,20 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
 // m_fix + log2(sum p). Only tiles on the causal diagonal or
 // the window edge compute a mask. The linear block id runs over (query
 // tile, head, batch), latest (costliest) tiles first.
-template <int D, bool ALIGNED>
-__global__ __launch_bounds__(512) void attn_fwd_tiled_kernel(const bf16* __restrict__ qkv,
-                                                             bf16* __restrict__ out,
-                                                             float* __restrict__ lse2, int T_,
-                                                             int H, int Hk, int W, int full,
-                                                             float c2, int nq, int nb) {
-  constexpr int BQ = 256, BKV = 64, S = 3;
+//
+// BQ = 128, S = 2 (the sliding-window layers): 4 wavefronts, all of them
+// loading, and two stages (72 KB of LDS), so two workgroups share a CU. A
+// window layer's query tiles all cost about the same, and 256-query tiles
+// (B H T / 256 of them, e.g. 384 at seq 2048, batch 8, 6 heads) would fill
+// 1.5 rounds of the CUs; 128-query tiles fill 1.5 rounds of the 512 slots
+// with half the work each.
+template <int D, bool ALIGNED, int BQ = 256, int S = 3>
+__global__ __launch_bounds__(2 * BQ) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_tiled_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ out,
+                           float* __restrict__ lse2, int T_, int H, int Hk, int W, int full,
+                           float c2, int nq, int nb) {
+  constexpr int BKV = 64;
+  static_assert((BQ == 256 && S == 3) || (BQ == 128 && S == 2), "tile forms");
   using GK = TileGeom<BKV, D, true>;    // K tile: rows = keys, contraction = d
   using GV = TileGeom<D, BKV, false>;   // V tile: [key][d + 32]
   using LK = DirectLoader<BKV, D, true>;
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(512) void attn_fwd_tiled_kernel(const bf16* __restr
 #pragma unroll
   for (int it = 0; it < S - 1; ++it)
     if (it < ntile) issue(it);
-  if (ntile > 1 && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);  // tile 0 landed
+  if (S == 3 && ntile > 1 && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);  // tile 0 landed
   else __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
   // One tile; the stage buffer CUR is a compile-time index so every LDS
@@ -421,16 +428,17 @@ __global__ __launch_bounds__(512) void attn_fwd_tiled_kernel(const bf16* __restr
           }
         }
     }
-    // tile it + 1 landed (tile it + 2 may still be in flight)
-    if (it + S - 1 < ntile && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
+    // tile it + 1 landed (with three stages tile it + 2 may still be in flight)
+    if (S == 3 && it + S - 1 < ntile && loader) __builtin_amdgcn_s_waitcnt(0x0f70 | PER_WAVE);
     else __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   };
-  static_assert(S == 3, "the tile loop is unrolled by the stage count");
+  // the tile loop is unrolled by the stage count
   for (int it = 0; it < ntile; it += S) {
     tile(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntile) tile(it + 1, std::integral_constant<int, 1>{});
-    if (it + 2 < ntile) tile(it + 2, std::integral_constant<int, 2>{});
+    if constexpr (S == 3)
+      if (it + 2 < ntile) tile(it + 2, std::integral_constant<int, 2>{});
   }
   if (t < T_) {
     const float inv = 1.0f / l_i;
@@ -1502,7 +1510,12 @@ void fwd(const gpt::Dims& d, bool full, const void* qkv, void* out, float* lse, 
   const float c2 = 1.4426950408889634f / sqrtf((float)D);
   if constexpr (sizeof(T) == 2) {
     const int nq = (d.T + 255) / 256;
-    if (d.T % 64 == 0)
+    if (!full && d.T % 64 == 0) {  // window layers: 128-query tiles
+      const int nq2 = d.T / 128 + (d.T % 128 != 0);
+      GK_LAUNCH((attn_fwd_tiled_kernel<D, true, 128, 2>), dim3((unsigned)(nq2 * d.H * d.B)),
+                dim3(256), 0, s, static_cast<const bf16*>(qkv), static_cast<bf16*>(out), lse, d.T,
+                d.H, d.Hk, d.W, 0, c2, nq2, d.B);
+    } else if (d.T % 64 == 0)
       GK_LAUNCH((attn_fwd_tiled_kernel<D, true>), dim3((unsigned)(nq * d.H * d.B)),
                          dim3(512), 0, s, static_cast<const bf16*>(qkv), static_cast<bf16*>(out),
                          lse, d.T, d.H, d.Hk, d.W, full ? 1 : 0, c2, nq, d.B);
