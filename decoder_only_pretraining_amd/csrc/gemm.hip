@@ -1047,9 +1047,33 @@ SplitSum gemm_nn_f32_splitk(const Dims& d, int64_t M, int N, int K, const void* 
   return SplitSum{};
 }
 
+// K splits of a bf16 weight gradient (chunks multiples of 64, at least 512
+// long): the count s with the least modelled time, where the split product
+// takes ceil(tiles * s / slots) rounds of workgroups (slots: 256, or 512 for
+// 128 x 128 tiles, two to a CU), each as long as its chunk, and every split
+// beyond one adds an fp32 partial of C written and read back. Work is priced
+// in MFMA flops per CU (~3.9 TFLOP/s in these products) against partial
+// bytes at ~5 TB/s of HBM: 0.8 flops per byte. Rounding 256 / tiles to the
+// nearest count instead can spill a few workgroups into a second round (a
+// 1280 x 768 gradient over 32,768 tokens: 13 splits of 20 tiles = 260
+// workgroups; 5120 x 1280: 3 splits of 100 tiles = 300).
 static KSplit tn_split(int64_t M, int64_t N, int64_t K) {
   const Tile t = pick_tile_wgrad(M, N);
-  return plan_split(tile_count(t, M, N), K, 64, 512, wgrad_target(t));
+  const int64_t tiles = tile_count(t, M, N), slots = wgrad_target(t);
+  const int64_t units = (K + 63) / 64;
+  KSplit best{K, 1};
+  double best_cost = -1.0;
+  for (int64_t sp = 1; sp <= 64 && sp <= units; ++sp) {
+    const int64_t chunk = (units + sp - 1) / sp * 64;
+    if (sp > 1 && chunk < 512) break;
+    const int64_t splits = (K + chunk - 1) / chunk;
+    if (splits != sp) continue;
+    const double rounds = (double)((tiles * splits + slots - 1) / slots);
+    double cost = rounds * (double)chunk * t.bm * t.bn * 2.0 * ((double)slots / 256.0);
+    if (splits > 1) cost += 0.8 * (double)splits * M * N * 8.0;
+    if (best_cost < 0 || cost < best_cost) best = KSplit{splits > 1 ? chunk : K, splits}, best_cost = cost;
+  }
+  return best;
 }
 int64_t part_bytes_tn_wgrad(const Dims& d, int64_t M, int64_t N, int64_t K) {
   if (!d.bf16) return 0;
