@@ -302,8 +302,8 @@ def optimizer_bench(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="d12")
     ap.add_argument("--fp8", default="auto", choices=["auto", "on", "off"],
                     help="block linears in fp8 (auto: as the workload defines)")
