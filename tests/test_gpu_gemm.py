@@ -119,7 +119,9 @@ WG = [(2304, 768, 16384, False), (3072, 768, 16384, False), (768, 3072, 16384, F
       (768, 768, 16384, True), (192, 128, 300, False), (192, 128, 300, True), (64, 64, 1, True),
       # token-major direct-fill kernel with tiles that end inside M and N:
       # 256 x 128 tiles (split-K, plain and accumulating), 256 x 192 tiles
-      (1984, 832, 4096, False), (1984, 832, 4096, True), (960, 960, 2048, False)]
+      (1984, 832, 4096, False), (1984, 832, 4096, True), (960, 960, 2048, False),
+      # 256 x 256 tiles with ragged edges (padding under an eighth of the area)
+      (2240, 1664, 4096, False)]
 
 
 @pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
