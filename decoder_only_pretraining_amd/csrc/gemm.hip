@@ -521,14 +521,30 @@ struct Tile {
 // wider tile. Measured on the d12 shapes (16384 rows, K = 768): N = 3072 runs
 // 100 us as 256 x 256 against 111 as 128 x 128, N = 2304 85 us as 256 x 192
 // (256 x 256 leaves a quarter wave) against 89, N = 768 35 us as 256 x 192.
+// A tile plan's cost: rounds of 256 workgroups x tile area, 256 x 128 tiles
+// priced 1.4x per area (they measured about that much slower per flop than
+// the wider tiles: d20's 1280-column products, moved from 3 rounds of 256 x
+// 256 to 5 of 256 x 128, made the step 5% slower). A tile must divide N,
+// except that 256 x 256 tiles may overhang M and N while the padding stays
+// under an eighth of the area (the 1664-wide d26 products).
+static bool tile_fits(Tile t, int64_t M, int64_t N) {
+  if (N % t.bn == 0) return true;
+  const int64_t pm = (M + t.bm - 1) / t.bm * t.bm, pn = (N + t.bn - 1) / t.bn * t.bn;
+  return t.bm == 256 && t.bn == 256 && pm * pn * 8 <= M * N * 9;
+}
+static int64_t tile_cost(Tile t, int64_t M, int64_t N) {
+  const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+  return (tiles + 255) / 256 * t.bm * t.bn * (t.bn == 128 ? 7 : 5);
+}
+
 static Tile pick_tile_bf16(int64_t M, int64_t N, int64_t K) {
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  const Tile cand[2] = {{256, 256}, {256, 192}};
+  const Tile cand[3] = {{256, 256}, {256, 192}, {256, 128}};
   Tile best{0, 0};
   int64_t best_cost = -1;
   for (const Tile& t : cand) {
-    if (N % t.bn != 0 || tiles(t.bm, t.bn) < 256) continue;
-    const int64_t cost = (tiles(t.bm, t.bn) + 255) / 256 * t.bm * t.bn;
+    if (!tile_fits(t, M, N) || tiles(t.bm, t.bn) < 256) continue;
+    const int64_t cost = tile_cost(t, M, N);
     if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;
   }
   if (best_cost >= 0) return best;
@@ -553,10 +569,11 @@ static Tile pick_tile(int64_t M, int64_t N, int64_t K) {
 // the product runs unsplit and the tile with the fewest tile-area x waves
 // wins (the lm_head gradient: 2 waves of 256 x 192 beat 1.5 of 256 x 256).
 // Otherwise split-K fills the machine: 256 x 256 where the shape has at
-// least 16 of them, else 256 x 192 with as many, 256 x 128 with at least 32,
-// else 128 x 128 (measured on the d12 weight gradients with the partial-sum
-// split-K below: the 768 x 768 one runs 36 vs 41 us as 128 x 128 x 14
-// splits instead of 256 x 128 x 14).
+// least 16 of them, else 256 x 192 with as many, 256 x 256 overhanging the
+// edges (below), 256 x 128 with at least 16, else 128 x 128 (the 768 x 768
+// gradient: 256 x 128 x 14 splits on the token-major K-major kernel beat
+// 128 x 128 x 14 splits on the register-staged one, d12 +0.3%; on the
+// register-staged kernel it had been the other way round, 41 vs 36 us).
 static Tile pick_tile_wgrad(int64_t M, int64_t N) {
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(256, 256) >= 256) {
@@ -564,8 +581,8 @@ static Tile pick_tile_wgrad(int64_t M, int64_t N) {
     Tile best = cand[0];
     int64_t best_cost = -1;
     for (const Tile& t : cand) {
-      if (N % t.bn != 0) continue;
-      const int64_t cost = (tiles(t.bm, t.bn) + 255) / 256 * t.bm * t.bn;
+      if (!tile_fits(t, M, N)) continue;
+      const int64_t cost = tile_cost(t, M, N);
       if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;
     }
     return best;
@@ -576,7 +593,7 @@ static Tile pick_tile_wgrad(int64_t M, int64_t N) {
   // eighth of the area (the d26 gradients with 1664-wide sides: 4992 x 1664
   // pads 10.5%, 6656 x 1664 7.7%), the narrower tile being the slower one
   if (tiles(256, 256) >= 16 && tiles(256, 256) * 65536 * 8 <= M * N * 9) return {256, 256};
-  if (tiles(256, 128) >= 32) return {256, 128};
+  if (tiles(256, 128) >= 16) return {256, 128};
   return {128, 128};
 }
 

@@ -78,7 +78,8 @@ def _splits(kind, M, N, K):
 
 NT = [(16384, 768, 2304, "QKV input gradient"), (16384, 3072, 768, "c_fc forward"),
       (16384, 768, 768, "o-proj forward"), (16384, 2304, 768, "QKV forward"),
-      (300, 192, 512, "ragged"), (77, 64, 64, "one tile, ragged")]
+      (300, 192, 512, "ragged"), (77, 64, 64, "one tile, ragged"),
+      (16384, 1664, 512, "256 x 256 tiles overhanging N")]
 
 
 @pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
@@ -120,8 +121,9 @@ WG = [(2304, 768, 16384, False), (3072, 768, 16384, False), (768, 3072, 16384, F
       # token-major direct-fill kernel with tiles that end inside M and N:
       # 256 x 128 tiles (split-K, plain and accumulating), 256 x 192 tiles
       (1984, 832, 4096, False), (1984, 832, 4096, True), (960, 960, 2048, False),
-      # 256 x 256 tiles with ragged edges (padding under an eighth of the area)
-      (2240, 1664, 4096, False)]
+      # 256 x 256 tiles with ragged edges (padding under an eighth of the area),
+      # split and unsplit
+      (2240, 1664, 4096, False), (32768, 1664, 256, False)]
 
 
 @pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
