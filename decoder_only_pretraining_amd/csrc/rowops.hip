@@ -661,8 +661,11 @@ __global__ __launch_bounds__(256) void lambda_finalize_kernel(const float* __res
 // the tokens [b * per, (b + 1) * per), per <= kVegPer: thread (phase,
 // column group) owns 8 consecutive columns and every NP-th token of the
 // range; the phases are then added in a fixed order and the block writes
-// its partial. A second kernel adds the partials in block order.
-constexpr int kVegPer = 64;
+// its partial. A second kernel adds the partials in block order. 32 tokens
+// per block (d12: 512 blocks, two per CU) keep twice the loads in flight of
+// 64-token blocks, whose threads walked their tokens in twice as many
+// dependent rounds.
+constexpr int kVegPer = 32;
 // the smear partials (one per kSmearRows rows) fit the gate-weight partial buffer
 static_assert(kSmearRows >= kVegPer, "smear partials exceed the veg partial rows");
 template <typename T, int HK>
