@@ -90,8 +90,8 @@ ROOF_KERNELS = {
         sites="gemm.qkv.wgrad,gemm.fc.wgrad,gemm.mp.wgrad,gemm.o.wgrad",
         desc="weight-gradient GEMMs of the blocks, split-K partial sums (their reduction, "
              "splitk_reduce_kernel, is timed apart): gemm_kmaj_kernel<256, EpPart, 0, NoDeq, true> "
-             "(token-major operands, direct LDS fills, 8 wavefronts) and gemm_bf16_kernel<128, 128, "
-             "..., EpPart, NoDeq, 4>; with fp8 block linears gemm_kmaj_kernel<BN, EpPart, 2, Deq8> "
+             "(token-major operands, direct LDS fills, 8 wavefronts; the 768 x 768 o-proj gradient "
+             "as gemm_kmaj_kernel<128, EpPart, 0, NoDeq, true>); with fp8 block linears gemm_kmaj_kernel<BN, EpPart, 2, Deq8> "
              "on the transposed e5m2 / e4m3 codes",
         flops=_wgrad_flops, pmc="profiles/gemm_wgrad_d12_pmc.txt", fp8_peak=True),
     # every product of the block linears (with fp8 linears: the fp8 MFMA
