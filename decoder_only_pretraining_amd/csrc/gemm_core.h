@@ -902,9 +902,15 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
       for (int ks = 0; ks < KS; ++ks) {
         const int p = ks & 1;
         if (ks == KS - 1) {
+          // wave priority: 1 while issuing a slice's MFMAs and fragment reads,
+          // 0 in the wait / barrier / fill section, so a wavefront in its
+          // MFMA burst wins issue over its SIMD partner (d12 +0.2%)
+          __builtin_amdgcn_s_setprio(0);
           __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
           __syncthreads();
           if (kt + 2 < nk) fill(kt + 2, cur);
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_setprio(1);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -922,6 +928,7 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __syncthreads();                     // the stage buffers become the epilogue's staging area
