@@ -539,7 +539,9 @@ static int64_t tile_cost(Tile t, int64_t M, int64_t N) {
 
 static Tile pick_tile_bf16(int64_t M, int64_t N, int64_t K) {
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  const Tile cand[3] = {{256, 256}, {256, 192}, {256, 128}};
+  // 256 x 320 (fewer operand bytes per flop than 256 x 256) where it saves a
+  // round: the d20 products with 1280 columns take 2 rounds instead of 2.5
+  const Tile cand[4] = {{256, 256}, {256, 192}, {256, 320}, {256, 128}};
   Tile best{0, 0};
   int64_t best_cost = -1;
   for (const Tile& t : cand) {
@@ -653,12 +655,32 @@ static bool check_part(int64_t need, int64_t cap) {
   return false;
 }
 
+// Epilogues that fit 256 registers with 256 x 320 tiles (all but ReLU²).
+template <class EP>
+struct WideEp : std::true_type {};
+template <typename T>
+struct WideEp<EpRelu2<T>> : std::false_type {};
+template <typename T>
+struct WideEp<EpRelu2Bwd<T>> : std::false_type {};
+
 // Products with 256-row tiles run 8 wavefronts per workgroup (two per SIMD,
 // measured 4-10% faster than 4 on the d12 products); the others 4.
 template <int BM, int BN, bool AK, bool BKM, class PA, class PB, class EP>
 void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N,
                  int64_t K, int64_t kchunk, PA pa, PB pb, EP ep, hipStream_t s, int batch = 1,
                  int64_t sA = 0, int64_t sB = 0) {
+  // 256 x 320 tiles exist only on the K-major kernel, and not for the ReLU²
+  // epilogues (with their 160-column wavefront tiles those exceed 256
+  // registers); anything else takes 256 x 256 tiles instead
+  if constexpr (BN == 320 && !(AK && BKM && !PA::kActive && !PB::kActive && WideEp<EP>::value)) {
+    launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
+  } else {
+  if constexpr (BN == 320) {
+    if (K % 64 != 0 || (kchunk < K && kchunk % 64 != 0)) {
+      launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
+      return;
+    }
+  }
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const int splits = K > 0 && kchunk > 0 ? (int)((K + kchunk - 1) / kchunk) : 1;
   // padded to a multiple of 8: see the kernel's tile order; y: batch entries
@@ -674,7 +696,7 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
   // both operands token-major (the weight gradients): the same kernel with
   // padded row-major stages and transposing fragment reads; the direct fills
   // move 16 aligned bytes along M or N
-  if constexpr (BM == 256 && !AK && !BKM && !PA::kActive && !PB::kActive) {
+  if constexpr (BM == 256 && BN != 320 && !AK && !BKM && !PA::kActive && !PB::kActive) {
     const bool aligned16 = ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
     if (K % 64 == 0 && (splits == 1 || kchunk % 64 == 0) && M >= 8 && N >= 8 && M % 8 == 0 &&
         N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && sA % 8 == 0 && sB % 8 == 0 && aligned16) {
@@ -685,10 +707,12 @@ void launch_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t
     }
   }
   constexpr int NW = BM == 256 ? 8 : 4;
+  if constexpr (BN != 320)
   GK_LAUNCH((gemm_bf16_kernel<BM, BN, 64, AK, BKM, 0, PA, PB, EP, NoDeq, NW>), grid,
                      dim3(64 * NW), 0, s, static_cast<const bf16*>(A), lda,
                      static_cast<const bf16*>(B), ldb, M, N, K, kchunk, tm, tn, pa, pb, ep, NoDeq{},
                      sA, sB);
+  }
 }
 
 template <bool AK, bool BKM, class PA, class PB, class EP>
@@ -697,6 +721,8 @@ void run_bf16(Tile t, const void* A, int64_t lda, const void* B, int64_t ldb, in
               int64_t sA = 0, int64_t sB = 0) {
   if (t.bm == 256 && t.bn == 256)
     launch_bf16<256, 256, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
+  else if (t.bm == 256 && t.bn == 320)
+    launch_bf16<256, 320, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
   else if (t.bm == 256 && t.bn == 192)
     launch_bf16<256, 192, AK, BKM>(A, lda, B, ldb, M, N, K, kchunk, pa, pb, ep, s, batch, sA, sB);
   else if (t.bm == 256 && t.bn == 128)

@@ -744,8 +744,12 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
   constexpr int AEL = TNL ? TnFill<BM>::BYTES / 2 : BM * 64;
   constexpr int BEL = TNL ? TnFill<BN>::BYTES / 2 : BN * 64;
   constexpr int SP = WN + 4;                   // epilogue staging row pitch (floats)
+  // rows of a wavefront's tile staged per epilogue pass: 32, or 8 for tiles
+  // wider than 256 columns (the staging area stays within the LDS, and the
+  // staged values and operand loads of a pass fit beside the accumulators)
+  constexpr int RS = WN > 128 ? 8 : 32;
   constexpr int MAIN_BYTES = 2 * (AEL + BEL) * 2;
-  constexpr int STAGE_BYTES = NW * 32 * SP * 4;
+  constexpr int STAGE_BYTES = NW * RS * SP * 4;
   __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES];
   const bf16* As = reinterpret_cast<const bf16*>(smem);
   const bf16* Bs = reinterpret_cast<const bf16*>(smem + 2 * AEL * 2);
@@ -938,11 +942,12 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
   // 4-column vectors; operand-reading epilogues load a slab of the operand
   // ahead of its stores.
   const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
-  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SP;
+  float* stage = reinterpret_cast<float*>(smem) + wave * RS * SP;
   constexpr bool kAux = !std::is_same<typename EP::Aux, NoAux>::value;
-  constexpr int NVS = 32 * WN / 4 / 64;
-  constexpr int NCH = 2, CV = NVS / NCH;
-  static_assert(NVS % NCH == 0, "value chunks must tile the slab");
+  constexpr int NVS = RS * WN / 4 / 64;
+  constexpr int NCH = RS == 32 ? 2 : NVS, CV = NVS / NCH;
+  constexpr int NH = 32 / RS;  // staging passes per 32-row slab
+  static_assert(NVS % NCH == 0 && RS * WN / 4 % 64 == 0, "value chunks must tile the slab");
   using AuxT = typename EP::Aux;
   float amx = 0.0f;  // max |stored value| of this thread (kAmax epilogues)
   auto epilogue = [&](auto full_c) {
@@ -950,19 +955,21 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
     auto in_range = [&](int64_t m, int64_t n) { return FULL || (m < M && n < N); };
     auto count = [&](int64_t n) { return FULL ? 4 : (int)min<int64_t>(4, N - n); };
     AuxT ax[kAux ? NVS : 1];
-    auto load_aux = [&](int i) {
+    auto load_aux = [&](int row0) {  // the operand of the RS rows from row0 of the wave tile
 #pragma unroll
       for (int t = 0; t < NVS; ++t) {
         const int v = lane + 64 * t;
         const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
-        const int64_t m = mw + i * 32 + r, n = nw + c4;
+        const int64_t m = mw + row0 + r, n = nw + c4;
         if (in_range(m, n)) ax[t] = ep.aux(m, n, count(n));
       }
     };
     if constexpr (kAux) load_aux(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int ih = 0; ih < TM * NH; ++ih) {
+      const int i = ih / NH, h = ih % NH;
       const int64_t m = mw + i * 32 + r32;
+      const bool mine = NH == 1 || r32 / RS == h;  // this lane's row is staged in this pass
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -979,7 +986,7 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             v[t] = ep.value(m, nw + nl + t, F8 ? acc[i][j][4 * g + t] * f : acc[i][j][4 * g + t]);
-          *reinterpret_cast<f32x4*>(stage + r32 * SP + nl) = v;
+          if (mine) *reinterpret_cast<f32x4*>(stage + (r32 % RS) * SP + nl) = v;
         }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged slab visible to the wavefront
       __builtin_amdgcn_wave_barrier();
@@ -996,7 +1003,7 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
         for (int t = 0; t < CV; ++t) {
           const int v = lane + 64 * (c * CV + t);
           const int r = v / (WN / 4), c4 = (v % (WN / 4)) * 4;
-          const int64_t mm = mw + i * 32 + r, n = nw + c4;
+          const int64_t mm = mw + i * 32 + h * RS + r, n = nw + c4;
           if (in_range(mm, n)) {
             if constexpr (kAux) {
               if constexpr (EpAmax<EP>::value)
@@ -1013,7 +1020,7 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
         }
       }
       if constexpr (kAux)
-        if (i + 1 < TM) load_aux(i + 1);
+        if (ih + 1 < TM * NH) load_aux((ih + 1) / NH * 32 + (ih + 1) % NH * RS);
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
     }

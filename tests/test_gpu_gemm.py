@@ -79,7 +79,8 @@ def _splits(kind, M, N, K):
 NT = [(16384, 768, 2304, "QKV input gradient"), (16384, 3072, 768, "c_fc forward"),
       (16384, 768, 768, "o-proj forward"), (16384, 2304, 768, "QKV forward"),
       (300, 192, 512, "ragged"), (77, 64, 64, "one tile, ragged"),
-      (16384, 1664, 512, "256 x 256 tiles overhanging N")]
+      (16384, 1664, 512, "256 x 256 tiles overhanging N"),
+      (16384, 1280, 768, "256 x 320 tiles"), (16200, 1280, 512, "256 x 320 tiles, ragged M")]
 
 
 @pytest.mark.parametrize("ints", [False, True], ids=["normal", "integer"])
