@@ -215,6 +215,7 @@ struct EpLin : EpBase<EpLin<T>> {
 };
 template <typename T>
 struct EpRelu2 : EpBase<EpRelu2<T>> {  // C = relu(acc)^2 (the MLP hidden activation h)
+  static constexpr bool kStage32 = true;
   static constexpr bool kAmax = true;
   T* C;
   int64_t ldc;
@@ -237,6 +238,7 @@ struct EpRelu2 : EpBase<EpRelu2<T>> {  // C = relu(acc)^2 (the MLP hidden activa
 };
 template <typename T>
 struct EpRelu2Bwd : EpBase<EpRelu2Bwd<T>> {
+  static constexpr bool kStage32 = true;
   // g_u = g_h * d/du relu(u)^2 = g_h * 2 relu(u), with relu(u) = sqrt(h)
   static constexpr bool kAmax = true;
   const T* H;
@@ -561,8 +563,19 @@ static Tile pick_tile_bf16(int64_t M, int64_t N, int64_t K) {
 static Tile pick_tile(int64_t M, int64_t N, int64_t K) {
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (K <= 1024 && tiles(128, 128) >= 1024 && tiles(128, 128) <= 8192) return {128, 128};
-  if (N % 256 == 0 && tiles(256, 256) >= 512) return {256, 256};
-  if (N % 192 == 0 && tiles(256, 192) >= 256) return {256, 192};
+  // otherwise the bf16 rule: the 256-row tile with the least rounds x area
+  // (256 x 128 at 1.4x per area; 256 x 256 may overhang by up to an eighth,
+  // e.g. the d26 products with 1664 columns: 2 rounds of 256 x 256 against 4
+  // of 256 x 128)
+  const Tile cand[3] = {{256, 256}, {256, 192}, {256, 128}};
+  Tile best{0, 0};
+  int64_t best_cost = -1;
+  for (const Tile& t : cand) {
+    if (!tile_fits(t, M, N) || tiles(t.bm, t.bn) < 256) continue;
+    const int64_t cost = tile_cost(t, M, N);
+    if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;
+  }
+  if (best_cost >= 0) return best;
   if (tiles(256, 128) >= 256) return {256, 128};
   return {128, 128};
 }
@@ -751,11 +764,10 @@ void launch_f8(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int
   const int64_t Kp = K / 2, kc = kchunk / 2;
   const int splits = Kp > 0 && kc > 0 ? (int)((Kp + kc - 1) / kc) : 1;
   dim3 grid((unsigned)((tm * tn * splits + 7) / 8 * 8));  // padded: see the kernel's tile order
-  // The K-major kernel's fp8 mode (8 wavefronts, direct fills); at 256
-  // columns the epilogues that read an fp32 operand do not fit its 256
-  // registers and stay on the 4-wavefront kernel.
-  constexpr bool kKmaj = BM == 256 && !(BN == 256 && (std::is_same<EP, EpResid>::value ||
-                                                      std::is_same<EP, EpF32>::value));
+  // The K-major kernel's fp8 mode (8 wavefronts, direct fills); its 256-
+  // column epilogues stage 8 rows per pass, so those that read an fp32
+  // operand fit its 256 registers too.
+  constexpr bool kKmaj = BM == 256;
   if constexpr (kKmaj) {
     if (Kp % 64 == 0 && (splits == 1 || kc % 64 == 0)) {
       GK_LAUNCH((gemm_kmaj_kernel<BN, EP, MODE, Deq8>), grid, dim3(512), 0, s,
@@ -872,7 +884,7 @@ SplitSum gemm8_product(bool wgrad, int64_t M, int64_t N, int64_t K, const uint8_
 
 static bool f8_kseg_fused(int64_t M, int64_t N, int64_t K, const Fp8Deq& dq) {
   const Tile t = pick_tile(M, N, K);
-  if (t.bm != 256 || (t.bn != 192 && t.bn != 128) || K % 128) return false;
+  if (t.bm != 256 || (t.bn != 256 && t.bn != 192 && t.bn != 128) || K % 128) return false;
   for (int i = 0; i + 1 < dq.nseg; ++i)
     if (dq.end[i] % 128 || dq.end[i] > K) return false;
   return true;
@@ -887,7 +899,10 @@ void gemm8_f32_kseg(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t l
     q.axis = 2;
     const EpF32 ep = mk_f32(C, N, accumulate ? 1 : 0);
     const Tile t = pick_tile(M, N, K);
-    if (t.bn == 192)
+    if (t.bn == 256)
+      GPT_F8_DISPATCH(dq, (launch_f8_kseg<256, 1>(A, lda, B, ldb, M, N, K, ep, q, s)),
+                      (launch_f8_kseg<256, 2>(A, lda, B, ldb, M, N, K, ep, q, s)));
+    else if (t.bn == 192)
       GPT_F8_DISPATCH(dq, (launch_f8_kseg<192, 1>(A, lda, B, ldb, M, N, K, ep, q, s)),
                       (launch_f8_kseg<192, 2>(A, lda, B, ldb, M, N, K, ep, q, s)));
     else

@@ -290,6 +290,15 @@ struct EpAmax : std::false_type {};
 template <class EP>
 struct EpAmax<EP, std::void_t<decltype(EP::kAmax)>> : std::integral_constant<bool, EP::kAmax> {};
 
+// Epilogues with kStage32 stage 32 rows per pass at any width (the ReLU²
+// ones: with 8-row passes their values stay live across more passes and
+// spill).
+template <class EP, class = void>
+struct EpStage32 : std::false_type {};
+template <class EP>
+struct EpStage32<EP, std::void_t<decltype(EP::kStage32)>>
+    : std::integral_constant<bool, EP::kStage32> {};
+
 template <class EP>
 __device__ __forceinline__ void amax_merge(const EP& ep, float mx) {
   if (ep.amax == nullptr) return;  // uniform over the block
@@ -744,10 +753,11 @@ __global__ __launch_bounds__(512) void gemm_kmaj_kernel(
   constexpr int AEL = TNL ? TnFill<BM>::BYTES / 2 : BM * 64;
   constexpr int BEL = TNL ? TnFill<BN>::BYTES / 2 : BN * 64;
   constexpr int SP = WN + 4;                   // epilogue staging row pitch (floats)
-  // rows of a wavefront's tile staged per epilogue pass: 32, or 8 for tiles
-  // wider than 256 columns (the staging area stays within the LDS, and the
-  // staged values and operand loads of a pass fit beside the accumulators)
-  constexpr int RS = WN > 128 ? 8 : 32;
+  // rows of a wavefront's tile staged per epilogue pass: 32, or 8 for bf16
+  // tiles wider than 256 columns and fp8 tiles of 256 (the staging area stays
+  // within the LDS, and the staged values and operand loads of a pass fit
+  // beside the accumulators and, in fp8 mode, the dequantisation factors)
+  constexpr int RS = (WN > 128 || (F8 && WN == 128)) && !EpStage32<EP>::value ? 8 : 32;
   constexpr int MAIN_BYTES = 2 * (AEL + BEL) * 2;
   constexpr int STAGE_BYTES = NW * RS * SP * 4;
   __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > STAGE_BYTES ? MAIN_BYTES : STAGE_BYTES];
